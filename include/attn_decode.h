@@ -1,0 +1,273 @@
+/*
+ * attn_decode.h — C ABI of the MI355X (gfx950) single-query GQA decode
+ * attention library (libattn_decode.so).
+ *
+ * What the library computes, and where the pages define it:
+ *  - Decode attention of one new query per head over a long KV cache,
+ *    out = sum_t softmax_t(q.k_t / sqrt(d)) v_t ("优化稀疏注意力中的令牌丢弃机制"
+ *    §2; "注意力优化（Attention Optimization）" 原理说明, softmax(QK^T/sqrt(d_k))V).
+ *  - Grouped-query attention: G query heads share one KV head; query head
+ *    qh = kh*G + g reads KV head kh ("注意力优化" 结构 2 and its GQA
+ *    repeat_interleave example; the NVIDIA blog "共同设计 AI 模型注意力…",
+ *    section 组规模, where G is the number of query heads per KV head).
+ *  - Flash-style tiling with an online softmax (running max m, sum l,
+ *    rescaled output) ("注意力优化" Flash Attention pseudo-code; NVIDIA blog,
+ *    section on how FlashAttention kernels compute attention).
+ *  - Split-KV: each sequence is cut into chunks processed in parallel whose
+ *    partial (max, sum-exp, output) triples are merged with the log-sum-exp
+ *    rule, with work balanced over variable-length sequences
+ *    ("优化稀疏注意力中的令牌丢弃机制" §5, Split-KV method and its cross-shard
+ *    online softmax).
+ *  - INT8 KV: q_val = round(val/scale); K scale per token partition
+ *    (scale = max|k| / 127 over the partition), V one per-tensor scale
+ *    ("优化稀疏注意力中的令牌丢弃机制" §6, per-tensor baseline and Scheme A).
+ *  - Output-aware token dropping (OAM): score_i = q.k_i/sqrt(d) +
+ *    beta*log(||v_i|| + eps), keep the top-K, attend exactly to those
+ *    ("优化稀疏注意力中的令牌丢弃机制" §3 pseudo-code and §7 composition).
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless a comment says otherwise.  The caller
+ *    owns every buffer, including workspaces; the library never allocates or
+ *    frees device memory and keeps no pointer after a call returns.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *    default stream).  Outputs are valid once the stream reaches that point.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    failed validation returns a status and enqueues nothing.  A failed
+ *    launch returns ATTN_ERR_HIP.  attn_last_error() describes the most
+ *    recent failure of the calling thread.  No C++ exception crosses the ABI.
+ *  - Calls hold no global state besides a per-device cache of the compute
+ *    unit count; they are safe to call from several host threads.  Calls
+ *    that share a workspace must be ordered on one stream.
+ *  - Non-finite inputs give undefined (but memory-safe) results.
+ *  - Element types: ATTN_F32 = IEEE fp32, ATTN_BF16 = bfloat16,
+ *    ATTN_I8 = int8 codes with fp32 scales.
+ */
+#ifndef LCDG_ATTN_DECODE_H
+#define LCDG_ATTN_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *attn_stream_t; /* a hipStream_t */
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1,
+  ATTN_ERR_UNSUPPORTED = 2,
+  ATTN_ERR_WORKSPACE_TOO_SMALL = 3,
+  ATTN_ERR_HIP = 4
+} attn_status;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1, ATTN_I8 = 2 } attn_dtype;
+
+/*
+ * KV-cache geometry shared by all calls (the problem statement of the NVIDIA
+ * blog's decode equations: batch DB = B, KV heads KH, head size Hsz = D,
+ * per-sequence KV length).  Row (b, kh, t) of K (or V) holds D contiguous
+ * elements starting at element seq_offset[b] + kh*stride_h + t*stride_t of
+ * the tensor.  This covers [B][KH][L][D], packed token-major [sum L][KH][D]
+ * and packed head-major [KH][sum L][D] caches.
+ *   B, KH, D      host ints; B >= 0, KH >= 1, D in {64, 128} for bf16/int8
+ *                 KV, D in [4, 256] and a multiple of 4 for fp32 KV
+ *   max_seq_len   host int >= every seq_lens[b]; sizes workspaces and
+ *                 scale tables (it is not checked against the device data)
+ *   seq_lens      device int32[B], 0 <= L_b <= max_seq_len
+ *   seq_offset    device int64[B], element offsets, >= 0
+ *   stride_h, stride_t  element strides, >= D; every row must be 16-byte
+ *                 aligned (so offsets and strides are multiples of 8 bf16 /
+ *                 4 fp32 / 16 int8 elements)
+ */
+typedef struct {
+  int32_t B, KH, D, max_seq_len;
+  const int32_t *seq_lens;
+  const int64_t *seq_offset;
+  int64_t stride_h, stride_t;
+} attn_kv_geom;
+
+/*
+ * Arguments of one decode step.
+ *   G           query heads per KV head, 1 <= G <= 64
+ *   q           [B][KH*G][D] in q_dtype (ATTN_BF16, or ATTN_F32 with fp32 KV)
+ *   k, v        KV cache in kv_dtype, geometry `kv`
+ *   k_scale     ATTN_I8 only: fp32 scale of K row (b, kh, t) is
+ *               k_scale[(b*KH + kh)*k_scale_stride + t / k_part_tokens];
+ *               k_part_tokens is a multiple of 16 (64 or 128 on the page),
+ *               k_scale_stride >= ceil(max_seq_len / k_part_tokens)
+ *   v_scale     ATTN_I8 only: the per-tensor V scale (host value)
+ *   token_idx   optional: when not NULL, (b, kh) attends only to the tokens
+ *               token_idx[(b*KH + kh)*idx_stride + j], j < n_idx[b*KH + kh]
+ *               (each < L_b; any order; n_idx <= idx_stride), e.g. the kept
+ *               set written by oam_score_topk
+ *   softmax_scale  multiplies q.k; 0 selects 1/sqrt(D)
+ *   split_tokens   tokens per split-KV chunk (multiple of 32); 0 = library
+ *               default (1024 for bf16/int8, 256 for fp32)
+ *   workspace   caller-owned scratch of at least attn_decode_workspace_size()
+ *               bytes, 256-byte aligned; holds the work-list and partials
+ *   out         [B][KH*G][D] in out_dtype (ATTN_F32 or ATTN_BF16)
+ *   lse         optional fp32 [B][KH*G]: natural-log log-sum-exp of the
+ *               scaled scores (-inf for a sequence with no tokens)
+ * A sequence (or kept set) with no tokens gives out = 0.
+ */
+typedef struct {
+  attn_kv_geom kv;
+  int32_t G;
+  int32_t q_dtype, kv_dtype, out_dtype;
+  const void *q;
+  const void *k;
+  const void *v;
+  const float *k_scale;
+  int32_t k_part_tokens, k_scale_stride;
+  float v_scale;
+  const int32_t *token_idx;
+  const int32_t *n_idx;
+  int32_t idx_stride;
+  float softmax_scale;
+  int32_t split_tokens;
+  void *workspace;
+  size_t workspace_bytes;
+  void *out;
+  float *lse;
+} attn_decode_args;
+
+/* Host-only: bytes of workspace attn_decode_splitkv needs for these args
+ * (depends on B, KH, G, D, max_seq_len or idx_stride, split_tokens, dtypes).
+ * Writes *bytes; returns ATTN_ERR_INVALID_ARG / ATTN_ERR_UNSUPPORTED for
+ * arguments attn_decode_splitkv would reject. */
+attn_status attn_decode_workspace_size(const attn_decode_args *args, size_t *bytes);
+
+/*
+ * Split-KV decode attention ("优化稀疏注意力中的令牌丢弃机制" §5 Split-KV;
+ * "注意力优化" Flash Attention online softmax).  One call enqueues:
+ *  (1) a work-list pass that cuts every (b, kh) token range into chunks of
+ *      split_tokens and lays out partial slots,
+ *  (2) a persistent decode kernel whose workgroups claim chunks from the list
+ *      with an integer atomic, stream each chunk's K/V rows once, and write
+ *      the chunk's partial (m, l, o) for each of the G query heads,
+ *  (3) the log-sum-exp merge of attn_merge_lse into out (and lse).
+ * Results are deterministic: no floating-point atomics are used.
+ */
+attn_status attn_decode_splitkv(const attn_decode_args *args, attn_stream_t stream);
+
+/*
+ * Log-sum-exp merge of partial triples ("优化稀疏注意力中的令牌丢弃机制" §5,
+ * cross-shard online softmax; read with the chunk term weighted by
+ * exp(m_chunk - m_new), which makes the result independent of the split).
+ * Row r (0 <= r < rows) owns partials row_split_start[r] ..
+ * row_split_start[r+1]-1 (device int32, CSR, non-decreasing, starting at 0).
+ * Partial i: m_part[i] = max scaled score (natural log units), l_part[i] =
+ * sum exp(s - m_part[i]) >= 0, o_part[i*D .. i*D+D-1] = that chunk's
+ * normalised output.  Partials with l_part = 0 are ignored.
+ *   out[r*D + d] = sum_i exp(m_i - M) l_i o_i[d] / sum_i exp(m_i - M) l_i,
+ *   lse[r] = M + ln(sum_i exp(m_i - M) l_i), M = max over partials with l > 0;
+ * a row with no (non-empty) partial gets out = 0 and lse = -inf.
+ * out_dtype is ATTN_F32 or ATTN_BF16; lse may be NULL.  1 <= D <= 256.
+ */
+attn_status attn_merge_lse(const float *o_part, const float *m_part, const float *l_part,
+                           const int32_t *row_split_start, int32_t rows, int32_t D, int32_t out_dtype,
+                           void *out, float *lse, attn_stream_t stream);
+
+/* Host-only: workspace bytes for kv_quant_int8 (0 for per-partition mode). */
+attn_status kv_quant_int8_workspace_size(const attn_kv_geom *geom, int32_t partition_tokens, size_t *bytes);
+
+/*
+ * INT8 quantisation of a bf16 K or V cache ("优化稀疏注意力中的令牌丢弃机制"
+ * §6): q_val = round(val / scale), round half to even on the IEEE fp32
+ * quotient, clamped to [-127, 127].
+ *   partition_tokens > 0 (a multiple of 16; 64 or 128 on the page): Scheme A
+ *     per-token-partition scales.  Partitions start at token 0 of every
+ *     (b, kh); scale = fl32(max|x| / 127) over the partition's tokens and all
+ *     D channels; it is written to scales[(b*KH + kh)*scale_stride + t/P]
+ *     (scale_stride >= ceil(max_seq_len / P)).  An all-zero partition gets
+ *     scale 0 and codes 0.
+ *   partition_tokens == 0: one per-tensor scale over every valid row of every
+ *     (b, kh), written to scales[0] (the page's per-tensor baseline, used for V).
+ *   x_bf16   bf16 cache in geometry `geom`
+ *   codes    int8 output in the same geometry (same offsets and strides, in
+ *            elements); rows t >= L_b are not touched
+ *   workspace  per-tensor mode only: >= kv_quant_int8_workspace_size() bytes
+ * Run once when the cache is written, not per decode step.
+ */
+attn_status kv_quant_int8(const attn_kv_geom *geom, const void *x_bf16, int32_t partition_tokens,
+                          int32_t scale_stride, int8_t *codes, float *scales, void *workspace,
+                          size_t workspace_bytes, attn_stream_t stream);
+
+/*
+ * ln(||v_t||_2 + eps) of every bf16 V row, the value term of the OAM score
+ * ("优化稀疏注意力中的令牌丢弃机制" §3: torch.log(v_i.norm() + eps)).  A row never
+ * changes once appended, so this can be computed at append time and passed
+ * to oam_score_topk.  vlog[(b*KH + kh)*vlog_stride + t] for t < L_b
+ * (vlog_stride >= max_seq_len).  Accumulates in fp32.
+ */
+attn_status oam_value_lognorm(const attn_kv_geom *geom, const void *v_bf16, float eps, float *vlog,
+                              int32_t vlog_stride, attn_stream_t stream);
+
+/*
+ * Arguments of output-aware top-K token selection.
+ *   q, k        bf16; q [B][KH*G][D], k in geometry `kv`; 1 <= G <= 16
+ *   v, vlog     the value term comes from vlog (fp32, layout of
+ *               oam_value_lognorm, stride vlog_stride) when vlog != NULL,
+ *               else it is computed from the bf16 rows of v on the fly
+ *   softmax_scale  0 selects 1/sqrt(D); beta, eps as on the page
+ *   top_k       >= 1 tokens kept per (b, kh)
+ *   idx_out     int32 [B][KH][top_k]: kept token indices in ascending order;
+ *               entries past n_kept are set to -1
+ *   n_kept      int32 [B][KH] = min(top_k, L_b)
+ *   scores_out  optional fp32 [B][KH][max_seq_len]: the scores
+ *   workspace   >= oam_score_topk_workspace_size() bytes, 256-byte aligned
+ */
+typedef struct {
+  attn_kv_geom kv;
+  int32_t G;
+  const void *q;
+  const void *k;
+  const void *v;
+  const float *vlog;
+  int32_t vlog_stride;
+  float softmax_scale, beta, eps;
+  int32_t top_k;
+  int32_t *idx_out;
+  int32_t *n_kept;
+  float *scores_out;
+  void *workspace;
+  size_t workspace_bytes;
+} oam_topk_args;
+
+/* Host-only: workspace bytes of oam_score_topk. */
+attn_status oam_score_topk_workspace_size(const oam_topk_args *args, size_t *bytes);
+
+/*
+ * OAM scoring and top-K selection ("优化稀疏注意力中的令牌丢弃机制" §3: score
+ * tokens by routing logit plus value magnitude and drop the lowest; §2 for
+ * the classic q.k top-K it replaces).  For each (b, kh):
+ *   score_t = mean_g (q_g . k_t) * softmax_scale + beta * ln(||v_t||_2 + eps)
+ * (the mean over the G query heads gives one kept set per KV head), then the
+ * top_k tokens by (score descending, index ascending) are kept.  Scores are
+ * fp32; the selection is an exact radix select on order-preserving integer
+ * keys of the fp32 scores.  Feed idx_out/n_kept to attn_decode_splitkv's
+ * token_idx/n_idx for exact attention over the kept tokens (§7).
+ */
+attn_status oam_score_topk(const oam_topk_args *args, attn_stream_t stream);
+
+/* Static description of a status code. */
+const char *attn_status_string(attn_status status);
+
+/* Message describing the calling thread's most recent failed call ("" if none). */
+const char *attn_last_error(void);
+
+/*
+ * Measurement helpers (not part of the method): a plain device copy of
+ * `bytes` (multiple of 16, 16-byte aligned pointers) and a read-only sweep
+ * that writes one checksum word per workgroup into sink (>= 4096 floats).
+ * They calibrate hardware byte counters and the achievable HBM bandwidth.
+ */
+attn_status attn_util_copy(void *dst, const void *src, size_t bytes, attn_stream_t stream);
+attn_status attn_util_read(const void *src, size_t bytes, float *sink, attn_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LCDG_ATTN_DECODE_H */

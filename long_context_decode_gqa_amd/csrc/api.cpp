@@ -1,0 +1,259 @@
+// C ABI of libattn_decode.so: host-side validation, workspace layout and
+// dispatch.  Nothing is enqueued until every argument check has passed.
+#include <math.h>
+#include <stdio.h>
+
+#include <mutex>
+#include <string>
+
+#include "common.hpp"
+
+namespace lcdg {
+namespace {
+
+thread_local std::string g_last_error;
+
+attn_status fail(attn_status st, const char *msg) {
+  g_last_error = msg;
+  return st;
+}
+
+attn_status fail_hip(hipError_t e, const char *where) {
+  g_last_error = std::string(where) + ": " + hipGetErrorString(e);
+  return ATTN_ERR_HIP;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int elem_size(int dt) { return dt == ATTN_F32 ? 4 : dt == ATTN_BF16 ? 2 : 1; }
+
+std::mutex g_cu_mutex;
+int g_cu_cache[64] = {0};
+
+}  // namespace
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(g_cu_mutex);
+  if (g_cu_cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    g_cu_cache[dev] = n;
+  }
+  return g_cu_cache[dev];
+}
+
+namespace {
+
+// Validation shared by every call that takes a KV geometry.
+attn_status check_geom(const attn_kv_geom &g, int es, bool need_ptrs) {
+  if (g.B < 0 || g.KH < 1 || g.D < 1 || g.max_seq_len < 0)
+    return fail(ATTN_ERR_INVALID_ARG, "geometry: need B >= 0, KH >= 1, D >= 1, max_seq_len >= 0");
+  if ((int64_t)g.B * g.KH > (1 << 24)) return fail(ATTN_ERR_UNSUPPORTED, "geometry: B*KH above 2^24");
+  if (g.stride_t < g.D || g.stride_h < g.D) return fail(ATTN_ERR_INVALID_ARG, "geometry: strides must be >= D");
+  if ((g.stride_t * es) % 16 || (g.stride_h * es) % 16 || ((int64_t)g.D * es) % 4)
+    return fail(ATTN_ERR_INVALID_ARG, "geometry: rows must be 16-byte aligned (stride_t, stride_h in bytes % 16)");
+  if (need_ptrs && g.B > 0 && (!g.seq_lens || !g.seq_offset))
+    return fail(ATTN_ERR_INVALID_ARG, "geometry: seq_lens and seq_offset are required");
+  return ATTN_OK;
+}
+
+struct DecodeLayout {
+  size_t hdr, item_start, rss, chunks, m, l, o, total;
+  int64_t max_partials;
+  int32_t split, ngb, max_tokens;
+  bool mfma;
+};
+
+attn_status plan_decode(const attn_decode_args *a, DecodeLayout *L) {
+  if (!a) return fail(ATTN_ERR_INVALID_ARG, "args is NULL");
+  const attn_kv_geom &g = a->kv;
+  if (a->kv_dtype != ATTN_F32 && a->kv_dtype != ATTN_BF16 && a->kv_dtype != ATTN_I8)
+    return fail(ATTN_ERR_INVALID_ARG, "kv_dtype must be ATTN_F32, ATTN_BF16 or ATTN_I8");
+  if (a->out_dtype != ATTN_F32 && a->out_dtype != ATTN_BF16)
+    return fail(ATTN_ERR_INVALID_ARG, "out_dtype must be ATTN_F32 or ATTN_BF16");
+  if (a->q_dtype != ATTN_F32 && a->q_dtype != ATTN_BF16) return fail(ATTN_ERR_INVALID_ARG, "q_dtype must be F32 or BF16");
+  if (a->kv_dtype == ATTN_F32 && a->q_dtype != ATTN_F32)
+    return fail(ATTN_ERR_UNSUPPORTED, "fp32 KV needs fp32 Q");
+  if (a->kv_dtype != ATTN_F32 && a->q_dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "bf16 and int8 KV need bf16 Q");
+  attn_status st = check_geom(g, elem_size(a->kv_dtype), true);
+  if (st != ATTN_OK) return st;
+  if (a->G < 1 || a->G > 64) return fail(ATTN_ERR_UNSUPPORTED, "G must be in [1, 64]");
+  const bool mfma = a->kv_dtype != ATTN_F32;
+  if (mfma && g.D != 64 && g.D != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, "bf16/int8 KV supports head size D = 64 or 128");
+  if (!mfma && (g.D < 4 || g.D > 256 || g.D % 4))
+    return fail(ATTN_ERR_UNSUPPORTED, "fp32 KV supports D in [4, 256], a multiple of 4");
+  if (a->kv_dtype == ATTN_I8 && (g.stride_t % 16 || g.stride_h % 16))
+    return fail(ATTN_ERR_INVALID_ARG, "int8 KV rows must be 16-byte aligned");
+  if (!(fabsf(a->softmax_scale) < INFINITY)) return fail(ATTN_ERR_INVALID_ARG, "softmax_scale must be finite");
+  if (a->split_tokens < 0 || (a->split_tokens && (a->split_tokens % 32 || a->split_tokens > (1 << 20))))
+    return fail(ATTN_ERR_INVALID_ARG, "split_tokens must be 0 or a positive multiple of 32 (<= 2^20)");
+  if (a->token_idx && (!a->n_idx || a->idx_stride < 0))
+    return fail(ATTN_ERR_INVALID_ARG, "token_idx needs n_idx and idx_stride >= 0");
+  if (a->kv_dtype == ATTN_I8) {
+    if (!a->k_scale) return fail(ATTN_ERR_INVALID_ARG, "int8 KV needs k_scale");
+    if (a->k_part_tokens < 16 || a->k_part_tokens % 16)
+      return fail(ATTN_ERR_INVALID_ARG, "k_part_tokens must be a positive multiple of 16");
+    const int64_t need = ((int64_t)g.max_seq_len + a->k_part_tokens - 1) / a->k_part_tokens;
+    if (a->k_scale_stride < need || a->k_scale_stride < 1)
+      return fail(ATTN_ERR_INVALID_ARG, "k_scale_stride must be >= ceil(max_seq_len / k_part_tokens)");
+    if (!(fabsf(a->v_scale) < INFINITY)) return fail(ATTN_ERR_INVALID_ARG, "v_scale must be finite");
+  }
+  if (g.B > 0) {
+    if (!a->q || !a->k || !a->v || !a->out) return fail(ATTN_ERR_INVALID_ARG, "q, k, v and out are required");
+    if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v))
+      return fail(ATTN_ERR_INVALID_ARG, "q, k and v must be 16-byte aligned");
+  }
+  L->mfma = mfma;
+  L->split = a->split_tokens ? a->split_tokens : (mfma ? 1024 : 256);
+  L->ngb = (a->G + 15) / 16;
+  L->max_tokens = a->token_idx ? a->idx_stride : g.max_seq_len;
+  const int64_t max_chunks = ((int64_t)L->max_tokens + L->split - 1) / L->split;
+  const int64_t QH = (int64_t)g.KH * a->G;
+  L->max_partials = (int64_t)g.B * QH * max_chunks;
+  const int64_t max_items = (int64_t)g.B * g.KH * max_chunks * L->ngb;
+  if (L->max_partials >= (int64_t(1) << 31) || max_items >= (int64_t(1) << 31))
+    return fail(ATTN_ERR_UNSUPPORTED, "too many split-KV partials (reduce max_seq_len or raise split_tokens)");
+  const int64_t npairs = (int64_t)g.B * g.KH;
+  size_t off = 0;
+  L->hdr = off; off = align256(off + 64 * sizeof(int32_t));
+  L->item_start = off; off = align256(off + (npairs + 1) * sizeof(int32_t));
+  L->rss = off; off = align256(off + ((int64_t)g.B * QH + 1) * sizeof(int32_t));
+  L->chunks = off; off = align256(off + npairs * sizeof(int32_t));
+  L->m = off; off = align256(off + L->max_partials * sizeof(float));
+  L->l = off; off = align256(off + L->max_partials * sizeof(float));
+  L->o = off; off = align256(off + (size_t)L->max_partials * g.D * sizeof(float));
+  L->total = off;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+attn_status api_fail(attn_status st, const char *msg) { return fail(st, msg); }
+attn_status api_fail_hip(hipError_t e, const char *where) { return fail_hip(e, where); }
+attn_status api_check_geom(const attn_kv_geom &g, int es, bool need_ptrs) { return check_geom(g, es, need_ptrs); }
+
+}  // namespace lcdg
+
+using namespace lcdg;
+
+extern "C" {
+
+const char *attn_status_string(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char *attn_last_error(void) { return g_last_error.c_str(); }
+
+attn_status attn_decode_workspace_size(const attn_decode_args *args, size_t *bytes) {
+  if (!bytes) return fail(ATTN_ERR_INVALID_ARG, "bytes is NULL");
+  DecodeLayout L;
+  attn_status st = plan_decode(args, &L);
+  if (st != ATTN_OK) return st;
+  *bytes = L.total;
+  return ATTN_OK;
+}
+
+attn_status attn_decode_splitkv(const attn_decode_args *a, attn_stream_t stream) {
+  DecodeLayout L;
+  attn_status st = plan_decode(a, &L);
+  if (st != ATTN_OK) return st;
+  if (a->kv.B == 0) return ATTN_OK;
+  if (!a->workspace || (reinterpret_cast<uintptr_t>(a->workspace) & 255))
+    return fail(ATTN_ERR_INVALID_ARG, "workspace must be a 256-byte aligned device pointer");
+  if (a->workspace_bytes < L.total) return fail(ATTN_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than required");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char *ws = static_cast<char *>(a->workspace);
+  DecodeParams p;
+  p.B = a->kv.B;
+  p.KH = a->kv.KH;
+  p.G = a->G;
+  p.D = a->kv.D;
+  p.QH = a->kv.KH * a->G;
+  p.ngb = L.ngb;
+  p.seq_lens = a->kv.seq_lens;
+  p.seq_offset = a->kv.seq_offset;
+  p.stride_h = a->kv.stride_h;
+  p.stride_t = a->kv.stride_t;
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.k_scale = a->k_scale;
+  p.k_part = a->k_part_tokens > 0 ? a->k_part_tokens : 64;
+  p.k_scale_stride = a->k_scale_stride;
+  p.v_scale = a->v_scale;
+  p.token_idx = a->token_idx;
+  p.n_idx = a->n_idx;
+  p.idx_stride = a->idx_stride;
+  p.softmax_scale = a->softmax_scale != 0.f ? a->softmax_scale : 1.0f / sqrtf((float)a->kv.D);
+  p.split = L.split;
+  p.max_seq_len = a->kv.max_seq_len;
+  p.wl.counter = reinterpret_cast<int32_t *>(ws + L.hdr);
+  p.wl.total_items = reinterpret_cast<int32_t *>(ws + L.hdr) + 1;
+  p.wl.item_start = reinterpret_cast<int32_t *>(ws + L.item_start);
+  p.wl.row_split_start = reinterpret_cast<int32_t *>(ws + L.rss);
+  p.wl.chunks = reinterpret_cast<int32_t *>(ws + L.chunks);
+  p.wl.m_part = reinterpret_cast<float *>(ws + L.m);
+  p.wl.l_part = reinterpret_cast<float *>(ws + L.l);
+  p.wl.o_part = reinterpret_cast<float *>(ws + L.o);
+
+  hipError_t e = launch_worklist(p, s);
+  if (e != hipSuccess) return fail_hip(e, "work-list launch");
+  const int64_t max_chunks = ((int64_t)L.max_tokens + L.split - 1) / L.split;
+  const int64_t max_items = (int64_t)p.B * p.KH * max_chunks * L.ngb;
+  const int cus = device_cu_count();
+  int64_t grid = (int64_t)cus * (L.mfma ? 2 : 4);
+  if (grid > max_items) grid = max_items;
+  if (grid < 1) grid = 1;
+  if (L.mfma) e = launch_decode_mfma(p, a->kv_dtype, (int)grid, s);
+  else e = launch_decode_valu(p, a->q_dtype, a->kv_dtype, (int)grid, s);
+  if (e != hipSuccess) return fail_hip(e, "decode launch");
+  e = launch_merge(p.wl.o_part, p.wl.m_part, p.wl.l_part, p.wl.row_split_start, p.B * p.QH, p.D, a->out_dtype,
+                   a->out, a->lse, s);
+  if (e != hipSuccess) return fail_hip(e, "merge launch");
+  return ATTN_OK;
+}
+
+attn_status attn_merge_lse(const float *o_part, const float *m_part, const float *l_part,
+                           const int32_t *row_split_start, int32_t rows, int32_t D, int32_t out_dtype, void *out,
+                           float *lse, attn_stream_t stream) {
+  if (rows < 0) return fail(ATTN_ERR_INVALID_ARG, "rows must be >= 0");
+  if (D < 1 || D > 256) return fail(ATTN_ERR_UNSUPPORTED, "D must be in [1, 256]");
+  if (out_dtype != ATTN_F32 && out_dtype != ATTN_BF16)
+    return fail(ATTN_ERR_INVALID_ARG, "out_dtype must be ATTN_F32 or ATTN_BF16");
+  if (rows == 0) return ATTN_OK;
+  if (!o_part || !m_part || !l_part || !row_split_start || !out)
+    return fail(ATTN_ERR_INVALID_ARG, "o_part, m_part, l_part, row_split_start and out are required");
+  hipError_t e = launch_merge(o_part, m_part, l_part, row_split_start, rows, D, out_dtype, out, lse,
+                              reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail_hip(e, "merge launch");
+  return ATTN_OK;
+}
+
+attn_status attn_util_copy(void *dst, const void *src, size_t bytes, attn_stream_t stream) {
+  if (bytes % 16 || (bytes && (!dst || !src || !aligned16(dst) || !aligned16(src))))
+    return fail(ATTN_ERR_INVALID_ARG, "copy: bytes % 16 == 0 and 16-byte aligned pointers required");
+  hipError_t e = launch_copy(dst, src, bytes, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : fail_hip(e, "copy launch");
+}
+
+attn_status attn_util_read(const void *src, size_t bytes, float *sink, attn_stream_t stream) {
+  if (bytes % 16 || (bytes && (!src || !sink || !aligned16(src))))
+    return fail(ATTN_ERR_INVALID_ARG, "read: bytes % 16 == 0, aligned src and a sink are required");
+  hipError_t e = launch_read(src, bytes, sink, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : fail_hip(e, "read launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,110 @@
+// Shared device/host definitions of the gfx950 decode-attention library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_decode.h"
+
+namespace lcdg {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- device helpers
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// ---------------------------------------------------------------- work-list
+
+// Device work-list shared by the decode kernels.  One "pair" is (b, kh);
+// pair p owns chunks [cum[p], cum[p+1]) of split_tokens token positions
+// each, times ngb query-head blocks of up to 16 heads.
+struct WorkList {
+  int32_t *counter;          // claimed-item counter (zeroed by the list pass)
+  int32_t *total_items;      // written by the list pass
+  int32_t *item_start;       // [npairs + 1] first item of each pair
+  int32_t *row_split_start;  // [B*QH + 1] first partial slot of each output row
+  int32_t *chunks;           // [npairs] chunks of each pair
+  float *m_part;             // [max partials] natural-log max
+  float *l_part;             // [max partials]
+  float *o_part;             // [max partials][D]
+};
+
+struct DecodeParams {
+  int32_t B, KH, G, D, QH, ngb;
+  const int32_t *seq_lens;
+  const int64_t *seq_offset;
+  int64_t stride_h, stride_t;
+  const void *q, *k, *v;
+  const float *k_scale;
+  int32_t k_part, k_scale_stride;
+  float v_scale;
+  const int32_t *token_idx, *n_idx;
+  int32_t idx_stride;
+  float softmax_scale;
+  int32_t split;        // tokens per chunk
+  int32_t max_seq_len;  // lengths are clamped to this bound
+  WorkList wl;
+};
+
+// Host-side launchers (each returns hipSuccess or the launch error).
+hipError_t launch_worklist(const DecodeParams &p, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeParams &p, int kv_dtype, int grid, hipStream_t s);
+hipError_t launch_decode_valu(const DecodeParams &p, int q_dtype, int kv_dtype, int grid, hipStream_t s);
+hipError_t launch_merge(const float *o_part, const float *m_part, const float *l_part, const int32_t *rss,
+                        int32_t rows, int32_t D, int32_t out_dtype, void *out, float *lse, hipStream_t s);
+hipError_t launch_quant_partitions(const attn_kv_geom &g, const void *x, int32_t part, int32_t scale_stride,
+                                   int8_t *codes, float *scales, hipStream_t s);
+hipError_t launch_quant_tensor(const attn_kv_geom &g, const void *x, int8_t *codes, float *scales,
+                               uint32_t *ws, hipStream_t s);
+hipError_t launch_value_lognorm(const attn_kv_geom &g, const void *v, float eps, float *vlog, int32_t stride,
+                                hipStream_t s);
+hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
+hipError_t launch_read(const void *src, size_t bytes, float *sink, hipStream_t s);
+
+struct OamPlan {
+  float *scores;        // [npairs][max_len]
+  uint32_t *hist;       // [3][npairs][2048]
+  int32_t *state;       // [npairs][4]: prefix, need, eq_take, pad
+  int32_t *chunk_cnt;   // [npairs][nchunk][2]
+  int32_t chunk;        // tokens per selection chunk
+  int32_t nchunk;       // chunks per pair
+};
+hipError_t launch_oam(const oam_topk_args &a, const OamPlan &plan, hipStream_t s);
+
+int device_cu_count();
+
+}  // namespace lcdg

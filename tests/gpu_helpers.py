@@ -1,0 +1,36 @@
+"""Device-side helpers for the GPU parity tests (data movement only)."""
+import math
+
+import numpy as np
+import torch
+
+import long_context_decode_gqa_amd as pkg
+import oracle
+import synth
+
+DEV = torch.device("cuda:0")
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    """Host array -> device tensor; uint16 arrays are bf16 bit patterns."""
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def dev_geom(g: synth.Geometry) -> pkg.KVGeometry:
+    return pkg.KVGeometry(g.B, g.KH, g.D, int(g.max_len) if g.B else 0, torch.from_numpy(g.lens).to(DEV),
+                          torch.from_numpy(g.seq_offset).to(DEV), g.stride_h, g.stride_t)
+
+
+def problem(w, q, k, v, g, **kw):
+    return oracle.Problem(w.B, w.KH, w.G, w.D, g.lens, g.seq_offset, g.stride_h, g.stride_t,
+                          np.ascontiguousarray(q), k, v, 1.0 / math.sqrt(w.D), **kw)
+
+
+def bf16_to_f32(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy()
+
+
+def log_case(msg: str):
+    print(f"[case] {msg}", flush=True)

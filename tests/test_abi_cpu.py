@@ -1,0 +1,133 @@
+"""The C ABI library loads, exports every declared entry point, and rejects bad
+arguments on the host before touching a GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_decode_gqa_amd as pkg
+from long_context_decode_gqa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_decode.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^(?:const\s+)?(?:attn_status|char|size_t|void|int32_t)\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_four_method_calls():
+    names = declared_functions()
+    for n in ("attn_decode_splitkv", "attn_merge_lse", "kv_quant_int8", "oam_score_topk"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.load()
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_status_strings():
+    L = _lib.load()
+    assert L.attn_status_string(0) == b"ok"
+    assert L.attn_status_string(3) == b"workspace too small"
+
+
+FAKE = 0x10000  # never dereferenced: validation fails or only sizes are computed
+
+
+def _args(**over):
+    a = _lib.AttnDecodeArgs()
+    a.kv = _lib.AttnKvGeom(2, 8, 128, 4096, FAKE, FAKE, 4096 * 128, 128)
+    a.G = 8
+    a.q_dtype = a.kv_dtype = _lib.ATTN_BF16
+    a.out_dtype = _lib.ATTN_F32
+    a.q = a.k = a.v = a.out = FAKE
+    for k, v in over.items():
+        if k.startswith("g_"):
+            setattr(a.kv, k[2:], v)
+        else:
+            setattr(a, k, v)
+    return a
+
+
+def _ws(a):
+    n = ctypes.c_size_t(0)
+    st = _lib.load().attn_decode_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size_counts_partials():
+    st, n = _ws(_args(split_tokens=1024))
+    assert st == 0
+    partials = 2 * 64 * 4   # B * QH * ceil(4096 / 1024)
+    assert n >= partials * (128 + 2) * 4
+    st2, n2 = _ws(_args(split_tokens=512))
+    assert st2 == 0 and n2 > n
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(G=0), _lib.ATTN_ERR_UNSUPPORTED),
+    (dict(G=65), _lib.ATTN_ERR_UNSUPPORTED),
+    (dict(g_D=96), _lib.ATTN_ERR_UNSUPPORTED),
+    (dict(g_KH=0), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(g_B=-1), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(g_stride_t=100), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(g_stride_t=132), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(q_dtype=_lib.ATTN_F32), _lib.ATTN_ERR_UNSUPPORTED),
+    (dict(kv_dtype=7), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(out_dtype=_lib.ATTN_I8), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(split_tokens=48), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(q=None), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(k=FAKE + 8), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(g_seq_lens=None), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(kv_dtype=_lib.ATTN_I8), _lib.ATTN_ERR_INVALID_ARG),          # no k_scale
+    (dict(kv_dtype=_lib.ATTN_I8, k_scale=FAKE, k_part_tokens=64, k_scale_stride=3), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(kv_dtype=_lib.ATTN_I8, k_scale=FAKE, k_part_tokens=40, k_scale_stride=64), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(token_idx=FAKE), _lib.ATTN_ERR_INVALID_ARG),                 # no n_idx
+    (dict(softmax_scale=float("inf")), _lib.ATTN_ERR_INVALID_ARG),
+])
+def test_invalid_arguments_are_rejected_on_the_host(over, status):
+    a = _args(**over)
+    st, _ = _ws(a)
+    assert st == status
+    # the enqueueing call fails the same way, before any HIP call
+    assert _lib.load().attn_decode_splitkv(ctypes.byref(a), None) == status
+    assert _lib.load().attn_last_error()
+
+
+def test_workspace_too_small_is_reported_before_launch():
+    a = _args(workspace=0x100000, workspace_bytes=1024)
+    assert _lib.load().attn_decode_splitkv(ctypes.byref(a), None) == _lib.ATTN_ERR_WORKSPACE_TOO_SMALL
+    a = _args(workspace=0x100010, workspace_bytes=1 << 30)
+    assert _lib.load().attn_decode_splitkv(ctypes.byref(a), None) == _lib.ATTN_ERR_INVALID_ARG  # misaligned
+
+
+def test_int8_and_fp32_paths_validate():
+    assert _ws(_args(kv_dtype=_lib.ATTN_I8, k_scale=FAKE, k_part_tokens=64, k_scale_stride=64))[0] == 0
+    a = _args(q_dtype=_lib.ATTN_F32, kv_dtype=_lib.ATTN_F32, g_D=64, g_stride_h=4096 * 64, g_stride_t=64)
+    assert _ws(a)[0] == 0
+    a = _args(q_dtype=_lib.ATTN_F32, kv_dtype=_lib.ATTN_F32, g_D=66, g_stride_h=4096 * 68, g_stride_t=68)
+    assert _ws(a)[0] == _lib.ATTN_ERR_UNSUPPORTED
+
+
+def test_merge_and_quant_validation():
+    L = _lib.load()
+    assert L.attn_merge_lse(None, None, None, None, 0, 128, 0, None, None, None) == 0
+    assert L.attn_merge_lse(FAKE, FAKE, FAKE, None, 4, 128, 0, FAKE, None, None) == _lib.ATTN_ERR_INVALID_ARG
+    assert L.attn_merge_lse(FAKE, FAKE, FAKE, FAKE, 4, 300, 0, FAKE, None, None) == _lib.ATTN_ERR_UNSUPPORTED
+    g = _lib.AttnKvGeom(2, 8, 128, 4096, FAKE, FAKE, 4096 * 128, 128)
+    assert L.kv_quant_int8(ctypes.byref(g), FAKE, 40, 200, FAKE, FAKE, None, 0, None) == _lib.ATTN_ERR_INVALID_ARG
+    assert L.kv_quant_int8(ctypes.byref(g), FAKE, 64, 10, FAKE, FAKE, None, 0, None) == _lib.ATTN_ERR_INVALID_ARG
+    assert L.kv_quant_int8(ctypes.byref(g), FAKE, 0, 1, FAKE, FAKE, None, 0, None) == \
+        _lib.ATTN_ERR_WORKSPACE_TOO_SMALL
+    n = ctypes.c_size_t(7)
+    assert L.kv_quant_int8_workspace_size(ctypes.byref(g), 0, ctypes.byref(n)) == 0 and n.value >= 4
