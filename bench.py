@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+Headline: bf16 GQA decode at 128K KV (B=4 sequences, 8 KV heads, G=8 query
+heads per KV head, head dim 128, 131072 tokens each, 1024-token split-KV
+chunks merged by log-sum-exp).  One step = one attn_decode_splitkv call
+(work-list pass + decode kernel + merge) over inputs already resident in HBM.
+Prints one JSON line: KV GB/s (value), us/step, fraction of HBM peak, the
+roofline of the decode kernel, the CPU oracle baseline and, unless
+--headline-only, the other workloads (32K GQA, ragged batch, INT8 KV, OAM).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, vendor figure
+METRIC = "decode-attention KV GB/s (% of MI355X HBM peak) + µs/step at 128K KV"
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_mfma_dense128k_pmc.txt")
+DECODE_SOURCE = os.path.join(ROOT, "long_context_decode_gqa_amd", "csrc", "decode_mfma.hip")
+
+
+# ------------------------------------------------------------------ byte/flop accounting
+
+def gqa_cache_elements(kv_heads: int, head_dim: int, seq_len: int) -> int:
+    """K plus V cache entries of one sequence (the GQA example's 2 x heads x dim x len)."""
+    return 2 * kv_heads * head_dim * seq_len
+
+
+def decode_eq_elements(DB: int, KH: int, G: int, Hsz: int, KVSL: int) -> int:
+    """Decode bytes at one byte per element: 2 x DB x KH x Hsz x (G + KVSL) (Q/O plus the KV cache)."""
+    return 2 * DB * KH * Hsz * (G + KVSL)
+
+
+def decode_eq_flops(DB: int, QH: int, KVSL: int, Hsz: int) -> int:
+    """Decode FLOPs: 4 x DB x QH x KVSL x Hsz."""
+    return 4 * DB * QH * KVSL * Hsz
+
+
+def kv_bytes(total_tokens: int, KH: int, D: int, elem_bytes: int) -> int:
+    """Bytes of K plus V streamed for `total_tokens` cached tokens of every KV head."""
+    return 2 * total_tokens * KH * D * elem_bytes
+
+
+def partial_bytes(n_partials: int, D: int) -> int:
+    """Split-KV partial triples written by the decode kernel: o (D floats), m and l."""
+    return n_partials * (D + 2) * 4
+
+
+# ------------------------------------------------------------------ helpers
+
+def host_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def file_sha256(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_pmc_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; None otherwise."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    kv = {}
+    for line in open(PMC_SUMMARY):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            kv[key.strip()] = val.strip()
+    if kv.get("kernel_source_sha256") != file_sha256(DECODE_SOURCE):
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+class Timer:
+    """HIP events around K steps on the current stream, plus per-phase events."""
+
+    def __init__(self, torch, steps):
+        self.torch = torch
+        self.start = torch.cuda.Event(enable_timing=True)
+        self.end = torch.cuda.Event(enable_timing=True)
+        self.phase = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        for evs in self.phase:          # materialise the events so their handles exist
+            for e in evs:
+                e.record()
+        torch.cuda.synchronize()
+
+
+def to_dev(torch, a, dev):
+    import numpy as np
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def dev_geom(pkg, torch, g, dev):
+    return pkg.KVGeometry(g.B, g.KH, g.D, int(g.max_len), torch.from_numpy(g.lens).to(dev),
+                          torch.from_numpy(g.seq_offset).to(dev), g.stride_h, g.stride_t)
+
+
+def time_decode(torch, prepared, steps, warmup):
+    """Returns (ms per step, mean decode-kernel ms, mean merge ms, mean work-list ms)."""
+    for _ in range(warmup):
+        prepared()
+    t = Timer(torch, steps)
+    torch.cuda.synchronize()
+    t.start.record()
+    for i in range(steps):
+        prepared.profiled(t.phase[i])
+    t.end.record()
+    torch.cuda.synchronize()
+    total = t.start.elapsed_time(t.end)
+    wl = sum(e[0].elapsed_time(e[1]) for e in t.phase) / steps
+    dk = sum(e[1].elapsed_time(e[2]) for e in t.phase) / steps
+    mg = sum(e[2].elapsed_time(e[3]) for e in t.phase) / steps
+    return total / steps, dk, mg, wl
+
+
+# ------------------------------------------------------------------ workloads
+
+def bench_dense(pkg, torch, synth, name, steps, warmup, dev, **over):
+    w = synth.workload(name, **over)
+    q, k, v, g = synth.generate(w, nthreads=host_threads())
+    qd = to_dev(torch, q.reshape(-1), dev).view(w.B, w.QH, w.D)
+    kd, vd = to_dev(torch, k, dev), to_dev(torch, v, dev)
+    del k, v
+    geom = dev_geom(pkg, torch, g, dev)
+    p = pkg.prepare_decode(qd, kd, vd, geom, w.G, split_tokens=w.split_tokens)
+    ms, dk, mg, wl = time_decode(torch, p, steps, warmup)
+    tokens = w.kv_tokens()
+    kvb = kv_bytes(tokens, w.KH, w.D, 2)
+    nparts = w.QH * sum(-(-int(L) // w.split_tokens) for L in w.lens)
+    algo = kvb + w.B * w.QH * w.D * 2 + partial_bytes(nparts, w.D)
+    return dict(w=w, q=q, g=g, ms=ms, decode_ms=dk, merge_ms=mg, worklist_ms=wl, kv_bytes=kvb,
+                decode_algo_bytes=algo, tokens=tokens)
+
+
+def summary(r, extra=None):
+    d = {"us_per_step": round(r["ms"] * 1e3, 2), "kv_gbs": round(r["kv_bytes"] / r["ms"] / 1e6, 1),
+         "frac_of_peak": round(r["kv_bytes"] / r["ms"] / 1e6 / HBM_PEAK_GBS, 4),
+         "decode_kernel_us": round(r["decode_ms"] * 1e3, 2), "merge_us": round(r["merge_ms"] * 1e3, 2),
+         "worklist_us": round(r["worklist_ms"] * 1e3, 2)}
+    if extra:
+        d.update(extra)
+    return d
+
+
+def bench_int8(pkg, torch, synth, steps, warmup, dev):
+    w = synth.workload("int8_128k")
+    q, k, v, g = synth.generate(w, nthreads=host_threads())
+    geom = dev_geom(pkg, torch, g, dev)
+    kd, vd = to_dev(torch, k, dev), to_dev(torch, v, dev)
+    del k, v
+    kc, ks = pkg.kv_quant_int8(kd, geom, 64)
+    vc, vs = pkg.kv_quant_int8(vd, geom, 0)
+    torch.cuda.synchronize()
+    del kd, vd
+    qd = to_dev(torch, q.reshape(-1), dev).view(w.B, w.QH, w.D)
+    p = pkg.prepare_decode(qd, kc, vc, geom, w.G, k_scale=ks, k_part_tokens=64, v_scale=float(vs.item()),
+                           split_tokens=w.split_tokens)
+    ms, dk, mg, wl = time_decode(torch, p, steps, warmup)
+    tokens = w.kv_tokens()
+    kvb = kv_bytes(tokens, w.KH, w.D, 1) + ks.numel() * 4 + 4
+    return dict(ms=ms, decode_ms=dk, merge_ms=mg, worklist_ms=wl, kv_bytes=kvb)
+
+
+def cpu_baseline(r, budget_s=10.0):
+    """The fp64 oracle on host threads over whole (b, kh) pairs of the headline workload."""
+    import numpy as np
+
+    import oracle
+    w, q, g = r["w"], r["q"], r["g"]
+    import synth
+    k = synth.fill(w.seed, synth.T_K, g, nthreads=host_threads())
+    v = synth.fill(w.seed, synth.T_V, g, nthreads=host_threads())
+    p = oracle.Problem(w.B, w.KH, w.G, w.D, g.lens, g.seq_offset, g.stride_h, g.stride_t, np.ascontiguousarray(q),
+                       k, v, 1.0 / math.sqrt(w.D))
+    n = host_threads()
+    pairs = [(b, kh) for b in range(w.B) for kh in range(w.KH)]
+    per_batch = max(1, n // w.G)
+    done = 0
+    t0 = time.perf_counter()
+    while done < len(pairs) and time.perf_counter() - t0 < budget_s:
+        batch = pairs[done:done + per_batch]
+        rows = [(b, kh * w.G + gq) for b, kh in batch for gq in range(w.G)]
+        oracle.attention_rows(p, rows, nthreads=n)
+        done += len(batch)
+    dt = time.perf_counter() - t0
+    bytes_done = kv_bytes(int(w.lens[0]) * done, 1, w.D, 2)
+    return {"value": round(bytes_done / dt / 1e9, 3), "unit": "GB/s", "cores": n, "kind": "oracle",
+            "seconds": round(dt, 2), "us_per_step_equiv": round(dt / done * len(pairs) * 1e6, 1),
+            "sample": f"{done} of {len(pairs)} (sequence, KV head) pairs of the 128K bf16 workload, "
+                      f"all {w.G} query heads each, fp64 oracle on {n} host threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--headline-only", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run the library's plain copy kernel over this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU sharding is described in DESIGN.md but not built", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import long_context_decode_gqa_amd as pkg
+    import synth
+    if not os.path.exists(pkg._lib.LIB_PATH):
+        from long_context_decode_gqa_amd.build import build
+        build()
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    K, W = args.steps, args.warmup
+    if args.calibrate_copy_mib:
+        nbytes = args.calibrate_copy_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(W + K):
+            pkg.util_copy(dst, src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": W + K}), flush=True)
+        return
+
+    head = bench_dense(pkg, torch, synth, "dense128k", K, W, dev)
+    w = head["w"]
+    ms = head["ms"]
+    value = head["kv_bytes"] / ms / 1e6          # GB/s (1e9 bytes per second)
+    dk_s = head["decode_ms"] / 1e3
+    achieved = head["decode_algo_bytes"] / dk_s / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_pmc_traffic(),
+                "kernel": "decode_mfma_kernel<128, bf16>",
+                "algorithmic_bytes_per_launch": head["decode_algo_bytes"],
+                "avg_launch_us": round(head["decode_ms"] * 1e3, 2)}
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms, 4), "us_per_step": round(ms * 1e3, 2), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "config": {"workload": "gqa_decode_bf16_128k", "batch": w.B, "kv_heads": w.KH, "group_size": w.G,
+                   "head_dim": w.D, "kv_len": int(w.lens[0]), "split_tokens": w.split_tokens,
+                   "kv_bytes_per_step": head["kv_bytes"],
+                   "eq6_bytes_per_step": decode_eq_elements(w.B, w.KH, w.G, w.D, int(w.lens[0])) * 2,
+                   "flops_per_step": decode_eq_flops(w.B, w.QH, int(w.lens[0]), w.D)},
+        "phases_us": {"worklist": round(head["worklist_ms"] * 1e3, 2), "decode": round(head["decode_ms"] * 1e3, 2),
+                      "merge": round(head["merge_ms"] * 1e3, 2)},
+        "roofline": roofline,
+    }
+    if not args.headline_only:
+        others = {}
+        r = bench_dense(pkg, torch, synth, "gqa32k", max(5, K // 2), W, dev)
+        others["gqa32k_bf16"] = summary(r)
+        del r
+        r = bench_dense(pkg, torch, synth, "ragged", max(5, K // 2), W, dev, split_tokens=512)
+        others["ragged_bf16"] = summary(r, {"total_kv_tokens_per_head": r["tokens"],
+                                             "lens_min": int(r["w"].lens.min()), "lens_max": int(r["w"].lens.max())})
+        del r
+        try:
+            r = bench_int8(pkg, torch, synth, max(5, K // 2), W, dev)
+            others["int8_128k"] = summary(r)
+        except pkg.AttnError as e:
+            others["int8_128k"] = {"error": str(e)}
+        line["other_workloads"] = others
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(head)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

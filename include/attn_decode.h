@@ -153,6 +153,14 @@ attn_status attn_decode_workspace_size(const attn_decode_args *args, size_t *byt
 attn_status attn_decode_splitkv(const attn_decode_args *args, attn_stream_t stream);
 
 /*
+ * attn_decode_splitkv plus timing marks: events[0..3] (hipEvent_t created by
+ * the caller, any may be NULL) are recorded on `stream` before the work-list
+ * pass, before the decode kernel, before the merge and after the merge, so
+ * the caller can read each phase's duration.  Same arguments and errors.
+ */
+attn_status attn_decode_splitkv_profiled(const attn_decode_args *args, attn_stream_t stream, void *const events[4]);
+
+/*
  * Log-sum-exp merge of partial triples ("优化稀疏注意力中的令牌丢弃机制" §5,
  * cross-shard online softmax; read with the chunk term weighted by
  * exp(m_chunk - m_new), which makes the result independent of the split).

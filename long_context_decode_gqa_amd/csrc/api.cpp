@@ -62,7 +62,7 @@ attn_status check_geom(const attn_kv_geom &g, int es, bool need_ptrs) {
 }
 
 struct DecodeLayout {
-  size_t hdr, item_start, rss, chunks, m, l, o, total;
+  size_t hdr, tile_start, rss, m, l, o, total;
   int64_t max_partials;
   int32_t split, ngb, max_tokens;
   bool mfma;
@@ -111,20 +111,23 @@ attn_status plan_decode(const attn_decode_args *a, DecodeLayout *L) {
   }
   L->mfma = mfma;
   L->split = a->split_tokens ? a->split_tokens : (mfma ? 1024 : 256);
+  if (mfma && ((int64_t)g.max_seq_len + 64) * g.stride_t * elem_size(a->kv_dtype) >= (int64_t(1) << 31))
+    return fail(ATTN_ERR_UNSUPPORTED, "one (sequence, KV head) may span at most 2 GiB of rows");
+  if (mfma && a->token_idx && L->split > 1024)
+    return fail(ATTN_ERR_UNSUPPORTED, "with token_idx, split_tokens must be <= 1024");
   L->ngb = (a->G + 15) / 16;
   L->max_tokens = a->token_idx ? a->idx_stride : g.max_seq_len;
   const int64_t max_chunks = ((int64_t)L->max_tokens + L->split - 1) / L->split;
   const int64_t QH = (int64_t)g.KH * a->G;
-  L->max_partials = (int64_t)g.B * QH * max_chunks;
-  const int64_t max_items = (int64_t)g.B * g.KH * max_chunks * L->ngb;
-  if (L->max_partials >= (int64_t(1) << 31) || max_items >= (int64_t(1) << 31))
+  L->max_partials = 2 * (int64_t)g.B * QH * max_chunks;
+  const int64_t nlanes = (int64_t)g.B * g.KH * L->ngb;
+  const int64_t max_tiles = nlanes * (((int64_t)L->max_tokens + 31) / 32);
+  if (L->max_partials >= (int64_t(1) << 31) || max_tiles >= (int64_t(1) << 31))
     return fail(ATTN_ERR_UNSUPPORTED, "too many split-KV partials (reduce max_seq_len or raise split_tokens)");
-  const int64_t npairs = (int64_t)g.B * g.KH;
   size_t off = 0;
   L->hdr = off; off = align256(off + 64 * sizeof(int32_t));
-  L->item_start = off; off = align256(off + (npairs + 1) * sizeof(int32_t));
+  L->tile_start = off; off = align256(off + (nlanes + 1) * sizeof(int32_t));
   L->rss = off; off = align256(off + ((int64_t)g.B * QH + 1) * sizeof(int32_t));
-  L->chunks = off; off = align256(off + npairs * sizeof(int32_t));
   L->m = off; off = align256(off + L->max_partials * sizeof(float));
   L->l = off; off = align256(off + L->max_partials * sizeof(float));
   L->o = off; off = align256(off + (size_t)L->max_partials * g.D * sizeof(float));
@@ -166,7 +169,7 @@ attn_status attn_decode_workspace_size(const attn_decode_args *args, size_t *byt
   return ATTN_OK;
 }
 
-attn_status attn_decode_splitkv(const attn_decode_args *a, attn_stream_t stream) {
+static attn_status decode_impl(const attn_decode_args *a, attn_stream_t stream, void *const *events) {
   DecodeLayout L;
   attn_status st = plan_decode(a, &L);
   if (st != ATTN_OK) return st;
@@ -200,30 +203,48 @@ attn_status attn_decode_splitkv(const attn_decode_args *a, attn_stream_t stream)
   p.softmax_scale = a->softmax_scale != 0.f ? a->softmax_scale : 1.0f / sqrtf((float)a->kv.D);
   p.split = L.split;
   p.max_seq_len = a->kv.max_seq_len;
-  p.wl.counter = reinterpret_cast<int32_t *>(ws + L.hdr);
-  p.wl.total_items = reinterpret_cast<int32_t *>(ws + L.hdr) + 1;
-  p.wl.item_start = reinterpret_cast<int32_t *>(ws + L.item_start);
+  p.wl.hdr = reinterpret_cast<int32_t *>(ws + L.hdr);
+  p.wl.tile_start = reinterpret_cast<int32_t *>(ws + L.tile_start);
   p.wl.row_split_start = reinterpret_cast<int32_t *>(ws + L.rss);
-  p.wl.chunks = reinterpret_cast<int32_t *>(ws + L.chunks);
+  {
+    // persistent grid: two workgroups of four waves per compute unit (the MFMA
+    // kernel's register budget), capped by the largest possible tile count
+    const int cus = device_cu_count();
+    const int64_t max_tiles = (int64_t)p.B * p.KH * L.ngb * (((int64_t)L.max_tokens + 31) / 32);
+    int64_t grid = (int64_t)cus * (L.mfma ? 2 : 4);
+    if (grid > max_tiles) grid = max_tiles;
+    p.grid = (int)(grid < 1 ? 1 : grid);
+  }
   p.wl.m_part = reinterpret_cast<float *>(ws + L.m);
   p.wl.l_part = reinterpret_cast<float *>(ws + L.l);
   p.wl.o_part = reinterpret_cast<float *>(ws + L.o);
 
-  hipError_t e = launch_worklist(p, s);
+  auto mark = [&](int i) -> hipError_t {
+    if (events && events[i]) return hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s);
+    return hipSuccess;
+  };
+  hipError_t e = mark(0);
+  if (e != hipSuccess) return fail_hip(e, "event record");
+  e = launch_worklist(p, s);
   if (e != hipSuccess) return fail_hip(e, "work-list launch");
-  const int64_t max_chunks = ((int64_t)L.max_tokens + L.split - 1) / L.split;
-  const int64_t max_items = (int64_t)p.B * p.KH * max_chunks * L.ngb;
-  const int cus = device_cu_count();
-  int64_t grid = (int64_t)cus * (L.mfma ? 2 : 4);
-  if (grid > max_items) grid = max_items;
-  if (grid < 1) grid = 1;
-  if (L.mfma) e = launch_decode_mfma(p, a->kv_dtype, (int)grid, s);
-  else e = launch_decode_valu(p, a->q_dtype, a->kv_dtype, (int)grid, s);
+  if ((e = mark(1)) != hipSuccess) return fail_hip(e, "event record");
+  if (L.mfma) e = launch_decode_mfma(p, a->kv_dtype, s);
+  else e = launch_decode_valu(p, a->q_dtype, a->kv_dtype, s);
   if (e != hipSuccess) return fail_hip(e, "decode launch");
+  if ((e = mark(2)) != hipSuccess) return fail_hip(e, "event record");
   e = launch_merge(p.wl.o_part, p.wl.m_part, p.wl.l_part, p.wl.row_split_start, p.B * p.QH, p.D, a->out_dtype,
                    a->out, a->lse, s);
   if (e != hipSuccess) return fail_hip(e, "merge launch");
+  if ((e = mark(3)) != hipSuccess) return fail_hip(e, "event record");
   return ATTN_OK;
+}
+
+attn_status attn_decode_splitkv(const attn_decode_args *a, attn_stream_t stream) {
+  return decode_impl(a, stream, nullptr);
+}
+
+attn_status attn_decode_splitkv_profiled(const attn_decode_args *a, attn_stream_t stream, void *const events[4]) {
+  return decode_impl(a, stream, events);
 }
 
 attn_status attn_merge_lse(const float *o_part, const float *m_part, const float *l_part,

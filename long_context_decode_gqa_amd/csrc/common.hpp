@@ -49,15 +49,21 @@ __device__ __forceinline__ int wave_sum_int(int v) {
 
 // ---------------------------------------------------------------- work-list
 
-// Device work-list shared by the decode kernels.  One "pair" is (b, kh);
-// pair p owns chunks [cum[p], cum[p+1]) of split_tokens token positions
-// each, times ngb query-head blocks of up to 16 heads.
+// Device work-list shared by the decode kernels.
+//
+// A "lane" is (b, kh, query-head block of up to 16 heads); lane q covers
+// ceil(n_q / 32) tiles of 32 token positions, and all lanes' tiles are laid
+// end to end (lane q starts at tile_start[q]).  The decode grid splits this
+// tile stream into equal contiguous ranges, one per workgroup, so every
+// workgroup streams the same number of K/V bytes whatever the length mix.
+// Each lane is also cut into chunks of split_tokens positions; a chunk owns
+// two partial slots because at most one range boundary can fall inside it
+// (ranges are at least one chunk long).  Slot 2j is the part of chunk j
+// before that boundary (or all of it), slot 2j+1 the part after (or empty).
 struct WorkList {
-  int32_t *counter;          // claimed-item counter (zeroed by the list pass)
-  int32_t *total_items;      // written by the list pass
-  int32_t *item_start;       // [npairs + 1] first item of each pair
+  int32_t *hdr;              // [0] tiles in total, [1] workgroups in use
+  int32_t *tile_start;       // [nlanes + 1]
   int32_t *row_split_start;  // [B*QH + 1] first partial slot of each output row
-  int32_t *chunks;           // [npairs] chunks of each pair
   float *m_part;             // [max partials] natural-log max
   float *l_part;             // [max partials]
   float *o_part;             // [max partials][D]
@@ -75,15 +81,16 @@ struct DecodeParams {
   const int32_t *token_idx, *n_idx;
   int32_t idx_stride;
   float softmax_scale;
-  int32_t split;        // tokens per chunk
+  int32_t split;        // tokens per chunk (multiple of 32)
   int32_t max_seq_len;  // lengths are clamped to this bound
+  int32_t grid;         // workgroups launched for the decode kernel
   WorkList wl;
 };
 
 // Host-side launchers (each returns hipSuccess or the launch error).
 hipError_t launch_worklist(const DecodeParams &p, hipStream_t s);
-hipError_t launch_decode_mfma(const DecodeParams &p, int kv_dtype, int grid, hipStream_t s);
-hipError_t launch_decode_valu(const DecodeParams &p, int q_dtype, int kv_dtype, int grid, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeParams &p, int kv_dtype, hipStream_t s);
+hipError_t launch_decode_valu(const DecodeParams &p, int q_dtype, int kv_dtype, hipStream_t s);
 hipError_t launch_merge(const float *o_part, const float *m_part, const float *l_part, const int32_t *rss,
                         int32_t rows, int32_t D, int32_t out_dtype, void *out, float *lse, hipStream_t s);
 hipError_t launch_quant_partitions(const attn_kv_geom &g, const void *x, int32_t part, int32_t scale_stride,

@@ -67,18 +67,25 @@ __device__ __forceinline__ uint32_t codes_to_f16x2(uint32_t pair_lo16_hi16) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-template <int D, int KVT>
+// Registers of one 32-token tile: K in the MFMA operand layout, V as natural
+// per-lane row pieces, and (int8) the K scales of the lane's scores.
+template <int D, int KVT, bool IDX>
 struct Tile {
   static constexpr int ES = (KVT == ATTN_BF16) ? 2 : 1;
   static constexpr int KL = (KVT == ATTN_BF16) ? D / 32 : D / 64;  // 16-byte K loads per token block
   static constexpr int VW = (D / 16) * ES / 4;                      // V words per token per lane
+  static constexpr int NS = (KVT == ATTN_I8) ? (IDX ? 8 : 2) : 0;   // K scales per lane
   u32x4_t k[2][KL];
   typename VecW<VW>::T v[8];
+  float ks[NS > 0 ? NS : 1];
 };
 
-template <int D, int KVT>
+// Tokens per chunk of the indexed variant (its index list is staged in LDS).
+constexpr int kMaxIdxChunk = 1024;
+
+template <int D, int KVT, bool IDX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_mfma_kernel(DecodeParams p) {
-  typedef Tile<D, KVT> TileT;
+  typedef Tile<D, KVT, IDX> TileT;
   constexpr int NB = D / 16;
   constexpr int KB = D / 32;
   constexpr int ES = TileT::ES;
@@ -87,103 +94,127 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   typedef typename VecW<VW>::T VV;
   typedef typename std::conditional<KVT == ATTN_BF16, bf16x8_t, f16x8_t>::type OpT;
 
-  __shared__ int s_info[2];
+  __shared__ int s_idx[IDX ? kMaxIdxChunk : 1];
+  // Q^T operand of the current run: 16 query heads x D channels (bf16, or
+  // fp16 for int8 KV), rows padded by 16 bytes against bank conflicts.
+  constexpr int kQRow = D * 2 + 16;
+  __shared__ __attribute__((aligned(16))) unsigned char s_q[16 * kQRow];
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
   __shared__ float s_o[kWaves][16][D + 4];
+  __shared__ int s_slot[16];  // first partial slot of each query head of the run
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, cg = lane >> 4;
-  const int npairs = p.B * p.KH;
   const float c1 = p.softmax_scale * kLog2e;
   const float NEG_INF = -__builtin_huge_valf();
 
-  for (;;) {
-    if (tid == 0) {
-      const int item = atomicAdd(p.wl.counter, 1);
-      int pair = -1, rel = 0;
-      if (item < *p.wl.total_items) {
-        int lo = 0, hi = npairs - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (p.wl.item_start[mid] <= item) lo = mid; else hi = mid - 1;
-        }
-        pair = lo;
-        rel = item - p.wl.item_start[lo];
-      }
-      s_info[0] = pair;
-      s_info[1] = rel;
-    }
-    __syncthreads();
-    const int pair = s_info[0];
-    const int rel = s_info[1];
-    if (pair < 0) break;
+  // This workgroup's contiguous share of the tile stream.
+  const int nwg = p.wl.hdr[1];
+  if ((int)blockIdx.x >= nwg) return;
+  const int T = p.wl.hdr[0];
+  const int t_begin = (int)((int64_t)blockIdx.x * T / nwg);
+  const int t_end = (int)((int64_t)(blockIdx.x + 1) * T / nwg);
+  const int nlanes = p.B * p.KH * p.ngb;
+  const int ct = p.split / kTile;  // tiles per chunk
 
-    const int b = pair / p.KH, kh = pair - b * p.KH;
-    const int gb = rel % p.ngb, chunk = rel / p.ngb;
-    const int L = p.seq_lens[b];
-    int npos = L;
-    const int *idxp = nullptr;
-    if (p.token_idx) {
-      npos = L > 0 ? min(max(p.n_idx[pair], 0), p.idx_stride) : 0;
-      idxp = p.token_idx + (int64_t)pair * p.idx_stride;
+  for (int t = t_begin; t < t_end;) {
+    // the lane (b, kh, query-head block) that owns tile t
+    int lo = 0, hi = nlanes - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.wl.tile_start[mid] <= t) lo = mid; else hi = mid - 1;
     }
-    const int pos0 = chunk * p.split;
-    const int pos1 = min(npos, pos0 + p.split);
-    const int ntile = (pos1 - pos0 + kTile - 1) / kTile;
+    const int q = lo;
+    const int lane_t0 = p.wl.tile_start[q], lane_t1 = p.wl.tile_start[q + 1];
+    const int run_end = min(t_end, lane_t1);
+    const int pair = q / p.ngb, gb = q - pair * p.ngb;
+    const int b = pair / p.KH, kh = pair - b * p.KH;
+    const int L = min(max(p.seq_lens[b], 0), p.max_seq_len);
+    int npos = L;
+    if constexpr (IDX) npos = L > 0 ? min(max(p.n_idx[pair], 0), p.idx_stride) : 0;
     const int g0 = gb * 16;
     const int gcount = min(16, p.G - g0);
     const bool qvalid = col < gcount;
 
+    // Buffer resources over this (b, kh)'s rows: 32-bit offsets, and rows at
+    // or past L read as zero (their scores are masked), so no clamping.
     const int64_t head_off = p.seq_offset[b] + (int64_t)kh * p.stride_h;
     const char *kbase = (const char *)p.k + head_off * ES;
     const char *vbase = (const char *)p.v + head_off * ES;
-    const int64_t rstride = p.stride_t * ES;
+    const uint32_t rs = (uint32_t)(p.stride_t * ES);
+    const int nrec = L > 0 ? (int)((uint32_t)(L - 1) * rs + D * ES) : 0;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)kbase, (short)0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vbase, (short)0, nrec, 0x00020000);
+    const float *kscale = (KVT == ATTN_I8) ? p.k_scale + (int64_t)pair * p.k_scale_stride : nullptr;
 
-    // Q^T operand (B): column col = query head g0 + col, channels in K's order.
-    OpT qop[KB];
-    {
-      const uint16_t *qrow = (const uint16_t *)p.q +
-                             ((int64_t)b * p.QH + (int64_t)kh * p.G + g0 + (qvalid ? col : 0)) * D;
+    // Stage Q (16 heads of this block, zero past G) in LDS, in MFMA operand
+    // type; each tile reads its B operand from there instead of holding it in
+    // registers for the whole run.
+    __syncthreads();
+    for (int e = tid; e < 16 * (D / 8); e += 256) {
+      const int g = e / (D / 8), c8 = e - g * (D / 8);
+      u32x4_t w = (u32x4_t){0u, 0u, 0u, 0u};
+      if (g < gcount) w = *(const u32x4_t *)((const uint16_t *)p.q + ((int64_t)b * p.QH + (int64_t)kh * p.G + g0 + g) * D + 8 * c8);
+      if constexpr (KVT == ATTN_I8) {
+        f16x8_t h;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int d0 = (KVT == ATTN_BF16) ? 8 * (4 * kb + cg) : 64 * (kb >> 1) + 16 * cg + 8 * (kb & 1);
-        u32x4_t w = *(const u32x4_t *)(qrow + d0);
-        if (!qvalid) w = (u32x4_t){0u, 0u, 0u, 0u};
-        if constexpr (KVT == ATTN_BF16) {
-          qop[kb] = __builtin_bit_cast(bf16x8_t, w);
-        } else {
-          f16x8_t h;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            h[2 * e] = (_Float16)bf16_lo(w[e]);
-            h[2 * e + 1] = (_Float16)bf16_hi(w[e]);
-          }
-          qop[kb] = h;
+        for (int x = 0; x < 4; ++x) {
+          h[2 * x] = (_Float16)bf16_lo(w[x]);
+          h[2 * x + 1] = (_Float16)bf16_hi(w[x]);
         }
+        w = __builtin_bit_cast(u32x4_t, h);
       }
+      *(u32x4_t *)(s_q + g * kQRow + 16 * c8) = w;
     }
+    // (global loads inside the segment loop would make the compiler wait for
+    // every load in flight, the tile prefetch included, so stage these too)
+    if (tid < gcount) s_slot[tid] = p.wl.row_split_start[b * p.QH + kh * p.G + g0 + tid];
+    __syncthreads();
+    // operand of k-block kb: channels d0 .. d0+7 of query head `col`
+    auto q_operand = [&](int kb) -> OpT {
+      const int d0 = (KVT == ATTN_BF16) ? 8 * (4 * kb + cg) : 64 * (kb >> 1) + 16 * cg + 8 * (kb & 1);
+      return __builtin_bit_cast(OpT, *(const u32x4_t *)(s_q + col * kQRow + 2 * d0));
+    };
 
+    // Positions of the current segment (IDX: its staged index list starts at seg_pos0).
+    int seg_pos0 = 0, seg_pos1 = 0;
     auto row_of = [&](int pos) -> int {
-      pos = min(pos, pos1 - 1);
-      if (idxp) return min(max(idxp[pos], 0), L - 1);
+      if constexpr (IDX) return s_idx[min(pos, seg_pos1 - 1) - seg_pos0];
       return pos;
     };
 
-    auto load_tile = [&](TileT &R, int tile) {
-      const int tpos = pos0 + tile * kTile;
+    // Issue one tile's loads.  Every path through the loops issues the same
+    // number of loads, so the compiler's wait counts never drain the tile in
+    // flight; a tile that is not needed gets an out-of-range offset, which
+    // the buffer unit answers with zeros and no memory traffic.
+    auto load_tile = [&](TileT &R, int tile, bool valid) {
+      const int tpos = (tile - lane_t0) * kTile;
+      const uint32_t oob = valid ? 0u : 0x80000000u;
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
-        const char *row = kbase + (int64_t)row_of(tpos + 16 * tb + col) * rstride;
+        const uint32_t off = ((uint32_t)row_of(tpos + 16 * tb + col) * rs + 16 * cg) | oob;
 #pragma unroll
-        for (int kl = 0; kl < KL; ++kl) R.k[tb][kl] = *(const u32x4_t *)(row + 16 * (4 * kl + cg));
+        for (int kl = 0; kl < KL; ++kl) R.k[tb][kl] = __builtin_amdgcn_raw_buffer_load_b128(krs, off + 64 * kl, 0, 0);
       }
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const int slot = (jj < 4) ? (4 * cg + jj) : (16 + 4 * cg + jj - 4);
-        const char *row = vbase + (int64_t)row_of(tpos + slot) * rstride;
-        R.v[jj] = *(const VV *)(row + col * VW * 4);
+        const uint32_t off = ((uint32_t)row_of(tpos + slot) * rs + col * VW * 4) | oob;
+        if constexpr (VW == 4) R.v[jj] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
+        else if constexpr (VW == 2) R.v[jj] = __builtin_amdgcn_raw_buffer_load_b64(vrs, off, 0, 0);
+        else R.v[jj] = __builtin_amdgcn_raw_buffer_load_b32(vrs, off, 0, 0);
+      }
+      if constexpr (KVT == ATTN_I8) {
+        const int last = max(npos - 1, 0);
+        if constexpr (IDX) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) R.ks[i] = kscale[row_of(tpos + 16 * (i >> 2) + 4 * cg + (i & 3)) / p.k_part];
+        } else {
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) R.ks[tb] = kscale[min(tpos + 16 * tb, last) / p.k_part];
+        }
       }
     };
 
@@ -193,7 +224,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     float m_run = NEG_INF, l_run = 0.f;
 
     auto compute_tile = [&](const TileT &R, int tile) {
-      const int tpos = pos0 + tile * kTile;
+      const int tpos = (tile - lane_t0) * kTile;
       float s[8];
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
@@ -201,8 +232,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           if constexpr (KVT == ATTN_BF16) {
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, R.k[tb][kb]), qop[kb], acc,
-                                                          0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, R.k[tb][kb]), q_operand(kb),
+                                                          acc, 0, 0, 0);
           } else {
             const u32x4_t w = R.k[tb][kb >> 1];
             const uint32_t c0 = w[2 * (kb & 1)], c1w = w[2 * (kb & 1) + 1];
@@ -211,24 +242,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             hw[1] = codes_to_f16x2(((c0 >> 16) & 0xFFu) | ((c0 >> 8) & 0xFF0000u));
             hw[2] = codes_to_f16x2((c1w & 0xFFu) | ((c1w & 0xFF00u) << 8));
             hw[3] = codes_to_f16x2(((c1w >> 16) & 0xFFu) | ((c1w >> 8) & 0xFF0000u));
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, hw), qop[kb], acc, 0, 0, 0);
-          }
-        }
-        float scale_tb = c1;
-        if constexpr (KVT == ATTN_I8) {
-          if (!idxp) {
-            const int t = tpos + 16 * tb;
-            scale_tb *= p.k_scale[(int64_t)pair * p.k_scale_stride + t / p.k_part];
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, hw), q_operand(kb), acc, 0, 0, 0);
           }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int pos = tpos + 16 * tb + 4 * cg + i;
-          float sc = scale_tb;
-          if constexpr (KVT == ATTN_I8) {
-            if (idxp) sc *= p.k_scale[(int64_t)pair * p.k_scale_stride + row_of(pos) / p.k_part];
-          }
-          s[4 * tb + i] = (pos < pos1) ? acc[i] * sc : NEG_INF;
+          float sc = c1;
+          if constexpr (KVT == ATTN_I8) sc *= IDX ? R.ks[4 * tb + i] : R.ks[tb];
+          s[4 * tb + i] = (pos < seg_pos1) ? acc[i] * sc : NEG_INF;
         }
       }
       float mt = s[0];
@@ -269,18 +291,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if constexpr (KVT == ATTN_BF16) {
           const int w = nb >> 1;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t x = word_of<VW>(R.v[2 * q], w), y = word_of<VW>(R.v[2 * q + 1], w);
-            a[q] = (nb & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
+          for (int qq = 0; qq < 4; ++qq) {
+            const uint32_t x = word_of<VW>(R.v[2 * qq], w), y = word_of<VW>(R.v[2 * qq + 1], w);
+            a[qq] = (nb & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
           }
           O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), phi, O[nb], 0, 0, 0);
           O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), plo, O[nb], 0, 0, 0);
         } else {
           const int w = nb >> 2, sh = 8 * (nb & 3);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t x = word_of<VW>(R.v[2 * q], w), y = word_of<VW>(R.v[2 * q + 1], w);
-            a[q] = codes_to_f16x2(((x >> sh) & 0xFFu) | (((y >> sh) & 0xFFu) << 16));
+          for (int qq = 0; qq < 4; ++qq) {
+            const uint32_t x = word_of<VW>(R.v[2 * qq], w), y = word_of<VW>(R.v[2 * qq + 1], w);
+            a[qq] = codes_to_f16x2(((x >> sh) & 0xFFu) | (((y >> sh) & 0xFFu) << 16));
           }
           O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), phi, O[nb], 0, 0, 0);
           O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), plo, O[nb], 0, 0, 0);
@@ -288,71 +310,116 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     };
 
-    // Wave w handles tiles w, w+4, ...; two register buffers alternate.
-    {
-      TileT ra, rb;
-      int t = wave;
-      if (t < ntile) load_tile(ra, t);
-      while (t < ntile) {
-        if (t + kWaves < ntile) load_tile(rb, t + kWaves);
-        compute_tile(ra, t);
-        t += kWaves;
-        if (t >= ntile) break;
-        if (t + kWaves < ntile) load_tile(ra, t + kWaves);
-        compute_tile(rb, t);
-        t += kWaves;
+    // Segments: the run cut at chunk boundaries.  In a segment every wave
+    // takes the same even number of steps (tiles w, w+4, ...; steps past the
+    // segment are empty), so the two register buffers alternate statically
+    // and the last step already prefetches the next segment's first tile.
+    TileT ra, rb;
+    int seg_t0 = t;
+    auto seg_end_of = [&](int s0) { return min(run_end, lane_t0 + ((s0 - lane_t0) / ct + 1) * ct); };
+    if constexpr (!IDX) {
+      seg_pos1 = min(npos, (seg_end_of(seg_t0) - lane_t0) * kTile);
+      load_tile(ra, seg_t0 + wave, seg_t0 + wave < seg_end_of(seg_t0));
+    }
+    while (seg_t0 < run_end) {
+      const int seg_t1 = seg_end_of(seg_t0);
+      const int chunk = (seg_t0 - lane_t0) / ct;
+      const int chunk_t1 = min(lane_t1, lane_t0 + (chunk + 1) * ct);
+      seg_pos0 = (seg_t0 - lane_t0) * kTile;
+      seg_pos1 = min(npos, (seg_t1 - lane_t0) * kTile);
+      if constexpr (IDX) {
+        const int *src = p.token_idx + (int64_t)pair * p.idx_stride;
+        for (int i = tid; i < seg_pos1 - seg_pos0; i += 256) s_idx[i] = min(max(src[seg_pos0 + i], 0), L - 1);
+        __syncthreads();
+        load_tile(ra, seg_t0 + wave, seg_t0 + wave < seg_t1);
       }
-    }
+      const int steps = 2 * ((seg_t1 - seg_t0 + 2 * kWaves - 1) / (2 * kWaves));
+      const int next_t0 = seg_t1, next_t1 = seg_end_of(seg_t1);
+      for (int i = 0; i < steps; i += 2) {
+        const int ta = seg_t0 + wave + i * kWaves, tb2 = ta + kWaves;
+        load_tile(rb, tb2, tb2 < seg_t1);
+        compute_tile(ra, ta);
+        // next step of this segment, or (last step) the next segment's first
+        // tile in this run; one load site so both share the same registers
+        const bool in_seg = i + 2 < steps;
+        const int tn = in_seg ? tb2 + kWaves : next_t0 + wave;
+        const bool vn = in_seg ? tn < seg_t1 : (!IDX && tn < next_t1);
+        load_tile(ra, vn ? tn : seg_t0, vn);
+        compute_tile(rb, tb2);
+      }
 
-    // Combine the four waves' (m, l, O) and emit one partial per query head.
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
-    if (cg == 0) {
-      s_m[wave][col] = m_run;
-      s_l[wave][col] = l_run;
-    }
+      // Combine the four waves' (m, l, O) of this segment into its partial slot.
+      l_run += __shfl_xor(l_run, 16);
+      l_run += __shfl_xor(l_run, 32);
+      if (cg == 0) {
+        s_m[wave][col] = m_run;
+        s_l[wave][col] = l_run;
+      }
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_o[wave][col][NB * (4 * cg + i) + nb] = O[nb][i];
-    __syncthreads();
-    const float out_scale = (KVT == ATTN_I8) ? p.v_scale : 1.0f;
-    for (int e = tid; e < gcount * D; e += 256) {
-      const int g = e / D, d = e - g * D;
-      float M = NEG_INF;
+        for (int i = 0; i < 4; ++i) s_o[wave][col][NB * (4 * cg + i) + nb] = O[nb][i];
+      __syncthreads();
+      const float out_scale = (KVT == ATTN_I8) ? p.v_scale : 1.0f;
+      const int half = (seg_t0 == lane_t0 + chunk * ct) ? 0 : 1;
+      const bool fill_second = half == 0 && seg_t1 == chunk_t1;
+      for (int e = tid; e < gcount * D; e += 256) {
+        const int g = e / D, d = e - g * D;
+        float M = NEG_INF;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w)
-        if (s_l[w][g] > 0.f) M = fmaxf(M, s_m[w][g]);
-      float Ls = 0.f, acc = 0.f;
+        for (int w = 0; w < kWaves; ++w)
+          if (s_l[w][g] > 0.f) M = fmaxf(M, s_m[w][g]);
+        float Ls = 0.f, acc = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        if (s_l[w][g] > 0.f) {
-          const float f = __builtin_amdgcn_exp2f(s_m[w][g] - M);
-          Ls += f * s_l[w][g];
-          acc += f * s_o[w][g][d];
+        for (int w = 0; w < kWaves; ++w) {
+          if (s_l[w][g] > 0.f) {
+            const float f = __builtin_amdgcn_exp2f(s_m[w][g] - M);
+            Ls += f * s_l[w][g];
+            acc += f * s_o[w][g][d];
+          }
+        }
+        const int slot = s_slot[g] + 2 * chunk + half;
+        p.wl.o_part[(int64_t)slot * D + d] = (Ls > 0.f) ? acc / Ls * out_scale : 0.f;
+        if (d == 0) {
+          p.wl.m_part[slot] = (Ls > 0.f) ? M * kLn2 : NEG_INF;
+          p.wl.l_part[slot] = Ls;
+          if (fill_second) {
+            p.wl.m_part[slot + 1] = NEG_INF;
+            p.wl.l_part[slot + 1] = 0.f;
+          }
         }
       }
-      const int slot = p.wl.row_split_start[b * p.QH + kh * p.G + g0 + g] + chunk;
-      p.wl.o_part[(int64_t)slot * D + d] = (Ls > 0.f) ? acc / Ls * out_scale : 0.f;
-      if (d == 0) {
-        p.wl.m_part[slot] = (Ls > 0.f) ? M * kLn2 : NEG_INF;
-        p.wl.l_part[slot] = Ls;
-      }
+      __syncthreads();
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) O[nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+      m_run = NEG_INF;
+      l_run = 0.f;
+      seg_t0 = seg_t1;
     }
-    __syncthreads();
+    t = run_end;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode_mfma(const DecodeParams &p, int kv_dtype, int grid, hipStream_t s) {
-  dim3 g(grid), blk(256);
+template <bool IDX>
+static void launch_variant(const DecodeParams &p, int kv_dtype, dim3 g, hipStream_t s) {
+  dim3 blk(256);
   if (kv_dtype == ATTN_BF16) {
-    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_BF16>), g, blk, 0, s, p);
-    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_BF16>), g, blk, 0, s, p);
+    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_BF16, IDX>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_BF16, IDX>), g, blk, 0, s, p);
   } else {
-    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_I8>), g, blk, 0, s, p);
-    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_I8>), g, blk, 0, s, p);
+    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_I8, IDX>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_I8, IDX>), g, blk, 0, s, p);
+  }
+}
+
+hipError_t launch_decode_mfma(const DecodeParams &p, int kv_dtype, hipStream_t s) {
+  if (p.token_idx) {
+    if (p.split > kMaxIdxChunk) return hipErrorInvalidValue;
+    launch_variant<true>(p, kv_dtype, dim3(p.grid), s);
+  } else {
+    launch_variant<false>(p, kv_dtype, dim3(p.grid), s);
   }
   return hipGetLastError();
 }

@@ -26,148 +26,158 @@ __device__ __forceinline__ float load_elem(const void *base, int64_t i) {
 
 template <int QT, int KT>
 __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
-  __shared__ int s_info[2];
   __shared__ float s_q[16][257];
   __shared__ float s_p[16][kSub];
   __shared__ float s_m[16], s_l[16], s_alpha[16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int npairs = p.B * p.KH;
   const int D = p.D;
   const float NEG_INF = -__builtin_huge_valf();
 
-  for (;;) {
-    if (tid == 0) {
-      const int item = atomicAdd(p.wl.counter, 1);
-      int pair = -1, rel = 0;
-      if (item < *p.wl.total_items) {
-        int lo = 0, hi = npairs - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (p.wl.item_start[mid] <= item) lo = mid; else hi = mid - 1;
-        }
-        pair = lo;
-        rel = item - p.wl.item_start[lo];
-      }
-      s_info[0] = pair;
-      s_info[1] = rel;
-    }
-    __syncthreads();
-    const int pair = s_info[0];
-    const int rel = s_info[1];
-    if (pair < 0) break;
+  const int nwg = p.wl.hdr[1];
+  if ((int)blockIdx.x >= nwg) return;
+  const int T = p.wl.hdr[0];
+  const int t_begin = (int)((int64_t)blockIdx.x * T / nwg);
+  const int t_end = (int)((int64_t)(blockIdx.x + 1) * T / nwg);
+  const int nlanes = p.B * p.KH * p.ngb;
+  const int ct = p.split / 32;
 
+  for (int t = t_begin; t < t_end;) {
+    int lo = 0, hi = nlanes - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.wl.tile_start[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int q = lo;
+    const int lane_t0 = p.wl.tile_start[q], lane_t1 = p.wl.tile_start[q + 1];
+    const int run_end = min(t_end, lane_t1);
+    const int pair = q / p.ngb, gb = q - pair * p.ngb;
     const int b = pair / p.KH, kh = pair - b * p.KH;
-    const int gb = rel % p.ngb, chunk = rel / p.ngb;
-    const int L = p.seq_lens[b];
+    const int L = min(max(p.seq_lens[b], 0), p.max_seq_len);
     int npos = L;
     const int *idxp = nullptr;
     if (p.token_idx) {
       npos = L > 0 ? min(max(p.n_idx[pair], 0), p.idx_stride) : 0;
       idxp = p.token_idx + (int64_t)pair * p.idx_stride;
     }
-    const int pos0 = chunk * p.split;
-    const int pos1 = min(npos, pos0 + p.split);
     const int g0 = gb * 16;
     const int gcount = min(16, p.G - g0);
     const int64_t head_off = p.seq_offset[b] + (int64_t)kh * p.stride_h;
 
+    __syncthreads();
     for (int e = tid; e < gcount * D; e += 256) {
       const int g = e / D, d = e - g * D;
       s_q[g][d] = load_elem<QT>(p.q, ((int64_t)b * p.QH + (int64_t)kh * p.G + g0 + g) * D + d);
     }
-    if (tid < 16) {
-      s_m[tid] = NEG_INF;
-      s_l[tid] = 0.f;
-    }
-    float o[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) o[k] = 0.f;
-    __syncthreads();
 
-    for (int sub0 = pos0; sub0 < pos1; sub0 += kSub) {
-      const int n = min(kSub, pos1 - sub0);
-      // scores of this sub-tile: thread tt owns token position sub0 + tt
-      if (tid < n) {
-        int tok = sub0 + tid;
-        if (idxp) tok = min(max(idxp[tok], 0), L - 1);
-        const int64_t row = head_off + (int64_t)tok * p.stride_t;
-        float acc[16];
+    // one segment per chunk piece of this run
+    for (int seg_t0 = t; seg_t0 < run_end;) {
+      const int chunk = (seg_t0 - lane_t0) / ct;
+      const int chunk_t1 = min(lane_t1, lane_t0 + (chunk + 1) * ct);
+      const int seg_t1 = min(run_end, chunk_t1);
+      const int pos0 = (seg_t0 - lane_t0) * 32;
+      const int pos1 = min(npos, (seg_t1 - lane_t0) * 32);
+      if (tid < 16) {
+        s_m[tid] = NEG_INF;
+        s_l[tid] = 0.f;
+      }
+      float o[16];
 #pragma unroll
-        for (int g = 0; g < 16; ++g) acc[g] = 0.f;
-        for (int d = 0; d < D; ++d) {
-          const float kv = load_elem<KT>(p.k, row + d);
+      for (int k = 0; k < 16; ++k) o[k] = 0.f;
+      __syncthreads();
+
+      for (int sub0 = pos0; sub0 < pos1; sub0 += kSub) {
+        const int n = min(kSub, pos1 - sub0);
+        // scores of this sub-tile: thread tt owns token position sub0 + tt
+        if (tid < n) {
+          int tok = sub0 + tid;
+          if (idxp) tok = min(max(idxp[tok], 0), L - 1);
+          const int64_t row = head_off + (int64_t)tok * p.stride_t;
+          float acc[16];
+#pragma unroll
+          for (int g = 0; g < 16; ++g) acc[g] = 0.f;
+          for (int d = 0; d < D; ++d) {
+            const float kv = load_elem<KT>(p.k, row + d);
+#pragma unroll
+            for (int g = 0; g < 16; ++g)
+              if (g < gcount) acc[g] += s_q[g][d] * kv;
+          }
 #pragma unroll
           for (int g = 0; g < 16; ++g)
-            if (g < gcount) acc[g] += s_q[g][d] * kv;
+            if (g < gcount) s_p[g][tid] = acc[g] * p.softmax_scale;
         }
+        __syncthreads();
+        // running max, rescale factor and probabilities, one wave per head
+        for (int g = wave; g < gcount; g += 4) {
+          float mx = NEG_INF;
+          for (int i = lane; i < n; i += 64) mx = fmaxf(mx, s_p[g][i]);
+          mx = wave_max(mx);
+          const float m_old = s_m[g];
+          const float m_new = fmaxf(m_old, mx);
+          float sum = 0.f;
+          for (int i = lane; i < n; i += 64) {
+            const float e = expf(s_p[g][i] - m_new);
+            s_p[g][i] = e;
+            sum += e;
+          }
+          sum = wave_sum(sum);
+          if (lane == 0) {
+            const float alpha = (m_old == NEG_INF) ? 0.f : expf(m_old - m_new);
+            s_alpha[g] = alpha;
+            s_l[g] = alpha * s_l[g] + sum;
+            s_m[g] = m_new;
+          }
+        }
+        __syncthreads();
+        // O = alpha O + P V for the (g, d) outputs this thread owns
 #pragma unroll
-        for (int g = 0; g < 16; ++g)
-          if (g < gcount) s_p[g][tid] = acc[g] * p.softmax_scale;
-      }
-      __syncthreads();
-      // running max, rescale factor and probabilities, one wave per head
-      for (int g = wave; g < gcount; g += 4) {
-        float mx = NEG_INF;
-        for (int i = lane; i < n; i += 64) mx = fmaxf(mx, s_p[g][i]);
-        mx = wave_max(mx);
-        const float m_old = s_m[g];
-        const float m_new = fmaxf(m_old, mx);
-        float sum = 0.f;
-        for (int i = lane; i < n; i += 64) {
-          const float e = expf(s_p[g][i] - m_new);
-          s_p[g][i] = e;
-          sum += e;
+        for (int k = 0; k < 16; ++k) {
+          const int e = tid + 256 * k;
+          if (e < gcount * D) {
+            const int g = e / D, d = e - g * D;
+            float acc = o[k] * s_alpha[g];
+            for (int i = 0; i < n; ++i) {
+              int tok = sub0 + i;
+              if (idxp) tok = min(max(idxp[tok], 0), L - 1);
+              acc += s_p[g][i] * load_elem<KT>(p.v, head_off + (int64_t)tok * p.stride_t + d);
+            }
+            o[k] = acc;
+          }
         }
-        sum = wave_sum(sum);
-        if (lane == 0) {
-          const float alpha = (m_old == NEG_INF) ? 0.f : expf(m_old - m_new);
-          s_alpha[g] = alpha;
-          s_l[g] = alpha * s_l[g] + sum;
-          s_m[g] = m_new;
-        }
+        __syncthreads();
       }
-      __syncthreads();
-      // O = alpha O + P V for the (g, d) outputs this thread owns
+
+      const int half = (seg_t0 == lane_t0 + chunk * ct) ? 0 : 1;
+      const bool fill_second = half == 0 && seg_t1 == chunk_t1;
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const int e = tid + 256 * k;
         if (e < gcount * D) {
           const int g = e / D, d = e - g * D;
-          float acc = o[k] * s_alpha[g];
-          for (int i = 0; i < n; ++i) {
-            int tok = sub0 + i;
-            if (idxp) tok = min(max(idxp[tok], 0), L - 1);
-            acc += s_p[g][i] * load_elem<KT>(p.v, head_off + (int64_t)tok * p.stride_t + d);
+          const int slot = p.wl.row_split_start[b * p.QH + kh * p.G + g0 + g] + 2 * chunk + half;
+          const float l = s_l[g];
+          p.wl.o_part[(int64_t)slot * D + d] = (l > 0.f) ? o[k] / l : 0.f;
+          if (d == 0) {
+            p.wl.m_part[slot] = (l > 0.f) ? s_m[g] : NEG_INF;
+            p.wl.l_part[slot] = l;
+            if (fill_second) {
+              p.wl.m_part[slot + 1] = NEG_INF;
+              p.wl.l_part[slot + 1] = 0.f;
+            }
           }
-          o[k] = acc;
         }
       }
       __syncthreads();
+      seg_t0 = seg_t1;
     }
-
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int e = tid + 256 * k;
-      if (e < gcount * D) {
-        const int g = e / D, d = e - g * D;
-        const int slot = p.wl.row_split_start[b * p.QH + kh * p.G + g0 + g] + chunk;
-        const float l = s_l[g];
-        p.wl.o_part[(int64_t)slot * D + d] = (l > 0.f) ? o[k] / l : 0.f;
-        if (d == 0) {
-          p.wl.m_part[slot] = (l > 0.f) ? s_m[g] : NEG_INF;
-          p.wl.l_part[slot] = l;
-        }
-      }
-    }
-    __syncthreads();
+    t = run_end;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode_valu(const DecodeParams &p, int q_dtype, int kv_dtype, int grid, hipStream_t s) {
-  dim3 g(grid), blk(256);
+hipError_t launch_decode_valu(const DecodeParams &p, int q_dtype, int kv_dtype, hipStream_t s) {
+  dim3 g(p.grid), blk(256);
   if (q_dtype == ATTN_F32 && kv_dtype == ATTN_F32)
     hipLaunchKernelGGL((decode_valu_kernel<ATTN_F32, ATTN_F32>), g, blk, 0, s, p);
   else if (q_dtype == ATTN_BF16 && kv_dtype == ATTN_BF16)

@@ -4,81 +4,152 @@
 namespace lcdg {
 namespace {
 
+// Token positions of lane q = (pair, query-head block): the sequence length,
+// or the kept-index count in indexed mode; clamped to the declared bounds.
+__device__ __forceinline__ int lane_positions(const DecodeParams &p, int pair) {
+  const int b = pair / p.KH;
+  const int L = min(max(p.seq_lens[b], 0), p.max_seq_len);
+  if (p.token_idx) return L > 0 ? min(max(p.n_idx[pair], 0), p.idx_stride) : 0;
+  return L;
+}
+
+// Inclusive scan of one int per thread across the 1024-thread block.
+__device__ __forceinline__ int block_scan(int v, int *s_sum) {
+  const int tid = threadIdx.x;
+  s_sum[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int x = tid >= off ? s_sum[tid - off] : 0;
+    __syncthreads();
+    s_sum[tid] += x;
+    __syncthreads();
+  }
+  const int r = s_sum[tid];
+  __syncthreads();
+  return r;
+}
+
 // Ragged work-list ("优化稀疏注意力中的令牌丢弃机制" §5: long sequences are split
-// across many workgroups so a 128K sequence next to a 512-token one does not
-// leave compute units idle).  One workgroup scans the per-(b, kh) chunk
-// counts and lays out: the first item of every pair, the partial slot of
-// every (output row, chunk), the total item count; it also zeroes the claim
-// counter, so a decode launch right after it starts from item 0.
+// across many workgroups so a 128K sequence next to a 512-token one leaves no
+// compute unit idle).  One workgroup lays out the tile stream of all lanes,
+// the two partial slots of every (output row, chunk), the tile total and the
+// number of decode workgroups that get a range (each range >= one chunk).
 __global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p) {
   __shared__ int s_sum[1024];
   const int tid = threadIdx.x;
   const int np = p.B * p.KH;
-  const int per = (np + 1023) / 1024;
-  const int q0 = min(np, tid * per), q1 = min(np, q0 + per);
-  int local = 0;
-  for (int q = q0; q < q1; ++q) {
-    const int b = q / p.KH;
-    const int L = min(max(p.seq_lens[b], 0), p.max_seq_len);
-    int n = L;
-    if (p.token_idx) n = L > 0 ? min(max(p.n_idx[q], 0), p.idx_stride) : 0;
-    const int nc = (n + p.split - 1) / p.split;
-    p.wl.chunks[q] = nc;
-    local += nc;
+  const int nl = np * p.ngb;
+  // tiles of every lane, in lane order
+  {
+    const int per = (nl + 1023) / 1024;
+    const int q0 = min(nl, tid * per), q1 = min(nl, q0 + per);
+    int local = 0;
+    for (int q = q0; q < q1; ++q) local += (lane_positions(p, q / p.ngb) + 31) / 32;
+    int run = block_scan(local, s_sum) - local;
+    for (int q = q0; q < q1; ++q) {
+      p.wl.tile_start[q] = run;
+      run += (lane_positions(p, q / p.ngb) + 31) / 32;
+    }
+    if (tid == 1023) {
+      const int total = run;  // thread 1023 owns the last lanes (or none): run is the total
+      p.wl.tile_start[nl] = total;
+      const int ct = p.split / 32;
+      const int fit = total / ct;
+      p.wl.hdr[0] = total;
+      p.wl.hdr[1] = total == 0 ? 0 : min(p.grid, max(1, fit));
+    }
   }
-  s_sum[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? s_sum[tid - off] : 0;
-    __syncthreads();
-    s_sum[tid] += v;
-    __syncthreads();
-  }
-  int run = s_sum[tid] - local;
-  for (int q = q0; q < q1; ++q) {
-    const int nc = p.wl.chunks[q];
-    p.wl.item_start[q] = p.ngb * run;
-    const int b = q / p.KH, kh = q - b * p.KH;
-    for (int g = 0; g < p.G; ++g) p.wl.row_split_start[b * p.QH + kh * p.G + g] = p.G * run + g * nc;
-    run += nc;
-  }
-  if (tid == 1023) {
-    const int total = s_sum[1023];
-    p.wl.item_start[np] = p.ngb * total;
-    p.wl.row_split_start[p.B * p.QH] = p.G * total;
-    *p.wl.total_items = p.ngb * total;
-    *p.wl.counter = 0;
+  // two partial slots per (row, chunk)
+  {
+    const int per = (np + 1023) / 1024;
+    const int q0 = min(np, tid * per), q1 = min(np, q0 + per);
+    int local = 0;
+    for (int q = q0; q < q1; ++q) local += (lane_positions(p, q) + p.split - 1) / p.split;
+    int run = block_scan(local, s_sum) - local;
+    for (int q = q0; q < q1; ++q) {
+      const int nc = (lane_positions(p, q) + p.split - 1) / p.split;
+      const int b = q / p.KH, kh = q - b * p.KH;
+      for (int g = 0; g < p.G; ++g) p.wl.row_split_start[b * p.QH + kh * p.G + g] = 2 * (p.G * run + g * nc);
+      run += nc;
+    }
+    if (tid == 1023) p.wl.row_split_start[p.B * p.QH] = 2 * p.G * run;
   }
 }
 
-// Log-sum-exp merge of partial triples, one wave per output row:
+constexpr int kMergeThreads = 512;
+constexpr int kMergeWeights = 512;
+
+__device__ __forceinline__ float block_reduce(float v, float *s_red, bool is_max) {
+  v = is_max ? wave_max(v) : wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) s_red[wave] = v;
+  __syncthreads();
+  float r = s_red[0];
+  for (int w = 1; w < kMergeThreads / 64; ++w) r = is_max ? fmaxf(r, s_red[w]) : r + s_red[w];
+  return r;
+}
+
+// Log-sum-exp merge of partial triples, one workgroup per output row:
 // M = max m_i, w_i = exp(m_i - M) l_i, out = sum w_i o_i / sum w_i,
-// lse = M + ln(sum w_i).  Fixed summation order (deterministic).
+// lse = M + ln(sum w_i).  The row's partials are spread over thread groups
+// (each group sums a strided subset, then the groups are added in a fixed
+// order), so the result is deterministic.
 template <int OUT>
-__global__ __launch_bounds__(256) void merge_kernel(const float *o_part, const float *m_part, const float *l_part,
-                                                    const int32_t *rss, int32_t rows, int32_t D, void *out,
-                                                    float *lse) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *o_part, const float *m_part,
+                                                              const float *l_part, const int32_t *rss, int32_t rows,
+                                                              int32_t D, void *out, float *lse) {
+  __shared__ float s_red[kMergeThreads / 64];
+  __shared__ float s_w[kMergeWeights];
+  __shared__ float s_acc[kMergeThreads * 4];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
   const float NEG_INF = -__builtin_huge_valf();
-  const int s0 = rss[row], s1 = rss[row + 1];
+  const int s0 = rss[row], n = rss[row + 1] - s0;
   float M = NEG_INF;
-  for (int i = s0 + lane; i < s1; i += 64)
-    if (l_part[i] > 0.f) M = fmaxf(M, m_part[i]);
-  M = wave_max(M);
+  for (int i = tid; i < n; i += kMergeThreads)
+    if (l_part[s0 + i] > 0.f) M = fmaxf(M, m_part[s0 + i]);
+  M = block_reduce(M, s_red, true);
   float Ls = 0.f;
-  for (int i = s0 + lane; i < s1; i += 64) {
-    const float l = l_part[i];
-    if (l > 0.f) Ls += expf(m_part[i] - M) * l;
+  for (int i = tid; i < n; i += kMergeThreads) {
+    const float l = l_part[s0 + i];
+    const float w = (l > 0.f) ? expf(m_part[s0 + i] - M) * l : 0.f;
+    if (i < kMergeWeights) s_w[i] = w;
+    Ls += w;
   }
-  Ls = wave_sum(Ls);
-  for (int d = lane; d < D; d += 64) {
-    float acc = 0.f;
-    for (int i = s0; i < s1; ++i) {
-      const float l = l_part[i];
-      if (l > 0.f) acc += expf(m_part[i] - M) * l * o_part[(int64_t)i * D + d];
+  Ls = block_reduce(Ls, s_red, false);
+  __syncthreads();
+  auto weight = [&](int i) -> float {
+    if (i < kMergeWeights) return s_w[i];
+    const float l = l_part[s0 + i];
+    return (l > 0.f) ? expf(m_part[s0 + i] - M) * l : 0.f;
+  };
+  const bool vec = (D & 3) == 0;
+  const int nq = vec ? D / 4 : D;            // columns handled per group
+  const int ngrp = kMergeThreads / nq;
+  const int grp = tid / nq, q = tid - grp * nq;
+  if (grp < ngrp) {
+    if (vec) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int i = grp; i < n; i += ngrp) {
+        const float w = weight(i);
+        if (w > 0.f) acc += w * *(const f32x4_t *)(o_part + (int64_t)(s0 + i) * D + 4 * q);
+      }
+      *(f32x4_t *)(s_acc + grp * D + 4 * q) = acc;
+    } else {
+      float acc = 0.f;
+      for (int i = grp; i < n; i += ngrp) {
+        const float w = weight(i);
+        if (w > 0.f) acc += w * o_part[(int64_t)(s0 + i) * D + q];
+      }
+      s_acc[grp * D + q] = acc;
     }
+  }
+  __syncthreads();
+  for (int d = tid; d < D; d += kMergeThreads) {
+    float acc = 0.f;
+    for (int g = 0; g < ngrp; ++g) acc += s_acc[g * D + d];
     const float o = (Ls > 0.f) ? acc / Ls : 0.f;
     if constexpr (OUT == ATTN_F32) {
       ((float *)out)[(int64_t)row * D + d] = o;
@@ -86,7 +157,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *o_part, const f
       ((uint16_t *)out)[(int64_t)row * D + d] = (uint16_t)f32_to_bf16_bits(o);
     }
   }
-  if (lane == 0 && lse) lse[row] = (Ls > 0.f) ? M + logf(Ls) : NEG_INF;
+  if (tid == 0 && lse) lse[row] = (Ls > 0.f) ? M + logf(Ls) : NEG_INF;
 }
 
 __global__ __launch_bounds__(256) void copy_kernel(u32x4_t *dst, const u32x4_t *src, size_t n) {
@@ -119,7 +190,7 @@ hipError_t launch_worklist(const DecodeParams &p, hipStream_t s) {
 hipError_t launch_merge(const float *o_part, const float *m_part, const float *l_part, const int32_t *rss,
                         int32_t rows, int32_t D, int32_t out_dtype, void *out, float *lse, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  dim3 g((rows + 3) / 4), blk(256);
+  dim3 g(rows), blk(kMergeThreads);
   if (out_dtype == ATTN_F32)
     hipLaunchKernelGGL((merge_kernel<ATTN_F32>), g, blk, 0, s, o_part, m_part, l_part, rss, rows, D, out, lse);
   else
