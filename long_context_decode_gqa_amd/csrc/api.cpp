@@ -207,11 +207,12 @@ static attn_status decode_impl(const attn_decode_args *a, attn_stream_t stream, 
   p.wl.tile_start = reinterpret_cast<int32_t *>(ws + L.tile_start);
   p.wl.row_split_start = reinterpret_cast<int32_t *>(ws + L.rss);
   {
-    // persistent grid: two workgroups of four waves per compute unit (the MFMA
-    // kernel's register budget), capped by the largest possible tile count
+    // persistent grid: the MFMA kernel runs one-wave workers, eight per compute
+    // unit (two per SIMD, its register budget); the vector-ALU kernel four
+    // 256-thread workgroups per unit; capped by the largest possible tile count
     const int cus = device_cu_count();
     const int64_t max_tiles = (int64_t)p.B * p.KH * L.ngb * (((int64_t)L.max_tokens + 31) / 32);
-    int64_t grid = (int64_t)cus * (L.mfma ? 2 : 4);
+    int64_t grid = (int64_t)cus * (L.mfma ? 8 : 4);
     if (grid > max_tiles) grid = max_tiles;
     p.grid = (int)(grid < 1 ? 1 : grid);
   }

@@ -40,7 +40,6 @@ namespace lcdg {
 namespace {
 
 constexpr int kTile = 32;
-constexpr int kWaves = 4;
 
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
@@ -83,13 +82,20 @@ struct Tile {
 // Tokens per chunk of the indexed variant (its index list is staged in LDS).
 constexpr int kMaxIdxChunk = 1024;
 
+// One wave = one worker.  The work-list lays every (b, kh, head block) lane's
+// tiles end to end; worker w streams the contiguous tile range
+// [w*T/W, (w+1)*T/W), so all workers move the same number of K/V bytes
+// whatever the mix of sequence lengths, with no atomics and no barriers in
+// the loop.  A range is cut into runs (one lane each) and runs into segments
+// (one chunk piece each); a segment's partial (m, l, o) goes straight from
+// registers to its slot.
 template <int D, int KVT, bool IDX>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_mfma_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_mfma_kernel(DecodeParams p) {
   typedef Tile<D, KVT, IDX> TileT;
   constexpr int NB = D / 16;
-  constexpr int KB = D / 32;
   constexpr int ES = TileT::ES;
   constexpr int KL = TileT::KL;
+  constexpr int KB = D / 32;
   constexpr int VW = TileT::VW;
   typedef typename VecW<VW>::T VV;
   typedef typename std::conditional<KVT == ATTN_BF16, bf16x8_t, f16x8_t>::type OpT;
@@ -99,23 +105,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // fp16 for int8 KV), rows padded by 16 bytes against bank conflicts.
   constexpr int kQRow = D * 2 + 16;
   __shared__ __attribute__((aligned(16))) unsigned char s_q[16 * kQRow];
-  __shared__ float s_m[kWaves][16];
-  __shared__ float s_l[kWaves][16];
-  __shared__ float s_o[kWaves][16][D + 4];
-  __shared__ int s_slot[16];  // first partial slot of each query head of the run
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x;
   const int col = lane & 15, cg = lane >> 4;
   const float c1 = p.softmax_scale * kLog2e;
   const float NEG_INF = -__builtin_huge_valf();
 
-  // This workgroup's contiguous share of the tile stream.
-  const int nwg = p.wl.hdr[1];
-  if ((int)blockIdx.x >= nwg) return;
+  const int nworkers = p.wl.hdr[1];
+  if ((int)blockIdx.x >= nworkers) return;
   const int T = p.wl.hdr[0];
-  const int t_begin = (int)((int64_t)blockIdx.x * T / nwg);
-  const int t_end = (int)((int64_t)(blockIdx.x + 1) * T / nwg);
+  const int t_begin = (int)((int64_t)blockIdx.x * T / nworkers);
+  const int t_end = (int)((int64_t)(blockIdx.x + 1) * T / nworkers);
   const int nlanes = p.B * p.KH * p.ngb;
   const int ct = p.split / kTile;  // tiles per chunk
 
@@ -149,14 +149,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vbase, (short)0, nrec, 0x00020000);
     const float *kscale = (KVT == ATTN_I8) ? p.k_scale + (int64_t)pair * p.k_scale_stride : nullptr;
 
-    // Stage Q (16 heads of this block, zero past G) in LDS, in MFMA operand
-    // type; each tile reads its B operand from there instead of holding it in
-    // registers for the whole run.
+    // Stage Q (the 16 heads of this block, zero past G) in LDS in MFMA
+    // operand type; tiles read their B operand from there.  The partial
+    // slots of this lane's rows are loaded now as well: a global load inside
+    // the segment loop would make the compiler wait for every load in
+    // flight, the tile prefetch included.
     __syncthreads();
-    for (int e = tid; e < 16 * (D / 8); e += 256) {
+    for (int e = lane; e < 16 * (D / 8); e += 64) {
       const int g = e / (D / 8), c8 = e - g * (D / 8);
       u32x4_t w = (u32x4_t){0u, 0u, 0u, 0u};
-      if (g < gcount) w = *(const u32x4_t *)((const uint16_t *)p.q + ((int64_t)b * p.QH + (int64_t)kh * p.G + g0 + g) * D + 8 * c8);
+      if (g < gcount)
+        w = *(const u32x4_t *)((const uint16_t *)p.q + ((int64_t)b * p.QH + (int64_t)kh * p.G + g0 + g) * D + 8 * c8);
       if constexpr (KVT == ATTN_I8) {
         f16x8_t h;
 #pragma unroll
@@ -168,11 +171,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       *(u32x4_t *)(s_q + g * kQRow + 16 * c8) = w;
     }
-    // (global loads inside the segment loop would make the compiler wait for
-    // every load in flight, the tile prefetch included, so stage these too)
-    if (tid < gcount) s_slot[tid] = p.wl.row_split_start[b * p.QH + kh * p.G + g0 + tid];
+    const int slot_base = qvalid ? p.wl.row_split_start[b * p.QH + kh * p.G + g0 + col] : 0;
     __syncthreads();
-    // operand of k-block kb: channels d0 .. d0+7 of query head `col`
     auto q_operand = [&](int kb) -> OpT {
       const int d0 = (KVT == ATTN_BF16) ? 8 * (4 * kb + cg) : 64 * (kb >> 1) + 16 * cg + 8 * (kb & 1);
       return __builtin_bit_cast(OpT, *(const u32x4_t *)(s_q + col * kQRow + 2 * d0));
@@ -310,18 +310,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     };
 
-    // Segments: the run cut at chunk boundaries.  In a segment every wave
-    // takes the same even number of steps (tiles w, w+4, ...; steps past the
-    // segment are empty), so the two register buffers alternate statically
-    // and the last step already prefetches the next segment's first tile.
+    // Segments: the run cut at chunk boundaries.  A segment takes an even
+    // number of steps (the last may be empty), so the two register buffers
+    // alternate statically, and its last step already prefetches the first
+    // tile of the next segment of the run.
     TileT ra, rb;
-    int seg_t0 = t;
     auto seg_end_of = [&](int s0) { return min(run_end, lane_t0 + ((s0 - lane_t0) / ct + 1) * ct); };
-    if constexpr (!IDX) {
-      seg_pos1 = min(npos, (seg_end_of(seg_t0) - lane_t0) * kTile);
-      load_tile(ra, seg_t0 + wave, seg_t0 + wave < seg_end_of(seg_t0));
-    }
-    while (seg_t0 < run_end) {
+    if constexpr (!IDX) load_tile(ra, t, true);
+    for (int seg_t0 = t; seg_t0 < run_end;) {
       const int seg_t1 = seg_end_of(seg_t0);
       const int chunk = (seg_t0 - lane_t0) / ct;
       const int chunk_t1 = min(lane_t1, lane_t0 + (chunk + 1) * ct);
@@ -329,67 +325,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       seg_pos1 = min(npos, (seg_t1 - lane_t0) * kTile);
       if constexpr (IDX) {
         const int *src = p.token_idx + (int64_t)pair * p.idx_stride;
-        for (int i = tid; i < seg_pos1 - seg_pos0; i += 256) s_idx[i] = min(max(src[seg_pos0 + i], 0), L - 1);
         __syncthreads();
-        load_tile(ra, seg_t0 + wave, seg_t0 + wave < seg_t1);
+        for (int i = lane; i < seg_pos1 - seg_pos0; i += 64) s_idx[i] = min(max(src[seg_pos0 + i], 0), L - 1);
+        __syncthreads();
+        load_tile(ra, seg_t0, true);
       }
-      const int steps = 2 * ((seg_t1 - seg_t0 + 2 * kWaves - 1) / (2 * kWaves));
-      const int next_t0 = seg_t1, next_t1 = seg_end_of(seg_t1);
+      const int steps = (seg_t1 - seg_t0 + 1) & ~1;
+      const int next_t1 = seg_end_of(seg_t1);
       for (int i = 0; i < steps; i += 2) {
-        const int ta = seg_t0 + wave + i * kWaves, tb2 = ta + kWaves;
-        load_tile(rb, tb2, tb2 < seg_t1);
+        const int ta = seg_t0 + i;
+        load_tile(rb, ta + 1, ta + 1 < seg_t1);
         compute_tile(ra, ta);
         // next step of this segment, or (last step) the next segment's first
         // tile in this run; one load site so both share the same registers
         const bool in_seg = i + 2 < steps;
-        const int tn = in_seg ? tb2 + kWaves : next_t0 + wave;
+        const int tn = in_seg ? ta + 2 : seg_t1;
         const bool vn = in_seg ? tn < seg_t1 : (!IDX && tn < next_t1);
         load_tile(ra, vn ? tn : seg_t0, vn);
-        compute_tile(rb, tb2);
+        compute_tile(rb, ta + 1);
       }
 
-      // Combine the four waves' (m, l, O) of this segment into its partial slot.
+      // Partial of this segment, straight from registers.  Lane (col, cg)
+      // holds channels NB*(4*cg + i) + nb = 4*NB*cg + NB*i + nb of head col.
       l_run += __shfl_xor(l_run, 16);
       l_run += __shfl_xor(l_run, 32);
-      if (cg == 0) {
-        s_m[wave][col] = m_run;
-        s_l[wave][col] = l_run;
-      }
+      if (qvalid) {
+        const int half = (seg_t0 == lane_t0 + chunk * ct) ? 0 : 1;
+        const int slot = slot_base + 2 * chunk + half;
+        const float out_scale = (KVT == ATTN_I8) ? p.v_scale : 1.0f;
+        const float inv = l_run > 0.f ? out_scale / l_run : 0.f;
+        float *op = p.wl.o_part + (int64_t)slot * D + 4 * NB * cg;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s_o[wave][col][NB * (4 * cg + i) + nb] = O[nb][i];
-      __syncthreads();
-      const float out_scale = (KVT == ATTN_I8) ? p.v_scale : 1.0f;
-      const int half = (seg_t0 == lane_t0 + chunk * ct) ? 0 : 1;
-      const bool fill_second = half == 0 && seg_t1 == chunk_t1;
-      for (int e = tid; e < gcount * D; e += 256) {
-        const int g = e / D, d = e - g * D;
-        float M = NEG_INF;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w)
-          if (s_l[w][g] > 0.f) M = fmaxf(M, s_m[w][g]);
-        float Ls = 0.f, acc = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          if (s_l[w][g] > 0.f) {
-            const float f = __builtin_amdgcn_exp2f(s_m[w][g] - M);
-            Ls += f * s_l[w][g];
-            acc += f * s_o[w][g][d];
+          for (int n4 = 0; n4 < NB / 4; ++n4) {
+            const f32x4_t v = {O[4 * n4][i] * inv, O[4 * n4 + 1][i] * inv, O[4 * n4 + 2][i] * inv,
+                               O[4 * n4 + 3][i] * inv};
+            *(f32x4_t *)(op + NB * i + 4 * n4) = v;
           }
-        }
-        const int slot = s_slot[g] + 2 * chunk + half;
-        p.wl.o_part[(int64_t)slot * D + d] = (Ls > 0.f) ? acc / Ls * out_scale : 0.f;
-        if (d == 0) {
-          p.wl.m_part[slot] = (Ls > 0.f) ? M * kLn2 : NEG_INF;
-          p.wl.l_part[slot] = Ls;
-          if (fill_second) {
+        if (cg == 0) {
+          p.wl.m_part[slot] = l_run > 0.f ? m_run * kLn2 : NEG_INF;
+          p.wl.l_part[slot] = l_run;
+          if (half == 0 && seg_t1 == chunk_t1) {
             p.wl.m_part[slot + 1] = NEG_INF;
             p.wl.l_part[slot + 1] = 0.f;
           }
         }
       }
-      __syncthreads();
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) O[nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
       m_run = NEG_INF;
@@ -404,7 +386,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 template <bool IDX>
 static void launch_variant(const DecodeParams &p, int kv_dtype, dim3 g, hipStream_t s) {
-  dim3 blk(256);
+  dim3 blk(64);
   if (kv_dtype == ATTN_BF16) {
     if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_BF16, IDX>), g, blk, 0, s, p);
     else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_BF16, IDX>), g, blk, 0, s, p);
