@@ -70,16 +70,83 @@ attn_status oam_value_lognorm(const attn_kv_geom *geom, const void *v_bf16, floa
   return e == hipSuccess ? ATTN_OK : api_fail_hip(e, "value-norm launch");
 }
 
-attn_status oam_score_topk_workspace_size(const oam_topk_args *args, size_t *bytes) {
-  (void)args;
-  (void)bytes;
-  return api_fail(ATTN_ERR_UNSUPPORTED, "oam_score_topk is not built yet");
+}  // extern "C"
+
+namespace {
+
+struct OamLayout {
+  size_t scores, vlog, hist, counts, total;
+  int32_t nblk;
+};
+
+attn_status plan_oam(const oam_topk_args *a, OamLayout *L) {
+  if (!a) return api_fail(ATTN_ERR_INVALID_ARG, "args is NULL");
+  attn_status st = api_check_geom(a->kv, 2, true);
+  if (st != ATTN_OK) return st;
+  const attn_kv_geom &g = a->kv;
+  if (g.D != 64 && g.D != 128) return api_fail(ATTN_ERR_UNSUPPORTED, "oam_score_topk supports D = 64 or 128");
+  if (a->G < 1 || a->G > 16) return api_fail(ATTN_ERR_UNSUPPORTED, "oam_score_topk supports 1 <= G <= 16");
+  if (a->top_k < 1) return api_fail(ATTN_ERR_INVALID_ARG, "top_k must be >= 1");
+  if (!(fabsf(a->softmax_scale) < INFINITY) || !(fabsf(a->beta) < INFINITY))
+    return api_fail(ATTN_ERR_INVALID_ARG, "softmax_scale and beta must be finite");
+  if (!(a->eps >= 0.f) || !(a->eps < INFINITY)) return api_fail(ATTN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (((int64_t)g.max_seq_len + 64) * g.stride_t * 2 >= (int64_t(1) << 31))
+    return api_fail(ATTN_ERR_UNSUPPORTED, "one (sequence, KV head) may span at most 2 GiB of rows");
+  if (g.B > 0) {
+    if (!a->q || !a->k) return api_fail(ATTN_ERR_INVALID_ARG, "q and k are required");
+    if (!a->vlog && !a->v) return api_fail(ATTN_ERR_INVALID_ARG, "either vlog or v is required");
+    if (!a->idx_out || !a->n_kept) return api_fail(ATTN_ERR_INVALID_ARG, "idx_out and n_kept are required");
+    if ((reinterpret_cast<uintptr_t>(a->q) | reinterpret_cast<uintptr_t>(a->k)) & 15)
+      return api_fail(ATTN_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
+    if (!a->vlog && (reinterpret_cast<uintptr_t>(a->v) & 15))
+      return api_fail(ATTN_ERR_INVALID_ARG, "v must be 16-byte aligned");
+  }
+  if (a->vlog && a->vlog_stride < g.max_seq_len) return api_fail(ATTN_ERR_INVALID_ARG, "vlog_stride must be >= max_seq_len");
+  const int64_t npairs = (int64_t)g.B * g.KH;
+  const int64_t stride = g.max_seq_len;
+  L->nblk = (g.max_seq_len + oam_block_tokens() - 1) / oam_block_tokens();
+  auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+  size_t off = 0;
+  L->scores = off; off = al(off + (a->scores_out ? 0 : npairs * stride * sizeof(float)));
+  L->vlog = off; off = al(off + (a->vlog ? 0 : npairs * stride * sizeof(float)));
+  L->hist = off; off = al(off + (size_t)3 * npairs * 2048 * sizeof(uint32_t));
+  L->counts = off; off = al(off + (size_t)npairs * (L->nblk > 0 ? L->nblk : 1) * 2 * sizeof(int32_t));
+  L->total = off;
+  return ATTN_OK;
 }
 
-attn_status oam_score_topk(const oam_topk_args *args, attn_stream_t stream) {
-  (void)args;
-  (void)stream;
-  return api_fail(ATTN_ERR_UNSUPPORTED, "oam_score_topk is not built yet");
+}  // namespace
+
+extern "C" {
+
+attn_status oam_score_topk_workspace_size(const oam_topk_args *args, size_t *bytes) {
+  if (!bytes) return api_fail(ATTN_ERR_INVALID_ARG, "bytes is NULL");
+  OamLayout L;
+  attn_status st = plan_oam(args, &L);
+  if (st != ATTN_OK) return st;
+  *bytes = L.total;
+  return ATTN_OK;
+}
+
+attn_status oam_score_topk(const oam_topk_args *a, attn_stream_t stream) {
+  OamLayout L;
+  attn_status st = plan_oam(a, &L);
+  if (st != ATTN_OK) return st;
+  if (a->kv.B == 0) return ATTN_OK;
+  if (!a->workspace || (reinterpret_cast<uintptr_t>(a->workspace) & 255))
+    return api_fail(ATTN_ERR_INVALID_ARG, "workspace must be a 256-byte aligned device pointer");
+  if (a->workspace_bytes < L.total) return api_fail(ATTN_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than required");
+  char *ws = static_cast<char *>(a->workspace);
+  OamPlan plan;
+  plan.scores = a->scores_out ? a->scores_out : reinterpret_cast<float *>(ws + L.scores);
+  plan.score_stride = a->kv.max_seq_len;
+  plan.vlog = a->vlog ? const_cast<float *>(a->vlog) : reinterpret_cast<float *>(ws + L.vlog);
+  plan.vlog_stride = a->vlog ? a->vlog_stride : a->kv.max_seq_len;
+  plan.hist = reinterpret_cast<uint32_t *>(ws + L.hist);
+  plan.chunk_cnt = reinterpret_cast<int32_t *>(ws + L.counts);
+  plan.nchunk = L.nblk;
+  hipError_t e = launch_oam(*a, plan, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : api_fail_hip(e, "oam launch");
 }
 
 }  // extern "C"

@@ -103,14 +103,16 @@ hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
 hipError_t launch_read(const void *src, size_t bytes, float *sink, hipStream_t s);
 
 struct OamPlan {
-  float *scores;        // [npairs][max_len]
-  uint32_t *hist;       // [3][npairs][2048]
-  int32_t *state;       // [npairs][4]: prefix, need, eq_take, pad
-  int32_t *chunk_cnt;   // [npairs][nchunk][2]
-  int32_t chunk;        // tokens per selection chunk
-  int32_t nchunk;       // chunks per pair
+  float *scores;         // [npairs][score_stride]
+  int32_t score_stride;
+  float *vlog;           // value log-norms: the caller's or computed into the workspace
+  int32_t vlog_stride;
+  uint32_t *hist;        // [3][npairs][2048]
+  int32_t *chunk_cnt;    // [npairs][nchunk][2]
+  int32_t nchunk;        // selection blocks per pair
 };
 hipError_t launch_oam(const oam_topk_args &a, const OamPlan &plan, hipStream_t s);
+int oam_block_tokens();
 
 int device_cu_count();
 

@@ -1,0 +1,144 @@
+"""GPU parity of oam_score_topk (+ exact attention over the kept tokens).
+
+Scores: fp32 on the GPU vs fp64 oracle, |diff| <= 5e-5.  Kept sets: equal to
+the oracle's except for tokens whose oracle score lies within 1e-4 of the
+K-th largest oracle score; and exactly equal to the top-K of the GPU's own
+fp32 scores by (score desc, index asc), which checks the radix select and
+its tie rule bit for bit.  Attention over the kept set: 2e-3 max-abs.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_decode_gqa_amd as pkg
+import oracle
+import synth
+from gpu_helpers import DEV, dev_geom, log_case, problem, to_dev
+
+pytestmark = pytest.mark.gpu
+BAND = 1e-4
+
+
+def run_oam(w, q, k, v, g, top_k, beta=1.0, eps=1e-6, use_vlog=False, stride=None):
+    qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
+    kd, vd = to_dev(k), to_dev(v)
+    geom = dev_geom(g)
+    scores = torch.full((w.B * w.KH, max(1, geom.max_seq_len)), float("nan"), dtype=torch.float32, device=DEV)
+    kw = dict(scores_out=scores, beta=beta, eps=eps)
+    if use_vlog:
+        kw["vlog"] = pkg.oam_value_lognorm(vd, geom, eps)
+    else:
+        kw["v"] = vd
+    idx, nk = pkg.oam_score_topk(qd, kd, geom, w.G, top_k, **kw)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), nk.cpu().numpy(), scores.cpu().numpy()
+
+
+def exact_topk(s, k):
+    order = np.lexsort((np.arange(len(s)), -s.astype(np.float64)))
+    return np.sort(order[:min(k, len(s))])
+
+
+def check_pair(ref_s, gpu_s, idx_row, nk, top_k):
+    L = len(ref_s)
+    assert nk == min(top_k, L)
+    kept = idx_row[:nk]
+    assert np.all(idx_row[nk:] == -1)
+    assert np.all(np.diff(kept) > 0) and (nk == 0 or (kept[0] >= 0 and kept[-1] < L))
+    if L:
+        assert np.abs(gpu_s[:L] - ref_s).max() <= 5e-5
+    # exact w.r.t. the GPU's own fp32 scores (radix select + tie rule)
+    np.testing.assert_array_equal(kept, exact_topk(gpu_s[:L], top_k))
+    # equal to the oracle's set up to tokens within the band around its K-th score
+    ref = oracle.topk_sort(ref_s, top_k)
+    if nk < L:
+        thr = np.sort(ref_s)[::-1][nk - 1]
+        diff = set(kept.tolist()) ^ set(ref.tolist())
+        assert all(abs(ref_s[i] - thr) <= BAND for i in diff), f"{len(diff)} tokens outside the band"
+
+
+@pytest.mark.parametrize("D,G,top_k", [(128, 8, 100), (64, 4, 1), (128, 16, 333), (128, 1, 5000)])
+def test_oam_ragged_against_oracle(D, G, top_k):
+    lens = np.array([1, 700, 4096, 5000, 0, 2049], np.int32)
+    w = synth.workload("oam_128k", B=len(lens), KH=2, G=G, D=D, lens=lens, layout="token_major", seed=60 + G)
+    q, k, v, g = synth.generate(w)
+    log_case(f"oam ragged D={D} G={G} K={top_k}")
+    idx, nk, sc = run_oam(w, q, k, v, g, top_k)
+    p = problem(w, q, k, v, g)
+    for b in range(w.B):
+        for kh in range(w.KH):
+            pr = b * w.KH + kh
+            ref_s = oracle.oam_scores(p, b, kh, 1.0, 1e-6)
+            check_pair(ref_s, sc[pr], idx[pr], nk[pr], top_k)
+
+
+def test_oam_beta_zero_and_given_vlog():
+    lens = np.array([3000, 1234], np.int32)
+    w = synth.workload("oam_128k", B=2, KH=2, lens=lens, layout="head_major", seed=66)
+    q, k, v, g = synth.generate(w)
+    log_case("oam beta=0 / vlog given")
+    p = problem(w, q, k, v, g)
+    for beta, use_vlog in ((0.0, False), (1.0, True), (2.5, True)):
+        idx, nk, sc = run_oam(w, q, k, v, g, 200, beta=beta, use_vlog=use_vlog)
+        for b in range(2):
+            for kh in range(2):
+                check_pair(oracle.oam_scores(p, b, kh, beta, 1e-6), sc[b * 2 + kh], idx[b * 2 + kh], nk[b * 2 + kh],
+                           200)
+
+
+def test_oam_ties_keep_lowest_indices():
+    # zero keys and equal value norms: every score is the same
+    lens = np.array([5000], np.int32)
+    w = synth.workload("oam_128k", B=1, KH=1, lens=lens, seed=67)
+    q, k, v, g = synth.generate(w)
+    k[:] = 0
+    v[:] = synth.fill(1, synth.T_V, synth.dense_geometry(1, 1, 1, w.D))[0]  # first element pattern
+    v = np.ascontiguousarray(np.tile(v[:w.D], 5000))
+    log_case("oam ties")
+    idx, nk, sc = run_oam(w, q, k, v, g, 777)
+    assert np.all(sc[0, :5000] == sc[0, 0])
+    np.testing.assert_array_equal(idx[0, :777], np.arange(777))
+
+
+def test_oam_feeds_exact_attention_over_kept_tokens():
+    lens = np.array([6000, 2500, 300], np.int32)
+    w = synth.workload("oam_128k", B=3, KH=2, lens=lens, layout="token_major", seed=68)
+    q, k, v, g = synth.generate(w)
+    top_k = 512
+    log_case("oam -> indexed decode")
+    qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
+    kd, vd = to_dev(k), to_dev(v)
+    geom = dev_geom(g)
+    idx, nk = pkg.oam_score_topk(qd, kd, geom, w.G, top_k, v=vd)
+    out, _ = pkg.attn_decode_splitkv(qd, kd, vd, geom, w.G, token_idx=idx, n_idx=nk, split_tokens=256)
+    torch.cuda.synchronize()
+    idx_h, nk_h = idx.cpu().numpy(), nk.cpu().numpy()
+    p = problem(w, q, k, v, g, tok_idx=idx_h.reshape(-1), n_idx=nk_h, idx_stride=top_k)
+    ref, _ = oracle.attention_rows(p, oracle.all_rows(p), nthreads=8)
+    assert np.abs(out.cpu().numpy().reshape(-1, w.D) - ref).max() <= 2e-3
+
+
+def test_oam_128k_full_size():
+    """4 x 8 KV heads x 131072 tokens, keep 4096 per (b, kh), then exact attention."""
+    w = synth.workload("oam_128k")
+    q, k, v, g = synth.generate(w)
+    log_case("oam 128k full size")
+    idx, nk, sc = run_oam(w, q, k, v, g, w.top_k)
+    p = problem(w, q, k, v, g)
+    for pr in (0, 13, 31):
+        b, kh = divmod(pr, w.KH)
+        check_pair(oracle.oam_scores(p, b, kh, 1.0, 1e-6), sc[pr], idx[pr], nk[pr], w.top_k)
+    # every pair: exactness against its own fp32 scores
+    for pr in range(w.B * w.KH):
+        np.testing.assert_array_equal(idx[pr], exact_topk(sc[pr], w.top_k))
+    qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
+    out, _ = pkg.attn_decode_splitkv(qd, to_dev(k), to_dev(v), dev_geom(g), w.G, token_idx=to_dev(idx),
+                                     n_idx=to_dev(nk), split_tokens=w.split_tokens)
+    torch.cuda.synchronize()
+    pk = problem(w, q, k, v, g, tok_idx=idx.reshape(-1), n_idx=nk, idx_stride=w.top_k)
+    rows = [(0, 0), (1, 17), (2, 40), (3, 63)]
+    ref, _ = oracle.attention_rows(pk, rows, nthreads=4)
+    o = out.cpu().numpy().reshape(-1, w.D)[[b * w.QH + h for b, h in rows]]
+    assert np.abs(o - ref).max() <= 2e-3
