@@ -181,6 +181,49 @@ def bench_int8(pkg, torch, synth, steps, warmup, dev):
     return dict(ms=ms, decode_ms=dk, merge_ms=mg, worklist_ms=wl, kv_bytes=kvb)
 
 
+def bench_oam(pkg, torch, synth, steps, warmup, dev):
+    """OAM step: score + exact top-K over the cached value log-norms, then exact
+    attention over the kept tokens.  Also times the variant that reads V to get
+    the norms on the fly."""
+    w = synth.workload("oam_128k")
+    q, k, v, g = synth.generate(w, nthreads=host_threads())
+    geom = dev_geom(pkg, torch, g, dev)
+    qd = to_dev(torch, q.reshape(-1), dev).view(w.B, w.QH, w.D)
+    kd, vd = to_dev(torch, k, dev), to_dev(torch, v, dev)
+    del k, v
+    vlog = pkg.oam_value_lognorm(vd, geom, w.eps)          # computed when tokens are appended
+    sel = pkg.prepare_oam(qd, kd, geom, w.G, w.top_k, vlog=vlog, beta=w.beta, eps=w.eps)
+    sel_fly = pkg.prepare_oam(qd, kd, geom, w.G, w.top_k, v=vd, beta=w.beta, eps=w.eps)
+    att = pkg.prepare_decode(qd, kd, vd, geom, w.G, token_idx=sel.idx_out, n_idx=sel.n_kept,
+                             split_tokens=w.split_tokens)
+
+    def timed(fn_list, n):
+        for _ in range(warmup):
+            for f in fn_list:
+                f()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fn_list) + 1)] for _ in range(n)]
+        torch.cuda.synchronize()
+        for i in range(n):
+            evs[i][0].record()
+            for j, f in enumerate(fn_list):
+                f()
+                evs[i][j + 1].record()
+        torch.cuda.synchronize()
+        return [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / n for j in range(len(fn_list))]
+
+    t_sel, t_att = timed([sel, att], steps)
+    t_fly, = timed([sel_fly], max(3, steps // 2))
+    L, KH, D = int(w.lens[0]), w.KH, w.D
+    npairs = w.B * KH
+    algo = (npairs * L * D * 2 + npairs * L * 4 + 2 * npairs * L * 4 + 2 * npairs * w.top_k * D * 2
+            + npairs * w.top_k * 4)
+    ms = t_sel + t_att
+    return {"us_per_step": round(ms * 1e3, 2), "select_us": round(t_sel * 1e3, 2),
+            "kept_attention_us": round(t_att * 1e3, 2), "algorithmic_bytes_per_step": algo,
+            "gbs_algorithmic": round(algo / ms / 1e6, 1), "frac_of_peak": round(algo / ms / 1e6 / HBM_PEAK_GBS, 4),
+            "select_with_norms_from_v_us": round(t_fly * 1e3, 2), "top_k": w.top_k, "kv_len": L}
+
+
 def cpu_baseline(r, budget_s=10.0):
     """The fp64 oracle on host threads over whole (b, kh) pairs of the headline workload."""
     import numpy as np
@@ -216,6 +259,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--headline-only", action="store_true")
+    ap.add_argument("--others", default="gqa32k,ragged,int8,oam",
+                    help="comma-separated other workloads to time after the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run the library's plain copy kernel over this many MiB (counter calibration)")
@@ -274,18 +319,29 @@ def main():
     }
     if not args.headline_only:
         others = {}
-        r = bench_dense(pkg, torch, synth, "gqa32k", max(5, K // 2), W, dev)
-        others["gqa32k_bf16"] = summary(r)
-        del r
-        r = bench_dense(pkg, torch, synth, "ragged", max(5, K // 2), W, dev, split_tokens=512)
-        others["ragged_bf16"] = summary(r, {"total_kv_tokens_per_head": r["tokens"],
-                                             "lens_min": int(r["w"].lens.min()), "lens_max": int(r["w"].lens.max())})
-        del r
-        try:
-            r = bench_int8(pkg, torch, synth, max(5, K // 2), W, dev)
-            others["int8_128k"] = summary(r)
-        except pkg.AttnError as e:
-            others["int8_128k"] = {"error": str(e)}
+        todo = set(x.strip() for x in args.others.split(",") if x.strip())
+        if "gqa32k" in todo:
+            r = bench_dense(pkg, torch, synth, "gqa32k", max(5, K // 2), W, dev)
+            others["gqa32k_bf16"] = summary(r)
+            del r
+        if "ragged" in todo:
+            r = bench_dense(pkg, torch, synth, "ragged", max(5, K // 2), W, dev, split_tokens=512)
+            others["ragged_bf16"] = summary(r, {"total_kv_tokens_per_head": r["tokens"],
+                                                 "lens_min": int(r["w"].lens.min()),
+                                                 "lens_max": int(r["w"].lens.max())})
+            del r
+        if "int8" in todo:
+            try:
+                r = bench_int8(pkg, torch, synth, max(5, K // 2), W, dev)
+                others["int8_128k"] = summary(r)
+            except pkg.AttnError as e:
+                others["int8_128k"] = {"error": str(e)}
+        if "oam" in todo:
+            try:
+                others["oam_128k"] = bench_oam(pkg, torch, synth, max(5, K // 2), W, dev)
+                others["oam_128k"]["speedup_vs_dense_128k"] = round(ms * 1e3 / others["oam_128k"]["us_per_step"], 3)
+            except pkg.AttnError as e:
+                others["oam_128k"] = {"error": str(e)}
         line["other_workloads"] = others
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

@@ -75,7 +75,7 @@ attn_status oam_value_lognorm(const attn_kv_geom *geom, const void *v_bf16, floa
 namespace {
 
 struct OamLayout {
-  size_t scores, vlog, hist, counts, total;
+  size_t scores, vlog, hist, counts, offsets, state, total;
   int32_t nblk;
 };
 
@@ -111,6 +111,8 @@ attn_status plan_oam(const oam_topk_args *a, OamLayout *L) {
   L->vlog = off; off = al(off + (a->vlog ? 0 : npairs * stride * sizeof(float)));
   L->hist = off; off = al(off + (size_t)3 * npairs * 2048 * sizeof(uint32_t));
   L->counts = off; off = al(off + (size_t)npairs * (L->nblk > 0 ? L->nblk : 1) * 2 * sizeof(int32_t));
+  L->offsets = off; off = al(off + (size_t)npairs * (L->nblk > 0 ? L->nblk : 1) * 2 * sizeof(int32_t));
+  L->state = off; off = al(off + (size_t)npairs * 4 * sizeof(int32_t));
   L->total = off;
   return ATTN_OK;
 }
@@ -144,6 +146,8 @@ attn_status oam_score_topk(const oam_topk_args *a, attn_stream_t stream) {
   plan.vlog_stride = a->vlog ? a->vlog_stride : a->kv.max_seq_len;
   plan.hist = reinterpret_cast<uint32_t *>(ws + L.hist);
   plan.chunk_cnt = reinterpret_cast<int32_t *>(ws + L.counts);
+  plan.offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
+  plan.state = reinterpret_cast<int32_t *>(ws + L.state);
   plan.nchunk = L.nblk;
   hipError_t e = launch_oam(*a, plan, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : api_fail_hip(e, "oam launch");

@@ -109,6 +109,8 @@ struct OamPlan {
   int32_t vlog_stride;
   uint32_t *hist;        // [3][npairs][2048]
   int32_t *chunk_cnt;    // [npairs][nchunk][2]
+  int32_t *offsets;      // [npairs][nchunk][2]
+  int32_t *state;        // [npairs][4]
   int32_t nchunk;        // selection blocks per pair
 };
 hipError_t launch_oam(const oam_topk_args &a, const OamPlan &plan, hipStream_t s);

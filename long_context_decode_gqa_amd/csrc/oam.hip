@@ -40,7 +40,9 @@ struct OamDev {
   float score_scale, beta;
   float *scores;       // [npairs][L_max]
   uint32_t *hist;      // [3][npairs][kBins]
-  int32_t *counts;     // [npairs][nblk][2]
+  int32_t *counts;     // [npairs][nblk][2]  per block: keys > T, keys == T
+  int32_t *offsets;    // [npairs][nblk][2]  per block: kept before it, equal-to-T before it
+  int32_t *state;      // [npairs][4]        prefix, need, keep_all
   int32_t *idx_out;    // [npairs][top_k]
   int32_t *n_kept;     // [npairs]
 };
@@ -108,55 +110,128 @@ struct Thresh {
   bool keep_all;
 };
 
-__device__ Thresh resolve(const OamDev &o, int pair, int levels, int *s_tmp, int *s_res) {
+__device__ __forceinline__ Thresh load_state(const OamDev &o, int pair) {
+  const int32_t *st = o.state + 4 * pair;
   Thresh th;
-  const int L = pair_len(o, pair);
-  th.keep_all = o.top_k >= L;
-  th.prefix = 0;
-  th.need = min(o.top_k, L);
-  if (th.keep_all) return th;
-  const int npairs = o.B * o.KH;
-  for (int lev = 0; lev < levels; ++lev) {
-    const uint32_t *h = o.hist + ((size_t)lev * npairs + pair) * kBins;
-    const int nb = lev == 2 ? 1024 : kBins;
-    int above;
-    const int bin = select_bin(h, nb, th.need, &above, s_tmp, s_res);
-    th.need -= above;
-    th.prefix = lev == 0 ? (uint32_t)bin : (lev == 1 ? (th.prefix << 11) | bin : (th.prefix << 10) | bin);
-  }
+  th.prefix = (uint32_t)st[0];
+  th.need = st[1];
+  th.keep_all = st[2] != 0;
   return th;
+}
+
+// One workgroup per pair: fold histogram level LEVEL into the pair's
+// threshold state (level 0 also initialises it).
+template <int LEVEL>
+__global__ __launch_bounds__(256) void oam_resolve_kernel(OamDev o) {
+  __shared__ int s_tmp[4], s_res[2];
+  const int pair = blockIdx.x;
+  Thresh th;
+  if (LEVEL == 0) {
+    const int L = pair_len(o, pair);
+    th.keep_all = o.top_k >= L;
+    th.prefix = 0;
+    th.need = min(o.top_k, L);
+  } else {
+    th = load_state(o, pair);
+  }
+  if (!th.keep_all) {
+    const int npairs = o.B * o.KH;
+    const uint32_t *h = o.hist + ((size_t)LEVEL * npairs + pair) * kBins;
+    int above;
+    const int bin = select_bin(h, LEVEL == 2 ? 1024 : kBins, th.need, &above, s_tmp, s_res);
+    th.need -= above;
+    th.prefix = LEVEL == 0 ? (uint32_t)bin : (LEVEL == 1 ? (th.prefix << 11) | bin : (th.prefix << 10) | bin);
+  }
+  if (threadIdx.x == 0) {
+    int32_t *st = o.state + 4 * pair;
+    st[0] = (int32_t)th.prefix;
+    st[1] = th.need;
+    st[2] = th.keep_all ? 1 : 0;
+  }
+}
+
+// One workgroup per pair: exclusive prefix over its blocks of (kept, equal)
+// counts, so each write block knows where its indices start.
+__global__ __launch_bounds__(256) void oam_offsets_kernel(OamDev o) {
+  __shared__ int s_tmp[4];
+  const int pair = blockIdx.x;
+  const Thresh th = load_state(o, pair);
+  const int32_t *cnt = o.counts + (int64_t)pair * o.nblk * 2;
+  int32_t *off = o.offsets + (int64_t)pair * o.nblk * 2;
+  int run_k = 0, run_e = 0;
+  for (int j0 = 0; j0 < o.nblk; j0 += 256) {
+    const int j = j0 + threadIdx.x;
+    const int g = j < o.nblk ? cnt[2 * j] : 0, e = j < o.nblk ? cnt[2 * j + 1] : 0;
+    int te, tk;
+    const int e_before = run_e + block_exclusive_scan(e, s_tmp, &te);
+    const int take = th.keep_all ? 0 : min(e, max(0, th.need - e_before));
+    const int k_before = run_k + block_exclusive_scan(g + take, s_tmp, &tk);
+    if (j < o.nblk) {
+      off[2 * j] = k_before;
+      off[2 * j + 1] = e_before;
+    }
+    run_k += tk;
+    run_e += te;
+  }
 }
 
 __global__ __launch_bounds__(256) void zero_kernel(uint32_t *p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
 }
 
-// Score pass.  Wave w of the workgroup takes tiles [16w, 16w+16) of the
-// block's 64 tiles of 32 tokens (contiguous rows, two loads in flight); the
-// 16x16x32 MFMA gives S[t][g] (lane (c, n) holds tokens 4c..4c+3 of head n)
-// and a 16-lane sum reduces over the heads.
+// Score pass.  The mean query of the KV head's G heads, q_bar (fp32), is
+// split into three bf16 parts hi + mid + lo (24 significant bits) placed in
+// B-operand columns 4j, 4j+1, 4j+2 (column 4j+3 is zero), so one 16x16x32
+// MFMA chain per 16 tokens gives, in every lane quad, the three partial dot
+// products of its four tokens; two quad DPP adds finish q_bar . k_t.  Wave w
+// of the workgroup streams tiles [16w', 16w'+16) of 32 tokens, two in flight.
+constexpr int kScoreTok = 8192;   // tokens per workgroup of the score pass
+
+__device__ __forceinline__ float quad_sum3(float v) {
+  // lane 4j gets v(4j) + v(4j+1) + v(4j+2); quad_perm(1,2,3,0) = 0x39, (2,3,0,1) = 0x4E
+  const float a = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x39, 0xF, 0xF, true));
+  const float b = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+  return v + a + b;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
   constexpr int KB = D / 32;
+  constexpr int kTilesPerWave = kScoreTok / 32 / 4;
   __shared__ uint32_t s_hist[kBins];
+  __shared__ float s_qbar[D];
   const int pair = blockIdx.y;
   const int L = pair_len(o, pair);
-  const int blk0 = blockIdx.x * kBlockTok;
+  const int blk0 = blockIdx.x * kScoreTok;
   if (blk0 >= L) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, cg = lane >> 4;
   for (int i = tid; i < kBins; i += 256) s_hist[i] = 0u;
   const int b = pair / o.KH, kh = pair - b * o.KH;
-  const bool qvalid = col < o.G;
-
+  // mean query of the group, in fp32
+  for (int d = tid; d < D; d += 256) {
+    const uint16_t *q0 = o.q + ((int64_t)b * o.QH + (int64_t)kh * o.G) * D + d;
+    float acc = 0.f;
+    for (int g = 0; g < o.G; ++g) acc += bf16_bits_to_f32(q0[(int64_t)g * D]);
+    s_qbar[d] = acc / (float)o.G;
+  }
+  __syncthreads();
   bf16x8_t qop[KB];
   {
-    const uint16_t *qrow = o.q + ((int64_t)b * o.QH + (int64_t)kh * o.G + (qvalid ? col : 0)) * D;
+    const int part = col & 3;  // 0: hi, 1: mid, 2: lo, 3: zero
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      u32x4_t w = *(const u32x4_t *)(qrow + 8 * (4 * kb + cg));
-      if (!qvalid) w = (u32x4_t){0u, 0u, 0u, 0u};
-      qop[kb] = __builtin_bit_cast(bf16x8_t, w);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = s_qbar[8 * (4 * kb + cg) + j];
+        const uint32_t hb = f32_to_bf16_bits(x);
+        const float r1 = x - __uint_as_float(hb << 16);
+        const uint32_t mb = f32_to_bf16_bits(r1);
+        const float r2 = r1 - __uint_as_float(mb << 16);
+        const uint32_t lb = f32_to_bf16_bits(r2);
+        const uint32_t sel = part == 0 ? hb : part == 1 ? mb : part == 2 ? lb : 0u;
+        qop[kb][j] = __builtin_bit_cast(__bf16, (uint16_t)sel);
+      }
     }
   }
   const int64_t head_off = o.seq_offset[b] + (int64_t)kh * o.stride_h;
@@ -166,16 +241,22 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
       __builtin_amdgcn_make_buffer_rsrc((void *)(o.k + head_off), (short)0, nrec, 0x00020000);
   const float *vl = o.vlog + (int64_t)pair * o.vlog_stride;
   float *sc = o.scores + (int64_t)pair * o.L_max;
-  __syncthreads();
-
-  typedef u32x4_t KTile[2][KB];
-  auto load = [&](KTile &R, int tile) {
+  // the value term of the lane's four tokens is fetched with the tile (a
+  // load issued later would make the compiler wait for the prefetch too)
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vl, (short)0, L * 4, 0x00020000);
+  struct KTile {
+    u32x4_t k[2][KB];
+    u32x4_t vl[2];
+  };
+  auto load = [&](KTile &R, int tile, bool valid) {
     const int t0 = blk0 + 32 * tile;
+    const uint32_t oob = valid ? 0u : 0x80000000u;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      const uint32_t off = (uint32_t)(t0 + 16 * tb + col) * rs + 16 * cg;
+      const uint32_t off = ((uint32_t)(t0 + 16 * tb + col) * rs + 16 * cg) | oob;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) R[tb][kb] = __builtin_amdgcn_raw_buffer_load_b128(krs, off + 64 * kb, 0, 0);
+      for (int kb = 0; kb < KB; ++kb) R.k[tb][kb] = __builtin_amdgcn_raw_buffer_load_b128(krs, off + 64 * kb, 0, 0);
+      R.vl[tb] = __builtin_amdgcn_raw_buffer_load_b128(vrs, ((uint32_t)(t0 + 16 * tb + 4 * cg) * 4) | oob, 0, 0);
     }
   };
   auto compute = [&](const KTile &R, int tile) {
@@ -185,22 +266,15 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, R[tb][kb]), qop[kb], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, R.k[tb][kb]), qop[kb], acc, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = acc[i];
-        v += __shfl_xor(v, 1);
-        v += __shfl_xor(v, 2);
-        v += __shfl_xor(v, 4);
-        v += __shfl_xor(v, 8);
-        acc[i] = v;
-      }
+      for (int i = 0; i < 4; ++i) acc[i] = quad_sum3(acc[i]);
       const int t = t0 + 16 * tb + 4 * cg;
       if (col == 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if (t + i < L) {
-            const float s = acc[i] * o.score_scale + o.beta * vl[t + i];
+            const float s = acc[i] * o.score_scale + o.beta * __uint_as_float(R.vl[tb][i]);
             sc[t + i] = s;
             atomicAdd(&s_hist[order_key(s) >> 21], 1u);
           }
@@ -208,14 +282,16 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
       }
     }
   };
+  // this wave's tiles, stopping at the end of the sequence
+  const int tw0 = kTilesPerWave * wave;
+  const int ntw = max(0, min(kTilesPerWave, (L - blk0 - 32 * tw0 + 31) / 32));
   KTile ra, rb;
-  const int tw0 = 16 * wave;
-  load(ra, tw0);
-  for (int i = 0; i < 16; i += 2) {
-    load(rb, tw0 + i + 1);
+  load(ra, tw0, ntw > 0);
+  for (int i = 0; i < ntw; i += 2) {
+    load(rb, tw0 + i + 1, i + 1 < ntw);
     compute(ra, tw0 + i);
-    load(ra, i + 2 < 16 ? tw0 + i + 2 : tw0);
-    compute(rb, tw0 + i + 1);
+    load(ra, tw0 + i + 2, i + 2 < ntw);
+    if (i + 1 < ntw) compute(rb, tw0 + i + 1);
   }
   __syncthreads();
   uint32_t *gh = o.hist + (size_t)pair * kBins;
@@ -227,12 +303,11 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
 template <int LEVEL>
 __global__ __launch_bounds__(256) void oam_hist_kernel(OamDev o) {
   __shared__ uint32_t s_hist[kBins];
-  __shared__ int s_tmp[4], s_res[2];
   const int pair = blockIdx.y;
   const int L = pair_len(o, pair);
   const int blk0 = blockIdx.x * kBlockTok;
   if (blk0 >= L) return;
-  const Thresh th = resolve(o, pair, LEVEL, s_tmp, s_res);
+  const Thresh th = load_state(o, pair);
   if (th.keep_all) return;
   const int tid = threadIdx.x;
   for (int i = tid; i < kBins; i += 256) s_hist[i] = 0u;
@@ -256,12 +331,19 @@ __global__ __launch_bounds__(256) void oam_hist_kernel(OamDev o) {
 
 // Keys above the threshold and keys equal to it, per block.
 __global__ __launch_bounds__(256) void oam_count_kernel(OamDev o) {
-  __shared__ int s_tmp[4], s_res[2];
+  __shared__ int s_tmp[4];
   const int pair = blockIdx.y;
   const int L = pair_len(o, pair);
   const int blk0 = blockIdx.x * kBlockTok;
-  if (blk0 >= L) return;
-  const Thresh th = resolve(o, pair, 3, s_tmp, s_res);
+  if (blk0 >= L) {
+    if (threadIdx.x == 0) {
+      int32_t *c = o.counts + ((int64_t)pair * o.nblk + blockIdx.x) * 2;
+      c[0] = 0;
+      c[1] = 0;
+    }
+    return;
+  }
+  const Thresh th = load_state(o, pair);
   const int tid = threadIdx.x;
   const float *sc = o.scores + (int64_t)pair * o.L_max;
   const int n = min(kBlockTok, L - blk0);
@@ -285,7 +367,7 @@ __global__ __launch_bounds__(256) void oam_count_kernel(OamDev o) {
 
 // Ordered compaction: thread i of a block owns tokens 8i..8i+7 of it.
 __global__ __launch_bounds__(256) void oam_write_kernel(OamDev o) {
-  __shared__ int s_tmp[4], s_res[2];
+  __shared__ int s_tmp[4];
   const int pair = blockIdx.y;
   const int L = pair_len(o, pair);
   const int tid = threadIdx.x;
@@ -297,16 +379,10 @@ __global__ __launch_bounds__(256) void oam_write_kernel(OamDev o) {
   }
   const int blk0 = blockIdx.x * kBlockTok;
   if (blk0 >= L) return;
-  const Thresh th = resolve(o, pair, 3, s_tmp, s_res);
+  const Thresh th = load_state(o, pair);
   // kept and equal-to-threshold tokens in the blocks before this one
-  int kept_before = 0, eq_before = 0;
-  const int32_t *cnt = o.counts + (int64_t)pair * o.nblk * 2;
-  for (int j = 0; j < (int)blockIdx.x; ++j) {
-    const int g = cnt[2 * j], e = cnt[2 * j + 1];
-    const int take = th.keep_all ? 0 : min(e, max(0, th.need - eq_before));
-    kept_before += g + take;
-    eq_before += e;
-  }
+  const int32_t *off = o.offsets + ((int64_t)pair * o.nblk + blockIdx.x) * 2;
+  const int kept_before = off[0], eq_before = off[1];
   const float *sc = o.scores + (int64_t)pair * o.L_max;
   const int n = min(kBlockTok, L - blk0);
   uint32_t keys[8];
@@ -368,12 +444,13 @@ hipError_t launch_oam(const oam_topk_args &a, const OamPlan &plan, hipStream_t s
   o.vlog = plan.vlog;
   o.vlog_stride = plan.vlog_stride;
   o.L_max = plan.score_stride;
-  const float ss = a.softmax_scale != 0.f ? a.softmax_scale : 1.0f / sqrtf((float)g.D);
-  o.score_scale = ss / (float)a.G;
+  o.score_scale = a.softmax_scale != 0.f ? a.softmax_scale : 1.0f / sqrtf((float)g.D);
   o.beta = a.beta;
   o.scores = plan.scores;
   o.hist = plan.hist;
   o.counts = plan.chunk_cnt;
+  o.offsets = plan.offsets;
+  o.state = plan.state;
   o.idx_out = a.idx_out;
   o.n_kept = a.n_kept;
 
@@ -386,18 +463,29 @@ hipError_t launch_oam(const oam_topk_args &a, const OamPlan &plan, hipStream_t s
     e = launch_value_lognorm(g, a.v, a.eps, plan.vlog, plan.vlog_stride, s);
     if (e != hipSuccess) return e;
   }
-  dim3 grid(plan.nchunk, npairs), blk(256);
+  dim3 grid(plan.nchunk, npairs), blk(256), pgrid(npairs);
+#define LCDG_CHECK_LAUNCH() if ((e = hipGetLastError()) != hipSuccess) return e
   if (plan.nchunk > 0) {
-    if (g.D == 128) hipLaunchKernelGGL((oam_score_kernel<128>), grid, blk, 0, s, o);
-    else hipLaunchKernelGGL((oam_score_kernel<64>), grid, blk, 0, s, o);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    dim3 sgrid((g.max_seq_len + kScoreTok - 1) / kScoreTok, npairs);
+    if (g.D == 128) hipLaunchKernelGGL((oam_score_kernel<128>), sgrid, blk, 0, s, o);
+    else hipLaunchKernelGGL((oam_score_kernel<64>), sgrid, blk, 0, s, o);
+    LCDG_CHECK_LAUNCH();
+    hipLaunchKernelGGL((oam_resolve_kernel<0>), pgrid, blk, 0, s, o);
+    LCDG_CHECK_LAUNCH();
     hipLaunchKernelGGL((oam_hist_kernel<1>), grid, blk, 0, s, o);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    LCDG_CHECK_LAUNCH();
+    hipLaunchKernelGGL((oam_resolve_kernel<1>), pgrid, blk, 0, s, o);
+    LCDG_CHECK_LAUNCH();
     hipLaunchKernelGGL((oam_hist_kernel<2>), grid, blk, 0, s, o);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    LCDG_CHECK_LAUNCH();
+    hipLaunchKernelGGL((oam_resolve_kernel<2>), pgrid, blk, 0, s, o);
+    LCDG_CHECK_LAUNCH();
     hipLaunchKernelGGL(oam_count_kernel, grid, blk, 0, s, o);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    LCDG_CHECK_LAUNCH();
+    hipLaunchKernelGGL(oam_offsets_kernel, pgrid, blk, 0, s, o);
+    LCDG_CHECK_LAUNCH();
   }
+#undef LCDG_CHECK_LAUNCH
   // the write pass also runs for empty caches: it sets n_kept and the -1 fill
   dim3 wgrid(plan.nchunk > 0 ? plan.nchunk : 1, npairs);
   hipLaunchKernelGGL(oam_write_kernel, wgrid, blk, 0, s, o);

@@ -78,23 +78,30 @@ __global__ void zero_word_kernel(uint32_t *w) { *w = 0u; }
 
 constexpr int kRowsPerBlock = 64;
 
-// Per-tensor max |x|: workgroup maxima combined with an integer atomic max on
-// the fp32 bit pattern (non-negative floats order like their bit patterns).
+// Per-tensor max |x|: a grid-stride pass over every valid row of every
+// (b, kh); workgroup maxima are combined with an integer atomic max on the
+// fp32 bit pattern (non-negative floats order like their bit patterns).  The
+// grid is bounded so the atomic is taken once per workgroup, a few thousand times.
 __global__ __launch_bounds__(256) void tensor_absmax_kernel(attn_kv_geom g, const uint16_t *x, uint32_t *ws) {
   __shared__ float s_red[4];
-  const int pair = blockIdx.y;
-  const int b = pair / g.KH, kh = pair - b * g.KH;
-  const int L = min(max(g.seq_lens[b], 0), g.max_seq_len);
-  const int t0 = blockIdx.x * kRowsPerBlock;
-  if (t0 >= L) return;
-  const int t1 = min(L, t0 + kRowsPerBlock);
   const int cpr = g.D / 8;
-  const int n = (t1 - t0) * cpr;
-  const int64_t base = g.seq_offset[b] + (int64_t)kh * g.stride_h;
+  const int npairs = g.B * g.KH;
+  const int nblk_t = (g.max_seq_len + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int64_t units = (int64_t)npairs * nblk_t;
   float m = 0.f;
-  for (int i = threadIdx.x; i < n; i += 256) {
-    const int t = t0 + i / cpr, c = i - (i / cpr) * cpr;
-    m = fmaxf(m, absmax8(*(const u32x4_t *)(x + base + (int64_t)t * g.stride_t + 8 * c)));
+  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+    const int pair = (int)(u / nblk_t);
+    const int t0 = (int)(u - (int64_t)pair * nblk_t) * kRowsPerBlock;
+    const int b = pair / g.KH, kh = pair - b * g.KH;
+    const int L = min(max(g.seq_lens[b], 0), g.max_seq_len);
+    if (t0 >= L) continue;
+    const int t1 = min(L, t0 + kRowsPerBlock);
+    const int n = (t1 - t0) * cpr;
+    const int64_t base = g.seq_offset[b] + (int64_t)kh * g.stride_h;
+    for (int i = threadIdx.x; i < n; i += 256) {
+      const int t = t0 + i / cpr, c = i - (i / cpr) * cpr;
+      m = fmaxf(m, absmax8(*(const u32x4_t *)(x + base + (int64_t)t * g.stride_t + 8 * c)));
+    }
   }
   m = block_max(m, s_red);
   if (threadIdx.x == 0) atomicMax(ws, __float_as_uint(m));
@@ -165,7 +172,9 @@ hipError_t launch_quant_tensor(const attn_kv_geom &g, const void *x, int8_t *cod
   const int nblk = (g.max_seq_len + kRowsPerBlock - 1) / kRowsPerBlock;
   if (g.B > 0 && nblk > 0) {
     dim3 grid(nblk, g.B * g.KH);
-    hipLaunchKernelGGL(tensor_absmax_kernel, grid, dim3(256), 0, s, g, (const uint16_t *)x, ws);
+    const int64_t units = (int64_t)nblk * g.B * g.KH;
+    hipLaunchKernelGGL(tensor_absmax_kernel, dim3((unsigned)(units < 2048 ? units : 2048)), dim3(256), 0, s, g,
+                       (const uint16_t *)x, ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(tensor_codes_kernel, grid, dim3(256), 0, s, g, (const uint16_t *)x, ws, codes);
     if ((e = hipGetLastError()) != hipSuccess) return e;

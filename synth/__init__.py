@@ -243,7 +243,7 @@ def workload(name: str, **over) -> Workload:
         w = Workload("int8_128k", 4, 8, 8, 128, 4, "bf16", np.full(4, 131072, np.int32), outliers=2)
     elif name == "oam_128k":
         w = Workload("oam_128k", 4, 8, 8, 128, 5, "bf16", np.full(4, 131072, np.int32),
-                     v_kind=UNIT_DIR_LOGNORMAL, top_k=4096, split_tokens=512)
+                     v_kind=UNIT_DIR_LOGNORMAL, top_k=4096, split_tokens=128)
     elif name == "dense128k":
         w = Workload("dense128k", 4, 8, 8, 128, 6, "bf16", np.full(4, 131072, np.int32))
     else:
