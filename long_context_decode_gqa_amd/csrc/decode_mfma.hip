@@ -79,6 +79,18 @@ struct Tile {
   float ks[NS > 0 ? NS : 1];
 };
 
+// A pipeline step: TPS consecutive tiles, as many as fit a per-buffer
+// register budget (64 VGPRs for bf16; 32 for int8, whose dequantisation needs
+// more temporaries), so small tiles still keep more bytes in flight.
+template <int D, int KVT, bool IDX>
+struct Step {
+  typedef Tile<D, KVT, IDX> TileT;
+  static constexpr int kRegs = 2 * TileT::KL * 4 + 8 * TileT::VW;
+  static constexpr int kBudget = KVT == ATTN_BF16 ? 64 : 32;
+  static constexpr int TPS = kRegs >= kBudget ? 1 : kBudget / kRegs;
+  TileT t[TPS];
+};
+
 // Tokens per chunk of the indexed variant (its index list is staged in LDS).
 constexpr int kMaxIdxChunk = 1024;
 
@@ -92,6 +104,8 @@ constexpr int kMaxIdxChunk = 1024;
 template <int D, int KVT, bool IDX>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_mfma_kernel(DecodeParams p) {
   typedef Tile<D, KVT, IDX> TileT;
+  typedef Step<D, KVT, IDX> StepT;
+  constexpr int TPS = StepT::TPS;
   constexpr int NB = D / 16;
   constexpr int ES = TileT::ES;
   constexpr int KL = TileT::KL;
@@ -218,6 +232,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       }
     };
 
+    // a step = tiles tile0 .. tile0+TPS-1, each valid while below `limit`
+    auto load_step = [&](StepT &S, int tile0, int limit) {
+#pragma unroll
+      for (int j = 0; j < TPS; ++j) load_tile(S.t[j], tile0 + j, tile0 + j < limit);
+    };
+
     f32x4_t O[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) O[nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
@@ -310,13 +330,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       }
     };
 
+    auto compute_step = [&](const StepT &S, int tile0) {
+#pragma unroll
+      for (int j = 0; j < TPS; ++j) compute_tile(S.t[j], tile0 + j);
+    };
+
     // Segments: the run cut at chunk boundaries.  A segment takes an even
     // number of steps (the last may be empty), so the two register buffers
     // alternate statically, and its last step already prefetches the first
-    // tile of the next segment of the run.
-    TileT ra, rb;
+    // tiles of the next segment of the run.
+    StepT ra, rb;
     auto seg_end_of = [&](int s0) { return min(run_end, lane_t0 + ((s0 - lane_t0) / ct + 1) * ct); };
-    if constexpr (!IDX) load_tile(ra, t, true);
+    if constexpr (!IDX) load_step(ra, t, seg_end_of(t));
     for (int seg_t0 = t; seg_t0 < run_end;) {
       const int seg_t1 = seg_end_of(seg_t0);
       const int chunk = (seg_t0 - lane_t0) / ct;
@@ -328,21 +353,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         __syncthreads();
         for (int i = lane; i < seg_pos1 - seg_pos0; i += 64) s_idx[i] = min(max(src[seg_pos0 + i], 0), L - 1);
         __syncthreads();
-        load_tile(ra, seg_t0, true);
+        load_step(ra, seg_t0, seg_t1);
       }
-      const int steps = (seg_t1 - seg_t0 + 1) & ~1;
+      const int nsteps = (seg_t1 - seg_t0 + TPS - 1) / TPS;
+      const int steps = (nsteps + 1) & ~1;
       const int next_t1 = seg_end_of(seg_t1);
       for (int i = 0; i < steps; i += 2) {
-        const int ta = seg_t0 + i;
-        load_tile(rb, ta + 1, ta + 1 < seg_t1);
-        compute_tile(ra, ta);
+        const int ta = seg_t0 + i * TPS;
+        load_step(rb, ta + TPS, seg_t1);
+        compute_step(ra, ta);
         // next step of this segment, or (last step) the next segment's first
-        // tile in this run; one load site so both share the same registers
+        // tiles in this run; one load site so both share the same registers
         const bool in_seg = i + 2 < steps;
-        const int tn = in_seg ? ta + 2 : seg_t1;
-        const bool vn = in_seg ? tn < seg_t1 : (!IDX && tn < next_t1);
-        load_tile(ra, vn ? tn : seg_t0, vn);
-        compute_tile(rb, ta + 1);
+        const int tn = in_seg ? ta + 2 * TPS : seg_t1;
+        const int lim = in_seg ? seg_t1 : (IDX ? 0 : next_t1);
+        load_step(ra, tn < lim ? tn : seg_t0, tn < lim ? lim : 0);
+        compute_step(rb, ta + TPS);
       }
 
       // Partial of this segment, straight from registers.  Lane (col, cg)

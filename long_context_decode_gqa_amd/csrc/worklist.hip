@@ -90,17 +90,41 @@ __device__ __forceinline__ float block_reduce(float v, float *s_red, bool is_max
   return r;
 }
 
+// Exclusive scan of one int per thread over the merge workgroup.
+__device__ __forceinline__ int merge_scan(int v, int *s_red, int *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int x = __shfl_up(incl, o);
+    if (lane >= o) incl += x;
+  }
+  __syncthreads();
+  if (lane == 63) s_red[wave] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int w = 0; w < kMergeThreads / 64; ++w) {
+    if (w < wave) base += s_red[w];
+    tot += s_red[w];
+  }
+  *total = tot;
+  return base + incl - v;
+}
+
 // Log-sum-exp merge of partial triples, one workgroup per output row:
 // M = max m_i, w_i = exp(m_i - M) l_i, out = sum w_i o_i / sum w_i,
-// lse = M + ln(sum w_i).  The row's partials are spread over thread groups
-// (each group sums a strided subset, then the groups are added in a fixed
-// order), so the result is deterministic.
+// lse = M + ln(sum w_i).  The row's non-empty partials are compacted into an
+// LDS list (batches of 512), then spread over thread groups that each sum a
+// strided subset with branch-free loads; the groups are added in a fixed
+// order, so the result is deterministic.
 template <int OUT>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *o_part, const float *m_part,
                                                               const float *l_part, const int32_t *rss, int32_t rows,
                                                               int32_t D, void *out, float *lse) {
   __shared__ float s_red[kMergeThreads / 64];
+  __shared__ int s_cnt[kMergeThreads / 64];
   __shared__ float s_w[kMergeWeights];
+  __shared__ int s_sl[kMergeWeights];
   __shared__ float s_acc[kMergeThreads * 4];
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
@@ -110,41 +134,43 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *o_par
   for (int i = tid; i < n; i += kMergeThreads)
     if (l_part[s0 + i] > 0.f) M = fmaxf(M, m_part[s0 + i]);
   M = block_reduce(M, s_red, true);
-  float Ls = 0.f;
-  for (int i = tid; i < n; i += kMergeThreads) {
-    const float l = l_part[s0 + i];
-    const float w = (l > 0.f) ? expf(m_part[s0 + i] - M) * l : 0.f;
-    if (i < kMergeWeights) s_w[i] = w;
-    Ls += w;
-  }
-  Ls = block_reduce(Ls, s_red, false);
-  __syncthreads();
-  auto weight = [&](int i) -> float {
-    if (i < kMergeWeights) return s_w[i];
-    const float l = l_part[s0 + i];
-    return (l > 0.f) ? expf(m_part[s0 + i] - M) * l : 0.f;
-  };
+
   const bool vec = (D & 3) == 0;
   const int nq = vec ? D / 4 : D;            // columns handled per group
   const int ngrp = kMergeThreads / nq;
   const int grp = tid / nq, q = tid - grp * nq;
-  if (grp < ngrp) {
-    if (vec) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-      for (int i = grp; i < n; i += ngrp) {
-        const float w = weight(i);
-        if (w > 0.f) acc += w * *(const f32x4_t *)(o_part + (int64_t)(s0 + i) * D + 4 * q);
-      }
-      *(f32x4_t *)(s_acc + grp * D + 4 * q) = acc;
-    } else {
-      float acc = 0.f;
-      for (int i = grp; i < n; i += ngrp) {
-        const float w = weight(i);
-        if (w > 0.f) acc += w * o_part[(int64_t)(s0 + i) * D + q];
-      }
-      s_acc[grp * D + q] = acc;
+  f32x4_t acc4 = {0.f, 0.f, 0.f, 0.f};
+  float acc1 = 0.f, Lpart = 0.f;
+  for (int base = 0; base < n; base += kMergeWeights) {
+    const int i = base + tid;
+    float w = 0.f;
+    if (i < n) {
+      const float l = l_part[s0 + i];
+      if (l > 0.f) w = expf(m_part[s0 + i] - M) * l;
     }
+    Lpart += w;
+    int cnt;
+    const int pos = merge_scan(w > 0.f ? 1 : 0, s_cnt, &cnt);
+    if (w > 0.f) {
+      s_w[pos] = w;
+      s_sl[pos] = s0 + i;
+    }
+    __syncthreads();
+    if (grp < ngrp) {
+      if (vec) {
+#pragma unroll 4
+        for (int k = grp; k < cnt; k += ngrp)
+          acc4 += s_w[k] * *(const f32x4_t *)(o_part + (int64_t)s_sl[k] * D + 4 * q);
+      } else {
+        for (int k = grp; k < cnt; k += ngrp) acc1 += s_w[k] * o_part[(int64_t)s_sl[k] * D + q];
+      }
+    }
+    __syncthreads();
+  }
+  const float Ls = block_reduce(Lpart, s_red, false);
+  if (grp < ngrp) {
+    if (vec) *(f32x4_t *)(s_acc + grp * D + 4 * q) = acc4;
+    else s_acc[grp * D + q] = acc1;
   }
   __syncthreads();
   for (int d = tid; d < D; d += kMergeThreads) {
