@@ -96,7 +96,7 @@ class Timer:
         self.torch = torch
         self.start = torch.cuda.Event(enable_timing=True)
         self.end = torch.cuda.Event(enable_timing=True)
-        self.phase = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        self.phase = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
         for evs in self.phase:          # materialise the events so their handles exist
             for e in evs:
                 e.record()
@@ -127,10 +127,9 @@ def time_decode(torch, prepared, steps, warmup):
     t.end.record()
     torch.cuda.synchronize()
     total = t.start.elapsed_time(t.end)
-    wl = sum(e[0].elapsed_time(e[1]) for e in t.phase) / steps
-    dk = sum(e[1].elapsed_time(e[2]) for e in t.phase) / steps
-    mg = sum(e[2].elapsed_time(e[3]) for e in t.phase) / steps
-    return total / steps, dk, mg, wl
+    dk = sum(e[0].elapsed_time(e[1]) for e in t.phase) / steps
+    mg = sum(e[1].elapsed_time(e[2]) for e in t.phase) / steps
+    return total / steps, dk, mg
 
 
 # ------------------------------------------------------------------ workloads
@@ -143,20 +142,19 @@ def bench_dense(pkg, torch, synth, name, steps, warmup, dev, **over):
     del k, v
     geom = dev_geom(pkg, torch, g, dev)
     p = pkg.prepare_decode(qd, kd, vd, geom, w.G, split_tokens=w.split_tokens)
-    ms, dk, mg, wl = time_decode(torch, p, steps, warmup)
+    ms, dk, mg = time_decode(torch, p, steps, warmup)
     tokens = w.kv_tokens()
     kvb = kv_bytes(tokens, w.KH, w.D, 2)
     nparts = w.QH * sum(-(-int(L) // w.split_tokens) for L in w.lens)
     algo = kvb + w.B * w.QH * w.D * 2 + partial_bytes(nparts, w.D)
-    return dict(w=w, q=q, g=g, ms=ms, decode_ms=dk, merge_ms=mg, worklist_ms=wl, kv_bytes=kvb,
+    return dict(w=w, q=q, g=g, ms=ms, decode_ms=dk, merge_ms=mg, kv_bytes=kvb,
                 decode_algo_bytes=algo, tokens=tokens)
 
 
 def summary(r, extra=None):
     d = {"us_per_step": round(r["ms"] * 1e3, 2), "kv_gbs": round(r["kv_bytes"] / r["ms"] / 1e6, 1),
          "frac_of_peak": round(r["kv_bytes"] / r["ms"] / 1e6 / HBM_PEAK_GBS, 4),
-         "decode_kernel_us": round(r["decode_ms"] * 1e3, 2), "merge_us": round(r["merge_ms"] * 1e3, 2),
-         "worklist_us": round(r["worklist_ms"] * 1e3, 2)}
+         "decode_kernel_us": round(r["decode_ms"] * 1e3, 2), "merge_us": round(r["merge_ms"] * 1e3, 2)}
     if extra:
         d.update(extra)
     return d
@@ -175,10 +173,10 @@ def bench_int8(pkg, torch, synth, steps, warmup, dev):
     qd = to_dev(torch, q.reshape(-1), dev).view(w.B, w.QH, w.D)
     p = pkg.prepare_decode(qd, kc, vc, geom, w.G, k_scale=ks, k_part_tokens=64, v_scale=float(vs.item()),
                            split_tokens=w.split_tokens)
-    ms, dk, mg, wl = time_decode(torch, p, steps, warmup)
+    ms, dk, mg = time_decode(torch, p, steps, warmup)
     tokens = w.kv_tokens()
     kvb = kv_bytes(tokens, w.KH, w.D, 1) + ks.numel() * 4 + 4
-    return dict(ms=ms, decode_ms=dk, merge_ms=mg, worklist_ms=wl, kv_bytes=kvb)
+    return dict(ms=ms, decode_ms=dk, merge_ms=mg, kv_bytes=kvb)
 
 
 def bench_oam(pkg, torch, synth, steps, warmup, dev):
@@ -313,7 +311,7 @@ def main():
                    "kv_bytes_per_step": head["kv_bytes"],
                    "eq6_bytes_per_step": decode_eq_elements(w.B, w.KH, w.G, w.D, int(w.lens[0])) * 2,
                    "flops_per_step": decode_eq_flops(w.B, w.QH, int(w.lens[0]), w.D)},
-        "phases_us": {"worklist": round(head["worklist_ms"] * 1e3, 2), "decode": round(head["decode_ms"] * 1e3, 2),
+        "phases_us": {"decode": round(head["decode_ms"] * 1e3, 2),
                       "merge": round(head["merge_ms"] * 1e3, 2)},
         "roofline": roofline,
     }
@@ -325,7 +323,7 @@ def main():
             others["gqa32k_bf16"] = summary(r)
             del r
         if "ragged" in todo:
-            r = bench_dense(pkg, torch, synth, "ragged", max(5, K // 2), W, dev, split_tokens=512)
+            r = bench_dense(pkg, torch, synth, "ragged", max(5, K // 2), W, dev)
             others["ragged_bf16"] = summary(r, {"total_kv_tokens_per_head": r["tokens"],
                                                  "lens_min": int(r["w"].lens.min()),
                                                  "lens_max": int(r["w"].lens.max())})

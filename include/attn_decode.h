@@ -142,23 +142,25 @@ attn_status attn_decode_workspace_size(const attn_decode_args *args, size_t *byt
 /*
  * Split-KV decode attention ("优化稀疏注意力中的令牌丢弃机制" §5 Split-KV;
  * "注意力优化" Flash Attention online softmax).  One call enqueues:
- *  (1) a work-list pass that cuts every (b, kh) token range into chunks of
- *      split_tokens and lays out partial slots,
- *  (2) a persistent decode kernel whose workgroups claim chunks from the list
- *      with an integer atomic, stream each chunk's K/V rows once, and write
- *      the chunk's partial (m, l, o) for each of the G query heads,
- *  (3) the log-sum-exp merge of attn_merge_lse into out (and lse).
- * Results are deterministic: no floating-point atomics are used.
+ *  (1) a persistent decode kernel.  Every (b, kh) token range is cut into
+ *      tiles of 32 positions and all ranges are laid end to end; each worker
+ *      streams an equal contiguous share of that tile stream once, and for
+ *      each chunk of split_tokens positions it touches writes the partial
+ *      (m, l, o) of each of the G query heads;
+ *  (2) the log-sum-exp merge of those partials into out (and lse), the
+ *      operation attn_merge_lse exposes on its own.
+ * Results are deterministic: no floating-point atomics are used, and the
+ * work split depends only on the lengths and the device's compute-unit count.
  */
 attn_status attn_decode_splitkv(const attn_decode_args *args, attn_stream_t stream);
 
 /*
- * attn_decode_splitkv plus timing marks: events[0..3] (hipEvent_t created by
- * the caller, any may be NULL) are recorded on `stream` before the work-list
- * pass, before the decode kernel, before the merge and after the merge, so
- * the caller can read each phase's duration.  Same arguments and errors.
+ * attn_decode_splitkv plus timing marks: events[0..2] (hipEvent_t created by
+ * the caller, any may be NULL) are recorded on `stream` before the decode
+ * kernel, before the merge and after the merge, so the caller can read each
+ * phase's duration.  Same arguments and errors.
  */
-attn_status attn_decode_splitkv_profiled(const attn_decode_args *args, attn_stream_t stream, void *const events[4]);
+attn_status attn_decode_splitkv_profiled(const attn_decode_args *args, attn_stream_t stream, void *const events[3]);
 
 /*
  * Log-sum-exp merge of partial triples ("优化稀疏注意力中的令牌丢弃机制" §5,

@@ -112,8 +112,8 @@ class PreparedDecode:
         _lib.check(self._fn(ctypes.byref(self.args), _stream(stream)), "attn_decode_splitkv")
 
     def profiled(self, events, stream=None):
-        """Same call, recording four torch.cuda.Event marks around the work-list, decode and merge launches."""
-        arr = (ctypes.c_void_p * 4)(*[None if e is None else e.cuda_event for e in events])
+        """Same call, recording three torch.cuda.Event marks around the decode and merge launches."""
+        arr = (ctypes.c_void_p * 3)(*[None if e is None else e.cuda_event for e in events])
         st = _lib.load().attn_decode_splitkv_profiled(ctypes.byref(self.args), _stream(stream), ctypes.byref(arr))
         _lib.check(st, "attn_decode_splitkv_profiled")
 

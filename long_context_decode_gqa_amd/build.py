@@ -13,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn_decode.so")
 
-SOURCES = ["api.cpp", "api_ext.cpp", "decode_mfma.hip", "decode_valu.hip", "worklist.hip", "quant.hip", "oam.hip"]
+SOURCES = ["api.cpp", "api_ext.cpp", "decode_mfma.hip", "decode_valu.hip", "merge.hip", "quant.hip", "oam.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 instructions are kept out of the generated code on purpose.

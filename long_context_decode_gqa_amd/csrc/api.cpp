@@ -62,8 +62,8 @@ attn_status check_geom(const attn_kv_geom &g, int es, bool need_ptrs) {
 }
 
 struct DecodeLayout {
-  size_t hdr, tile_start, rss, m, l, o, total;
-  int64_t max_partials;
+  size_t m, l, o, total;
+  int64_t max_partials, max_chunks;
   int32_t split, ngb, max_tokens;
   bool mfma;
 };
@@ -117,17 +117,14 @@ attn_status plan_decode(const attn_decode_args *a, DecodeLayout *L) {
     return fail(ATTN_ERR_UNSUPPORTED, "with token_idx, split_tokens must be <= 1024");
   L->ngb = (a->G + 15) / 16;
   L->max_tokens = a->token_idx ? a->idx_stride : g.max_seq_len;
-  const int64_t max_chunks = ((int64_t)L->max_tokens + L->split - 1) / L->split;
+  L->max_chunks = ((int64_t)L->max_tokens + L->split - 1) / L->split;
   const int64_t QH = (int64_t)g.KH * a->G;
-  L->max_partials = 2 * (int64_t)g.B * QH * max_chunks;
+  L->max_partials = 2 * (int64_t)g.B * QH * L->max_chunks;
   const int64_t nlanes = (int64_t)g.B * g.KH * L->ngb;
   const int64_t max_tiles = nlanes * (((int64_t)L->max_tokens + 31) / 32);
   if (L->max_partials >= (int64_t(1) << 31) || max_tiles >= (int64_t(1) << 31))
     return fail(ATTN_ERR_UNSUPPORTED, "too many split-KV partials (reduce max_seq_len or raise split_tokens)");
   size_t off = 0;
-  L->hdr = off; off = align256(off + 64 * sizeof(int32_t));
-  L->tile_start = off; off = align256(off + (nlanes + 1) * sizeof(int32_t));
-  L->rss = off; off = align256(off + ((int64_t)g.B * QH + 1) * sizeof(int32_t));
   L->m = off; off = align256(off + L->max_partials * sizeof(float));
   L->l = off; off = align256(off + L->max_partials * sizeof(float));
   L->o = off; off = align256(off + (size_t)L->max_partials * g.D * sizeof(float));
@@ -203,9 +200,7 @@ static attn_status decode_impl(const attn_decode_args *a, attn_stream_t stream, 
   p.softmax_scale = a->softmax_scale != 0.f ? a->softmax_scale : 1.0f / sqrtf((float)a->kv.D);
   p.split = L.split;
   p.max_seq_len = a->kv.max_seq_len;
-  p.wl.hdr = reinterpret_cast<int32_t *>(ws + L.hdr);
-  p.wl.tile_start = reinterpret_cast<int32_t *>(ws + L.tile_start);
-  p.wl.row_split_start = reinterpret_cast<int32_t *>(ws + L.rss);
+  p.max_chunks = (int32_t)L.max_chunks;
   {
     // persistent grid: the MFMA kernel runs one-wave workers, eight per compute
     // unit (two per SIMD, its register budget); the vector-ALU kernel four
@@ -226,17 +221,13 @@ static attn_status decode_impl(const attn_decode_args *a, attn_stream_t stream, 
   };
   hipError_t e = mark(0);
   if (e != hipSuccess) return fail_hip(e, "event record");
-  e = launch_worklist(p, s);
-  if (e != hipSuccess) return fail_hip(e, "work-list launch");
-  if ((e = mark(1)) != hipSuccess) return fail_hip(e, "event record");
   if (L.mfma) e = launch_decode_mfma(p, a->kv_dtype, s);
   else e = launch_decode_valu(p, a->q_dtype, a->kv_dtype, s);
   if (e != hipSuccess) return fail_hip(e, "decode launch");
-  if ((e = mark(2)) != hipSuccess) return fail_hip(e, "event record");
-  e = launch_merge(p.wl.o_part, p.wl.m_part, p.wl.l_part, p.wl.row_split_start, p.B * p.QH, p.D, a->out_dtype,
-                   a->out, a->lse, s);
+  if ((e = mark(1)) != hipSuccess) return fail_hip(e, "event record");
+  e = launch_merge_decode(p, a->out_dtype, a->out, a->lse, s);
   if (e != hipSuccess) return fail_hip(e, "merge launch");
-  if ((e = mark(3)) != hipSuccess) return fail_hip(e, "event record");
+  if ((e = mark(2)) != hipSuccess) return fail_hip(e, "event record");
   return ATTN_OK;
 }
 
@@ -244,7 +235,7 @@ attn_status attn_decode_splitkv(const attn_decode_args *a, attn_stream_t stream)
   return decode_impl(a, stream, nullptr);
 }
 
-attn_status attn_decode_splitkv_profiled(const attn_decode_args *a, attn_stream_t stream, void *const events[4]) {
+attn_status attn_decode_splitkv_profiled(const attn_decode_args *a, attn_stream_t stream, void *const events[3]) {
   return decode_impl(a, stream, events);
 }
 

@@ -47,23 +47,25 @@ __device__ __forceinline__ int wave_sum_int(int v) {
   return v;
 }
 
-// ---------------------------------------------------------------- work-list
+// Wave-uniform copies of values every lane holds alike: they then live in
+// scalar registers, and a buffer resource built from them needs no per-lane
+// (waterfall) loop around each load.
+__device__ __forceinline__ int uniform_i32(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
-// Device work-list shared by the decode kernels.
-//
-// A "lane" is (b, kh, query-head block of up to 16 heads); lane q covers
-// ceil(n_q / 32) tiles of 32 token positions, and all lanes' tiles are laid
-// end to end (lane q starts at tile_start[q]).  The decode grid splits this
-// tile stream into equal contiguous ranges, one per workgroup, so every
-// workgroup streams the same number of K/V bytes whatever the length mix.
-// Each lane is also cut into chunks of split_tokens positions; a chunk owns
-// two partial slots because at most one range boundary can fall inside it
-// (ranges are at least one chunk long).  Slot 2j is the part of chunk j
-// before that boundary (or all of it), slot 2j+1 the part after (or empty).
+// ---------------------------------------------------------------- work split
+
+// Split-KV partial buffers.  Output row r = (b, kh, g) = b*QH + kh*G + g owns
+// the 2*max_chunks slots starting at 2*r*max_chunks, two per chunk of
+// split_tokens positions: at most one worker-range boundary can fall inside a
+// chunk, so slot 2j holds the part of chunk j before that boundary (or all of
+// it) and slot 2j+1 the part after it (or an empty partial: m = -inf, l = 0).
+// Slots of chunks past the row's own chunk count are never read.
 struct WorkList {
-  int32_t *hdr;              // [0] tiles in total, [1] workgroups in use
-  int32_t *tile_start;       // [nlanes + 1]
-  int32_t *row_split_start;  // [B*QH + 1] first partial slot of each output row
   float *m_part;             // [max partials] natural-log max
   float *l_part;             // [max partials]
   float *o_part;             // [max partials][D]
@@ -83,12 +85,94 @@ struct DecodeParams {
   float softmax_scale;
   int32_t split;        // tokens per chunk (multiple of 32)
   int32_t max_seq_len;  // lengths are clamped to this bound
+  int32_t max_chunks;   // chunks of the longest possible row
   int32_t grid;         // workgroups launched for the decode kernel
   WorkList wl;
 };
 
+// A "lane" is (b, kh, query-head block of up to 16 heads): lane q belongs to
+// pair q / ngb = b*KH + kh and covers ceil(n / 32) tiles of 32 positions,
+// n = the sequence length (or kept-index count in indexed mode), clamped to
+// the declared bounds.  All lanes' tiles are laid end to end in lane order;
+// decode workers split that stream into equal contiguous ranges, so every
+// worker streams the same number of K/V bytes whatever the length mix.
+__device__ __forceinline__ int pair_positions(const DecodeParams &p, int pair) {
+  const int b = pair / p.KH;
+  const int L = min(max(p.seq_lens[b], 0), p.max_seq_len);
+  if (p.token_idx) return L > 0 ? min(max(p.n_idx[pair], 0), p.idx_stride) : 0;
+  return L;
+}
+__device__ __forceinline__ int pair_chunks(const DecodeParams &p, int pair) {
+  return (pair_positions(p, pair) + p.split - 1) / p.split;
+}
+__device__ __forceinline__ int lane_tiles(const DecodeParams &p, int q) {
+  return q < p.B * p.KH * p.ngb ? (pair_positions(p, q / p.ngb) + 31) / 32 : 0;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int x = __shfl_up(v, o);
+    if (lane >= o) v += x;
+  }
+  return v;
+}
+
+// Tiles of all lanes (wave-wide; every thread of the wave gets the total).
+__device__ __forceinline__ int wave_total_tiles(const DecodeParams &p) {
+  const int nl = p.B * p.KH * p.ngb;
+  int acc = 0;
+  for (int q = threadIdx.x & 63; q < nl; q += 64) acc += lane_tiles(p, q);
+  return __builtin_amdgcn_readfirstlane(wave_sum_int(acc));
+}
+
+// The lane holding tile t (0 <= t < total) and that lane's first tile and tile
+// count, by a scan over the lanes 64 at a time (wave-wide, uniform result).
+struct LaneHit {
+  int q, t0, nt;
+};
+__device__ __forceinline__ LaneHit wave_find_lane(const DecodeParams &p, int t) {
+  const int lane = threadIdx.x & 63;
+  const int nl = p.B * p.KH * p.ngb;
+  LaneHit h = {0, 0, 0};
+  int run = 0;
+  for (int base = 0; base < nl; base += 64) {
+    const int nt = lane_tiles(p, base + lane);
+    const int incl = wave_incl_scan(nt);
+    const int excl = run + incl - nt;
+    const unsigned long long own = __ballot(nt > 0 && excl <= t && t < excl + nt);
+    if (own) {
+      const int src = __builtin_ctzll(own);
+      h.q = base + src;
+      h.t0 = __builtin_amdgcn_readlane(excl, src);
+      h.nt = __builtin_amdgcn_readlane(nt, src);
+      break;
+    }
+    run += __builtin_amdgcn_readlane(incl, 63);
+  }
+  return h;
+}
+
+// The lane after h that has tiles (its first tile follows h's last).
+__device__ __forceinline__ LaneHit next_lane(const DecodeParams &p, LaneHit h) {
+  const int nl = p.B * p.KH * p.ngb;
+  LaneHit n = {h.q, h.t0 + h.nt, 0};
+  while (n.nt == 0 && n.q + 1 < nl) {
+    ++n.q;
+    n.nt = __builtin_amdgcn_readfirstlane(lane_tiles(p, n.q));
+  }
+  return n;
+}
+
+// Workers that get a range: at most one per chunk's worth of tiles, so every
+// range is at least one chunk long.
+__device__ __forceinline__ int workers_for(const DecodeParams &p, int total_tiles) {
+  return total_tiles == 0 ? 0 : min(p.grid, max(1, total_tiles / (p.split / 32)));
+}
+
 // Host-side launchers (each returns hipSuccess or the launch error).
-hipError_t launch_worklist(const DecodeParams &p, hipStream_t s);
+hipError_t launch_merge_decode(const DecodeParams &p, int32_t out_dtype, void *out, float *lse, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeParams &p, int kv_dtype, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeParams &p, int q_dtype, int kv_dtype, hipStream_t s);
 hipError_t launch_merge(const float *o_part, const float *m_part, const float *l_part, const int32_t *rss,

@@ -125,36 +125,33 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const float c1 = p.softmax_scale * kLog2e;
   const float NEG_INF = -__builtin_huge_valf();
 
-  const int nworkers = p.wl.hdr[1];
+  const int T = wave_total_tiles(p);
+  const int nworkers = workers_for(p, T);
   if ((int)blockIdx.x >= nworkers) return;
-  const int T = p.wl.hdr[0];
   const int t_begin = (int)((int64_t)blockIdx.x * T / nworkers);
   const int t_end = (int)((int64_t)(blockIdx.x + 1) * T / nworkers);
-  const int nlanes = p.B * p.KH * p.ngb;
   const int ct = p.split / kTile;  // tiles per chunk
 
+  // the lane (b, kh, query-head block) holding the first tile of the range;
+  // each later run takes the next lane that has tiles
+  LaneHit hit = wave_find_lane(p, t_begin);
   for (int t = t_begin; t < t_end;) {
-    // the lane (b, kh, query-head block) that owns tile t
-    int lo = 0, hi = nlanes - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (p.wl.tile_start[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    const int q = lo;
-    const int lane_t0 = p.wl.tile_start[q], lane_t1 = p.wl.tile_start[q + 1];
+    if (hit.nt == 0) break;  // lane walk exhausted (cannot happen for t < total)
+    const int q = hit.q;
+    const int lane_t0 = hit.t0, lane_t1 = hit.t0 + hit.nt;
     const int run_end = min(t_end, lane_t1);
     const int pair = q / p.ngb, gb = q - pair * p.ngb;
     const int b = pair / p.KH, kh = pair - b * p.KH;
-    const int L = min(max(p.seq_lens[b], 0), p.max_seq_len);
+    const int L = uniform_i32(min(max(p.seq_lens[b], 0), p.max_seq_len));
     int npos = L;
-    if constexpr (IDX) npos = L > 0 ? min(max(p.n_idx[pair], 0), p.idx_stride) : 0;
+    if constexpr (IDX) npos = uniform_i32(L > 0 ? min(max(p.n_idx[pair], 0), p.idx_stride) : 0);
     const int g0 = gb * 16;
     const int gcount = min(16, p.G - g0);
     const bool qvalid = col < gcount;
 
     // Buffer resources over this (b, kh)'s rows: 32-bit offsets, and rows at
     // or past L read as zero (their scores are masked), so no clamping.
-    const int64_t head_off = p.seq_offset[b] + (int64_t)kh * p.stride_h;
+    const int64_t head_off = uniform_i64(p.seq_offset[b]) + (int64_t)kh * p.stride_h;
     const char *kbase = (const char *)p.k + head_off * ES;
     const char *vbase = (const char *)p.v + head_off * ES;
     const uint32_t rs = (uint32_t)(p.stride_t * ES);
@@ -185,7 +182,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       }
       *(u32x4_t *)(s_q + g * kQRow + 16 * c8) = w;
     }
-    const int slot_base = qvalid ? p.wl.row_split_start[b * p.QH + kh * p.G + g0 + col] : 0;
+    const int slot_base = 2 * (b * p.QH + kh * p.G + g0 + col) * p.max_chunks;
     __syncthreads();
     auto q_operand = [&](int kb) -> OpT {
       const int d0 = (KVT == ATTN_BF16) ? 8 * (4 * kb + cg) : 64 * (kb >> 1) + 16 * cg + 8 * (kb & 1);
@@ -405,6 +402,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       seg_t0 = seg_t1;
     }
     t = run_end;
+    if (t < t_end) hit = next_lane(p, hit);
   }
 }
 

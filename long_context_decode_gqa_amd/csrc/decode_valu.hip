@@ -34,22 +34,19 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
   const int D = p.D;
   const float NEG_INF = -__builtin_huge_valf();
 
-  const int nwg = p.wl.hdr[1];
+  const int T = wave_total_tiles(p);
+  const int nwg = workers_for(p, T);
   if ((int)blockIdx.x >= nwg) return;
-  const int T = p.wl.hdr[0];
   const int t_begin = (int)((int64_t)blockIdx.x * T / nwg);
   const int t_end = (int)((int64_t)(blockIdx.x + 1) * T / nwg);
-  const int nlanes = p.B * p.KH * p.ngb;
   const int ct = p.split / 32;
 
+  // every wave of the workgroup walks the lanes alike
+  LaneHit hit = wave_find_lane(p, t_begin);
   for (int t = t_begin; t < t_end;) {
-    int lo = 0, hi = nlanes - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (p.wl.tile_start[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    const int q = lo;
-    const int lane_t0 = p.wl.tile_start[q], lane_t1 = p.wl.tile_start[q + 1];
+    if (hit.nt == 0) break;  // lane walk exhausted (cannot happen for t < total)
+    const int q = hit.q;
+    const int lane_t0 = hit.t0, lane_t1 = hit.t0 + hit.nt;
     const int run_end = min(t_end, lane_t1);
     const int pair = q / p.ngb, gb = q - pair * p.ngb;
     const int b = pair / p.KH, kh = pair - b * p.KH;
@@ -154,7 +151,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
         const int e = tid + 256 * k;
         if (e < gcount * D) {
           const int g = e / D, d = e - g * D;
-          const int slot = p.wl.row_split_start[b * p.QH + kh * p.G + g0 + g] + 2 * chunk + half;
+          const int slot = 2 * (b * p.QH + kh * p.G + g0 + g) * p.max_chunks + 2 * chunk + half;
           const float l = s_l[g];
           p.wl.o_part[(int64_t)slot * D + d] = (l > 0.f) ? o[k] / l : 0.f;
           if (d == 0) {
@@ -171,6 +168,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
       seg_t0 = seg_t1;
     }
     t = run_end;
+    if (t < t_end) hit = next_lane(p, hit);
   }
 }
 

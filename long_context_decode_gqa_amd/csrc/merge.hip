@@ -1,80 +1,8 @@
-// Work-list construction, log-sum-exp merge and measurement helpers.
+// Log-sum-exp merge of split-KV partials, and measurement helpers.
 #include "common.hpp"
 
 namespace lcdg {
 namespace {
-
-// Token positions of lane q = (pair, query-head block): the sequence length,
-// or the kept-index count in indexed mode; clamped to the declared bounds.
-__device__ __forceinline__ int lane_positions(const DecodeParams &p, int pair) {
-  const int b = pair / p.KH;
-  const int L = min(max(p.seq_lens[b], 0), p.max_seq_len);
-  if (p.token_idx) return L > 0 ? min(max(p.n_idx[pair], 0), p.idx_stride) : 0;
-  return L;
-}
-
-// Inclusive scan of one int per thread across the 1024-thread block.
-__device__ __forceinline__ int block_scan(int v, int *s_sum) {
-  const int tid = threadIdx.x;
-  s_sum[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int x = tid >= off ? s_sum[tid - off] : 0;
-    __syncthreads();
-    s_sum[tid] += x;
-    __syncthreads();
-  }
-  const int r = s_sum[tid];
-  __syncthreads();
-  return r;
-}
-
-// Ragged work-list ("优化稀疏注意力中的令牌丢弃机制" §5: long sequences are split
-// across many workgroups so a 128K sequence next to a 512-token one leaves no
-// compute unit idle).  One workgroup lays out the tile stream of all lanes,
-// the two partial slots of every (output row, chunk), the tile total and the
-// number of decode workgroups that get a range (each range >= one chunk).
-__global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p) {
-  __shared__ int s_sum[1024];
-  const int tid = threadIdx.x;
-  const int np = p.B * p.KH;
-  const int nl = np * p.ngb;
-  // tiles of every lane, in lane order
-  {
-    const int per = (nl + 1023) / 1024;
-    const int q0 = min(nl, tid * per), q1 = min(nl, q0 + per);
-    int local = 0;
-    for (int q = q0; q < q1; ++q) local += (lane_positions(p, q / p.ngb) + 31) / 32;
-    int run = block_scan(local, s_sum) - local;
-    for (int q = q0; q < q1; ++q) {
-      p.wl.tile_start[q] = run;
-      run += (lane_positions(p, q / p.ngb) + 31) / 32;
-    }
-    if (tid == 1023) {
-      const int total = run;  // thread 1023 owns the last lanes (or none): run is the total
-      p.wl.tile_start[nl] = total;
-      const int ct = p.split / 32;
-      const int fit = total / ct;
-      p.wl.hdr[0] = total;
-      p.wl.hdr[1] = total == 0 ? 0 : min(p.grid, max(1, fit));
-    }
-  }
-  // two partial slots per (row, chunk)
-  {
-    const int per = (np + 1023) / 1024;
-    const int q0 = min(np, tid * per), q1 = min(np, q0 + per);
-    int local = 0;
-    for (int q = q0; q < q1; ++q) local += (lane_positions(p, q) + p.split - 1) / p.split;
-    int run = block_scan(local, s_sum) - local;
-    for (int q = q0; q < q1; ++q) {
-      const int nc = (lane_positions(p, q) + p.split - 1) / p.split;
-      const int b = q / p.KH, kh = q - b * p.KH;
-      for (int g = 0; g < p.G; ++g) p.wl.row_split_start[b * p.QH + kh * p.G + g] = 2 * (p.G * run + g * nc);
-      run += nc;
-    }
-    if (tid == 1023) p.wl.row_split_start[p.B * p.QH] = 2 * p.G * run;
-  }
-}
 
 constexpr int kMergeThreads = 512;
 constexpr int kMergeWeights = 512;
@@ -117,10 +45,14 @@ __device__ __forceinline__ int merge_scan(int v, int *s_red, int *total) {
 // LDS list (batches of 512), then spread over thread groups that each sum a
 // strided subset with branch-free loads; the groups are added in a fixed
 // order, so the result is deterministic.
-template <int OUT>
+//
+// Slot ranges: with DECODE, row r = (b, kh, g) of a decode call reads its
+// 2 * (chunks of its pair) slots from 2*r*max_chunks on; otherwise the
+// caller's CSR offsets rss[r] .. rss[r+1].
+template <int OUT, bool DECODE>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *o_part, const float *m_part,
-                                                              const float *l_part, const int32_t *rss, int32_t rows,
-                                                              int32_t D, void *out, float *lse) {
+                                                              const float *l_part, const int32_t *rss,
+                                                              DecodeParams dp, int32_t D, void *out, float *lse) {
   __shared__ float s_red[kMergeThreads / 64];
   __shared__ int s_cnt[kMergeThreads / 64];
   __shared__ float s_w[kMergeWeights];
@@ -129,7 +61,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *o_par
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const float NEG_INF = -__builtin_huge_valf();
-  const int s0 = rss[row], n = rss[row + 1] - s0;
+  int s0, n;
+  if constexpr (DECODE) {
+    s0 = 2 * row * dp.max_chunks;
+    n = 2 * pair_chunks(dp, row / dp.G);
+  } else {
+    s0 = rss[row];
+    n = rss[row + 1] - s0;
+  }
   float M = NEG_INF;
   for (int i = tid; i < n; i += kMergeThreads)
     if (l_part[s0 + i] > 0.f) M = fmaxf(M, m_part[s0 + i]);
@@ -208,19 +147,29 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4_t *src, size_t n,
 
 }  // namespace
 
-hipError_t launch_worklist(const DecodeParams &p, hipStream_t s) {
-  hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(1024), 0, s, p);
-  return hipGetLastError();
-}
-
 hipError_t launch_merge(const float *o_part, const float *m_part, const float *l_part, const int32_t *rss,
                         int32_t rows, int32_t D, int32_t out_dtype, void *out, float *lse, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  DecodeParams none = {};
   dim3 g(rows), blk(kMergeThreads);
   if (out_dtype == ATTN_F32)
-    hipLaunchKernelGGL((merge_kernel<ATTN_F32>), g, blk, 0, s, o_part, m_part, l_part, rss, rows, D, out, lse);
+    hipLaunchKernelGGL((merge_kernel<ATTN_F32, false>), g, blk, 0, s, o_part, m_part, l_part, rss, none, D, out, lse);
   else
-    hipLaunchKernelGGL((merge_kernel<ATTN_BF16>), g, blk, 0, s, o_part, m_part, l_part, rss, rows, D, out, lse);
+    hipLaunchKernelGGL((merge_kernel<ATTN_BF16, false>), g, blk, 0, s, o_part, m_part, l_part, rss, none, D, out, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_decode(const DecodeParams &p, int32_t out_dtype, void *out, float *lse, hipStream_t s) {
+  const int rows = p.B * p.QH;
+  if (rows <= 0) return hipSuccess;
+  dim3 g(rows), blk(kMergeThreads);
+  const WorkList &w = p.wl;
+  if (out_dtype == ATTN_F32)
+    hipLaunchKernelGGL((merge_kernel<ATTN_F32, true>), g, blk, 0, s, w.o_part, w.m_part, w.l_part, nullptr, p, p.D,
+                       out, lse);
+  else
+    hipLaunchKernelGGL((merge_kernel<ATTN_BF16, true>), g, blk, 0, s, w.o_part, w.m_part, w.l_part, nullptr, p, p.D,
+                       out, lse);
   return hipGetLastError();
 }
 

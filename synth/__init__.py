@@ -238,7 +238,7 @@ def workload(name: str, **over) -> Workload:
     elif name == "gqa32k":
         w = Workload("gqa32k", 16, 8, 8, 128, 2, "bf16", np.full(16, 32768, np.int32))
     elif name == "ragged":
-        w = Workload("ragged", 32, 8, 8, 128, 3, "bf16", loguniform_lengths(3, 32), layout="token_major")
+        w = Workload("ragged", 32, 8, 8, 128, 3, "bf16", loguniform_lengths(3, 32), layout="head_major")
     elif name == "int8_128k":
         w = Workload("int8_128k", 4, 8, 8, 128, 4, "bf16", np.full(4, 131072, np.int32), outliers=2)
     elif name == "oam_128k":
