@@ -26,7 +26,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, vendor figure
 METRIC = "decode-attention KV GB/s (% of MI355X HBM peak) + µs/step at 128K KV"
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_mfma_dense128k_pmc.txt")
-DECODE_SOURCE = os.path.join(ROOT, "long_context_decode_gqa_amd", "csrc", "decode_mfma.hip")
+# the decode kernel and the header it inlines; counters taken on other sources are stale
+DECODE_SOURCES = [os.path.join(ROOT, "long_context_decode_gqa_amd", "csrc", f) for f in ("decode_mfma.hip", "common.hpp")]
 
 
 # ------------------------------------------------------------------ byte/flop accounting
@@ -66,9 +67,12 @@ def host_threads() -> int:
     return max(1, min(16, n))
 
 
-def file_sha256(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def sources_sha256(paths) -> str:
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def read_pmc_traffic():
@@ -81,7 +85,7 @@ def read_pmc_traffic():
         if ":" in line and not line.startswith("#"):
             key, val = line.split(":", 1)
             kv[key.strip()] = val.strip()
-    if kv.get("kernel_source_sha256") != file_sha256(DECODE_SOURCE):
+    if kv.get("kernel_sources_sha256") != sources_sha256(DECODE_SOURCES):
         return None
     try:
         return int(float(kv["hbm_bytes_per_launch"]))
