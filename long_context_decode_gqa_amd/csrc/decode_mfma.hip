@@ -88,6 +88,11 @@ struct Step {
   static constexpr int kRegs = 2 * TileT::KL * 4 + 8 * TileT::VW;
   static constexpr int kBudget = KVT == ATTN_BF16 ? 64 : 32;
   static constexpr int TPS = kRegs >= kBudget ? 1 : kBudget / kRegs;
+  // Steps in flight: NBUF register buffers rotate, so while one step is
+  // consumed the next NBUF-1 are loading.  An int8 tile carries half the
+  // bytes of a bf16 one, so int8 keeps three buffers to have as many bytes
+  // in flight per wave.
+  static constexpr int NBUF = KVT == ATTN_BF16 ? 2 : 3;
   TileT t[TPS];
 };
 
@@ -158,7 +163,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const int nrec = L > 0 ? (int)((uint32_t)(L - 1) * rs + D * ES) : 0;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)kbase, (short)0, nrec, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vbase, (short)0, nrec, 0x00020000);
-    const float *kscale = (KVT == ATTN_I8) ? p.k_scale + (int64_t)pair * p.k_scale_stride : nullptr;
+    // int8 K scales of this pair, read through a buffer resource as well, so
+    // they are fetched in the same in-order stream as the tile they belong to
+    // (a plain load sunk towards its use would make every wait drain the
+    // tiles issued after it).
+    const bool i8 = KVT == ATTN_I8;
+    const __amdgpu_buffer_rsrc_t ksrs = __builtin_amdgcn_make_buffer_rsrc(
+        i8 ? (void *)(p.k_scale + (int64_t)pair * p.k_scale_stride) : nullptr, (short)0,
+        i8 ? max(p.k_scale_stride, 1) * 4 : 0, 0x00020000);
 
     // Stage Q (the 16 heads of this block, zero past G) in LDS in MFMA
     // operand type; tiles read their B operand from there.  The partial
@@ -221,18 +233,29 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         const int last = max(npos - 1, 0);
         if constexpr (IDX) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) R.ks[i] = kscale[row_of(tpos + 16 * (i >> 2) + 4 * cg + (i & 3)) / p.k_part];
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t part = (uint32_t)(row_of(tpos + 16 * (i >> 2) + 4 * cg + (i & 3)) / p.k_part);
+            R.ks[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ksrs, (4 * part) | oob, 0, 0));
+          }
         } else {
 #pragma unroll
-          for (int tb = 0; tb < 2; ++tb) R.ks[tb] = kscale[min(tpos + 16 * tb, last) / p.k_part];
+          for (int tb = 0; tb < 2; ++tb) {
+            const uint32_t part = (uint32_t)(min(tpos + 16 * tb, last) / p.k_part);
+            R.ks[tb] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ksrs, (4 * part) | oob, 0, 0));
+          }
         }
       }
     };
 
     // a step = tiles tile0 .. tile0+TPS-1, each valid while below `limit`
+    // The scheduling barrier keeps a step's loads (scales included) issued
+    // as one group, in program order: the wait counts then stay the same on
+    // every path into the loop, and a wait for one step never drains the
+    // steps issued after it.
     auto load_step = [&](StepT &S, int tile0, int limit) {
 #pragma unroll
       for (int j = 0; j < TPS; ++j) load_tile(S.t[j], tile0 + j, tile0 + j < limit);
+      __builtin_amdgcn_sched_barrier(0);
     };
 
     f32x4_t O[NB];
@@ -255,10 +278,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             const u32x4_t w = R.k[tb][kb >> 1];
             const uint32_t c0 = w[2 * (kb & 1)], c1w = w[2 * (kb & 1) + 1];
             u32x4_t hw;
-            hw[0] = codes_to_f16x2((c0 & 0xFFu) | ((c0 & 0xFF00u) << 8));
-            hw[1] = codes_to_f16x2(((c0 >> 16) & 0xFFu) | ((c0 >> 8) & 0xFF0000u));
-            hw[2] = codes_to_f16x2((c1w & 0xFFu) | ((c1w & 0xFF00u) << 8));
-            hw[3] = codes_to_f16x2(((c1w >> 16) & 0xFFu) | ((c1w >> 8) & 0xFF0000u));
+            // bytes 0,1 (then 2,3) of a word into the low byte of each half
+            hw[0] = codes_to_f16x2(__builtin_amdgcn_perm(c0, c0, 0x0c010c00u));
+            hw[1] = codes_to_f16x2(__builtin_amdgcn_perm(c0, c0, 0x0c030c02u));
+            hw[2] = codes_to_f16x2(__builtin_amdgcn_perm(c1w, c1w, 0x0c010c00u));
+            hw[3] = codes_to_f16x2(__builtin_amdgcn_perm(c1w, c1w, 0x0c030c02u));
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, hw), q_operand(kb), acc, 0, 0, 0);
           }
         }
@@ -310,16 +334,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq) {
             const uint32_t x = word_of<VW>(R.v[2 * qq], w), y = word_of<VW>(R.v[2 * qq + 1], w);
-            a[qq] = (nb & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
+            // the low (even nb) or high (odd nb) bf16 of tokens 2qq and 2qq+1
+            a[qq] = __builtin_amdgcn_perm(y, x, (nb & 1) ? 0x07060302u : 0x05040100u);
           }
           O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), phi, O[nb], 0, 0, 0);
           O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), plo, O[nb], 0, 0, 0);
         } else {
-          const int w = nb >> 2, sh = 8 * (nb & 3);
+          const int w = nb >> 2;
+          const uint32_t k = (uint32_t)(nb & 3);
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq) {
+            // byte k of tokens 2qq and 2qq+1 into the low byte of each half
             const uint32_t x = word_of<VW>(R.v[2 * qq], w), y = word_of<VW>(R.v[2 * qq + 1], w);
-            a[qq] = codes_to_f16x2(((x >> sh) & 0xFFu) | (((y >> sh) & 0xFFu) << 16));
+            a[qq] = codes_to_f16x2(__builtin_amdgcn_perm(y, x, 0x0c000c00u | k | ((4u + k) << 16)));
           }
           O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), phi, O[nb], 0, 0, 0);
           O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), plo, O[nb], 0, 0, 0);
@@ -332,13 +359,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       for (int j = 0; j < TPS; ++j) compute_tile(S.t[j], tile0 + j);
     };
 
-    // Segments: the run cut at chunk boundaries.  A segment takes an even
-    // number of steps (the last may be empty), so the two register buffers
-    // alternate statically, and its last step already prefetches the first
-    // tiles of the next segment of the run.
-    StepT ra, rb;
+    // Segments: the run cut at chunk boundaries.  The NBUF register buffers
+    // rotate statically: a segment takes a multiple of NBUF steps (the last
+    // ones may be empty), and step s is loaded NBUF-1 steps before it is
+    // consumed.  Loads issued past the segment's last step already fetch the
+    // first steps of the next segment of the run (positions, not index
+    // lists, so not in indexed mode), through one load site so that both
+    // cases share the same registers.
+    constexpr int NBUF = StepT::NBUF;
+    StepT buf[NBUF];
     auto seg_end_of = [&](int s0) { return min(run_end, lane_t0 + ((s0 - lane_t0) / ct + 1) * ct); };
-    if constexpr (!IDX) load_step(ra, t, seg_end_of(t));
+    if constexpr (!IDX) {
+      const int t1 = seg_end_of(t);
+#pragma unroll
+      for (int j = 0; j + 1 < NBUF; ++j) load_step(buf[j], t + j * TPS, t1);
+    }
     for (int seg_t0 = t; seg_t0 < run_end;) {
       const int seg_t1 = seg_end_of(seg_t0);
       const int chunk = (seg_t0 - lane_t0) / ct;
@@ -350,22 +385,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         __syncthreads();
         for (int i = lane; i < seg_pos1 - seg_pos0; i += 64) s_idx[i] = min(max(src[seg_pos0 + i], 0), L - 1);
         __syncthreads();
-        load_step(ra, seg_t0, seg_t1);
+#pragma unroll
+        for (int j = 0; j + 1 < NBUF; ++j) load_step(buf[j], seg_t0 + j * TPS, seg_t1);
       }
       const int nsteps = (seg_t1 - seg_t0 + TPS - 1) / TPS;
-      const int steps = (nsteps + 1) & ~1;
+      const int steps = (nsteps + NBUF - 1) / NBUF * NBUF;
       const int next_t1 = seg_end_of(seg_t1);
-      for (int i = 0; i < steps; i += 2) {
-        const int ta = seg_t0 + i * TPS;
-        load_step(rb, ta + TPS, seg_t1);
-        compute_step(ra, ta);
-        // next step of this segment, or (last step) the next segment's first
-        // tiles in this run; one load site so both share the same registers
-        const bool in_seg = i + 2 < steps;
-        const int tn = in_seg ? ta + 2 * TPS : seg_t1;
+      auto issue = [&](StepT &S, int s) {
+        const bool in_seg = s < steps;
+        const int tn = in_seg ? seg_t0 + s * TPS : seg_t1 + (s - steps) * TPS;
         const int lim = in_seg ? seg_t1 : (IDX ? 0 : next_t1);
-        load_step(ra, tn < lim ? tn : seg_t0, tn < lim ? lim : 0);
-        compute_step(rb, ta + TPS);
+        load_step(S, tn < lim ? tn : seg_t0, tn < lim ? lim : 0);
+      };
+      for (int i = 0; i < steps; i += NBUF) {
+#pragma unroll
+        for (int j = 0; j < NBUF; ++j) {
+          issue(buf[(j + NBUF - 1) % NBUF], i + j + NBUF - 1);
+          compute_step(buf[j], seg_t0 + (i + j) * TPS);
+        }
       }
 
       // Partial of this segment, straight from registers.  Lane (col, cg)
