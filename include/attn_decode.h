@@ -217,7 +217,8 @@ attn_status oam_value_lognorm(const attn_kv_geom *geom, const void *v_bf16, floa
 
 /*
  * Arguments of output-aware top-K token selection.
- *   q, k        bf16; q [B][KH*G][D], k in geometry `kv`; 1 <= G <= 16
+ *   q, k        bf16; q [B][KH*G][D], k in geometry `kv`; 1 <= G <= 16;
+ *               max_seq_len <= 2^21 (ATTN_ERR_UNSUPPORTED otherwise)
  *   v, vlog     the value term comes from vlog (fp32, layout of
  *               oam_value_lognorm, stride vlog_stride) when vlog != NULL,
  *               else it is computed from the bf16 rows of v on the fly

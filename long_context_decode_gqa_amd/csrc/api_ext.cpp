@@ -75,8 +75,7 @@ attn_status oam_value_lognorm(const attn_kv_geom *geom, const void *v_bf16, floa
 namespace {
 
 struct OamLayout {
-  size_t scores, vlog, hist, counts, offsets, state, total;
-  int32_t nblk;
+  size_t scores, vlog, hist, state, blk_gt, blk_off, cand_key, cand_idx, total;
 };
 
 attn_status plan_oam(const oam_topk_args *a, OamLayout *L) {
@@ -102,17 +101,21 @@ attn_status plan_oam(const oam_topk_args *a, OamLayout *L) {
       return api_fail(ATTN_ERR_INVALID_ARG, "v must be 16-byte aligned");
   }
   if (a->vlog && a->vlog_stride < g.max_seq_len) return api_fail(ATTN_ERR_INVALID_ARG, "vlog_stride must be >= max_seq_len");
+  if (g.max_seq_len > oam_max_tokens())
+    return api_fail(ATTN_ERR_UNSUPPORTED, "oam_score_topk supports max_seq_len up to 2^21 tokens");
   const int64_t npairs = (int64_t)g.B * g.KH;
   const int64_t stride = g.max_seq_len;
-  L->nblk = (g.max_seq_len + oam_block_tokens() - 1) / oam_block_tokens();
   auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
   size_t off = 0;
   L->scores = off; off = al(off + (a->scores_out ? 0 : npairs * stride * sizeof(float)));
   L->vlog = off; off = al(off + (a->vlog ? 0 : npairs * stride * sizeof(float)));
-  L->hist = off; off = al(off + (size_t)3 * npairs * 2048 * sizeof(uint32_t));
-  L->counts = off; off = al(off + (size_t)npairs * (L->nblk > 0 ? L->nblk : 1) * 2 * sizeof(int32_t));
-  L->offsets = off; off = al(off + (size_t)npairs * (L->nblk > 0 ? L->nblk : 1) * 2 * sizeof(int32_t));
-  L->state = off; off = al(off + (size_t)npairs * 4 * sizeof(int32_t));
+  const size_t nblk_max = (size_t)oam_max_tokens() / 2048;
+  L->hist = off; off = al(off + (size_t)npairs * (2048 + 4) * sizeof(uint32_t));  // histogram, then counters
+  L->state = off; off = al(off + (size_t)npairs * 8 * sizeof(int32_t));
+  L->blk_gt = off; off = al(off + (size_t)npairs * nblk_max * sizeof(int32_t));
+  L->blk_off = off; off = al(off + (size_t)npairs * nblk_max * sizeof(int32_t));
+  L->cand_key = off; off = al(off + (size_t)npairs * 4096 * sizeof(uint32_t));
+  L->cand_idx = off; off = al(off + (size_t)npairs * 4096 * sizeof(int32_t));
   L->total = off;
   return ATTN_OK;
 }
@@ -145,10 +148,12 @@ attn_status oam_score_topk(const oam_topk_args *a, attn_stream_t stream) {
   plan.vlog = a->vlog ? const_cast<float *>(a->vlog) : reinterpret_cast<float *>(ws + L.vlog);
   plan.vlog_stride = a->vlog ? a->vlog_stride : a->kv.max_seq_len;
   plan.hist = reinterpret_cast<uint32_t *>(ws + L.hist);
-  plan.chunk_cnt = reinterpret_cast<int32_t *>(ws + L.counts);
-  plan.offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
+  plan.counters = plan.hist + (size_t)a->kv.B * a->kv.KH * 2048;
   plan.state = reinterpret_cast<int32_t *>(ws + L.state);
-  plan.nchunk = L.nblk;
+  plan.blk_gt = reinterpret_cast<int32_t *>(ws + L.blk_gt);
+  plan.blk_off = reinterpret_cast<int32_t *>(ws + L.blk_off);
+  plan.cand_key = reinterpret_cast<uint32_t *>(ws + L.cand_key);
+  plan.cand_idx = reinterpret_cast<int32_t *>(ws + L.cand_idx);
   hipError_t e = launch_oam(*a, plan, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : api_fail_hip(e, "oam launch");
 }

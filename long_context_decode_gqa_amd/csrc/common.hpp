@@ -191,14 +191,16 @@ struct OamPlan {
   int32_t score_stride;
   float *vlog;           // value log-norms: the caller's or computed into the workspace
   int32_t vlog_stride;
-  uint32_t *hist;        // [3][npairs][2048]
-  int32_t *chunk_cnt;    // [npairs][nchunk][2]
-  int32_t *offsets;      // [npairs][nchunk][2]
-  int32_t *state;        // [npairs][4]
-  int32_t nchunk;        // selection blocks per pair
+  uint32_t *hist;        // [npairs][2048] level-0 key histogram, followed by
+  uint32_t *counters;    // [npairs][4] (zeroed together with hist)
+  int32_t *state;        // [npairs][8] selection state
+  int32_t *blk_gt;       // [npairs][oam_max_tokens() / 2048]
+  int32_t *blk_off;      // [npairs][oam_max_tokens() / 2048]
+  uint32_t *cand_key;    // [npairs][4096]
+  int32_t *cand_idx;     // [npairs][4096]
 };
 hipError_t launch_oam(const oam_topk_args &a, const OamPlan &plan, hipStream_t s);
-int oam_block_tokens();
+int oam_max_tokens();  // longest sequence oam_score_topk selects over
 
 int device_cu_count();
 

@@ -4,33 +4,53 @@
 // replaces).  For each (b, kh) the G query heads' routing logits are averaged,
 // so the G heads of a KV head share one kept set.
 //
-// Passes (grid = token blocks x (b, kh) pairs):
-//   score    S = K Q^T on the matrix cores, mean over the G heads, scale,
-//            + beta * vlog; write the fp32 score, and count the top 11 bits
-//            of its order-preserving key into histogram level 0
-//   level 1  keys whose top 11 bits are the threshold's: histogram of bits 20..10
-//   level 2  keys matching the 22-bit prefix: histogram of bits 9..0
-//            -> the K-th largest key T exactly, and how many keys equal to T
-//            are kept (the lowest-index ones)
-//   count    per block: keys > T and keys == T
-//   write    per block: ordered compaction of the kept indices (ascending)
-// Every pass recomputes the threshold digits from the histograms so no pass
-// depends on a single-workgroup step.  Integer atomics only.
+// The K-th largest score is found by radix selection on order-preserving
+// 32-bit keys of the fp32 scores: digits of 11, 11 and 10 bits from the top,
+// then, among keys equal to the threshold T, the lowest indices are kept.
+// Passes (each needs the previous one complete, so they are separate launches):
+//   score      (token blocks x pairs) S = K Q^T on the matrix cores, mean over
+//              the G heads, scale, + beta * vlog; write the fp32 score and
+//              count the top 11 key bits into the pair's level-0 histogram.
+//   candidates (2048-token blocks x pairs) every block reads the pair's
+//              histogram and finds the threshold's top digit b0 (all blocks
+//              find the same); it counts its keys above bin b0 and appends its
+//              keys of bin b0 to the pair's candidate list.
+//   select     (one workgroup per pair) among the candidates, the exact
+//              threshold key T and the last kept index I_T among keys equal
+//              to T; then the output offset of every block.  (If the list
+//              overflowed - many equal scores - it selects over the pair's
+//              scores directly.)
+//   write      (2048-token blocks x pairs) ordered compaction of the kept
+//              tokens, key > T or (key == T and index <= I_T), at the block's
+//              offset, so idx_out is ascending.
+// Only integer atomics (histogram counts, list positions) cross workgroups
+// within a pass.
 #include "common.hpp"
 
 namespace lcdg {
 namespace {
 
-constexpr int kBlockTok = 2048;   // tokens per workgroup in every pass
-constexpr int kBins = 2048;       // 11-bit digits (level 2 uses 1024)
+constexpr int kBins = 2048;       // 11-bit digits (the 10-bit ones use 1024)
+constexpr int kBlockTok = 2048;   // tokens per workgroup of the candidate and write passes
+constexpr int kCandCap = 4096;    // candidate list capacity per pair
+constexpr int kMaxBlocks = 1024;  // blocks of kBlockTok per pair (sequences up to 2M tokens)
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Per-pair selection state, passed from one pass to the next.
+struct OamState {
+  int32_t b0;        // top 11 bits of the threshold key
+  int32_t need;      // keys of bin b0 to keep
+  uint32_t T;        // threshold key
+  int32_t I_T;       // last kept index among keys equal to T
+  int32_t pad[4];
+};
+
 struct OamDev {
-  int32_t B, KH, G, D, QH, L_max, L_cap, top_k, nblk;  // L_max: score row stride; L_cap: length bound
+  int32_t B, KH, G, D, QH, L_max, L_cap, top_k;  // L_max: score row stride; L_cap: length bound
   const int32_t *seq_lens;
   const int64_t *seq_offset;
   int64_t stride_h, stride_t;
@@ -39,10 +59,13 @@ struct OamDev {
   int32_t vlog_stride;
   float score_scale, beta;
   float *scores;       // [npairs][L_max]
-  uint32_t *hist;      // [3][npairs][kBins]
-  int32_t *counts;     // [npairs][nblk][2]  per block: keys > T, keys == T
-  int32_t *offsets;    // [npairs][nblk][2]  per block: kept before it, equal-to-T before it
-  int32_t *state;      // [npairs][4]        prefix, need, keep_all
+  uint32_t *hist;      // [npairs][kBins]  level-0 histogram
+  uint32_t *counters;  // [npairs][4]  [2]: candidates appended
+  OamState *state;     // [npairs]
+  int32_t *blk_gt;     // [npairs][kMaxBlocks]  keys above bin b0 per block
+  int32_t *blk_off;    // [npairs][kMaxBlocks]  first output slot per block
+  uint32_t *cand_key;  // [npairs][kCandCap]
+  int32_t *cand_idx;   // [npairs][kCandCap]
   int32_t *idx_out;    // [npairs][top_k]
   int32_t *n_kept;     // [npairs]
 };
@@ -51,7 +74,8 @@ __device__ __forceinline__ int pair_len(const OamDev &o, int pair) {
   return min(max(o.seq_lens[pair / o.KH], 0), o.L_cap);
 }
 
-// Exclusive prefix sum of one value per thread over a 256-thread block.
+// Exclusive prefix sum of one value per thread over a 256-thread block;
+// *total gets the sum.  Every thread must call it.
 __device__ __forceinline__ int block_exclusive_scan(int v, int *s_tmp, int *total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int incl = v;
@@ -70,18 +94,16 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *s_tmp, int *tota
   return base + incl - v;
 }
 
-// In a histogram of nb bins, the bin holding the need-th largest key
-// (need >= 1): returns the bin and sets *above to the number of keys in
-// higher bins.  All 256 threads call it; every thread gets the result.
+// In a histogram of nb bins (1024 or 2048), the bin holding the need-th
+// largest entry (1 <= need <= entries): returns it and sets *above to the
+// entries in higher bins.  All 256 threads call it; all get the result.
 __device__ int select_bin(const uint32_t *hist, int nb, int need, int *above, int *s_tmp, int *s_res) {
   const int tid = threadIdx.x;
-  const int per = nb / 256;  // 8 or 4 bins per thread, taken from the top down
+  const int per = nb / 256;  // bins per thread, taken from the top down
   int local = 0;
   for (int j = 0; j < per; ++j) local += (int)hist[nb - 1 - (tid * per + j)];
   int tot;
   const int before = block_exclusive_scan(local, s_tmp, &tot);
-  if (tid == 0) s_res[0] = -1;
-  __syncthreads();
   if (before < need && need <= before + local) {
     int run = before;
     for (int j = 0; j < per; ++j) {
@@ -100,79 +122,6 @@ __device__ int select_bin(const uint32_t *hist, int nb, int need, int *above, in
   *above = s_res[1];
   __syncthreads();
   return bin;
-}
-
-// Threshold state of a pair after `levels` histogram levels: the key prefix
-// found so far and how many keys equal to that prefix must still be kept.
-struct Thresh {
-  uint32_t prefix;  // digits found so far
-  int need;         // keys to keep among those matching the prefix
-  bool keep_all;
-};
-
-__device__ __forceinline__ Thresh load_state(const OamDev &o, int pair) {
-  const int32_t *st = o.state + 4 * pair;
-  Thresh th;
-  th.prefix = (uint32_t)st[0];
-  th.need = st[1];
-  th.keep_all = st[2] != 0;
-  return th;
-}
-
-// One workgroup per pair: fold histogram level LEVEL into the pair's
-// threshold state (level 0 also initialises it).
-template <int LEVEL>
-__global__ __launch_bounds__(256) void oam_resolve_kernel(OamDev o) {
-  __shared__ int s_tmp[4], s_res[2];
-  const int pair = blockIdx.x;
-  Thresh th;
-  if (LEVEL == 0) {
-    const int L = pair_len(o, pair);
-    th.keep_all = o.top_k >= L;
-    th.prefix = 0;
-    th.need = min(o.top_k, L);
-  } else {
-    th = load_state(o, pair);
-  }
-  if (!th.keep_all) {
-    const int npairs = o.B * o.KH;
-    const uint32_t *h = o.hist + ((size_t)LEVEL * npairs + pair) * kBins;
-    int above;
-    const int bin = select_bin(h, LEVEL == 2 ? 1024 : kBins, th.need, &above, s_tmp, s_res);
-    th.need -= above;
-    th.prefix = LEVEL == 0 ? (uint32_t)bin : (LEVEL == 1 ? (th.prefix << 11) | bin : (th.prefix << 10) | bin);
-  }
-  if (threadIdx.x == 0) {
-    int32_t *st = o.state + 4 * pair;
-    st[0] = (int32_t)th.prefix;
-    st[1] = th.need;
-    st[2] = th.keep_all ? 1 : 0;
-  }
-}
-
-// One workgroup per pair: exclusive prefix over its blocks of (kept, equal)
-// counts, so each write block knows where its indices start.
-__global__ __launch_bounds__(256) void oam_offsets_kernel(OamDev o) {
-  __shared__ int s_tmp[4];
-  const int pair = blockIdx.x;
-  const Thresh th = load_state(o, pair);
-  const int32_t *cnt = o.counts + (int64_t)pair * o.nblk * 2;
-  int32_t *off = o.offsets + (int64_t)pair * o.nblk * 2;
-  int run_k = 0, run_e = 0;
-  for (int j0 = 0; j0 < o.nblk; j0 += 256) {
-    const int j = j0 + threadIdx.x;
-    const int g = j < o.nblk ? cnt[2 * j] : 0, e = j < o.nblk ? cnt[2 * j + 1] : 0;
-    int te, tk;
-    const int e_before = run_e + block_exclusive_scan(e, s_tmp, &te);
-    const int take = th.keep_all ? 0 : min(e, max(0, th.need - e_before));
-    const int k_before = run_k + block_exclusive_scan(g + take, s_tmp, &tk);
-    if (j < o.nblk) {
-      off[2 * j] = k_before;
-      off[2 * j + 1] = e_before;
-    }
-    run_k += tk;
-    run_e += te;
-  }
 }
 
 __global__ __launch_bounds__(256) void zero_kernel(uint32_t *p, size_t n) {
@@ -299,74 +248,180 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
     if (s_hist[i]) atomicAdd(gh + i, s_hist[i]);
 }
 
-// Histogram levels 1 and 2 over the keys matching the prefix found so far.
-template <int LEVEL>
-__global__ __launch_bounds__(256) void oam_hist_kernel(OamDev o) {
-  __shared__ uint32_t s_hist[kBins];
-  const int pair = blockIdx.y;
-  const int L = pair_len(o, pair);
-  const int blk0 = blockIdx.x * kBlockTok;
-  if (blk0 >= L) return;
-  const Thresh th = load_state(o, pair);
-  if (th.keep_all) return;
+// Exact selection inside bin b0 by the select pass: the
+// need-th largest key T among the items of bin b0, and, among the items equal
+// to T, the need'-th smallest index I_T (need' = how many of them are kept).
+// Items come from the candidate list or, if it overflowed, from all scores.
+template <bool FROM_LIST>
+__device__ void select_threshold(const OamDev &o, int pair, int n, int b0, int need, uint32_t *s_hist, int *s_tmp,
+                                 int *s_res, uint32_t *T_out, int *I_out) {
   const int tid = threadIdx.x;
+  const uint32_t *ck = o.cand_key + (size_t)pair * kCandCap;
+  const int32_t *ci = o.cand_idx + (size_t)pair * kCandCap;
+  const float *sc = o.scores + (int64_t)pair * o.L_max;
+  auto item = [&](int i, uint32_t &key, int &idx) {
+    if constexpr (FROM_LIST) {
+      key = ck[i];
+      idx = ci[i];
+    } else {
+      key = order_key(sc[i]);
+      idx = i;
+    }
+  };
+  int above;
+  // digit 2: key bits 20..10 of the items with top digit b0
   for (int i = tid; i < kBins; i += 256) s_hist[i] = 0u;
   __syncthreads();
-  const float *sc = o.scores + (int64_t)pair * o.L_max;
-  const int n = min(kBlockTok, L - blk0);
   for (int i = tid; i < n; i += 256) {
-    const uint32_t key = order_key(sc[blk0 + i]);
-    if (LEVEL == 1) {
-      if ((key >> 21) == th.prefix) atomicAdd(&s_hist[(key >> 10) & 0x7FFu], 1u);
-    } else {
-      if ((key >> 10) == th.prefix) atomicAdd(&s_hist[key & 0x3FFu], 1u);
-    }
+    uint32_t key; int idx;
+    item(i, key, idx);
+    if ((int)(key >> 21) == b0) atomicAdd(&s_hist[(key >> 10) & 0x7FFu], 1u);
   }
   __syncthreads();
-  const int npairs = o.B * o.KH;
-  uint32_t *gh = o.hist + ((size_t)LEVEL * npairs + pair) * kBins;
-  for (int i = tid; i < (LEVEL == 2 ? 1024 : kBins); i += 256)
-    if (s_hist[i]) atomicAdd(gh + i, s_hist[i]);
+  uint32_t prefix = ((uint32_t)b0 << 11) | (uint32_t)select_bin(s_hist, kBins, need, &above, s_tmp, s_res);
+  need -= above;
+  // digit 3: key bits 9..0
+  for (int i = tid; i < kBins; i += 256) s_hist[i] = 0u;
+  __syncthreads();
+  for (int i = tid; i < n; i += 256) {
+    uint32_t key; int idx;
+    item(i, key, idx);
+    if ((key >> 10) == prefix) atomicAdd(&s_hist[key & 0x3FFu], 1u);
+  }
+  __syncthreads();
+  const uint32_t T = (prefix << 10) | (uint32_t)select_bin(s_hist, 1024, need, &above, s_tmp, s_res);
+  need -= above;
+  // among keys equal to T, the need-th smallest index: digits of 11 and 10
+  // bits of the index, bins reversed so "largest bin" means smallest index
+  for (int i = tid; i < kBins; i += 256) s_hist[i] = 0u;
+  __syncthreads();
+  for (int i = tid; i < n; i += 256) {
+    uint32_t key; int idx;
+    item(i, key, idx);
+    if (key == T) atomicAdd(&s_hist[2047 - (idx >> 10)], 1u);
+  }
+  __syncthreads();
+  const int ihi = 2047 - select_bin(s_hist, kBins, need, &above, s_tmp, s_res);
+  need -= above;
+  for (int i = tid; i < kBins; i += 256) s_hist[i] = 0u;
+  __syncthreads();
+  for (int i = tid; i < n; i += 256) {
+    uint32_t key; int idx;
+    item(i, key, idx);
+    if (key == T && (idx >> 10) == ihi) atomicAdd(&s_hist[1023 - (idx & 0x3FF)], 1u);
+  }
+  __syncthreads();
+  const int ilo = 1023 - select_bin(s_hist, 1024, need, &above, s_tmp, s_res);
+  *T_out = T;
+  *I_out = (ihi << 10) | ilo;
 }
 
-// Keys above the threshold and keys equal to it, per block.
-__global__ __launch_bounds__(256) void oam_count_kernel(OamDev o) {
-  __shared__ int s_tmp[4];
+// Candidate pass: block j of pair p finds b0 from the pair's histogram,
+// counts its keys above bin b0 and appends its keys of bin b0 to the pair's
+// list.  Block 0 records b0 and how many keys of bin b0 are kept.
+__global__ __launch_bounds__(256) void oam_candidate_kernel(OamDev o) {
+  __shared__ uint32_t s_hist[kBins];
+  __shared__ int s_tmp[4], s_res[2], s_base;
   const int pair = blockIdx.y;
   const int L = pair_len(o, pair);
   const int blk0 = blockIdx.x * kBlockTok;
-  if (blk0 >= L) {
-    if (threadIdx.x == 0) {
-      int32_t *c = o.counts + ((int64_t)pair * o.nblk + blockIdx.x) * 2;
-      c[0] = 0;
-      c[1] = 0;
-    }
-    return;
-  }
-  const Thresh th = load_state(o, pair);
+  if (blk0 >= L || o.top_k >= L) return;  // top_k >= L: every token is kept
   const int tid = threadIdx.x;
+  for (int i = tid; i < kBins; i += 256) s_hist[i] = o.hist[(size_t)pair * kBins + i];
+  __syncthreads();
+  int above;
+  const int b0 = select_bin(s_hist, kBins, o.top_k, &above, s_tmp, s_res);
+  if (blockIdx.x == 0 && tid == 0) {
+    o.state[pair].b0 = b0;
+    o.state[pair].need = o.top_k - above;
+  }
   const float *sc = o.scores + (int64_t)pair * o.L_max;
   const int n = min(kBlockTok, L - blk0);
-  int gt = 0, eq = 0;
-  if (!th.keep_all) {
-    for (int i = tid; i < n; i += 256) {
-      const uint32_t key = order_key(sc[blk0 + i]);
-      gt += key > th.prefix;
-      eq += key == th.prefix;
-    }
+  uint32_t keys[8];
+  int gt = 0, nc = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int i = tid + 256 * j;
+    keys[j] = i < n ? order_key(sc[blk0 + i]) : 0u;
+    const int d = (int)(keys[j] >> 21);
+    gt += i < n && d > b0;
+    nc += i < n && d == b0;
   }
-  int tg, te;
+  int tg, tc;
   block_exclusive_scan(gt, s_tmp, &tg);
-  block_exclusive_scan(eq, s_tmp, &te);
+  const int cpos = block_exclusive_scan(nc, s_tmp, &tc);
   if (tid == 0) {
-    int32_t *c = o.counts + ((int64_t)pair * o.nblk + blockIdx.x) * 2;
-    c[0] = th.keep_all ? n : tg;
-    c[1] = th.keep_all ? 0 : te;
+    o.blk_gt[(size_t)pair * kMaxBlocks + blockIdx.x] = tg;
+    s_base = tc ? (int)atomicAdd(o.counters + 4 * pair + 2, (uint32_t)tc) : 0;
+  }
+  __syncthreads();
+  int pos = s_base + cpos;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int i = tid + 256 * j;
+    if (i < n && (int)(keys[j] >> 21) == b0) {
+      if (pos < kCandCap) {
+        o.cand_key[(size_t)pair * kCandCap + pos] = keys[j];
+        o.cand_idx[(size_t)pair * kCandCap + pos] = blk0 + i;
+      }
+      ++pos;
+    }
   }
 }
 
-// Ordered compaction: thread i of a block owns tokens 8i..8i+7 of it.
+// Select pass, one workgroup per pair: T and I_T, then the output offset of
+// every block (keys above bin b0 plus kept keys of bin b0 before it).
+__global__ __launch_bounds__(256) void oam_select_kernel(OamDev o) {
+  __shared__ uint32_t s_hist[kBins];
+  __shared__ int s_kept[kMaxBlocks];
+  __shared__ int s_tmp[4], s_res[2];
+  const int pair = blockIdx.x;
+  const int L = pair_len(o, pair);
+  if (L == 0 || o.top_k >= L) return;
+  const int tid = threadIdx.x;
+  const int b0 = o.state[pair].b0, need = o.state[pair].need;
+  const int C = (int)o.counters[4 * pair + 2];
+  const float *sc = o.scores + (int64_t)pair * o.L_max;
+  uint32_t T;
+  int I_T;
+  if (C <= kCandCap) select_threshold<true>(o, pair, C, b0, need, s_hist, s_tmp, s_res, &T, &I_T);
+  else select_threshold<false>(o, pair, L, b0, need, s_hist, s_tmp, s_res, &T, &I_T);
+  const int nblk = (L + kBlockTok - 1) / kBlockTok;
+  for (int j = tid; j < nblk; j += 256) s_kept[j] = 0;
+  __syncthreads();
+  const int nitems = C <= kCandCap ? C : L;
+  for (int i = tid; i < nitems; i += 256) {
+    uint32_t key;
+    int idx;
+    if (C <= kCandCap) {
+      key = o.cand_key[(size_t)pair * kCandCap + i];
+      idx = o.cand_idx[(size_t)pair * kCandCap + i];
+    } else {
+      key = order_key(sc[i]);
+      idx = i;
+    }
+    if ((int)(key >> 21) == b0 && (key > T || (key == T && idx <= I_T))) atomicAdd(&s_kept[idx / kBlockTok], 1);
+  }
+  __syncthreads();
+  int run = 0;
+  for (int j0 = 0; j0 < nblk; j0 += 256) {
+    const int j = j0 + tid;
+    const int v = j < nblk ? o.blk_gt[(size_t)pair * kMaxBlocks + j] + s_kept[j] : 0;
+    int tot;
+    const int ex = block_exclusive_scan(v, s_tmp, &tot);
+    if (j < nblk) o.blk_off[(size_t)pair * kMaxBlocks + j] = run + ex;
+    run += tot;
+  }
+  if (tid == 0) {
+    o.state[pair].T = T;
+    o.state[pair].I_T = I_T;
+  }
+}
+
+// Ordered compaction: the block's keys are staged in LDS with coalesced
+// loads, then thread t takes tokens 8t..8t+7 of the block in order.
 __global__ __launch_bounds__(256) void oam_write_kernel(OamDev o) {
+  __shared__ uint32_t s_key[kBlockTok + kBlockTok / 8];  // one pad word per 8 keys
   __shared__ int s_tmp[4];
   const int pair = blockIdx.y;
   const int L = pair_len(o, pair);
@@ -379,42 +434,32 @@ __global__ __launch_bounds__(256) void oam_write_kernel(OamDev o) {
   }
   const int blk0 = blockIdx.x * kBlockTok;
   if (blk0 >= L) return;
-  const Thresh th = load_state(o, pair);
-  // kept and equal-to-threshold tokens in the blocks before this one
-  const int32_t *off = o.offsets + ((int64_t)pair * o.nblk + blockIdx.x) * 2;
-  const int kept_before = off[0], eq_before = off[1];
+  const bool keep_all = o.top_k >= L;
   const float *sc = o.scores + (int64_t)pair * o.L_max;
   const int n = min(kBlockTok, L - blk0);
-  uint32_t keys[8];
-  int eqc = 0;
+  if (keep_all) {
+    for (int i = tid; i < n; i += 256) out[blk0 + i] = blk0 + i;
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int i = 8 * tid + j;
-    keys[j] = i < n ? order_key(sc[blk0 + i]) : 0u;
-    eqc += (i < n) && !th.keep_all && keys[j] == th.prefix;
+    const int r = tid + 256 * j;
+    s_key[r + (r >> 3)] = r < n ? order_key(sc[blk0 + r]) : 0u;
+  }
+  __syncthreads();
+  const uint32_t T = o.state[pair].T;
+  const int I_T = o.state[pair].I_T;
+  bool keep[8];
+  int kc = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = 8 * tid + j;
+    const uint32_t key = s_key[r + (r >> 3)];
+    keep[j] = r < n && (key > T || (key == T && blk0 + r <= I_T));
+    kc += keep[j];
   }
   int tot;
-  const int eq_rank0 = eq_before + block_exclusive_scan(eqc, s_tmp, &tot);
-  bool keep[8];
-  int kc = 0, er = eq_rank0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int i = 8 * tid + j;
-    bool k = false;
-    if (i < n) {
-      if (th.keep_all) {
-        k = true;
-      } else if (keys[j] > th.prefix) {
-        k = true;
-      } else if (keys[j] == th.prefix) {
-        k = er < th.need;
-        ++er;
-      }
-    }
-    keep[j] = k;
-    kc += k;
-  }
-  int pos = kept_before + block_exclusive_scan(kc, s_tmp, &tot);
+  int pos = o.blk_off[(size_t)pair * kMaxBlocks + blockIdx.x] + block_exclusive_scan(kc, s_tmp, &tot);
 #pragma unroll
   for (int j = 0; j < 8; ++j)
     if (keep[j]) out[pos++] = blk0 + 8 * tid + j;
@@ -434,7 +479,6 @@ hipError_t launch_oam(const oam_topk_args &a, const OamPlan &plan, hipStream_t s
   o.QH = g.KH * a.G;
   o.top_k = a.top_k;
   o.L_cap = g.max_seq_len;
-  o.nblk = plan.nchunk;
   o.seq_lens = g.seq_lens;
   o.seq_offset = g.seq_offset;
   o.stride_h = g.stride_h;
@@ -448,50 +492,41 @@ hipError_t launch_oam(const oam_topk_args &a, const OamPlan &plan, hipStream_t s
   o.beta = a.beta;
   o.scores = plan.scores;
   o.hist = plan.hist;
-  o.counts = plan.chunk_cnt;
-  o.offsets = plan.offsets;
-  o.state = plan.state;
+  o.counters = plan.counters;
+  o.state = reinterpret_cast<OamState *>(plan.state);
+  o.blk_gt = plan.blk_gt;
+  o.blk_off = plan.blk_off;
+  o.cand_key = plan.cand_key;
+  o.cand_idx = plan.cand_idx;
   o.idx_out = a.idx_out;
   o.n_kept = a.n_kept;
 
-  const size_t nhist = (size_t)3 * npairs * kBins;
-  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((nhist + 255) / 256 < 4096 ? (nhist + 255) / 256 : 4096)), dim3(256),
-                     0, s, plan.hist, nhist);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (!a.vlog) {
-    e = launch_value_lognorm(g, a.v, a.eps, plan.vlog, plan.vlog_stride, s);
-    if (e != hipSuccess) return e;
-  }
-  dim3 grid(plan.nchunk, npairs), blk(256), pgrid(npairs);
-#define LCDG_CHECK_LAUNCH() if ((e = hipGetLastError()) != hipSuccess) return e
-  if (plan.nchunk > 0) {
-    dim3 sgrid((g.max_seq_len + kScoreTok - 1) / kScoreTok, npairs);
+  hipError_t e;
+  const int nblk = (g.max_seq_len + kBlockTok - 1) / kBlockTok;
+  if (nblk > 0) {
+    // histogram and counters start at zero (a fill kernel, not a memset)
+    const size_t nz = (size_t)npairs * (kBins + 4);
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((nz + 255) / 256 < 4096 ? (nz + 255) / 256 : 4096)), dim3(256), 0,
+                       s, plan.hist, nz);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!a.vlog) {
+      e = launch_value_lognorm(g, a.v, a.eps, plan.vlog, plan.vlog_stride, s);
+      if (e != hipSuccess) return e;
+    }
+    dim3 sgrid((g.max_seq_len + kScoreTok - 1) / kScoreTok, npairs), blk(256);
     if (g.D == 128) hipLaunchKernelGGL((oam_score_kernel<128>), sgrid, blk, 0, s, o);
     else hipLaunchKernelGGL((oam_score_kernel<64>), sgrid, blk, 0, s, o);
-    LCDG_CHECK_LAUNCH();
-    hipLaunchKernelGGL((oam_resolve_kernel<0>), pgrid, blk, 0, s, o);
-    LCDG_CHECK_LAUNCH();
-    hipLaunchKernelGGL((oam_hist_kernel<1>), grid, blk, 0, s, o);
-    LCDG_CHECK_LAUNCH();
-    hipLaunchKernelGGL((oam_resolve_kernel<1>), pgrid, blk, 0, s, o);
-    LCDG_CHECK_LAUNCH();
-    hipLaunchKernelGGL((oam_hist_kernel<2>), grid, blk, 0, s, o);
-    LCDG_CHECK_LAUNCH();
-    hipLaunchKernelGGL((oam_resolve_kernel<2>), pgrid, blk, 0, s, o);
-    LCDG_CHECK_LAUNCH();
-    hipLaunchKernelGGL(oam_count_kernel, grid, blk, 0, s, o);
-    LCDG_CHECK_LAUNCH();
-    hipLaunchKernelGGL(oam_offsets_kernel, pgrid, blk, 0, s, o);
-    LCDG_CHECK_LAUNCH();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(oam_candidate_kernel, dim3(nblk, npairs), blk, 0, s, o);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(oam_select_kernel, dim3(npairs), blk, 0, s, o);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-#undef LCDG_CHECK_LAUNCH
   // the write pass also runs for empty caches: it sets n_kept and the -1 fill
-  dim3 wgrid(plan.nchunk > 0 ? plan.nchunk : 1, npairs);
-  hipLaunchKernelGGL(oam_write_kernel, wgrid, blk, 0, s, o);
+  hipLaunchKernelGGL(oam_write_kernel, dim3(nblk > 0 ? nblk : 1, npairs), dim3(256), 0, s, o);
   return hipGetLastError();
 }
 
-int oam_block_tokens() { return kBlockTok; }
+int oam_max_tokens() { return kMaxBlocks * kBlockTok; }
 
 }  // namespace lcdg

@@ -142,3 +142,48 @@ def test_oam_128k_full_size():
     ref, _ = oracle.attention_rows(pk, rows, nthreads=4)
     o = out.cpu().numpy().reshape(-1, w.D)[[b * w.QH + h for b, h in rows]]
     assert np.abs(o - ref).max() <= 2e-3
+
+
+def _topk_from_vlog(vlog_row, top_k, D=128, G=8):
+    """oam_score_topk with zero keys and a given value term: every score is
+    exactly beta * vlog (beta = 1), so the kept set is fixed by vlog alone."""
+    L = len(vlog_row)
+    lens = np.array([L], np.int32)
+    w = synth.workload("oam_128k", B=1, KH=1, G=G, D=D, lens=lens, seed=69)
+    q, k, v, g = synth.generate(w)
+    k[:] = 0
+    qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
+    kd = to_dev(k)
+    geom = dev_geom(g)
+    vl = torch.from_numpy(np.ascontiguousarray(vlog_row, dtype=np.float32)).to(DEV)
+    scores = torch.full((1, L), float("nan"), dtype=torch.float32, device=DEV)
+    idx, nk = pkg.oam_score_topk(qd, kd, geom, w.G, top_k, vlog=vl, vlog_stride=L, scores_out=scores)
+    torch.cuda.synchronize()
+    sc = scores.cpu().numpy()[0]
+    np.testing.assert_array_equal(sc, vlog_row.astype(np.float32))
+    return idx.cpu().numpy()[0], int(nk.cpu().numpy()[0])
+
+
+def test_oam_many_candidates_in_threshold_bin():
+    # 20000 distinct scores inside one top-digit bin ([1.0, 1.25)): more
+    # candidates than the list holds, so the selection reads the scores
+    rng = np.random.default_rng(70)
+    vl = (1.0 + 0.2 * rng.permutation(20000) / 20000.0).astype(np.float32)
+    log_case("oam candidate overflow")
+    for top_k in (1, 4096, 12345, 19999):
+        idx, nk = _topk_from_vlog(vl, top_k)
+        assert nk == top_k
+        np.testing.assert_array_equal(idx[:nk], exact_topk(vl, top_k))
+
+
+def test_oam_tie_group_cut_at_threshold():
+    # few distinct values, so the K-th key has many equals; the kept ones must
+    # be the lowest indices of that tie group (list path and overflow path)
+    rng = np.random.default_rng(71)
+    for L, top_k in ((3000, 1000), (3000, 1), (9000, 4500)):
+        vl = (1.0 + 0.01 * rng.integers(0, 7, L)).astype(np.float32)
+        log_case(f"oam tie group L={L} K={top_k}")
+        idx, nk = _topk_from_vlog(vl, top_k)
+        assert nk == top_k
+        np.testing.assert_array_equal(idx[:nk], exact_topk(vl, top_k))
+        assert np.all(idx[nk:] == -1)
