@@ -132,9 +132,10 @@ __global__ __launch_bounds__(256) void zero_kernel(uint32_t *p, size_t n) {
 // split into three bf16 parts hi + mid + lo (24 significant bits) placed in
 // B-operand columns 4j, 4j+1, 4j+2 (column 4j+3 is zero), so one 16x16x32
 // MFMA chain per 16 tokens gives, in every lane quad, the three partial dot
-// products of its four tokens; two quad DPP adds finish q_bar . k_t.  Wave w
-// of the workgroup streams tiles [16w', 16w'+16) of 32 tokens, two in flight.
+// products of its four tokens; two quad DPP adds finish q_bar . k_t.  Each
+// wave of the workgroup streams a quarter of its tokens in 32-token tiles.
 constexpr int kScoreTok = 8192;   // tokens per workgroup of the score pass
+constexpr int kScoreBufs = 3;     // tiles in the register ring of each wave
 
 __device__ __forceinline__ float quad_sum3(float v) {
   // lane 4j gets v(4j) + v(4j+1) + v(4j+2); quad_perm(1,2,3,0) = 0x39, (2,3,0,1) = 0x4E
@@ -149,11 +150,13 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
   constexpr int kTilesPerWave = kScoreTok / 32 / 4;
   __shared__ uint32_t s_hist[kBins];
   __shared__ float s_qbar[D];
+  __shared__ float s_sc[kScoreTok];
   const int pair = blockIdx.y;
   const int L = pair_len(o, pair);
   const int blk0 = blockIdx.x * kScoreTok;
   if (blk0 >= L) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the tile loop is a scalar loop
   const int col = lane & 15, cg = lane >> 4;
   for (int i = tid; i < kBins; i += 256) s_hist[i] = 0u;
   const int b = pair / o.KH, kh = pair - b * o.KH;
@@ -197,6 +200,9 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
     u32x4_t k[2][KB];
     u32x4_t vl[2];
   };
+  // Scores are collected in LDS and written out once, in full coalesced
+  // lines, when the block's tiles are done: small scattered stores between
+  // the K loads cost far more HBM time than their bytes.
   auto load = [&](KTile &R, int tile, bool valid) {
     const int t0 = blk0 + 32 * tile;
     const uint32_t oob = valid ? 0u : 0x80000000u;
@@ -207,8 +213,13 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
       for (int kb = 0; kb < KB; ++kb) R.k[tb][kb] = __builtin_amdgcn_raw_buffer_load_b128(krs, off + 64 * kb, 0, 0);
       R.vl[tb] = __builtin_amdgcn_raw_buffer_load_b128(vrs, ((uint32_t)(t0 + 16 * tb + 4 * cg) * 4) | oob, 0, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
-  auto compute = [&](const KTile &R, int tile) {
+  // Lane (col = 4j + p, cg) ends with, for p == 0, the full q_bar . k of the
+  // four tokens 4cg..4cg+3 of each 16-token block; it publishes token 4cg + j.
+  const int jq = col >> 2;
+  const bool leader = (col & 3) == 0;
+  auto compute = [&](const KTile &R, int tile, bool valid) {
     const int t0 = blk0 + 32 * tile;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
@@ -218,31 +229,38 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, R.k[tb][kb]), qop[kb], acc, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = quad_sum3(acc[i]);
-      const int t = t0 + 16 * tb + 4 * cg;
-      if (col == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (t + i < L) {
-            const float s = acc[i] * o.score_scale + o.beta * __uint_as_float(R.vl[tb][i]);
-            sc[t + i] = s;
-            atomicAdd(&s_hist[order_key(s) >> 21], 1u);
-          }
-        }
+      const float dot = jq == 0 ? acc[0] : jq == 1 ? acc[1] : jq == 2 ? acc[2] : acc[3];
+      const uint32_t vw = jq == 0 ? R.vl[tb][0] : jq == 1 ? R.vl[tb][1] : jq == 2 ? R.vl[tb][2] : R.vl[tb][3];
+      const int t = t0 + 16 * tb + 4 * cg + jq;
+      const bool mine = valid && leader && t < L;
+      const float sv = dot * o.score_scale + o.beta * __uint_as_float(vw);
+      if (mine) {
+        s_sc[t - blk0] = sv;
+        atomicAdd(&s_hist[order_key(sv) >> 21], 1u);
       }
     }
   };
-  // this wave's tiles, stopping at the end of the sequence
+  // This wave's tiles through a ring of kScoreBufs register buffers: tile i
+  // is loaded kScoreBufs-1 tiles before it is scored.  The step count is
+  // rounded up to a multiple of the ring; the extra steps load and publish
+  // nothing.
   const int tw0 = kTilesPerWave * wave;
   const int ntw = max(0, min(kTilesPerWave, (L - blk0 - 32 * tw0 + 31) / 32));
-  KTile ra, rb;
-  load(ra, tw0, ntw > 0);
-  for (int i = 0; i < ntw; i += 2) {
-    load(rb, tw0 + i + 1, i + 1 < ntw);
-    compute(ra, tw0 + i);
-    load(ra, tw0 + i + 2, i + 2 < ntw);
-    if (i + 1 < ntw) compute(rb, tw0 + i + 1);
+  const int nst = (ntw + kScoreBufs - 1) / kScoreBufs * kScoreBufs;
+  KTile buf[kScoreBufs];
+#pragma unroll
+  for (int j = 0; j + 1 < kScoreBufs; ++j) load(buf[j], tw0 + j, j < ntw);
+  for (int i = 0; i < nst; i += kScoreBufs) {
+#pragma unroll
+    for (int j = 0; j < kScoreBufs; ++j) {
+      const int ahead = i + j + kScoreBufs - 1;
+      load(buf[(j + kScoreBufs - 1) % kScoreBufs], tw0 + ahead, ahead < ntw);
+      compute(buf[j], tw0 + i + j, i + j < ntw);
+    }
   }
   __syncthreads();
+  const int nblk_tok = min(kScoreTok, L - blk0);
+  for (int i = tid; i < nblk_tok; i += 256) sc[blk0 + i] = s_sc[i];
   uint32_t *gh = o.hist + (size_t)pair * kBins;
   for (int i = tid; i < kBins; i += 256)
     if (s_hist[i]) atomicAdd(gh + i, s_hist[i]);
