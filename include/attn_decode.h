@@ -104,7 +104,10 @@ typedef struct {
  *               set written by oam_score_topk
  *   softmax_scale  multiplies q.k; 0 selects 1/sqrt(D)
  *   split_tokens   tokens per split-KV chunk (multiple of 32); 0 = library
- *               default (1024 for bf16/int8, 256 for fp32)
+ *               default: for bf16/int8 about one chunk per decode worker
+ *               of a 256-CU device, from B, KH, G and max_seq_len (or
+ *               idx_stride), between 32 and 2048 (1024 with token_idx)
+ *               tokens; 256 for fp32
  *   workspace   caller-owned scratch of at least attn_decode_workspace_size()
  *               bytes, 256-byte aligned; holds the work-list and partials
  *   out         [B][KH*G][D] in out_dtype (ATTN_F32 or ATTN_BF16)

@@ -1,5 +1,6 @@
 // C ABI of libattn_decode.so: host-side validation, workspace layout and
 // dispatch.  Nothing is enqueued until every argument check has passed.
+#include <algorithm>
 #include <math.h>
 #include <stdio.h>
 
@@ -110,13 +111,25 @@ attn_status plan_decode(const attn_decode_args *a, DecodeLayout *L) {
       return fail(ATTN_ERR_INVALID_ARG, "q, k and v must be 16-byte aligned");
   }
   L->mfma = mfma;
-  L->split = a->split_tokens ? a->split_tokens : (mfma ? 1024 : 256);
+  L->ngb = (a->G + 15) / 16;
+  L->max_tokens = a->token_idx ? a->idx_stride : g.max_seq_len;
+  if (a->split_tokens) {
+    L->split = a->split_tokens;
+  } else if (!mfma) {
+    L->split = 256;
+  } else {
+    // About one chunk per worker of a full decode grid (2048 one-wave
+    // workers on a 256-CU device): each worker then writes about one partial
+    // per head, and partial writes cost far more HBM time than their bytes
+    // while the KV stream runs.  32..2048 tokens (1024 with an index list).
+    const int64_t tiles = (int64_t)g.B * g.KH * L->ngb * (((int64_t)L->max_tokens + 31) / 32);
+    const int64_t ct = std::min<int64_t>(std::max<int64_t>(tiles / 2048, 1), a->token_idx ? 32 : 64);
+    L->split = (int32_t)(32 * ct);
+  }
   if (mfma && ((int64_t)g.max_seq_len + 64) * g.stride_t * elem_size(a->kv_dtype) >= (int64_t(1) << 31))
     return fail(ATTN_ERR_UNSUPPORTED, "one (sequence, KV head) may span at most 2 GiB of rows");
   if (mfma && a->token_idx && L->split > 1024)
     return fail(ATTN_ERR_UNSUPPORTED, "with token_idx, split_tokens must be <= 1024");
-  L->ngb = (a->G + 15) / 16;
-  L->max_tokens = a->token_idx ? a->idx_stride : g.max_seq_len;
   L->max_chunks = ((int64_t)L->max_tokens + L->split - 1) / L->split;
   const int64_t QH = (int64_t)g.KH * a->G;
   L->max_partials = 2 * (int64_t)g.B * QH * L->max_chunks;

@@ -146,18 +146,40 @@ def test_merge_lse_of_oracle_partials():
             assert abs(lse[r] - rl) <= 1e-5
 
 
-def test_gqa32k_full_size_sampled_rows():
-    """The 16 x 8 x 8 x 128 x 32768 bf16 workload in the benchmark's launch configuration."""
-    w = synth.workload("gqa32k")
+def _full_size_sampled_rows(name, nrows, seed):
+    """A full-size workload in the benchmark's launch configuration (its own
+    split-KV chunk size), compared with the oracle on sampled output rows;
+    then, for every row, the property that the softmax weights sum to one: a
+    constant V comes back unchanged, and lse does not depend on V."""
+    w = synth.workload(name)
     q, k, v, g = synth.generate(w)
-    log_case("gqa32k full size")
-    out, lse = run_decode(w, q, k, v, g, split_tokens=1024)
+    log_case(f"{name} full size, split {w.split_tokens}")
+    out, lse = run_decode(w, q, k, v, g, split_tokens=w.split_tokens)
     p = problem(w, q, k, v, g)
-    rng = np.random.default_rng(1)
-    rows = [(int(b), int(h)) for b, h in zip(rng.integers(0, w.B, 24), rng.integers(0, w.QH, 24))]
+    rng = np.random.default_rng(seed)
+    rows = [(int(b), int(h)) for b, h in zip(rng.integers(0, w.B, nrows), rng.integers(0, w.QH, nrows))]
     rows += [(0, 0), (w.B - 1, w.QH - 1)]
     ref, ref_lse = oracle.attention_rows(p, rows, nthreads=16)
     idx = [b * w.QH + h for b, h in rows]
     check(out[idx], lse[idx], ref, ref_lse)
-    # weights sum to one: a constant-V run returns the constant (checked for all rows)
-    del k
+    del p, v
+    vc = np.full(k.shape, 0x3FC0, dtype=np.uint16)  # bf16 1.5 everywhere
+    out_c, lse_c = run_decode(w, q, k, vc, g, split_tokens=w.split_tokens)
+    live = np.repeat(g.lens > 0, w.QH)
+    assert np.abs(out_c[live] - 1.5).max() <= 1e-5
+    assert np.array_equal(lse_c, lse)
+
+
+def test_gqa32k_full_size_sampled_rows():
+    """The 16 x 8 x 8 x 128 x 32768 bf16 workload."""
+    _full_size_sampled_rows("gqa32k", 24, 1)
+
+
+def test_dense128k_full_size_sampled_rows():
+    """The 4 x 8 x 8 x 128 x 131072 bf16 workload the benchmark's headline line times."""
+    _full_size_sampled_rows("dense128k", 16, 3)
+
+
+def test_ragged_full_size_sampled_rows():
+    """The 32-sequence ragged batch (512..131072 tokens, head-major packed cache)."""
+    _full_size_sampled_rows("ragged", 16, 4)

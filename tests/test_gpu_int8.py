@@ -139,7 +139,7 @@ def test_int8_128k_full_size():
     assert vsa[0] == np.float32(ref_vs)
     assert np.array_equal(vc, ref_v)
     del ref_v
-    out, lse = run_int8_decode(w, q, kc, vc, ks, vsa[0], g)
+    out, lse = run_int8_decode(w, q, kc, vc, ks, vsa[0], g, split=w.split_tokens)
     p = problem(w, q, kc, vc, g, k_scale=ks, k_part=64, k_scale_stride=2048, v_scale=float(vsa[0]))
     rng = np.random.default_rng(2)
     rows = [(int(b), int(h)) for b, h in zip(rng.integers(0, w.B, 12), rng.integers(0, w.QH, 12))] + [(3, 63)]
