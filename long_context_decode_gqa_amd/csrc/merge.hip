@@ -125,6 +125,99 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *o_par
   if (tid == 0 && lse) lse[row] = (Ls > 0.f) ? M + logf(Ls) : NEG_INF;
 }
 
+// Single-pass merge for D % 4 == 0, one 256-thread workgroup per row.
+// Thread (grp, q) owns the 16-byte column slice q and the slots grp,
+// grp + ng, ... of the row, and folds them in order with a running maximum
+// (online log-sum-exp: on a larger m the sums so far are rescaled), so every
+// load of the row is issued up front and there is one round trip to memory.
+// The ng slot groups are then combined through LDS in a fixed order.
+constexpr int kMergeV4Threads = 512;
+constexpr int kMergeV4Unroll = 8;
+
+template <int OUT, bool DECODE>
+__global__ __launch_bounds__(kMergeV4Threads) void merge_v4_kernel(const float *o_part, const float *m_part,
+                                                                 const float *l_part, const int32_t *rss,
+                                                                 DecodeParams dp, int32_t D, void *out, float *lse) {
+  __shared__ f32x4_t s_acc[kMergeV4Threads];
+  __shared__ float s_m[kMergeV4Threads], s_l[kMergeV4Threads];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float NEG_INF = -__builtin_huge_valf();
+  int s0, n;
+  if constexpr (DECODE) {
+    s0 = 2 * row * dp.max_chunks;
+    n = 2 * pair_chunks(dp, row / dp.G);
+  } else {
+    s0 = rss[row];
+    n = rss[row + 1] - s0;
+  }
+  const int nq = D / 4;            // column slices
+  const int ng = kMergeV4Threads / nq;
+  const int grp = tid / nq, q = tid - grp * nq;
+  float mt = NEG_INF, lt = 0.f;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  if (grp < ng) {
+    for (int base = grp; base < n; base += ng * kMergeV4Unroll) {
+      float m[kMergeV4Unroll], l[kMergeV4Unroll];
+      f32x4_t o[kMergeV4Unroll];
+#pragma unroll
+      for (int u = 0; u < kMergeV4Unroll; ++u) {
+        const int sl = base + u * ng;
+        const bool in = sl < n;
+        const int64_t i = s0 + (in ? sl : 0);
+        l[u] = in ? l_part[i] : 0.f;
+        m[u] = m_part[i];
+        o[u] = *(const f32x4_t *)(o_part + i * D + 4 * q);
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeV4Unroll; ++u) {
+        if (l[u] > 0.f) {  // empty partials (l = 0) may hold any o
+          if (m[u] > mt) {
+            const float sc = expf(mt - m[u]);
+            acc *= sc;
+            lt *= sc;
+            mt = m[u];
+          }
+          const float w = expf(m[u] - mt) * l[u];
+          acc += w * o[u];
+          lt += w;
+        }
+      }
+    }
+  }
+  s_acc[tid] = acc;
+  s_m[tid] = mt;
+  s_l[tid] = lt;
+  __syncthreads();
+  if (tid < nq) {
+    float M = NEG_INF;
+    for (int g = 0; g < ng; ++g)
+      if (s_l[g * nq + q] > 0.f) M = fmaxf(M, s_m[g * nq + q]);
+    f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+    float Ls = 0.f;
+    for (int g = 0; g < ng; ++g) {
+      const float lg = s_l[g * nq + q];
+      if (lg > 0.f) {
+        const float sc = expf(s_m[g * nq + q] - M);
+        a += sc * s_acc[g * nq + q];
+        Ls += sc * lg;
+      }
+    }
+    const float inv = Ls > 0.f ? 1.0f / Ls : 0.f;
+    const f32x4_t r = a * inv;
+    if constexpr (OUT == ATTN_F32) {
+      *(f32x4_t *)((float *)out + (int64_t)row * D + 4 * q) = r;
+    } else {
+      uint16_t *po = (uint16_t *)out + (int64_t)row * D + 4 * q;
+      const uint32_t w0 = f32_to_bf16_bits(r[0]) | (f32_to_bf16_bits(r[1]) << 16);
+      const uint32_t w1 = f32_to_bf16_bits(r[2]) | (f32_to_bf16_bits(r[3]) << 16);
+      *(uint32_t *)po = w0;
+      *(uint32_t *)(po + 2) = w1;
+    }
+    if (q == 0 && lse) lse[row] = Ls > 0.f ? M + logf(Ls) : NEG_INF;
+  }
+}
+
 __global__ __launch_bounds__(256) void copy_kernel(u32x4_t *dst, const u32x4_t *src, size_t n) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) dst[i] = src[i];
 }
@@ -151,24 +244,44 @@ hipError_t launch_merge(const float *o_part, const float *m_part, const float *l
                         int32_t rows, int32_t D, int32_t out_dtype, void *out, float *lse, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   DecodeParams none = {};
-  dim3 g(rows), blk(kMergeThreads);
-  if (out_dtype == ATTN_F32)
+  dim3 g(rows);
+  const uintptr_t oa = reinterpret_cast<uintptr_t>(o_part), ua = reinterpret_cast<uintptr_t>(out);
+  const bool v4 = D % 4 == 0 && oa % 16 == 0 && ua % (out_dtype == ATTN_F32 ? 16 : 4) == 0;
+  dim3 blk(v4 ? kMergeV4Threads : kMergeThreads);
+  if (v4 && out_dtype == ATTN_F32)
+    hipLaunchKernelGGL((merge_v4_kernel<ATTN_F32, false>), g, blk, 0, s, o_part, m_part, l_part, rss, none, D, out, lse);
+  else if (v4)
+    hipLaunchKernelGGL((merge_v4_kernel<ATTN_BF16, false>), g, blk, 0, s, o_part, m_part, l_part, rss, none, D, out, lse);
+  else if (out_dtype == ATTN_F32)
     hipLaunchKernelGGL((merge_kernel<ATTN_F32, false>), g, blk, 0, s, o_part, m_part, l_part, rss, none, D, out, lse);
   else
     hipLaunchKernelGGL((merge_kernel<ATTN_BF16, false>), g, blk, 0, s, o_part, m_part, l_part, rss, none, D, out, lse);
   return hipGetLastError();
 }
 
+// The decode path's head sizes are multiples of 4 and its partials 16-byte
+// aligned; the output may be less aligned, then the general kernel runs.
 hipError_t launch_merge_decode(const DecodeParams &p, int32_t out_dtype, void *out, float *lse, hipStream_t s) {
   const int rows = p.B * p.QH;
   if (rows <= 0) return hipSuccess;
-  dim3 g(rows), blk(kMergeThreads);
   const WorkList &w = p.wl;
+  const uintptr_t ua = reinterpret_cast<uintptr_t>(out);
+  if (p.D % 4 || ua % (out_dtype == ATTN_F32 ? 16 : 4)) {
+    dim3 g(rows), blk(kMergeThreads);
+    if (out_dtype == ATTN_F32)
+      hipLaunchKernelGGL((merge_kernel<ATTN_F32, true>), g, blk, 0, s, w.o_part, w.m_part, w.l_part, nullptr, p, p.D,
+                         out, lse);
+    else
+      hipLaunchKernelGGL((merge_kernel<ATTN_BF16, true>), g, blk, 0, s, w.o_part, w.m_part, w.l_part, nullptr, p, p.D,
+                         out, lse);
+    return hipGetLastError();
+  }
+  dim3 g(rows), blk(kMergeV4Threads);
   if (out_dtype == ATTN_F32)
-    hipLaunchKernelGGL((merge_kernel<ATTN_F32, true>), g, blk, 0, s, w.o_part, w.m_part, w.l_part, nullptr, p, p.D,
+    hipLaunchKernelGGL((merge_v4_kernel<ATTN_F32, true>), g, blk, 0, s, w.o_part, w.m_part, w.l_part, nullptr, p, p.D,
                        out, lse);
   else
-    hipLaunchKernelGGL((merge_kernel<ATTN_BF16, true>), g, blk, 0, s, w.o_part, w.m_part, w.l_part, nullptr, p, p.D,
+    hipLaunchKernelGGL((merge_v4_kernel<ATTN_BF16, true>), g, blk, 0, s, w.o_part, w.m_part, w.l_part, nullptr, p, p.D,
                        out, lse);
   return hipGetLastError();
 }

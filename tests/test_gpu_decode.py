@@ -117,28 +117,39 @@ def test_token_index_subset():
     check(out, lse, ref, ref_lse)
 
 
-def test_merge_lse_of_oracle_partials():
-    rng = np.random.default_rng(3)
-    rows, D = 37, 128
-    counts = rng.integers(0, 9, size=rows)
+@pytest.mark.parametrize("D,maxc,misaligned", [(128, 9, False), (128, 300, False), (64, 300, False),
+                                               (4, 70, False), (37, 40, False), (128, 50, True)])
+def test_merge_lse_of_oracle_partials(D, maxc, misaligned):
+    """attn_merge_lse on random partials: empty rows, empty partials holding
+    NaN outputs (they must be ignored), rows longer than one pass of the
+    single-pass kernel, odd head sizes and an output not 16-byte aligned
+    (the general kernel)."""
+    rng = np.random.default_rng(3 + D + maxc)
+    rows = 37
+    counts = rng.integers(0, maxc, size=rows)
+    counts[0] = 0
     rss = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     n = int(rss[-1])
     m = rng.normal(0, 3, n)
     l = rng.uniform(0.5, 40, n)
     l[rng.random(n) < 0.1] = 0.0          # empty chunks
     o = rng.normal(0, 1, (n, D))
-    log_case("merge of oracle partials")
+    o[l == 0.0] = np.nan
+    log_case(f"merge of oracle partials D={D} max count={maxc} misaligned={misaligned}")
+    out_buf = torch.empty(rows * D + 1, dtype=torch.float32, device=DEV)
+    out_t = out_buf[1:].view(rows, D) if misaligned else out_buf[:rows * D].view(rows, D)
     out, lse = pkg.attn_merge_lse(to_dev(o.astype(np.float32)), to_dev(m.astype(np.float32)),
-                                  to_dev(l.astype(np.float32)), to_dev(rss),
+                                  to_dev(l.astype(np.float32)), to_dev(rss), out=out_t,
                                   lse=torch.empty(rows, dtype=torch.float32, device=DEV))
     torch.cuda.synchronize()
     out = out.cpu().numpy()
     lse = lse.cpu().numpy()
     for r in range(rows):
         s0, s1 = rss[r], rss[r + 1]
-        ro, rl = oracle.merge(m[s0:s1].astype(np.float32).astype(np.float64),
-                              l[s0:s1].astype(np.float32).astype(np.float64),
-                              o[s0:s1].astype(np.float32).astype(np.float64))
+        keep = l[s0:s1] > 0
+        ro, rl = oracle.merge(m[s0:s1][keep].astype(np.float32).astype(np.float64),
+                              l[s0:s1][keep].astype(np.float32).astype(np.float64),
+                              o[s0:s1][keep].astype(np.float32).astype(np.float64))
         assert np.abs(out[r] - ro).max() <= 1e-5
         if math.isinf(rl):
             assert math.isinf(lse[r]) and lse[r] < 0
