@@ -59,12 +59,13 @@ __device__ __forceinline__ int64_t uniform_i64(int64_t v) {
 
 // ---------------------------------------------------------------- work split
 
-// Split-KV partial buffers.  Output row r = (b, kh, g) = b*QH + kh*G + g owns
-// the 2*max_chunks slots starting at 2*r*max_chunks, two per chunk of
-// split_tokens positions: at most one worker-range boundary can fall inside a
-// chunk, so slot 2j holds the part of chunk j before that boundary (or all of
-// it) and slot 2j+1 the part after it (or an empty partial: m = -inf, l = 0).
-// Slots of chunks past the row's own chunk count are never read.
+// Split-KV partial buffers.  Pair (b, kh) = b*KH + kh owns 2*max_chunks slots,
+// two per chunk of split_tokens positions: at most one worker-range boundary
+// can fall inside a chunk, so slot 2j holds the part of chunk j before that
+// boundary (or all of it) and slot 2j+1 the part after it (or an empty
+// partial: m = -inf, l = 0).  The partial of head g in slot j is entry
+// (pair*2*max_chunks + j)*G + g, so one worker's partials of a head group are
+// contiguous.  Slots of chunks past the pair's own chunk count are never read.
 struct WorkList {
   float *m_part;             // [max partials] natural-log max
   float *l_part;             // [max partials]

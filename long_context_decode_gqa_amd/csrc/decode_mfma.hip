@@ -194,7 +194,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       }
       *(u32x4_t *)(s_q + g * kQRow + 16 * c8) = w;
     }
-    const int slot_base = 2 * (b * p.QH + kh * p.G + g0 + col) * p.max_chunks;
+    // partial (pair, slot j, head g) lives at (pair*2*max_chunks + j)*G + g
+    const int slot_base = pair * 2 * p.max_chunks * p.G + g0 + col;
     __syncthreads();
     auto q_operand = [&](int kb) -> OpT {
       const int d0 = (KVT == ATTN_BF16) ? 8 * (4 * kb + cg) : 64 * (kb >> 1) + 16 * cg + 8 * (kb & 1);
@@ -411,7 +412,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       l_run += __shfl_xor(l_run, 32);
       if (qvalid) {
         const int half = (seg_t0 == lane_t0 + chunk * ct) ? 0 : 1;
-        const int slot = slot_base + 2 * chunk + half;
+        const int slot = slot_base + (2 * chunk + half) * p.G;
         const float out_scale = (KVT == ATTN_I8) ? p.v_scale : 1.0f;
         const float inv = l_run > 0.f ? out_scale / l_run : 0.f;
         float *op = p.wl.o_part + (int64_t)slot * D + 4 * NB * cg;
@@ -427,8 +428,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
           p.wl.m_part[slot] = l_run > 0.f ? m_run * kLn2 : NEG_INF;
           p.wl.l_part[slot] = l_run;
           if (half == 0 && seg_t1 == chunk_t1) {
-            p.wl.m_part[slot + 1] = NEG_INF;
-            p.wl.l_part[slot + 1] = 0.f;
+            p.wl.m_part[slot + p.G] = NEG_INF;
+            p.wl.l_part[slot + p.G] = 0.f;
           }
         }
       }

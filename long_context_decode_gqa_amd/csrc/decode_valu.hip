@@ -151,15 +151,15 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
         const int e = tid + 256 * k;
         if (e < gcount * D) {
           const int g = e / D, d = e - g * D;
-          const int slot = 2 * (b * p.QH + kh * p.G + g0 + g) * p.max_chunks + 2 * chunk + half;
+          const int slot = (pair * 2 * p.max_chunks + 2 * chunk + half) * p.G + g0 + g;
           const float l = s_l[g];
           p.wl.o_part[(int64_t)slot * D + d] = (l > 0.f) ? o[k] / l : 0.f;
           if (d == 0) {
             p.wl.m_part[slot] = (l > 0.f) ? s_m[g] : NEG_INF;
             p.wl.l_part[slot] = l;
             if (fill_second) {
-              p.wl.m_part[slot + 1] = NEG_INF;
-              p.wl.l_part[slot + 1] = 0.f;
+              p.wl.m_part[slot + p.G] = NEG_INF;
+              p.wl.l_part[slot + p.G] = 0.f;
             }
           }
         }

@@ -39,6 +39,25 @@ __device__ __forceinline__ int merge_scan(int v, int *s_red, int *total) {
   return base + incl - v;
 }
 
+// The partials of output row `row`: index s0 + j*ss of slot j < n.  A decode
+// call's row (b, kh, g) = pair*G + g owns the slots of its pair's chunks,
+// laid out (pair, slot, head) so that one decode worker's partial of all the
+// group's heads is one contiguous block; otherwise the caller's CSR offsets.
+template <bool DECODE>
+__device__ __forceinline__ void row_slots(int row, const int32_t *rss, const DecodeParams &dp, int *s0, int *n,
+                                          int *ss) {
+  if constexpr (DECODE) {
+    const int pair = row / dp.G, g = row - pair * dp.G;
+    *s0 = pair * 2 * dp.max_chunks * dp.G + g;
+    *n = 2 * pair_chunks(dp, pair);
+    *ss = dp.G;
+  } else {
+    *s0 = rss[row];
+    *n = rss[row + 1] - *s0;
+    *ss = 1;
+  }
+}
+
 // Log-sum-exp merge of partial triples, one workgroup per output row:
 // M = max m_i, w_i = exp(m_i - M) l_i, out = sum w_i o_i / sum w_i,
 // lse = M + ln(sum w_i).  The row's non-empty partials are compacted into an
@@ -46,9 +65,6 @@ __device__ __forceinline__ int merge_scan(int v, int *s_red, int *total) {
 // strided subset with branch-free loads; the groups are added in a fixed
 // order, so the result is deterministic.
 //
-// Slot ranges: with DECODE, row r = (b, kh, g) of a decode call reads its
-// 2 * (chunks of its pair) slots from 2*r*max_chunks on; otherwise the
-// caller's CSR offsets rss[r] .. rss[r+1].
 template <int OUT, bool DECODE>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *o_part, const float *m_part,
                                                               const float *l_part, const int32_t *rss,
@@ -61,17 +77,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *o_par
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const float NEG_INF = -__builtin_huge_valf();
-  int s0, n;
-  if constexpr (DECODE) {
-    s0 = 2 * row * dp.max_chunks;
-    n = 2 * pair_chunks(dp, row / dp.G);
-  } else {
-    s0 = rss[row];
-    n = rss[row + 1] - s0;
-  }
+  int s0, n, ss;
+  row_slots<DECODE>(row, rss, dp, &s0, &n, &ss);
   float M = NEG_INF;
   for (int i = tid; i < n; i += kMergeThreads)
-    if (l_part[s0 + i] > 0.f) M = fmaxf(M, m_part[s0 + i]);
+    if (l_part[s0 + i * ss] > 0.f) M = fmaxf(M, m_part[s0 + i * ss]);
   M = block_reduce(M, s_red, true);
 
   const bool vec = (D & 3) == 0;
@@ -84,15 +94,15 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *o_par
     const int i = base + tid;
     float w = 0.f;
     if (i < n) {
-      const float l = l_part[s0 + i];
-      if (l > 0.f) w = expf(m_part[s0 + i] - M) * l;
+      const float l = l_part[s0 + i * ss];
+      if (l > 0.f) w = expf(m_part[s0 + i * ss] - M) * l;
     }
     Lpart += w;
     int cnt;
     const int pos = merge_scan(w > 0.f ? 1 : 0, s_cnt, &cnt);
     if (w > 0.f) {
       s_w[pos] = w;
-      s_sl[pos] = s0 + i;
+      s_sl[pos] = s0 + i * ss;
     }
     __syncthreads();
     if (grp < ngrp) {
@@ -143,14 +153,8 @@ __global__ __launch_bounds__(kMergeV4Threads) void merge_v4_kernel(const float *
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const float NEG_INF = -__builtin_huge_valf();
-  int s0, n;
-  if constexpr (DECODE) {
-    s0 = 2 * row * dp.max_chunks;
-    n = 2 * pair_chunks(dp, row / dp.G);
-  } else {
-    s0 = rss[row];
-    n = rss[row + 1] - s0;
-  }
+  int s0, n, ss;
+  row_slots<DECODE>(row, rss, dp, &s0, &n, &ss);
   const int nq = D / 4;            // column slices
   const int ng = kMergeV4Threads / nq;
   const int grp = tid / nq, q = tid - grp * nq;
@@ -164,7 +168,7 @@ __global__ __launch_bounds__(kMergeV4Threads) void merge_v4_kernel(const float *
       for (int u = 0; u < kMergeV4Unroll; ++u) {
         const int sl = base + u * ng;
         const bool in = sl < n;
-        const int64_t i = s0 + (in ? sl : 0);
+        const int64_t i = s0 + (int64_t)(in ? sl : 0) * ss;
         l[u] = in ? l_part[i] : 0.f;
         m[u] = m_part[i];
         o[u] = *(const f32x4_t *)(o_part + i * D + 4 * q);
