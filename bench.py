@@ -119,6 +119,17 @@ def dev_geom(pkg, torch, g, dev):
                           torch.from_numpy(g.seq_offset).to(dev), g.stride_h, g.stride_t)
 
 
+def effective_split(torch, w) -> int:
+    """Tokens per split-KV chunk of a dense (no index list) bf16/int8 decode of
+    workload w: as given, or for 0 the library default, about one chunk per
+    decode worker of a full grid: 32 * clamp(T_max / 2048, 1, 64) with T_max
+    the tiles of 32 tokens at the longest length (G <= 16 here)."""
+    if w.split_tokens:
+        return w.split_tokens
+    t_max = w.B * w.KH * (-(-int(max(w.lens)) // 32))
+    return 32 * min(max(t_max // 2048, 1), 64)
+
+
 def time_decode(torch, prepared, steps, warmup):
     """Returns (ms per step, mean decode-kernel ms, mean merge ms).
 
@@ -157,16 +168,21 @@ def bench_dense(pkg, torch, synth, name, steps, warmup, dev, **over):
     ms, dk, mg = time_decode(torch, p, steps, warmup)
     tokens = w.kv_tokens()
     kvb = kv_bytes(tokens, w.KH, w.D, 2)
-    nparts = w.QH * sum(-(-int(L) // w.split_tokens) for L in w.lens)
+    split = effective_split(torch, w)
+    nparts = w.QH * sum(-(-int(L) // split) for L in w.lens)
     algo = kvb + w.B * w.QH * w.D * 2 + partial_bytes(nparts, w.D)
     return dict(w=w, q=q, g=g, ms=ms, decode_ms=dk, merge_ms=mg, kv_bytes=kvb,
-                decode_algo_bytes=algo, tokens=tokens)
+                decode_algo_bytes=algo, tokens=tokens, split=split)
 
 
 def summary(r, extra=None):
     d = {"us_per_step": round(r["ms"] * 1e3, 2), "kv_gbs": round(r["kv_bytes"] / r["ms"] / 1e6, 1),
          "frac_of_peak": round(r["kv_bytes"] / r["ms"] / 1e6 / HBM_PEAK_GBS, 4),
-         "decode_kernel_us": round(r["decode_ms"] * 1e3, 2), "merge_us": round(r["merge_ms"] * 1e3, 2)}
+         "decode_kernel_us": round(r["decode_ms"] * 1e3, 2), "merge_us": round(r["merge_ms"] * 1e3, 2),
+         "kernel_kv_gbs": round(r["kv_bytes"] / r["decode_ms"] / 1e6, 1),
+         "kernel_frac_of_peak": round(r["kv_bytes"] / r["decode_ms"] / 1e6 / HBM_PEAK_GBS, 4)}
+    if "split" in r:
+        d["split_tokens"] = r["split"]
     if extra:
         d.update(extra)
     return d
@@ -188,7 +204,7 @@ def bench_int8(pkg, torch, synth, steps, warmup, dev):
     ms, dk, mg = time_decode(torch, p, steps, warmup)
     tokens = w.kv_tokens()
     kvb = kv_bytes(tokens, w.KH, w.D, 1) + ks.numel() * 4 + 4
-    return dict(ms=ms, decode_ms=dk, merge_ms=mg, kv_bytes=kvb)
+    return dict(ms=ms, decode_ms=dk, merge_ms=mg, kv_bytes=kvb, split=effective_split(torch, w))
 
 
 def bench_oam(pkg, torch, synth, steps, warmup, dev):
@@ -327,7 +343,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "config": {"workload": "gqa_decode_bf16_128k", "batch": w.B, "kv_heads": w.KH, "group_size": w.G,
-                   "head_dim": w.D, "kv_len": int(w.lens[0]), "split_tokens": w.split_tokens,
+                   "head_dim": w.D, "kv_len": int(w.lens[0]), "split_tokens": head["split"],
+                   "split_chosen_by": "library" if w.split_tokens == 0 else "caller",
                    "kv_bytes_per_step": head["kv_bytes"],
                    "eq6_bytes_per_step": decode_eq_elements(w.B, w.KH, w.G, w.D, int(w.lens[0])) * 2,
                    "flops_per_step": decode_eq_flops(w.B, w.QH, int(w.lens[0]), w.D)},

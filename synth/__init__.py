@@ -11,7 +11,7 @@ channels, output-aware token dropping at 128K):
 
 =========  ==========================================================================
 tiny       B=1, KH=1, G=4, D=64, L=1024, fp32 N(0,1); 4 splits of 256
-gqa32k     B=16, KH=8, G=8, D=128, L=32768, bf16 N(0,1)
+gqa32k     B=16, KH=8, G=8, D=128, L=32768, bf16 N(0,1); 1024-token splits
 ragged     32 sequences, L_b log-uniform in [512, 131072], KH=8, G=8, D=128, bf16,
            head-major packed cache
 int8_128k  B=4, KH=8, G=8, D=128, L=131072; bf16 N(0,1) K/V with 2 outlier
@@ -21,9 +21,10 @@ oam_128k   B=4, KH=8, G=8, D=128, L=131072; K N(0,1); V = unit N(0,1) direction
 dense128k  B=4, KH=8, G=8, D=128, L=131072, bf16 N(0,1)
 =========  ==========================================================================
 
-The four large decode workloads are run with 2048-token split-KV chunks (one
-chunk per decode worker at these sizes); the attention over OAM's 4096 kept
-tokens uses 128-token chunks.
+split_tokens 0 means the library default (about one chunk per decode worker:
+2048 tokens for the 128K, INT8 and ragged workloads).  gqa32k keeps the
+1024-token split-KV chunks its definition names; the attention over OAM's
+4096 kept tokens uses 128-token chunks.
 """
 from __future__ import annotations
 
@@ -206,7 +207,7 @@ class Workload:
     seed: int
     dtype: str                 # "f32" or "bf16" element type of Q/K/V as generated
     lens: np.ndarray
-    split_tokens: int = 1024
+    split_tokens: int = 1024   # 0: the library default
     layout: str = "dense"      # dense | token_major | head_major
     outliers: int = 0
     v_kind: int = NORMAL
@@ -241,16 +242,16 @@ def workload(name: str, **over) -> Workload:
     if name == "tiny":
         w = Workload("tiny", 1, 1, 4, 64, 1, "f32", np.array([1024], np.int32), split_tokens=256)
     elif name == "gqa32k":
-        w = Workload("gqa32k", 16, 8, 8, 128, 2, "bf16", np.full(16, 32768, np.int32), split_tokens=2048)
+        w = Workload("gqa32k", 16, 8, 8, 128, 2, "bf16", np.full(16, 32768, np.int32), split_tokens=1024)
     elif name == "ragged":
-        w = Workload("ragged", 32, 8, 8, 128, 3, "bf16", loguniform_lengths(3, 32), layout="head_major", split_tokens=2048)
+        w = Workload("ragged", 32, 8, 8, 128, 3, "bf16", loguniform_lengths(3, 32), layout="head_major", split_tokens=0)
     elif name == "int8_128k":
-        w = Workload("int8_128k", 4, 8, 8, 128, 4, "bf16", np.full(4, 131072, np.int32), outliers=2, split_tokens=2048)
+        w = Workload("int8_128k", 4, 8, 8, 128, 4, "bf16", np.full(4, 131072, np.int32), outliers=2, split_tokens=0)
     elif name == "oam_128k":
         w = Workload("oam_128k", 4, 8, 8, 128, 5, "bf16", np.full(4, 131072, np.int32),
                      v_kind=UNIT_DIR_LOGNORMAL, top_k=4096, split_tokens=128)
     elif name == "dense128k":
-        w = Workload("dense128k", 4, 8, 8, 128, 6, "bf16", np.full(4, 131072, np.int32), split_tokens=2048)
+        w = Workload("dense128k", 4, 8, 8, 128, 6, "bf16", np.full(4, 131072, np.int32), split_tokens=0)
     else:
         raise KeyError(name)
     for k, v in over.items():

@@ -57,7 +57,9 @@ def test_bf16_ragged_tails_and_group_sizes(D, G):
     log_case(f"bf16 ragged D={D} G={G}")
     p = problem(w, q, k, v, g)
     ref, ref_lse = oracle.attention_rows(p, oracle.all_rows(p), nthreads=8)
-    for split, od in ((1024, torch.float32), (256, torch.bfloat16)):
+    # split 0: the library's default chunk size
+    for split, od in ((1024, torch.float32), (256, torch.bfloat16), (0, torch.float32), (0, torch.bfloat16)):
+        log_case(f"bf16 ragged D={D} G={G} split={split} out={od}")
         out, lse = run_decode(w, q, k, v, g, out_dtype=od, split_tokens=split)
         check(out, lse, ref, ref_lse, bf16_out=(od == torch.bfloat16))
 
@@ -69,8 +71,9 @@ def test_bf16_head_major_layout_and_lse():
     log_case("bf16 head-major")
     p = problem(w, q, k, v, g)
     ref, ref_lse = oracle.attention_rows(p, oracle.all_rows(p), nthreads=8)
-    out, lse = run_decode(w, q, k, v, g, split_tokens=512)
-    check(out, lse, ref, ref_lse)
+    for split in (512, 0):
+        out, lse = run_decode(w, q, k, v, g, split_tokens=split)
+        check(out, lse, ref, ref_lse)
 
 
 def test_bitwise_repeatable():

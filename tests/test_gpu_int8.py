@@ -97,7 +97,7 @@ def test_int8_decode_matches_oracle_on_dequantised_values(G, D):
     vc, vsa = gpu_quant(v, g, 0)
     p = problem(w, q, kc, vc, g, k_scale=ks, k_part=64, k_scale_stride=stride, v_scale=float(vsa[0]))
     ref, ref_lse = oracle.attention_rows(p, oracle.all_rows(p), nthreads=8)
-    for split in (1024, 256):
+    for split in (1024, 256, 0):
         out, lse = run_int8_decode(w, q, kc, vc, ks, vsa[0], g, split=split)
         assert np.abs(out - ref).max() <= 2e-3
         assert np.abs(lse - ref_lse).max() <= 1e-3
