@@ -92,9 +92,9 @@ typedef struct {
  * Arguments of one decode step.
  *   G           query heads per KV head, 1 <= G <= 64
  *   q           [B][KH*G][D] in q_dtype (ATTN_BF16, or ATTN_F32 with fp32 KV);
- *               with ATTN_I8 KV the matrix cores take q as fp16, which holds
- *               every bf16 value of magnitude in [6.1e-5, 65504) exactly:
- *               |q| must stay below 65504
+ *               with ATTN_I8 KV the int8 matrix cores take each head's q as
+ *               a 22-bit fixed-point value with its own scale (max|q_g| /
+ *               2^22), error at most max|q_g| * 2^-23 per element
  *   k, v        KV cache in kv_dtype, geometry `kv`
  *   k_scale     ATTN_I8 only: fp32 scale of K row (b, kh, t) is
  *               k_scale[(b*KH + kh)*k_scale_stride + t / k_part_tokens];

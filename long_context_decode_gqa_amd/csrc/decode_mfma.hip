@@ -120,10 +120,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   typedef typename std::conditional<KVT == ATTN_BF16, bf16x8_t, f16x8_t>::type OpT;
 
   __shared__ int s_idx[IDX ? kMaxIdxChunk : 1];
-  // Q^T operand of the current run: 16 query heads x D channels (bf16, or
-  // fp16 for int8 KV), rows padded by 16 bytes against bank conflicts.
+  // Q^T operand of the current run, 16 query heads x D channels, rows padded
+  // by 16 bytes against bank conflicts: bf16 for bf16 KV; for int8 KV three
+  // int8 digit planes of each head's 22-bit fixed-point query (see below).
   constexpr int kQRow = D * 2 + 16;
-  __shared__ __attribute__((aligned(16))) unsigned char s_q[16 * kQRow];
+  constexpr int kQDRow = D + 16;
+  constexpr int kQBytes = KVT == ATTN_I8 ? 3 * 16 * kQDRow : 16 * kQRow;
+  __shared__ __attribute__((aligned(16))) unsigned char s_q[kQBytes];
 
   const int lane = threadIdx.x;
   const int col = lane & 15, cg = lane >> 4;
@@ -173,33 +176,81 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         i8 ? max(p.k_scale_stride, 1) * 4 : 0, 0x00020000);
 
     // Stage Q (the 16 heads of this block, zero past G) in LDS in MFMA
-    // operand type; tiles read their B operand from there.  The partial
+    // operand form; tiles read their B operand from there.  The partial
     // slots of this lane's rows are loaded now as well: a global load inside
     // the segment loop would make the compiler wait for every load in
     // flight, the tile prefetch included.
+    //
+    // int8 KV: the scores run on the int8 matrix cores straight from the K
+    // codes.  Head g's query becomes q = s_g * n with s_g = max|q_g| / 2^22
+    // and n = rint(q / s_g) = 65536 d2 + 256 d1 + d0, d0, d1 in [-128, 127]
+    // and |d2| <= 64 (|error| <= max|q_g| * 2^-23); each digit plane is one
+    // int8 MFMA, and the three integer sums recombine exactly in fp32.
+    float qs = 0.f;  // int8: this lane's head (col) scale s_col
     __syncthreads();
-    for (int e = lane; e < 16 * (D / 8); e += 64) {
-      const int g = e / (D / 8), c8 = e - g * (D / 8);
-      u32x4_t w = (u32x4_t){0u, 0u, 0u, 0u};
-      if (g < gcount)
-        w = *(const u32x4_t *)((const uint16_t *)p.q + ((int64_t)b * p.QH + (int64_t)kh * p.G + g0 + g) * D + 8 * c8);
-      if constexpr (KVT == ATTN_I8) {
-        f16x8_t h;
+    if constexpr (KVT == ATTN_I8) {
+      constexpr int CPL = D / 4;  // lane (col, cg) takes head col, channels [cg*CPL, cg*CPL + CPL)
+      float qv[CPL];
+      const uint16_t *qrow = (const uint16_t *)p.q + ((int64_t)b * p.QH + (int64_t)kh * p.G + g0 + col) * D + cg * CPL;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          h[2 * x] = (_Float16)bf16_lo(w[x]);
-          h[2 * x + 1] = (_Float16)bf16_hi(w[x]);
+      for (int x = 0; x < CPL / 8; ++x) {
+        u32x4_t w = (u32x4_t){0u, 0u, 0u, 0u};
+        if (qvalid) w = *(const u32x4_t *)(qrow + 8 * x);
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          qv[8 * x + 2 * y] = bf16_lo(w[y]);
+          qv[8 * x + 2 * y + 1] = bf16_hi(w[y]);
         }
-        w = __builtin_bit_cast(u32x4_t, h);
       }
-      *(u32x4_t *)(s_q + g * kQRow + 16 * c8) = w;
+      float mx = 0.f;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) mx = fmaxf(mx, fabsf(qv[j]));
+      mx = rows_max(mx);  // the four lanes of head col hold all D channels
+      const float inv = mx > 0.f ? 4194304.0f / mx : 0.f;
+      qs = mx * (1.0f / 4194304.0f);
+      uint32_t dw[3][CPL / 4];
+#pragma unroll
+      for (int j4 = 0; j4 < CPL / 4; ++j4) {
+        uint32_t w0 = 0u, w1 = 0u, w2 = 0u;
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          const int n = (int)__builtin_rintf(qv[4 * j4 + y] * inv);
+          const int d0 = (int)(int8_t)(n & 0xFF);
+          const int r1 = (n - d0) >> 8;
+          const int d1 = (int)(int8_t)(r1 & 0xFF);
+          const int d2 = (r1 - d1) >> 8;
+          w0 |= (uint32_t)(d0 & 0xFF) << (8 * y);
+          w1 |= (uint32_t)(d1 & 0xFF) << (8 * y);
+          w2 |= (uint32_t)(d2 & 0xFF) << (8 * y);
+        }
+        dw[0][j4] = w0;
+        dw[1][j4] = w1;
+        dw[2][j4] = w2;
+      }
+#pragma unroll
+      for (int dg = 0; dg < 3; ++dg)
+#pragma unroll
+        for (int x = 0; x < CPL / 16; ++x)
+          *(u32x4_t *)(s_q + (dg * 16 + col) * kQDRow + cg * CPL + 16 * x) =
+              (u32x4_t){dw[dg][4 * x], dw[dg][4 * x + 1], dw[dg][4 * x + 2], dw[dg][4 * x + 3]};
+    } else {
+      for (int e = lane; e < 16 * (D / 8); e += 64) {
+        const int g = e / (D / 8), c8 = e - g * (D / 8);
+        u32x4_t w = (u32x4_t){0u, 0u, 0u, 0u};
+        if (g < gcount)
+          w = *(const u32x4_t *)((const uint16_t *)p.q + ((int64_t)b * p.QH + (int64_t)kh * p.G + g0 + g) * D + 8 * c8);
+        *(u32x4_t *)(s_q + g * kQRow + 16 * c8) = w;
+      }
     }
     // partial (pair, slot j, head g) lives at (pair*2*max_chunks + j)*G + g
     const int slot_base = pair * 2 * p.max_chunks * p.G + g0 + col;
     __syncthreads();
-    auto q_operand = [&](int kb) -> OpT {
-      const int d0 = (KVT == ATTN_BF16) ? 8 * (4 * kb + cg) : 64 * (kb >> 1) + 16 * cg + 8 * (kb & 1);
-      return __builtin_bit_cast(OpT, *(const u32x4_t *)(s_q + col * kQRow + 2 * d0));
+    auto q_operand = [&](int kb) -> bf16x8_t {
+      return __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(s_q + col * kQRow + 16 * (4 * kb + cg)));
+    };
+    // int8: digit plane dg of channels 64kb + 16cg .. + 15 of head col
+    auto q_digits = [&](int dg, int kb) -> i32x4_t {
+      return __builtin_bit_cast(i32x4_t, *(const u32x4_t *)(s_q + (dg * 16 + col) * kQDRow + 64 * kb + 16 * cg));
     };
 
     // Positions of the current segment (IDX: its staged index list starts at seg_pos0).
@@ -270,36 +321,37 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (KVT == ATTN_BF16) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          if constexpr (KVT == ATTN_BF16) {
+          for (int kb = 0; kb < KB; ++kb)
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, R.k[tb][kb]), q_operand(kb),
                                                           acc, 0, 0, 0);
-          } else {
-            const u32x4_t w = R.k[tb][kb >> 1];
-            const uint32_t c0 = w[2 * (kb & 1)], c1w = w[2 * (kb & 1) + 1];
-            u32x4_t hw;
-            // bytes 0,1 (then 2,3) of a word into the low byte of each half
-            hw[0] = codes_to_f16x2(__builtin_amdgcn_perm(c0, c0, 0x0c010c00u));
-            hw[1] = codes_to_f16x2(__builtin_amdgcn_perm(c0, c0, 0x0c030c02u));
-            hw[2] = codes_to_f16x2(__builtin_amdgcn_perm(c1w, c1w, 0x0c010c00u));
-            hw[3] = codes_to_f16x2(__builtin_amdgcn_perm(c1w, c1w, 0x0c030c02u));
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, hw), q_operand(kb), acc, 0, 0, 0);
+        } else {
+          // the K codes as loaded are the int8 A operand (lane (col, cg):
+          // token col, channels 64kb + 16cg .. + 15)
+          i32x4_t a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0}, a2 = {0, 0, 0, 0};
+#pragma unroll
+          for (int kb = 0; kb < KL; ++kb) {
+            const i32x4_t kop = __builtin_bit_cast(i32x4_t, R.k[tb][kb]);
+            a0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, q_digits(0, kb), a0, 0, 0, 0);
+            a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, q_digits(1, kb), a1, 0, 0, 0);
+            a2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, q_digits(2, kb), a2, 0, 0, 0);
           }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] = ((float)a2[i] * 65536.0f + (float)a1[i] * 256.0f) + (float)a0[i];
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int pos = tpos + 16 * tb + 4 * cg + i;
           float sc = c1;
-          if constexpr (KVT == ATTN_I8) sc *= IDX ? R.ks[4 * tb + i] : R.ks[tb];
+          if constexpr (KVT == ATTN_I8) sc *= qs * (IDX ? R.ks[4 * tb + i] : R.ks[tb]);
           s[4 * tb + i] = (pos < seg_pos1) ? acc[i] * sc : NEG_INF;
         }
       }
       float mt = s[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) mt = fmaxf(mt, s[i]);
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      mt = rows_max(mt);
       const float m_new = fmaxf(m_run, mt);
       if (__any(m_new > m_run)) {
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -408,8 +460,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
       // Partial of this segment, straight from registers.  Lane (col, cg)
       // holds channels NB*(4*cg + i) + nb = 4*NB*cg + NB*i + nb of head col.
-      l_run += __shfl_xor(l_run, 16);
-      l_run += __shfl_xor(l_run, 32);
+      l_run = rows_sum(l_run);
       if (qvalid) {
         const int half = (seg_t0 == lane_t0 + chunk * ct) ? 0 : 1;
         const int slot = slot_base + (2 * chunk + half) * p.G;
