@@ -89,10 +89,13 @@ struct Step {
   static constexpr int kBudget = KVT == ATTN_BF16 ? 64 : 32;
   static constexpr int TPS = kRegs >= kBudget ? 1 : kBudget / kRegs;
   // Steps in flight: NBUF register buffers rotate, so while one step is
-  // consumed the next NBUF-1 are loading.  An int8 tile carries half the
-  // bytes of a bf16 one, so int8 keeps three buffers to have as many bytes
-  // in flight per wave.
-  static constexpr int NBUF = KVT == ATTN_BF16 ? 2 : 3;
+  // consumed the next NBUF-1 are loading.  int8 starts a step's scores one
+  // step early (its score chain, not its bytes, limits it), so the K of that
+  // step has only NBUF-2 steps to arrive; it keeps four buffers where they
+  // fit in registers (one-tile steps over the whole cache) and three where a
+  // step holds two tiles or token indices take registers.
+  static constexpr int NBUF = KVT == ATTN_BF16 ? 2 : (TPS == 1 && !IDX ? 4 : 3);
+  static constexpr bool PIPE = KVT == ATTN_I8;
   TileT t[TPS];
 };
 
@@ -315,9 +318,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     for (int nb = 0; nb < NB; ++nb) O[nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     float m_run = NEG_INF, l_run = 0.f;
 
-    auto compute_tile = [&](const TileT &R, int tile) {
-      const int tpos = (tile - lane_t0) * kTile;
-      float s[8];
+    // Raw q.k of a tile's 8 scores of this lane (before scale and mask).
+    struct Raw {
+      float v[8];
+    };
+    auto qk_tile = [&](const TileT &R) -> Raw {
+      Raw r;
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -341,13 +347,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
           for (int i = 0; i < 4; ++i) acc[i] = ((float)a2[i] * 65536.0f + (float)a1[i] * 256.0f) + (float)a0[i];
         }
 #pragma unroll
+        for (int i = 0; i < 4; ++i) r.v[4 * tb + i] = acc[i];
+      }
+      return r;
+    };
+
+    // Online softmax and P.V of a tile whose raw scores are given.
+    auto finish_tile = [&](const TileT &R, int tile, const Raw &raw) {
+      const int tpos = (tile - lane_t0) * kTile;
+      float s[8];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int pos = tpos + 16 * tb + 4 * cg + i;
           float sc = c1;
           if constexpr (KVT == ATTN_I8) sc *= qs * (IDX ? R.ks[4 * tb + i] : R.ks[tb]);
-          s[4 * tb + i] = (pos < seg_pos1) ? acc[i] * sc : NEG_INF;
+          s[4 * tb + i] = (pos < seg_pos1) ? raw.v[4 * tb + i] * sc : NEG_INF;
         }
-      }
       float mt = s[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) mt = fmaxf(mt, s[i]);
@@ -407,9 +424,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       }
     };
 
-    auto compute_step = [&](const StepT &S, int tile0) {
+    struct RawStep {
+      Raw t[TPS];
+    };
+    auto qk_step = [&](const StepT &S) -> RawStep {
+      RawStep r;
 #pragma unroll
-      for (int j = 0; j < TPS; ++j) compute_tile(S.t[j], tile0 + j);
+      for (int j = 0; j < TPS; ++j) r.t[j] = qk_tile(S.t[j]);
+      return r;
+    };
+    auto finish_step = [&](const StepT &S, int tile0, const RawStep &r) {
+#pragma unroll
+      for (int j = 0; j < TPS; ++j) finish_tile(S.t[j], tile0 + j, r.t[j]);
     };
 
     // Segments: the run cut at chunk boundaries.  The NBUF register buffers
@@ -450,11 +476,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         const int lim = in_seg ? seg_t1 : (IDX ? 0 : next_t1);
         load_step(S, tn < lim ? tn : seg_t0, tn < lim ? lim : 0);
       };
-      for (int i = 0; i < steps; i += NBUF) {
+      if constexpr (StepT::PIPE) {
+        // the raw scores of step s + 1 are started before step s's softmax
+        // and P.V, so the score MFMAs' latency overlaps that work
+        RawStep pend = qk_step(buf[0]);
+        for (int i = 0; i < steps; i += NBUF) {
 #pragma unroll
-        for (int j = 0; j < NBUF; ++j) {
-          issue(buf[(j + NBUF - 1) % NBUF], i + j + NBUF - 1);
-          compute_step(buf[j], seg_t0 + (i + j) * TPS);
+          for (int j = 0; j < NBUF; ++j) {
+            issue(buf[(j + NBUF - 1) % NBUF], i + j + NBUF - 1);
+            const RawStep nxt = qk_step(buf[(j + 1) % NBUF]);
+            finish_step(buf[j], seg_t0 + (i + j) * TPS, pend);
+            pend = nxt;
+          }
+        }
+      } else {
+        for (int i = 0; i < steps; i += NBUF) {
+#pragma unroll
+          for (int j = 0; j < NBUF; ++j) {
+            issue(buf[(j + NBUF - 1) % NBUF], i + j + NBUF - 1);
+            finish_step(buf[j], seg_t0 + (i + j) * TPS, qk_step(buf[j]));
+          }
         }
       }
 
