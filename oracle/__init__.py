@@ -42,6 +42,7 @@ class _Problem(ctypes.Structure):
         ("k_scale", ctypes.c_void_p), ("k_part", ctypes.c_int32), ("k_scale_stride", ctypes.c_int32),
         ("v_scale", ctypes.c_float), ("softmax_scale", ctypes.c_double),
         ("tok_idx", ctypes.c_void_p), ("n_idx", ctypes.c_void_p), ("idx_stride", ctypes.c_int32),
+        ("q_scale", ctypes.c_void_p),
     ]
 
 
@@ -62,6 +63,8 @@ def lib():
         L.oracle_merge.argtypes = [i32, i32, vp, vp, vp, vp, vp]
         L.oracle_quant_partitions.argtypes = [i32, i32, i32, vp, vp, i64, i64, vp, i32, vp, vp, i32]
         L.oracle_quant_tensor.argtypes = [i32, i32, i32, vp, vp, i64, i64, vp, vp, vp]
+        L.oracle_quant_rows.argtypes = [i32, i32, vp, vp, vp]
+        L.oracle_quant_static.argtypes = [i64, vp, ctypes.c_float, vp]
         L.oracle_oam_scores.argtypes = [P, i32, i32, f64, f64, vp]
         L.oracle_value_lognorm.argtypes = [P, i32, i32, f64, vp]
         L.oracle_topk_sort.argtypes = [vp, i32, i32, vp]
@@ -92,6 +95,7 @@ class Problem:
 
     K/V row (b, kh, t) starts at element seq_offset[b] + kh*stride_h + t*stride_t
     of the flat arrays ``k``/``v``.  ``q`` is [B, KH*G, D].  bf16 is uint16 bits.
+    An int8 ``q`` holds codes; row (b, qh) is multiplied by q_scale[b*KH*G + qh].
     """
     B: int
     KH: int
@@ -112,6 +116,7 @@ class Problem:
     tok_idx: Optional[np.ndarray] = None
     n_idx: Optional[np.ndarray] = None
     idx_stride: int = 0
+    q_scale: Optional[np.ndarray] = None
 
     def _struct(self) -> _Problem:
         self._keep = [np.ascontiguousarray(self.lens, dtype=np.int32),
@@ -138,6 +143,10 @@ class Problem:
             ni = np.ascontiguousarray(self.n_idx, dtype=np.int32)
             self._keep += [ti, ni]
             s.tok_idx, s.n_idx, s.idx_stride = _ptr(ti), _ptr(ni), self.idx_stride
+        if self.q_scale is not None:
+            qs = np.ascontiguousarray(self.q_scale, dtype=np.float32)
+            self._keep.append(qs)
+            s.q_scale = _ptr(qs)
         return s
 
 
@@ -203,6 +212,26 @@ def quant_partitions(B, KH, D, lens, seq_offset, stride_h, stride_t, x_bf16: np.
                                      _ptr(codes), _ptr(scales), scale_stride):
         raise ValueError("oracle_quant_partitions: invalid arguments")
     return codes, scales
+
+
+def quant_rows(x_bf16: np.ndarray):
+    """Per-row INT8 of a [rows, D] bf16 array (the query of Schemes A and B) -> (codes, scales)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    rows, D = x.shape
+    codes = np.zeros(x.shape, dtype=np.int8)
+    scales = np.zeros(rows, dtype=np.float32)
+    if lib().oracle_quant_rows(rows, D, _ptr(x), _ptr(codes), _ptr(scales)):
+        raise ValueError("oracle_quant_rows: invalid arguments")
+    return codes, scales
+
+
+def quant_static(x_bf16: np.ndarray, scale: float) -> np.ndarray:
+    """INT8 codes of bf16 values with a given per-tensor scale (the baseline scheme)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    codes = np.zeros(x.shape, dtype=np.int8)
+    if lib().oracle_quant_static(x.size, _ptr(x), float(scale), _ptr(codes)):
+        raise ValueError("oracle_quant_static: invalid arguments")
+    return codes
 
 
 def quant_tensor(B, KH, D, lens, seq_offset, stride_h, stride_t, x_bf16: np.ndarray):

@@ -25,6 +25,9 @@ double bf16_to_double(uint16_t h) {
 double q_at(const oracle_problem *p, int32_t b, int32_t qh, int32_t d) {
   size_t i = (static_cast<size_t>(b) * p->KH * p->G + qh) * p->D + d;
   if (p->q_type == ORACLE_F32) return static_cast<const float *>(p->q)[i];
+  if (p->q_type == ORACLE_I8)
+    return static_cast<const int8_t *>(p->q)[i] *
+           static_cast<double>(p->q_scale[static_cast<size_t>(b) * p->KH * p->G + qh]);
   return bf16_to_double(static_cast<const uint16_t *>(p->q)[i]);
 }
 
@@ -68,6 +71,7 @@ bool problem_ok(const oracle_problem *p) {
   if (!p->lens || !p->seq_offset || !p->q || !p->k || !p->v) return false;
   if (p->kv_type == ORACLE_I8 && (!p->k_scale || p->k_part < 1 || p->k_scale_stride < 1)) return false;
   if (p->tok_idx && (!p->n_idx || p->idx_stride < 0)) return false;
+  if (p->q_type == ORACLE_I8 && !p->q_scale) return false;
   return true;
 }
 
@@ -292,6 +296,25 @@ int oracle_quant_tensor(int32_t B, int32_t KH, int32_t D, const int32_t *lens,
           const int64_t off = seq_offset[b] + kh * stride_h + t * stride_t + d;
           codes[off] = quantise(bf16_to_float(x_bf16[off]), s);
         }
+  return 0;
+}
+
+int oracle_quant_rows(int32_t rows, int32_t D, const uint16_t *x_bf16, int8_t *codes, float *scales) {
+  if (rows < 0 || D < 1 || !x_bf16 || !codes || !scales) return 1;
+  for (int32_t r = 0; r < rows; ++r) {
+    const uint16_t *x = x_bf16 + static_cast<int64_t>(r) * D;
+    float amax = 0.0f;
+    for (int32_t d = 0; d < D; ++d) amax = std::max(amax, std::fabs(bf16_to_float(x[d])));
+    const float scale = amax / 127.0f;
+    scales[r] = scale;
+    for (int32_t d = 0; d < D; ++d) codes[static_cast<int64_t>(r) * D + d] = quantise(bf16_to_float(x[d]), scale);
+  }
+  return 0;
+}
+
+int oracle_quant_static(int64_t n, const uint16_t *x_bf16, float scale, int8_t *codes) {
+  if (n < 0 || !x_bf16 || !codes || !(scale >= 0.0f)) return 1;
+  for (int64_t i = 0; i < n; ++i) codes[i] = quantise(bf16_to_float(x_bf16[i]), scale);
   return 0;
 }
 

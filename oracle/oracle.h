@@ -33,6 +33,7 @@ enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_I8 = 2 };
  * Q is [B][KH*G][D]; query head qh = kh*G + g reads KV head kh = qh / G.
  * INT8 K: value = code * k_scale[(b*KH + kh)*k_scale_stride + t / k_part];
  * INT8 V: value = code * v_scale.
+ * INT8 Q (q_type ORACLE_I8): value = code * q_scale[b*KH*G + qh].
  * If tok_idx is not NULL, (b, kh) attends only to the tokens
  * tok_idx[(b*KH + kh)*idx_stride + j], j < n_idx[b*KH + kh].
  */
@@ -49,6 +50,7 @@ typedef struct {
   double softmax_scale;
   const int32_t *tok_idx, *n_idx;
   int32_t idx_stride;
+  const float *q_scale;
 } oracle_problem;
 
 /* Plain definition: out = sum_t softmax_t(s) v_t, lse = log sum_t exp(s_t). */
@@ -81,6 +83,16 @@ int oracle_quant_partitions(int32_t B, int32_t KH, int32_t D, const int32_t *len
 int oracle_quant_tensor(int32_t B, int32_t KH, int32_t D, const int32_t *lens,
                         const int64_t *seq_offset, int64_t stride_h, int64_t stride_t,
                         const uint16_t *x_bf16, int8_t *codes, float *scale);
+
+/* INT8 query of the page's Schemes A and B (§6: the query quantised in
+ * per-token partitions).  A decode step has one token per sequence, so each
+ * query row (b, qh) of D values is one partition: scales[r] = max|x_r| / 127
+ * and codes by the rule above.  x_bf16 is [rows][D]. */
+int oracle_quant_rows(int32_t rows, int32_t D, const uint16_t *x_bf16, int8_t *codes, float *scales);
+
+/* INT8 codes of n values with a given (static, calibrated) per-tensor scale:
+ * the page's baseline scheme; quotients beyond 127 clamp. */
+int oracle_quant_static(int64_t n, const uint16_t *x_bf16, float scale, int8_t *codes);
 
 /* OAM score of every token of (b, kh):
  * score_t = mean_g (q_g . k_t) * softmax_scale + beta * ln(||v_t||_2 + eps). */

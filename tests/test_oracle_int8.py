@@ -136,3 +136,79 @@ def test_int8_attention_uses_dequantised_values():
     out3, _ = oracle.attention_rows(pb, oracle.all_rows(pb))
     rel = np.linalg.norm(out - out3) / np.linalg.norm(out3)
     assert rel < 0.05
+
+
+# --- INT8 query (Schemes A/B per-token query partitions, baseline static per-tensor scale) ---
+
+
+def test_query_rows_and_static_scale_hand_worked(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "int8_query_examples.json")))
+    codes, scales = oracle.quant_rows(_bf16(g["rows"]).reshape(-1, g["D"]))
+    np.testing.assert_array_equal(codes, np.array(g["row_codes"], np.int8))
+    np.testing.assert_array_equal(scales, np.array(g["row_scales"], np.float32))
+    sc = oracle.quant_static(_bf16(g["static_values"]), g["static_scale"])
+    np.testing.assert_array_equal(sc, np.array(g["static_codes"], np.int8))
+    assert not oracle.quant_static(_bf16(g["static_values"]), 0.0).any()
+
+
+def _query_rows(seed, rows, D):
+    q = synth.fill_q(seed, 1, rows, D, synth.BF16).reshape(rows, D).copy()
+    q[3, 5] = _bf16([-37.5])[0]   # an outlier row
+    q[7] = 0                      # an all-zero row
+    return q
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_query_rows_max_maps_to_127_and_error_bound(D):
+    q = _query_rows(61, 12, D)
+    codes, scales = oracle.quant_rows(q)
+    qf = to32(q).astype(np.float64)
+    assert scales[7] == 0 and not codes[7].any()
+    for r in range(12):
+        if r == 7:
+            continue
+        s, cs, vals = np.float64(scales[r]), codes[r].astype(np.int32), qf[r]
+        big = np.abs(vals) == np.abs(vals).max()
+        assert np.all(cs[big] == np.sign(vals[big]) * 127)
+        assert np.all(np.abs(vals - cs * s) <= s * (0.5 + 2.0 ** -17))
+
+
+def test_query_rows_scale_with_the_row():
+    # doubling a row (exact in bf16) doubles its scale exactly and keeps its codes
+    q = _query_rows(62, 9, 64)
+    q2 = _bf16(to32(q) * np.float32(2.0))
+    c1, s1 = oracle.quant_rows(q)
+    c2, s2 = oracle.quant_rows(q2)
+    np.testing.assert_array_equal(c1, c2)
+    np.testing.assert_array_equal(s2, s1 * np.float32(2.0))
+
+
+def test_static_scale_of_a_row_reproduces_its_row_codes():
+    q = _query_rows(63, 9, 64)
+    codes, scales = oracle.quant_rows(q)
+    for r in range(9):
+        np.testing.assert_array_equal(oracle.quant_static(q[r], scales[r]), codes[r])
+    # a static scale below the row's own clamps the largest values to +-127
+    c = oracle.quant_static(q[3], scales[3] / np.float32(4.0))
+    big = np.abs(to32(q[3])) >= 127.5 * scales[3] / 4.0
+    assert big.any() and np.all(np.abs(c[big]) == 127)
+
+
+def test_int8_query_attention_uses_the_row_scale():
+    # codes with a distinct power-of-two scale per query row: code*scale is exact in fp32, so the
+    # int8-query problem must equal the fp32-query problem on those values (a transposed or shifted
+    # scale index would not)
+    B, KH, G, D, L = 2, 2, 4, 32, 70
+    q, k, v = random_dense(64, B, KH, G, D, L, fmt=synth.BF16)
+    rows = B * KH * G
+    rng = np.random.default_rng(64)
+    codes = rng.integers(-127, 128, size=(rows, D)).astype(np.int8)
+    qs = (2.0 ** -np.arange(3, 3 + rows)).astype(np.float32)
+    p8 = dense_problem(codes.reshape(B, KH * G, D), k, v)
+    p8.q_scale = qs
+    out8, lse8 = oracle.attention_rows(p8, oracle.all_rows(p8))
+    qf = (codes.astype(np.float32) * qs[:, None]).reshape(B, KH * G, D)
+    pf = dense_problem(qf, k, v)
+    outf, lsef = oracle.attention_rows(pf, oracle.all_rows(pf))
+    np.testing.assert_allclose(out8, outf, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse8, lsef, rtol=0, atol=1e-12)
