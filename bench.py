@@ -189,22 +189,50 @@ def summary(r, extra=None):
 
 
 def bench_int8(pkg, torch, synth, steps, warmup, dev):
+    """INT8 KV decode at 128K: the configured workload (bf16 query, K per 64-token partition, V per
+    tensor), then the page's scheme table (§6): A = per-row int8 query with 64- or 128-token K
+    partitions, B = per-row query with one K scale, baseline = static per-tensor query, K and V.
+    Each scheme reports its step time and its output's relative error against the bf16 path."""
     w = synth.workload("int8_128k")
     q, k, v, g = synth.generate(w, nthreads=host_threads())
     geom = dev_geom(pkg, torch, g, dev)
     kd, vd = to_dev(torch, k, dev), to_dev(torch, v, dev)
     del k, v
-    kc, ks = pkg.kv_quant_int8(kd, geom, 64)
-    vc, vs = pkg.kv_quant_int8(vd, geom, 0)
-    torch.cuda.synchronize()
-    del kd, vd
     qd = to_dev(torch, q.reshape(-1), dev).view(w.B, w.QH, w.D)
-    p = pkg.prepare_decode(qd, kc, vc, geom, w.G, k_scale=ks, k_part_tokens=64, v_scale=float(vs.item()),
-                           split_tokens=w.split_tokens)
-    ms, dk, mg = time_decode(torch, p, steps, warmup)
+    ref = pkg.prepare_decode(qd, kd, vd, geom, w.G, split_tokens=w.split_tokens)
+    ref()
+    k_codes = {part: pkg.kv_quant_int8(kd, geom, part) for part in (64, 128, 0)}
+    vc, vs = pkg.kv_quant_int8(vd, geom, 0)
+    # static per-tensor query scale, calibrated once on this query with the library's quantiser
+    qgeom = pkg.KVGeometry(w.B, w.QH, w.D, 1, torch.ones(w.B, dtype=torch.int32, device=dev),
+                           torch.arange(w.B, dtype=torch.int64, device=dev) * (w.QH * w.D), w.D, w.D)
+    _, q_static = pkg.kv_quant_int8(qd.reshape(-1), qgeom, 0)
+    torch.cuda.synchronize()
+    ref_out = ref.out.clone()
+    del kd, vd, ref
+    vs_f, qs_f = float(vs.item()), float(q_static.item())
+
+    def prep(part, q_quant):
+        kc, ks = k_codes[part]
+        return pkg.prepare_decode(qd, kc, vc, geom, w.G, k_scale=ks, k_part_tokens=part, v_scale=vs_f,
+                                  split_tokens=w.split_tokens, q_quant=q_quant, q_scale=qs_f)
+
     tokens = w.kv_tokens()
-    kvb = kv_bytes(tokens, w.KH, w.D, 1) + ks.numel() * 4 + 4
-    return dict(ms=ms, decode_ms=dk, merge_ms=mg, kv_bytes=kvb, split=effective_split(torch, w))
+    p = prep(64, pkg.QUANT_EXACT)
+    ms, dk, mg = time_decode(torch, p, steps, warmup)
+    kvb = kv_bytes(tokens, w.KH, w.D, 1) + k_codes[64][1].numel() * 4 + 4
+    schemes = {}
+    for name, part, qq in (("A_k64", 64, pkg.QUANT_ROW), ("A_k128", 128, pkg.QUANT_ROW),
+                           ("B", 0, pkg.QUANT_ROW), ("baseline", 0, pkg.QUANT_STATIC),
+                           ("bf16_query_k64", 64, pkg.QUANT_EXACT)):
+        ps = prep(part, qq)
+        ms_s, dk_s, mg_s = time_decode(torch, ps, steps, warmup)
+        err = float(torch.linalg.norm(ps.out - ref_out) / torch.linalg.norm(ref_out))
+        b = kv_bytes(tokens, w.KH, w.D, 1) + k_codes[part][1].numel() * 4 + 4
+        schemes[name] = {"us_per_step": round(ms_s * 1e3, 2), "decode_kernel_us": round(dk_s * 1e3, 2),
+                         "kv_gbs": round(b / ms_s / 1e6, 1), "rel_err_vs_bf16": round(err, 5)}
+        del ps
+    return dict(ms=ms, decode_ms=dk, merge_ms=mg, kv_bytes=kvb, split=effective_split(torch, w), schemes=schemes)
 
 
 def bench_oam(pkg, torch, synth, steps, warmup, dev):
@@ -369,6 +397,7 @@ def main():
             try:
                 r = bench_int8(pkg, torch, synth, max(5, K // 2), W, dev)
                 others["int8_128k"] = summary(r)
+                others["int8_128k_schemes"] = r["schemes"]
             except pkg.AttnError as e:
                 others["int8_128k"] = {"error": str(e)}
         if "oam" in todo:

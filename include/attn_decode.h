@@ -64,6 +64,16 @@ typedef enum {
 
 typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1, ATTN_I8 = 2 } attn_dtype;
 
+/* How the query enters the int8 matrix cores with ATTN_I8 KV
+ * ("优化稀疏注意力中的令牌丢弃机制" §6, the scheme table: the baseline scheme
+ * quantises Q with one static per-tensor scale, Schemes A and B in per-token
+ * partitions). */
+typedef enum {
+  ATTN_QUANT_EXACT = 0,  /* no query quantisation (22-bit fixed point, below) */
+  ATTN_QUANT_ROW = 1,    /* int8, one scale per query row (b, qh) */
+  ATTN_QUANT_STATIC = 2  /* int8, one static per-tensor scale given by the caller */
+} attn_q_quant;
+
 /*
  * KV-cache geometry shared by all calls (the problem statement of the NVIDIA
  * blog's decode equations: batch DB = B, KV heads KH, head size Hsz = D,
@@ -99,8 +109,19 @@ typedef struct {
  *   k_scale     ATTN_I8 only: fp32 scale of K row (b, kh, t) is
  *               k_scale[(b*KH + kh)*k_scale_stride + t / k_part_tokens];
  *               k_part_tokens is a multiple of 16 (64 or 128 on the page),
- *               k_scale_stride >= ceil(max_seq_len / k_part_tokens)
+ *               k_scale_stride >= ceil(max_seq_len / k_part_tokens).
+ *               k_part_tokens = 0 selects one per-tensor K scale, k_scale[0]
+ *               (k_scale_stride is then ignored)
  *   v_scale     ATTN_I8 only: the per-tensor V scale (host value)
+ *   q_quant     ATTN_I8 only, an attn_q_quant.  ATTN_QUANT_EXACT keeps the
+ *               query as above.  ATTN_QUANT_ROW quantises each query row in
+ *               the kernel: s = max|q_row| / 127 and code = clamp(rint(q / s),
+ *               -127, 127), both in IEEE fp32 (correctly rounded divide,
+ *               round half to even; s = 0 gives codes 0), so the scores use
+ *               code * s.  ATTN_QUANT_STATIC uses the same rule with
+ *               s = q_scale for every row (quotients beyond 127 clamp).
+ *   q_scale     ATTN_QUANT_STATIC only: the static per-tensor query scale,
+ *               finite and >= 0 (host value)
  *   token_idx   optional: when not NULL, (b, kh) attends only to the tokens
  *               token_idx[(b*KH + kh)*idx_stride + j], j < n_idx[b*KH + kh]
  *               (each < L_b; any order; n_idx <= idx_stride), e.g. the kept
@@ -128,6 +149,8 @@ typedef struct {
   const float *k_scale;
   int32_t k_part_tokens, k_scale_stride;
   float v_scale;
+  int32_t q_quant;
+  float q_scale;
   const int32_t *token_idx;
   const int32_t *n_idx;
   int32_t idx_stride;

@@ -17,6 +17,8 @@ import torch
 
 from . import _lib
 from ._lib import ATTN_BF16, ATTN_F32, ATTN_I8, AttnError  # noqa: F401
+from ._lib import ATTN_QUANT_EXACT as QUANT_EXACT, ATTN_QUANT_ROW as QUANT_ROW  # noqa: F401
+from ._lib import ATTN_QUANT_STATIC as QUANT_STATIC  # noqa: F401
 
 __all__ = ["KVGeometry", "attn_decode_splitkv", "attn_merge_lse", "kv_quant_int8", "oam_value_lognorm",
            "oam_score_topk", "decode_workspace_size", "oam_workspace_size", "prepare_decode", "util_copy",
@@ -74,7 +76,7 @@ class KVGeometry:
 
 
 def _decode_args(q, k, v, geom: KVGeometry, G, out, lse, k_scale, k_part_tokens, k_scale_stride, v_scale,
-                 token_idx, n_idx, idx_stride, softmax_scale, split_tokens, workspace):
+                 token_idx, n_idx, idx_stride, softmax_scale, split_tokens, workspace, q_quant=0, q_scale=0.0):
     a = _lib.AttnDecodeArgs()
     a.kv = geom.c()
     a.G = G
@@ -84,6 +86,7 @@ def _decode_args(q, k, v, geom: KVGeometry, G, out, lse, k_scale, k_part_tokens,
     a.k_part_tokens = k_part_tokens
     a.k_scale_stride = k_scale_stride
     a.v_scale = v_scale
+    a.q_quant, a.q_scale = q_quant, q_scale
     a.token_idx, a.n_idx, a.idx_stride = _ptr(token_idx), _ptr(n_idx), idx_stride
     a.softmax_scale = softmax_scale
     a.split_tokens = split_tokens
@@ -124,18 +127,24 @@ def prepare_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, geom: KVGe
                    k_part_tokens: int = 64, k_scale_stride: Optional[int] = None, v_scale: float = 1.0,
                    token_idx: Optional[torch.Tensor] = None, n_idx: Optional[torch.Tensor] = None,
                    idx_stride: Optional[int] = None, softmax_scale: float = 0.0, split_tokens: int = 0,
+                   q_quant: int = 0, q_scale: float = 0.0,
                    workspace: Optional[torch.Tensor] = None) -> PreparedDecode:
-    """Build (and allocate outputs/workspace for) one ``attn_decode_splitkv`` call."""
+    """Build (and allocate outputs/workspace for) one ``attn_decode_splitkv`` call.
+
+    With int8 KV, ``k_part_tokens=0`` selects one per-tensor K scale (``k_scale[0]``) and
+    ``q_quant`` (QUANT_EXACT / QUANT_ROW / QUANT_STATIC, with ``q_scale``) how the query is
+    quantised."""
     dev = q.device
     QH = geom.KH * G
     if out is None:
         out = torch.empty((geom.B, QH, geom.D), dtype=out_dtype, device=dev)
     if k_scale_stride is None:
-        k_scale_stride = max(1, -(-geom.max_seq_len // k_part_tokens)) if k_scale is not None else 0
+        k_scale_stride = (max(1, -(-geom.max_seq_len // k_part_tokens))
+                          if k_scale is not None and k_part_tokens > 0 else 0)
     if token_idx is not None and idx_stride is None:
         idx_stride = token_idx.shape[-1]
     a = _decode_args(q, k, v, geom, G, out, lse, k_scale, k_part_tokens, k_scale_stride, v_scale, token_idx, n_idx,
-                     idx_stride or 0, softmax_scale, split_tokens, None)
+                     idx_stride or 0, softmax_scale, split_tokens, None, q_quant, q_scale)
     need = decode_workspace_size(a)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)

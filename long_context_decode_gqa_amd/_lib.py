@@ -9,6 +9,7 @@ LIB_PATH = os.path.join(PKG, "libattn_decode.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE_TOO_SMALL, ATTN_ERR_HIP = range(5)
 ATTN_F32, ATTN_BF16, ATTN_I8 = 0, 1, 2
+ATTN_QUANT_EXACT, ATTN_QUANT_ROW, ATTN_QUANT_STATIC = 0, 1, 2
 
 vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 
@@ -21,7 +22,7 @@ class AttnKvGeom(ctypes.Structure):
 class AttnDecodeArgs(ctypes.Structure):
     _fields_ = [("kv", AttnKvGeom), ("G", i32), ("q_dtype", i32), ("kv_dtype", i32), ("out_dtype", i32),
                 ("q", vp), ("k", vp), ("v", vp), ("k_scale", vp), ("k_part_tokens", i32), ("k_scale_stride", i32),
-                ("v_scale", f32), ("token_idx", vp), ("n_idx", vp), ("idx_stride", i32), ("softmax_scale", f32),
+                ("v_scale", f32), ("q_quant", i32), ("q_scale", f32), ("token_idx", vp), ("n_idx", vp), ("idx_stride", i32), ("softmax_scale", f32),
                 ("split_tokens", i32), ("workspace", vp), ("workspace_bytes", sz), ("out", vp), ("lse", vp)]
 
 

@@ -96,13 +96,21 @@ attn_status plan_decode(const attn_decode_args *a, DecodeLayout *L) {
     return fail(ATTN_ERR_INVALID_ARG, "split_tokens must be 0 or a positive multiple of 32 (<= 2^20)");
   if (a->token_idx && (!a->n_idx || a->idx_stride < 0))
     return fail(ATTN_ERR_INVALID_ARG, "token_idx needs n_idx and idx_stride >= 0");
+  if (a->q_quant != ATTN_QUANT_EXACT && a->q_quant != ATTN_QUANT_ROW && a->q_quant != ATTN_QUANT_STATIC)
+    return fail(ATTN_ERR_INVALID_ARG, "q_quant must be ATTN_QUANT_EXACT, ATTN_QUANT_ROW or ATTN_QUANT_STATIC");
+  if (a->q_quant != ATTN_QUANT_EXACT && a->kv_dtype != ATTN_I8)
+    return fail(ATTN_ERR_UNSUPPORTED, "query quantisation needs int8 KV");
+  if (a->q_quant == ATTN_QUANT_STATIC && !(a->q_scale >= 0.f && a->q_scale < INFINITY))
+    return fail(ATTN_ERR_INVALID_ARG, "q_scale must be finite and >= 0");
   if (a->kv_dtype == ATTN_I8) {
     if (!a->k_scale) return fail(ATTN_ERR_INVALID_ARG, "int8 KV needs k_scale");
-    if (a->k_part_tokens < 16 || a->k_part_tokens % 16)
-      return fail(ATTN_ERR_INVALID_ARG, "k_part_tokens must be a positive multiple of 16");
-    const int64_t need = ((int64_t)g.max_seq_len + a->k_part_tokens - 1) / a->k_part_tokens;
-    if (a->k_scale_stride < need || a->k_scale_stride < 1)
-      return fail(ATTN_ERR_INVALID_ARG, "k_scale_stride must be >= ceil(max_seq_len / k_part_tokens)");
+    if (a->k_part_tokens != 0) {  // 0: one per-tensor K scale
+      if (a->k_part_tokens < 16 || a->k_part_tokens % 16)
+        return fail(ATTN_ERR_INVALID_ARG, "k_part_tokens must be 0 or a positive multiple of 16");
+      const int64_t need = ((int64_t)g.max_seq_len + a->k_part_tokens - 1) / a->k_part_tokens;
+      if (a->k_scale_stride < need || a->k_scale_stride < 1)
+        return fail(ATTN_ERR_INVALID_ARG, "k_scale_stride must be >= ceil(max_seq_len / k_part_tokens)");
+    }
     if (!(fabsf(a->v_scale) < INFINITY)) return fail(ATTN_ERR_INVALID_ARG, "v_scale must be finite");
   }
   if (g.B > 0) {
@@ -204,9 +212,12 @@ static attn_status decode_impl(const attn_decode_args *a, attn_stream_t stream, 
   p.k = a->k;
   p.v = a->v;
   p.k_scale = a->k_scale;
-  p.k_part = a->k_part_tokens > 0 ? a->k_part_tokens : 64;
-  p.k_scale_stride = a->k_scale_stride;
+  // a per-tensor K scale is one partition longer than any sequence
+  p.k_part = a->k_part_tokens > 0 ? a->k_part_tokens : (1 << 30);
+  p.k_scale_stride = a->k_part_tokens > 0 ? a->k_scale_stride : 0;
   p.v_scale = a->v_scale;
+  p.q_quant = a->q_quant;
+  p.q_scale = a->q_scale;
   p.token_idx = a->token_idx;
   p.n_idx = a->n_idx;
   p.idx_stride = a->idx_stride;

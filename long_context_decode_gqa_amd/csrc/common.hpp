@@ -100,6 +100,8 @@ struct DecodeParams {
   const float *k_scale;
   int32_t k_part, k_scale_stride;
   float v_scale;
+  int32_t q_quant;  // attn_q_quant (int8 KV)
+  float q_scale;    // static query scale (ATTN_QUANT_STATIC)
   const int32_t *token_idx, *n_idx;
   int32_t idx_stride;
   float softmax_scale;

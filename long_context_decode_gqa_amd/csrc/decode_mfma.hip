@@ -109,7 +109,7 @@ constexpr int kMaxIdxChunk = 1024;
 // the loop.  A range is cut into runs (one lane each) and runs into segments
 // (one chunk piece each); a segment's partial (m, l, o) goes straight from
 // registers to its slot.
-template <int D, int KVT, bool IDX>
+template <int D, int KVT, bool IDX, bool QI8>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_mfma_kernel(DecodeParams p) {
   typedef Tile<D, KVT, IDX> TileT;
   typedef Step<D, KVT, IDX> StepT;
@@ -188,7 +188,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // codes.  Head g's query becomes q = s_g * n with s_g = max|q_g| / 2^22
     // and n = rint(q / s_g) = 65536 d2 + 256 d1 + d0, d0, d1 in [-128, 127]
     // and |d2| <= 64 (|error| <= max|q_g| * 2^-23); each digit plane is one
-    // int8 MFMA, and the three integer sums recombine exactly in fp32.
+    // int8 MFMA, and the three integer sums recombine exactly in fp32.  An
+    // int8 query (QI8: per-row or static scale) is plane 0 alone.
     float qs = 0.f;  // int8: this lane's head (col) scale s_col
     __syncthreads();
     if constexpr (KVT == ATTN_I8) {
@@ -209,33 +210,57 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
       for (int j = 0; j < CPL; ++j) mx = fmaxf(mx, fabsf(qv[j]));
       mx = rows_max(mx);  // the four lanes of head col hold all D channels
-      const float inv = mx > 0.f ? 4194304.0f / mx : 0.f;
-      qs = mx * (1.0f / 4194304.0f);
-      uint32_t dw[3][CPL / 4];
+      if constexpr (QI8) {
+        // int8 query (one digit plane): s = max|q_row| / 127, or the static
+        // scale, and code = clamp(rint(q / s), -127, 127), in IEEE fp32
+        // (correctly rounded divides, round half to even).
+        const float sq = p.q_quant == ATTN_QUANT_ROW ? mx / 127.0f : p.q_scale;
+        qs = sq;
 #pragma unroll
-      for (int j4 = 0; j4 < CPL / 4; ++j4) {
-        uint32_t w0 = 0u, w1 = 0u, w2 = 0u;
+        for (int x = 0; x < CPL / 16; ++x) {
+          uint32_t w[4];
 #pragma unroll
-        for (int y = 0; y < 4; ++y) {
-          const int n = (int)__builtin_rintf(qv[4 * j4 + y] * inv);
-          const int d0 = (int)(int8_t)(n & 0xFF);
-          const int r1 = (n - d0) >> 8;
-          const int d1 = (int)(int8_t)(r1 & 0xFF);
-          const int d2 = (r1 - d1) >> 8;
-          w0 |= (uint32_t)(d0 & 0xFF) << (8 * y);
-          w1 |= (uint32_t)(d1 & 0xFF) << (8 * y);
-          w2 |= (uint32_t)(d2 & 0xFF) << (8 * y);
+          for (int j4 = 0; j4 < 4; ++j4) {
+            uint32_t acc = 0u;
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+              float c = 0.f;
+              if (sq > 0.f) c = fminf(127.f, fmaxf(-127.f, __builtin_rintf(qv[16 * x + 4 * j4 + y] / sq)));
+              acc |= ((uint32_t)(int)c & 0xFFu) << (8 * y);
+            }
+            w[j4] = acc;
+          }
+          *(u32x4_t *)(s_q + col * kQDRow + cg * CPL + 16 * x) = (u32x4_t){w[0], w[1], w[2], w[3]};
         }
-        dw[0][j4] = w0;
-        dw[1][j4] = w1;
-        dw[2][j4] = w2;
+      } else {
+        const float inv = mx > 0.f ? 4194304.0f / mx : 0.f;
+        qs = mx * (1.0f / 4194304.0f);
+        uint32_t dw[3][CPL / 4];
+#pragma unroll
+        for (int j4 = 0; j4 < CPL / 4; ++j4) {
+          uint32_t w0 = 0u, w1 = 0u, w2 = 0u;
+#pragma unroll
+          for (int y = 0; y < 4; ++y) {
+            const int n = (int)__builtin_rintf(qv[4 * j4 + y] * inv);
+            const int d0 = (int)(int8_t)(n & 0xFF);
+            const int r1 = (n - d0) >> 8;
+            const int d1 = (int)(int8_t)(r1 & 0xFF);
+            const int d2 = (r1 - d1) >> 8;
+            w0 |= (uint32_t)(d0 & 0xFF) << (8 * y);
+            w1 |= (uint32_t)(d1 & 0xFF) << (8 * y);
+            w2 |= (uint32_t)(d2 & 0xFF) << (8 * y);
+          }
+          dw[0][j4] = w0;
+          dw[1][j4] = w1;
+          dw[2][j4] = w2;
+        }
+#pragma unroll
+        for (int dg = 0; dg < 3; ++dg)
+#pragma unroll
+          for (int x = 0; x < CPL / 16; ++x)
+            *(u32x4_t *)(s_q + (dg * 16 + col) * kQDRow + cg * CPL + 16 * x) =
+                (u32x4_t){dw[dg][4 * x], dw[dg][4 * x + 1], dw[dg][4 * x + 2], dw[dg][4 * x + 3]};
       }
-#pragma unroll
-      for (int dg = 0; dg < 3; ++dg)
-#pragma unroll
-        for (int x = 0; x < CPL / 16; ++x)
-          *(u32x4_t *)(s_q + (dg * 16 + col) * kQDRow + cg * CPL + 16 * x) =
-              (u32x4_t){dw[dg][4 * x], dw[dg][4 * x + 1], dw[dg][4 * x + 2], dw[dg][4 * x + 3]};
     } else {
       for (int e = lane; e < 16 * (D / 8); e += 64) {
         const int g = e / (D / 8), c8 = e - g * (D / 8);
@@ -340,11 +365,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
           for (int kb = 0; kb < KL; ++kb) {
             const i32x4_t kop = __builtin_bit_cast(i32x4_t, R.k[tb][kb]);
             a0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, q_digits(0, kb), a0, 0, 0, 0);
-            a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, q_digits(1, kb), a1, 0, 0, 0);
-            a2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, q_digits(2, kb), a2, 0, 0, 0);
+            if constexpr (!QI8) {
+              a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, q_digits(1, kb), a1, 0, 0, 0);
+              a2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, q_digits(2, kb), a2, 0, 0, 0);
+            }
           }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] = ((float)a2[i] * 65536.0f + (float)a1[i] * 256.0f) + (float)a0[i];
+          for (int i = 0; i < 4; ++i)
+            acc[i] = QI8 ? (float)a0[i] : ((float)a2[i] * 65536.0f + (float)a1[i] * 256.0f) + (float)a0[i];
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) r.v[4 * tb + i] = acc[i];
@@ -542,11 +570,14 @@ template <bool IDX>
 static void launch_variant(const DecodeParams &p, int kv_dtype, dim3 g, hipStream_t s) {
   dim3 blk(64);
   if (kv_dtype == ATTN_BF16) {
-    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_BF16, IDX>), g, blk, 0, s, p);
-    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_BF16, IDX>), g, blk, 0, s, p);
+    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_BF16, IDX, false>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_BF16, IDX, false>), g, blk, 0, s, p);
+  } else if (p.q_quant == ATTN_QUANT_EXACT) {
+    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_I8, IDX, false>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_I8, IDX, false>), g, blk, 0, s, p);
   } else {
-    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_I8, IDX>), g, blk, 0, s, p);
-    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_I8, IDX>), g, blk, 0, s, p);
+    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_I8, IDX, true>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_I8, IDX, true>), g, blk, 0, s, p);
   }
 }
 

@@ -94,6 +94,13 @@ def test_workspace_size_counts_partials():
     (dict(kv_dtype=_lib.ATTN_I8, k_scale=FAKE, k_part_tokens=40, k_scale_stride=64), _lib.ATTN_ERR_INVALID_ARG),
     (dict(token_idx=FAKE), _lib.ATTN_ERR_INVALID_ARG),                 # no n_idx
     (dict(softmax_scale=float("inf")), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(q_quant=3), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(q_quant=_lib.ATTN_QUANT_ROW), _lib.ATTN_ERR_UNSUPPORTED),   # int8 query needs int8 KV
+    (dict(kv_dtype=_lib.ATTN_I8, k_scale=FAKE, k_part_tokens=0, q_quant=_lib.ATTN_QUANT_STATIC, q_scale=-1.0),
+     _lib.ATTN_ERR_INVALID_ARG),
+    (dict(kv_dtype=_lib.ATTN_I8, k_scale=FAKE, k_part_tokens=0, q_quant=_lib.ATTN_QUANT_STATIC,
+          q_scale=float("inf")), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(kv_dtype=_lib.ATTN_I8, k_scale=FAKE, k_part_tokens=-64, k_scale_stride=64), _lib.ATTN_ERR_INVALID_ARG),
 ])
 def test_invalid_arguments_are_rejected_on_the_host(over, status):
     a = _args(**over)
@@ -113,6 +120,9 @@ def test_workspace_too_small_is_reported_before_launch():
 
 def test_int8_and_fp32_paths_validate():
     assert _ws(_args(kv_dtype=_lib.ATTN_I8, k_scale=FAKE, k_part_tokens=64, k_scale_stride=64))[0] == 0
+    # per-tensor K (k_part_tokens 0, stride ignored) with each query mode
+    for qq, qs in ((_lib.ATTN_QUANT_EXACT, 0.0), (_lib.ATTN_QUANT_ROW, 0.0), (_lib.ATTN_QUANT_STATIC, 0.02)):
+        assert _ws(_args(kv_dtype=_lib.ATTN_I8, k_scale=FAKE, k_part_tokens=0, q_quant=qq, q_scale=qs))[0] == 0
     a = _args(q_dtype=_lib.ATTN_F32, kv_dtype=_lib.ATTN_F32, g_D=64, g_stride_h=4096 * 64, g_stride_t=64)
     assert _ws(a)[0] == 0
     a = _args(q_dtype=_lib.ATTN_F32, kv_dtype=_lib.ATTN_F32, g_D=66, g_stride_h=4096 * 68, g_stride_t=68)
@@ -131,3 +141,26 @@ def test_merge_and_quant_validation():
         _lib.ATTN_ERR_WORKSPACE_TOO_SMALL
     n = ctypes.c_size_t(7)
     assert L.kv_quant_int8_workspace_size(ctypes.byref(g), 0, ctypes.byref(n)) == 0 and n.value >= 4
+
+
+def test_argument_structs_match_the_header_layout(tmp_path):
+    """The binding's ctypes structs have the C header's field offsets and sizes (gcc on this host)."""
+    structs = {"attn_decode_args": _lib.AttnDecodeArgs, "attn_kv_geom": _lib.AttnKvGeom,
+               "oam_topk_args": _lib.OamTopkArgs}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "attn_decode.h"', "int main(void) {"]
+    for cname, cls in structs.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f in cls._fields_:
+            lines.append(f'printf("{cname} {f[0]} %zu\\n", offsetof({cname}, {f[0]}));')
+    lines += ["return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    import subprocess
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l}
+    for cname, cls in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(cls), cname
+        for f in cls._fields_:
+            assert got[(cname, f[0])] == getattr(cls, f[0]).offset, (cname, f[0])

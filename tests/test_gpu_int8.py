@@ -74,12 +74,12 @@ def test_tensor_quant_bit_exact_and_zero_partitions():
     assert ks[(0 * g.KH + 1) * 5 + 1] == 0.0
 
 
-def run_int8_decode(w, q, kc, vc, ks, vs, g, part=64, token_idx=None, n_idx=None, split=1024):
+def run_int8_decode(w, q, kc, vc, ks, vs, g, part=64, token_idx=None, n_idx=None, split=1024, **extra):
     qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
     lse = torch.empty((w.B, w.QH), dtype=torch.float32, device=DEV)
-    kw = {}
+    kw = dict(extra)
     if token_idx is not None:
-        kw = dict(token_idx=to_dev(token_idx), n_idx=to_dev(n_idx))
+        kw.update(token_idx=to_dev(token_idx), n_idx=to_dev(n_idx))
     out, _ = pkg.attn_decode_splitkv(qd, to_dev(kc), to_dev(vc), dev_geom(g), w.G, lse=lse, k_scale=to_dev(ks),
                                      k_part_tokens=part, v_scale=float(vs), split_tokens=split, **kw)
     torch.cuda.synchronize()
@@ -152,3 +152,128 @@ def test_int8_128k_full_size():
     refb, _ = oracle.attention_rows(pb, rows[:4], nthreads=16)
     rel = np.linalg.norm(out[idx[:4]] - refb) / np.linalg.norm(refb)
     print(f"[info] int8 vs bf16 relative error on sampled rows: {rel:.4f}")
+
+
+# --- the page's INT8 schemes (§6 scheme table): query per row (A, B) or static per tensor (baseline);
+# K per 64/128-token partition (A) or per tensor (B, baseline); V per tensor ---
+
+SCHEMES = {
+    "A64": dict(k_part=64, q_quant=pkg.QUANT_ROW),
+    "A128": dict(k_part=128, q_quant=pkg.QUANT_ROW),
+    "B": dict(k_part=0, q_quant=pkg.QUANT_ROW),
+    "baseline": dict(k_part=0, q_quant=pkg.QUANT_STATIC),
+}
+
+
+def scheme_inputs(w, q, k, v, g, scheme, static_shrink=1.0):
+    """GPU-quantised K/V codes for the scheme, plus the oracle's own int8 query (codes and per-row
+    scales) and the oracle problem on those values."""
+    sc = SCHEMES[scheme]
+    kc, ks = gpu_quant(k, g, sc["k_part"])
+    vc, vsa = gpu_quant(v, g, 0)
+    rows = q.reshape(w.B * w.QH, w.D)
+    q_scale = 0.0
+    if sc["q_quant"] == pkg.QUANT_ROW:
+        qc, qs = oracle.quant_rows(rows)
+    else:
+        # a static scale calibrated on this query (max|Q| / 127), optionally shrunk so that codes clamp
+        q_scale = float(np.float32(np.abs(synth.bf16_bits_to_f32(rows)).max()) / np.float32(127.0)
+                        * np.float32(static_shrink))
+        qc = oracle.quant_static(rows, q_scale)
+        qs = np.full(w.B * w.QH, q_scale, np.float32)
+    if sc["k_part"]:
+        stride = -(-int(g.max_len) // sc["k_part"])
+        kk = dict(k_scale=ks, k_part=sc["k_part"], k_scale_stride=stride)
+    else:
+        kk = dict(k_scale=np.full(w.B * w.KH, ks[0], np.float32), k_part=1 << 30, k_scale_stride=1)
+    p = problem(w, qc.reshape(q.shape), kc, vc, g, v_scale=float(vsa[0]), q_scale=qs, **kk)
+    run = dict(part=sc["k_part"], q_quant=sc["q_quant"], q_scale=q_scale)
+    return kc, vc, ks, vsa[0], p, run, qc, qs
+
+
+@pytest.mark.parametrize("scheme", list(SCHEMES))
+@pytest.mark.parametrize("G,D", [(8, 128), (4, 64)])
+def test_int8_schemes_match_oracle(scheme, G, D):
+    lens = np.array([3000, 1, 64, 1500, 0], np.int32)
+    w = synth.workload("int8_128k", B=len(lens), KH=2, G=G, D=D, lens=lens, layout="token_major", seed=70 + G)
+    q, k, v, g = gen_kv(w)
+    log_case(f"int8 scheme {scheme} G={G} D={D}")
+    kc, vc, ks, vs, p, run, _, _ = scheme_inputs(w, q, k, v, g, scheme)
+    ref, ref_lse = oracle.attention_rows(p, oracle.all_rows(p), nthreads=8)
+    fin = np.isfinite(ref_lse)
+    for split in (1024, 0):
+        log_case(f"int8 scheme {scheme} G={G} D={D} split={split}")
+        out, lse = run_int8_decode(w, q, kc, vc, ks, vs, g, split=split, **run)
+        assert np.abs(out - ref).max() <= 2e-3
+        assert np.abs(lse[fin] - ref_lse[fin]).max() <= 1e-3
+        assert np.all(np.isneginf(lse[~fin]))
+
+
+def test_int8_static_query_scale_clamps():
+    # a static scale below the query's range: the largest query values clamp to +-127 on both sides
+    lens = np.array([900, 2100], np.int32)
+    w = synth.workload("int8_128k", B=2, KH=2, G=8, lens=lens, layout="token_major", seed=77)
+    q, k, v, g = gen_kv(w)
+    log_case("int8 static query scale with clamping")
+    kc, vc, ks, vs, p, run, qc, _ = scheme_inputs(w, q, k, v, g, "baseline", static_shrink=0.5)
+    assert np.any(np.abs(qc) == 127) and np.count_nonzero(np.abs(qc) == 127) > 4
+    ref, _ = oracle.attention_rows(p, oracle.all_rows(p), nthreads=8)
+    out, _ = run_int8_decode(w, q, kc, vc, ks, vs, g, split=512, **run)
+    assert np.abs(out - ref).max() <= 2e-3
+
+
+@pytest.mark.parametrize("q_quant", [pkg.QUANT_ROW, pkg.QUANT_STATIC, pkg.QUANT_EXACT])
+@pytest.mark.parametrize("D", [128, 64])
+def test_query_codes_read_back_through_one_hot_keys(q_quant, D):
+    """The kernel's query codes, bit for bit: with K row t = e_t (code 1, per-tensor scale 1),
+    V row t = e_t and softmax scale 1, out[d] = exp(q_hat[d] - lse), so q_hat[d] = ln(out[d]) + lse
+    and code[d] = q_hat[d] / s.  Each (b, qh) row has its own scale."""
+    B, KH, G = 2, 2, 8
+    geom = synth.dense_geometry(B, KH, D, D)
+    kc = np.zeros((B, KH, D, D), np.int8)
+    kc[:, :, np.arange(D), np.arange(D)] = 1
+    q = synth.fill_q(78 + D, B, KH * G, D, synth.BF16).reshape(B * KH * G, D).copy()
+    q[5] = 0                                       # an all-zero row: scale 0, codes 0
+    qf = synth.bf16_bits_to_f32(q).astype(np.float64)
+    static = float(np.float32(np.abs(qf).max()) / np.float32(127.0) * np.float32(0.75))
+    log_case(f"query codes via one-hot keys q_quant={q_quant} D={D}")
+    lse = torch.empty((B, KH * G), dtype=torch.float32, device=DEV)
+    out, _ = pkg.attn_decode_splitkv(to_dev(q).view(B, KH * G, D), to_dev(kc.reshape(-1)), to_dev(kc.reshape(-1)),
+                                     dev_geom(geom), G, lse=lse, k_scale=to_dev(np.ones(1, np.float32)),
+                                     k_part_tokens=0, v_scale=1.0, softmax_scale=1.0, split_tokens=0,
+                                     q_quant=q_quant, q_scale=static)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy().reshape(B * KH * G, D).astype(np.float64)
+    lse = lse.cpu().numpy().reshape(-1).astype(np.float64)
+    qhat = np.log(out) + lse[:, None]
+    if q_quant == pkg.QUANT_EXACT:
+        # the 22-bit form reproduces the bf16 query to far below the read-back noise
+        assert np.abs(qhat - qf).max() <= 1e-4
+        return
+    if q_quant == pkg.QUANT_ROW:
+        codes, scales = oracle.quant_rows(q)
+    else:
+        codes = oracle.quant_static(q, static)
+        scales = np.full(len(q), static, np.float32)
+    live = scales > 0
+    got = qhat[live] / scales[live, None].astype(np.float64)
+    assert np.abs(got - np.rint(got)).max() <= 0.02
+    np.testing.assert_array_equal(np.rint(got).astype(np.int32), codes[live].astype(np.int32))
+    # the zero row: uniform softmax, q_hat = 0 (scale 0 per row; a static scale codes it as 0 too)
+    assert np.abs(qhat[5]).max() <= 1e-5
+
+
+def test_int8_scheme_a_128k_full_size():
+    """Scheme A at full size (4 x 8 KV heads x 131072 tokens x 128, 64-token K partitions, per-row
+    int8 query), in the benchmark's launch configuration, on sampled rows."""
+    w = synth.workload("int8_128k")
+    q, k, v, g = gen_kv(w)
+    log_case("int8 scheme A 128k full size")
+    kc, vc, ks, vs, p, run, _, _ = scheme_inputs(w, q, k, v, g, "A64")
+    out, lse = run_int8_decode(w, q, kc, vc, ks, vs, g, split=w.split_tokens, **run)
+    rng = np.random.default_rng(6)
+    rows = [(int(b), int(h)) for b, h in zip(rng.integers(0, w.B, 10), rng.integers(0, w.QH, 10))] + [(3, 63)]
+    ref, ref_lse = oracle.attention_rows(p, rows, nthreads=16)
+    idx = [b * w.QH + h for b, h in rows]
+    assert np.abs(out[idx] - ref).max() <= 2e-3
+    assert np.abs(lse[idx] - ref_lse).max() <= 1e-3
