@@ -115,3 +115,31 @@ def test_one_dominant_token_with_k1_returns_its_value():
     assert list(idx) == [17]
     out, _ = oracle.attention_rows(with_tokens(p, [idx]), oracle.all_rows(p))
     np.testing.assert_allclose(out, np.broadcast_to(v[0, 0, 17].astype(np.float64), out.shape), rtol=0, atol=1e-9)
+
+
+def test_oam_over_an_int8_cache_uses_the_dequantised_values():
+    """The page's §7 stack: OAM over an INT8 cache scores the values the attention reads, code x
+    scale.  With power-of-two K partition scales and V scale, code x scale is exact in fp32, so the
+    INT8 problem's scores and value terms equal those of the fp32 problem on those values (a wrong
+    partition index or a missing V scale would not)."""
+    B, KH, G, D, L, part = 2, 2, 4, 32, 200, 64
+    rng = np.random.default_rng(81)
+    geom = synth.dense_geometry(B, KH, L, D)
+    kc = rng.integers(-127, 128, size=(B, KH, L, D)).astype(np.int8)
+    vc = rng.integers(-127, 128, size=(B, KH, L, D)).astype(np.int8)
+    stride = -(-L // part)
+    ks = (2.0 ** -rng.integers(3, 9, size=B * KH * stride)).astype(np.float32)
+    vs = np.float32(2.0 ** -6)
+    q = synth.fill_q(81, B, KH * G, D, synth.BF16)
+    p8 = dense_problem(q, kc, vc)
+    p8.k_scale, p8.k_part, p8.k_scale_stride, p8.v_scale = ks, part, stride, float(vs)
+    kf = kc.astype(np.float32) * np.repeat(ks.reshape(B, KH, stride), part, axis=2)[:, :, :L, None]
+    vf = vc.astype(np.float32) * vs
+    pf = dense_problem(q, kf, vf)
+    for b in range(B):
+        for kh in range(KH):
+            np.testing.assert_allclose(oracle.value_lognorm(p8, b, kh, 1e-6), oracle.value_lognorm(pf, b, kh, 1e-6),
+                                       rtol=0, atol=1e-12)
+            s8 = oracle.oam_scores(p8, b, kh, 1.0, 1e-6)
+            np.testing.assert_allclose(s8, oracle.oam_scores(pf, b, kh, 1.0, 1e-6), rtol=0, atol=1e-12)
+            assert list(oracle.topk_sort(s8, 37)) == list(oracle.topk_sort(oracle.oam_scores(pf, b, kh, 1.0, 1e-6), 37))
