@@ -235,22 +235,30 @@ attn_status kv_quant_int8(const attn_kv_geom *geom, const void *x_bf16, int32_t 
                           size_t workspace_bytes, attn_stream_t stream);
 
 /*
- * ln(||v_t||_2 + eps) of every bf16 V row, the value term of the OAM score
+ * ln(||v_t||_2 + eps) of every V row, the value term of the OAM score
  * ("优化稀疏注意力中的令牌丢弃机制" §3: torch.log(v_i.norm() + eps)).  A row never
  * changes once appended, so this can be computed at append time and passed
  * to oam_score_topk.  vlog[(b*KH + kh)*vlog_stride + t] for t < L_b
- * (vlog_stride >= max_seq_len).  Accumulates in fp32.
+ * (vlog_stride >= max_seq_len).  v_dtype is ATTN_BF16, or ATTN_I8 for an
+ * INT8 cache whose rows are code * v_scale (the norm of those values; §7
+ * stacks OAM on the INT8 cache).  Accumulates in fp32.
  */
-attn_status oam_value_lognorm(const attn_kv_geom *geom, const void *v_bf16, float eps, float *vlog,
-                              int32_t vlog_stride, attn_stream_t stream);
+attn_status oam_value_lognorm(const attn_kv_geom *geom, const void *v, int32_t v_dtype, float v_scale, float eps,
+                              float *vlog, int32_t vlog_stride, attn_stream_t stream);
 
 /*
  * Arguments of output-aware top-K token selection.
- *   q, k        bf16; q [B][KH*G][D], k in geometry `kv`; 1 <= G <= 16;
- *               max_seq_len <= 2^21 (ATTN_ERR_UNSUPPORTED otherwise)
+ *   q           bf16 [B][KH*G][D]; 1 <= G <= 16
+ *   k           KV cache in kv_dtype and geometry `kv`; max_seq_len <= 2^21
+ *               (ATTN_ERR_UNSUPPORTED otherwise)
+ *   kv_dtype    ATTN_BF16, or ATTN_I8 to score an INT8 cache (the page's §7
+ *               stack: OAM, then INT8 attention over the kept tokens) with
+ *               the K scales of attn_decode_args: k_scale[(b*KH + kh)*
+ *               k_scale_stride + t / k_part_tokens], k_part_tokens = 0 for
+ *               one per-tensor scale k_scale[0]; v rows are code * v_scale
  *   v, vlog     the value term comes from vlog (fp32, layout of
  *               oam_value_lognorm, stride vlog_stride) when vlog != NULL,
- *               else it is computed from the bf16 rows of v on the fly
+ *               else it is computed from the rows of v (kv_dtype) on the fly
  *   softmax_scale  0 selects 1/sqrt(D); beta, eps as on the page
  *   top_k       >= 1 tokens kept per (b, kh)
  *   idx_out     int32 [B][KH][top_k]: kept token indices in ascending order;
@@ -265,6 +273,10 @@ typedef struct {
   const void *q;
   const void *k;
   const void *v;
+  int32_t kv_dtype;
+  const float *k_scale;
+  int32_t k_part_tokens, k_scale_stride;
+  float v_scale;
   const float *vlog;
   int32_t vlog_stride;
   float softmax_scale, beta, eps;
@@ -284,7 +296,9 @@ attn_status oam_score_topk_workspace_size(const oam_topk_args *args, size_t *byt
  * tokens by routing logit plus value magnitude and drop the lowest; §2 for
  * the classic q.k top-K it replaces).  For each (b, kh):
  *   score_t = mean_g (q_g . k_t) * softmax_scale + beta * ln(||v_t||_2 + eps)
- * (the mean over the G query heads gives one kept set per KV head), then the
+ * (the mean over the G query heads gives one kept set per KV head; with
+ * INT8 K the int8 matrix cores take the mean query as a 22-bit fixed-point
+ * value, as attn_decode_splitkv does for its query), then the
  * top_k tokens by (score descending, index ascending) are kept.  Scores are
  * fp32; the selection is an exact radix select on order-preserving integer
  * keys of the fp32 scores.  Feed idx_out/n_kept to attn_decode_splitkv's

@@ -204,24 +204,27 @@ def kv_quant_int8(x: torch.Tensor, geom: KVGeometry, partition_tokens: int = 64,
 
 
 def oam_value_lognorm(v: torch.Tensor, geom: KVGeometry, eps: float = 1e-6, vlog=None,
-                      vlog_stride: Optional[int] = None, stream=None):
-    """ln(||v_t|| + eps) per V row -> fp32 [B*KH, vlog_stride]."""
+                      vlog_stride: Optional[int] = None, stream=None, v_scale: float = 1.0):
+    """ln(||v_t|| + eps) per V row -> fp32 [B*KH, vlog_stride]; an int8 ``v`` holds codes of scale ``v_scale``."""
     if vlog_stride is None:
         vlog_stride = max(1, geom.max_seq_len)
     if vlog is None:
         vlog = torch.zeros((geom.B * geom.KH, vlog_stride), dtype=torch.float32, device=v.device)
     g = geom.c()
-    st = _lib.load().oam_value_lognorm(ctypes.byref(g), _ptr(v), eps, _ptr(vlog), vlog_stride, _stream(stream))
+    st = _lib.load().oam_value_lognorm(ctypes.byref(g), _ptr(v), _code(v), v_scale, eps, _ptr(vlog), vlog_stride,
+                                       _stream(stream))
     _lib.check(st, "oam_value_lognorm")
     return vlog
 
 
 def _oam_args(q, k, geom, G, top_k, v, vlog, vlog_stride, softmax_scale, beta, eps, idx_out, n_kept, scores_out,
-              workspace):
+              workspace, k_scale=None, k_part_tokens=0, k_scale_stride=0, v_scale=1.0):
     a = _lib.OamTopkArgs()
     a.kv = geom.c()
     a.G = G
     a.q, a.k, a.v, a.vlog = _ptr(q), _ptr(k), _ptr(v), _ptr(vlog)
+    a.kv_dtype = _code(k)
+    a.k_scale, a.k_part_tokens, a.k_scale_stride, a.v_scale = _ptr(k_scale), k_part_tokens, k_scale_stride, v_scale
     a.vlog_stride = vlog_stride
     a.softmax_scale, a.beta, a.eps = softmax_scale, beta, eps
     a.top_k = top_k
@@ -250,8 +253,14 @@ class PreparedOam:
 
 def prepare_oam(q, k, geom: KVGeometry, G: int, top_k: int, *, v=None, vlog=None, vlog_stride: Optional[int] = None,
                 softmax_scale: float = 0.0, beta: float = 1.0, eps: float = 1e-6, idx_out=None, n_kept=None,
-                scores_out=None, workspace=None) -> PreparedOam:
+                scores_out=None, workspace=None, k_scale=None, k_part_tokens: int = 64,
+                k_scale_stride: Optional[int] = None, v_scale: float = 1.0) -> PreparedOam:
+    """One ``oam_score_topk`` call.  An int8 ``k`` (and ``v``) is an INT8 cache with the K scales of
+    ``prepare_decode`` (``k_part_tokens=0``: one per-tensor scale) and the V scale ``v_scale``."""
     dev = q.device
+    if k_scale_stride is None:
+        k_scale_stride = (max(1, -(-geom.max_seq_len // k_part_tokens))
+                          if k_scale is not None and k_part_tokens > 0 else 0)
     npairs = geom.B * geom.KH
     if idx_out is None:
         idx_out = torch.empty((npairs, top_k), dtype=torch.int32, device=dev)
@@ -260,12 +269,12 @@ def prepare_oam(q, k, geom: KVGeometry, G: int, top_k: int, *, v=None, vlog=None
     if vlog is not None and vlog_stride is None:
         vlog_stride = vlog.shape[-1]
     a = _oam_args(q, k, geom, G, top_k, v, vlog, vlog_stride or 0, softmax_scale, beta, eps, idx_out, n_kept,
-                  scores_out, None)
+                  scores_out, None, k_scale, k_part_tokens if k_scale is not None else 0, k_scale_stride, v_scale)
     need = oam_workspace_size(a)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
-    p = PreparedOam(a, [q, k, v, vlog, geom, idx_out, n_kept, scores_out, workspace])
+    p = PreparedOam(a, [q, k, v, vlog, geom, idx_out, n_kept, scores_out, workspace, k_scale])
     p.idx_out, p.n_kept, p.scores_out, p.workspace = idx_out, n_kept, scores_out, workspace
     return p
 

@@ -27,7 +27,8 @@ class AttnDecodeArgs(ctypes.Structure):
 
 
 class OamTopkArgs(ctypes.Structure):
-    _fields_ = [("kv", AttnKvGeom), ("G", i32), ("q", vp), ("k", vp), ("v", vp), ("vlog", vp), ("vlog_stride", i32),
+    _fields_ = [("kv", AttnKvGeom), ("G", i32), ("q", vp), ("k", vp), ("v", vp), ("kv_dtype", i32), ("k_scale", vp),
+                ("k_part_tokens", i32), ("k_scale_stride", i32), ("v_scale", f32), ("vlog", vp), ("vlog_stride", i32),
                 ("softmax_scale", f32), ("beta", f32), ("eps", f32), ("top_k", i32), ("idx_out", vp),
                 ("n_kept", vp), ("scores_out", vp), ("workspace", vp), ("workspace_bytes", sz)]
 
@@ -40,7 +41,7 @@ SIGNATURES = {
     "attn_merge_lse": ([vp, vp, vp, vp, i32, i32, i32, vp, vp, vp], i32),
     "kv_quant_int8_workspace_size": ([ctypes.POINTER(AttnKvGeom), i32, ctypes.POINTER(sz)], i32),
     "kv_quant_int8": ([ctypes.POINTER(AttnKvGeom), vp, i32, i32, vp, vp, vp, sz, vp], i32),
-    "oam_value_lognorm": ([ctypes.POINTER(AttnKvGeom), vp, f32, vp, i32, vp], i32),
+    "oam_value_lognorm": ([ctypes.POINTER(AttnKvGeom), vp, i32, f32, f32, vp, i32, vp], i32),
     "oam_score_topk_workspace_size": ([ctypes.POINTER(OamTopkArgs), ctypes.POINTER(sz)], i32),
     "oam_score_topk": ([ctypes.POINTER(OamTopkArgs), vp], i32),
     "attn_status_string": ([i32], ctypes.c_char_p),

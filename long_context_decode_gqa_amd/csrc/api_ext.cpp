@@ -54,19 +54,24 @@ attn_status kv_quant_int8(const attn_kv_geom *geom, const void *x_bf16, int32_t 
   return e == hipSuccess ? ATTN_OK : api_fail_hip(e, "quantisation launch");
 }
 
-attn_status oam_value_lognorm(const attn_kv_geom *geom, const void *v_bf16, float eps, float *vlog,
-                              int32_t vlog_stride, attn_stream_t stream) {
+attn_status oam_value_lognorm(const attn_kv_geom *geom, const void *v, int32_t v_dtype, float v_scale, float eps,
+                              float *vlog, int32_t vlog_stride, attn_stream_t stream) {
   if (!geom) return api_fail(ATTN_ERR_INVALID_ARG, "geom is NULL");
-  attn_status st = api_check_geom(*geom, 2, true);
+  if (v_dtype != ATTN_BF16 && v_dtype != ATTN_I8) return api_fail(ATTN_ERR_INVALID_ARG, "v_dtype must be ATTN_BF16 or ATTN_I8");
+  const bool i8 = v_dtype == ATTN_I8;
+  attn_status st = api_check_geom(*geom, i8 ? 1 : 2, true);
   if (st != ATTN_OK) return st;
   if (geom->D != 64 && geom->D != 128 && geom->D != 256)
     return api_fail(ATTN_ERR_UNSUPPORTED, "oam_value_lognorm supports D = 64, 128 or 256");
+  if (i8 && (geom->stride_t % 16 || geom->stride_h % 16))
+    return api_fail(ATTN_ERR_INVALID_ARG, "int8 rows must be 16-byte aligned");
+  if (i8 && !(fabsf(v_scale) < INFINITY)) return api_fail(ATTN_ERR_INVALID_ARG, "v_scale must be finite");
   if (!(eps >= 0.f) || !(eps < INFINITY)) return api_fail(ATTN_ERR_INVALID_ARG, "eps must be finite and >= 0");
   if (vlog_stride < geom->max_seq_len) return api_fail(ATTN_ERR_INVALID_ARG, "vlog_stride must be >= max_seq_len");
-  if (geom->B > 0 && (!v_bf16 || !vlog)) return api_fail(ATTN_ERR_INVALID_ARG, "v_bf16 and vlog are required");
-  if (v_bf16 && (reinterpret_cast<uintptr_t>(v_bf16) & 15))
-    return api_fail(ATTN_ERR_INVALID_ARG, "v_bf16 must be 16-byte aligned");
-  hipError_t e = launch_value_lognorm(*geom, v_bf16, eps, vlog, vlog_stride, reinterpret_cast<hipStream_t>(stream));
+  if (geom->B > 0 && (!v || !vlog)) return api_fail(ATTN_ERR_INVALID_ARG, "v and vlog are required");
+  if (v && (reinterpret_cast<uintptr_t>(v) & 15)) return api_fail(ATTN_ERR_INVALID_ARG, "v must be 16-byte aligned");
+  hipError_t e = launch_value_lognorm(*geom, v, v_dtype, v_scale, eps, vlog, vlog_stride,
+                                      reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : api_fail_hip(e, "value-norm launch");
 }
 
@@ -80,16 +85,32 @@ struct OamLayout {
 
 attn_status plan_oam(const oam_topk_args *a, OamLayout *L) {
   if (!a) return api_fail(ATTN_ERR_INVALID_ARG, "args is NULL");
-  attn_status st = api_check_geom(a->kv, 2, true);
+  if (a->kv_dtype != ATTN_BF16 && a->kv_dtype != ATTN_I8)
+    return api_fail(ATTN_ERR_INVALID_ARG, "kv_dtype must be ATTN_BF16 or ATTN_I8");
+  const bool i8 = a->kv_dtype == ATTN_I8;
+  const int es = i8 ? 1 : 2;
+  attn_status st = api_check_geom(a->kv, es, true);
   if (st != ATTN_OK) return st;
   const attn_kv_geom &g = a->kv;
+  if (i8) {
+    if (g.stride_t % 16 || g.stride_h % 16) return api_fail(ATTN_ERR_INVALID_ARG, "int8 rows must be 16-byte aligned");
+    if (!a->k_scale) return api_fail(ATTN_ERR_INVALID_ARG, "int8 K needs k_scale");
+    if (a->k_part_tokens != 0) {  // 0: one per-tensor K scale
+      if (a->k_part_tokens < 16 || a->k_part_tokens % 16)
+        return api_fail(ATTN_ERR_INVALID_ARG, "k_part_tokens must be 0 or a positive multiple of 16");
+      const int64_t need = ((int64_t)g.max_seq_len + a->k_part_tokens - 1) / a->k_part_tokens;
+      if (a->k_scale_stride < need || a->k_scale_stride < 1)
+        return api_fail(ATTN_ERR_INVALID_ARG, "k_scale_stride must be >= ceil(max_seq_len / k_part_tokens)");
+    }
+    if (!(fabsf(a->v_scale) < INFINITY)) return api_fail(ATTN_ERR_INVALID_ARG, "v_scale must be finite");
+  }
   if (g.D != 64 && g.D != 128) return api_fail(ATTN_ERR_UNSUPPORTED, "oam_score_topk supports D = 64 or 128");
   if (a->G < 1 || a->G > 16) return api_fail(ATTN_ERR_UNSUPPORTED, "oam_score_topk supports 1 <= G <= 16");
   if (a->top_k < 1) return api_fail(ATTN_ERR_INVALID_ARG, "top_k must be >= 1");
   if (!(fabsf(a->softmax_scale) < INFINITY) || !(fabsf(a->beta) < INFINITY))
     return api_fail(ATTN_ERR_INVALID_ARG, "softmax_scale and beta must be finite");
   if (!(a->eps >= 0.f) || !(a->eps < INFINITY)) return api_fail(ATTN_ERR_INVALID_ARG, "eps must be finite and >= 0");
-  if (((int64_t)g.max_seq_len + 64) * g.stride_t * 2 >= (int64_t(1) << 31))
+  if (((int64_t)g.max_seq_len + 64) * g.stride_t * es >= (int64_t(1) << 31))
     return api_fail(ATTN_ERR_UNSUPPORTED, "one (sequence, KV head) may span at most 2 GiB of rows");
   if (g.B > 0) {
     if (!a->q || !a->k) return api_fail(ATTN_ERR_INVALID_ARG, "q and k are required");

@@ -203,8 +203,8 @@ hipError_t launch_quant_partitions(const attn_kv_geom &g, const void *x, int32_t
                                    int8_t *codes, float *scales, hipStream_t s);
 hipError_t launch_quant_tensor(const attn_kv_geom &g, const void *x, int8_t *codes, float *scales,
                                uint32_t *ws, hipStream_t s);
-hipError_t launch_value_lognorm(const attn_kv_geom &g, const void *v, float eps, float *vlog, int32_t stride,
-                                hipStream_t s);
+hipError_t launch_value_lognorm(const attn_kv_geom &g, const void *v, int32_t v_dtype, float v_scale, float eps,
+                                float *vlog, int32_t stride, hipStream_t s);
 hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
 hipError_t launch_read(const void *src, size_t bytes, float *sink, hipStream_t s);
 

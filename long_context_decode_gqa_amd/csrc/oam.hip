@@ -54,7 +54,10 @@ struct OamDev {
   const int32_t *seq_lens;
   const int64_t *seq_offset;
   int64_t stride_h, stride_t;
-  const uint16_t *q, *k;
+  const uint16_t *q;
+  const void *k;       // bf16 or int8 codes
+  const float *k_scale;  // int8: scale of row t is k_scale[pair*k_scale_stride + t/k_part]
+  int32_t k_part, k_scale_stride;
   const float *vlog;
   int32_t vlog_stride;
   float score_scale, beta;
@@ -132,8 +135,12 @@ __global__ __launch_bounds__(256) void zero_kernel(uint32_t *p, size_t n) {
 // split into three bf16 parts hi + mid + lo (24 significant bits) placed in
 // B-operand columns 4j, 4j+1, 4j+2 (column 4j+3 is zero), so one 16x16x32
 // MFMA chain per 16 tokens gives, in every lane quad, the three partial dot
-// products of its four tokens; two quad DPP adds finish q_bar . k_t.  Each
-// wave of the workgroup streams a quarter of its tokens in 32-token tiles.
+// products of its four tokens; two quad DPP adds finish q_bar . k_t.  For an
+// INT8 cache the same columns hold the three int8 digits of q_bar as a 22-bit
+// fixed-point integer, the int8 MFMA consumes the K codes as loaded, and the
+// quad add recombines the digit sums (weights 1, 256, 65536) before the
+// scale of q_bar and the K partition scale apply.  Each wave of the
+// workgroup streams a quarter of its tokens in 32-token tiles.
 constexpr int kScoreTok = 8192;   // tokens per workgroup of the score pass
 constexpr int kScoreBufs = 3;     // tiles in the register ring of each wave
 
@@ -144,9 +151,13 @@ __device__ __forceinline__ float quad_sum3(float v) {
   return v + a + b;
 }
 
-template <int D>
+template <int D, int KVT>
 __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
-  constexpr int KB = D / 32;
+  constexpr bool I8 = KVT == ATTN_I8;
+  constexpr int KB = I8 ? D / 64 : D / 32;  // MFMAs per 16 tokens (16x16x64 int8 or 16x16x32 bf16)
+  constexpr int ES = I8 ? 1 : 2;            // bytes per K element
+  // an int8 tile carries half the bytes of a bf16 one: more tiles in flight
+  constexpr int NBUF = I8 ? 5 : kScoreBufs;
   constexpr int kTilesPerWave = kScoreTok / 32 / 4;
   __shared__ uint32_t s_hist[kBins];
   __shared__ float s_qbar[D];
@@ -168,9 +179,36 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
     s_qbar[d] = acc / (float)o.G;
   }
   __syncthreads();
-  bf16x8_t qop[KB];
-  {
-    const int part = col & 3;  // 0: hi, 1: mid, 2: lo, 3: zero
+  typedef typename std::conditional<I8, i32x4_t, bf16x8_t>::type QOp;
+  QOp qop[KB];
+  const int part = col & 3;  // bf16: 0 hi, 1 mid, 2 lo; int8: digit plane 0, 1, 2; 3: zero
+  float qscale = 1.f;        // int8: q_bar = qscale * (fixed-point integer)
+  if constexpr (I8) {
+    // q_bar as a 22-bit fixed-point integer n = rint(q_bar / s), s = max|q_bar| / 2^22,
+    // in three balanced int8 digits n = 65536 d2 + 256 d1 + d0 (column part p holds digit p)
+    float mx = 0.f;
+    for (int d = 0; d < D; ++d) mx = fmaxf(mx, fabsf(s_qbar[d]));
+    const float inv = mx > 0.f ? 4194304.0f / mx : 0.f;
+    qscale = mx * (1.0f / 4194304.0f);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        uint32_t w = 0u;
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          const int n = (int)__builtin_rintf(s_qbar[64 * kb + 16 * cg + 4 * j4 + y] * inv);
+          const int d0 = (int)(int8_t)(n & 0xFF);
+          const int r1 = (n - d0) >> 8;
+          const int d1 = (int)(int8_t)(r1 & 0xFF);
+          const int d2 = (r1 - d1) >> 8;
+          const int dg = part == 0 ? d0 : part == 1 ? d1 : part == 2 ? d2 : 0;
+          w |= (uint32_t)(dg & 0xFF) << (8 * y);
+        }
+        qop[kb][j4] = (int)w;
+      }
+    }
+  } else {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -186,19 +224,26 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
       }
     }
   }
+  // int8: the integer digit sums recombine with weights 1, 256, 65536 in the quad add
+  const float dweight = part == 0 ? 1.f : part == 1 ? 256.f : part == 2 ? 65536.f : 0.f;
   const int64_t head_off = o.seq_offset[b] + (int64_t)kh * o.stride_h;
-  const uint32_t rs = (uint32_t)(o.stride_t * 2);
-  const int nrec = (int)((uint32_t)(L - 1) * rs + D * 2);
+  const uint32_t rs = (uint32_t)(o.stride_t * ES);
+  const int nrec = (int)((uint32_t)(L - 1) * rs + D * ES);
   const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void *)(o.k + head_off), (short)0, nrec, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)o.k + head_off * ES), (short)0, nrec, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ksrs = __builtin_amdgcn_make_buffer_rsrc(
+      I8 ? (void *)(o.k_scale + (int64_t)pair * o.k_scale_stride) : nullptr, (short)0,
+      I8 ? max(o.k_scale_stride, 1) * 4 : 0, 0x00020000);
   const float *vl = o.vlog + (int64_t)pair * o.vlog_stride;
   float *sc = o.scores + (int64_t)pair * o.L_max;
-  // the value term of the lane's four tokens is fetched with the tile (a
-  // load issued later would make the compiler wait for the prefetch too)
+  // the value term of the lane's four tokens (and an int8 tile's K scales)
+  // are fetched with the tile: a load issued later would make the compiler
+  // wait for the prefetch too
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vl, (short)0, L * 4, 0x00020000);
   struct KTile {
     u32x4_t k[2][KB];
     u32x4_t vl[2];
+    float ks[2];
   };
   // Scores are collected in LDS and written out once, in full coalesced
   // lines, when the block's tiles are done: small scattered stores between
@@ -212,6 +257,11 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) R.k[tb][kb] = __builtin_amdgcn_raw_buffer_load_b128(krs, off + 64 * kb, 0, 0);
       R.vl[tb] = __builtin_amdgcn_raw_buffer_load_b128(vrs, ((uint32_t)(t0 + 16 * tb + 4 * cg) * 4) | oob, 0, 0);
+      if constexpr (I8) {
+        // k_part is a multiple of 16, so a 16-token block has one scale
+        const uint32_t pi = (uint32_t)((t0 + 16 * tb) / o.k_part);
+        R.ks[tb] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ksrs, (4 * pi) | oob, 0, 0));
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -224,37 +274,48 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      float mult = o.score_scale;
+      if constexpr (I8) {
+        i32x4_t ai = {0, 0, 0, 0};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, R.k[tb][kb]), qop[kb], acc, 0, 0, 0);
+        for (int kb = 0; kb < KB; ++kb)
+          ai = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, R.k[tb][kb]), qop[kb], ai, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = (float)ai[i] * dweight;
+        mult = qscale * R.ks[tb] * o.score_scale;
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, R.k[tb][kb]), qop[kb], acc, 0, 0,
+                                                        0);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = quad_sum3(acc[i]);
       const float dot = jq == 0 ? acc[0] : jq == 1 ? acc[1] : jq == 2 ? acc[2] : acc[3];
       const uint32_t vw = jq == 0 ? R.vl[tb][0] : jq == 1 ? R.vl[tb][1] : jq == 2 ? R.vl[tb][2] : R.vl[tb][3];
       const int t = t0 + 16 * tb + 4 * cg + jq;
       const bool mine = valid && leader && t < L;
-      const float sv = dot * o.score_scale + o.beta * __uint_as_float(vw);
+      const float sv = dot * mult + o.beta * __uint_as_float(vw);
       if (mine) {
         s_sc[t - blk0] = sv;
         atomicAdd(&s_hist[order_key(sv) >> 21], 1u);
       }
     }
   };
-  // This wave's tiles through a ring of kScoreBufs register buffers: tile i
-  // is loaded kScoreBufs-1 tiles before it is scored.  The step count is
-  // rounded up to a multiple of the ring; the extra steps load and publish
-  // nothing.
+  // This wave's tiles through a ring of NBUF register buffers: tile i is
+  // loaded NBUF-1 tiles before it is scored.  The step count is rounded up
+  // to a multiple of the ring; the extra steps load and publish nothing.
   const int tw0 = kTilesPerWave * wave;
   const int ntw = max(0, min(kTilesPerWave, (L - blk0 - 32 * tw0 + 31) / 32));
-  const int nst = (ntw + kScoreBufs - 1) / kScoreBufs * kScoreBufs;
-  KTile buf[kScoreBufs];
+  const int nst = (ntw + NBUF - 1) / NBUF * NBUF;
+  KTile buf[NBUF];
 #pragma unroll
-  for (int j = 0; j + 1 < kScoreBufs; ++j) load(buf[j], tw0 + j, j < ntw);
-  for (int i = 0; i < nst; i += kScoreBufs) {
+  for (int j = 0; j + 1 < NBUF; ++j) load(buf[j], tw0 + j, j < ntw);
+  for (int i = 0; i < nst; i += NBUF) {
 #pragma unroll
-    for (int j = 0; j < kScoreBufs; ++j) {
-      const int ahead = i + j + kScoreBufs - 1;
-      load(buf[(j + kScoreBufs - 1) % kScoreBufs], tw0 + ahead, ahead < ntw);
+    for (int j = 0; j < NBUF; ++j) {
+      const int ahead = i + j + NBUF - 1;
+      load(buf[(j + NBUF - 1) % NBUF], tw0 + ahead, ahead < ntw);
       compute(buf[j], tw0 + i + j, i + j < ntw);
     }
   }
@@ -502,7 +563,11 @@ hipError_t launch_oam(const oam_topk_args &a, const OamPlan &plan, hipStream_t s
   o.stride_h = g.stride_h;
   o.stride_t = g.stride_t;
   o.q = (const uint16_t *)a.q;
-  o.k = (const uint16_t *)a.k;
+  o.k = a.k;
+  // a per-tensor K scale is one partition longer than any sequence
+  o.k_scale = a.k_scale;
+  o.k_part = a.k_part_tokens > 0 ? a.k_part_tokens : (1 << 30);
+  o.k_scale_stride = a.k_part_tokens > 0 ? a.k_scale_stride : 0;
   o.vlog = plan.vlog;
   o.vlog_stride = plan.vlog_stride;
   o.L_max = plan.score_stride;
@@ -528,12 +593,17 @@ hipError_t launch_oam(const oam_topk_args &a, const OamPlan &plan, hipStream_t s
                        s, plan.hist, nz);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (!a.vlog) {
-      e = launch_value_lognorm(g, a.v, a.eps, plan.vlog, plan.vlog_stride, s);
+      e = launch_value_lognorm(g, a.v, a.kv_dtype, a.v_scale, a.eps, plan.vlog, plan.vlog_stride, s);
       if (e != hipSuccess) return e;
     }
     dim3 sgrid((g.max_seq_len + kScoreTok - 1) / kScoreTok, npairs), blk(256);
-    if (g.D == 128) hipLaunchKernelGGL((oam_score_kernel<128>), sgrid, blk, 0, s, o);
-    else hipLaunchKernelGGL((oam_score_kernel<64>), sgrid, blk, 0, s, o);
+    if (a.kv_dtype == ATTN_I8) {
+      if (g.D == 128) hipLaunchKernelGGL((oam_score_kernel<128, ATTN_I8>), sgrid, blk, 0, s, o);
+      else hipLaunchKernelGGL((oam_score_kernel<64, ATTN_I8>), sgrid, blk, 0, s, o);
+    } else {
+      if (g.D == 128) hipLaunchKernelGGL((oam_score_kernel<128, ATTN_BF16>), sgrid, blk, 0, s, o);
+      else hipLaunchKernelGGL((oam_score_kernel<64, ATTN_BF16>), sgrid, blk, 0, s, o);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(oam_candidate_kernel, dim3(nblk, npairs), blk, 0, s, o);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -128,11 +128,14 @@ __global__ __launch_bounds__(256) void tensor_codes_kernel(attn_kv_geom g, const
   }
 }
 
-// ln(||v_t||_2 + eps): D/8 lanes per row, one 16-byte chunk each, fp32 sums.
-template <int LPR>
-__global__ __launch_bounds__(256) void value_lognorm_kernel(attn_kv_geom g, const uint16_t *v, float eps, float *out,
-                                                            int32_t stride) {
+// ln(||v_t||_2 + eps): one 16-byte chunk per lane (8 bf16 or 16 int8 values),
+// LPR lanes per row, fp32 sums.  An int8 row's norm is v_scale * ||codes||
+// (the integer sum of squares is exact).
+template <int LPR, bool I8>
+__global__ __launch_bounds__(256) void value_lognorm_kernel(attn_kv_geom g, const void *v, float v_scale, float eps,
+                                                            float *out, int32_t stride) {
   constexpr int RPB = 256 / LPR;
+  constexpr int EPC = I8 ? 16 : 8;  // elements per lane chunk
   const int pair = blockIdx.y;
   const int b = pair / g.KH, kh = pair - b * g.KH;
   const int L = min(max(g.seq_lens[b], 0), g.max_seq_len);
@@ -140,16 +143,30 @@ __global__ __launch_bounds__(256) void value_lognorm_kernel(attn_kv_geom g, cons
   const int c = threadIdx.x % LPR;
   float ss = 0.f;
   if (t < L) {
-    const u32x4_t w = *(const u32x4_t *)(v + g.seq_offset[b] + (int64_t)kh * g.stride_h + (int64_t)t * g.stride_t + 8 * c);
+    const int64_t e0 = g.seq_offset[b] + (int64_t)kh * g.stride_h + (int64_t)t * g.stride_t + EPC * c;
+    if constexpr (I8) {
+      const u32x4_t w = *(const u32x4_t *)((const int8_t *)v + e0);
+      int acc = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float a = bf16_lo(w[e]), h = bf16_hi(w[e]);
-      ss += a * a + h * h;
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          const int x = (int)(int8_t)(w[e] >> (8 * y));
+          acc += x * x;
+        }
+      ss = (float)acc;
+    } else {
+      const u32x4_t w = *(const u32x4_t *)((const uint16_t *)v + e0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = bf16_lo(w[e]), h = bf16_hi(w[e]);
+        ss += a * a + h * h;
+      }
     }
   }
 #pragma unroll
   for (int o = LPR / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-  if (t < L && c == 0) out[(int64_t)pair * stride + t] = logf(sqrtf(ss) + eps);
+  if (t < L && c == 0) out[(int64_t)pair * stride + t] = logf((I8 ? v_scale * sqrtf(ss) : sqrtf(ss)) + eps);
 }
 
 }  // namespace
@@ -183,16 +200,24 @@ hipError_t launch_quant_tensor(const attn_kv_geom &g, const void *x, int8_t *cod
   return hipGetLastError();
 }
 
-hipError_t launch_value_lognorm(const attn_kv_geom &g, const void *v, float eps, float *vlog, int32_t stride,
-                                hipStream_t s) {
+hipError_t launch_value_lognorm(const attn_kv_geom &g, const void *v, int32_t v_dtype, float v_scale, float eps,
+                                float *vlog, int32_t stride, hipStream_t s) {
   if (g.B == 0 || g.max_seq_len == 0) return hipSuccess;
-  const int lpr = g.D / 8;
+  const bool i8 = v_dtype == ATTN_I8;
+  const int lpr = g.D / (i8 ? 16 : 8);
   const int rpb = 256 / lpr;
-  dim3 grid((g.max_seq_len + rpb - 1) / rpb, g.B * g.KH);
-  if (lpr == 8) hipLaunchKernelGGL((value_lognorm_kernel<8>), grid, dim3(256), 0, s, g, (const uint16_t *)v, eps, vlog, stride);
-  else if (lpr == 16) hipLaunchKernelGGL((value_lognorm_kernel<16>), grid, dim3(256), 0, s, g, (const uint16_t *)v, eps, vlog, stride);
-  else if (lpr == 32) hipLaunchKernelGGL((value_lognorm_kernel<32>), grid, dim3(256), 0, s, g, (const uint16_t *)v, eps, vlog, stride);
-  else return hipErrorInvalidValue;
+  dim3 grid((g.max_seq_len + rpb - 1) / rpb, g.B * g.KH), blk(256);
+  if (i8) {
+    if (lpr == 4) hipLaunchKernelGGL((value_lognorm_kernel<4, true>), grid, blk, 0, s, g, v, v_scale, eps, vlog, stride);
+    else if (lpr == 8) hipLaunchKernelGGL((value_lognorm_kernel<8, true>), grid, blk, 0, s, g, v, v_scale, eps, vlog, stride);
+    else if (lpr == 16) hipLaunchKernelGGL((value_lognorm_kernel<16, true>), grid, blk, 0, s, g, v, v_scale, eps, vlog, stride);
+    else return hipErrorInvalidValue;
+  } else {
+    if (lpr == 8) hipLaunchKernelGGL((value_lognorm_kernel<8, false>), grid, blk, 0, s, g, v, v_scale, eps, vlog, stride);
+    else if (lpr == 16) hipLaunchKernelGGL((value_lognorm_kernel<16, false>), grid, blk, 0, s, g, v, v_scale, eps, vlog, stride);
+    else if (lpr == 32) hipLaunchKernelGGL((value_lognorm_kernel<32, false>), grid, blk, 0, s, g, v, v_scale, eps, vlog, stride);
+    else return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

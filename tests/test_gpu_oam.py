@@ -187,3 +187,104 @@ def test_oam_tie_group_cut_at_threshold():
         assert nk == top_k
         np.testing.assert_array_equal(idx[:nk], exact_topk(vl, top_k))
         assert np.all(idx[nk:] == -1)
+
+
+# --- the page's §7 stack: OAM over an INT8 cache, then INT8 attention over the kept tokens ---
+
+
+def quant_cache(k, v, g, part):
+    """Library INT8 codes (bit-exact against the oracle's, tested elsewhere) of K per partition or
+    per tensor (part 0) and V per tensor; returns host and device copies plus the oracle's scale args."""
+    geom = dev_geom(g)
+    kc, ks = pkg.kv_quant_int8(to_dev(k), geom, part)
+    vc, vs = pkg.kv_quant_int8(to_dev(v), geom, 0)
+    torch.cuda.synchronize()
+    if part:
+        stride = -(-int(g.max_len) // part)
+        kk = dict(k_scale=ks.cpu().numpy(), k_part=part, k_scale_stride=stride)
+    else:
+        kk = dict(k_scale=np.full(g.B * g.KH, ks.cpu().numpy()[0], np.float32), k_part=1 << 30, k_scale_stride=1)
+    return kc, ks, vc, float(vs.item()), kk
+
+
+def run_oam_int8(w, q, g, kc, ks, vc, vs, part, top_k, use_vlog):
+    qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
+    geom = dev_geom(g)
+    scores = torch.full((w.B * w.KH, max(1, geom.max_seq_len)), float("nan"), dtype=torch.float32, device=DEV)
+    kw = dict(scores_out=scores, k_scale=ks, k_part_tokens=part, v_scale=vs)
+    if use_vlog:
+        kw["vlog"] = pkg.oam_value_lognorm(vc, geom, 1e-6, v_scale=vs)
+    else:
+        kw["v"] = vc
+    idx, nk = pkg.oam_score_topk(qd, kc, geom, w.G, top_k, **kw)
+    torch.cuda.synchronize()
+    return idx, nk, scores.cpu().numpy()
+
+
+@pytest.mark.parametrize("D,G,top_k,part,use_vlog", [(128, 8, 100, 64, False), (64, 4, 7, 128, True),
+                                                     (128, 16, 333, 0, True), (128, 1, 5000, 64, True)])
+def test_oam_int8_cache_against_oracle(D, G, top_k, part, use_vlog):
+    lens = np.array([1, 700, 4096, 5000, 0, 2049], np.int32)
+    w = synth.workload("oam_128k", B=len(lens), KH=2, G=G, D=D, lens=lens, layout="token_major", seed=90 + G)
+    q, k, v, g = synth.generate(w)
+    log_case(f"oam int8 cache D={D} G={G} K={top_k} part={part} vlog={use_vlog}")
+    kc, ks, vc, vs, kk = quant_cache(k, v, g, part)
+    idx, nk, sc = run_oam_int8(w, q, g, kc, ks, vc, vs, part, top_k, use_vlog)
+    idx, nk = idx.cpu().numpy(), nk.cpu().numpy()
+    p = problem(w, q, kc.cpu().numpy(), vc.cpu().numpy(), g, v_scale=vs, **kk)
+    for b in range(w.B):
+        for kh in range(w.KH):
+            pr = b * w.KH + kh
+            check_pair(oracle.oam_scores(p, b, kh, 1.0, 1e-6), sc[pr], idx[pr], nk[pr], top_k)
+
+
+@pytest.mark.parametrize("q_quant", [pkg.QUANT_EXACT, pkg.QUANT_ROW])
+def test_oam_int8_stack_feeds_int8_attention(q_quant):
+    lens = np.array([6000, 2500, 300], np.int32)
+    w = synth.workload("oam_128k", B=3, KH=2, lens=lens, layout="token_major", seed=98)
+    q, k, v, g = synth.generate(w)
+    top_k = 512
+    log_case(f"oam int8 -> indexed int8 decode q_quant={q_quant}")
+    kc, ks, vc, vs, kk = quant_cache(k, v, g, 64)
+    idx, nk, _ = run_oam_int8(w, q, g, kc, ks, vc, vs, 64, top_k, True)
+    qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
+    out, _ = pkg.attn_decode_splitkv(qd, kc, vc, dev_geom(g), w.G, token_idx=idx, n_idx=nk, k_scale=ks,
+                                     k_part_tokens=64, v_scale=vs, q_quant=q_quant, split_tokens=0)
+    torch.cuda.synchronize()
+    qq = {}
+    if q_quant == pkg.QUANT_ROW:
+        qc, qs = oracle.quant_rows(q.reshape(w.B * w.QH, w.D))
+        q_in, qq = qc.reshape(q.shape), dict(q_scale=qs)
+    else:
+        q_in = q
+    p = problem(w, q_in, kc.cpu().numpy(), vc.cpu().numpy(), g, v_scale=vs,
+                tok_idx=idx.cpu().numpy().reshape(-1), n_idx=nk.cpu().numpy(), idx_stride=top_k, **kk, **qq)
+    ref, _ = oracle.attention_rows(p, oracle.all_rows(p), nthreads=8)
+    assert np.abs(out.cpu().numpy().reshape(-1, w.D) - ref).max() <= 2e-3
+
+
+def test_oam_int8_128k_full_size_sampled_pairs():
+    """The 128K OAM workload (4 x 8 KV heads x 131072 tokens, top 4096) on an INT8 cache (64-token K
+    partitions, per-tensor V), in the benchmark's configuration: scores and kept sets of sampled
+    (b, kh) pairs against the oracle, then INT8 attention over the kept tokens on sampled rows."""
+    w = synth.workload("oam_128k")
+    q, k, v, g = synth.generate(w)
+    log_case("oam int8 128k full size")
+    kc, ks, vc, vs, kk = quant_cache(k, v, g, 64)
+    del k, v
+    idx, nk, sc = run_oam_int8(w, q, g, kc, ks, vc, vs, 64, w.top_k, True)
+    qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
+    out, _ = pkg.attn_decode_splitkv(qd, kc, vc, dev_geom(g), w.G, token_idx=idx, n_idx=nk, k_scale=ks,
+                                     k_part_tokens=64, v_scale=vs, split_tokens=w.split_tokens)
+    torch.cuda.synchronize()
+    idx_h, nk_h = idx.cpu().numpy(), nk.cpu().numpy()
+    p = problem(w, q, kc.cpu().numpy(), vc.cpu().numpy(), g, v_scale=vs, **kk)
+    for b, kh in ((0, 0), (3, 7), (2, 5)):
+        pr = b * w.KH + kh
+        check_pair(oracle.oam_scores(p, b, kh, w.beta, w.eps), sc[pr], idx_h[pr], nk_h[pr], w.top_k)
+    pk = problem(w, q, kc.cpu().numpy(), vc.cpu().numpy(), g, v_scale=vs, tok_idx=idx_h.reshape(-1), n_idx=nk_h,
+                 idx_stride=w.top_k, **kk)
+    rows = [(0, 0), (3, 63), (2, 41), (1, 17)]
+    ref, _ = oracle.attention_rows(pk, rows, nthreads=16)
+    got = out.cpu().numpy().reshape(w.B * w.QH, w.D)[[b * w.QH + h for b, h in rows]]
+    assert np.abs(got - ref).max() <= 2e-3
