@@ -370,6 +370,15 @@ __device__ void select_threshold(const OamDev &o, int pair, int n, int b0, int n
   __syncthreads();
   const uint32_t T = (prefix << 10) | (uint32_t)select_bin(s_hist, 1024, need, &above, s_tmp, s_res);
   need -= above;
+  // When every key equal to T is kept (the usual case: T is a single key),
+  // the index passes are not needed.
+  const int n_eq = (int)s_hist[T & 0x3FFu];
+  if (need == n_eq) {
+    *T_out = T;
+    *I_out = 0x7FFFFFFF;
+    return;
+  }
+  __syncthreads();  // every thread has read n_eq before the histogram is cleared
   // among keys equal to T, the need-th smallest index: digits of 11 and 10
   // bits of the index, bins reversed so "largest bin" means smallest index
   for (int i = tid; i < kBins; i += 256) s_hist[i] = 0u;
@@ -406,7 +415,24 @@ __global__ __launch_bounds__(256) void oam_candidate_kernel(OamDev o) {
   const int blk0 = blockIdx.x * kBlockTok;
   if (blk0 >= L || o.top_k >= L) return;  // top_k >= L: every token is kept
   const int tid = threadIdx.x;
-  for (int i = tid; i < kBins; i += 256) s_hist[i] = o.hist[(size_t)pair * kBins + i];
+  // The histogram loads go first, then the block's scores, which do not
+  // depend on b0: loads complete in order, so the bin search waits for the
+  // histogram only and the score loads' latency overlaps it.
+  const float *sc = o.scores + (int64_t)pair * o.L_max;
+  const int n = min(kBlockTok, L - blk0);
+  uint32_t hv[kBins / 256];
+#pragma unroll
+  for (int j = 0; j < kBins / 256; ++j) hv[j] = o.hist[(size_t)pair * kBins + tid + 256 * j];
+  // unconditional buffer loads (past n they read zero), so the wait for the
+  // histogram can leave all eight in flight
+  const __amdgpu_buffer_rsrc_t srs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(sc + blk0), (short)0, n * 4, 0x00020000);
+  float sv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    sv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(srs, (uint32_t)(tid + 256 * j) * 4u, 0, 0));
+#pragma unroll
+  for (int j = 0; j < kBins / 256; ++j) s_hist[tid + 256 * j] = hv[j];
   __syncthreads();
   int above;
   const int b0 = select_bin(s_hist, kBins, o.top_k, &above, s_tmp, s_res);
@@ -414,14 +440,12 @@ __global__ __launch_bounds__(256) void oam_candidate_kernel(OamDev o) {
     o.state[pair].b0 = b0;
     o.state[pair].need = o.top_k - above;
   }
-  const float *sc = o.scores + (int64_t)pair * o.L_max;
-  const int n = min(kBlockTok, L - blk0);
   uint32_t keys[8];
   int gt = 0, nc = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int i = tid + 256 * j;
-    keys[j] = i < n ? order_key(sc[blk0 + i]) : 0u;
+    keys[j] = i < n ? order_key(sv[j]) : 0u;
     const int d = (int)(keys[j] >> 21);
     gt += i < n && d > b0;
     nc += i < n && d == b0;
@@ -589,7 +613,7 @@ hipError_t launch_oam(const oam_topk_args &a, const OamPlan &plan, hipStream_t s
   if (nblk > 0) {
     // histogram and counters start at zero (a fill kernel, not a memset)
     const size_t nz = (size_t)npairs * (kBins + 4);
-    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((nz + 255) / 256 < 4096 ? (nz + 255) / 256 : 4096)), dim3(256), 0,
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((nz + 255) / 256 < 128 ? (nz + 255) / 256 : 128)), dim3(256), 0,
                        s, plan.hist, nz);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (!a.vlog) {
