@@ -80,7 +80,7 @@ attn_status oam_value_lognorm(const attn_kv_geom *geom, const void *v, int32_t v
 namespace {
 
 struct OamLayout {
-  size_t scores, vlog, hist, state, blk_gt, blk_off, cand_key, cand_idx, total;
+  size_t scores, vlog, hist, state, blk_gt, blk_off, blk_nc, cand_key, cand_idx, total;
 };
 
 attn_status plan_oam(const oam_topk_args *a, OamLayout *L) {
@@ -131,12 +131,13 @@ attn_status plan_oam(const oam_topk_args *a, OamLayout *L) {
   L->scores = off; off = al(off + (a->scores_out ? 0 : npairs * stride * sizeof(float)));
   L->vlog = off; off = al(off + (a->vlog ? 0 : npairs * stride * sizeof(float)));
   const size_t nblk_max = (size_t)oam_max_tokens() / 2048;
-  L->hist = off; off = al(off + (size_t)npairs * (2048 + 4) * sizeof(uint32_t));  // histogram, then counters
+  L->hist = off; off = al(off + (size_t)npairs * 2048 * sizeof(uint32_t));
   L->state = off; off = al(off + (size_t)npairs * 8 * sizeof(int32_t));
   L->blk_gt = off; off = al(off + (size_t)npairs * nblk_max * sizeof(int32_t));
   L->blk_off = off; off = al(off + (size_t)npairs * nblk_max * sizeof(int32_t));
-  L->cand_key = off; off = al(off + (size_t)npairs * 4096 * sizeof(uint32_t));
-  L->cand_idx = off; off = al(off + (size_t)npairs * 4096 * sizeof(int32_t));
+  L->blk_nc = off; off = al(off + (size_t)npairs * nblk_max * sizeof(int32_t));
+  L->cand_key = off; off = al(off + (size_t)npairs * stride * sizeof(uint32_t));
+  L->cand_idx = off; off = al(off + (size_t)npairs * stride * sizeof(int32_t));
   L->total = off;
   return ATTN_OK;
 }
@@ -169,7 +170,7 @@ attn_status oam_score_topk(const oam_topk_args *a, attn_stream_t stream) {
   plan.vlog = a->vlog ? const_cast<float *>(a->vlog) : reinterpret_cast<float *>(ws + L.vlog);
   plan.vlog_stride = a->vlog ? a->vlog_stride : a->kv.max_seq_len;
   plan.hist = reinterpret_cast<uint32_t *>(ws + L.hist);
-  plan.counters = plan.hist + (size_t)a->kv.B * a->kv.KH * 2048;
+  plan.blk_nc = reinterpret_cast<int32_t *>(ws + L.blk_nc);
   plan.state = reinterpret_cast<int32_t *>(ws + L.state);
   plan.blk_gt = reinterpret_cast<int32_t *>(ws + L.blk_gt);
   plan.blk_off = reinterpret_cast<int32_t *>(ws + L.blk_off);

@@ -214,12 +214,12 @@ struct OamPlan {
   float *vlog;           // value log-norms: the caller's or computed into the workspace
   int32_t vlog_stride;
   uint32_t *hist;        // [npairs][2048] level-0 key histogram, followed by
-  uint32_t *counters;    // [npairs][4] (zeroed together with hist)
   int32_t *state;        // [npairs][8] selection state
   int32_t *blk_gt;       // [npairs][oam_max_tokens() / 2048]
   int32_t *blk_off;      // [npairs][oam_max_tokens() / 2048]
-  uint32_t *cand_key;    // [npairs][4096]
-  int32_t *cand_idx;     // [npairs][4096]
+  int32_t *blk_nc;       // [npairs][1024] candidates per block
+  uint32_t *cand_key;    // [npairs][score_stride] per-block candidate regions
+  int32_t *cand_idx;     // [npairs][score_stride]
 };
 hipError_t launch_oam(const oam_topk_args &a, const OamPlan &plan, hipStream_t s);
 int oam_max_tokens();  // longest sequence oam_score_topk selects over

@@ -13,18 +13,18 @@
 //              count the top 11 key bits into the pair's level-0 histogram.
 //   candidates (2048-token blocks x pairs) every block reads the pair's
 //              histogram and finds the threshold's top digit b0 (all blocks
-//              find the same); it counts its keys above bin b0 and appends its
-//              keys of bin b0 to the pair's candidate list.
-//   select     (one workgroup per pair) among the candidates, the exact
-//              threshold key T and the last kept index I_T among keys equal
-//              to T; then the output offset of every block.  (If the list
-//              overflowed - many equal scores - it selects over the pair's
-//              scores directly.)
+//              find the same); it counts its keys above bin b0 and writes its
+//              keys of bin b0, with their indices, to its own region of the
+//              pair's candidate array, and their count.
+//   select     (one workgroup per pair) gathers the candidates into LDS, then
+//              finds the exact threshold key T and the last kept index I_T
+//              among keys equal to T; then the output offset of every block.
+//              (If there are more candidates than LDS holds - many equal
+//              scores - it selects over the pair's scores directly.)
 //   write      (2048-token blocks x pairs) ordered compaction of the kept
 //              tokens, key > T or (key == T and index <= I_T), at the block's
 //              offset, so idx_out is ascending.
-// Only integer atomics (histogram counts, list positions) cross workgroups
-// within a pass.
+// Only integer atomics (histogram counts) cross workgroups within a pass.
 #include "common.hpp"
 
 namespace lcdg {
@@ -32,7 +32,7 @@ namespace {
 
 constexpr int kBins = 2048;       // 11-bit digits (the 10-bit ones use 1024)
 constexpr int kBlockTok = 2048;   // tokens per workgroup of the candidate and write passes
-constexpr int kCandCap = 4096;    // candidate list capacity per pair
+constexpr int kCandCap = 4096;    // candidates the select pass holds in LDS
 constexpr int kMaxBlocks = 1024;  // blocks of kBlockTok per pair (sequences up to 2M tokens)
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -63,12 +63,12 @@ struct OamDev {
   float score_scale, beta;
   float *scores;       // [npairs][L_max]
   uint32_t *hist;      // [npairs][kBins]  level-0 histogram
-  uint32_t *counters;  // [npairs][4]  [2]: candidates appended
   OamState *state;     // [npairs]
   int32_t *blk_gt;     // [npairs][kMaxBlocks]  keys above bin b0 per block
   int32_t *blk_off;    // [npairs][kMaxBlocks]  first output slot per block
-  uint32_t *cand_key;  // [npairs][kCandCap]
-  int32_t *cand_idx;   // [npairs][kCandCap]
+  int32_t *blk_nc;     // [npairs][kMaxBlocks]  candidates (keys in bin b0) per block
+  uint32_t *cand_key;  // [npairs][L_max]  block j's candidates at [j*kBlockTok, + blk_nc)
+  int32_t *cand_idx;   // [npairs][L_max]
   int32_t *idx_out;    // [npairs][top_k]
   int32_t *n_kept;     // [npairs]
 };
@@ -332,11 +332,10 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
 // to T, the need'-th smallest index I_T (need' = how many of them are kept).
 // Items come from the candidate list or, if it overflowed, from all scores.
 template <bool FROM_LIST>
-__device__ void select_threshold(const OamDev &o, int pair, int n, int b0, int need, uint32_t *s_hist, int *s_tmp,
-                                 int *s_res, uint32_t *T_out, int *I_out) {
+__device__ void select_threshold(const OamDev &o, int pair, int n, int b0, int need, const uint32_t *ck,
+                                 const int32_t *ci, uint32_t *s_hist, int *s_tmp, int *s_res, uint32_t *T_out,
+                                 int *I_out) {
   const int tid = threadIdx.x;
-  const uint32_t *ck = o.cand_key + (size_t)pair * kCandCap;
-  const int32_t *ci = o.cand_idx + (size_t)pair * kCandCap;
   const float *sc = o.scores + (int64_t)pair * o.L_max;
   auto item = [&](int i, uint32_t &key, int &idx) {
     if constexpr (FROM_LIST) {
@@ -409,7 +408,7 @@ __device__ void select_threshold(const OamDev &o, int pair, int n, int b0, int n
 // list.  Block 0 records b0 and how many keys of bin b0 are kept.
 __global__ __launch_bounds__(256) void oam_candidate_kernel(OamDev o) {
   __shared__ uint32_t s_hist[kBins];
-  __shared__ int s_tmp[4], s_res[2], s_base;
+  __shared__ int s_tmp[4], s_res[2];
   const int pair = blockIdx.y;
   const int L = pair_len(o, pair);
   const int blk0 = blockIdx.x * kBlockTok;
@@ -452,21 +451,20 @@ __global__ __launch_bounds__(256) void oam_candidate_kernel(OamDev o) {
   }
   int tg, tc;
   block_exclusive_scan(gt, s_tmp, &tg);
-  const int cpos = block_exclusive_scan(nc, s_tmp, &tc);
+  int pos = block_exclusive_scan(nc, s_tmp, &tc);
   if (tid == 0) {
     o.blk_gt[(size_t)pair * kMaxBlocks + blockIdx.x] = tg;
-    s_base = tc ? (int)atomicAdd(o.counters + 4 * pair + 2, (uint32_t)tc) : 0;
+    o.blk_nc[(size_t)pair * kMaxBlocks + blockIdx.x] = tc;
   }
-  __syncthreads();
-  int pos = s_base + cpos;
+  // this block's region of the candidate array: its own token range
+  uint32_t *ck = o.cand_key + (int64_t)pair * o.L_max + blk0;
+  int32_t *ci = o.cand_idx + (int64_t)pair * o.L_max + blk0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int i = tid + 256 * j;
     if (i < n && (int)(keys[j] >> 21) == b0) {
-      if (pos < kCandCap) {
-        o.cand_key[(size_t)pair * kCandCap + pos] = keys[j];
-        o.cand_idx[(size_t)pair * kCandCap + pos] = blk0 + i;
-      }
+      ck[pos] = keys[j];
+      ci[pos] = blk0 + i;
       ++pos;
     }
   }
@@ -477,28 +475,78 @@ __global__ __launch_bounds__(256) void oam_candidate_kernel(OamDev o) {
 __global__ __launch_bounds__(256) void oam_select_kernel(OamDev o) {
   __shared__ uint32_t s_hist[kBins];
   __shared__ int s_kept[kMaxBlocks];
+  __shared__ int s_pre[kMaxBlocks + 1];
+  __shared__ uint32_t s_ck[kCandCap];
+  __shared__ int32_t s_ci[kCandCap];
+  __shared__ uint16_t s_own[kCandCap];  // block of each gathered candidate
   __shared__ int s_tmp[4], s_res[2];
   const int pair = blockIdx.x;
   const int L = pair_len(o, pair);
   if (L == 0 || o.top_k >= L) return;
   const int tid = threadIdx.x;
   const int b0 = o.state[pair].b0, need = o.state[pair].need;
-  const int C = (int)o.counters[4 * pair + 2];
-  const float *sc = o.scores + (int64_t)pair * o.L_max;
+  const int nblk = (L + kBlockTok - 1) / kBlockTok;
+  // where each block's candidates start in the gathered list
+  int C = 0;
+  for (int j0 = 0; j0 < nblk; j0 += 256) {
+    const int j = j0 + tid;
+    const int v = j < nblk ? o.blk_nc[(size_t)pair * kMaxBlocks + j] : 0;
+    int tot;
+    const int ex = block_exclusive_scan(v, s_tmp, &tot);
+    if (j < nblk) s_pre[j] = C + ex;
+    C += tot;
+  }
+  if (tid == 0) s_pre[nblk] = C;
+  __syncthreads();
   uint32_t T;
   int I_T;
-  if (C <= kCandCap) select_threshold<true>(o, pair, C, b0, need, s_hist, s_tmp, s_res, &T, &I_T);
-  else select_threshold<false>(o, pair, L, b0, need, s_hist, s_tmp, s_res, &T, &I_T);
-  const int nblk = (L + kBlockTok - 1) / kBlockTok;
+  const bool in_lds = C > 0 && C <= kCandCap;
+  if (in_lds) {
+    // Gather into LDS: item i lies in the block j with s_pre[j] <= i < s_pre[j+1].
+    constexpr int kPer = kCandCap / 256;
+    const uint32_t *gk = o.cand_key + (int64_t)pair * o.L_max;
+    const int32_t *gi = o.cand_idx + (int64_t)pair * o.L_max;
+    // Owner map first (LDS only): wave w writes block j's number over its
+    // items, for blocks j = w, w+4, ...  Then each item costs two LDS reads
+    // before its loads, and all of a thread's loads are in flight together
+    // (clamped to the last item, so they are unconditional).
+    const int wave = tid >> 6, lane = tid & 63;
+    for (int j = wave; j < nblk; j += 4)
+      for (int l = s_pre[j] + lane; l < s_pre[j + 1]; l += 64) s_own[l] = (uint16_t)j;
+    __syncthreads();
+    uint32_t kr[kPer];
+    int32_t ir[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int i = min(tid + 256 * r, C - 1);
+      const int j = s_own[i];
+      const int64_t src = (int64_t)j * kBlockTok + (i - s_pre[j]);
+      kr[r] = gk[src];
+      ir[r] = gi[src];
+    }
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int i = tid + 256 * r;
+      if (i < C) {
+        s_ck[i] = kr[r];
+        s_ci[i] = ir[r];
+      }
+    }
+    __syncthreads();
+    select_threshold<true>(o, pair, C, b0, need, s_ck, s_ci, s_hist, s_tmp, s_res, &T, &I_T);
+  } else {
+    select_threshold<false>(o, pair, L, b0, need, nullptr, nullptr, s_hist, s_tmp, s_res, &T, &I_T);
+  }
   for (int j = tid; j < nblk; j += 256) s_kept[j] = 0;
   __syncthreads();
-  const int nitems = C <= kCandCap ? C : L;
+  const float *sc = o.scores + (int64_t)pair * o.L_max;
+  const int nitems = in_lds ? C : L;
   for (int i = tid; i < nitems; i += 256) {
     uint32_t key;
     int idx;
-    if (C <= kCandCap) {
-      key = o.cand_key[(size_t)pair * kCandCap + i];
-      idx = o.cand_idx[(size_t)pair * kCandCap + i];
+    if (in_lds) {
+      key = s_ck[i];
+      idx = s_ci[i];
     } else {
       key = order_key(sc[i]);
       idx = i;
@@ -544,14 +592,24 @@ __global__ __launch_bounds__(256) void oam_write_kernel(OamDev o) {
     for (int i = tid; i < n; i += 256) out[blk0 + i] = blk0 + i;
     return;
   }
+  // the threshold and this block's offset are read first, then the scores
+  // with unconditional buffer loads (past n they read zero), all in flight
+  // together
+  const uint32_t T = o.state[pair].T;
+  const int I_T = o.state[pair].I_T;
+  const int off0 = o.blk_off[(size_t)pair * kMaxBlocks + blockIdx.x];
+  const __amdgpu_buffer_rsrc_t srs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(sc + blk0), (short)0, n * 4, 0x00020000);
+  float sv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    sv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(srs, (uint32_t)(tid + 256 * j) * 4u, 0, 0));
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int r = tid + 256 * j;
-    s_key[r + (r >> 3)] = r < n ? order_key(sc[blk0 + r]) : 0u;
+    s_key[r + (r >> 3)] = order_key(sv[j]);
   }
   __syncthreads();
-  const uint32_t T = o.state[pair].T;
-  const int I_T = o.state[pair].I_T;
   bool keep[8];
   int kc = 0;
 #pragma unroll
@@ -562,7 +620,7 @@ __global__ __launch_bounds__(256) void oam_write_kernel(OamDev o) {
     kc += keep[j];
   }
   int tot;
-  int pos = o.blk_off[(size_t)pair * kMaxBlocks + blockIdx.x] + block_exclusive_scan(kc, s_tmp, &tot);
+  int pos = off0 + block_exclusive_scan(kc, s_tmp, &tot);
 #pragma unroll
   for (int j = 0; j < 8; ++j)
     if (keep[j]) out[pos++] = blk0 + 8 * tid + j;
@@ -599,7 +657,7 @@ hipError_t launch_oam(const oam_topk_args &a, const OamPlan &plan, hipStream_t s
   o.beta = a.beta;
   o.scores = plan.scores;
   o.hist = plan.hist;
-  o.counters = plan.counters;
+  o.blk_nc = plan.blk_nc;
   o.state = reinterpret_cast<OamState *>(plan.state);
   o.blk_gt = plan.blk_gt;
   o.blk_off = plan.blk_off;
@@ -611,8 +669,8 @@ hipError_t launch_oam(const oam_topk_args &a, const OamPlan &plan, hipStream_t s
   hipError_t e;
   const int nblk = (g.max_seq_len + kBlockTok - 1) / kBlockTok;
   if (nblk > 0) {
-    // histogram and counters start at zero (a fill kernel, not a memset)
-    const size_t nz = (size_t)npairs * (kBins + 4);
+    // the histogram starts at zero (a fill kernel, not a memset)
+    const size_t nz = (size_t)npairs * kBins;
     hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((nz + 255) / 256 < 128 ? (nz + 255) / 256 : 128)), dim3(256), 0,
                        s, plan.hist, nz);
     if ((e = hipGetLastError()) != hipSuccess) return e;
