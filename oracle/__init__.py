@@ -71,6 +71,8 @@ def lib():
         L.oracle_topk_sort.restype = i32
         L.oracle_topk_select.argtypes = [vp, i32, i32, vp]
         L.oracle_topk_select.restype = i32
+        L.oracle_block_select.argtypes = [P, i32, i32, i32, i32, f64, f64, vp, vp]
+        L.oracle_block_select.restype = i32
         _lib = L
     return _lib
 
@@ -277,3 +279,17 @@ def topk_select(scores: np.ndarray, k: int) -> np.ndarray:
     if n < 0:
         raise ValueError("oracle_topk_select: invalid arguments")
     return idx[:n].copy()
+
+
+def block_select(p: Problem, b: int, kh: int, block_tokens: int, n_blocks: int, beta: float = 0.0,
+                 eps: float = 1e-6):
+    """Block-granular top-n selection -> (kept token indices ascending, block scores)."""
+    L = int(p.lens[b])
+    idx = np.zeros(max(1, L), dtype=np.int32)
+    bs = np.zeros(max(1, -(-L // block_tokens)), dtype=np.float64)
+    s = p._struct()
+    n = lib().oracle_block_select(ctypes.byref(s), b, kh, block_tokens, n_blocks, float(beta), float(eps),
+                                  _ptr(idx), _ptr(bs))
+    if n < 0:
+        raise ValueError("oracle_block_select: invalid arguments")
+    return idx[:n].copy(), bs[:-(-L // block_tokens)].copy()

@@ -369,6 +369,31 @@ int32_t oracle_topk_sort(const double *scores, int32_t L, int32_t k, int32_t *id
   return n;
 }
 
+int32_t oracle_block_select(const oracle_problem *p, int32_t b, int32_t kh, int32_t block_tokens, int32_t n_blocks,
+                            double beta, double eps, int32_t *idx_out, double *block_scores) {
+  if (!problem_ok(p) || !idx_out || block_tokens < 1 || n_blocks < 0 || b < 0 || b >= p->B || kh < 0 ||
+      kh >= p->KH)
+    return -1;
+  const int32_t L = std::max(0, p->lens[b]);
+  std::vector<double> tok(L);
+  if (L > 0 && oracle_oam_scores(p, b, kh, beta, eps, tok.data())) return -1;
+  const int32_t nb = (L + block_tokens - 1) / block_tokens;
+  std::vector<double> bs(nb);
+  for (int32_t j = 0; j < nb; ++j) {
+    const int32_t t0 = j * block_tokens, t1 = std::min(L, t0 + block_tokens);
+    double sum = 0.0;
+    for (int32_t t = t0; t < t1; ++t) sum += tok[t];
+    bs[j] = sum / (t1 - t0);
+  }
+  if (block_scores) std::copy(bs.begin(), bs.end(), block_scores);
+  std::vector<int32_t> kept(nb);
+  const int32_t nk = oracle_topk_sort(bs.data(), nb, n_blocks, kept.data());
+  int32_t n = 0;
+  for (int32_t i = 0; i < nk; ++i)
+    for (int32_t t = kept[i] * block_tokens; t < std::min(L, (kept[i] + 1) * block_tokens); ++t) idx_out[n++] = t;
+  return n;
+}
+
 int32_t oracle_topk_select(const double *scores, int32_t L, int32_t k, int32_t *idx_out) {
   if (L < 0 || k < 0 || (L > 0 && !scores) || !idx_out) return -1;
   std::vector<int32_t> order(L);

@@ -106,6 +106,20 @@ int oracle_value_lognorm(const oracle_problem *p, int32_t b, int32_t kh, double 
  * ascending order and returns that count (negative on error).  The first
  * form sorts everything; the second uses a selection followed by a sort. */
 int32_t oracle_topk_sort(const double *scores, int32_t L, int32_t k, int32_t *idx_out);
+
+/* Block-granular selection ("NSA" page §2.1, selected attention: the top-n
+ * blocks of contiguous tokens by an importance shared by the GQA group).
+ * The page's importance comes from a learned compression of each block;
+ * with that compression taken as the mean over the block (a reading), a
+ * block's score is the mean of its tokens' scores (token scores as in
+ * oracle_oam_scores with the given beta and eps; beta = 0 gives the plain
+ * routing logits).  Blocks are [j*block_tokens, min((j+1)*block_tokens, L))
+ * of (b, kh); the n_blocks best by (score descending, block index ascending)
+ * are kept, and their token indices are written to idx_out in ascending
+ * order.  block_scores (optional) receives every block's score.  Returns
+ * the number of kept tokens, or -1 on invalid arguments. */
+int32_t oracle_block_select(const oracle_problem *p, int32_t b, int32_t kh, int32_t block_tokens, int32_t n_blocks,
+                            double beta, double eps, int32_t *idx_out, double *block_scores);
 int32_t oracle_topk_select(const double *scores, int32_t L, int32_t k, int32_t *idx_out);
 
 #ifdef __cplusplus
