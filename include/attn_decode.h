@@ -260,10 +260,19 @@ attn_status oam_value_lognorm(const attn_kv_geom *geom, const void *v, int32_t v
  *               oam_value_lognorm, stride vlog_stride) when vlog != NULL,
  *               else it is computed from the rows of v (kv_dtype) on the fly
  *   softmax_scale  0 selects 1/sqrt(D); beta, eps as on the page
- *   top_k       >= 1 tokens kept per (b, kh)
- *   idx_out     int32 [B][KH][top_k]: kept token indices in ascending order;
- *               entries past n_kept are set to -1
- *   n_kept      int32 [B][KH] = min(top_k, L_b)
+ *   top_k       >= 1 tokens kept per (b, kh); with block_tokens > 1, blocks
+ *   block_tokens  0 or 1: token-granular selection.  A power of two in
+ *               [16, 256]: block-granular selection ("原生稀疏注意力(NSA)"
+ *               §2.1, selected attention: the top-n blocks of contiguous
+ *               tokens, shared by the GQA group).  Blocks are [j*block_tokens,
+ *               (j+1)*block_tokens) cut at L_b; a block's score is the mean of
+ *               its tokens' scores (the page's learned block compression read
+ *               as the mean over the block; beta = 0 gives the plain routing
+ *               score); the top_k blocks by (score descending, block index
+ *               ascending) are kept.  At most 8192 blocks per sequence
+ *   idx_out     int32 [B][KH][top_k * max(block_tokens, 1)]: kept token
+ *               indices in ascending order; entries past n_kept are -1
+ *   n_kept      int32 [B][KH]: kept tokens, min(top_k, L_b) for tokens
  *   scores_out  optional fp32 [B][KH][max_seq_len]: the scores
  *   workspace   >= oam_score_topk_workspace_size() bytes, 256-byte aligned
  */
@@ -281,6 +290,7 @@ typedef struct {
   int32_t vlog_stride;
   float softmax_scale, beta, eps;
   int32_t top_k;
+  int32_t block_tokens;
   int32_t *idx_out;
   int32_t *n_kept;
   float *scores_out;

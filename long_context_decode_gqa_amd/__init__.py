@@ -218,7 +218,7 @@ def oam_value_lognorm(v: torch.Tensor, geom: KVGeometry, eps: float = 1e-6, vlog
 
 
 def _oam_args(q, k, geom, G, top_k, v, vlog, vlog_stride, softmax_scale, beta, eps, idx_out, n_kept, scores_out,
-              workspace, k_scale=None, k_part_tokens=0, k_scale_stride=0, v_scale=1.0):
+              workspace, k_scale=None, k_part_tokens=0, k_scale_stride=0, v_scale=1.0, block_tokens=0):
     a = _lib.OamTopkArgs()
     a.kv = geom.c()
     a.G = G
@@ -228,6 +228,7 @@ def _oam_args(q, k, geom, G, top_k, v, vlog, vlog_stride, softmax_scale, beta, e
     a.vlog_stride = vlog_stride
     a.softmax_scale, a.beta, a.eps = softmax_scale, beta, eps
     a.top_k = top_k
+    a.block_tokens = block_tokens
     a.idx_out, a.n_kept, a.scores_out = _ptr(idx_out), _ptr(n_kept), _ptr(scores_out)
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel()
@@ -254,22 +255,24 @@ class PreparedOam:
 def prepare_oam(q, k, geom: KVGeometry, G: int, top_k: int, *, v=None, vlog=None, vlog_stride: Optional[int] = None,
                 softmax_scale: float = 0.0, beta: float = 1.0, eps: float = 1e-6, idx_out=None, n_kept=None,
                 scores_out=None, workspace=None, k_scale=None, k_part_tokens: int = 64,
-                k_scale_stride: Optional[int] = None, v_scale: float = 1.0) -> PreparedOam:
+                k_scale_stride: Optional[int] = None, v_scale: float = 1.0, block_tokens: int = 0) -> PreparedOam:
     """One ``oam_score_topk`` call.  An int8 ``k`` (and ``v``) is an INT8 cache with the K scales of
-    ``prepare_decode`` (``k_part_tokens=0``: one per-tensor scale) and the V scale ``v_scale``."""
+    ``prepare_decode`` (``k_part_tokens=0``: one per-tensor scale) and the V scale ``v_scale``.
+    ``block_tokens`` > 1 keeps the ``top_k`` best blocks of that many tokens instead of tokens."""
     dev = q.device
     if k_scale_stride is None:
         k_scale_stride = (max(1, -(-geom.max_seq_len // k_part_tokens))
                           if k_scale is not None and k_part_tokens > 0 else 0)
     npairs = geom.B * geom.KH
     if idx_out is None:
-        idx_out = torch.empty((npairs, top_k), dtype=torch.int32, device=dev)
+        idx_out = torch.empty((npairs, top_k * max(block_tokens, 1)), dtype=torch.int32, device=dev)
     if n_kept is None:
         n_kept = torch.empty(npairs, dtype=torch.int32, device=dev)
     if vlog is not None and vlog_stride is None:
         vlog_stride = vlog.shape[-1]
     a = _oam_args(q, k, geom, G, top_k, v, vlog, vlog_stride or 0, softmax_scale, beta, eps, idx_out, n_kept,
-                  scores_out, None, k_scale, k_part_tokens if k_scale is not None else 0, k_scale_stride, v_scale)
+                  scores_out, None, k_scale, k_part_tokens if k_scale is not None else 0, k_scale_stride, v_scale,
+                  block_tokens)
     need = oam_workspace_size(a)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)

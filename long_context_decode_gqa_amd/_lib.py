@@ -29,7 +29,8 @@ class AttnDecodeArgs(ctypes.Structure):
 class OamTopkArgs(ctypes.Structure):
     _fields_ = [("kv", AttnKvGeom), ("G", i32), ("q", vp), ("k", vp), ("v", vp), ("kv_dtype", i32), ("k_scale", vp),
                 ("k_part_tokens", i32), ("k_scale_stride", i32), ("v_scale", f32), ("vlog", vp), ("vlog_stride", i32),
-                ("softmax_scale", f32), ("beta", f32), ("eps", f32), ("top_k", i32), ("idx_out", vp),
+                ("softmax_scale", f32), ("beta", f32), ("eps", f32), ("top_k", i32), ("block_tokens", i32),
+                ("idx_out", vp),
                 ("n_kept", vp), ("scores_out", vp), ("workspace", vp), ("workspace_bytes", sz)]
 
 

@@ -80,7 +80,8 @@ attn_status oam_value_lognorm(const attn_kv_geom *geom, const void *v, int32_t v
 namespace {
 
 struct OamLayout {
-  size_t scores, vlog, hist, state, blk_gt, blk_off, blk_nc, cand_key, cand_idx, total;
+  size_t scores, vlog, hist, state, blk_gt, blk_off, blk_nc, cand_key, cand_idx, bscores, total;
+  int32_t bs_stride;
 };
 
 attn_status plan_oam(const oam_topk_args *a, OamLayout *L) {
@@ -107,6 +108,13 @@ attn_status plan_oam(const oam_topk_args *a, OamLayout *L) {
   if (g.D != 64 && g.D != 128) return api_fail(ATTN_ERR_UNSUPPORTED, "oam_score_topk supports D = 64 or 128");
   if (a->G < 1 || a->G > 16) return api_fail(ATTN_ERR_UNSUPPORTED, "oam_score_topk supports 1 <= G <= 16");
   if (a->top_k < 1) return api_fail(ATTN_ERR_INVALID_ARG, "top_k must be >= 1");
+  const int bt = a->block_tokens;
+  if (bt < 0 || (bt > 1 && (bt < 16 || bt > 256 || (bt & (bt - 1)))))
+    return api_fail(ATTN_ERR_INVALID_ARG, "block_tokens must be 0, 1 or a power of two in [16, 256]");
+  if (bt > 1 && ((int64_t)g.max_seq_len + bt - 1) / bt > oam_max_select_blocks())
+    return api_fail(ATTN_ERR_UNSUPPORTED, "block-granular selection supports up to 8192 blocks per sequence");
+  if (bt > 1 && (int64_t)a->top_k * bt >= (int64_t(1) << 31))
+    return api_fail(ATTN_ERR_INVALID_ARG, "top_k * block_tokens must fit in int32");
   if (!(fabsf(a->softmax_scale) < INFINITY) || !(fabsf(a->beta) < INFINITY))
     return api_fail(ATTN_ERR_INVALID_ARG, "softmax_scale and beta must be finite");
   if (!(a->eps >= 0.f) || !(a->eps < INFINITY)) return api_fail(ATTN_ERR_INVALID_ARG, "eps must be finite and >= 0");
@@ -138,6 +146,8 @@ attn_status plan_oam(const oam_topk_args *a, OamLayout *L) {
   L->blk_nc = off; off = al(off + (size_t)npairs * nblk_max * sizeof(int32_t));
   L->cand_key = off; off = al(off + (size_t)npairs * stride * sizeof(uint32_t));
   L->cand_idx = off; off = al(off + (size_t)npairs * stride * sizeof(int32_t));
+  L->bs_stride = bt > 1 ? (int32_t)((g.max_seq_len + bt - 1) / bt) : 0;
+  L->bscores = off; off = al(off + (size_t)npairs * L->bs_stride * sizeof(float));
   L->total = off;
   return ATTN_OK;
 }
@@ -171,6 +181,8 @@ attn_status oam_score_topk(const oam_topk_args *a, attn_stream_t stream) {
   plan.vlog_stride = a->vlog ? a->vlog_stride : a->kv.max_seq_len;
   plan.hist = reinterpret_cast<uint32_t *>(ws + L.hist);
   plan.blk_nc = reinterpret_cast<int32_t *>(ws + L.blk_nc);
+  plan.bscores = reinterpret_cast<float *>(ws + L.bscores);
+  plan.bs_stride = L.bs_stride;
   plan.state = reinterpret_cast<int32_t *>(ws + L.state);
   plan.blk_gt = reinterpret_cast<int32_t *>(ws + L.blk_gt);
   plan.blk_off = reinterpret_cast<int32_t *>(ws + L.blk_off);

@@ -218,11 +218,14 @@ struct OamPlan {
   int32_t *blk_gt;       // [npairs][oam_max_tokens() / 2048]
   int32_t *blk_off;      // [npairs][oam_max_tokens() / 2048]
   int32_t *blk_nc;       // [npairs][1024] candidates per block
+  float *bscores;        // [npairs][bs_stride] block scores (block-granular selection)
+  int32_t bs_stride;
   uint32_t *cand_key;    // [npairs][score_stride] per-block candidate regions
   int32_t *cand_idx;     // [npairs][score_stride]
 };
 hipError_t launch_oam(const oam_topk_args &a, const OamPlan &plan, hipStream_t s);
 int oam_max_tokens();  // longest sequence oam_score_topk selects over
+int oam_max_select_blocks();  // most token blocks per pair in block-granular selection
 
 int device_cu_count();
 

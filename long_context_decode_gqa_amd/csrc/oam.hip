@@ -34,6 +34,7 @@ constexpr int kBins = 2048;       // 11-bit digits (the 10-bit ones use 1024)
 constexpr int kBlockTok = 2048;   // tokens per workgroup of the candidate and write passes
 constexpr int kCandCap = 4096;    // candidates the select pass holds in LDS
 constexpr int kMaxBlocks = 1024;  // blocks of kBlockTok per pair (sequences up to 2M tokens)
+constexpr int kMaxSelBlocks = 8192;  // token blocks per pair the block-granular select holds
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -69,8 +70,12 @@ struct OamDev {
   int32_t *blk_nc;     // [npairs][kMaxBlocks]  candidates (keys in bin b0) per block
   uint32_t *cand_key;  // [npairs][L_max]  block j's candidates at [j*kBlockTok, + blk_nc)
   int32_t *cand_idx;   // [npairs][L_max]
-  int32_t *idx_out;    // [npairs][top_k]
+  int32_t *idx_out;    // [npairs][top_k * max(block_tokens, 1)]
   int32_t *n_kept;     // [npairs]
+  int32_t block_tokens;  // > 1: block-granular selection of top_k blocks
+  int32_t write_scores;  // token scores are written (token mode, or asked for)
+  float *bscores;        // [npairs][bs_stride] block scores (block mode)
+  int32_t bs_stride;
 };
 
 __device__ __forceinline__ int pair_len(const OamDev &o, int pair) {
@@ -267,6 +272,7 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
   };
   // Lane (col = 4j + p, cg) ends with, for p == 0, the full q_bar . k of the
   // four tokens 4cg..4cg+3 of each 16-token block; it publishes token 4cg + j.
+  const bool token_mode = o.block_tokens <= 1;
   const int jq = col >> 2;
   const bool leader = (col & 3) == 0;
   auto compute = [&](const KTile &R, int tile, bool valid) {
@@ -298,7 +304,7 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
       const float sv = dot * mult + o.beta * __uint_as_float(vw);
       if (mine) {
         s_sc[t - blk0] = sv;
-        atomicAdd(&s_hist[order_key(sv) >> 21], 1u);
+        if (token_mode) atomicAdd(&s_hist[order_key(sv) >> 21], 1u);
       }
     }
   };
@@ -321,10 +327,26 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
   }
   __syncthreads();
   const int nblk_tok = min(kScoreTok, L - blk0);
-  for (int i = tid; i < nblk_tok; i += 256) sc[blk0 + i] = s_sc[i];
-  uint32_t *gh = o.hist + (size_t)pair * kBins;
-  for (int i = tid; i < kBins; i += 256)
-    if (s_hist[i]) atomicAdd(gh + i, s_hist[i]);
+  if (o.write_scores)
+    for (int i = tid; i < nblk_tok; i += 256) sc[blk0 + i] = s_sc[i];
+  if (token_mode) {
+    uint32_t *gh = o.hist + (size_t)pair * kBins;
+    for (int i = tid; i < kBins; i += 256)
+      if (s_hist[i]) atomicAdd(gh + i, s_hist[i]);
+  } else {
+    // block scores: the mean of each block's token scores (block_tokens is a
+    // power of two dividing kScoreTok, so blocks never straddle workgroups)
+    const int bt = o.block_tokens;
+    const int nbb = (nblk_tok + bt - 1) / bt;
+    float *bs = o.bscores + (int64_t)pair * o.bs_stride + blk0 / bt;
+    for (int jb = wave; jb < nbb; jb += 4) {
+      const int t0 = jb * bt, cnt = min(bt, nblk_tok - t0);
+      float sum = 0.f;
+      for (int i = lane; i < cnt; i += 64) sum += s_sc[t0 + i];
+      sum = wave_sum(sum);
+      if (lane == 0) bs[jb] = sum / (float)cnt;
+    }
+  }
 }
 
 // Exact selection inside bin b0 by the select pass: the
@@ -626,6 +648,90 @@ __global__ __launch_bounds__(256) void oam_write_kernel(OamDev o) {
     if (keep[j]) out[pos++] = blk0 + 8 * tid + j;
 }
 
+// Block-granular select, one workgroup per pair: the top_k blocks by
+// (block score descending, block index ascending), by radix selection on the
+// order-preserving keys of the block scores (digits of 11, 11 and 10 bits;
+// ties at the threshold go to the lowest block indices), then the kept
+// blocks' tokens in ascending order, n_kept, and -1 past it.  Thread t owns
+// the contiguous blocks [32t, 32t + 32), its keys held in registers.
+__global__ __launch_bounds__(256) void oam_block_select_kernel(OamDev o) {
+  constexpr int kPer = kMaxSelBlocks / 256;
+  __shared__ uint32_t s_hist[kBins];
+  __shared__ int s_kb[kMaxSelBlocks];  // kept blocks in ascending order
+  __shared__ int s_tmp[4], s_res[2];
+  const int pair = blockIdx.x;
+  const int L = pair_len(o, pair);
+  const int tid = threadIdx.x;
+  const int bt = o.block_tokens;
+  const int cap = o.top_k * bt;
+  int32_t *out = o.idx_out + (int64_t)pair * cap;
+  const int nb = (L + bt - 1) / bt;
+  const int n = min(o.top_k, nb);
+  const float *bsp = o.bscores + (int64_t)pair * o.bs_stride;
+  uint32_t key[kPer];
+  const int j0 = tid * kPer;
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) key[r] = j0 + r < nb ? order_key(bsp[j0 + r]) : 0u;
+  uint32_t T = 0u;
+  int need = n;  // kept blocks still to place at the current prefix
+  if (n > 0 && n < nb) {
+    // three digit passes: prefix of the n-th largest key
+    uint32_t prefix = 0u;
+    const int shifts[3] = {21, 10, 0};
+    const int widths[3] = {11, 11, 10};
+    for (int d = 0; d < 3; ++d) {
+      for (int i = tid; i < kBins; i += 256) s_hist[i] = 0u;
+      __syncthreads();
+      const int sh = shifts[d];
+      const uint32_t mask = (1u << widths[d]) - 1u;
+#pragma unroll
+      for (int r = 0; r < kPer; ++r)
+        if (j0 + r < nb && (d == 0 || (key[r] >> (sh + widths[d])) == prefix))
+          atomicAdd(&s_hist[(key[r] >> sh) & mask], 1u);
+      __syncthreads();
+      int above;
+      const int bin = select_bin(s_hist, 1 << widths[d], need, &above, s_tmp, s_res);
+      need -= above;
+      prefix = (prefix << widths[d]) | (uint32_t)bin;
+    }
+    T = prefix;
+  }
+  // kept: key > T, or key == T among the first `need` such blocks by index
+  // (all blocks when n == nb)
+  int nt = 0;
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) nt += j0 + r < nb && key[r] == T;
+  int ttot;
+  int trank = block_exclusive_scan(nt, s_tmp, &ttot);
+  int kc = 0;
+  bool kept[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const bool live = j0 + r < nb;
+    const bool tie = live && key[r] == T;
+    kept[r] = n >= nb ? live : (live && (key[r] > T || (tie && trank < need)));
+    trank += tie;
+    kc += kept[r];
+  }
+  int ktot;
+  int pos = block_exclusive_scan(kc, s_tmp, &ktot);
+#pragma unroll
+  for (int r = 0; r < kPer; ++r)
+    if (kept[r]) s_kb[pos++] = j0 + r;
+  __syncthreads();
+  // tokens of the kept blocks; only the last block of the sequence is partial
+  // and it is the last kept one if kept, so kept block q starts at q * bt
+  const int last = ktot > 0 ? s_kb[ktot - 1] : 0;
+  const int nk = ktot > 0 ? (ktot - 1) * bt + min(bt, L - last * bt) : 0;
+  for (int e = tid; e < cap; e += 256) {
+    const int q = e / bt, i = e - q * bt;
+    int v = -1;
+    if (e < nk) v = s_kb[q] * bt + i;
+    out[e] = v;
+  }
+  if (tid == 0) o.n_kept[pair] = nk;
+}
+
 }  // namespace
 
 hipError_t launch_oam(const oam_topk_args &a, const OamPlan &plan, hipStream_t s) {
@@ -665,15 +771,22 @@ hipError_t launch_oam(const oam_topk_args &a, const OamPlan &plan, hipStream_t s
   o.cand_idx = plan.cand_idx;
   o.idx_out = a.idx_out;
   o.n_kept = a.n_kept;
+  o.block_tokens = a.block_tokens;
+  o.write_scores = a.block_tokens <= 1 || a.scores_out != nullptr;
+  o.bscores = plan.bscores;
+  o.bs_stride = plan.bs_stride;
 
   hipError_t e;
+  const bool block_mode = a.block_tokens > 1;
   const int nblk = (g.max_seq_len + kBlockTok - 1) / kBlockTok;
   if (nblk > 0) {
-    // the histogram starts at zero (a fill kernel, not a memset)
-    const size_t nz = (size_t)npairs * kBins;
-    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((nz + 255) / 256 < 128 ? (nz + 255) / 256 : 128)), dim3(256), 0,
-                       s, plan.hist, nz);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!block_mode) {
+      // the histogram starts at zero (a fill kernel, not a memset)
+      const size_t nz = (size_t)npairs * kBins;
+      hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((nz + 255) / 256 < 128 ? (nz + 255) / 256 : 128)), dim3(256),
+                         0, s, plan.hist, nz);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if (!a.vlog) {
       e = launch_value_lognorm(g, a.v, a.kv_dtype, a.v_scale, a.eps, plan.vlog, plan.vlog_stride, s);
       if (e != hipSuccess) return e;
@@ -687,16 +800,20 @@ hipError_t launch_oam(const oam_topk_args &a, const OamPlan &plan, hipStream_t s
       else hipLaunchKernelGGL((oam_score_kernel<64, ATTN_BF16>), sgrid, blk, 0, s, o);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(oam_candidate_kernel, dim3(nblk, npairs), blk, 0, s, o);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(oam_select_kernel, dim3(npairs), blk, 0, s, o);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!block_mode) {
+      hipLaunchKernelGGL(oam_candidate_kernel, dim3(nblk, npairs), blk, 0, s, o);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      hipLaunchKernelGGL(oam_select_kernel, dim3(npairs), blk, 0, s, o);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
-  // the write pass also runs for empty caches: it sets n_kept and the -1 fill
-  hipLaunchKernelGGL(oam_write_kernel, dim3(nblk > 0 ? nblk : 1, npairs), dim3(256), 0, s, o);
+  // the last pass also runs for empty caches: it sets n_kept and the -1 fill
+  if (block_mode) hipLaunchKernelGGL(oam_block_select_kernel, dim3(npairs), dim3(256), 0, s, o);
+  else hipLaunchKernelGGL(oam_write_kernel, dim3(nblk > 0 ? nblk : 1, npairs), dim3(256), 0, s, o);
   return hipGetLastError();
 }
 
 int oam_max_tokens() { return kMaxBlocks * kBlockTok; }
+int oam_max_select_blocks() { return kMaxSelBlocks; }
 
 }  // namespace lcdg

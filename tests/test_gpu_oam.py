@@ -288,3 +288,101 @@ def test_oam_int8_128k_full_size_sampled_pairs():
     ref, _ = oracle.attention_rows(pk, rows, nthreads=16)
     got = out.cpu().numpy().reshape(w.B * w.QH, w.D)[[b * w.QH + h for b, h in rows]]
     assert np.abs(got - ref).max() <= 2e-3
+
+
+# --- block-granular selection (NSA page §2.1, selected attention; block score = mean of its tokens' scores) ---
+
+
+def check_blocks(ref_idx, ref_bs, row, nk, n, bt, L):
+    """Kept tokens are whole blocks in ascending order, min(n, blocks) of them, equal to the oracle's
+    set except for blocks whose oracle score lies within the band around its n-th best score."""
+    kept = row[:nk]
+    assert np.all(row[nk:] == -1)
+    nb = -(-L // bt)
+    if nb == 0:
+        assert nk == 0
+        return
+    assert np.all(np.diff(kept) > 0)
+    blocks = sorted(set((kept // bt).tolist()))
+    assert len(blocks) == min(n, nb)
+    want = np.concatenate([np.arange(j * bt, min(L, (j + 1) * bt)) for j in blocks])
+    np.testing.assert_array_equal(kept, want)
+    ref_blocks = set((ref_idx // bt).tolist())
+    if n < nb:
+        thr = np.sort(ref_bs)[::-1][n - 1]
+        diff = set(blocks) ^ ref_blocks
+        assert all(abs(ref_bs[j] - thr) <= BAND for j in diff), f"{len(diff)} blocks outside the band"
+    else:
+        assert set(blocks) == ref_blocks
+
+
+@pytest.mark.parametrize("bt,n,D,G,beta", [(64, 5, 128, 8, 0.0), (16, 40, 64, 4, 1.0), (256, 3, 128, 16, 0.0),
+                                           (32, 1000, 128, 1, 0.0)])
+def test_block_select_against_oracle(bt, n, D, G, beta):
+    lens = np.array([1, 700, 4096, 5000, 0, 2049, 40], np.int32)
+    w = synth.workload("oam_128k", B=len(lens), KH=2, G=G, D=D, lens=lens, layout="token_major", seed=110 + bt)
+    q, k, v, g = synth.generate(w)
+    log_case(f"block select bt={bt} n={n} D={D} G={G} beta={beta}")
+    qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
+    idx, nk = pkg.oam_score_topk(qd, to_dev(k), dev_geom(g), w.G, n, v=to_dev(v), beta=beta, block_tokens=bt)
+    torch.cuda.synchronize()
+    idx, nk = idx.cpu().numpy(), nk.cpu().numpy()
+    assert idx.shape[1] == n * bt
+    p = problem(w, q, k, v, g)
+    for b in range(w.B):
+        for kh in range(w.KH):
+            ref_idx, ref_bs = oracle.block_select(p, b, kh, bt, n, beta=beta)
+            pr = b * w.KH + kh
+            check_blocks(ref_idx, ref_bs, idx[pr], nk[pr], n, bt, int(lens[b]))
+
+
+def test_block_select_on_int8_cache_feeds_attention():
+    lens = np.array([6000, 2500, 300], np.int32)
+    w = synth.workload("oam_128k", B=3, KH=2, lens=lens, layout="token_major", seed=120)
+    q, k, v, g = synth.generate(w)
+    bt, n = 64, 12
+    log_case("block select on an int8 cache -> indexed int8 decode")
+    kc, ks, vc, vs, kk = quant_cache(k, v, g, 64)
+    qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
+    geom = dev_geom(g)
+    idx, nk = pkg.oam_score_topk(qd, kc, geom, w.G, n, v=vc, beta=0.0, k_scale=ks, k_part_tokens=64, v_scale=vs,
+                                 block_tokens=bt)
+    out, _ = pkg.attn_decode_splitkv(qd, kc, vc, geom, w.G, token_idx=idx, n_idx=nk, k_scale=ks, k_part_tokens=64,
+                                     v_scale=vs, split_tokens=0)
+    torch.cuda.synchronize()
+    idx_h, nk_h = idx.cpu().numpy(), nk.cpu().numpy()
+    p = problem(w, q, kc.cpu().numpy(), vc.cpu().numpy(), g, v_scale=vs, **kk)
+    for b in range(w.B):
+        for kh in range(w.KH):
+            ref_idx, ref_bs = oracle.block_select(p, b, kh, bt, n, beta=0.0)
+            pr = b * w.KH + kh
+            check_blocks(ref_idx, ref_bs, idx_h[pr], nk_h[pr], n, bt, int(lens[b]))
+    pk = problem(w, q, kc.cpu().numpy(), vc.cpu().numpy(), g, v_scale=vs, tok_idx=idx_h.reshape(-1), n_idx=nk_h,
+                 idx_stride=n * bt, **kk)
+    ref, _ = oracle.attention_rows(pk, oracle.all_rows(pk), nthreads=8)
+    assert np.abs(out.cpu().numpy().reshape(-1, w.D) - ref).max() <= 2e-3
+
+
+def test_block_select_128k_full_size_sampled_pairs():
+    """128K tokens, 64-token blocks, the best 64 blocks (4096 tokens, as many as the token top-K keeps),
+    on sampled (b, kh) pairs, then attention over them on sampled rows."""
+    w = synth.workload("oam_128k")
+    q, k, v, g = synth.generate(w)
+    bt, n = 64, 64
+    log_case("block select 128k full size")
+    qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
+    kd, vd = to_dev(k), to_dev(v)
+    geom = dev_geom(g)
+    idx, nk = pkg.oam_score_topk(qd, kd, geom, w.G, n, v=vd, beta=0.0, block_tokens=bt)
+    out, _ = pkg.attn_decode_splitkv(qd, kd, vd, geom, w.G, token_idx=idx, n_idx=nk, split_tokens=w.split_tokens)
+    torch.cuda.synchronize()
+    idx_h, nk_h = idx.cpu().numpy(), nk.cpu().numpy()
+    p = problem(w, q, k, v, g)
+    for b, kh in ((0, 0), (3, 7), (1, 4)):
+        ref_idx, ref_bs = oracle.block_select(p, b, kh, bt, n, beta=0.0)
+        check_blocks(ref_idx, ref_bs, idx_h[b * w.KH + kh], nk_h[b * w.KH + kh], n, bt, int(w.lens[b]))
+    pk = problem(w, q, k, v, g, tok_idx=idx_h.reshape(-1), n_idx=nk_h, idx_stride=n * bt)
+    rows = [(0, 0), (3, 63), (2, 9)]
+    ref, _ = oracle.attention_rows(pk, rows, nthreads=16)
+    got = out.cpu().numpy().reshape(w.B * w.QH, w.D)[[b * w.QH + h for b, h in rows]]
+    assert np.abs(got - ref).max() <= 2e-3
