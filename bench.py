@@ -2,12 +2,14 @@
 """Decode-attention benchmark on one MI355X.
 
 Headline: bf16 GQA decode at 128K KV (B=4 sequences, 8 KV heads, G=8 query
-heads per KV head, head dim 128, 131072 tokens each, 1024-token split-KV
-chunks merged by log-sum-exp).  One step = one attn_decode_splitkv call
-(work-list pass + decode kernel + merge) over inputs already resident in HBM.
-Prints one JSON line: KV GB/s (value), us/step, fraction of HBM peak, the
-roofline of the decode kernel, the CPU oracle baseline and, unless
---headline-only, the other workloads (32K GQA, ragged batch, INT8 KV, OAM).
+heads per KV head, head dim 128, 131072 tokens each, split-KV chunks of the
+library's default size merged by log-sum-exp).  One step = one
+attn_decode_splitkv call (decode kernel + merge) over inputs already resident
+in HBM.  Prints one JSON line: KV GB/s (value), us/step, fraction of HBM peak,
+the roofline of the decode kernel, the CPU oracle baseline and, unless
+--headline-only, the other workloads (32K GQA, ragged batch, INT8 KV and its
+scheme table, a paged cache, OAM token dropping on bf16 and INT8 caches, and
+block-granular selection).
 """
 from __future__ import annotations
 
@@ -235,6 +237,35 @@ def bench_int8(pkg, torch, synth, steps, warmup, dev):
     return dict(ms=ms, decode_ms=dk, merge_ms=mg, kv_bytes=kvb, split=effective_split(torch, w), schemes=schemes)
 
 
+def bench_paged(pkg, torch, synth, steps, warmup, dev, page_tokens=64):
+    """The 128K bf16 decode over a paged cache: the same K/V rows moved into a pool of
+    token-major pages ([pages][page_tokens][KH][D]) in scrambled order, read through a block
+    table.  Pool construction is setup, outside the timed region."""
+    w = synth.workload("dense128k")
+    q, k, v, g = synth.generate(w, nthreads=host_threads())
+    B, KH, D, L, P = w.B, w.KH, w.D, int(w.lens[0]), page_tokens
+    npg = L // P
+    gen = torch.Generator().manual_seed(12)
+    perm = torch.randperm(B * npg, generator=gen).to(dev)
+
+    def pool_of(x):
+        t = to_dev(torch, x, dev).view(B, KH, npg, P, D).permute(0, 2, 3, 1, 4).reshape(B * npg, P, KH, D)
+        pool = torch.empty_like(t)
+        pool[perm] = t                      # logical page i of the batch lives at pool page perm[i]
+        return pool.reshape(-1)
+
+    kp, vp = pool_of(k), pool_of(v)
+    del k, v
+    table = perm.view(B, npg).to(torch.int32).contiguous()
+    geom = pkg.KVGeometry(B, KH, D, L, torch.full((B,), L, dtype=torch.int32, device=dev), None, D, KH * D,
+                          block_table=table, page_tokens=P, page_stride=P * KH * D)
+    qd = to_dev(torch, q.reshape(-1), dev).view(w.B, w.QH, w.D)
+    p = pkg.prepare_decode(qd, kp, vp, geom, w.G, split_tokens=w.split_tokens)
+    ms, dk, mg = time_decode(torch, p, steps, warmup)
+    return dict(ms=ms, decode_ms=dk, merge_ms=mg, kv_bytes=kv_bytes(w.kv_tokens(), KH, D, 2),
+                split=effective_split(torch, w))
+
+
 def bench_oam(pkg, torch, synth, steps, warmup, dev):
     """OAM step: score + exact top-K over the cached value log-norms, then exact
     attention over the kept tokens.  Also times the variant that reads V to get
@@ -354,7 +385,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--headline-only", action="store_true")
-    ap.add_argument("--others", default="gqa32k,ragged,int8,oam",
+    ap.add_argument("--others", default="gqa32k,ragged,int8,oam,paged",
                     help="comma-separated other workloads to time after the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -362,7 +393,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
-              "multi-GPU sharding is described in DESIGN.md but not built", file=sys.stderr)
+              "the multi-GPU sharding of this path is not built", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -433,6 +464,10 @@ def main():
                 others["int8_128k_schemes"] = r["schemes"]
             except pkg.AttnError as e:
                 others["int8_128k"] = {"error": str(e)}
+        if "paged" in todo:
+            r = bench_paged(pkg, torch, synth, max(5, K // 2), W, dev)
+            others["paged_128k_bf16"] = summary(r, {"page_tokens": 64})
+            del r
         if "oam" in todo:
             try:
                 others["oam_128k"] = bench_oam(pkg, torch, synth, max(5, K // 2), W, dev)

@@ -90,12 +90,31 @@ typedef enum {
  *   stride_h, stride_t  element strides, >= D; every row must be 16-byte
  *                 aligned (so offsets and strides are multiples of 8 bf16 /
  *                 4 fp32 / 16 int8 elements)
+ * Paged cache ("注意力优化" 结构 4, PagedAttention: the cache is cut into
+ * fixed-size pages allocated on demand), optional: when block_table is not
+ * NULL, row (b, kh, t) starts at element
+ *   block_table[b*table_stride + t/page_tokens]*page_stride + kh*stride_h
+ *   + (t % page_tokens)*stride_t
+ * of a page pool, and seq_offset is ignored.
+ *   block_table   device int32, page ids >= 0, table_stride >=
+ *                 ceil(max_seq_len / page_tokens) entries per sequence
+ *   page_tokens   tokens per page, a positive multiple of 32
+ *   page_stride   elements between pages, > 0, 16-byte aligned
+ * Only attn_decode_splitkv with bf16 or int8 KV and no token_idx reads a
+ * paged cache; the other calls return ATTN_ERR_UNSUPPORTED for one.  The
+ * token-major pool [pages][page_tokens][KH][D] has stride_t = KH*D,
+ * stride_h = D, page_stride = page_tokens*KH*D; the head-major pool
+ * [pages][KH][page_tokens][D] has stride_t = D, stride_h = page_tokens*D,
+ * page_stride = KH*page_tokens*D.
  */
 typedef struct {
   int32_t B, KH, D, max_seq_len;
   const int32_t *seq_lens;
   const int64_t *seq_offset;
   int64_t stride_h, stride_t;
+  const int32_t *block_table;
+  int32_t page_tokens, table_stride;
+  int64_t page_stride;
 } attn_kv_geom;
 
 /*

@@ -50,22 +50,36 @@ def _stream(stream) -> int:
 class KVGeometry:
     """KV-cache geometry: row (b, kh, t) starts at element seq_offset[b] + kh*stride_h + t*stride_t.
 
-    ``seq_lens`` (int32) and ``seq_offset`` (int64) are device tensors of length B.
+    ``seq_lens`` (int32) and ``seq_offset`` (int64) are device tensors of length B.  A paged cache
+    gives ``block_table`` (device int32 [B, table_stride]) instead of ``seq_offset``: row (b, kh, t)
+    then starts at block_table[b, t // page_tokens] * page_stride + kh*stride_h
+    + (t % page_tokens)*stride_t.
     """
     B: int
     KH: int
     D: int
     max_seq_len: int
     seq_lens: torch.Tensor
-    seq_offset: torch.Tensor
+    seq_offset: Optional[torch.Tensor]
     stride_h: int
     stride_t: int
+    block_table: Optional[torch.Tensor] = None
+    page_tokens: int = 0
+    page_stride: int = 0
 
     def c(self) -> _lib.AttnKvGeom:
         if self.B:
-            assert self.seq_lens.dtype == torch.int32 and self.seq_offset.dtype == torch.int64
-        return _lib.AttnKvGeom(self.B, self.KH, self.D, self.max_seq_len, _ptr(self.seq_lens), _ptr(self.seq_offset),
-                               self.stride_h, self.stride_t)
+            assert self.seq_lens.dtype == torch.int32
+            assert self.seq_offset is None or self.seq_offset.dtype == torch.int64
+        g = _lib.AttnKvGeom(self.B, self.KH, self.D, self.max_seq_len, _ptr(self.seq_lens), _ptr(self.seq_offset),
+                            self.stride_h, self.stride_t)
+        if self.block_table is not None:
+            assert self.block_table.dtype == torch.int32 and self.block_table.dim() == 2
+            g.block_table = _ptr(self.block_table)
+            g.page_tokens = self.page_tokens
+            g.table_stride = self.block_table.shape[1]
+            g.page_stride = self.page_stride
+        return g
 
     @staticmethod
     def dense(B: int, KH: int, L: int, D: int, device="cuda") -> "KVGeometry":

@@ -16,7 +16,8 @@ vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.
 
 class AttnKvGeom(ctypes.Structure):
     _fields_ = [("B", i32), ("KH", i32), ("D", i32), ("max_seq_len", i32),
-                ("seq_lens", vp), ("seq_offset", vp), ("stride_h", i64), ("stride_t", i64)]
+                ("seq_lens", vp), ("seq_offset", vp), ("stride_h", i64), ("stride_t", i64),
+                ("block_table", vp), ("page_tokens", i32), ("table_stride", i32), ("page_stride", i64)]
 
 
 class AttnDecodeArgs(ctypes.Structure):

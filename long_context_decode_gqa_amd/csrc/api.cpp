@@ -57,8 +57,16 @@ attn_status check_geom(const attn_kv_geom &g, int es, bool need_ptrs) {
   if (g.stride_t < g.D || g.stride_h < g.D) return fail(ATTN_ERR_INVALID_ARG, "geometry: strides must be >= D");
   if ((g.stride_t * es) % 16 || (g.stride_h * es) % 16 || ((int64_t)g.D * es) % 4)
     return fail(ATTN_ERR_INVALID_ARG, "geometry: rows must be 16-byte aligned (stride_t, stride_h in bytes % 16)");
-  if (need_ptrs && g.B > 0 && (!g.seq_lens || !g.seq_offset))
-    return fail(ATTN_ERR_INVALID_ARG, "geometry: seq_lens and seq_offset are required");
+  if (need_ptrs && g.B > 0 && (!g.seq_lens || (!g.seq_offset && !g.block_table)))
+    return fail(ATTN_ERR_INVALID_ARG, "geometry: seq_lens and seq_offset (or a block table) are required");
+  if (g.block_table) {
+    if (g.page_tokens < 32 || g.page_tokens % 32)
+      return fail(ATTN_ERR_INVALID_ARG, "geometry: page_tokens must be a positive multiple of 32");
+    if (g.table_stride < ((int64_t)g.max_seq_len + g.page_tokens - 1) / g.page_tokens)
+      return fail(ATTN_ERR_INVALID_ARG, "geometry: table_stride must be >= ceil(max_seq_len / page_tokens)");
+    if (g.page_stride <= 0 || (g.page_stride * es) % 16)
+      return fail(ATTN_ERR_INVALID_ARG, "geometry: page_stride must be positive and 16-byte aligned");
+  }
   return ATTN_OK;
 }
 
@@ -85,6 +93,8 @@ attn_status plan_decode(const attn_decode_args *a, DecodeLayout *L) {
   if (st != ATTN_OK) return st;
   if (a->G < 1 || a->G > 64) return fail(ATTN_ERR_UNSUPPORTED, "G must be in [1, 64]");
   const bool mfma = a->kv_dtype != ATTN_F32;
+  if (g.block_table && (!mfma || a->token_idx))
+    return fail(ATTN_ERR_UNSUPPORTED, "a paged cache needs bf16 or int8 KV and no token_idx");
   if (mfma && g.D != 64 && g.D != 128)
     return fail(ATTN_ERR_UNSUPPORTED, "bf16/int8 KV supports head size D = 64 or 128");
   if (!mfma && (g.D < 4 || g.D > 256 || g.D % 4))
@@ -138,6 +148,8 @@ attn_status plan_decode(const attn_decode_args *a, DecodeLayout *L) {
     return fail(ATTN_ERR_UNSUPPORTED, "one (sequence, KV head) may span at most 2 GiB of rows");
   if (mfma && a->token_idx && L->split > 1024)
     return fail(ATTN_ERR_UNSUPPORTED, "with token_idx, split_tokens must be <= 1024");
+  if (g.block_table && (int64_t)L->split > 64 * (int64_t)g.page_tokens)
+    return fail(ATTN_ERR_UNSUPPORTED, "with a paged cache, split_tokens must be <= 64 * page_tokens");
   L->max_chunks = ((int64_t)L->max_tokens + L->split - 1) / L->split;
   const int64_t QH = (int64_t)g.KH * a->G;
   L->max_partials = 2 * (int64_t)g.B * QH * L->max_chunks;
@@ -218,6 +230,10 @@ static attn_status decode_impl(const attn_decode_args *a, attn_stream_t stream, 
   p.v_scale = a->v_scale;
   p.q_quant = a->q_quant;
   p.q_scale = a->q_scale;
+  p.block_table = a->kv.block_table;
+  p.page_tokens = a->kv.page_tokens;
+  p.table_stride = a->kv.table_stride;
+  p.page_stride = a->kv.page_stride;
   p.token_idx = a->token_idx;
   p.n_idx = a->n_idx;
   p.idx_stride = a->idx_stride;

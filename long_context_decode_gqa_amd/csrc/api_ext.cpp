@@ -28,6 +28,7 @@ attn_status kv_quant_int8(const attn_kv_geom *geom, const void *x_bf16, int32_t 
   if (!geom) return api_fail(ATTN_ERR_INVALID_ARG, "geom is NULL");
   attn_status st = api_check_geom(*geom, 2, true);
   if (st != ATTN_OK) return st;
+  if (geom->block_table) return api_fail(ATTN_ERR_UNSUPPORTED, "kv_quant_int8 does not read a paged cache");
   if (geom->D % 8 || geom->D > 4096) return api_fail(ATTN_ERR_UNSUPPORTED, "kv_quant_int8 needs D % 8 == 0");
   if (geom->stride_t % 8 || geom->stride_h % 8)
     return api_fail(ATTN_ERR_INVALID_ARG, "kv_quant_int8 needs strides that are multiples of 8 elements");
@@ -61,6 +62,7 @@ attn_status oam_value_lognorm(const attn_kv_geom *geom, const void *v, int32_t v
   const bool i8 = v_dtype == ATTN_I8;
   attn_status st = api_check_geom(*geom, i8 ? 1 : 2, true);
   if (st != ATTN_OK) return st;
+  if (geom->block_table) return api_fail(ATTN_ERR_UNSUPPORTED, "oam_value_lognorm does not read a paged cache");
   if (geom->D != 64 && geom->D != 128 && geom->D != 256)
     return api_fail(ATTN_ERR_UNSUPPORTED, "oam_value_lognorm supports D = 64, 128 or 256");
   if (i8 && (geom->stride_t % 16 || geom->stride_h % 16))
@@ -93,6 +95,7 @@ attn_status plan_oam(const oam_topk_args *a, OamLayout *L) {
   attn_status st = api_check_geom(a->kv, es, true);
   if (st != ATTN_OK) return st;
   const attn_kv_geom &g = a->kv;
+  if (g.block_table) return api_fail(ATTN_ERR_UNSUPPORTED, "oam_score_topk does not read a paged cache");
   if (i8) {
     if (g.stride_t % 16 || g.stride_h % 16) return api_fail(ATTN_ERR_INVALID_ARG, "int8 rows must be 16-byte aligned");
     if (!a->k_scale) return api_fail(ATTN_ERR_INVALID_ARG, "int8 K needs k_scale");

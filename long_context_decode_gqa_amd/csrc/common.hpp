@@ -102,6 +102,9 @@ struct DecodeParams {
   float v_scale;
   int32_t q_quant;  // attn_q_quant (int8 KV)
   float q_scale;    // static query scale (ATTN_QUANT_STATIC)
+  const int32_t *block_table;  // paged cache (NULL: rows at seq_offset[b])
+  int32_t page_tokens, table_stride;
+  int64_t page_stride;
   const int32_t *token_idx, *n_idx;
   int32_t idx_stride;
   float softmax_scale;

@@ -101,6 +101,9 @@ struct Step {
 
 // Tokens per chunk of the indexed variant (its index list is staged in LDS).
 constexpr int kMaxIdxChunk = 1024;
+// Page ids a segment of the paged variant stages in LDS (a chunk may span at
+// most 64 pages, so at most 65 are touched).
+constexpr int kMaxSegPages = 72;
 
 // One wave = one worker.  The work-list lays every (b, kh, head block) lane's
 // tiles end to end; worker w streams the contiguous tile range
@@ -109,8 +112,9 @@ constexpr int kMaxIdxChunk = 1024;
 // the loop.  A range is cut into runs (one lane each) and runs into segments
 // (one chunk piece each); a segment's partial (m, l, o) goes straight from
 // registers to its slot.
-template <int D, int KVT, bool IDX, bool QI8>
+template <int D, int KVT, bool IDX, bool QI8, bool PAGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_mfma_kernel(DecodeParams p) {
+  static_assert(!(IDX && PAGED), "a paged cache is read by position");
   typedef Tile<D, KVT, IDX> TileT;
   typedef Step<D, KVT, IDX> StepT;
   constexpr int TPS = StepT::TPS;
@@ -123,6 +127,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   typedef typename std::conditional<KVT == ATTN_BF16, bf16x8_t, f16x8_t>::type OpT;
 
   __shared__ int s_idx[IDX ? kMaxIdxChunk : 1];
+  __shared__ int s_pages[PAGED ? kMaxSegPages : 1];  // page ids of the current segment
   // Q^T operand of the current run, 16 query heads x D channels, rows padded
   // by 16 bytes against bank conflicts: bf16 for bf16 KV; for int8 KV three
   // int8 digit planes of each head's 22-bit fixed-point query (see below).
@@ -161,8 +166,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const bool qvalid = col < gcount;
 
     // Buffer resources over this (b, kh)'s rows: 32-bit offsets, and rows at
-    // or past L read as zero (their scores are masked), so no clamping.
-    const int64_t head_off = uniform_i64(p.seq_offset[b]) + (int64_t)kh * p.stride_h;
+    // or past L read as zero (their scores are masked), so no clamping.  A
+    // paged cache gets one resource per tile instead (see load_tile).
+    const int64_t head_off = PAGED ? 0 : uniform_i64(p.seq_offset[b]) + (int64_t)kh * p.stride_h;
     const char *kbase = (const char *)p.k + head_off * ES;
     const char *vbase = (const char *)p.v + head_off * ES;
     const uint32_t rs = (uint32_t)(p.stride_t * ES);
@@ -281,8 +287,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       return __builtin_bit_cast(i32x4_t, *(const u32x4_t *)(s_q + (dg * 16 + col) * kQDRow + 64 * kb + 16 * cg));
     };
 
-    // Positions of the current segment (IDX: its staged index list starts at seg_pos0).
-    int seg_pos0 = 0, seg_pos1 = 0;
+    // Positions of the current segment (IDX: its staged index list starts at
+    // seg_pos0; PAGED: its staged page ids start at page seg_page0).
+    int seg_pos0 = 0, seg_pos1 = 0, seg_page0 = 0;
     auto row_of = [&](int pos) -> int {
       if constexpr (IDX) return s_idx[min(pos, seg_pos1 - 1) - seg_pos0];
       return pos;
@@ -295,19 +302,33 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     auto load_tile = [&](TileT &R, int tile, bool valid) {
       const int tpos = (tile - lane_t0) * kTile;
       const uint32_t oob = valid ? 0u : 0x80000000u;
+      __amdgpu_buffer_rsrc_t tk = krs, tv = vrs;
+      int rshift = 0;  // row of position x in the resource: row_of(x) + rshift
+      if constexpr (PAGED) {
+        // page_tokens is a multiple of 32, so the tile lies in one page;
+        // rows of that page at or past L read as zero
+        const int pidx = tpos / p.page_tokens;
+        const int pg = __builtin_amdgcn_readfirstlane(s_pages[min(max(pidx - seg_page0, 0), kMaxSegPages - 1)]);
+        const int rows = min(p.page_tokens, L - pidx * p.page_tokens);
+        const int nrec_p = rows > 0 ? (int)((uint32_t)(rows - 1) * rs + D * ES) : 0;
+        const int64_t eoff = (int64_t)pg * p.page_stride + (int64_t)kh * p.stride_h;
+        tk = __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)p.k + eoff * ES), (short)0, nrec_p, 0x00020000);
+        tv = __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)p.v + eoff * ES), (short)0, nrec_p, 0x00020000);
+        rshift = -pidx * p.page_tokens;
+      }
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
-        const uint32_t off = ((uint32_t)row_of(tpos + 16 * tb + col) * rs + 16 * cg) | oob;
+        const uint32_t off = ((uint32_t)(row_of(tpos + 16 * tb + col) + rshift) * rs + 16 * cg) | oob;
 #pragma unroll
-        for (int kl = 0; kl < KL; ++kl) R.k[tb][kl] = __builtin_amdgcn_raw_buffer_load_b128(krs, off + 64 * kl, 0, 0);
+        for (int kl = 0; kl < KL; ++kl) R.k[tb][kl] = __builtin_amdgcn_raw_buffer_load_b128(tk, off + 64 * kl, 0, 0);
       }
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const int slot = (jj < 4) ? (4 * cg + jj) : (16 + 4 * cg + jj - 4);
-        const uint32_t off = ((uint32_t)row_of(tpos + slot) * rs + col * VW * 4) | oob;
-        if constexpr (VW == 4) R.v[jj] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
-        else if constexpr (VW == 2) R.v[jj] = __builtin_amdgcn_raw_buffer_load_b64(vrs, off, 0, 0);
-        else R.v[jj] = __builtin_amdgcn_raw_buffer_load_b32(vrs, off, 0, 0);
+        const uint32_t off = ((uint32_t)(row_of(tpos + slot) + rshift) * rs + col * VW * 4) | oob;
+        if constexpr (VW == 4) R.v[jj] = __builtin_amdgcn_raw_buffer_load_b128(tv, off, 0, 0);
+        else if constexpr (VW == 2) R.v[jj] = __builtin_amdgcn_raw_buffer_load_b64(tv, off, 0, 0);
+        else R.v[jj] = __builtin_amdgcn_raw_buffer_load_b32(tv, off, 0, 0);
       }
       if constexpr (KVT == ATTN_I8) {
         const int last = max(npos - 1, 0);
@@ -476,7 +497,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     constexpr int NBUF = StepT::NBUF;
     StepT buf[NBUF];
     auto seg_end_of = [&](int s0) { return min(run_end, lane_t0 + ((s0 - lane_t0) / ct + 1) * ct); };
-    if constexpr (!IDX) {
+    if constexpr (!IDX && !PAGED) {
       const int t1 = seg_end_of(t);
 #pragma unroll
       for (int j = 0; j + 1 < NBUF; ++j) load_step(buf[j], t + j * TPS, t1);
@@ -495,13 +516,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
         for (int j = 0; j + 1 < NBUF; ++j) load_step(buf[j], seg_t0 + j * TPS, seg_t1);
       }
+      if constexpr (PAGED) {
+        // the page ids of this segment's positions (at most kMaxSegPages)
+        seg_page0 = seg_pos0 / p.page_tokens;
+        const int npg = (seg_pos1 - 1) / p.page_tokens - seg_page0 + 1;
+        const int *tbl = p.block_table + (int64_t)b * p.table_stride + seg_page0;
+        __syncthreads();
+        for (int i = lane; i < min(npg, kMaxSegPages); i += 64) s_pages[i] = max(tbl[i], 0);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j + 1 < NBUF; ++j) load_step(buf[j], seg_t0 + j * TPS, seg_t1);
+      }
       const int nsteps = (seg_t1 - seg_t0 + TPS - 1) / TPS;
       const int steps = (nsteps + NBUF - 1) / NBUF * NBUF;
       const int next_t1 = seg_end_of(seg_t1);
       auto issue = [&](StepT &S, int s) {
         const bool in_seg = s < steps;
         const int tn = in_seg ? seg_t0 + s * TPS : seg_t1 + (s - steps) * TPS;
-        const int lim = in_seg ? seg_t1 : (IDX ? 0 : next_t1);
+        const int lim = in_seg ? seg_t1 : (IDX || PAGED ? 0 : next_t1);
         load_step(S, tn < lim ? tn : seg_t0, tn < lim ? lim : 0);
       };
       if constexpr (StepT::PIPE) {
@@ -566,27 +598,30 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
 }  // namespace
 
-template <bool IDX>
+template <bool IDX, bool PAGED>
 static void launch_variant(const DecodeParams &p, int kv_dtype, dim3 g, hipStream_t s) {
   dim3 blk(64);
   if (kv_dtype == ATTN_BF16) {
-    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_BF16, IDX, false>), g, blk, 0, s, p);
-    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_BF16, IDX, false>), g, blk, 0, s, p);
+    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_BF16, IDX, false, PAGED>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_BF16, IDX, false, PAGED>), g, blk, 0, s, p);
   } else if (p.q_quant == ATTN_QUANT_EXACT) {
-    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_I8, IDX, false>), g, blk, 0, s, p);
-    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_I8, IDX, false>), g, blk, 0, s, p);
+    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_I8, IDX, false, PAGED>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_I8, IDX, false, PAGED>), g, blk, 0, s, p);
   } else {
-    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_I8, IDX, true>), g, blk, 0, s, p);
-    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_I8, IDX, true>), g, blk, 0, s, p);
+    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_I8, IDX, true, PAGED>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_I8, IDX, true, PAGED>), g, blk, 0, s, p);
   }
 }
 
 hipError_t launch_decode_mfma(const DecodeParams &p, int kv_dtype, hipStream_t s) {
   if (p.token_idx) {
-    if (p.split > kMaxIdxChunk) return hipErrorInvalidValue;
-    launch_variant<true>(p, kv_dtype, dim3(p.grid), s);
+    if (p.split > kMaxIdxChunk || p.block_table) return hipErrorInvalidValue;
+    launch_variant<true, false>(p, kv_dtype, dim3(p.grid), s);
+  } else if (p.block_table) {
+    if (p.split > 64 * p.page_tokens) return hipErrorInvalidValue;
+    launch_variant<false, true>(p, kv_dtype, dim3(p.grid), s);
   } else {
-    launch_variant<false>(p, kv_dtype, dim3(p.grid), s);
+    launch_variant<false, false>(p, kv_dtype, dim3(p.grid), s);
   }
   return hipGetLastError();
 }

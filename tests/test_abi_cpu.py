@@ -164,3 +164,27 @@ def test_argument_structs_match_the_header_layout(tmp_path):
         assert got[(cname, "size")] == ctypes.sizeof(cls), cname
         for f in cls._fields_:
             assert got[(cname, f[0])] == getattr(cls, f[0]).offset, (cname, f[0])
+
+
+def test_paged_geometry_is_validated_and_limited_to_decode():
+    L = _lib.load()
+    paged = dict(g_block_table=FAKE, g_page_tokens=64, g_table_stride=64, g_page_stride=64 * 8 * 128,
+                 g_seq_offset=None)
+    assert _ws(_args(**paged))[0] == 0
+    assert _ws(_args(**paged, kv_dtype=_lib.ATTN_I8, k_scale=FAKE, k_part_tokens=64, k_scale_stride=64))[0] == 0
+    for over, status in ((dict(g_page_tokens=48), _lib.ATTN_ERR_INVALID_ARG),
+                         (dict(g_table_stride=63), _lib.ATTN_ERR_INVALID_ARG),
+                         (dict(g_page_stride=0), _lib.ATTN_ERR_INVALID_ARG),
+                         (dict(g_page_tokens=32, split_tokens=4096), _lib.ATTN_ERR_UNSUPPORTED),
+                         (dict(token_idx=FAKE, n_idx=FAKE, idx_stride=10), _lib.ATTN_ERR_UNSUPPORTED),
+                         (dict(q_dtype=_lib.ATTN_F32, kv_dtype=_lib.ATTN_F32), _lib.ATTN_ERR_UNSUPPORTED)):
+        a = _args(**{**paged, **over})
+        if "g_page_tokens" in over and over["g_page_tokens"] == 32:
+            a.kv.table_stride = 128
+        assert _ws(a)[0] == status, over
+    g = _lib.AttnKvGeom(2, 8, 128, 4096, FAKE, None, 128, 1024)
+    g.block_table, g.page_tokens, g.table_stride, g.page_stride = FAKE, 64, 64, 64 * 1024
+    assert L.kv_quant_int8(ctypes.byref(g), FAKE, 64, 64, FAKE, FAKE, None, 0, None) == _lib.ATTN_ERR_UNSUPPORTED
+    vlog = ctypes.c_void_p(FAKE)
+    assert L.oam_value_lognorm(ctypes.byref(g), FAKE, _lib.ATTN_BF16, 1.0, 1e-6, vlog, 4096, None) == \
+        _lib.ATTN_ERR_UNSUPPORTED

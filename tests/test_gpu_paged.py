@@ -1,0 +1,129 @@
+"""GPU parity of decode over a paged KV cache ("注意力优化" 结构 4, PagedAttention).
+
+The same logical cache is laid out contiguously and in a page pool with scrambled page
+order (token-major or head-major pages, NaN or random values in the unused rows of the last
+pages).  The work split depends only on the lengths, so the paged decode must reproduce the
+contiguous decode bit for bit; it is also compared with the fp64 oracle on the logical values.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_decode_gqa_amd as pkg
+import oracle
+import synth
+from gpu_helpers import DEV, dev_geom, log_case, problem, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def logical_rows(x, g, b, kh, L):
+    off = g.seq_offset[b] + kh * g.stride_h
+    return x[off + np.arange(L)[:, None] * g.stride_t + np.arange(g.D)[None, :]]
+
+
+def make_pool(x, g, P, layout, seed, junk):
+    """Page pool holding the logical rows of x (geometry g), its block table and strides."""
+    rng = np.random.default_rng(seed)
+    B, KH, D = g.B, g.KH, g.D
+    lens = [int(L) for L in g.lens]
+    need = [-(-L // P) for L in lens]
+    total = sum(need) + 3
+    perm = rng.permutation(total)
+    pool = np.full((total, P, KH, D) if layout == "token_major" else (total, KH, P, D), junk, dtype=x.dtype)
+    if x.dtype == np.int8:
+        pool[...] = rng.integers(-127, 128, size=pool.shape).astype(np.int8)
+    table = np.zeros((B, max(1, -(-int(g.max_len) // P))), np.int32)
+    table[...] = perm[-1]  # entries past a sequence's pages name a spare page
+    nxt = 0
+    for b in range(B):
+        if need[b] == 0:
+            continue
+        pages = perm[nxt:nxt + need[b]]
+        nxt += need[b]
+        table[b, :need[b]] = pages
+        for kh in range(KH):
+            rows = logical_rows(x, g, b, kh, lens[b])
+            full = (lens[b] // P) * P
+            if layout == "token_major":
+                pool[pages[:full // P], :, kh] = rows[:full].reshape(-1, P, D)
+                if full < lens[b]:
+                    pool[pages[-1], :lens[b] - full, kh] = rows[full:]
+            else:
+                pool[pages[:full // P], kh] = rows[:full].reshape(-1, P, D)
+                if full < lens[b]:
+                    pool[pages[-1], kh, :lens[b] - full] = rows[full:]
+    if layout == "token_major":
+        st, sh, ps = KH * D, D, P * KH * D
+    else:
+        st, sh, ps = D, P * D, KH * P * D
+    return pool.reshape(-1), table, st, sh, ps
+
+
+def paged_geom(g, table, P, st, sh, ps):
+    return pkg.KVGeometry(g.B, g.KH, g.D, int(g.max_len), torch.from_numpy(g.lens).to(DEV), None, sh, st,
+                          block_table=torch.from_numpy(table).to(DEV), page_tokens=P, page_stride=ps)
+
+
+def run(qd, k, v, geom, G, B, QH, **kw):
+    lse = torch.empty((B, QH), dtype=torch.float32, device=DEV)
+    out, _ = pkg.attn_decode_splitkv(qd, k, v, geom, G, lse=lse, **kw)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("P,layout", [(32, "token_major"), (64, "head_major"), (256, "token_major")])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "int8_qrow"])
+@pytest.mark.parametrize("D", [128, 64])
+def test_paged_equals_contiguous_bit_exact(P, layout, kv, D):
+    lens = np.array([1, 700, 4096, 2049, 0, 33], np.int32)
+    w = synth.workload("gqa32k", B=len(lens), KH=2, G=8, D=D, lens=lens, layout="token_major", seed=130 + P)
+    q, k, v, g = synth.generate(w)
+    log_case(f"paged P={P} {layout} {kv} D={D}")
+    qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
+    kw = dict(split_tokens=0)
+    if kv == "bf16":
+        kx, vx = k, v
+        junk = np.uint16(0x7FC0)  # NaN: rows past L must never be read
+    else:
+        geom_c = dev_geom(g)
+        kc, ks = pkg.kv_quant_int8(to_dev(k), geom_c, 64)
+        vc, vs = pkg.kv_quant_int8(to_dev(v), geom_c, 0)
+        torch.cuda.synchronize()
+        kx, vx = kc.cpu().numpy(), vc.cpu().numpy()
+        junk = np.int8(0)
+        kw.update(k_scale=ks, k_part_tokens=64, v_scale=float(vs.item()))
+        if kv == "int8_qrow":
+            kw["q_quant"] = pkg.QUANT_ROW
+    out_c, lse_c = run(qd, to_dev(kx), to_dev(vx), dev_geom(g), w.G, w.B, w.QH, **kw)
+    kp, table, st, sh, ps = make_pool(kx, g, P, layout, 7 + P, junk)
+    vp, _, _, _, _ = make_pool(vx, g, P, layout, 7 + P, junk)
+    out_p, lse_p = run(qd, to_dev(kp), to_dev(vp), paged_geom(g, table, P, st, sh, ps), w.G, w.B, w.QH, **kw)
+    assert np.isfinite(out_p).all()
+    np.testing.assert_array_equal(out_p, out_c)
+    np.testing.assert_array_equal(lse_p, lse_c)
+    if kv == "bf16":
+        p = problem(w, q, k, v, g)
+        ref, _ = oracle.attention_rows(p, oracle.all_rows(p), nthreads=8)
+        assert np.abs(out_p.reshape(-1, w.D) - ref).max() <= 2e-3
+
+
+def test_paged_128k_full_size_equals_contiguous():
+    """The 128K bf16 workload (4 x 8 KV heads x 131072 tokens) in a scrambled pool of 64-token
+    token-major pages, in the benchmark's launch configuration: bit-identical to the contiguous cache."""
+    w = synth.workload("dense128k")
+    q, k, v, g = synth.generate(w)
+    log_case("paged 128k full size")
+    qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
+    out_c, lse_c = run(qd, to_dev(k), to_dev(v), dev_geom(g), w.G, w.B, w.QH, split_tokens=w.split_tokens)
+    P = 64
+    kp, table, st, sh, ps = make_pool(k, g, P, "token_major", 11, np.uint16(0x7FC0))
+    del k
+    vp, _, _, _, _ = make_pool(v, g, P, "token_major", 11, np.uint16(0x7FC0))
+    del v
+    out_p, lse_p = run(qd, to_dev(kp), to_dev(vp), paged_geom(g, table, P, st, sh, ps), w.G, w.B, w.QH,
+                       split_tokens=w.split_tokens)
+    np.testing.assert_array_equal(out_p, out_c)
+    np.testing.assert_array_equal(lse_p, lse_c)
