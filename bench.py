@@ -237,10 +237,11 @@ def bench_int8(pkg, torch, synth, steps, warmup, dev):
     return dict(ms=ms, decode_ms=dk, merge_ms=mg, kv_bytes=kvb, split=effective_split(torch, w), schemes=schemes)
 
 
-def bench_paged(pkg, torch, synth, steps, warmup, dev, page_tokens=64):
+def bench_paged(pkg, torch, synth, steps, warmup, dev, page_tokens=64, layout="head_major"):
     """The 128K bf16 decode over a paged cache: the same K/V rows moved into a pool of
-    token-major pages ([pages][page_tokens][KH][D]) in scrambled order, read through a block
-    table.  Pool construction is setup, outside the timed region."""
+    head-major ([pages][KH][page_tokens][D]) or token-major ([pages][page_tokens][KH][D]) pages
+    in scrambled order, read through a block table.  Pool construction is setup, outside the
+    timed region."""
     w = synth.workload("dense128k")
     q, k, v, g = synth.generate(w, nthreads=host_threads())
     B, KH, D, L, P = w.B, w.KH, w.D, int(w.lens[0]), page_tokens
@@ -249,7 +250,11 @@ def bench_paged(pkg, torch, synth, steps, warmup, dev, page_tokens=64):
     perm = torch.randperm(B * npg, generator=gen).to(dev)
 
     def pool_of(x):
-        t = to_dev(torch, x, dev).view(B, KH, npg, P, D).permute(0, 2, 3, 1, 4).reshape(B * npg, P, KH, D)
+        t = to_dev(torch, x, dev).view(B, KH, npg, P, D)
+        if layout == "head_major":
+            t = t.permute(0, 2, 1, 3, 4).reshape(B * npg, KH, P, D)
+        else:
+            t = t.permute(0, 2, 3, 1, 4).reshape(B * npg, P, KH, D)
         pool = torch.empty_like(t)
         pool[perm] = t                      # logical page i of the batch lives at pool page perm[i]
         return pool.reshape(-1)
@@ -257,7 +262,8 @@ def bench_paged(pkg, torch, synth, steps, warmup, dev, page_tokens=64):
     kp, vp = pool_of(k), pool_of(v)
     del k, v
     table = perm.view(B, npg).to(torch.int32).contiguous()
-    geom = pkg.KVGeometry(B, KH, D, L, torch.full((B,), L, dtype=torch.int32, device=dev), None, D, KH * D,
+    stride_h, stride_t = (P * D, D) if layout == "head_major" else (D, KH * D)
+    geom = pkg.KVGeometry(B, KH, D, L, torch.full((B,), L, dtype=torch.int32, device=dev), None, stride_h, stride_t,
                           block_table=table, page_tokens=P, page_stride=P * KH * D)
     qd = to_dev(torch, q.reshape(-1), dev).view(w.B, w.QH, w.D)
     p = pkg.prepare_decode(qd, kp, vp, geom, w.G, split_tokens=w.split_tokens)
@@ -465,9 +471,10 @@ def main():
             except pkg.AttnError as e:
                 others["int8_128k"] = {"error": str(e)}
         if "paged" in todo:
-            r = bench_paged(pkg, torch, synth, max(5, K // 2), W, dev)
-            others["paged_128k_bf16"] = summary(r, {"page_tokens": 64})
-            del r
+            for lay in ("head_major", "token_major"):
+                r = bench_paged(pkg, torch, synth, max(5, K // 2), W, dev, layout=lay)
+                others[f"paged_128k_bf16_{lay}"] = summary(r, {"page_tokens": 64})
+                del r
         if "oam" in todo:
             try:
                 others["oam_128k"] = bench_oam(pkg, torch, synth, max(5, K // 2), W, dev)
