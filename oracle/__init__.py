@@ -8,6 +8,7 @@ the caller owns (bf16 is carried as uint16 bit patterns).
 from __future__ import annotations
 
 import ctypes
+import dataclasses
 import os
 import subprocess
 from dataclasses import dataclass
@@ -163,6 +164,29 @@ def attention_rows(p: Problem, rows: Sequence[tuple], nthreads: int = 1):
                                      int(nthreads))
     if rc:
         raise ValueError("oracle_attention_rows: invalid arguments")
+    return out, lse
+
+
+def attention_multirow(p: Problem, q_rows: int, rows: Sequence[tuple], nthreads: int = 1):
+    """Multi-row (speculative) decode, the NV blog's (1 + draft) x G GEMM-M: ``p.q`` is
+    [B, R, KH*G, D] (int8 ``q_scale`` then [B, R, KH*G]); the R query tokens are the last R tokens
+    of each cache, so row (b, r, qh) attends to the first L_b - (R - 1) + r tokens (itself and
+    what precedes it).  Each row is the plain definition on that prefix.  rows: (b, r, qh)."""
+    R = int(q_rows)
+    out = np.zeros((len(rows), p.D), dtype=np.float64)
+    lse = np.zeros(len(rows), dtype=np.float64)
+    q = np.asarray(p.q).reshape(p.B, R, p.KH * p.G, p.D)
+    for r in range(R):
+        sel = [i for i, row in enumerate(rows) if row[1] == r]
+        if not sel:
+            continue
+        lens_r = np.maximum(np.asarray(p.lens, np.int64) - (R - 1) + r, 0).astype(np.int32)
+        qs = None if p.q_scale is None else np.ascontiguousarray(
+            np.asarray(p.q_scale).reshape(p.B, R, p.KH * p.G)[:, r]).reshape(-1)
+        pr = dataclasses.replace(p, q=np.ascontiguousarray(q[:, r]), lens=lens_r, q_scale=qs)
+        o, l = attention_rows(pr, [(rows[i][0], rows[i][2]) for i in sel], nthreads)
+        out[sel] = o
+        lse[sel] = l
     return out, lse
 
 

@@ -17,6 +17,7 @@ import pytest
 from scipy.special import logsumexp, softmax
 
 import oracle
+import synth
 from helpers import dense_problem, random_dense, with_tokens
 
 
@@ -180,3 +181,49 @@ def test_bf16_inputs_are_read_exactly():
     b = oracle.attention_rows(p32, oracle.all_rows(p32))
     np.testing.assert_array_equal(a[0], b[0])
     np.testing.assert_array_equal(a[1], b[1])
+
+
+# --- multi-row (speculative) decode: the NV blog's (1 + draft) x G GEMM-M ---
+
+
+def test_multirow_hand_worked(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "multirow_hand_example.json")))
+    L, R, D = g["L"], g["R"], g["D"]
+    q = np.zeros((1, R, 1, D), np.float32)
+    k = np.array([[1.0, 2.0], [-4.0, 0.5], [7.0, 7.0]], np.float32).reshape(1, 1, L, D)
+    v = np.array(g["v"], np.float32).reshape(1, 1, L, D)
+    p = dense_problem(np.ascontiguousarray(q[:, 0]), k, v)   # G = 1 query head per KV head
+    p.q = q
+    out, lse = oracle.attention_multirow(p, R, [(0, 0, 0), (0, 1, 0)])
+    np.testing.assert_allclose(out, g["out"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, g["lse"], rtol=0, atol=1e-12)
+
+
+def test_multirow_one_row_is_plain_decode_and_last_row_sees_everything():
+    B, KH, G, D, L, R = 2, 2, 4, 32, 90, 3
+    q, k, v = random_dense(75, B, KH, G * R, D, L, fmt=synth.BF16)  # q values reshaped to [B, R, KH*G, D]
+    qr = np.ascontiguousarray(q.reshape(B, R, KH * G, D))
+    p = dense_problem(np.ascontiguousarray(qr[:, 0]), k, v)
+    p.q = qr
+    rows = [(b, r, qh) for b in range(B) for r in range(R) for qh in range(KH * G)]
+    out, lse = oracle.attention_multirow(p, R, rows)
+    # the last row attends to the whole cache: the plain definition with that row's query
+    plast = dense_problem(np.ascontiguousarray(qr[:, R - 1]), k, v)
+    o2, l2 = oracle.attention_rows(plast, oracle.all_rows(plast))
+    last = [i for i, r in enumerate(rows) if r[1] == R - 1]
+    np.testing.assert_allclose(out[last], o2, rtol=0, atol=1e-12)
+    # one row: identical to attention_rows
+    p1 = dense_problem(np.ascontiguousarray(qr[:, 0]), k, v)
+    o1, l1 = oracle.attention_multirow(p1, 1, [(b, 0, qh) for b in range(B) for qh in range(KH * G)])
+    o0, l0 = oracle.attention_rows(p1, oracle.all_rows(p1))
+    np.testing.assert_array_equal(o1, o0)
+    # row r sees the first L - (R - 1) + r tokens: the same row over a cache cut to that prefix and
+    # asked as the last of R rows gives the same result
+    for r in range(R - 1):
+        cut = L - (R - 1) + r
+        pc = dense_problem(np.ascontiguousarray(qr[:, 0]), np.ascontiguousarray(k[:, :, :cut]),
+                           np.ascontiguousarray(v[:, :, :cut]))
+        pc.q = np.ascontiguousarray(np.concatenate([qr[:, r:r + 1]] * R, axis=1))
+        oc, _ = oracle.attention_multirow(pc, R, [(b, R - 1, qh) for b in range(B) for qh in range(KH * G)])
+        rr = [i for i, x in enumerate(rows) if x[1] == r]
+        np.testing.assert_allclose(out[rr], oc, rtol=0, atol=1e-12)
