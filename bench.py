@@ -8,8 +8,8 @@ attn_decode_splitkv call (decode kernel + merge) over inputs already resident
 in HBM.  Prints one JSON line: KV GB/s (value), us/step, fraction of HBM peak,
 the roofline of the decode kernel, the CPU oracle baseline and, unless
 --headline-only, the other workloads (32K GQA, ragged batch, INT8 KV and its
-scheme table, a paged cache, OAM token dropping on bf16 and INT8 caches, and
-block-granular selection).
+scheme table, a paged cache, multi-row speculative steps, OAM token dropping
+on bf16 and INT8 caches, and block-granular selection).
 """
 from __future__ import annotations
 
@@ -272,6 +272,22 @@ def bench_paged(pkg, torch, synth, steps, warmup, dev, page_tokens=64, layout="h
                 split=effective_split(torch, w))
 
 
+def bench_multirow(pkg, torch, synth, steps, warmup, dev, R):
+    """The 128K bf16 decode with R query rows per sequence (speculative verification: each step
+    checks R tokens).  Same K/V bytes as one row; G * R rows of a KV head share each load."""
+    w = synth.workload("dense128k")
+    _, k, v, g = synth.generate(w, nthreads=host_threads())
+    geom = dev_geom(pkg, torch, g, dev)
+    kd, vd = to_dev(torch, k, dev), to_dev(torch, v, dev)
+    del k, v
+    q = synth.fill_q(151, w.B, R * w.QH, w.D, synth.BF16)
+    qd = to_dev(torch, q.reshape(-1), dev).view(w.B, R, w.QH, w.D)
+    p = pkg.prepare_decode(qd, kd, vd, geom, w.G, split_tokens=w.split_tokens, q_rows=R)
+    ms, dk, mg = time_decode(torch, p, steps, warmup)
+    return dict(ms=ms, decode_ms=dk, merge_ms=mg, kv_bytes=kv_bytes(w.kv_tokens(), w.KH, w.D, 2),
+                split=effective_split(torch, w))
+
+
 def bench_oam(pkg, torch, synth, steps, warmup, dev):
     """OAM step: score + exact top-K over the cached value log-norms, then exact
     attention over the kept tokens.  Also times the variant that reads V to get
@@ -391,7 +407,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--headline-only", action="store_true")
-    ap.add_argument("--others", default="gqa32k,ragged,int8,oam,paged",
+    ap.add_argument("--others", default="gqa32k,ragged,int8,oam,paged,multirow",
                     help="comma-separated other workloads to time after the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -470,6 +486,12 @@ def main():
                 others["int8_128k_schemes"] = r["schemes"]
             except pkg.AttnError as e:
                 others["int8_128k"] = {"error": str(e)}
+        if "multirow" in todo:
+            for R in (2, 4):
+                r = bench_multirow(pkg, torch, synth, max(5, K // 2), W, dev, R)
+                others[f"multirow_128k_bf16_R{R}"] = summary(r, {"query_rows": R,
+                                                                 "us_per_query_row": round(r["ms"] * 1e3 / R, 2)})
+                del r
         if "paged" in todo:
             for lay in ("head_major", "token_major"):
                 r = bench_paged(pkg, torch, synth, max(5, K // 2), W, dev, layout=lay)

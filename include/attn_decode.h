@@ -120,6 +120,14 @@ typedef struct {
 /*
  * Arguments of one decode step.
  *   G           query heads per KV head, 1 <= G <= 64
+ *   q_rows      query rows per sequence R (0 or 1: one).  R > 1 is the
+ *               multi-row step of speculative decoding (NVIDIA blog, GEMM
+ *               shapes: with D draft tokens GEMM-M = (1 + D) x G): the R query
+ *               tokens are the last R tokens of each cache, so row r attends
+ *               to the first L_b - (R - 1) + r tokens.  q, out and lse are
+ *               then [B][R][KH*G][...].  R*G <= 64, bf16 or int8 KV, no
+ *               token_idx.  The R*G rows of a KV head share each K/V load
+ *               (G = 8, R = 2 fill the 16 matrix-core columns)
  *   q           [B][KH*G][D] in q_dtype (ATTN_BF16, or ATTN_F32 with fp32 KV);
  *               with ATTN_I8 KV the int8 matrix cores take each head's q as
  *               a 22-bit fixed-point value with its own scale (max|q_g| /
@@ -161,6 +169,7 @@ typedef struct {
 typedef struct {
   attn_kv_geom kv;
   int32_t G;
+  int32_t q_rows;
   int32_t q_dtype, kv_dtype, out_dtype;
   const void *q;
   const void *k;

@@ -90,10 +90,12 @@ class KVGeometry:
 
 
 def _decode_args(q, k, v, geom: KVGeometry, G, out, lse, k_scale, k_part_tokens, k_scale_stride, v_scale,
-                 token_idx, n_idx, idx_stride, softmax_scale, split_tokens, workspace, q_quant=0, q_scale=0.0):
+                 token_idx, n_idx, idx_stride, softmax_scale, split_tokens, workspace, q_quant=0, q_scale=0.0,
+                 q_rows=1):
     a = _lib.AttnDecodeArgs()
     a.kv = geom.c()
     a.G = G
+    a.q_rows = q_rows
     a.q_dtype, a.kv_dtype, a.out_dtype = _code(q), _code(k), _code(out)
     a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
     a.k_scale = _ptr(k_scale)
@@ -141,24 +143,26 @@ def prepare_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, geom: KVGe
                    k_part_tokens: int = 64, k_scale_stride: Optional[int] = None, v_scale: float = 1.0,
                    token_idx: Optional[torch.Tensor] = None, n_idx: Optional[torch.Tensor] = None,
                    idx_stride: Optional[int] = None, softmax_scale: float = 0.0, split_tokens: int = 0,
-                   q_quant: int = 0, q_scale: float = 0.0,
+                   q_quant: int = 0, q_scale: float = 0.0, q_rows: int = 1,
                    workspace: Optional[torch.Tensor] = None) -> PreparedDecode:
     """Build (and allocate outputs/workspace for) one ``attn_decode_splitkv`` call.
 
     With int8 KV, ``k_part_tokens=0`` selects one per-tensor K scale (``k_scale[0]``) and
     ``q_quant`` (QUANT_EXACT / QUANT_ROW / QUANT_STATIC, with ``q_scale``) how the query is
-    quantised."""
+    quantised.  ``q_rows`` > 1 is a multi-row (speculative) step: q, out and lse are
+    [B, q_rows, KH*G, ...] and row r attends to the first L - (q_rows - 1) + r tokens."""
     dev = q.device
     QH = geom.KH * G
     if out is None:
-        out = torch.empty((geom.B, QH, geom.D), dtype=out_dtype, device=dev)
+        shape = (geom.B, QH, geom.D) if q_rows <= 1 else (geom.B, q_rows, QH, geom.D)
+        out = torch.empty(shape, dtype=out_dtype, device=dev)
     if k_scale_stride is None:
         k_scale_stride = (max(1, -(-geom.max_seq_len // k_part_tokens))
                           if k_scale is not None and k_part_tokens > 0 else 0)
     if token_idx is not None and idx_stride is None:
         idx_stride = token_idx.shape[-1]
     a = _decode_args(q, k, v, geom, G, out, lse, k_scale, k_part_tokens, k_scale_stride, v_scale, token_idx, n_idx,
-                     idx_stride or 0, softmax_scale, split_tokens, None, q_quant, q_scale)
+                     idx_stride or 0, softmax_scale, split_tokens, None, q_quant, q_scale, q_rows)
     need = decode_workspace_size(a)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)

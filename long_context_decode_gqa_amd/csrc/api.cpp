@@ -92,9 +92,14 @@ attn_status plan_decode(const attn_decode_args *a, DecodeLayout *L) {
   attn_status st = check_geom(g, elem_size(a->kv_dtype), true);
   if (st != ATTN_OK) return st;
   if (a->G < 1 || a->G > 64) return fail(ATTN_ERR_UNSUPPORTED, "G must be in [1, 64]");
+  const int R = a->q_rows > 1 ? a->q_rows : 1;
+  if (a->q_rows < 0 || (int64_t)R * a->G > 64)
+    return fail(ATTN_ERR_UNSUPPORTED, "q_rows must be >= 0 with q_rows * G <= 64");
   const bool mfma = a->kv_dtype != ATTN_F32;
   if (g.block_table && (!mfma || a->token_idx))
     return fail(ATTN_ERR_UNSUPPORTED, "a paged cache needs bf16 or int8 KV and no token_idx");
+  if (R > 1 && (!mfma || a->token_idx))
+    return fail(ATTN_ERR_UNSUPPORTED, "q_rows > 1 needs bf16 or int8 KV and no token_idx");
   if (mfma && g.D != 64 && g.D != 128)
     return fail(ATTN_ERR_UNSUPPORTED, "bf16/int8 KV supports head size D = 64 or 128");
   if (!mfma && (g.D < 4 || g.D > 256 || g.D % 4))
@@ -129,7 +134,7 @@ attn_status plan_decode(const attn_decode_args *a, DecodeLayout *L) {
       return fail(ATTN_ERR_INVALID_ARG, "q, k and v must be 16-byte aligned");
   }
   L->mfma = mfma;
-  L->ngb = (a->G + 15) / 16;
+  L->ngb = (R * a->G + 15) / 16;
   L->max_tokens = a->token_idx ? a->idx_stride : g.max_seq_len;
   if (a->split_tokens) {
     L->split = a->split_tokens;
@@ -151,7 +156,7 @@ attn_status plan_decode(const attn_decode_args *a, DecodeLayout *L) {
   if (g.block_table && (int64_t)L->split > 64 * (int64_t)g.page_tokens)
     return fail(ATTN_ERR_UNSUPPORTED, "with a paged cache, split_tokens must be <= 64 * page_tokens");
   L->max_chunks = ((int64_t)L->max_tokens + L->split - 1) / L->split;
-  const int64_t QH = (int64_t)g.KH * a->G;
+  const int64_t QH = (int64_t)g.KH * a->G * R;
   L->max_partials = 2 * (int64_t)g.B * QH * L->max_chunks;
   const int64_t nlanes = (int64_t)g.B * g.KH * L->ngb;
   const int64_t max_tiles = nlanes * (((int64_t)L->max_tokens + 31) / 32);
@@ -212,9 +217,11 @@ static attn_status decode_impl(const attn_decode_args *a, attn_stream_t stream, 
   DecodeParams p;
   p.B = a->kv.B;
   p.KH = a->kv.KH;
-  p.G = a->G;
+  p.R = a->q_rows > 1 ? a->q_rows : 1;
+  p.Gq = a->G;
+  p.G = a->G * p.R;
   p.D = a->kv.D;
-  p.QH = a->kv.KH * a->G;
+  p.QH = a->kv.KH * p.G;
   p.ngb = L.ngb;
   p.seq_lens = a->kv.seq_lens;
   p.seq_offset = a->kv.seq_offset;

@@ -92,7 +92,9 @@ struct WorkList {
 };
 
 struct DecodeParams {
+  // G: query rows per KV head (the matrix-core columns), R * Gq; QH = KH * G
   int32_t B, KH, G, D, QH, ngb;
+  int32_t Gq, R;  // query heads per KV head, query rows per sequence
   const int32_t *seq_lens;
   const int64_t *seq_offset;
   int64_t stride_h, stride_t;
@@ -114,6 +116,12 @@ struct DecodeParams {
   int32_t grid;         // workgroups launched for the decode kernel
   WorkList wl;
 };
+
+// Row of q/out/lse ([B][R][KH*Gq]) of column gc (= r*Gq + g) of KV head kh.
+__device__ __forceinline__ int64_t q_row_index(const DecodeParams &p, int b, int kh, int gc) {
+  const int r = gc / p.Gq, g = gc - r * p.Gq;
+  return ((int64_t)(b * p.R + r) * p.KH + kh) * p.Gq + g;
+}
 
 // A "lane" is (b, kh, query-head block of up to 16 heads): lane q belongs to
 // pair q / ngb = b*KH + kh and covers ceil(n / 32) tiles of 32 positions,

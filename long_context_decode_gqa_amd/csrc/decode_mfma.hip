@@ -164,6 +164,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const int g0 = gb * 16;
     const int gcount = min(16, p.G - g0);
     const bool qvalid = col < gcount;
+    // with R query rows per sequence, column g0 + col is row r = (g0 + col) / Gq,
+    // the token at position L - R + r: it sees the first L - (R - 1) + r tokens
+    const int col_end = p.R > 1 ? L - (p.R - 1) + (g0 + col) / p.Gq : 0x7FFFFFFF;
 
     // Buffer resources over this (b, kh)'s rows: 32-bit offsets, and rows at
     // or past L read as zero (their scores are masked), so no clamping.  A
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     if constexpr (KVT == ATTN_I8) {
       constexpr int CPL = D / 4;  // lane (col, cg) takes head col, channels [cg*CPL, cg*CPL + CPL)
       float qv[CPL];
-      const uint16_t *qrow = (const uint16_t *)p.q + ((int64_t)b * p.QH + (int64_t)kh * p.G + g0 + col) * D + cg * CPL;
+      const uint16_t *qrow = (const uint16_t *)p.q + q_row_index(p, b, kh, g0 + col) * D + cg * CPL;
 #pragma unroll
       for (int x = 0; x < CPL / 8; ++x) {
         u32x4_t w = (u32x4_t){0u, 0u, 0u, 0u};
@@ -272,7 +275,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         const int g = e / (D / 8), c8 = e - g * (D / 8);
         u32x4_t w = (u32x4_t){0u, 0u, 0u, 0u};
         if (g < gcount)
-          w = *(const u32x4_t *)((const uint16_t *)p.q + ((int64_t)b * p.QH + (int64_t)kh * p.G + g0 + g) * D + 8 * c8);
+          w = *(const u32x4_t *)((const uint16_t *)p.q + q_row_index(p, b, kh, g0 + g) * D + 8 * c8);
         *(u32x4_t *)(s_q + g * kQRow + 16 * c8) = w;
       }
     }
@@ -404,6 +407,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // Online softmax and P.V of a tile whose raw scores are given.
     auto finish_tile = [&](const TileT &R, int tile, const Raw &raw) {
       const int tpos = (tile - lane_t0) * kTile;
+      const int lim = min(seg_pos1, col_end);
       float s[8];
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
@@ -412,7 +416,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
           const int pos = tpos + 16 * tb + 4 * cg + i;
           float sc = c1;
           if constexpr (KVT == ATTN_I8) sc *= qs * (IDX ? R.ks[4 * tb + i] : R.ks[tb]);
-          s[4 * tb + i] = (pos < seg_pos1) ? raw.v[4 * tb + i] * sc : NEG_INF;
+          s[4 * tb + i] = (pos < lim) ? raw.v[4 * tb + i] * sc : NEG_INF;
         }
       float mt = s[0];
 #pragma unroll

@@ -75,6 +75,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *o_par
   __shared__ int s_sl[kMergeWeights];
   __shared__ float s_acc[kMergeThreads * 4];
   const int row = blockIdx.x;
+  // decode partials are laid out per (pair, column); the output row of a
+  // column follows q's layout ([B][R][KH*Gq])
+  int64_t orow = row;
+  if constexpr (DECODE) {
+    const int pair = row / dp.G;
+    orow = q_row_index(dp, pair / dp.KH, pair % dp.KH, row - pair * dp.G);
+  }
   const int tid = threadIdx.x;
   const float NEG_INF = -__builtin_huge_valf();
   int s0, n, ss;
@@ -127,12 +134,12 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *o_par
     for (int g = 0; g < ngrp; ++g) acc += s_acc[g * D + d];
     const float o = (Ls > 0.f) ? acc / Ls : 0.f;
     if constexpr (OUT == ATTN_F32) {
-      ((float *)out)[(int64_t)row * D + d] = o;
+      ((float *)out)[orow * D + d] = o;
     } else {
-      ((uint16_t *)out)[(int64_t)row * D + d] = (uint16_t)f32_to_bf16_bits(o);
+      ((uint16_t *)out)[orow * D + d] = (uint16_t)f32_to_bf16_bits(o);
     }
   }
-  if (tid == 0 && lse) lse[row] = (Ls > 0.f) ? M + logf(Ls) : NEG_INF;
+  if (tid == 0 && lse) lse[orow] = (Ls > 0.f) ? M + logf(Ls) : NEG_INF;
 }
 
 // Single-pass merge for D % 4 == 0, one 256-thread workgroup per row.
@@ -151,6 +158,13 @@ __global__ __launch_bounds__(kMergeV4Threads) void merge_v4_kernel(const float *
   __shared__ f32x4_t s_acc[kMergeV4Threads];
   __shared__ float s_m[kMergeV4Threads], s_l[kMergeV4Threads];
   const int row = blockIdx.x;
+  // decode partials are laid out per (pair, column); the output row of a
+  // column follows q's layout ([B][R][KH*Gq])
+  int64_t orow = row;
+  if constexpr (DECODE) {
+    const int pair = row / dp.G;
+    orow = q_row_index(dp, pair / dp.KH, pair % dp.KH, row - pair * dp.G);
+  }
   const int tid = threadIdx.x;
   const float NEG_INF = -__builtin_huge_valf();
   int s0, n, ss;
@@ -210,15 +224,15 @@ __global__ __launch_bounds__(kMergeV4Threads) void merge_v4_kernel(const float *
     const float inv = Ls > 0.f ? 1.0f / Ls : 0.f;
     const f32x4_t r = a * inv;
     if constexpr (OUT == ATTN_F32) {
-      *(f32x4_t *)((float *)out + (int64_t)row * D + 4 * q) = r;
+      *(f32x4_t *)((float *)out + orow * D + 4 * q) = r;
     } else {
-      uint16_t *po = (uint16_t *)out + (int64_t)row * D + 4 * q;
+      uint16_t *po = (uint16_t *)out + orow * D + 4 * q;
       const uint32_t w0 = f32_to_bf16_bits(r[0]) | (f32_to_bf16_bits(r[1]) << 16);
       const uint32_t w1 = f32_to_bf16_bits(r[2]) | (f32_to_bf16_bits(r[3]) << 16);
       *(uint32_t *)po = w0;
       *(uint32_t *)(po + 2) = w1;
     }
-    if (q == 0 && lse) lse[row] = Ls > 0.f ? M + logf(Ls) : NEG_INF;
+    if (q == 0 && lse) lse[orow] = Ls > 0.f ? M + logf(Ls) : NEG_INF;
   }
 }
 

@@ -1,0 +1,97 @@
+"""GPU parity of multi-row (speculative) decode: R query rows per sequence (the NVIDIA blog's
+GEMM-M = (1 + draft) x G); row r attends to the first L - (R - 1) + r tokens.
+
+Outputs against the fp64 oracle (2e-3, lse 1e-3, -inf for rows that see no token); and, as the
+matrix-core columns are independent and the work split does not change, the last row of an R-row
+step equals the one-row decode of that query bit for bit when both use one column block.
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_decode_gqa_amd as pkg
+import oracle
+import synth
+from gpu_helpers import DEV, dev_geom, log_case, problem, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def multirow_q(w, R, seed):
+    q = synth.fill_q(seed, w.B, R * w.QH, w.D, synth.BF16)
+    return np.ascontiguousarray(q.reshape(w.B, R, w.QH, w.D))
+
+
+def run(w, q, k, v, g, R, **kw):
+    qd = to_dev(q.reshape(-1)).view(w.B, R, w.QH, w.D) if R > 1 else to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
+    lse = torch.empty((w.B, R, w.QH) if R > 1 else (w.B, w.QH), dtype=torch.float32, device=DEV)
+    out, _ = pkg.attn_decode_splitkv(qd, k, v, dev_geom(g), w.G, lse=lse, q_rows=R, **kw)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("R,G,D", [(2, 8, 128), (4, 4, 128), (2, 16, 64), (3, 8, 64), (8, 8, 128)])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "int8_qrow"])
+def test_multirow_against_oracle(R, G, D, kv):
+    lens = np.array([1, 2, 700, 4096, 0, 2049, 5], np.int32)
+    w = synth.workload("gqa32k", B=len(lens), KH=2, G=G, D=D, lens=lens, layout="token_major", seed=140 + R + G)
+    _, k, v, g = synth.generate(w)
+    q = multirow_q(w, R, 141 + R)
+    log_case(f"multirow R={R} G={G} D={D} {kv}")
+    kw, pk = dict(split_tokens=0), {}
+    if kv == "bf16":
+        kd, vd, kh_, vh_ = to_dev(k), to_dev(v), k, v
+    else:
+        geom = dev_geom(g)
+        kd, ks = pkg.kv_quant_int8(to_dev(k), geom, 64)
+        vd, vs = pkg.kv_quant_int8(to_dev(v), geom, 0)
+        torch.cuda.synchronize()
+        kh_, vh_ = kd.cpu().numpy(), vd.cpu().numpy()
+        kw.update(k_scale=ks, k_part_tokens=64, v_scale=float(vs.item()))
+        pk = dict(k_scale=ks.cpu().numpy(), k_part=64, k_scale_stride=-(-int(g.max_len) // 64),
+                  v_scale=float(vs.item()))
+    qo = q
+    if kv == "int8_qrow":
+        kw["q_quant"] = pkg.QUANT_ROW
+        qc, qs = oracle.quant_rows(q.reshape(-1, w.D))
+        qo, pk["q_scale"] = qc.reshape(q.shape), qs
+    out, lse = run(w, q, kd, vd, g, R, **kw)
+    p = problem(w, np.ascontiguousarray(qo[:, 0]), kh_, vh_, g, **pk)
+    p.q = qo
+    rows = [(b, r, qh) for b in range(w.B) for r in range(R) for qh in range(w.QH)]
+    ref, ref_lse = oracle.attention_multirow(p, R, rows, nthreads=8)
+    out = out.reshape(-1, w.D)
+    lse = lse.reshape(-1)
+    assert np.abs(out - ref).max() <= 2e-3
+    fin = np.isfinite(ref_lse)
+    assert np.all(np.isneginf(lse[~fin]))
+    assert np.abs(lse[fin] - ref_lse[fin]).max() <= 1e-3
+    if R * G <= 16:
+        # the last row sees the whole cache: the one-row decode of that query, bit for bit
+        q1 = np.ascontiguousarray(q[:, R - 1])
+        o1, l1 = run(w, q1, kd, vd, g, 1, **kw)
+        np.testing.assert_array_equal(out.reshape(w.B, R, w.QH, w.D)[:, R - 1], o1)
+        np.testing.assert_array_equal(lse.reshape(w.B, R, w.QH)[:, R - 1], l1)
+
+
+def test_multirow_128k_full_size():
+    """R = 2 at the 128K bf16 shape (4 x 8 KV heads x 131072, G = 8: the 16 matrix-core columns are
+    full), in the benchmark's configuration: sampled rows against the oracle, the last row bit-exact
+    against the one-row decode."""
+    w = synth.workload("dense128k")
+    _, k, v, g = synth.generate(w)
+    R = 2
+    q = multirow_q(w, R, 150)
+    log_case("multirow 128k full size")
+    kd, vd = to_dev(k), to_dev(v)
+    out, lse = run(w, q, kd, vd, g, R, split_tokens=w.split_tokens)
+    o1, l1 = run(w, np.ascontiguousarray(q[:, 1]), kd, vd, g, 1, split_tokens=w.split_tokens)
+    np.testing.assert_array_equal(out[:, 1], o1)
+    np.testing.assert_array_equal(lse[:, 1], l1)
+    p = problem(w, np.ascontiguousarray(q[:, 0]), k, v, g)
+    p.q = q
+    rows = [(0, 0, 0), (3, 0, 63), (1, 0, 17), (2, 1, 40), (0, 1, 5)]
+    ref, ref_lse = oracle.attention_multirow(p, R, rows, nthreads=16)
+    got = np.stack([out[b, r, qh] for b, r, qh in rows])
+    assert np.abs(got - ref).max() <= 2e-3
+    assert np.abs(np.array([lse[b, r, qh] for b, r, qh in rows]) - ref_lse).max() <= 1e-3
