@@ -388,8 +388,10 @@ def cpu_baseline(r, budget_s=10.0):
     per_batch = max(1, n // w.G)
     done = 0
     t0 = time.perf_counter()
-    while done < len(pairs) and time.perf_counter() - t0 < budget_s:
-        batch = pairs[done:done + per_batch]
+    # batches of whole (b, kh) pairs, cycling over the workload until about budget_s of CPU work
+    while time.perf_counter() - t0 < budget_s:
+        i0 = done % len(pairs)
+        batch = pairs[i0:i0 + per_batch]
         rows = [(b, kh * w.G + gq) for b, kh in batch for gq in range(w.G)]
         oracle.attention_rows(p, rows, nthreads=n)
         done += len(batch)
@@ -397,8 +399,9 @@ def cpu_baseline(r, budget_s=10.0):
     bytes_done = kv_bytes(int(w.lens[0]) * done, 1, w.D, 2)
     return {"value": round(bytes_done / dt / 1e9, 3), "unit": "GB/s", "cores": n, "kind": "oracle",
             "seconds": round(dt, 2), "us_per_step_equiv": round(dt / done * len(pairs) * 1e6, 1),
-            "sample": f"{done} of {len(pairs)} (sequence, KV head) pairs of the 128K bf16 workload, "
-                      f"all {w.G} query heads each, fp64 oracle on {n} host threads"}
+            "sample": f"{done} (sequence, KV head) pair passes ({done / len(pairs):.1f} sweeps of the "
+                      f"{len(pairs)} pairs) of the 128K bf16 workload, all {w.G} query heads each, fp64 oracle "
+                      f"on {n} host threads, about {budget_s:.0f} s"}
 
 
 def main():
