@@ -490,7 +490,7 @@ def main():
             except pkg.AttnError as e:
                 others["int8_128k"] = {"error": str(e)}
         if "multirow" in todo:
-            for R in (2, 4):
+            for R in (2, 4, 8):
                 r = bench_multirow(pkg, torch, synth, max(5, K // 2), W, dev, R)
                 others[f"multirow_128k_bf16_R{R}"] = summary(r, {"query_rows": R,
                                                                  "us_per_query_row": round(r["ms"] * 1e3 / R, 2)})

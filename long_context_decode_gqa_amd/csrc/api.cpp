@@ -74,6 +74,7 @@ struct DecodeLayout {
   size_t m, l, o, total;
   int64_t max_partials, max_chunks;
   int32_t split, ngb, max_tokens;
+  int32_t cols;  // matrix-core columns per decode worker (16, or 32 for more than 16 rows per KV head)
   bool mfma;
 };
 
@@ -134,7 +135,11 @@ attn_status plan_decode(const attn_decode_args *a, DecodeLayout *L) {
       return fail(ATTN_ERR_INVALID_ARG, "q, k and v must be 16-byte aligned");
   }
   L->mfma = mfma;
-  L->ngb = (R * a->G + 15) / 16;
+  // More than 16 query rows per KV head: each worker computes 32 columns
+  // (two blocks sharing every K/V load) instead of streaming the cache once
+  // per 16-column block.
+  L->cols = (mfma && R * a->G > 16) ? 32 : 16;
+  L->ngb = (R * a->G + L->cols - 1) / L->cols;
   L->max_tokens = a->token_idx ? a->idx_stride : g.max_seq_len;
   if (a->split_tokens) {
     L->split = a->split_tokens;
@@ -142,11 +147,13 @@ attn_status plan_decode(const attn_decode_args *a, DecodeLayout *L) {
     L->split = 256;
   } else {
     // About one chunk per worker of a full decode grid (2048 one-wave
-    // workers on a 256-CU device): each worker then writes about one partial
-    // per head, and partial writes cost far more HBM time than their bytes
-    // while the KV stream runs.  32..2048 tokens (1024 with an index list).
+    // workers on a 256-CU device, 1024 for 32-column workers): each worker
+    // then writes about one partial per column, and partial writes cost far
+    // more HBM time than their bytes while the KV stream runs.  32..2048
+    // tokens (1024 with an index list).
     const int64_t tiles = (int64_t)g.B * g.KH * L->ngb * (((int64_t)L->max_tokens + 31) / 32);
-    const int64_t ct = std::min<int64_t>(std::max<int64_t>(tiles / 2048, 1), a->token_idx ? 32 : 64);
+    const int64_t workers = L->cols == 32 ? 1024 : 2048;
+    const int64_t ct = std::min<int64_t>(std::max<int64_t>(tiles / workers, 1), a->token_idx ? 32 : 64);
     L->split = (int32_t)(32 * ct);
   }
   if (mfma && ((int64_t)g.max_seq_len + 64) * g.stride_t * elem_size(a->kv_dtype) >= (int64_t(1) << 31))
@@ -223,6 +230,7 @@ static attn_status decode_impl(const attn_decode_args *a, attn_stream_t stream, 
   p.D = a->kv.D;
   p.QH = a->kv.KH * p.G;
   p.ngb = L.ngb;
+  p.cols_per_wave = L.cols;
   p.seq_lens = a->kv.seq_lens;
   p.seq_offset = a->kv.seq_offset;
   p.stride_h = a->kv.stride_h;
@@ -250,11 +258,12 @@ static attn_status decode_impl(const attn_decode_args *a, attn_stream_t stream, 
   p.max_chunks = (int32_t)L.max_chunks;
   {
     // persistent grid: the MFMA kernel runs one-wave workers, eight per compute
-    // unit (two per SIMD, its register budget); the vector-ALU kernel four
-    // 256-thread workgroups per unit; capped by the largest possible tile count
+    // unit (two per SIMD, its register budget; four, one per SIMD, for
+    // 32-column workers); the vector-ALU kernel four 256-thread workgroups
+    // per unit; capped by the largest possible tile count
     const int cus = device_cu_count();
     const int64_t max_tiles = (int64_t)p.B * p.KH * L.ngb * (((int64_t)L.max_tokens + 31) / 32);
-    int64_t grid = (int64_t)cus * (L.mfma ? 8 : 4);
+    int64_t grid = (int64_t)cus * (L.mfma ? (L.cols == 32 ? 4 : 8) : 4);
     if (grid > max_tiles) grid = max_tiles;
     p.grid = (int)(grid < 1 ? 1 : grid);
   }

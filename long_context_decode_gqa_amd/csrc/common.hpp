@@ -95,6 +95,7 @@ struct DecodeParams {
   // G: query rows per KV head (the matrix-core columns), R * Gq; QH = KH * G
   int32_t B, KH, G, D, QH, ngb;
   int32_t Gq, R;  // query heads per KV head, query rows per sequence
+  int32_t cols_per_wave;  // matrix-core columns a decode worker computes: 16, or 32 when G > 16
   const int32_t *seq_lens;
   const int64_t *seq_offset;
   int64_t stride_h, stride_t;

@@ -1,10 +1,10 @@
 // Split-KV GQA decode attention on gfx950 matrix cores (bf16 or int8 KV).
 //
-// One workgroup (4 waves) takes one work item = (sequence b, KV head kh,
-// query-head block, chunk of split_tokens token positions) from the
-// work-list, claimed with an integer atomic.  Each wave streams 32-token
-// tiles of the chunk (tile w, w+4, ...), prefetching its next tile into
-// registers while it computes the current one:
+// One wave is one worker of a persistent grid.  The 32-token tiles of every
+// (sequence b, KV head kh, column block) are laid end to end and each wave
+// streams one balanced contiguous range of them, cut into chunks of
+// split_tokens positions, with its next tiles in flight in a register ring
+// while it computes the current one:
 //
 //   S^T[t][g]  = K[t][:] . Q[g][:]            v_mfma_f32_16x16x32_{bf16,f16}
 //   online softmax per query head g (running max m, sum l; exp2 domain)
@@ -34,6 +34,10 @@
 //    permute, no LDS round trip).
 //  * P is split as p = hi + lo with hi = bf16(p) and lo = bf16(p - hi); both
 //    are multiplied into the same accumulator, so P carries ~16 bits.
+//  * A KV head with more than 16 query rows runs 32-column workers (CB = 2):
+//    two 16-column blocks whose MFMAs take the same K and V operands, so 32
+//    rows share one read of the cache; such a wave holds twice the
+//    accumulators and runs alone on its SIMD.
 #include "common.hpp"
 
 namespace lcdg {
@@ -82,7 +86,7 @@ struct Tile {
 // A pipeline step: TPS consecutive tiles, as many as fit a per-buffer
 // register budget (64 VGPRs for bf16; 32 for int8, whose dequantisation needs
 // more temporaries), so small tiles still keep more bytes in flight.
-template <int D, int KVT, bool IDX>
+template <int D, int KVT, bool IDX, int CB>
 struct Step {
   typedef Tile<D, KVT, IDX> TileT;
   static constexpr int kRegs = 2 * TileT::KL * 4 + 8 * TileT::VW;
@@ -94,7 +98,10 @@ struct Step {
   // step has only NBUF-2 steps to arrive; it keeps four buffers where they
   // fit in registers (one-tile steps over the whole cache) and three where a
   // step holds two tiles or token indices take registers.
-  static constexpr int NBUF = KVT == ATTN_BF16 ? 2 : (TPS == 1 && !IDX ? 4 : 3);
+  // Two column blocks per wave (CB = 2) run one wave per SIMD with twice the
+  // registers, so the ring is deeper to keep as many bytes in flight per SIMD.
+  static constexpr int NBUF = CB == 2 ? (KVT == ATTN_BF16 ? 4 : (TPS == 1 && !IDX ? 6 : 4))
+                                      : (KVT == ATTN_BF16 ? 2 : (TPS == 1 && !IDX ? 4 : 3));
   static constexpr bool PIPE = KVT == ATTN_I8;
   TileT t[TPS];
 };
@@ -112,11 +119,13 @@ constexpr int kMaxSegPages = 72;
 // the loop.  A range is cut into runs (one lane each) and runs into segments
 // (one chunk piece each); a segment's partial (m, l, o) goes straight from
 // registers to its slot.
-template <int D, int KVT, bool IDX, bool QI8, bool PAGED>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_mfma_kernel(DecodeParams p) {
+template <int D, int KVT, bool IDX, bool QI8, bool PAGED, int CB>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(CB == 2 ? 1 : 2, CB == 2 ? 1 : 2))) void
+decode_mfma_kernel(DecodeParams p) {
   static_assert(!(IDX && PAGED), "a paged cache is read by position");
+  static_assert(CB == 1 || CB == 2, "one or two 16-column blocks per wave");
   typedef Tile<D, KVT, IDX> TileT;
-  typedef Step<D, KVT, IDX> StepT;
+  typedef Step<D, KVT, IDX, CB> StepT;
   constexpr int TPS = StepT::TPS;
   constexpr int NB = D / 16;
   constexpr int ES = TileT::ES;
@@ -128,12 +137,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
   __shared__ int s_idx[IDX ? kMaxIdxChunk : 1];
   __shared__ int s_pages[PAGED ? kMaxSegPages : 1];  // page ids of the current segment
-  // Q^T operand of the current run, 16 query heads x D channels, rows padded
+  // Q^T operand of the current run, 16*CB query rows x D channels, rows padded
   // by 16 bytes against bank conflicts: bf16 for bf16 KV; for int8 KV three
-  // int8 digit planes of each head's 22-bit fixed-point query (see below).
+  // int8 digit planes of each row's 22-bit fixed-point query (see below).
   constexpr int kQRow = D * 2 + 16;
   constexpr int kQDRow = D + 16;
-  constexpr int kQBytes = KVT == ATTN_I8 ? 3 * 16 * kQDRow : 16 * kQRow;
+  constexpr int kQBytes = CB * (KVT == ATTN_I8 ? 3 * 16 * kQDRow : 16 * kQRow);
   __shared__ __attribute__((aligned(16))) unsigned char s_q[kQBytes];
 
   const int lane = threadIdx.x;
@@ -161,12 +170,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const int L = uniform_i32(min(max(p.seq_lens[b], 0), p.max_seq_len));
     int npos = L;
     if constexpr (IDX) npos = uniform_i32(L > 0 ? min(max(p.n_idx[pair], 0), p.idx_stride) : 0);
-    const int g0 = gb * 16;
-    const int gcount = min(16, p.G - g0);
-    const bool qvalid = col < gcount;
-    // with R query rows per sequence, column g0 + col is row r = (g0 + col) / Gq,
-    // the token at position L - R + r: it sees the first L - (R - 1) + r tokens
-    const int col_end = p.R > 1 ? L - (p.R - 1) + (g0 + col) / p.Gq : 0x7FFFFFFF;
+    // this lane's column of block cb is query row g0 + 16*cb + col of the KV head
+    const int g0 = gb * 16 * CB;
+    bool qvalid[CB];
+    int col_end[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      qvalid[cb] = g0 + 16 * cb + col < p.G;
+      // with R query rows per sequence, column gc is row r = gc / Gq, the token
+      // at position L - R + r: it sees the first L - (R - 1) + r tokens
+      col_end[cb] = p.R > 1 ? L - (p.R - 1) + (g0 + 16 * cb + col) / p.Gq : 0x7FFFFFFF;
+    }
 
     // Buffer resources over this (b, kh)'s rows: 32-bit offsets, and rows at
     // or past L read as zero (their scores are masked), so no clamping.  A
@@ -199,95 +213,102 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // and |d2| <= 64 (|error| <= max|q_g| * 2^-23); each digit plane is one
     // int8 MFMA, and the three integer sums recombine exactly in fp32.  An
     // int8 query (QI8: per-row or static scale) is plane 0 alone.
-    float qs = 0.f;  // int8: this lane's head (col) scale s_col
+    float qs[CB];  // int8: this lane's column scale s_col in each block
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) qs[cb] = 0.f;
     __syncthreads();
     if constexpr (KVT == ATTN_I8) {
-      constexpr int CPL = D / 4;  // lane (col, cg) takes head col, channels [cg*CPL, cg*CPL + CPL)
-      float qv[CPL];
-      const uint16_t *qrow = (const uint16_t *)p.q + q_row_index(p, b, kh, g0 + col) * D + cg * CPL;
+      constexpr int CPL = D / 4;  // lane (col, cg) takes column col, channels [cg*CPL, cg*CPL + CPL)
+      unsigned char *sq_blk = s_q;
 #pragma unroll
-      for (int x = 0; x < CPL / 8; ++x) {
-        u32x4_t w = (u32x4_t){0u, 0u, 0u, 0u};
-        if (qvalid) w = *(const u32x4_t *)(qrow + 8 * x);
+      for (int cb = 0; cb < CB; ++cb, sq_blk += 3 * 16 * kQDRow) {
+        float qv[CPL];
+        const uint16_t *qrow = (const uint16_t *)p.q + q_row_index(p, b, kh, g0 + 16 * cb + col) * D + cg * CPL;
 #pragma unroll
-        for (int y = 0; y < 4; ++y) {
-          qv[8 * x + 2 * y] = bf16_lo(w[y]);
-          qv[8 * x + 2 * y + 1] = bf16_hi(w[y]);
-        }
-      }
-      float mx = 0.f;
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) mx = fmaxf(mx, fabsf(qv[j]));
-      mx = rows_max(mx);  // the four lanes of head col hold all D channels
-      if constexpr (QI8) {
-        // int8 query (one digit plane): s = max|q_row| / 127, or the static
-        // scale, and code = clamp(rint(q / s), -127, 127), in IEEE fp32
-        // (correctly rounded divides, round half to even).
-        const float sq = p.q_quant == ATTN_QUANT_ROW ? mx / 127.0f : p.q_scale;
-        qs = sq;
-#pragma unroll
-        for (int x = 0; x < CPL / 16; ++x) {
-          uint32_t w[4];
-#pragma unroll
-          for (int j4 = 0; j4 < 4; ++j4) {
-            uint32_t acc = 0u;
-#pragma unroll
-            for (int y = 0; y < 4; ++y) {
-              float c = 0.f;
-              if (sq > 0.f) c = fminf(127.f, fmaxf(-127.f, __builtin_rintf(qv[16 * x + 4 * j4 + y] / sq)));
-              acc |= ((uint32_t)(int)c & 0xFFu) << (8 * y);
-            }
-            w[j4] = acc;
-          }
-          *(u32x4_t *)(s_q + col * kQDRow + cg * CPL + 16 * x) = (u32x4_t){w[0], w[1], w[2], w[3]};
-        }
-      } else {
-        const float inv = mx > 0.f ? 4194304.0f / mx : 0.f;
-        qs = mx * (1.0f / 4194304.0f);
-        uint32_t dw[3][CPL / 4];
-#pragma unroll
-        for (int j4 = 0; j4 < CPL / 4; ++j4) {
-          uint32_t w0 = 0u, w1 = 0u, w2 = 0u;
+        for (int x = 0; x < CPL / 8; ++x) {
+          u32x4_t w = (u32x4_t){0u, 0u, 0u, 0u};
+          if (qvalid[cb]) w = *(const u32x4_t *)(qrow + 8 * x);
 #pragma unroll
           for (int y = 0; y < 4; ++y) {
-            const int n = (int)__builtin_rintf(qv[4 * j4 + y] * inv);
-            const int d0 = (int)(int8_t)(n & 0xFF);
-            const int r1 = (n - d0) >> 8;
-            const int d1 = (int)(int8_t)(r1 & 0xFF);
-            const int d2 = (r1 - d1) >> 8;
-            w0 |= (uint32_t)(d0 & 0xFF) << (8 * y);
-            w1 |= (uint32_t)(d1 & 0xFF) << (8 * y);
-            w2 |= (uint32_t)(d2 & 0xFF) << (8 * y);
+            qv[8 * x + 2 * y] = bf16_lo(w[y]);
+            qv[8 * x + 2 * y + 1] = bf16_hi(w[y]);
           }
-          dw[0][j4] = w0;
-          dw[1][j4] = w1;
-          dw[2][j4] = w2;
         }
+        float mx = 0.f;
 #pragma unroll
-        for (int dg = 0; dg < 3; ++dg)
+        for (int j = 0; j < CPL; ++j) mx = fmaxf(mx, fabsf(qv[j]));
+        mx = rows_max(mx);  // the four lanes of column col hold all D channels
+        if constexpr (QI8) {
+          // int8 query (one digit plane): s = max|q_row| / 127, or the static
+          // scale, and code = clamp(rint(q / s), -127, 127), in IEEE fp32
+          // (correctly rounded divides, round half to even).
+          const float sq = p.q_quant == ATTN_QUANT_ROW ? mx / 127.0f : p.q_scale;
+          qs[cb] = sq;
 #pragma unroll
-          for (int x = 0; x < CPL / 16; ++x)
-            *(u32x4_t *)(s_q + (dg * 16 + col) * kQDRow + cg * CPL + 16 * x) =
-                (u32x4_t){dw[dg][4 * x], dw[dg][4 * x + 1], dw[dg][4 * x + 2], dw[dg][4 * x + 3]};
+          for (int x = 0; x < CPL / 16; ++x) {
+            uint32_t w[4];
+#pragma unroll
+            for (int j4 = 0; j4 < 4; ++j4) {
+              uint32_t acc = 0u;
+#pragma unroll
+              for (int y = 0; y < 4; ++y) {
+                float c = 0.f;
+                if (sq > 0.f) c = fminf(127.f, fmaxf(-127.f, __builtin_rintf(qv[16 * x + 4 * j4 + y] / sq)));
+                acc |= ((uint32_t)(int)c & 0xFFu) << (8 * y);
+              }
+              w[j4] = acc;
+            }
+            *(u32x4_t *)(sq_blk + col * kQDRow + cg * CPL + 16 * x) = (u32x4_t){w[0], w[1], w[2], w[3]};
+          }
+        } else {
+          const float inv = mx > 0.f ? 4194304.0f / mx : 0.f;
+          qs[cb] = mx * (1.0f / 4194304.0f);
+          uint32_t dw[3][CPL / 4];
+#pragma unroll
+          for (int j4 = 0; j4 < CPL / 4; ++j4) {
+            uint32_t w0 = 0u, w1 = 0u, w2 = 0u;
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+              const int n = (int)__builtin_rintf(qv[4 * j4 + y] * inv);
+              const int d0 = (int)(int8_t)(n & 0xFF);
+              const int r1 = (n - d0) >> 8;
+              const int d1 = (int)(int8_t)(r1 & 0xFF);
+              const int d2 = (r1 - d1) >> 8;
+              w0 |= (uint32_t)(d0 & 0xFF) << (8 * y);
+              w1 |= (uint32_t)(d1 & 0xFF) << (8 * y);
+              w2 |= (uint32_t)(d2 & 0xFF) << (8 * y);
+            }
+            dw[0][j4] = w0;
+            dw[1][j4] = w1;
+            dw[2][j4] = w2;
+          }
+#pragma unroll
+          for (int dg = 0; dg < 3; ++dg)
+#pragma unroll
+            for (int x = 0; x < CPL / 16; ++x)
+              *(u32x4_t *)(sq_blk + (dg * 16 + col) * kQDRow + cg * CPL + 16 * x) =
+                  (u32x4_t){dw[dg][4 * x], dw[dg][4 * x + 1], dw[dg][4 * x + 2], dw[dg][4 * x + 3]};
+        }
       }
     } else {
-      for (int e = lane; e < 16 * (D / 8); e += 64) {
+      for (int e = lane; e < 16 * CB * (D / 8); e += 64) {
         const int g = e / (D / 8), c8 = e - g * (D / 8);
         u32x4_t w = (u32x4_t){0u, 0u, 0u, 0u};
-        if (g < gcount)
+        if (g0 + g < p.G)
           w = *(const u32x4_t *)((const uint16_t *)p.q + q_row_index(p, b, kh, g0 + g) * D + 8 * c8);
         *(u32x4_t *)(s_q + g * kQRow + 16 * c8) = w;
       }
     }
-    // partial (pair, slot j, head g) lives at (pair*2*max_chunks + j)*G + g
+    // partial (pair, slot j, column g) lives at (pair*2*max_chunks + j)*G + g
     const int slot_base = pair * 2 * p.max_chunks * p.G + g0 + col;
     __syncthreads();
-    auto q_operand = [&](int kb) -> bf16x8_t {
-      return __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(s_q + col * kQRow + 16 * (4 * kb + cg)));
+    auto q_operand = [&](int cb, int kb) -> bf16x8_t {
+      return __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(s_q + (16 * cb + col) * kQRow + 16 * (4 * kb + cg)));
     };
-    // int8: digit plane dg of channels 64kb + 16cg .. + 15 of head col
-    auto q_digits = [&](int dg, int kb) -> i32x4_t {
-      return __builtin_bit_cast(i32x4_t, *(const u32x4_t *)(s_q + (dg * 16 + col) * kQDRow + 64 * kb + 16 * cg));
+    // int8: digit plane dg of channels 64kb + 16cg .. + 15 of column col of block cb
+    auto q_digits = [&](int cb, int dg, int kb) -> i32x4_t {
+      return __builtin_bit_cast(i32x4_t,
+                                *(const u32x4_t *)(s_q + ((3 * cb + dg) * 16 + col) * kQDRow + 64 * kb + 16 * cg));
     };
 
     // Positions of the current segment (IDX: its staged index list starts at
@@ -362,91 +383,105 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    f32x4_t O[NB];
+    // running output, max and sum of each column block
+    f32x4_t O[CB][NB];
+    float m_run[CB], l_run[CB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) O[nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    float m_run = NEG_INF, l_run = 0.f;
+    for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) O[cb][nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+      m_run[cb] = NEG_INF;
+      l_run[cb] = 0.f;
+    }
 
-    // Raw q.k of a tile's 8 scores of this lane (before scale and mask).
+    // Raw q.k of a tile's 8 scores of this lane in each column block (before
+    // scale and mask).  The K operands as loaded serve every block.
     struct Raw {
-      float v[8];
+      float v[CB][8];
     };
     auto qk_tile = [&](const TileT &R) -> Raw {
       Raw r;
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (KVT == ATTN_BF16) {
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, R.k[tb][kb]), q_operand(kb),
-                                                          acc, 0, 0, 0);
-        } else {
-          // the K codes as loaded are the int8 A operand (lane (col, cg):
-          // token col, channels 64kb + 16cg .. + 15)
-          i32x4_t a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0}, a2 = {0, 0, 0, 0};
+        for (int cb = 0; cb < CB; ++cb) {
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (KVT == ATTN_BF16) {
 #pragma unroll
-          for (int kb = 0; kb < KL; ++kb) {
-            const i32x4_t kop = __builtin_bit_cast(i32x4_t, R.k[tb][kb]);
-            a0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, q_digits(0, kb), a0, 0, 0, 0);
-            if constexpr (!QI8) {
-              a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, q_digits(1, kb), a1, 0, 0, 0);
-              a2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, q_digits(2, kb), a2, 0, 0, 0);
+            for (int kb = 0; kb < KB; ++kb)
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, R.k[tb][kb]),
+                                                            q_operand(cb, kb), acc, 0, 0, 0);
+          } else {
+            // the K codes as loaded are the int8 A operand (lane (col, cg):
+            // token col, channels 64kb + 16cg .. + 15)
+            i32x4_t a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0}, a2 = {0, 0, 0, 0};
+#pragma unroll
+            for (int kb = 0; kb < KL; ++kb) {
+              const i32x4_t kop = __builtin_bit_cast(i32x4_t, R.k[tb][kb]);
+              a0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, q_digits(cb, 0, kb), a0, 0, 0, 0);
+              if constexpr (!QI8) {
+                a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, q_digits(cb, 1, kb), a1, 0, 0, 0);
+                a2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, q_digits(cb, 2, kb), a2, 0, 0, 0);
+              }
             }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[i] = QI8 ? (float)a0[i] : ((float)a2[i] * 65536.0f + (float)a1[i] * 256.0f) + (float)a0[i];
           }
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[i] = QI8 ? (float)a0[i] : ((float)a2[i] * 65536.0f + (float)a1[i] * 256.0f) + (float)a0[i];
+          for (int i = 0; i < 4; ++i) r.v[cb][4 * tb + i] = acc[i];
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r.v[4 * tb + i] = acc[i];
       }
       return r;
     };
 
-    // Online softmax and P.V of a tile whose raw scores are given.
+    // Online softmax and P.V of a tile whose raw scores are given; the V
+    // operands are assembled once and serve every column block.
     auto finish_tile = [&](const TileT &R, int tile, const Raw &raw) {
       const int tpos = (tile - lane_t0) * kTile;
-      const int lim = min(seg_pos1, col_end);
-      float s[8];
+      OpT phi[CB], plo[CB];
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+      for (int cb = 0; cb < CB; ++cb) {
+        const int lim = min(seg_pos1, col_end[cb]);
+        float s[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int pos = tpos + 16 * tb + 4 * cg + i;
-          float sc = c1;
-          if constexpr (KVT == ATTN_I8) sc *= qs * (IDX ? R.ks[4 * tb + i] : R.ks[tb]);
-          s[4 * tb + i] = (pos < lim) ? raw.v[4 * tb + i] * sc : NEG_INF;
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int pos = tpos + 16 * tb + 4 * cg + i;
+            float sc = c1;
+            if constexpr (KVT == ATTN_I8) sc *= qs[cb] * (IDX ? R.ks[4 * tb + i] : R.ks[tb]);
+            s[4 * tb + i] = (pos < lim) ? raw.v[cb][4 * tb + i] * sc : NEG_INF;
+          }
+        float mt = s[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) mt = fmaxf(mt, s[i]);
+        mt = rows_max(mt);
+        const float m_new = fmaxf(m_run[cb], mt);
+        if (__any(m_new > m_run[cb])) {
+          const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - m_new);
+          l_run[cb] *= alpha;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) O[cb][nb] *= alpha;
+          m_run[cb] = m_new;
         }
-      float mt = s[0];
+        const float mref = (m_run[cb] == NEG_INF) ? 0.f : m_run[cb];
 #pragma unroll
-      for (int i = 1; i < 8; ++i) mt = fmaxf(mt, s[i]);
-      mt = rows_max(mt);
-      const float m_new = fmaxf(m_run, mt);
-      if (__any(m_new > m_run)) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) O[nb] *= alpha;
-        m_run = m_new;
-      }
-      const float mref = (m_run == NEG_INF) ? 0.f : m_run;
-      OpT phi, plo;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float pv = __builtin_amdgcn_exp2f(s[i] - mref);
-        pv = qvalid ? pv : 0.f;
-        l_run += pv;
-        if constexpr (KVT == ATTN_BF16) {
-          const uint32_t hb = f32_to_bf16_bits(pv);
-          const float hf = __uint_as_float(hb << 16);
-          const uint32_t lb = f32_to_bf16_bits(pv - hf);
-          phi[i] = __builtin_bit_cast(__bf16, (uint16_t)hb);
-          plo[i] = __builtin_bit_cast(__bf16, (uint16_t)lb);
-        } else {
-          const _Float16 h = (_Float16)pv;
-          phi[i] = h;
-          plo[i] = (_Float16)(pv - (float)h);
+        for (int i = 0; i < 8; ++i) {
+          float pv = __builtin_amdgcn_exp2f(s[i] - mref);
+          pv = qvalid[cb] ? pv : 0.f;
+          l_run[cb] += pv;
+          if constexpr (KVT == ATTN_BF16) {
+            const uint32_t hb = f32_to_bf16_bits(pv);
+            const float hf = __uint_as_float(hb << 16);
+            const uint32_t lb = f32_to_bf16_bits(pv - hf);
+            phi[cb][i] = __builtin_bit_cast(__bf16, (uint16_t)hb);
+            plo[cb][i] = __builtin_bit_cast(__bf16, (uint16_t)lb);
+          } else {
+            const _Float16 h = (_Float16)pv;
+            phi[cb][i] = h;
+            plo[cb][i] = (_Float16)(pv - (float)h);
+          }
         }
       }
 #pragma unroll
@@ -460,8 +495,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             // the low (even nb) or high (odd nb) bf16 of tokens 2qq and 2qq+1
             a[qq] = __builtin_amdgcn_perm(y, x, (nb & 1) ? 0x07060302u : 0x05040100u);
           }
-          O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), phi, O[nb], 0, 0, 0);
-          O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), plo, O[nb], 0, 0, 0);
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) {
+            O[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), phi[cb], O[cb][nb],
+                                                                0, 0, 0);
+            O[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), plo[cb], O[cb][nb],
+                                                                0, 0, 0);
+          }
         } else {
           const int w = nb >> 2;
           const uint32_t k = (uint32_t)(nb & 3);
@@ -471,8 +511,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             const uint32_t x = word_of<VW>(R.v[2 * qq], w), y = word_of<VW>(R.v[2 * qq + 1], w);
             a[qq] = codes_to_f16x2(__builtin_amdgcn_perm(y, x, 0x0c000c00u | k | ((4u + k) << 16)));
           }
-          O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), phi, O[nb], 0, 0, 0);
-          O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), plo, O[nb], 0, 0, 0);
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) {
+            O[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), phi[cb], O[cb][nb],
+                                                               0, 0, 0);
+            O[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), plo[cb], O[cb][nb],
+                                                               0, 0, 0);
+          }
         }
       }
     };
@@ -563,36 +608,40 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         }
       }
 
-      // Partial of this segment, straight from registers.  Lane (col, cg)
-      // holds channels NB*(4*cg + i) + nb = 4*NB*cg + NB*i + nb of head col.
-      l_run = rows_sum(l_run);
-      if (qvalid) {
-        const int half = (seg_t0 == lane_t0 + chunk * ct) ? 0 : 1;
-        const int slot = slot_base + (2 * chunk + half) * p.G;
-        const float out_scale = (KVT == ATTN_I8) ? p.v_scale : 1.0f;
-        const float inv = l_run > 0.f ? out_scale / l_run : 0.f;
-        float *op = p.wl.o_part + (int64_t)slot * D + 4 * NB * cg;
+      // Partial of this segment, straight from registers, for each column
+      // block.  Lane (col, cg) holds channels NB*(4*cg + i) + nb =
+      // 4*NB*cg + NB*i + nb of its column.
+      const int half = (seg_t0 == lane_t0 + chunk * ct) ? 0 : 1;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+      for (int cb = 0; cb < CB; ++cb) {
+        const float lsum = rows_sum(l_run[cb]);
+        if (qvalid[cb]) {
+          const int slot = slot_base + 16 * cb + (2 * chunk + half) * p.G;
+          const float out_scale = (KVT == ATTN_I8) ? p.v_scale : 1.0f;
+          const float inv = lsum > 0.f ? out_scale / lsum : 0.f;
+          float *op = p.wl.o_part + (int64_t)slot * D + 4 * NB * cg;
 #pragma unroll
-          for (int n4 = 0; n4 < NB / 4; ++n4) {
-            const f32x4_t v = {O[4 * n4][i] * inv, O[4 * n4 + 1][i] * inv, O[4 * n4 + 2][i] * inv,
-                               O[4 * n4 + 3][i] * inv};
-            *(f32x4_t *)(op + NB * i + 4 * n4) = v;
-          }
-        if (cg == 0) {
-          p.wl.m_part[slot] = l_run > 0.f ? m_run * kLn2 : NEG_INF;
-          p.wl.l_part[slot] = l_run;
-          if (half == 0 && seg_t1 == chunk_t1) {
-            p.wl.m_part[slot + p.G] = NEG_INF;
-            p.wl.l_part[slot + p.G] = 0.f;
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int n4 = 0; n4 < NB / 4; ++n4) {
+              const f32x4_t v = {O[cb][4 * n4][i] * inv, O[cb][4 * n4 + 1][i] * inv, O[cb][4 * n4 + 2][i] * inv,
+                                 O[cb][4 * n4 + 3][i] * inv};
+              *(f32x4_t *)(op + NB * i + 4 * n4) = v;
+            }
+          if (cg == 0) {
+            p.wl.m_part[slot] = lsum > 0.f ? m_run[cb] * kLn2 : NEG_INF;
+            p.wl.l_part[slot] = lsum;
+            if (half == 0 && seg_t1 == chunk_t1) {
+              p.wl.m_part[slot + p.G] = NEG_INF;
+              p.wl.l_part[slot + p.G] = 0.f;
+            }
           }
         }
-      }
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) O[nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-      m_run = NEG_INF;
-      l_run = 0.f;
+        for (int nb = 0; nb < NB; ++nb) O[cb][nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        m_run[cb] = NEG_INF;
+        l_run[cb] = 0.f;
+      }
       seg_t0 = seg_t1;
     }
     t = run_end;
@@ -602,30 +651,36 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
 }  // namespace
 
-template <bool IDX, bool PAGED>
+template <bool IDX, bool PAGED, int CB>
 static void launch_variant(const DecodeParams &p, int kv_dtype, dim3 g, hipStream_t s) {
   dim3 blk(64);
   if (kv_dtype == ATTN_BF16) {
-    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_BF16, IDX, false, PAGED>), g, blk, 0, s, p);
-    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_BF16, IDX, false, PAGED>), g, blk, 0, s, p);
+    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_BF16, IDX, false, PAGED, CB>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_BF16, IDX, false, PAGED, CB>), g, blk, 0, s, p);
   } else if (p.q_quant == ATTN_QUANT_EXACT) {
-    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_I8, IDX, false, PAGED>), g, blk, 0, s, p);
-    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_I8, IDX, false, PAGED>), g, blk, 0, s, p);
+    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_I8, IDX, false, PAGED, CB>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_I8, IDX, false, PAGED, CB>), g, blk, 0, s, p);
   } else {
-    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_I8, IDX, true, PAGED>), g, blk, 0, s, p);
-    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_I8, IDX, true, PAGED>), g, blk, 0, s, p);
+    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_I8, IDX, true, PAGED, CB>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_I8, IDX, true, PAGED, CB>), g, blk, 0, s, p);
   }
+}
+
+template <bool IDX, bool PAGED>
+static void launch_cb(const DecodeParams &p, int kv_dtype, dim3 g, hipStream_t s) {
+  if (p.cols_per_wave == 32) launch_variant<IDX, PAGED, 2>(p, kv_dtype, g, s);
+  else launch_variant<IDX, PAGED, 1>(p, kv_dtype, g, s);
 }
 
 hipError_t launch_decode_mfma(const DecodeParams &p, int kv_dtype, hipStream_t s) {
   if (p.token_idx) {
     if (p.split > kMaxIdxChunk || p.block_table) return hipErrorInvalidValue;
-    launch_variant<true, false>(p, kv_dtype, dim3(p.grid), s);
+    launch_cb<true, false>(p, kv_dtype, dim3(p.grid), s);
   } else if (p.block_table) {
     if (p.split > 64 * p.page_tokens) return hipErrorInvalidValue;
-    launch_variant<false, true>(p, kv_dtype, dim3(p.grid), s);
+    launch_cb<false, true>(p, kv_dtype, dim3(p.grid), s);
   } else {
-    launch_variant<false, false>(p, kv_dtype, dim3(p.grid), s);
+    launch_cb<false, false>(p, kv_dtype, dim3(p.grid), s);
   }
   return hipGetLastError();
 }
