@@ -109,6 +109,20 @@ class Timer:
         torch.cuda.synchronize()
 
 
+def time_calls(torch, fn, steps, warmup):
+    """Mean ms per call of fn (launches on the current stream), between two events."""
+    for _ in range(warmup):
+        fn()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        fn()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
 def to_dev(torch, a, dev):
     import numpy as np
     if a.dtype == np.uint16:
@@ -205,6 +219,16 @@ def bench_int8(pkg, torch, synth, steps, warmup, dev):
     ref()
     k_codes = {part: pkg.kv_quant_int8(kd, geom, part) for part in (64, 128, 0)}
     vc, vs = pkg.kv_quant_int8(vd, geom, 0)
+    # cache-write-time quantisation (not part of a decode step): K per 64-token partition (one read,
+    # one write) and V per tensor (a max pass, then a code pass: two reads, one write)
+    elems = w.kv_tokens() * w.KH * w.D
+    kc64, ks64 = k_codes[64]
+    t_kq = time_calls(torch, lambda: pkg.kv_quant_int8(kd, geom, 64, codes=kc64, scales=ks64), steps, warmup)
+    t_vq = time_calls(torch, lambda: pkg.kv_quant_int8(vd, geom, 0, codes=vc, scales=vs), steps, warmup)
+    quant = {"k_partition64_us": round(t_kq * 1e3, 2),
+             "k_partition64_gbs": round((elems * 3 + ks64.numel() * 4) / t_kq / 1e6, 1),
+             "v_tensor_us": round(t_vq * 1e3, 2),
+             "v_tensor_gbs": round((elems * 5 + 4) / t_vq / 1e6, 1)}
     # static per-tensor query scale, calibrated once on this query with the library's quantiser
     qgeom = pkg.KVGeometry(w.B, w.QH, w.D, 1, torch.ones(w.B, dtype=torch.int32, device=dev),
                            torch.arange(w.B, dtype=torch.int64, device=dev) * (w.QH * w.D), w.D, w.D)
@@ -234,7 +258,8 @@ def bench_int8(pkg, torch, synth, steps, warmup, dev):
         schemes[name] = {"us_per_step": round(ms_s * 1e3, 2), "decode_kernel_us": round(dk_s * 1e3, 2),
                          "kv_gbs": round(b / ms_s / 1e6, 1), "rel_err_vs_bf16": round(err, 5)}
         del ps
-    return dict(ms=ms, decode_ms=dk, merge_ms=mg, kv_bytes=kvb, split=effective_split(torch, w), schemes=schemes)
+    return dict(ms=ms, decode_ms=dk, merge_ms=mg, kv_bytes=kvb, split=effective_split(torch, w), schemes=schemes,
+                quant=quant)
 
 
 def bench_paged(pkg, torch, synth, steps, warmup, dev, page_tokens=64, layout="head_major"):
@@ -338,6 +363,10 @@ def bench_oam(pkg, torch, synth, steps, warmup, dev):
            "gbs_algorithmic": round(algo / ms / 1e6, 1), "frac_of_peak": round(algo / ms / 1e6 / HBM_PEAK_GBS, 4),
            "select_with_norms_from_v_us": round(t_fly * 1e3, 2), "top_k": w.top_k, "kv_len": L}
     del sel, sel_fly, att
+    # the cached value term, computed when tokens are appended (V read once, 4 bytes written per token)
+    t_vl = time_calls(torch, lambda: pkg.oam_value_lognorm(vd, geom, w.eps, vlog=vlog), steps, warmup)
+    res["value_lognorm_us"] = round(t_vl * 1e3, 2)
+    res["value_lognorm_gbs"] = round(npairs * L * (D * 2 + 4) / t_vl / 1e6, 1)
     # The page's §7 stack on the same data: the cache quantised once (K per 64-token partition, V per
     # tensor), OAM scores over the K codes with the value term from the INT8 values, then INT8
     # attention over the kept tokens.
@@ -487,6 +516,7 @@ def main():
                 r = bench_int8(pkg, torch, synth, max(5, K // 2), W, dev)
                 others["int8_128k"] = summary(r)
                 others["int8_128k_schemes"] = r["schemes"]
+                others["int8_128k_quantisation"] = r["quant"]
             except pkg.AttnError as e:
                 others["int8_128k"] = {"error": str(e)}
         if "multirow" in todo:

@@ -54,6 +54,58 @@ def test_partition_quant_bit_exact_ragged(part):
             np.testing.assert_array_equal(scales[base:base + n], ref_scales[base:base + n])
 
 
+@pytest.mark.parametrize("D,part,layout", [(64, 64, "head_major"), (256, 32, "token_major"), (40, 64, "head_major"),
+                                           (128, 256, "token_major"), (64, 512, "head_major"), (128, 32, "head_major")])
+def test_quant_geometries_bit_exact_and_nothing_written_outside_rows(D, part, layout):
+    """Partition and per-tensor quantisation over head sizes with compile-time (64, 256) and run-time (40)
+    row geometry and partitions from 32 to 512 tokens, ragged lengths: codes and scales bit-exact, and
+    every code outside the sequences' valid rows left as the zeros it started from."""
+    lens = np.array([1, 63, 64, 65, 700, 2049, 0, 130, 511, 513], np.int32)
+    w = synth.workload("int8_128k", B=len(lens), KH=2, D=D, lens=lens, layout=layout, seed=60 + D + part)
+    q, k, v, g = gen_kv(w)
+    log_case(f"int8 quant geometry D={D} part={part} {layout}")
+    mask = np.zeros(g.numel, bool)
+    for b in range(g.B):
+        for kh in range(g.KH):
+            for t in range(lens[b]):
+                o = g.seq_offset[b] + kh * g.stride_h + t * g.stride_t
+                mask[o:o + g.D] = True
+    stride = max(1, -(-int(lens.max()) // part))
+    ref_codes, ref_scales = oracle.quant_partitions(g.B, g.KH, g.D, g.lens, g.seq_offset, g.stride_h, g.stride_t,
+                                                    k, part, stride)
+    codes, scales = gpu_quant(k, g, part)
+    np.testing.assert_array_equal(codes[mask], ref_codes[mask])
+    assert not codes[~mask].any()
+    for b in range(g.B):
+        for kh in range(g.KH):
+            n = -(-int(lens[b]) // part)
+            base = (b * g.KH + kh) * stride
+            np.testing.assert_array_equal(scales[base:base + n], ref_scales[base:base + n])
+    ref_v, ref_vs = oracle.quant_tensor(g.B, g.KH, g.D, g.lens, g.seq_offset, g.stride_h, g.stride_t, v)
+    vc, vs = gpu_quant(v, g, 0)
+    assert vs[0] == np.float32(ref_vs)
+    np.testing.assert_array_equal(vc[mask], ref_v[mask])
+    assert not vc[~mask].any()
+
+
+def test_quant_rounds_exact_ties_to_even():
+    """Values whose quotient by the scale is exactly a half-integer: max |x| = 254 gives scale 2, so
+    x = 3, 5, -3, 1, 253 sit on ties (1.5, 2.5, -1.5, 0.5, 126.5) and round to even (2, 2, -2, 0, 126)."""
+    lens = np.array([64], np.int32)
+    w = synth.workload("int8_128k", B=1, KH=1, lens=lens, layout="head_major", seed=71)
+    q, k, v, g = gen_kv(w)
+    vals = np.array([254, 3, 5, -3, 1, 253, -253, 7, 0, 127, 129, -129], np.float32)
+    kf = np.zeros(g.numel, np.float32)
+    kf[:len(vals)] = vals
+    k16 = (kf.view(np.uint32) >> 16).astype(np.uint16)       # all exactly representable in bf16
+    codes, scales = gpu_quant(k16, g, 64)
+    assert scales[0] == np.float32(2.0)
+    expect = np.array([127, 2, 2, -2, 0, 126, -126, 4, 0, 64, 64, -64], np.int8)
+    np.testing.assert_array_equal(codes[:len(vals)], expect)
+    ref_codes, _ = oracle.quant_partitions(g.B, g.KH, g.D, g.lens, g.seq_offset, g.stride_h, g.stride_t, k16, 64, 1)
+    np.testing.assert_array_equal(codes, ref_codes)
+
+
 def test_tensor_quant_bit_exact_and_zero_partitions():
     lens = np.array([300, 5, 129], np.int32)
     w = synth.workload("int8_128k", B=3, KH=2, lens=lens, layout="head_major", seed=47)
