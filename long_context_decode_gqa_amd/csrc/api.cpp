@@ -150,10 +150,15 @@ attn_status plan_decode(const attn_decode_args *a, DecodeLayout *L) {
     // workers on a 256-CU device, 1024 for 32-column workers): each worker
     // then writes about one partial per column, and partial writes cost far
     // more HBM time than their bytes while the KV stream runs.  32..2048
-    // tokens (1024 with an index list).
+    // tokens; with an index list at least 256 (bf16) or 128 (int8) and at
+    // most 1024, since gathered runs are short and a worker's fixed costs
+    // weigh more (4096 kept tokens per pair, bf16: 2048 two-tile workers
+    // took 26.6 us, 512 eight-tile workers 23.3 us, 256 sixteen-tile workers
+    // 26.7 us; int8: 27.6, 24.8 with four-tile workers, 26.1 us).
     const int64_t tiles = (int64_t)g.B * g.KH * L->ngb * (((int64_t)L->max_tokens + 31) / 32);
     const int64_t workers = L->cols == 32 ? 1024 : 2048;
-    const int64_t ct = std::min<int64_t>(std::max<int64_t>(tiles / workers, 1), a->token_idx ? 32 : 64);
+    const int64_t min_ct = a->token_idx ? (a->kv_dtype == ATTN_I8 ? 4 : 8) : 1;
+    const int64_t ct = std::min<int64_t>(std::max<int64_t>(tiles / workers, min_ct), a->token_idx ? 32 : 64);
     L->split = (int32_t)(32 * ct);
   }
   if (mfma && ((int64_t)g.max_seq_len + 64) * g.stride_t * elem_size(a->kv_dtype) >= (int64_t(1) << 31))

@@ -249,7 +249,7 @@ def workload(name: str, **over) -> Workload:
         w = Workload("int8_128k", 4, 8, 8, 128, 4, "bf16", np.full(4, 131072, np.int32), outliers=2, split_tokens=0)
     elif name == "oam_128k":
         w = Workload("oam_128k", 4, 8, 8, 128, 5, "bf16", np.full(4, 131072, np.int32),
-                     v_kind=UNIT_DIR_LOGNORMAL, top_k=4096, split_tokens=128)
+                     v_kind=UNIT_DIR_LOGNORMAL, top_k=4096, split_tokens=0)
     elif name == "dense128k":
         w = Workload("dense128k", 4, 8, 8, 128, 6, "bf16", np.full(4, 131072, np.int32), split_tokens=0)
     else:
