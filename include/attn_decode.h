@@ -237,7 +237,10 @@ attn_status attn_merge_lse(const float *o_part, const float *m_part, const float
                            const int32_t *row_split_start, int32_t rows, int32_t D, int32_t out_dtype,
                            void *out, float *lse, attn_stream_t stream);
 
-/* Host-only: workspace bytes for kv_quant_int8 (0 for per-partition mode). */
+/* Host-only: workspace bytes for kv_quant_int8: 0 in per-partition mode; in
+ * per-tensor mode 256 bytes plus one fp32 maximum per group of four row
+ * blocks (a row block is 8192 elements: 64 rows at D = 128) per (b, kh), about
+ * 1/8192 of the cache's bytes.  Validates the geometry's sizes. */
 attn_status kv_quant_int8_workspace_size(const attn_kv_geom *geom, int32_t partition_tokens, size_t *bytes);
 
 /*

@@ -18,7 +18,11 @@ extern "C" {
 attn_status kv_quant_int8_workspace_size(const attn_kv_geom *geom, int32_t partition_tokens, size_t *bytes) {
   if (!geom || !bytes) return api_fail(ATTN_ERR_INVALID_ARG, "geom and bytes are required");
   if (partition_tokens < 0) return api_fail(ATTN_ERR_INVALID_ARG, "partition_tokens must be >= 0");
-  *bytes = partition_tokens == 0 ? 256 : 0;
+  if (partition_tokens == 0) {
+    attn_status st = api_check_geom(*geom, 2, false);
+    if (st != ATTN_OK) return st;
+  }
+  *bytes = partition_tokens == 0 ? quant_tensor_workspace_bytes(*geom) : 0;
   return ATTN_OK;
 }
 
@@ -48,9 +52,11 @@ attn_status kv_quant_int8(const attn_kv_geom *geom, const void *x_bf16, int32_t 
       return api_fail(ATTN_ERR_INVALID_ARG, "scale_stride must be >= ceil(max_seq_len / partition_tokens)");
     e = launch_quant_partitions(*geom, x_bf16, partition_tokens, scale_stride, codes, scales, s);
   } else {
-    if (!workspace || workspace_bytes < 256 || (reinterpret_cast<uintptr_t>(workspace) & 255))
-      return api_fail(ATTN_ERR_WORKSPACE_TOO_SMALL, "per-tensor mode needs a 256-byte aligned workspace of 256 bytes");
-    e = launch_quant_tensor(*geom, x_bf16, codes, scales, static_cast<uint32_t *>(workspace), s);
+    if (!workspace || workspace_bytes < quant_tensor_workspace_bytes(*geom) ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255))
+      return api_fail(ATTN_ERR_WORKSPACE_TOO_SMALL,
+                      "per-tensor mode needs a 256-byte aligned workspace of kv_quant_int8_workspace_size() bytes");
+    e = launch_quant_tensor(*geom, x_bf16, codes, scales, workspace, s);
   }
   return e == hipSuccess ? ATTN_OK : api_fail_hip(e, "quantisation launch");
 }

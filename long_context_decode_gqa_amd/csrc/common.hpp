@@ -213,8 +213,9 @@ hipError_t launch_merge(const float *o_part, const float *m_part, const float *l
                         int32_t rows, int32_t D, int32_t out_dtype, void *out, float *lse, hipStream_t s);
 hipError_t launch_quant_partitions(const attn_kv_geom &g, const void *x, int32_t part, int32_t scale_stride,
                                    int8_t *codes, float *scales, hipStream_t s);
-hipError_t launch_quant_tensor(const attn_kv_geom &g, const void *x, int8_t *codes, float *scales,
-                               uint32_t *ws, hipStream_t s);
+hipError_t launch_quant_tensor(const attn_kv_geom &g, const void *x, int8_t *codes, float *scales, void *ws,
+                               hipStream_t s);
+size_t quant_tensor_workspace_bytes(const attn_kv_geom &g);
 hipError_t launch_value_lognorm(const attn_kv_geom &g, const void *v, int32_t v_dtype, float v_scale, float eps,
                                 float *vlog, int32_t stride, hipStream_t s);
 hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s);

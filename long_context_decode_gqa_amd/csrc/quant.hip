@@ -224,8 +224,6 @@ __global__ __launch_bounds__(256) void quant_partition_kernel(attn_kv_geom g, co
   }
 }
 
-__global__ void zero_word_kernel(uint32_t *w) { *w = 0u; }
-
 // Per-tensor passes work on wave row blocks of 1024 chunks (64 rows at
 // D = 128), sixteen 16-byte loads per lane in flight; four waves per
 // workgroup, each on its own block.
@@ -235,24 +233,20 @@ __host__ __device__ __forceinline__ int tensor_block_rows(int D) {
   return r > 0 ? r : 1;
 }
 
-// Per-tensor max |x|: each wave walks row blocks of every (b, kh) with a grid
-// stride; workgroup maxima are combined with an integer atomic max on the
-// fp32 bit pattern (non-negative floats order like their bit patterns).  The
-// grid is bounded so the atomic is taken once per workgroup, a few thousand times.
+// Per-tensor max |x|, first level: one wave per row block, each workgroup
+// writes the maximum of its four blocks to its own word of the workspace
+// (no atomics; blocks past a sequence's end count as 0).
 template <int CPR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void tensor_absmax_kernel(
-    attn_kv_geom g, const uint16_t *x, uint32_t *ws) {
+    attn_kv_geom g, const uint16_t *x, float *wg_max) {
   __shared__ float s_red[4];
   const int lane = threadIdx.x & 63;
+  const int pair = blockIdx.y;
+  const int L = min(max(g.seq_lens[pair / g.KH], 0), g.max_seq_len);
   const int rows = tensor_block_rows(g.D);
-  const int nblk_t = (g.max_seq_len + rows - 1) / rows;
-  const int64_t units = (int64_t)g.B * g.KH * nblk_t;
+  const int t0 = (blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * rows;
   uint32_t mb = 0u;
-  for (int64_t u = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); u < units; u += (int64_t)gridDim.x * 4) {
-    const int pair = (int)(u / nblk_t);
-    const int t0 = (int)(u - (int64_t)pair * nblk_t) * rows;
-    const int L = min(max(g.seq_lens[pair / g.KH], 0), g.max_seq_len);
-    if (t0 >= L) continue;
+  if (t0 < L) {
     const LaneChunks<CPR> lc = lane_chunks<CPR>(g, x, nullptr, pair, t0, min(L, t0 + rows), lane);
     u32x4_t w[kTensorCPL];
     load_chunks<kTensorCPL, CPR>(lc, x, w);
@@ -260,15 +254,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void t
     for (int j = 0; j < kTensorCPL; ++j) mb = absmax8_bits(w[j], mb);
   }
   const float m = block_max(absmax_of_bits(mb), s_red);
-  if (threadIdx.x == 0) atomicMax(ws, __float_as_uint(m));
+  if (threadIdx.x == 0) wg_max[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = m;
 }
 
-__global__ void tensor_scale_kernel(const uint32_t *ws, float *scales) { scales[0] = __uint_as_float(*ws) / 127.0f; }
+// Second level: one workgroup folds the n workgroup maxima; scale = fl32(max / 127).
+__global__ __launch_bounds__(256) void tensor_scale_kernel(const float *wg_max, int64_t n, float *scales) {
+  __shared__ float s_red[4];
+  float m = 0.f;
+  for (int64_t i = threadIdx.x; i < n; i += 256) m = fmaxf(m, wg_max[i]);
+  m = block_max(m, s_red);
+  if (threadIdx.x == 0) scales[0] = m / 127.0f;
+}
 
 // One wave per row block of a (b, kh): the codes under the tensor's scale.
 template <int CPR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void tensor_codes_kernel(
-    attn_kv_geom g, const uint16_t *x, const uint32_t *ws, int8_t *codes) {
+    attn_kv_geom g, const uint16_t *x, const float *scales, int8_t *codes) {
   const int lane = threadIdx.x & 63;
   const int pair = blockIdx.y;
   const int L = min(max(g.seq_lens[pair / g.KH], 0), g.max_seq_len);
@@ -278,7 +279,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void t
   const LaneChunks<CPR> lc = lane_chunks<CPR>(g, x, codes, pair, t0, min(L, t0 + rows), lane);
   u32x4_t w[kTensorCPL];
   load_chunks<kTensorCPL, CPR>(lc, x, w);
-  store_codes<kTensorCPL, CPR>(lc, w, make_quantiser(__uint_as_float(*ws) / 127.0f), codes);
+  store_codes<kTensorCPL, CPR>(lc, w, make_quantiser(scales[0]), codes);
 }
 
 // ln(||v_t||_2 + eps): one 16-byte chunk per lane (8 bf16 or 16 int8 values),
@@ -377,36 +378,44 @@ hipError_t launch_quant_partitions(const attn_kv_geom &g, const void *x, int32_t
   return hipGetLastError();
 }
 
-template <int CPR>
-static hipError_t launch_tensor_passes(const attn_kv_geom &g, const uint16_t *x, int8_t *codes, uint32_t *ws,
-                                       hipStream_t s) {
+// Workgroups of the per-tensor passes: four row blocks each, per (b, kh).
+static int64_t tensor_groups(const attn_kv_geom &g) {
   const int rows = tensor_block_rows(g.D);
-  const int nblk = (g.max_seq_len + rows - 1) / rows;
-  const int64_t wgs = ((int64_t)nblk * g.B * g.KH + 3) / 4;
-  hipLaunchKernelGGL(tensor_absmax_kernel<CPR>, dim3((unsigned)(wgs < 2048 ? wgs : 2048)), dim3(256), 0, s, g, x, ws);
+  const int64_t nblk = ((int64_t)g.max_seq_len + rows - 1) / rows;
+  return (nblk + 3) / 4;
+}
+
+size_t quant_tensor_workspace_bytes(const attn_kv_geom &g) {
+  return 256 + 4 * (size_t)(tensor_groups(g) * (int64_t)g.B * g.KH);
+}
+
+template <int CPR>
+static hipError_t launch_tensor_passes(const attn_kv_geom &g, const uint16_t *x, int8_t *codes, float *scales,
+                                       float *wg_max, hipStream_t s) {
+  const dim3 grid((unsigned)tensor_groups(g), g.B * g.KH);
+  hipLaunchKernelGGL(tensor_absmax_kernel<CPR>, grid, dim3(256), 0, s, g, x, wg_max);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(tensor_codes_kernel<CPR>, dim3((nblk + 3) / 4, g.B * g.KH), dim3(256), 0, s, g, x, ws, codes);
+  hipLaunchKernelGGL(tensor_scale_kernel, dim3(1), dim3(256), 0, s, wg_max, (int64_t)grid.x * grid.y, scales);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(tensor_codes_kernel<CPR>, grid, dim3(256), 0, s, g, x, scales, codes);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_tensor(const attn_kv_geom &g, const void *x, int8_t *codes, float *scales, uint32_t *ws,
+hipError_t launch_quant_tensor(const attn_kv_geom &g, const void *x, int8_t *codes, float *scales, void *ws,
                                hipStream_t s) {
-  hipLaunchKernelGGL(zero_word_kernel, dim3(1), dim3(1), 0, s, ws);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (g.B > 0 && g.max_seq_len > 0) {
-    const uint16_t *xs = (const uint16_t *)x;
-    switch (offsets_fit(g, tensor_block_rows(g.D)) ? g.D : 0) {
-      case 64: e = launch_tensor_passes<8>(g, xs, codes, ws, s); break;
-      case 128: e = launch_tensor_passes<16>(g, xs, codes, ws, s); break;
-      case 256: e = launch_tensor_passes<32>(g, xs, codes, ws, s); break;
-      default: e = launch_tensor_passes<0>(g, xs, codes, ws, s);
-    }
-    if (e != hipSuccess) return e;
+  if (g.B == 0 || g.max_seq_len == 0) {
+    hipLaunchKernelGGL(tensor_scale_kernel, dim3(1), dim3(256), 0, s, (const float *)ws, (int64_t)0, scales);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL(tensor_scale_kernel, dim3(1), dim3(1), 0, s, ws, scales);
-  return hipGetLastError();
+  const uint16_t *xs = (const uint16_t *)x;
+  float *wg_max = (float *)((char *)ws + 256);
+  switch (offsets_fit(g, tensor_block_rows(g.D)) ? g.D : 0) {
+    case 64: return launch_tensor_passes<8>(g, xs, codes, scales, wg_max, s);
+    case 128: return launch_tensor_passes<16>(g, xs, codes, scales, wg_max, s);
+    case 256: return launch_tensor_passes<32>(g, xs, codes, scales, wg_max, s);
+    default: return launch_tensor_passes<0>(g, xs, codes, scales, wg_max, s);
+  }
 }
 
 hipError_t launch_value_lognorm(const attn_kv_geom &g, const void *v, int32_t v_dtype, float v_scale, float eps,

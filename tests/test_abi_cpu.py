@@ -140,7 +140,13 @@ def test_merge_and_quant_validation():
     assert L.kv_quant_int8(ctypes.byref(g), FAKE, 0, 1, FAKE, FAKE, None, 0, None) == \
         _lib.ATTN_ERR_WORKSPACE_TOO_SMALL
     n = ctypes.c_size_t(7)
-    assert L.kv_quant_int8_workspace_size(ctypes.byref(g), 0, ctypes.byref(n)) == 0 and n.value >= 4
+    assert L.kv_quant_int8_workspace_size(ctypes.byref(g), 0, ctypes.byref(n)) == 0
+    # per-tensor mode: 256 bytes + one float per four 64-row blocks (D = 128) per (b, kh):
+    # 4096 rows -> 64 blocks -> 16 groups, x 2 sequences x 8 KV heads
+    assert n.value == 256 + 4 * 16 * 2 * 8
+    assert L.kv_quant_int8(ctypes.byref(g), FAKE, 0, 1, FAKE, FAKE, FAKE, n.value - 4, None) == \
+        _lib.ATTN_ERR_WORKSPACE_TOO_SMALL
+    assert L.kv_quant_int8_workspace_size(ctypes.byref(g), 64, ctypes.byref(n)) == 0 and n.value == 0
 
 
 def test_argument_structs_match_the_header_layout(tmp_path):
