@@ -36,9 +36,9 @@ __device__ __forceinline__ float absmax_of_bits(uint32_t acc) {
 // by less than 2^-16; fl32(x / s) differs from x / s by at most half an ulp
 // below 128, 2^-18.  So fl32(x / s) lies within 2^-15 of q, and whenever q
 // is more than 2^-14 away from every half-integer, both round to the same
-// integer.  Values nearer a half-integer (about one in 8000) and scales
-// whose reciprocal overflows take the IEEE divide, so every code equals
-// rint(fl32(x / s)) exactly, ties to even included.
+// integer.  Values nearer a half-integer (about one in 8000) and subnormal
+// scales take the IEEE divide, so every code equals rint(fl32(x / s))
+// exactly, ties to even included.
 struct Quantiser {
   float scale, inv;
   bool fast;
@@ -48,17 +48,21 @@ __device__ __forceinline__ Quantiser make_quantiser(float scale) {
   Quantiser z;
   z.scale = scale;
   z.inv = scale > 0.f ? 1.0f / scale : 0.f;  // scale 0: every code is 0
-  z.fast = z.inv < __builtin_huge_valf();
+  // a subnormal scale takes the divide: its products could meet flushed
+  // subnormal operands, and its reciprocal may overflow
+  z.fast = scale == 0.f || scale >= 0x1p-126f;
   return z;
 }
 
-__device__ __forceinline__ uint32_t pack_code(float c, int byte) {
-  c = fminf(127.f, fmaxf(-127.f, c));
-  return ((uint32_t)(int32_t)c & 0xFFu) << (8 * byte);
-}
+// Adding M = 1.5 * 2^23 to |c| < 2^22 rounds c to an integer, half to even,
+// and leaves that integer in the low mantissa bits: the low byte of the sum's
+// bit pattern is the integer's two's-complement byte, and the sum minus M is
+// the integer itself, exactly.
+constexpr float kRoundMagic = 12582912.0f;
 
 __device__ __forceinline__ u32x2_t codes8(u32x4_t w, const Quantiser &z) {
-  float x[8], c[8];
+#pragma clang fp contract(off)
+  float x[8], t[8];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     x[2 * e] = bf16_lo(w[e]);
@@ -68,16 +72,24 @@ __device__ __forceinline__ u32x2_t codes8(u32x4_t w, const Quantiser &z) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float q = x[i] * z.inv;
-    c[i] = __builtin_rintf(q);
-    near |= fabsf(q - c[i]) > 0.5f - 0x1p-14f;  // q - c is exact
+    t[i] = q + kRoundMagic;                                   // rint(q) + M
+    near |= fabsf(q - (t[i] - kRoundMagic)) > 0.5f - 0x1p-14f;  // |q - rint(q)|, exact
   }
   if (near) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = z.scale > 0.f ? __builtin_rintf(x[i] / z.scale) : 0.f;
+    for (int i = 0; i < 8; ++i) {
+      float c = z.scale > 0.f ? __builtin_rintf(x[i] / z.scale) : 0.f;
+      t[i] = fminf(127.f, fmaxf(-127.f, c)) + kRoundMagic;
+    }
   }
+  // the low bytes of the eight sums, in order
   u32x2_t out;
-  out[0] = pack_code(c[0], 0) | pack_code(c[1], 1) | pack_code(c[2], 2) | pack_code(c[3], 3);
-  out[1] = pack_code(c[4], 0) | pack_code(c[5], 1) | pack_code(c[6], 2) | pack_code(c[7], 3);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(t[4 * h + 1]), __float_as_uint(t[4 * h]), 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(t[4 * h + 3]), __float_as_uint(t[4 * h + 2]), 0x0c0c0400u);
+    out[h] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+  }
   return out;
 }
 

@@ -106,6 +106,26 @@ def test_quant_rounds_exact_ties_to_even():
     np.testing.assert_array_equal(codes, ref_codes)
 
 
+def test_quant_tiny_partitions_with_subnormal_scales():
+    """Partitions whose max |x| is below 127 * 2^-126, so the scale is subnormal (and x / s still spans
+    the code range): codes and scales bit-exact against the oracle's IEEE fp32 arithmetic."""
+    lens = np.array([256], np.int32)
+    w = synth.workload("int8_128k", B=1, KH=1, lens=lens, layout="head_major", seed=73)
+    q, k, v, g = gen_kv(w)
+    kf = (k.astype(np.uint32) << 16).view(np.float32).copy()
+    for p_, mx in enumerate((1e-37, 3e-39, 1e-39, 4e-40)):   # one tiny magnitude per 64-token partition
+        seg = slice(p_ * 64 * g.D, (p_ + 1) * 64 * g.D)
+        kf[seg] = kf[seg] / np.abs(kf[seg]).max() * np.float32(mx)
+    k16 = (kf.view(np.uint32) >> 16).astype(np.uint16)       # truncation keeps them tiny bf16 values
+    ref_codes, ref_scales = oracle.quant_partitions(g.B, g.KH, g.D, g.lens, g.seq_offset, g.stride_h, g.stride_t,
+                                                    k16, 64, 4)
+    codes, scales = gpu_quant(k16, g, 64)
+    assert (ref_scales < np.float32(2.0 ** -126)).all() and (ref_scales > 0).all()
+    np.testing.assert_array_equal(scales, ref_scales)
+    np.testing.assert_array_equal(codes, ref_codes)
+    assert np.abs(codes.astype(np.int32)).max() == 127
+
+
 def test_tensor_quant_bit_exact_and_zero_partitions():
     lens = np.array([300, 5, 129], np.int32)
     w = synth.workload("int8_128k", B=3, KH=2, lens=lens, layout="head_major", seed=47)
