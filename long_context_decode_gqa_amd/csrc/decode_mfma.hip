@@ -132,7 +132,6 @@ decode_mfma_kernel(DecodeParams p) {
   constexpr int KL = TileT::KL;
   constexpr int KB = D / 32;
   constexpr int VW = TileT::VW;
-  typedef typename VecW<VW>::T VV;
   typedef typename std::conditional<KVT == ATTN_BF16, bf16x8_t, f16x8_t>::type OpT;
 
   __shared__ int s_idx[IDX ? kMaxIdxChunk : 1];

@@ -176,11 +176,18 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
   const int col = lane & 15, cg = lane >> 4;
   for (int i = tid; i < kBins; i += 256) s_hist[i] = 0u;
   const int b = pair / o.KH, kh = pair - b * o.KH;
-  // mean query of the group, in fp32
+  // mean query of the group, in fp32, summed in head order; the G (<= 16)
+  // loads of a channel are all issued before the first is used
   for (int d = tid; d < D; d += 256) {
     const uint16_t *q0 = o.q + ((int64_t)b * o.QH + (int64_t)kh * o.G) * D + d;
+    float qv[16];
+#pragma unroll
+    for (int g = 0; g < 16; ++g) qv[g] = bf16_bits_to_f32(q0[(int64_t)min(g, o.G - 1) * D]);
+#pragma unroll
+    for (int g = 0; g < 16; ++g) qv[g] = g < o.G ? qv[g] : 0.f;
     float acc = 0.f;
-    for (int g = 0; g < o.G; ++g) acc += bf16_bits_to_f32(q0[(int64_t)g * D]);
+#pragma unroll
+    for (int g = 0; g < 16; ++g) acc += qv[g];  // adding the zeros past G changes nothing
     s_qbar[d] = acc / (float)o.G;
   }
   __syncthreads();
