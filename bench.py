@@ -293,8 +293,16 @@ def bench_paged(pkg, torch, synth, steps, warmup, dev, page_tokens=64, layout="h
     qd = to_dev(torch, q.reshape(-1), dev).view(w.B, w.QH, w.D)
     p = pkg.prepare_decode(qd, kp, vp, geom, w.G, split_tokens=w.split_tokens)
     ms, dk, mg = time_decode(torch, p, steps, warmup)
-    return dict(ms=ms, decode_ms=dk, merge_ms=mg, kv_bytes=kv_bytes(w.kv_tokens(), KH, D, 2),
-                split=effective_split(torch, w))
+    res = dict(ms=ms, decode_ms=dk, merge_ms=mg, kv_bytes=kv_bytes(w.kv_tokens(), KH, D, 2),
+               split=effective_split(torch, w))
+    if layout == "head_major":
+        # OAM selection (top 4096 of the 128K tokens) over the same pool, value term cached
+        vlog = pkg.oam_value_lognorm(vp, geom, 1e-6)
+        sel = pkg.prepare_oam(qd, kp, geom, w.G, 4096, vlog=vlog, beta=1.0, eps=1e-6)
+        res["oam_select_ms"] = time_calls(torch, sel, steps, warmup)
+        res["value_lognorm_ms"] = time_calls(torch, lambda: pkg.oam_value_lognorm(vp, geom, 1e-6, vlog=vlog),
+                                             steps, warmup)
+    return res
 
 
 def bench_multirow(pkg, torch, synth, steps, warmup, dev, R):
@@ -528,7 +536,11 @@ def main():
         if "paged" in todo:
             for lay in ("head_major", "token_major"):
                 r = bench_paged(pkg, torch, synth, max(5, K // 2), W, dev, layout=lay)
-                others[f"paged_128k_bf16_{lay}"] = summary(r, {"page_tokens": 64})
+                extra = {"page_tokens": 64}
+                if "oam_select_ms" in r:
+                    extra["oam_select_top4096_us"] = round(r["oam_select_ms"] * 1e3, 2)
+                    extra["value_lognorm_us"] = round(r["value_lognorm_ms"] * 1e3, 2)
+                others[f"paged_128k_bf16_{lay}"] = summary(r, extra)
                 del r
         if "oam" in todo:
             try:

@@ -100,8 +100,10 @@ typedef enum {
  *                 ceil(max_seq_len / page_tokens) entries per sequence
  *   page_tokens   tokens per page, a positive multiple of 32
  *   page_stride   elements between pages, > 0, 16-byte aligned
- * Only attn_decode_splitkv with bf16 or int8 KV and no token_idx reads a
- * paged cache; the other calls return ATTN_ERR_UNSUPPORTED for one.  The
+ * attn_decode_splitkv (bf16 or int8 KV, no token_idx), kv_quant_int8 (the
+ * codes go to the same rows of a pool with the same geometry),
+ * oam_value_lognorm and oam_score_topk read a paged cache; the decode's
+ * indexed mode and fp32 KV return ATTN_ERR_UNSUPPORTED for one.  The
  * token-major pool [pages][page_tokens][KH][D] has stride_t = KH*D,
  * stride_h = D, page_stride = page_tokens*KH*D; the head-major pool
  * [pages][KH][page_tokens][D] has stride_t = D, stride_h = page_tokens*D,

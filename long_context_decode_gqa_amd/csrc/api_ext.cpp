@@ -32,9 +32,8 @@ attn_status kv_quant_int8(const attn_kv_geom *geom, const void *x_bf16, int32_t 
   if (!geom) return api_fail(ATTN_ERR_INVALID_ARG, "geom is NULL");
   attn_status st = api_check_geom(*geom, 2, true);
   if (st != ATTN_OK) return st;
-  if (geom->block_table) return api_fail(ATTN_ERR_UNSUPPORTED, "kv_quant_int8 does not read a paged cache");
   if (geom->D % 8 || geom->D > 4096) return api_fail(ATTN_ERR_UNSUPPORTED, "kv_quant_int8 needs D % 8 == 0");
-  if (geom->stride_t % 8 || geom->stride_h % 8)
+  if (geom->stride_t % 8 || geom->stride_h % 8 || (geom->block_table && geom->page_stride % 8))
     return api_fail(ATTN_ERR_INVALID_ARG, "kv_quant_int8 needs strides that are multiples of 8 elements");
   if (partition_tokens < 0 || (partition_tokens > 0 && partition_tokens % 16))
     return api_fail(ATTN_ERR_INVALID_ARG, "partition_tokens must be 0 or a positive multiple of 16");
@@ -68,7 +67,6 @@ attn_status oam_value_lognorm(const attn_kv_geom *geom, const void *v, int32_t v
   const bool i8 = v_dtype == ATTN_I8;
   attn_status st = api_check_geom(*geom, i8 ? 1 : 2, true);
   if (st != ATTN_OK) return st;
-  if (geom->block_table) return api_fail(ATTN_ERR_UNSUPPORTED, "oam_value_lognorm does not read a paged cache");
   if (geom->D != 64 && geom->D != 128 && geom->D != 256)
     return api_fail(ATTN_ERR_UNSUPPORTED, "oam_value_lognorm supports D = 64, 128 or 256");
   if (i8 && (geom->stride_t % 16 || geom->stride_h % 16))
@@ -101,7 +99,6 @@ attn_status plan_oam(const oam_topk_args *a, OamLayout *L) {
   attn_status st = api_check_geom(a->kv, es, true);
   if (st != ATTN_OK) return st;
   const attn_kv_geom &g = a->kv;
-  if (g.block_table) return api_fail(ATTN_ERR_UNSUPPORTED, "oam_score_topk does not read a paged cache");
   if (i8) {
     if (g.stride_t % 16 || g.stride_h % 16) return api_fail(ATTN_ERR_INVALID_ARG, "int8 rows must be 16-byte aligned");
     if (!a->k_scale) return api_fail(ATTN_ERR_INVALID_ARG, "int8 K needs k_scale");
@@ -127,8 +124,11 @@ attn_status plan_oam(const oam_topk_args *a, OamLayout *L) {
   if (!(fabsf(a->softmax_scale) < INFINITY) || !(fabsf(a->beta) < INFINITY))
     return api_fail(ATTN_ERR_INVALID_ARG, "softmax_scale and beta must be finite");
   if (!(a->eps >= 0.f) || !(a->eps < INFINITY)) return api_fail(ATTN_ERR_INVALID_ARG, "eps must be finite and >= 0");
-  if (((int64_t)g.max_seq_len + 64) * g.stride_t * es >= (int64_t(1) << 31))
-    return api_fail(ATTN_ERR_UNSUPPORTED, "one (sequence, KV head) may span at most 2 GiB of rows");
+  // the score pass reads a (sequence, KV head)'s rows, or a page's, through
+  // one buffer resource with 32-bit offsets
+  const int64_t span_rows = g.block_table ? (int64_t)g.page_tokens : (int64_t)g.max_seq_len + 64;
+  if (span_rows * g.stride_t * es >= (int64_t(1) << 31))
+    return api_fail(ATTN_ERR_UNSUPPORTED, "one (sequence, KV head) or page may span at most 2 GiB of rows");
   if (g.B > 0) {
     if (!a->q || !a->k) return api_fail(ATTN_ERR_INVALID_ARG, "q and k are required");
     if (!a->vlog && !a->v) return api_fail(ATTN_ERR_INVALID_ARG, "either vlog or v is required");

@@ -32,7 +32,7 @@ namespace {
 
 constexpr int kBins = 2048;       // 11-bit digits (the 10-bit ones use 1024)
 constexpr int kBlockTok = 2048;   // tokens per workgroup of the candidate and write passes
-constexpr int kCandCap = 4096;    // candidates the select pass holds in LDS
+constexpr int kCandCap = 12288;   // candidates the select pass holds in LDS (10 bytes each)
 constexpr int kMaxBlocks = 1024;  // blocks of kBlockTok per pair (sequences up to 2M tokens)
 constexpr int kMaxSelBlocks = 8192;  // token blocks per pair the block-granular select holds
 
@@ -55,6 +55,9 @@ struct OamDev {
   const int32_t *seq_lens;
   const int64_t *seq_offset;
   int64_t stride_h, stride_t;
+  const int32_t *block_table;  // paged cache (else null): page of row t of sequence b
+  int32_t page_tokens, table_stride;
+  int64_t page_stride;
   const uint16_t *q;
   const void *k;       // bf16 or int8 codes
   const float *k_scale;  // int8: scale of row t is k_scale[pair*k_scale_stride + t/k_part]
@@ -156,7 +159,7 @@ __device__ __forceinline__ float quad_sum3(float v) {
   return v + a + b;
 }
 
-template <int D, int KVT>
+template <int D, int KVT, bool PAGED>
 __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
   constexpr bool I8 = KVT == ATTN_I8;
   constexpr int KB = I8 ? D / 64 : D / 32;  // MFMAs per 16 tokens (16x16x64 int8 or 16x16x32 bf16)
@@ -167,6 +170,9 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
   __shared__ uint32_t s_hist[kBins];
   __shared__ float s_qbar[D];
   __shared__ float s_sc[kScoreTok];
+  // paged: the page ids under each wave's tokens (at most kTilesPerWave * 32 /
+  // 32 + 1 pages, as a page holds a positive multiple of 32 tokens)
+  __shared__ int s_pages[PAGED ? 4 : 1][PAGED ? kScoreTok / 4 / 32 + 1 : 1];
   const int pair = blockIdx.y;
   const int L = pair_len(o, pair);
   const int blk0 = blockIdx.x * kScoreTok;
@@ -238,11 +244,19 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
   }
   // int8: the integer digit sums recombine with weights 1, 256, 65536 in the quad add
   const float dweight = part == 0 ? 1.f : part == 1 ? 256.f : part == 2 ? 65536.f : 0.f;
-  const int64_t head_off = o.seq_offset[b] + (int64_t)kh * o.stride_h;
+  const int64_t head_off = (PAGED ? 0 : o.seq_offset[b]) + (int64_t)kh * o.stride_h;
   const uint32_t rs = (uint32_t)(o.stride_t * ES);
   const int nrec = (int)((uint32_t)(L - 1) * rs + D * ES);
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)o.k + head_off * ES), (short)0, nrec, 0x00020000);
+  // paged: this wave's page ids, staged once (a wave reads only its own)
+  const int wtok0 = blk0 + 32 * kTilesPerWave * wave;  // the wave's first token
+  const int wpage0 = PAGED ? wtok0 / o.page_tokens : 0;
+  if constexpr (PAGED) {
+    const int npg = min(kScoreTok / 4 / 32 + 1, (min(L, wtok0 + 32 * kTilesPerWave) - 1) / o.page_tokens - wpage0 + 1);
+    const int *tbl = o.block_table + (int64_t)b * o.table_stride + wpage0;
+    for (int i = lane; i < npg; i += 64) s_pages[wave][i] = max(tbl[i], 0);
+  }
   const __amdgpu_buffer_rsrc_t ksrs = __builtin_amdgcn_make_buffer_rsrc(
       I8 ? (void *)(o.k_scale + (int64_t)pair * o.k_scale_stride) : nullptr, (short)0,
       I8 ? max(o.k_scale_stride, 1) * 4 : 0, 0x00020000);
@@ -263,11 +277,25 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
   auto load = [&](KTile &R, int tile, bool valid) {
     const int t0 = blk0 + 32 * tile;
     const uint32_t oob = valid ? 0u : 0x80000000u;
+    // a 32-token tile lies in one page: one resource over that page's valid
+    // rows (rows past L read as zero), row t0 % page_tokens + i of it
+    __amdgpu_buffer_rsrc_t tk = krs;
+    int rbase = t0;
+    if constexpr (PAGED) {
+      const int pidx = t0 / o.page_tokens;
+      const int pg = __builtin_amdgcn_readfirstlane(
+          s_pages[wave][min(max(pidx - wpage0, 0), kScoreTok / 4 / 32)]);
+      const int prows = min(o.page_tokens, L - pidx * o.page_tokens);
+      const int nrec_p = prows > 0 ? (int)((uint32_t)(prows - 1) * rs + D * ES) : 0;
+      tk = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)((const char *)o.k + ((int64_t)pg * o.page_stride + head_off) * ES), (short)0, nrec_p, 0x00020000);
+      rbase = t0 - pidx * o.page_tokens;
+    }
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      const uint32_t off = ((uint32_t)(t0 + 16 * tb + col) * rs + 16 * cg) | oob;
+      const uint32_t off = ((uint32_t)(rbase + 16 * tb + col) * rs + 16 * cg) | oob;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) R.k[tb][kb] = __builtin_amdgcn_raw_buffer_load_b128(krs, off + 64 * kb, 0, 0);
+      for (int kb = 0; kb < KB; ++kb) R.k[tb][kb] = __builtin_amdgcn_raw_buffer_load_b128(tk, off + 64 * kb, 0, 0);
       R.vl[tb] = __builtin_amdgcn_raw_buffer_load_b128(vrs, ((uint32_t)(t0 + 16 * tb + 4 * cg) * 4) | oob, 0, 0);
       if constexpr (I8) {
         // k_part is a multiple of 16, so a 16-token block has one scale
@@ -360,41 +388,51 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
 // need-th largest key T among the items of bin b0, and, among the items equal
 // to T, the need'-th smallest index I_T (need' = how many of them are kept).
 // Items come from the candidate list or, if it overflowed, from all scores.
+// Calls f(key, idx) for the items 0..n-1, thread tid taking i = tid + 256 r:
+// the candidate list in LDS, or the pair's whole score row, whose loads are
+// issued 16 per thread before any is used.
+template <bool FROM_LIST, typename F>
+__device__ __forceinline__ void for_items(const uint32_t *ck, const int32_t *ci, const float *sc, int n, F &&f) {
+  const int tid = threadIdx.x;
+  if constexpr (FROM_LIST) {
+    for (int i = tid; i < n; i += 256) f(ck[i], ci[i]);
+  } else {
+    constexpr int U = 16;
+    for (int i0 = 0; i0 < n; i0 += 256 * U) {
+      float v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = sc[min(i0 + tid + 256 * u, n - 1)];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + tid + 256 * u;
+        if (i < n) f(order_key(v[u]), i);
+      }
+    }
+  }
+}
+
 template <bool FROM_LIST>
 __device__ void select_threshold(const OamDev &o, int pair, int n, int b0, int need, const uint32_t *ck,
                                  const int32_t *ci, uint32_t *s_hist, int *s_tmp, int *s_res, uint32_t *T_out,
                                  int *I_out) {
   const int tid = threadIdx.x;
   const float *sc = o.scores + (int64_t)pair * o.L_max;
-  auto item = [&](int i, uint32_t &key, int &idx) {
-    if constexpr (FROM_LIST) {
-      key = ck[i];
-      idx = ci[i];
-    } else {
-      key = order_key(sc[i]);
-      idx = i;
-    }
-  };
   int above;
   // digit 2: key bits 20..10 of the items with top digit b0
   for (int i = tid; i < kBins; i += 256) s_hist[i] = 0u;
   __syncthreads();
-  for (int i = tid; i < n; i += 256) {
-    uint32_t key; int idx;
-    item(i, key, idx);
+  for_items<FROM_LIST>(ck, ci, sc, n, [&](uint32_t key, int idx) {
     if ((int)(key >> 21) == b0) atomicAdd(&s_hist[(key >> 10) & 0x7FFu], 1u);
-  }
+  });
   __syncthreads();
   uint32_t prefix = ((uint32_t)b0 << 11) | (uint32_t)select_bin(s_hist, kBins, need, &above, s_tmp, s_res);
   need -= above;
   // digit 3: key bits 9..0
   for (int i = tid; i < kBins; i += 256) s_hist[i] = 0u;
   __syncthreads();
-  for (int i = tid; i < n; i += 256) {
-    uint32_t key; int idx;
-    item(i, key, idx);
+  for_items<FROM_LIST>(ck, ci, sc, n, [&](uint32_t key, int idx) {
     if ((key >> 10) == prefix) atomicAdd(&s_hist[key & 0x3FFu], 1u);
-  }
+  });
   __syncthreads();
   const uint32_t T = (prefix << 10) | (uint32_t)select_bin(s_hist, 1024, need, &above, s_tmp, s_res);
   need -= above;
@@ -411,21 +449,17 @@ __device__ void select_threshold(const OamDev &o, int pair, int n, int b0, int n
   // bits of the index, bins reversed so "largest bin" means smallest index
   for (int i = tid; i < kBins; i += 256) s_hist[i] = 0u;
   __syncthreads();
-  for (int i = tid; i < n; i += 256) {
-    uint32_t key; int idx;
-    item(i, key, idx);
+  for_items<FROM_LIST>(ck, ci, sc, n, [&](uint32_t key, int idx) {
     if (key == T) atomicAdd(&s_hist[2047 - (idx >> 10)], 1u);
-  }
+  });
   __syncthreads();
   const int ihi = 2047 - select_bin(s_hist, kBins, need, &above, s_tmp, s_res);
   need -= above;
   for (int i = tid; i < kBins; i += 256) s_hist[i] = 0u;
   __syncthreads();
-  for (int i = tid; i < n; i += 256) {
-    uint32_t key; int idx;
-    item(i, key, idx);
+  for_items<FROM_LIST>(ck, ci, sc, n, [&](uint32_t key, int idx) {
     if (key == T && (idx >> 10) == ihi) atomicAdd(&s_hist[1023 - (idx & 0x3FF)], 1u);
-  }
+  });
   __syncthreads();
   const int ilo = 1023 - select_bin(s_hist, 1024, need, &above, s_tmp, s_res);
   *T_out = T;
@@ -532,7 +566,7 @@ __global__ __launch_bounds__(256) void oam_select_kernel(OamDev o) {
   const bool in_lds = C > 0 && C <= kCandCap;
   if (in_lds) {
     // Gather into LDS: item i lies in the block j with s_pre[j] <= i < s_pre[j+1].
-    constexpr int kPer = kCandCap / 256;
+    constexpr int kPer = 16;  // loads of one gather round per thread
     const uint32_t *gk = o.cand_key + (int64_t)pair * o.L_max;
     const int32_t *gi = o.cand_idx + (int64_t)pair * o.L_max;
     // Owner map first (LDS only): wave w writes block j's number over its
@@ -543,22 +577,24 @@ __global__ __launch_bounds__(256) void oam_select_kernel(OamDev o) {
     for (int j = wave; j < nblk; j += 4)
       for (int l = s_pre[j] + lane; l < s_pre[j + 1]; l += 64) s_own[l] = (uint16_t)j;
     __syncthreads();
-    uint32_t kr[kPer];
-    int32_t ir[kPer];
+    for (int i0 = 0; i0 < C; i0 += 256 * kPer) {
+      uint32_t kr[kPer];
+      int32_t ir[kPer];
 #pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-      const int i = min(tid + 256 * r, C - 1);
-      const int j = s_own[i];
-      const int64_t src = (int64_t)j * kBlockTok + (i - s_pre[j]);
-      kr[r] = gk[src];
-      ir[r] = gi[src];
-    }
+      for (int r = 0; r < kPer; ++r) {
+        const int i = min(i0 + tid + 256 * r, C - 1);
+        const int j = s_own[i];
+        const int64_t src = (int64_t)j * kBlockTok + (i - s_pre[j]);
+        kr[r] = gk[src];
+        ir[r] = gi[src];
+      }
 #pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-      const int i = tid + 256 * r;
-      if (i < C) {
-        s_ck[i] = kr[r];
-        s_ci[i] = ir[r];
+      for (int r = 0; r < kPer; ++r) {
+        const int i = i0 + tid + 256 * r;
+        if (i < C) {
+          s_ck[i] = kr[r];
+          s_ci[i] = ir[r];
+        }
       }
     }
     __syncthreads();
@@ -569,19 +605,11 @@ __global__ __launch_bounds__(256) void oam_select_kernel(OamDev o) {
   for (int j = tid; j < nblk; j += 256) s_kept[j] = 0;
   __syncthreads();
   const float *sc = o.scores + (int64_t)pair * o.L_max;
-  const int nitems = in_lds ? C : L;
-  for (int i = tid; i < nitems; i += 256) {
-    uint32_t key;
-    int idx;
-    if (in_lds) {
-      key = s_ck[i];
-      idx = s_ci[i];
-    } else {
-      key = order_key(sc[i]);
-      idx = i;
-    }
+  auto count_kept = [&](uint32_t key, int idx) {
     if ((int)(key >> 21) == b0 && (key > T || (key == T && idx <= I_T))) atomicAdd(&s_kept[idx / kBlockTok], 1);
-  }
+  };
+  if (in_lds) for_items<true>(s_ck, s_ci, sc, C, count_kept);
+  else for_items<false>(s_ck, s_ci, sc, L, count_kept);
   __syncthreads();
   int run = 0;
   for (int j0 = 0; j0 < nblk; j0 += 256) {
@@ -741,6 +769,18 @@ __global__ __launch_bounds__(256) void oam_block_select_kernel(OamDev o) {
 
 }  // namespace
 
+template <bool PAGED>
+static void launch_score(const OamDev &o, int kv_dtype, int D, dim3 grid, hipStream_t s) {
+  const dim3 blk(256);
+  if (kv_dtype == ATTN_I8) {
+    if (D == 128) hipLaunchKernelGGL((oam_score_kernel<128, ATTN_I8, PAGED>), grid, blk, 0, s, o);
+    else hipLaunchKernelGGL((oam_score_kernel<64, ATTN_I8, PAGED>), grid, blk, 0, s, o);
+  } else {
+    if (D == 128) hipLaunchKernelGGL((oam_score_kernel<128, ATTN_BF16, PAGED>), grid, blk, 0, s, o);
+    else hipLaunchKernelGGL((oam_score_kernel<64, ATTN_BF16, PAGED>), grid, blk, 0, s, o);
+  }
+}
+
 hipError_t launch_oam(const oam_topk_args &a, const OamPlan &plan, hipStream_t s) {
   const attn_kv_geom &g = a.kv;
   const int npairs = g.B * g.KH;
@@ -757,6 +797,10 @@ hipError_t launch_oam(const oam_topk_args &a, const OamPlan &plan, hipStream_t s
   o.seq_offset = g.seq_offset;
   o.stride_h = g.stride_h;
   o.stride_t = g.stride_t;
+  o.block_table = g.block_table;
+  o.page_tokens = g.page_tokens;
+  o.table_stride = g.table_stride;
+  o.page_stride = g.page_stride;
   o.q = (const uint16_t *)a.q;
   o.k = a.k;
   // a per-tensor K scale is one partition longer than any sequence
@@ -799,13 +843,8 @@ hipError_t launch_oam(const oam_topk_args &a, const OamPlan &plan, hipStream_t s
       if (e != hipSuccess) return e;
     }
     dim3 sgrid((g.max_seq_len + kScoreTok - 1) / kScoreTok, npairs), blk(256);
-    if (a.kv_dtype == ATTN_I8) {
-      if (g.D == 128) hipLaunchKernelGGL((oam_score_kernel<128, ATTN_I8>), sgrid, blk, 0, s, o);
-      else hipLaunchKernelGGL((oam_score_kernel<64, ATTN_I8>), sgrid, blk, 0, s, o);
-    } else {
-      if (g.D == 128) hipLaunchKernelGGL((oam_score_kernel<128, ATTN_BF16>), sgrid, blk, 0, s, o);
-      else hipLaunchKernelGGL((oam_score_kernel<64, ATTN_BF16>), sgrid, blk, 0, s, o);
-    }
+    if (g.block_table) launch_score<true>(o, a.kv_dtype, g.D, sgrid, s);
+    else launch_score<false>(o, a.kv_dtype, g.D, sgrid, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (!block_mode) {
       hipLaunchKernelGGL(oam_candidate_kernel, dim3(nblk, npairs), blk, 0, s, o);

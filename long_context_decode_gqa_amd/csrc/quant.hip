@@ -104,6 +104,34 @@ __device__ __forceinline__ float block_max(float v, float *s_red) {
   return r;
 }
 
+// Element offset of row t of one (b, kh): contiguous caches add t rows to
+// the sequence's offset; a paged cache looks the row's page up in the
+// sequence's block-table row (the page holds page_tokens consecutive rows).
+struct RowAddr {
+  const int32_t *tbl;  // paged: block_table + b * table_stride; else null
+  int64_t base;        // contiguous: seq_offset[b] + kh * stride_h; paged: kh * stride_h
+  int64_t stride_t, page_stride;
+  int page_tokens;
+  __device__ __forceinline__ int64_t row(int t) const {
+    if (tbl) {
+      const int pg = tbl[t / page_tokens];
+      return (int64_t)pg * page_stride + base + (int64_t)(t % page_tokens) * stride_t;
+    }
+    return base + (int64_t)t * stride_t;
+  }
+};
+
+__device__ __forceinline__ RowAddr row_addr(const attn_kv_geom &g, int pair) {
+  const int b = pair / g.KH, kh = pair - b * g.KH;
+  RowAddr r;
+  r.tbl = g.block_table ? g.block_table + (int64_t)b * g.table_stride : nullptr;
+  r.base = (g.block_table ? 0 : g.seq_offset[b]) + (int64_t)kh * g.stride_h;
+  r.stride_t = g.stride_t;
+  r.page_stride = g.page_stride;
+  r.page_tokens = g.page_tokens;
+  return r;
+}
+
 // A row block of one wave: rows [t0, t1) of one (b, kh) as 16-byte chunks
 // (8 bf16 values), row-major; chunk j of a lane is chunk lane + 64 j of the
 // block.  CPR > 0 is the number of chunks per row known at compile time (a
@@ -116,35 +144,36 @@ __device__ __forceinline__ float block_max(float v, float *s_red) {
 // run time, with 64-bit offsets and guarded accesses.
 template <int CPR>
 struct LaneChunks {
-  int64_t blk;  // element offset of the block's first row
+  int64_t blk;  // CPR > 0: element offset of the block's first row
   __amdgpu_buffer_rsrc_t src, dst;
   uint32_t off0, step;  // CPR > 0: lane's element offset from blk, step per j
-  int64_t stride_t;
-  int cpr, n, rows, lane;
+  RowAddr ra;           // CPR = 0: rows through their (possibly paged) address
+  int t0, cpr, n, rows, lane;
   __device__ __forceinline__ int64_t off(int j) const {
     const int i = lane + 64 * j, r = i / cpr;
-    return blk + (int64_t)r * stride_t + 8 * (i - r * cpr);
+    return ra.row(t0 + r) + 8 * (i - r * cpr);
   }
 };
 
 template <int CPR>
 __device__ __forceinline__ LaneChunks<CPR> lane_chunks(const attn_kv_geom &g, const uint16_t *x, int8_t *codes,
                                                        int pair, int t0, int t1, int lane) {
-  const int b = pair / g.KH, kh = pair - b * g.KH;
   LaneChunks<CPR> c;
-  c.blk = g.seq_offset[b] + (int64_t)kh * g.stride_h + (int64_t)t0 * g.stride_t;
-  c.stride_t = g.stride_t;
+  c.ra = row_addr(g, pair);
+  c.t0 = t0;
   c.cpr = g.D / 8;
   c.rows = t1 - t0;
   c.n = c.rows * c.cpr;
   c.lane = lane;
-  if constexpr (CPR > 0) {
+  if constexpr (CPR > 0) {  // contiguous caches only
+    c.blk = c.ra.base + (int64_t)t0 * g.stride_t;
     const int span = (c.rows - 1) * (int)g.stride_t + g.D;  // elements from the first row to the end of the last
     c.src = __builtin_amdgcn_make_buffer_rsrc((void *)(x + c.blk), (short)0, 2 * span, 0x00020000);
     c.dst = __builtin_amdgcn_make_buffer_rsrc((void *)(codes + c.blk), (short)0, span, 0x00020000);
     c.off0 = (uint32_t)(lane / CPR) * (uint32_t)g.stride_t + 8u * (uint32_t)(lane % CPR);
     c.step = (uint32_t)(64 / CPR) * (uint32_t)g.stride_t;
   } else {
+    c.blk = 0;
     c.off0 = c.step = 0u;
   }
   return c;
@@ -214,15 +243,15 @@ __global__ __launch_bounds__(256) void quant_partition_kernel(attn_kv_geom g, co
                                                               int32_t scale_stride, int8_t *codes, float *scales) {
   __shared__ float s_red[4];
   const int pair = blockIdx.y;
-  const int b = pair / g.KH, kh = pair - b * g.KH;
+  const int b = pair / g.KH;
   const int L = min(max(g.seq_lens[b], 0), g.max_seq_len);
   const int t0 = blockIdx.x * part;
   if (t0 >= L) return;
   const int cpr = g.D / 8, n = (min(L, t0 + part) - t0) * cpr;
-  const int64_t base = g.seq_offset[b] + (int64_t)kh * g.stride_h;
+  const RowAddr ra = row_addr(g, pair);
   auto off = [&](int i) -> int64_t {
     const int r = i / cpr;
-    return base + (int64_t)(t0 + r) * g.stride_t + 8 * (i - r * cpr);
+    return ra.row(t0 + r) + 8 * (i - r * cpr);
   };
   uint32_t mb = 0u;
   for (int i = threadIdx.x; i < n; i += 256) mb = absmax8_bits(*(const u32x4_t *)(x + off(i)), mb);
@@ -306,18 +335,18 @@ __global__ __launch_bounds__(256) void value_lognorm_kernel(attn_kv_geom g, cons
   constexpr int RPB = 256 / LPR;
   constexpr int EPC = I8 ? 16 : 8;  // elements per lane chunk
   const int pair = blockIdx.y;
-  const int b = pair / g.KH, kh = pair - b * g.KH;
+  const int b = pair / g.KH;
   const int L = min(max(g.seq_lens[b], 0), g.max_seq_len);
   const int tb = blockIdx.x * RPB * kLognormRPT + threadIdx.x / LPR;
   const int c = threadIdx.x % LPR;
-  const int64_t e0 = g.seq_offset[b] + (int64_t)kh * g.stride_h + EPC * c;
+  const RowAddr ra = row_addr(g, pair);
   u32x4_t w[kLognormRPT];
 #pragma unroll
   for (int j = 0; j < kLognormRPT; ++j) {
     const int t = tb + RPB * j;
     w[j] = (u32x4_t){0u, 0u, 0u, 0u};
     if (t < L) {
-      const int64_t e = e0 + (int64_t)t * g.stride_t;
+      const int64_t e = ra.row(t) + EPC * c;
       if constexpr (I8) w[j] = *(const u32x4_t *)((const int8_t *)v + e);
       else w[j] = *(const u32x4_t *)((const uint16_t *)v + e);
     }
@@ -347,7 +376,8 @@ __global__ __launch_bounds__(256) void value_lognorm_kernel(attn_kv_geom g, cons
 }  // namespace
 
 // Whether a block of `rows` rows spans less than 2^30 elements, so that the
-// compile-time-geometry kernels may take 32-bit offsets within it.
+// compile-time-geometry kernels may take 32-bit offsets within it (contiguous
+// caches; a paged cache takes the run-time path, row by row).
 static bool offsets_fit(const attn_kv_geom &g, int64_t rows) {
   return rows * g.stride_t + g.D < (int64_t(1) << 30);
 }
@@ -357,7 +387,7 @@ static void launch_partition_wave(const attn_kv_geom &g, const uint16_t *x, int3
                                   int32_t scale_stride, int8_t *codes, float *scales, hipStream_t s) {
   dim3 grid((nparts + 3) / 4, g.B * g.KH), blk(256);
   // a lane's chunk offsets reach 64 * CPL chunks into the partition
-  switch (offsets_fit(g, 64 * CPL / (g.D / 8) + 1) ? g.D : 0) {
+  switch (!g.block_table && offsets_fit(g, 64 * CPL / (g.D / 8) + 1) ? g.D : 0) {
     case 64:
       hipLaunchKernelGGL((quant_partition_wave_kernel<CPL, 8>), grid, blk, 0, s, g, x, part, nparts, scale_stride,
                          codes, scales);
@@ -422,7 +452,7 @@ hipError_t launch_quant_tensor(const attn_kv_geom &g, const void *x, int8_t *cod
   }
   const uint16_t *xs = (const uint16_t *)x;
   float *wg_max = (float *)((char *)ws + 256);
-  switch (offsets_fit(g, tensor_block_rows(g.D)) ? g.D : 0) {
+  switch (!g.block_table && offsets_fit(g, tensor_block_rows(g.D)) ? g.D : 0) {
     case 64: return launch_tensor_passes<8>(g, xs, codes, scales, wg_max, s);
     case 128: return launch_tensor_passes<16>(g, xs, codes, scales, wg_max, s);
     case 256: return launch_tensor_passes<32>(g, xs, codes, scales, wg_max, s);

@@ -172,7 +172,7 @@ def test_argument_structs_match_the_header_layout(tmp_path):
             assert got[(cname, f[0])] == getattr(cls, f[0]).offset, (cname, f[0])
 
 
-def test_paged_geometry_is_validated_and_limited_to_decode():
+def test_paged_geometry_is_validated():
     L = _lib.load()
     paged = dict(g_block_table=FAKE, g_page_tokens=64, g_table_stride=64, g_page_stride=64 * 8 * 128,
                  g_seq_offset=None)
@@ -188,9 +188,21 @@ def test_paged_geometry_is_validated_and_limited_to_decode():
         if "g_page_tokens" in over and over["g_page_tokens"] == 32:
             a.kv.table_stride = 128
         assert _ws(a)[0] == status, over
+    # the quantiser, the value norms and OAM selection read a paged cache too; their geometry
+    # checks still run before any launch (a page stride of 4 bf16 elements is not 16-byte aligned)
     g = _lib.AttnKvGeom(2, 8, 128, 4096, FAKE, None, 128, 1024)
-    g.block_table, g.page_tokens, g.table_stride, g.page_stride = FAKE, 64, 64, 64 * 1024
-    assert L.kv_quant_int8(ctypes.byref(g), FAKE, 64, 64, FAKE, FAKE, None, 0, None) == _lib.ATTN_ERR_UNSUPPORTED
+    g.block_table, g.page_tokens, g.table_stride, g.page_stride = FAKE, 64, 64, 64 * 1024 + 4
+    assert L.kv_quant_int8(ctypes.byref(g), FAKE, 64, 64, FAKE, FAKE, None, 0, None) == _lib.ATTN_ERR_INVALID_ARG
     vlog = ctypes.c_void_p(FAKE)
     assert L.oam_value_lognorm(ctypes.byref(g), FAKE, _lib.ATTN_BF16, 1.0, 1e-6, vlog, 4096, None) == \
-        _lib.ATTN_ERR_UNSUPPORTED
+        _lib.ATTN_ERR_INVALID_ARG
+    n = ctypes.c_size_t(0)
+    assert L.kv_quant_int8_workspace_size(ctypes.byref(g), 0, ctypes.byref(n)) == _lib.ATTN_ERR_INVALID_ARG
+    g.page_stride = 64 * 1024
+    assert L.kv_quant_int8_workspace_size(ctypes.byref(g), 0, ctypes.byref(n)) == 0 and n.value > 256
+    o = _lib.OamTopkArgs()
+    o.kv, o.G, o.q, o.k, o.kv_dtype, o.vlog, o.vlog_stride = g, 8, FAKE, FAKE, _lib.ATTN_BF16, FAKE, 4096
+    o.top_k, o.idx_out, o.n_kept, o.beta, o.eps = 512, FAKE, FAKE, 1.0, 1e-6
+    assert L.oam_score_topk_workspace_size(ctypes.byref(o), ctypes.byref(n)) == 0 and n.value > 0
+    o.kv.page_stride = 64 * 1024 + 4
+    assert L.oam_score_topk_workspace_size(ctypes.byref(o), ctypes.byref(n)) == _lib.ATTN_ERR_INVALID_ARG

@@ -164,13 +164,15 @@ def _topk_from_vlog(vlog_row, top_k, D=128, G=8):
     return idx.cpu().numpy()[0], int(nk.cpu().numpy()[0])
 
 
-def test_oam_many_candidates_in_threshold_bin():
-    # 20000 distinct scores inside one top-digit bin ([1.0, 1.25)): more
-    # candidates than the list holds, so the selection reads the scores
+@pytest.mark.parametrize("n", [10000, 20000])
+def test_oam_many_candidates_in_threshold_bin(n):
+    # n distinct scores inside one top-digit bin ([1.0, 1.25)): 10000 candidates
+    # are gathered into LDS in several rounds; 20000 are more than the list
+    # holds, so the selection reads the pair's scores
     rng = np.random.default_rng(70)
-    vl = (1.0 + 0.2 * rng.permutation(20000) / 20000.0).astype(np.float32)
-    log_case("oam candidate overflow")
-    for top_k in (1, 4096, 12345, 19999):
+    vl = (1.0 + 0.2 * rng.permutation(n) / n).astype(np.float32)
+    log_case(f"oam candidates in one bin n={n}")
+    for top_k in (1, 4096, n // 2 + 345, n - 1):
         idx, nk = _topk_from_vlog(vl, top_k)
         assert nk == top_k
         np.testing.assert_array_equal(idx[:nk], exact_topk(vl, top_k))
@@ -180,7 +182,7 @@ def test_oam_tie_group_cut_at_threshold():
     # few distinct values, so the K-th key has many equals; the kept ones must
     # be the lowest indices of that tie group (list path and overflow path)
     rng = np.random.default_rng(71)
-    for L, top_k in ((3000, 1000), (3000, 1), (9000, 4500)):
+    for L, top_k in ((3000, 1000), (3000, 1), (9000, 4500), (20000, 10000)):
         vl = (1.0 + 0.01 * rng.integers(0, 7, L)).astype(np.float32)
         log_case(f"oam tie group L={L} K={top_k}")
         idx, nk = _topk_from_vlog(vl, top_k)

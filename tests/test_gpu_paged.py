@@ -127,3 +127,110 @@ def test_paged_128k_full_size_equals_contiguous():
                        split_tokens=w.split_tokens)
     np.testing.assert_array_equal(out_p, out_c)
     np.testing.assert_array_equal(lse_p, lse_c)
+
+
+# --- the rest of the path over a paged cache: quantisation when rows are written, the cached
+# value norms, and OAM selection read the pool through the same block table; each must equal
+# its contiguous counterpart bit for bit (the contiguous results are compared with the oracle
+# in test_gpu_int8.py and test_gpu_oam.py) ---
+
+def pool_rows(pool, g, table, P, st, sh, ps, b, kh, L):
+    """The logical rows (b, kh, 0..L-1) of a page pool, as an array [L, D]."""
+    t = np.arange(L)
+    start = table[b, t // P].astype(np.int64) * ps + kh * sh + (t % P) * st
+    return pool[start[:, None] + np.arange(g.D)[None, :]]
+
+
+def valid_mask(g, table, P, st, sh, ps, n):
+    m = np.zeros(n, bool)
+    for b in range(g.B):
+        for kh in range(g.KH):
+            L = int(g.lens[b])
+            t = np.arange(L)
+            start = table[b, t // P].astype(np.int64) * ps + kh * sh + (t % P) * st
+            m[(start[:, None] + np.arange(g.D)[None, :]).reshape(-1)] = True
+    return m
+
+
+@pytest.mark.parametrize("P,layout,part", [(32, "token_major", 64), (64, "head_major", 64), (128, "token_major", 16),
+                                           (64, "head_major", 128)])
+def test_paged_quantisation_equals_contiguous(P, layout, part):
+    """K per token partition (partitions may straddle pages) and V per tensor over a page pool:
+    codes of every logical row and the scales equal the contiguous quantiser's; pool rows that
+    hold no token keep the zeros the codes started from."""
+    lens = np.array([1, 63, 700, 2049, 0, 130], np.int32)
+    w = synth.workload("int8_128k", B=len(lens), KH=2, lens=lens, layout="head_major", seed=200 + P + part)
+    q, k, v, g = synth.generate(w)
+    log_case(f"paged quant P={P} {layout} part={part}")
+    geom = dev_geom(g)
+    kc, ks = pkg.kv_quant_int8(to_dev(k), geom, part)
+    vc, vs = pkg.kv_quant_int8(to_dev(v), geom, 0)
+    kp, table, st, sh, ps = make_pool(k, g, P, layout, seed=P, junk=0)
+    vp, _, _, _, _ = make_pool(v, g, P, layout, seed=P, junk=0)
+    pg = paged_geom(g, table, P, st, sh, ps)
+    kcp, ksp = pkg.kv_quant_int8(to_dev(kp), pg, part)
+    vcp, vsp = pkg.kv_quant_int8(to_dev(vp), pg, 0)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ksp.cpu().numpy(), ks.cpu().numpy())
+    assert vsp.item() == vs.item()
+    kc, vc, kcp, vcp = kc.cpu().numpy(), vc.cpu().numpy(), kcp.cpu().numpy(), vcp.cpu().numpy()
+    for b in range(g.B):
+        for kh in range(g.KH):
+            L = int(lens[b])
+            np.testing.assert_array_equal(pool_rows(kcp, g, table, P, st, sh, ps, b, kh, L),
+                                          logical_rows(kc, g, b, kh, L))
+            np.testing.assert_array_equal(pool_rows(vcp, g, table, P, st, sh, ps, b, kh, L),
+                                          logical_rows(vc, g, b, kh, L))
+    m = valid_mask(g, table, P, st, sh, ps, kcp.size)
+    assert not kcp[~m].any() and not vcp[~m].any()
+
+
+@pytest.mark.parametrize("P,layout,kv", [(32, "token_major", "bf16"), (64, "head_major", "bf16"),
+                                         (64, "token_major", "int8")])
+def test_paged_value_norms_and_oam_equal_contiguous(P, layout, kv):
+    """Value log-norms, OAM scores and kept sets (token and 64-token block selection, value term
+    cached or read from V) over a page pool equal the contiguous results bit for bit."""
+    lens = np.array([9000, 1, 8192, 3000, 0, 16500], np.int32)
+    w = synth.workload("oam_128k", B=len(lens), KH=2, lens=lens, layout="head_major", seed=300 + P)
+    q, k, v, g = synth.generate(w)
+    log_case(f"paged oam P={P} {layout} {kv}")
+    geom = dev_geom(g)
+    qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
+    kd, vd = to_dev(k), to_dev(v)
+    extra, vsc = {}, 1.0
+    if kv == "int8":
+        kd, ks = pkg.kv_quant_int8(kd, geom, 64)
+        vd, vs = pkg.kv_quant_int8(vd, geom, 0)
+        torch.cuda.synchronize()
+        vsc = float(vs.item())
+        extra = dict(k_scale=ks, k_part_tokens=64, v_scale=vsc)
+    kh_, vh_ = (kd.cpu().numpy(), vd.cpu().numpy()) if kv == "int8" else (k, v)   # host bf16 stays uint16
+    kp, table, st, sh, ps = make_pool(kh_, g, P, layout, seed=P + 1, junk=0)
+    vp, _, _, _, _ = make_pool(vh_, g, P, layout, seed=P + 1, junk=0)
+    pg = paged_geom(g, table, P, st, sh, ps)
+    kpd, vpd = to_dev(kp), to_dev(vp)
+    vl = pkg.oam_value_lognorm(vd, geom, w.eps, v_scale=vsc)
+    vlp = pkg.oam_value_lognorm(vpd, pg, w.eps, v_scale=vsc)
+    torch.cuda.synchronize()
+    vl_h, vlp_h = vl.cpu().numpy(), vlp.cpu().numpy()
+    for b in range(g.B):
+        for kh in range(g.KH):
+            L = int(lens[b])
+            np.testing.assert_array_equal(vlp_h[b * g.KH + kh, :L], vl_h[b * g.KH + kh, :L])
+    for mode in (dict(vlog=vl), dict(v=vd), dict(vlog=vl, block_tokens=64)):
+        top_k = 8 if "block_tokens" in mode else 700
+        n = w.B * w.KH
+        sc = torch.full((n, int(g.max_len)), float("nan"), dtype=torch.float32, device=DEV)
+        scp = torch.full_like(sc, float("nan"))
+        modep = {kk: (vpd if kk == "v" else vv) for kk, vv in mode.items()}
+        idx, nk = pkg.oam_score_topk(qd, kd, geom, w.G, top_k, scores_out=sc, beta=w.beta, eps=w.eps, **mode, **extra)
+        idxp, nkp = pkg.oam_score_topk(qd, kpd, pg, w.G, top_k, scores_out=scp, beta=w.beta, eps=w.eps, **modep,
+                                       **extra)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(nkp.cpu().numpy(), nk.cpu().numpy())
+        np.testing.assert_array_equal(idxp.cpu().numpy(), idx.cpu().numpy())
+        s_h, sp_h = sc.cpu().numpy(), scp.cpu().numpy()
+        for b in range(g.B):
+            for kh in range(g.KH):
+                L = int(lens[b])
+                np.testing.assert_array_equal(sp_h[b * g.KH + kh, :L], s_h[b * g.KH + kh, :L])
