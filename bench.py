@@ -135,17 +135,6 @@ def dev_geom(pkg, torch, g, dev):
                           torch.from_numpy(g.seq_offset).to(dev), g.stride_h, g.stride_t)
 
 
-def effective_split(torch, w) -> int:
-    """Tokens per split-KV chunk of a dense (no index list) bf16/int8 decode of
-    workload w: as given, or for 0 the library default, about one chunk per
-    decode worker of a full grid: 32 * clamp(T_max / 2048, 1, 64) with T_max
-    the tiles of 32 tokens at the longest length (G <= 16 here)."""
-    if w.split_tokens:
-        return w.split_tokens
-    t_max = w.B * w.KH * (-(-int(max(w.lens)) // 32))
-    return 32 * min(max(t_max // 2048, 1), 64)
-
-
 def time_decode(torch, prepared, steps, warmup):
     """Returns (ms per step, mean decode-kernel ms, mean merge ms).
 
@@ -184,7 +173,7 @@ def bench_dense(pkg, torch, synth, name, steps, warmup, dev, **over):
     ms, dk, mg = time_decode(torch, p, steps, warmup)
     tokens = w.kv_tokens()
     kvb = kv_bytes(tokens, w.KH, w.D, 2)
-    split = effective_split(torch, w)
+    split = p.split_tokens
     nparts = w.QH * sum(-(-int(L) // split) for L in w.lens)
     algo = kvb + w.B * w.QH * w.D * 2 + partial_bytes(nparts, w.D)
     return dict(w=w, q=q, g=g, ms=ms, decode_ms=dk, merge_ms=mg, kv_bytes=kvb,
@@ -258,7 +247,7 @@ def bench_int8(pkg, torch, synth, steps, warmup, dev):
         schemes[name] = {"us_per_step": round(ms_s * 1e3, 2), "decode_kernel_us": round(dk_s * 1e3, 2),
                          "kv_gbs": round(b / ms_s / 1e6, 1), "rel_err_vs_bf16": round(err, 5)}
         del ps
-    return dict(ms=ms, decode_ms=dk, merge_ms=mg, kv_bytes=kvb, split=effective_split(torch, w), schemes=schemes,
+    return dict(ms=ms, decode_ms=dk, merge_ms=mg, kv_bytes=kvb, split=p.split_tokens, schemes=schemes,
                 quant=quant)
 
 
@@ -294,7 +283,7 @@ def bench_paged(pkg, torch, synth, steps, warmup, dev, page_tokens=64, layout="h
     p = pkg.prepare_decode(qd, kp, vp, geom, w.G, split_tokens=w.split_tokens)
     ms, dk, mg = time_decode(torch, p, steps, warmup)
     res = dict(ms=ms, decode_ms=dk, merge_ms=mg, kv_bytes=kv_bytes(w.kv_tokens(), KH, D, 2),
-               split=effective_split(torch, w))
+               split=p.split_tokens)
     if layout == "head_major":
         # OAM selection (top 4096 of the 128K tokens) over the same pool, value term cached
         vlog = pkg.oam_value_lognorm(vp, geom, 1e-6)
@@ -318,7 +307,7 @@ def bench_multirow(pkg, torch, synth, steps, warmup, dev, R):
     p = pkg.prepare_decode(qd, kd, vd, geom, w.G, split_tokens=w.split_tokens, q_rows=R)
     ms, dk, mg = time_decode(torch, p, steps, warmup)
     return dict(ms=ms, decode_ms=dk, merge_ms=mg, kv_bytes=kv_bytes(w.kv_tokens(), w.KH, w.D, 2),
-                split=effective_split(torch, w))
+                split=p.split_tokens)
 
 
 def bench_oam(pkg, torch, synth, steps, warmup, dev):
@@ -447,7 +436,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--headline-only", action="store_true")
-    ap.add_argument("--others", default="gqa32k,ragged,int8,oam,paged,multirow",
+    ap.add_argument("--others", default="gqa32k,tp8,ragged,int8,oam,paged,multirow",
                     help="comma-separated other workloads to time after the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -513,6 +502,13 @@ def main():
             r = bench_dense(pkg, torch, synth, "gqa32k", max(5, K // 2), W, dev)
             others["gqa32k_bf16"] = summary(r)
             del r
+        if "tp8" in todo:
+            # one GPU's share of a tensor-parallel split over 8 GPUs by KV heads (KH = 8 -> 1 per GPU):
+            # the same per-head work at 1/8 of the bytes, where fixed costs weigh more
+            for name in ("gqa32k", "dense128k"):
+                r = bench_dense(pkg, torch, synth, name, max(5, K // 2), W, dev, KH=1, split_tokens=0)
+                others[f"{name}_tp8_share_kh1"] = summary(r, {"kv_heads": 1, "batch": int(r["w"].B)})
+                del r
         if "ragged" in todo:
             r = bench_dense(pkg, torch, synth, "ragged", max(5, K // 2), W, dev)
             others["ragged_bf16"] = summary(r, {"total_kv_tokens_per_head": r["tokens"],

@@ -198,6 +198,12 @@ typedef struct {
  * arguments attn_decode_splitkv would reject. */
 attn_status attn_decode_workspace_size(const attn_decode_args *args, size_t *bytes);
 
+/* Host-only: the chunk length in tokens (split_tokens) attn_decode_splitkv
+ * uses for these args: the given one, or for split_tokens = 0 the library's
+ * default, chosen from the lengths' upper bound, dtypes and query rows.
+ * Writes *split_tokens; same argument errors as attn_decode_workspace_size. */
+attn_status attn_decode_split_tokens(const attn_decode_args *args, int32_t *split_tokens);
+
 /*
  * Split-KV decode attention ("优化稀疏注意力中的令牌丢弃机制" §5 Split-KV;
  * "注意力优化" Flash Attention online softmax).  One call enqueues:

@@ -22,7 +22,7 @@ from ._lib import ATTN_QUANT_STATIC as QUANT_STATIC  # noqa: F401
 
 __all__ = ["KVGeometry", "attn_decode_splitkv", "attn_merge_lse", "kv_quant_int8", "oam_value_lognorm",
            "oam_score_topk", "decode_workspace_size", "oam_workspace_size", "prepare_decode", "util_copy",
-           "util_read", "AttnError"]
+           "util_read", "decode_split_tokens", "AttnError"]
 
 _DT = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16, torch.int8: ATTN_I8}
 
@@ -119,6 +119,12 @@ def decode_workspace_size(args: _lib.AttnDecodeArgs) -> int:
     return n.value
 
 
+def decode_split_tokens(args: _lib.AttnDecodeArgs) -> int:
+    n = ctypes.c_int32(0)
+    _lib.check(_lib.load().attn_decode_split_tokens(ctypes.byref(args), ctypes.byref(n)), "attn_decode_split_tokens")
+    return n.value
+
+
 class PreparedDecode:
     """A validated argument block; calling it enqueues one decode step on a stream."""
 
@@ -129,6 +135,11 @@ class PreparedDecode:
 
     def __call__(self, stream=None):
         _lib.check(self._fn(ctypes.byref(self.args), _stream(stream)), "attn_decode_splitkv")
+
+    @property
+    def split_tokens(self) -> int:
+        """The chunk length the library uses for this call (its default when 0 was asked)."""
+        return decode_split_tokens(self.args)
 
     def profiled(self, events, stream=None):
         """Same call, recording three torch.cuda.Event marks around the decode and merge launches."""

@@ -38,6 +38,7 @@ class OamTopkArgs(ctypes.Structure):
 # Every entry point of the header, with its ctypes signature.
 SIGNATURES = {
     "attn_decode_workspace_size": ([ctypes.POINTER(AttnDecodeArgs), ctypes.POINTER(sz)], i32),
+    "attn_decode_split_tokens": ([ctypes.POINTER(AttnDecodeArgs), ctypes.POINTER(i32)], i32),
     "attn_decode_splitkv": ([ctypes.POINTER(AttnDecodeArgs), vp], i32),
     "attn_decode_splitkv_profiled": ([ctypes.POINTER(AttnDecodeArgs), vp, ctypes.POINTER(vp * 3)], i32),
     "attn_merge_lse": ([vp, vp, vp, vp, i32, i32, i32, vp, vp, vp], i32),

@@ -145,20 +145,31 @@ attn_status plan_decode(const attn_decode_args *a, DecodeLayout *L) {
     L->split = a->split_tokens;
   } else if (!mfma) {
     L->split = 256;
-  } else {
-    // About one chunk per worker of a full decode grid (2048 one-wave
-    // workers on a 256-CU device, 1024 for 32-column workers): each worker
-    // then writes about one partial per column, and partial writes cost far
-    // more HBM time than their bytes while the KV stream runs.  32..2048
-    // tokens; with an index list at least 256 (bf16) or 128 (int8) and at
-    // most 1024, since gathered runs are short and a worker's fixed costs
-    // weigh more (4096 kept tokens per pair, bf16: 2048 two-tile workers
-    // took 26.6 us, 512 eight-tile workers 23.3 us, 256 sixteen-tile workers
-    // 26.7 us; int8: 27.6, 24.8 with four-tile workers, 26.1 us).
+  } else if (a->token_idx) {
+    // Gathered runs are short and a worker's fixed costs weigh more: chunks
+    // of at least 256 (bf16) or 128 (int8) and at most 1024 kept tokens
+    // (4096 kept tokens per pair, bf16: 2048 two-tile workers took 26.6 us,
+    // 512 eight-tile workers 23.3 us, 256 sixteen-tile workers 26.7 us;
+    // int8: 27.6, 24.8 with four-tile workers, 26.1 us).
     const int64_t tiles = (int64_t)g.B * g.KH * L->ngb * (((int64_t)L->max_tokens + 31) / 32);
-    const int64_t workers = L->cols == 32 ? 1024 : 2048;
-    const int64_t min_ct = a->token_idx ? (a->kv_dtype == ATTN_I8 ? 4 : 8) : 1;
-    const int64_t ct = std::min<int64_t>(std::max<int64_t>(tiles / workers, min_ct), a->token_idx ? 32 : 64);
+    const int64_t ct = std::min<int64_t>(std::max<int64_t>(tiles / 2048, a->kv_dtype == ATTN_I8 ? 4 : 8), 32);
+    L->split = (int32_t)(32 * ct);
+  } else {
+    // About one chunk per worker, each worker streaming at least 32 tiles
+    // when there are enough: every partial costs a write in the stream and
+    // a read in the merge, and two one-wave workers per compute unit with
+    // their register rings already keep HBM busy.  At most 2048 bf16
+    // workers (two per SIMD) and 1024 int8 or 32-column workers (one per
+    // SIMD); chunks of at most 2048 (bf16) or 4096 (int8) tokens.  Measured
+    // on a 256 MiB bf16 step (16384 tiles): 2048 workers 61 us, 512 workers
+    // 52 us; on the 1 GiB int8 128K step: 2048 workers 205 us, 1024 with
+    // 4096-token chunks 193 us.
+    const int64_t tiles = (int64_t)g.B * g.KH * L->ngb * (((int64_t)L->max_tokens + 31) / 32);
+    const bool one_per_simd = L->cols == 32 || a->kv_dtype == ATTN_I8;
+    const int64_t wmax = one_per_simd ? 1024 : 2048;
+    const int64_t workers = std::min<int64_t>(std::max<int64_t>(tiles / 32, 256), wmax);
+    int64_t ct = std::min<int64_t>(std::max<int64_t>(tiles / workers, 1), a->kv_dtype == ATTN_I8 ? 128 : 64);
+    if (g.block_table) ct = std::min<int64_t>(ct, 2 * (int64_t)g.page_tokens);  // a chunk spans <= 64 pages
     L->split = (int32_t)(32 * ct);
   }
   if (mfma && ((int64_t)g.max_seq_len + 64) * g.stride_t * elem_size(a->kv_dtype) >= (int64_t(1) << 31))
@@ -216,6 +227,15 @@ attn_status attn_decode_workspace_size(const attn_decode_args *args, size_t *byt
   return ATTN_OK;
 }
 
+attn_status attn_decode_split_tokens(const attn_decode_args *args, int32_t *split_tokens) {
+  if (!split_tokens) return fail(ATTN_ERR_INVALID_ARG, "split_tokens is NULL");
+  DecodeLayout L;
+  attn_status st = plan_decode(args, &L);
+  if (st != ATTN_OK) return st;
+  *split_tokens = L.split;
+  return ATTN_OK;
+}
+
 static attn_status decode_impl(const attn_decode_args *a, attn_stream_t stream, void *const *events) {
   DecodeLayout L;
   attn_status st = plan_decode(a, &L);
@@ -270,6 +290,10 @@ static attn_status decode_impl(const attn_decode_args *a, attn_stream_t stream, 
     const int64_t max_tiles = (int64_t)p.B * p.KH * L.ngb * (((int64_t)L.max_tokens + 31) / 32);
     int64_t grid = (int64_t)cus * (L.mfma ? (L.cols == 32 ? 4 : 8) : 4);
     if (grid > max_tiles) grid = max_tiles;
+    // no more workers than ranges of at least one chunk (the kernel's own
+    // rule), so the workers in use are the first ones dispatched
+    const int64_t ct = L.split / 32;
+    if (grid > (max_tiles + ct - 1) / ct) grid = (max_tiles + ct - 1) / ct;
     p.grid = (int)(grid < 1 ? 1 : grid);
   }
   p.wl.m_part = reinterpret_cast<float *>(ws + L.m);

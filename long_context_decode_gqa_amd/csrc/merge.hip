@@ -142,19 +142,24 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *o_par
   if (tid == 0 && lse) lse[orow] = (Ls > 0.f) ? M + logf(Ls) : NEG_INF;
 }
 
-// Single-pass merge for D % 4 == 0, one 256-thread workgroup per row.
+// Single-pass merge for D % 4 == 0.  Workgroup (row, c) of csplit takes
+// the row's channel slices [c*nq, (c+1)*nq), nq = D/4/csplit, with nq * 16
+// threads, so rows with many partials get more, smaller workgroups.
 // Thread (grp, q) owns the 16-byte column slice q and the slots grp,
-// grp + ng, ... of the row, and folds them in order with a running maximum
-// (online log-sum-exp: on a larger m the sums so far are rescaled), so every
-// load of the row is issued up front and there is one round trip to memory.
-// The ng slot groups are then combined through LDS in a fixed order.
-constexpr int kMergeV4Threads = 512;
-constexpr int kMergeV4Unroll = 8;
+// grp + 16, ... of the row, and folds them in order with a running maximum
+// (online log-sum-exp: on a larger m the sums so far are rescaled); it
+// issues U slots' loads before folding them, so a pass covers 16 U slots in
+// one round trip to memory.  The 16 slot groups are then combined through
+// LDS in a fixed order.  Neither csplit nor U changes which slots a thread
+// folds or in what order, so the result depends only on the partials.
+constexpr int kMergeV4Threads = 512;  // at most: D = 128 in one workgroup
+constexpr int kMergeGroups = 16;      // slot groups per column slice
 
-template <int OUT, bool DECODE>
+template <int OUT, bool DECODE, int U>
 __global__ __launch_bounds__(kMergeV4Threads) void merge_v4_kernel(const float *o_part, const float *m_part,
                                                                  const float *l_part, const int32_t *rss,
-                                                                 DecodeParams dp, int32_t D, void *out, float *lse) {
+                                                                 DecodeParams dp, int32_t D, int32_t csplit,
+                                                                 void *out, float *lse) {
   __shared__ f32x4_t s_acc[kMergeV4Threads];
   __shared__ float s_m[kMergeV4Threads], s_l[kMergeV4Threads];
   const int row = blockIdx.x;
@@ -169,17 +174,18 @@ __global__ __launch_bounds__(kMergeV4Threads) void merge_v4_kernel(const float *
   const float NEG_INF = -__builtin_huge_valf();
   int s0, n, ss;
   row_slots<DECODE>(row, rss, dp, &s0, &n, &ss);
-  const int nq = D / 4;            // column slices
-  const int ng = kMergeV4Threads / nq;
-  const int grp = tid / nq, q = tid - grp * nq;
+  const int nq = D / 4 / csplit;   // column slices of this workgroup
+  constexpr int ng = kMergeGroups;
+  const int grp = tid / nq, ql = tid - grp * nq;
+  const int q = blockIdx.y * nq + ql;  // the row's slice
   float mt = NEG_INF, lt = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  if (grp < ng) {
-    for (int base = grp; base < n; base += ng * kMergeV4Unroll) {
-      float m[kMergeV4Unroll], l[kMergeV4Unroll];
-      f32x4_t o[kMergeV4Unroll];
+  {
+    for (int base = grp; base < n; base += ng * U) {
+      float m[U], l[U];
+      f32x4_t o[U];
 #pragma unroll
-      for (int u = 0; u < kMergeV4Unroll; ++u) {
+      for (int u = 0; u < U; ++u) {
         const int sl = base + u * ng;
         const bool in = sl < n;
         const int64_t i = s0 + (int64_t)(in ? sl : 0) * ss;
@@ -188,7 +194,7 @@ __global__ __launch_bounds__(kMergeV4Threads) void merge_v4_kernel(const float *
         o[u] = *(const f32x4_t *)(o_part + i * D + 4 * q);
       }
 #pragma unroll
-      for (int u = 0; u < kMergeV4Unroll; ++u) {
+      for (int u = 0; u < U; ++u) {
         if (l[u] > 0.f) {  // empty partials (l = 0) may hold any o
           if (m[u] > mt) {
             const float sc = expf(mt - m[u]);
@@ -210,14 +216,14 @@ __global__ __launch_bounds__(kMergeV4Threads) void merge_v4_kernel(const float *
   if (tid < nq) {
     float M = NEG_INF;
     for (int g = 0; g < ng; ++g)
-      if (s_l[g * nq + q] > 0.f) M = fmaxf(M, s_m[g * nq + q]);
+      if (s_l[g * nq + ql] > 0.f) M = fmaxf(M, s_m[g * nq + ql]);
     f32x4_t a = {0.f, 0.f, 0.f, 0.f};
     float Ls = 0.f;
     for (int g = 0; g < ng; ++g) {
-      const float lg = s_l[g * nq + q];
+      const float lg = s_l[g * nq + ql];
       if (lg > 0.f) {
-        const float sc = expf(s_m[g * nq + q] - M);
-        a += sc * s_acc[g * nq + q];
+        const float sc = expf(s_m[g * nq + ql] - M);
+        a += sc * s_acc[g * nq + ql];
         Ls += sc * lg;
       }
     }
@@ -258,22 +264,55 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4_t *src, size_t n,
 
 }  // namespace
 
+// Channel split of the single-pass merge: a divisor of the D/4 slices with at
+// most 32 slices (512 threads) per workgroup and at least 4 (one wave), as
+// close as that allows to about 512 workgroups in all.
+static int merge_csplit(int rows, int D) {
+  const int nqt = D / 4;
+  const int target = (512 + rows - 1) / rows;
+  int best = 0;
+  for (int c = 1; c <= nqt; ++c) {
+    if (nqt % c || nqt / c > 32) continue;
+    if (best == 0) best = c;                // the fewest workgroups that fit
+    if (nqt / c < 4 && c > best) break;     // keep a full wave per workgroup
+    best = c;
+    if (c >= target) break;
+  }
+  return best;
+}
+
+template <int OUT, bool DECODE>
+static void launch_merge_v4(const float *o_part, const float *m_part, const float *l_part, const int32_t *rss,
+                            const DecodeParams &dp, int rows, int D, bool many_slots, void *out, float *lse,
+                            hipStream_t s) {
+  const int cs = merge_csplit(rows, D);
+  const dim3 g(rows, cs), blk((D / 4 / cs) * kMergeGroups);
+  if (many_slots)
+    hipLaunchKernelGGL((merge_v4_kernel<OUT, DECODE, 32>), g, blk, 0, s, o_part, m_part, l_part, rss, dp, D, cs, out,
+                       lse);
+  else
+    hipLaunchKernelGGL((merge_v4_kernel<OUT, DECODE, 8>), g, blk, 0, s, o_part, m_part, l_part, rss, dp, D, cs, out,
+                       lse);
+}
+
 hipError_t launch_merge(const float *o_part, const float *m_part, const float *l_part, const int32_t *rss,
                         int32_t rows, int32_t D, int32_t out_dtype, void *out, float *lse, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   DecodeParams none = {};
-  dim3 g(rows);
   const uintptr_t oa = reinterpret_cast<uintptr_t>(o_part), ua = reinterpret_cast<uintptr_t>(out);
   const bool v4 = D % 4 == 0 && oa % 16 == 0 && ua % (out_dtype == ATTN_F32 ? 16 : 4) == 0;
-  dim3 blk(v4 ? kMergeV4Threads : kMergeThreads);
-  if (v4 && out_dtype == ATTN_F32)
-    hipLaunchKernelGGL((merge_v4_kernel<ATTN_F32, false>), g, blk, 0, s, o_part, m_part, l_part, rss, none, D, out, lse);
-  else if (v4)
-    hipLaunchKernelGGL((merge_v4_kernel<ATTN_BF16, false>), g, blk, 0, s, o_part, m_part, l_part, rss, none, D, out, lse);
-  else if (out_dtype == ATTN_F32)
-    hipLaunchKernelGGL((merge_kernel<ATTN_F32, false>), g, blk, 0, s, o_part, m_part, l_part, rss, none, D, out, lse);
-  else
-    hipLaunchKernelGGL((merge_kernel<ATTN_BF16, false>), g, blk, 0, s, o_part, m_part, l_part, rss, none, D, out, lse);
+  if (v4 && out_dtype == ATTN_F32) {
+    launch_merge_v4<ATTN_F32, false>(o_part, m_part, l_part, rss, none, rows, D, false, out, lse, s);
+  } else if (v4) {
+    launch_merge_v4<ATTN_BF16, false>(o_part, m_part, l_part, rss, none, rows, D, false, out, lse, s);
+  } else {
+    dim3 g(rows), blk(kMergeThreads);
+    if (out_dtype == ATTN_F32)
+      hipLaunchKernelGGL((merge_kernel<ATTN_F32, false>), g, blk, 0, s, o_part, m_part, l_part, rss, none, D, out, lse);
+    else
+      hipLaunchKernelGGL((merge_kernel<ATTN_BF16, false>), g, blk, 0, s, o_part, m_part, l_part, rss, none, D, out,
+                         lse);
+  }
   return hipGetLastError();
 }
 
@@ -294,13 +333,12 @@ hipError_t launch_merge_decode(const DecodeParams &p, int32_t out_dtype, void *o
                          out, lse);
     return hipGetLastError();
   }
-  dim3 g(rows), blk(kMergeV4Threads);
+  // two slots per chunk of the longest row; past 128 slots a pass takes 512
+  const bool many = 2 * p.max_chunks > kMergeGroups * 8;
   if (out_dtype == ATTN_F32)
-    hipLaunchKernelGGL((merge_v4_kernel<ATTN_F32, true>), g, blk, 0, s, w.o_part, w.m_part, w.l_part, nullptr, p, p.D,
-                       out, lse);
+    launch_merge_v4<ATTN_F32, true>(w.o_part, w.m_part, w.l_part, nullptr, p, rows, p.D, many, out, lse, s);
   else
-    hipLaunchKernelGGL((merge_v4_kernel<ATTN_BF16, true>), g, blk, 0, s, w.o_part, w.m_part, w.l_part, nullptr, p, p.D,
-                       out, lse);
+    launch_merge_v4<ATTN_BF16, true>(w.o_part, w.m_part, w.l_part, nullptr, p, rows, p.D, many, out, lse, s);
   return hipGetLastError();
 }
 

@@ -74,6 +74,43 @@ def test_workspace_size_counts_partials():
     assert st2 == 0 and n2 > n
 
 
+def _split(a):
+    n = ctypes.c_int32(0)
+    st = _lib.load().attn_decode_split_tokens(ctypes.byref(a), ctypes.byref(n))
+    return st, n.value
+
+
+I8 = dict(kv_dtype=_lib.ATTN_I8, k_scale=FAKE, k_part_tokens=64, k_scale_stride=2048)
+
+
+@pytest.mark.parametrize("over,split", [
+    # 128K tokens x 4 sequences x 8 KV heads = 131072 tiles of 32: 2048 bf16 workers of 64 tiles
+    (dict(g_B=4, g_max_seq_len=131072), 2048),
+    # int8: 1024 workers (one per SIMD) of 128 tiles
+    (dict(g_B=4, g_max_seq_len=131072, **I8), 4096),
+    # 4 query rows per sequence (32 columns): 1024 workers
+    (dict(g_B=4, g_max_seq_len=131072, q_rows=4), 4096 // 2),
+    # one KV head (a tensor-parallel share): 16384 tiles, 512 workers of at least 32 tiles
+    (dict(g_B=4, g_KH=1, g_max_seq_len=131072), 1024),
+    # small problems: at least 256 workers
+    (dict(g_B=1, g_KH=1, g_max_seq_len=4096), 32),
+    # paged int8 with 32-token pages: a chunk spans at most 64 pages
+    (dict(g_B=4, g_max_seq_len=131072, g_seq_offset=None, g_block_table=FAKE, g_page_tokens=32,
+          g_table_stride=4096, g_page_stride=32 * 8 * 128, **I8), 2048),
+    # kept-token lists of 4096: chunks of 256 (bf16) or 128 (int8) kept tokens
+    (dict(g_B=4, g_max_seq_len=131072, token_idx=FAKE, n_idx=FAKE, idx_stride=4096), 256),
+    (dict(g_B=4, g_max_seq_len=131072, token_idx=FAKE, n_idx=FAKE, idx_stride=4096, **I8), 128),
+    # a given split is kept
+    (dict(split_tokens=96), 96),
+])
+def test_default_split_tokens(over, split):
+    """The library's default chunk length, as attn_decode_split_tokens reports it (the device-size
+    independent part of the work split; workers = tiles / chunk tiles)."""
+    st, n = _split(_args(**over))
+    assert st == 0 and n == split, (over, n)
+    assert _split(_args(G=0))[0] == _lib.ATTN_ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("over,status", [
     (dict(G=0), _lib.ATTN_ERR_UNSUPPORTED),
     (dict(G=65), _lib.ATTN_ERR_UNSUPPORTED),
