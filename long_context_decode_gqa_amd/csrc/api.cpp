@@ -160,15 +160,17 @@ attn_status plan_decode(const attn_decode_args *a, DecodeLayout *L) {
     // a read in the merge, and two one-wave workers per compute unit with
     // their register rings already keep HBM busy.  At most 2048 bf16
     // workers (two per SIMD) and 1024 int8 or 32-column workers (one per
-    // SIMD); chunks of at most 2048 (bf16) or 4096 (int8) tokens.  Measured
-    // on a 256 MiB bf16 step (16384 tiles): 2048 workers 61 us, 512 workers
+    // SIMD); chunks of at most 4096 tokens.  The tile count is the bound
+    // from max_seq_len (the lengths are on the device).  Measured on a
+    // 256 MiB bf16 step (16384 tiles): 2048 workers 61 us, 512 workers
     // 52 us; on the 1 GiB int8 128K step: 2048 workers 205 us, 1024 with
-    // 4096-token chunks 193 us.
+    // 4096-token chunks 193 us; on the ragged bf16 batch: 2048-token chunks
+    // 648 us, 4096-token 640 us.
     const int64_t tiles = (int64_t)g.B * g.KH * L->ngb * (((int64_t)L->max_tokens + 31) / 32);
     const bool one_per_simd = L->cols == 32 || a->kv_dtype == ATTN_I8;
     const int64_t wmax = one_per_simd ? 1024 : 2048;
     const int64_t workers = std::min<int64_t>(std::max<int64_t>(tiles / 32, 256), wmax);
-    int64_t ct = std::min<int64_t>(std::max<int64_t>(tiles / workers, 1), a->kv_dtype == ATTN_I8 ? 128 : 64);
+    int64_t ct = std::min<int64_t>(std::max<int64_t>(tiles / workers, 1), 128);
     if (g.block_table) ct = std::min<int64_t>(ct, 2 * (int64_t)g.page_tokens);  // a chunk spans <= 64 pages
     L->split = (int32_t)(32 * ct);
   }

@@ -89,7 +89,7 @@ I8 = dict(kv_dtype=_lib.ATTN_I8, k_scale=FAKE, k_part_tokens=64, k_scale_stride=
     # int8: 1024 workers (one per SIMD) of 128 tiles
     (dict(g_B=4, g_max_seq_len=131072, **I8), 4096),
     # 4 query rows per sequence (32 columns): 1024 workers
-    (dict(g_B=4, g_max_seq_len=131072, q_rows=4), 4096 // 2),
+    (dict(g_B=4, g_max_seq_len=131072, q_rows=4), 4096),
     # one KV head (a tensor-parallel share): 16384 tiles, 512 workers of at least 32 tiles
     (dict(g_B=4, g_KH=1, g_max_seq_len=131072), 1024),
     # small problems: at least 256 workers
