@@ -295,6 +295,33 @@ def bench_paged(pkg, torch, synth, steps, warmup, dev, page_tokens=64, layout="h
     return res
 
 
+def bench_tiny(pkg, torch, synth, steps, warmup, dev):
+    """The tiny fp32 case (B1, KH1, G4, D64, L1024): 512 KiB of K/V, so a step is launch-bound, not a
+    bandwidth point.  Unsplit and in 4 chunks of 256 + merge; warm (back to back) and cold (a 512 MiB
+    write between calls)."""
+    w = synth.workload("tiny")
+    q, k, v, g = synth.generate(w)
+    geom = dev_geom(pkg, torch, g, dev)
+    qd = to_dev(torch, q.reshape(-1), dev).view(w.B, w.QH, w.D)
+    kd, vd = to_dev(torch, k, dev), to_dev(torch, v, dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    res = {"kv_bytes": int(w.B * w.KH * int(w.lens[0]) * w.D * 4 * 2)}
+    for name, split in (("unsplit", 1024), ("split4", 256)):
+        p = pkg.prepare_decode(qd, kd, vd, geom, w.G, split_tokens=split)
+        res[f"{name}_warm_us"] = round(time_calls(torch, p, steps, warmup) * 1e3, 2)
+        cold = []
+        for _ in range(max(3, steps // 2)):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            p()
+            e1.record()
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        res[f"{name}_cold_us"] = round(sorted(cold)[len(cold) // 2] * 1e3, 2)
+    return res
+
+
 def bench_multirow(pkg, torch, synth, steps, warmup, dev, R):
     """The 128K bf16 decode with R query rows per sequence (speculative verification: each step
     checks R tokens).  Same K/V bytes as one row; G * R rows of a KV head share each load."""
@@ -360,7 +387,21 @@ def bench_oam(pkg, torch, synth, steps, warmup, dev):
            "kept_attention_us": round(t_att * 1e3, 2), "algorithmic_bytes_per_step": algo,
            "gbs_algorithmic": round(algo / ms / 1e6, 1), "frac_of_peak": round(algo / ms / 1e6 / HBM_PEAK_GBS, 4),
            "select_with_norms_from_v_us": round(t_fly * 1e3, 2), "top_k": w.top_k, "kv_len": L}
-    del sel, sel_fly, att
+    # the kept-token attention alone, warm (back to back: its 64 MiB of gathered rows stay in the
+    # 256 MB Infinity Cache) and cold (a 512 MiB write between calls evicts them)
+    res["kept_attention_warm_us"] = round(time_calls(torch, att, steps, warmup) * 1e3, 2)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(max(3, steps // 2)):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        att()
+        e1.record()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    res["kept_attention_cold_us"] = round(sorted(cold)[len(cold) // 2] * 1e3, 2)
+    del flush, sel, sel_fly, att
     # the cached value term, computed when tokens are appended (V read once, 4 bytes written per token)
     t_vl = time_calls(torch, lambda: pkg.oam_value_lognorm(vd, geom, w.eps, vlog=vlog), steps, warmup)
     res["value_lognorm_us"] = round(t_vl * 1e3, 2)
@@ -437,7 +478,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--headline-only", action="store_true")
-    ap.add_argument("--others", default="gqa32k,tp8,ragged,int8,oam,paged,multirow",
+    ap.add_argument("--others", default="tiny,gqa32k,tp8,ragged,int8,oam,paged,multirow",
                     help="comma-separated other workloads to time after the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -503,6 +544,8 @@ def main():
             r = bench_dense(pkg, torch, synth, "gqa32k", max(5, K // 2), W, dev)
             others["gqa32k_bf16"] = summary(r)
             del r
+        if "tiny" in todo:
+            others["tiny_fp32"] = bench_tiny(pkg, torch, synth, K, W, dev)
         if "tp8" in todo:
             # one GPU's share of a tensor-parallel split over 8 GPUs by KV heads (KH = 8 -> 1 per GPU):
             # the same per-head work at 1/8 of the bytes, where fixed costs weigh more

@@ -1,37 +1,51 @@
-// Split-KV decode attention on the vector ALUs, for fp32 (or bf16) Q/K/V of
-// any head size 4..256 and any group size.  Same work-list and partial format
-// as the matrix-core kernel; used where the inputs are fp32 (no fp32 input
-// path exists for the 16x16x32 MFMA) or the head size has no MFMA variant.
+// Split-KV decode attention on the vector ALUs, for fp32 Q/K/V of any head
+// size 4..256 (a multiple of 4) and any group size.  Same work split and
+// partial format as the matrix-core kernel; used for fp32 inputs.
 //
-// Per work item, 256-token sub-tiles follow the online softmax of the
-// Flash Attention block pseudo-code ("注意力优化（Attention Optimization）"):
-// scores of the sub-tile -> new running max -> rescale (alpha) -> probabilities
-// -> O = alpha*O + P V, with natural-log scores; the chunk's (m, l, O/l) is the
-// partial triple of "优化稀疏注意力中的令牌丢弃机制" §5.
+// One 256-thread workgroup per worker.  Each 32-token tile of a segment is
+// staged in LDS with coalesced 16-byte loads (K transposed, so the score
+// loop reads consecutive tokens across lanes), and the next two tiles' loads
+// are in flight in registers while the current one is computed.  The tile then
+// follows the online softmax of the Flash Attention block pseudo-code
+// ("注意力优化（Attention Optimization）"): scores -> new running max ->
+// rescale (alpha) -> probabilities -> O = alpha*O + P V, in natural-log
+// units; the chunk's (m, l, O/l) is the partial triple of
+// "优化稀疏注意力中的令牌丢弃机制" §5.  Thread (head g, token i) of a half
+// wave computes that score and takes the head's running max and sum with
+// half-wave shuffles, so the softmax needs no serial loop.
 #include "common.hpp"
 
 namespace lcdg {
 namespace {
 
-constexpr int kSub = 256;
+constexpr int kVTile = 32;   // tokens per tile = lanes per head in the score phase
+constexpr int kVMaxD = 256;  // largest head size
 
-template <int T>
-__device__ __forceinline__ float load_elem(const void *base, int64_t i) {
-  if constexpr (T == ATTN_F32) {
-    return ((const float *)base)[i];
-  } else {
-    return bf16_bits_to_f32(((const uint16_t *)base)[i]);
-  }
+__device__ __forceinline__ float half_max(float v) {
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 32));
+  return v;
+}
+__device__ __forceinline__ float half_sum(float v) {
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, 32);
+  return v;
 }
 
-template <int QT, int KT>
-__global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
-  __shared__ float s_q[16][257];
-  __shared__ float s_p[16][kSub];
-  __shared__ float s_m[16], s_l[16], s_alpha[16];
+// DC: the head-size class (64, 128 or 256) that sizes the per-thread load
+// registers; two tiles' loads are in flight while one is computed.
+template <int DC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_valu_kernel(DecodeParams p) {
+  constexpr int kVChunks = kVTile * DC / 4 / 256;  // 16-byte loads per thread for K (and V) of a tile
+  __shared__ float s_q[16][kVMaxD];                  // q * softmax_scale
+  __shared__ float s_kt[kVMaxD][kVTile + 1];         // K^T of the tile
+  __shared__ __attribute__((aligned(16))) float s_v[kVTile][kVMaxD];
+  __shared__ float s_p[16][kVTile];                  // probabilities (0 past the segment)
+  __shared__ float s_alpha[16], s_m[16], s_l[16];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int D = p.D;
+  const int cpr = D / 4;  // 16-byte chunks per row
   const float NEG_INF = -__builtin_huge_valf();
 
   const int T = wave_total_tiles(p);
@@ -39,7 +53,9 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
   if ((int)blockIdx.x >= nwg) return;
   const int t_begin = (int)((int64_t)blockIdx.x * T / nwg);
   const int t_end = (int)((int64_t)(blockIdx.x + 1) * T / nwg);
-  const int ct = p.split / 32;
+  const int ct = p.split / kVTile;
+  // score-phase roles: head tid / 32 (+ 8 for the second pass), token tid % 32
+  const int sg = tid / kVTile, si = tid % kVTile;
 
   // every wave of the workgroup walks the lanes alike
   LaneHit hit = wave_find_lane(p, t_begin);
@@ -60,69 +76,92 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
     const int g0 = gb * 16;
     const int gcount = min(16, p.G - g0);
     const int64_t head_off = p.seq_offset[b] + (int64_t)kh * p.stride_h;
+    const float *kb = (const float *)p.k + head_off, *vb = (const float *)p.v + head_off;
 
     __syncthreads();
     for (int e = tid; e < gcount * D; e += 256) {
       const int g = e / D, d = e - g * D;
-      s_q[g][d] = load_elem<QT>(p.q, ((int64_t)b * p.QH + (int64_t)kh * p.G + g0 + g) * D + d);
+      s_q[g][d] = ((const float *)p.q)[((int64_t)b * p.QH + (int64_t)kh * p.G + g0 + g) * D + d] * p.softmax_scale;
     }
+
+    // The K and V rows of the tile starting at position pos: chunk
+    // c = tid + 256 j is row c / cpr, channels 4 (c % cpr) ..; rows at or past
+    // the segment's end load nothing (zeros).
+    struct TileRegs {
+      f32x4_t k[kVChunks], v[kVChunks];
+    };
+    auto load_tile = [&](TileRegs &R, int pos, int pos_end) {
+      f32x4_t(&rk)[kVChunks] = R.k;
+      f32x4_t(&rv)[kVChunks] = R.v;
+#pragma unroll
+      for (int j = 0; j < kVChunks; ++j) {
+        const int c = tid + 256 * j, r = c / cpr;
+        rk[j] = rv[j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        if (r < kVTile && pos + r < pos_end) {
+          int tok = pos + r;
+          if (idxp) tok = min(max(idxp[tok], 0), L - 1);
+          const int64_t off = (int64_t)tok * p.stride_t + 4 * (c - r * cpr);
+          rk[j] = *(const f32x4_t *)(kb + off);
+          rv[j] = *(const f32x4_t *)(vb + off);
+        }
+      }
+    };
+    auto store_tile = [&](const TileRegs &R) {
+      const f32x4_t(&rk)[kVChunks] = R.k;
+      const f32x4_t(&rv)[kVChunks] = R.v;
+#pragma unroll
+      for (int j = 0; j < kVChunks; ++j) {
+        const int c = tid + 256 * j, r = c / cpr;
+        if (r < kVTile) {
+          const int d = 4 * (c - r * cpr);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s_kt[d + i][r] = rk[j][i];
+          *(f32x4_t *)&s_v[r][d] = rv[j];
+        }
+      }
+    };
 
     // one segment per chunk piece of this run
     for (int seg_t0 = t; seg_t0 < run_end;) {
       const int chunk = (seg_t0 - lane_t0) / ct;
       const int chunk_t1 = min(lane_t1, lane_t0 + (chunk + 1) * ct);
       const int seg_t1 = min(run_end, chunk_t1);
-      const int pos0 = (seg_t0 - lane_t0) * 32;
-      const int pos1 = min(npos, (seg_t1 - lane_t0) * 32);
-      if (tid < 16) {
-        s_m[tid] = NEG_INF;
-        s_l[tid] = 0.f;
-      }
+      const int pos0 = (seg_t0 - lane_t0) * kVTile;
+      const int pos1 = min(npos, (seg_t1 - lane_t0) * kVTile);
+      // running max and sum of heads sg and sg + 8 (every lane of a half wave holds its head's)
+      float m_run[2] = {NEG_INF, NEG_INF}, l_run[2] = {0.f, 0.f};
       float o[16];
 #pragma unroll
       for (int k = 0; k < 16; ++k) o[k] = 0.f;
-      __syncthreads();
 
-      for (int sub0 = pos0; sub0 < pos1; sub0 += kSub) {
-        const int n = min(kSub, pos1 - sub0);
-        // scores of this sub-tile: thread tt owns token position sub0 + tt
-        if (tid < n) {
-          int tok = sub0 + tid;
-          if (idxp) tok = min(max(idxp[tok], 0), L - 1);
-          const int64_t row = head_off + (int64_t)tok * p.stride_t;
-          float acc[16];
-#pragma unroll
-          for (int g = 0; g < 16; ++g) acc[g] = 0.f;
-          for (int d = 0; d < D; ++d) {
-            const float kv = load_elem<KT>(p.k, row + d);
-#pragma unroll
-            for (int g = 0; g < 16; ++g)
-              if (g < gcount) acc[g] += s_q[g][d] * kv;
-          }
-#pragma unroll
-          for (int g = 0; g < 16; ++g)
-            if (g < gcount) s_p[g][tid] = acc[g] * p.softmax_scale;
-        }
+      // tile tp: stage it (its loads were issued two tiles ago), issue the
+      // loads of tile tp + 2 tiles into the same registers, compute
+      auto step = [&](TileRegs &R, int tp) {
+        if (tp >= pos1) return;
+        __syncthreads();  // the previous tile's readers are done
+        store_tile(R);
+        load_tile(R, tp + 2 * kVTile, pos1);
         __syncthreads();
-        // running max, rescale factor and probabilities, one wave per head
-        for (int g = wave; g < gcount; g += 4) {
-          float mx = NEG_INF;
-          for (int i = lane; i < n; i += 64) mx = fmaxf(mx, s_p[g][i]);
-          mx = wave_max(mx);
-          const float m_old = s_m[g];
-          const float m_new = fmaxf(m_old, mx);
-          float sum = 0.f;
-          for (int i = lane; i < n; i += 64) {
-            const float e = expf(s_p[g][i] - m_new);
-            s_p[g][i] = e;
-            sum += e;
-          }
-          sum = wave_sum(sum);
-          if (lane == 0) {
-            const float alpha = (m_old == NEG_INF) ? 0.f : expf(m_old - m_new);
-            s_alpha[g] = alpha;
-            s_l[g] = alpha * s_l[g] + sum;
-            s_m[g] = m_new;
+        const int n = min(kVTile, pos1 - tp);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int g = sg + 8 * h;
+          if (g < gcount) {  // uniform over the half wave
+            float acc = 0.f;
+            int d = 0;
+            for (; d + 8 <= D; d += 8) {
+#pragma unroll
+              for (int u = 0; u < 8; ++u) acc += s_q[g][d + u] * s_kt[d + u][si];
+            }
+            for (; d < D; ++d) acc += s_q[g][d] * s_kt[d][si];
+            const float s = si < n ? acc : NEG_INF;
+            const float m_new = fmaxf(m_run[h], half_max(s));  // finite: the tile has a token
+            const float e = si < n ? expf(s - m_new) : 0.f;
+            const float alpha = m_run[h] == NEG_INF ? 0.f : expf(m_run[h] - m_new);
+            l_run[h] = alpha * l_run[h] + half_sum(e);
+            m_run[h] = m_new;
+            s_p[g][si] = e;
+            if (si == 0) s_alpha[g] = alpha;
           }
         }
         __syncthreads();
@@ -133,16 +172,28 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
           if (e < gcount * D) {
             const int g = e / D, d = e - g * D;
             float acc = o[k] * s_alpha[g];
-            for (int i = 0; i < n; ++i) {
-              int tok = sub0 + i;
-              if (idxp) tok = min(max(idxp[tok], 0), L - 1);
-              acc += s_p[g][i] * load_elem<KT>(p.v, head_off + (int64_t)tok * p.stride_t + d);
-            }
+#pragma unroll
+            for (int i = 0; i < kVTile; ++i) acc += s_p[g][i] * s_v[i][d];
             o[k] = acc;
           }
         }
-        __syncthreads();
+      };
+      TileRegs ra, rb;
+      load_tile(ra, pos0, pos1);
+      load_tile(rb, pos0 + kVTile, pos1);
+      for (int tp = pos0; tp < pos1; tp += 2 * kVTile) {
+        step(ra, tp);
+        step(rb, tp + kVTile);
       }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int g = sg + 8 * h;
+        if (g < gcount && si == 0) {
+          s_m[g] = m_run[h];
+          s_l[g] = l_run[h];
+        }
+      }
+      __syncthreads();
 
       const int half = (seg_t0 == lane_t0 + chunk * ct) ? 0 : 1;
       const bool fill_second = half == 0 && seg_t1 == chunk_t1;
@@ -164,7 +215,6 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
           }
         }
       }
-      __syncthreads();
       seg_t0 = seg_t1;
     }
     t = run_end;
@@ -175,13 +225,10 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
 }  // namespace
 
 hipError_t launch_decode_valu(const DecodeParams &p, int q_dtype, int kv_dtype, hipStream_t s) {
-  dim3 g(p.grid), blk(256);
-  if (q_dtype == ATTN_F32 && kv_dtype == ATTN_F32)
-    hipLaunchKernelGGL((decode_valu_kernel<ATTN_F32, ATTN_F32>), g, blk, 0, s, p);
-  else if (q_dtype == ATTN_BF16 && kv_dtype == ATTN_BF16)
-    hipLaunchKernelGGL((decode_valu_kernel<ATTN_BF16, ATTN_BF16>), g, blk, 0, s, p);
-  else
-    return hipErrorInvalidValue;
+  if (q_dtype != ATTN_F32 || kv_dtype != ATTN_F32 || p.D > kVMaxD || p.D % 4) return hipErrorInvalidValue;
+  if (p.D <= 64) hipLaunchKernelGGL(decode_valu_kernel<64>, dim3(p.grid), dim3(256), 0, s, p);
+  else if (p.D <= 128) hipLaunchKernelGGL(decode_valu_kernel<128>, dim3(p.grid), dim3(256), 0, s, p);
+  else hipLaunchKernelGGL(decode_valu_kernel<256>, dim3(p.grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -48,6 +48,41 @@ def test_tiny_fp32_unsplit_and_split(split):
     check(out, lse, ref, ref_lse, tol=1e-5)
 
 
+@pytest.mark.parametrize("D,G,split", [(4, 3, 0), (36, 20, 64), (100, 7, 96), (256, 16, 0), (64, 33, 256)])
+def test_fp32_ragged_head_sizes_and_groups(D, G, split):
+    """The fp32 path over ragged lengths (empty, shorter than a tile, tile and chunk boundaries)
+    for head sizes 4..256 and group sizes beyond one 16-head block."""
+    lens = np.array([0, 1, 31, 32, 33, 300, 1000], np.int32)
+    w = synth.workload("tiny", B=len(lens), KH=2, G=G, D=D, lens=lens, layout="token_major", seed=120 + D)
+    q, k, v, g = synth.generate(w)
+    log_case(f"fp32 ragged D={D} G={G} split={split}")
+    out, lse = run_decode(w, q, k, v, g, split_tokens=split)
+    p = problem(w, q, k, v, g)
+    ref, ref_lse = oracle.attention_rows(p, oracle.all_rows(p))
+    check(out, lse, ref, ref_lse, tol=1e-5)
+
+
+def test_fp32_kept_token_subset():
+    """The fp32 path with a per-(sequence, KV head) list of kept positions."""
+    lens = np.array([500, 77, 0, 1200], np.int32)
+    w = synth.workload("tiny", B=len(lens), KH=2, G=4, D=64, lens=lens, layout="head_major", seed=131)
+    q, k, v, g = synth.generate(w)
+    rng = np.random.default_rng(5)
+    stride = 256
+    idx = np.full((w.B, w.KH, stride), -1, np.int32)
+    nidx = np.zeros((w.B, w.KH), np.int32)
+    for b in range(w.B):
+        for kh in range(w.KH):
+            n = min(int(lens[b]), int(rng.integers(1, stride + 1)))
+            idx[b, kh, :n] = np.sort(rng.choice(int(lens[b]), n, replace=False)) if n else []
+            nidx[b, kh] = n
+    log_case("fp32 kept tokens")
+    out, lse = run_decode(w, q, k, v, g, split_tokens=64, token_idx=to_dev(idx), n_idx=to_dev(nidx))
+    p = problem(w, q, k, v, g, tok_idx=idx.reshape(-1), n_idx=nidx.reshape(-1), idx_stride=stride)
+    ref, ref_lse = oracle.attention_rows(p, oracle.all_rows(p))
+    check(out, lse, ref, ref_lse, tol=1e-5)
+
+
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("G", [1, 4, 8, 16, 24])
 def test_bf16_ragged_tails_and_group_sizes(D, G):
@@ -160,12 +195,12 @@ def test_merge_lse_of_oracle_partials(D, maxc, misaligned):
             assert abs(lse[r] - rl) <= 1e-5
 
 
-def _full_size_sampled_rows(name, nrows, seed):
+def _full_size_sampled_rows(name, nrows, seed, **over):
     """A full-size workload in the benchmark's launch configuration (its own
     split-KV chunk size), compared with the oracle on sampled output rows;
     then, for every row, the property that the softmax weights sum to one: a
     constant V comes back unchanged, and lse does not depend on V."""
-    w = synth.workload(name)
+    w = synth.workload(name, **over)
     q, k, v, g = synth.generate(w)
     log_case(f"{name} full size, split {w.split_tokens}")
     out, lse = run_decode(w, q, k, v, g, split_tokens=w.split_tokens)
@@ -197,3 +232,10 @@ def test_dense128k_full_size_sampled_rows():
 def test_ragged_full_size_sampled_rows():
     """The 32-sequence ragged batch (512..131072 tokens, head-major packed cache)."""
     _full_size_sampled_rows("ragged", 16, 4)
+
+
+@pytest.mark.parametrize("name", ["gqa32k", "dense128k"])
+def test_one_kv_head_share_full_size_sampled_rows(name):
+    """One GPU's share of a split over 8 GPUs by KV heads (KH = 1, the rest of the shape as named),
+    in the library's default launch: 512 workers of 32 tiles instead of 2048."""
+    _full_size_sampled_rows(name, 12, 5, KH=1, split_tokens=0)
