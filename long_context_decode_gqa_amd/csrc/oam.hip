@@ -360,10 +360,15 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
       compute(buf[j], tw0 + i + j, i + j < ntw);
     }
   }
-  __syncthreads();
+  // each wave writes its own tokens' scores as soon as its tiles are done
+  // (its LDS writes are its own), so early waves' writes overlap the others'
+  // loads instead of all landing after the workgroup's last tile
   const int nblk_tok = min(kScoreTok, L - blk0);
-  if (o.write_scores)
-    for (int i = tid; i < nblk_tok; i += 256) sc[blk0 + i] = s_sc[i];
+  if (o.write_scores) {
+    const int w0 = 32 * tw0, w1 = min(nblk_tok, w0 + 32 * kTilesPerWave);
+    for (int i = w0 + lane; i < w1; i += 64) sc[blk0 + i] = s_sc[i];
+  }
+  __syncthreads();
   if (token_mode) {
     uint32_t *gh = o.hist + (size_t)pair * kBins;
     for (int i = tid; i < kBins; i += 256)
