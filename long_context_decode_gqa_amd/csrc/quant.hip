@@ -298,11 +298,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void t
   if (threadIdx.x == 0) wg_max[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = m;
 }
 
-// Second level: one workgroup folds the n workgroup maxima; scale = fl32(max / 127).
+// Second level: one workgroup folds the n workgroup maxima (16 loads per
+// thread in flight per round); scale = fl32(max / 127).
 __global__ __launch_bounds__(256) void tensor_scale_kernel(const float *wg_max, int64_t n, float *scales) {
   __shared__ float s_red[4];
+  constexpr int U = 16;
   float m = 0.f;
-  for (int64_t i = threadIdx.x; i < n; i += 256) m = fmaxf(m, wg_max[i]);
+  for (int64_t i0 = 0; i0 < n; i0 += 256 * U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + threadIdx.x + 256 * u;
+      v[u] = i < n ? wg_max[i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) m = fmaxf(m, v[u]);
+  }
   m = block_max(m, s_red);
   if (threadIdx.x == 0) scales[0] = m / 127.0f;
 }
