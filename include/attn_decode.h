@@ -158,9 +158,11 @@ typedef struct {
  *   softmax_scale  multiplies q.k; 0 selects 1/sqrt(D)
  *   split_tokens   tokens per split-KV chunk (multiple of 32); 0 = library
  *               default: for bf16/int8 about one chunk per decode worker
- *               of a 256-CU device, from B, KH, G and max_seq_len (or
- *               idx_stride), between 32 and 2048 (1024 with token_idx)
- *               tokens; 256 for fp32
+ *               (up to 2048 bf16 workers, 1024 int8 or 32-column ones),
+ *               from B, KH, G, q_rows and max_seq_len (or idx_stride),
+ *               between 32 and 4096 tokens (at most 64 pages of a paged
+ *               cache; 128 to 1024 kept tokens with token_idx); 256 for
+ *               fp32.  attn_decode_split_tokens reports the choice
  *   workspace   caller-owned scratch of at least attn_decode_workspace_size()
  *               bytes, 256-byte aligned; holds the work-list and partials
  *   out         [B][KH*G][D] in out_dtype (ATTN_F32 or ATTN_BF16)
