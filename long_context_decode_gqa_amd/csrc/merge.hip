@@ -146,22 +146,43 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *o_par
 // the row's channel slices [c*nq, (c+1)*nq), nq = D/4/csplit, with nq * 16
 // threads, so rows with many partials get more, smaller workgroups.
 // Thread (grp, q) owns the 16-byte column slice q and the slots grp,
-// grp + 16, ... of the row, and folds them in order with a running maximum
-// (online log-sum-exp: on a larger m the sums so far are rescaled); it
-// issues U slots' loads before folding them, so a pass covers 16 U slots in
-// one round trip to memory.  The 16 slot groups are then combined through
-// LDS in a fixed order.  Neither csplit nor U changes which slots a thread
-// folds or in what order, so the result depends only on the partials.
+// grp + 16, ... of the row (consecutive threads read consecutive slices of
+// one slot), and folds them in order with a running maximum (online
+// log-sum-exp: on a larger m the sums so far are rescaled), issuing U slots'
+// loads before folding them, so a pass covers 16 U slots in one round trip
+// to memory.  A decode call's first pass is addressed from the workspace
+// layout alone and goes out together with the read of the sequence length
+// that says how many of its slots count.  The 16 groups' states of a slice
+// then meet in 16 consecutive lanes (one transpose through LDS) and combine
+// by a fixed butterfly (xor 8, 4, 2, 1); lane 0 of the 16 writes the slice.
+// Neither csplit nor U changes which slots a thread folds, in what order, or
+// how the groups combine, so the result depends only on the partials.
 constexpr int kMergeV4Threads = 512;  // at most: D = 128 in one workgroup
 constexpr int kMergeGroups = 16;      // slot groups per column slice
 
-template <int OUT, bool DECODE, int U>
+// (m, l, acc) of a fold, rescaled to the larger maximum and added; an empty
+// state has l = 0 and is the identity
+__device__ __forceinline__ void merge_state(float &m, float &l, f32x4_t &acc, float m2, float l2, f32x4_t acc2) {
+  if (l2 > 0.f) {
+    if (l > 0.f) {
+      const float M = fmaxf(m, m2);
+      const float s1 = expf(m - M), s2 = expf(m2 - M);
+      acc = s1 * acc + s2 * acc2;
+      l = s1 * l + s2 * l2;
+      m = M;
+    } else {
+      m = m2;
+      l = l2;
+      acc = acc2;
+    }
+  }
+}
+
+template <int OUT, bool DECODE, int U, bool FEW>
 __global__ __launch_bounds__(kMergeV4Threads) void merge_v4_kernel(const float *o_part, const float *m_part,
                                                                  const float *l_part, const int32_t *rss,
                                                                  DecodeParams dp, int32_t D, int32_t csplit,
                                                                  void *out, float *lse) {
-  __shared__ f32x4_t s_acc[kMergeV4Threads];
-  __shared__ float s_m[kMergeV4Threads], s_l[kMergeV4Threads];
   const int row = blockIdx.x;
   // decode partials are laid out per (pair, column); the output row of a
   // column follows q's layout ([B][R][KH*Gq])
@@ -172,74 +193,117 @@ __global__ __launch_bounds__(kMergeV4Threads) void merge_v4_kernel(const float *
   }
   const int tid = threadIdx.x;
   const float NEG_INF = -__builtin_huge_valf();
-  int s0, n, ss;
-  row_slots<DECODE>(row, rss, dp, &s0, &n, &ss);
-  const int nq = D / 4 / csplit;   // column slices of this workgroup
   constexpr int ng = kMergeGroups;
+  const int nq = D / 4 / csplit;  // column slices of this workgroup
   const int grp = tid / nq, ql = tid - grp * nq;
   const int q = blockIdx.y * nq + ql;  // the row's slice
   float mt = NEG_INF, lt = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  {
-    for (int base = grp; base < n; base += ng * U) {
-      float m[U], l[U];
-      f32x4_t o[U];
+  auto fold = [&](float m, float l, f32x4_t o) {
+    if (l > 0.f) {  // empty partials (l = 0) may hold any o
+      if (m > mt) {
+        const float sc = expf(mt - m);
+        acc *= sc;
+        lt *= sc;
+        mt = m;
+      }
+      const float w = expf(m - mt) * l;
+      acc += w * o;
+      lt += w;
+    }
+  };
+  int s0, n, ss;
+  int first = 0;  // slots already folded
+  if constexpr (DECODE && FEW) {
+    // slot j of row (pair, g) is entry s0 + j*G, j < 2*max_chunks in the
+    // workspace; the pair's own count n arrives with the first pass's loads
+    const int pair = row / dp.G, g = row - pair * dp.G;
+    s0 = pair * 2 * dp.max_chunks * dp.G + g;
+    ss = dp.G;
+    const int ncap = 2 * dp.max_chunks;
+    constexpr int U1 = U < 16 ? U : 16;  // a first pass of 32 would spill
+    if (ncap > 0) {
+      float m[U1], l[U1];
+      f32x4_t o[U1];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int sl = base + u * ng;
-        const bool in = sl < n;
-        const int64_t i = s0 + (int64_t)(in ? sl : 0) * ss;
-        l[u] = in ? l_part[i] : 0.f;
+      for (int u = 0; u < U1; ++u) {
+        const int sl = grp + u * ng;
+        const int64_t i = s0 + (int64_t)(sl < ncap ? sl : 0) * ss;
+        l[u] = l_part[i];
         m[u] = m_part[i];
         o[u] = *(const f32x4_t *)(o_part + i * D + 4 * q);
       }
+      n = 2 * pair_chunks(dp, pair);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (l[u] > 0.f) {  // empty partials (l = 0) may hold any o
-          if (m[u] > mt) {
-            const float sc = expf(mt - m[u]);
-            acc *= sc;
-            lt *= sc;
-            mt = m[u];
-          }
-          const float w = expf(m[u] - mt) * l[u];
-          acc += w * o[u];
-          lt += w;
-        }
-      }
+      for (int u = 0; u < U1; ++u) fold(m[u], grp + u * ng < n ? l[u] : 0.f, o[u]);
+      first = ng * U1;
+    } else {
+      n = 0;
     }
+  } else {
+    row_slots<DECODE>(row, rss, dp, &s0, &n, &ss);
   }
+  for (int base = first + grp; base < n; base += ng * U) {
+    float m[U], l[U];
+    f32x4_t o[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int sl = base + u * ng;
+      const bool in = sl < n;
+      const int64_t i = s0 + (int64_t)(in ? sl : 0) * ss;
+      l[u] = in ? l_part[i] : 0.f;
+      m[u] = m_part[i];
+      o[u] = *(const f32x4_t *)(o_part + i * D + 4 * q);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) fold(m[u], l[u], o[u]);
+  }
+  __shared__ f32x4_t s_acc[kMergeV4Threads];
+  __shared__ float s_m[kMergeV4Threads], s_l[kMergeV4Threads];
   s_acc[tid] = acc;
   s_m[tid] = mt;
   s_l[tid] = lt;
   __syncthreads();
-  if (tid < nq) {
-    float M = NEG_INF;
-    for (int g = 0; g < ng; ++g)
-      if (s_l[g * nq + ql] > 0.f) M = fmaxf(M, s_m[g * nq + ql]);
-    f32x4_t a = {0.f, 0.f, 0.f, 0.f};
-    float Ls = 0.f;
-    for (int g = 0; g < ng; ++g) {
-      const float lg = s_l[g * nq + ql];
-      if (lg > 0.f) {
-        const float sc = expf(s_m[g * nq + ql] - M);
-        a += sc * s_acc[g * nq + ql];
-        Ls += sc * lg;
-      }
+  int qo;
+  if constexpr (FEW) {
+    // transpose: thread (slice tid / 16, group tid % 16) takes that state,
+    // and the 16 lanes of a slice combine by the butterfly
+    const int tq = tid / ng, tg = tid - tq * ng;
+    const int src = tg * nq + tq;
+    acc = s_acc[src];
+    mt = s_m[src];
+    lt = s_l[src];
+#pragma unroll
+    for (int off = ng / 2; off >= 1; off >>= 1) {
+      const float m2 = __shfl_xor(mt, off, ng), l2 = __shfl_xor(lt, off, ng);
+      f32x4_t a2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a2[i] = __shfl_xor(acc[i], off, ng);
+      merge_state(mt, lt, acc, m2, l2, a2);
     }
-    const float inv = Ls > 0.f ? 1.0f / Ls : 0.f;
-    const f32x4_t r = a * inv;
-    if constexpr (OUT == ATTN_F32) {
-      *(f32x4_t *)((float *)out + orow * D + 4 * q) = r;
-    } else {
-      uint16_t *po = (uint16_t *)out + orow * D + 4 * q;
-      const uint32_t w0 = f32_to_bf16_bits(r[0]) | (f32_to_bf16_bits(r[1]) << 16);
-      const uint32_t w1 = f32_to_bf16_bits(r[2]) | (f32_to_bf16_bits(r[3]) << 16);
-      *(uint32_t *)po = w0;
-      *(uint32_t *)(po + 2) = w1;
-    }
-    if (q == 0 && lse) lse[orow] = Ls > 0.f ? M + logf(Ls) : NEG_INF;
+    if (tg != 0) return;
+    qo = blockIdx.y * nq + tq;
+  } else {
+    // thread q of the first nq combines the 16 groups of its slice in order
+    if (tid >= nq) return;
+    mt = NEG_INF;
+    lt = 0.f;
+    acc = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < ng; ++g) merge_state(mt, lt, acc, s_m[g * nq + ql], s_l[g * nq + ql], s_acc[g * nq + ql]);
+    qo = q;
   }
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const f32x4_t r = acc * inv;
+  if constexpr (OUT == ATTN_F32) {
+    *(f32x4_t *)((float *)out + orow * D + 4 * qo) = r;
+  } else {
+    uint16_t *po = (uint16_t *)out + orow * D + 4 * qo;
+    const uint32_t w0 = f32_to_bf16_bits(r[0]) | (f32_to_bf16_bits(r[1]) << 16);
+    const uint32_t w1 = f32_to_bf16_bits(r[2]) | (f32_to_bf16_bits(r[3]) << 16);
+    *(uint32_t *)po = w0;
+    *(uint32_t *)(po + 2) = w1;
+  }
+  if (qo == 0 && lse) lse[orow] = lt > 0.f ? mt + logf(lt) : NEG_INF;
 }
 
 __global__ __launch_bounds__(256) void copy_kernel(u32x4_t *dst, const u32x4_t *src, size_t n) {
@@ -287,12 +351,23 @@ static void launch_merge_v4(const float *o_part, const float *m_part, const floa
                             hipStream_t s) {
   const int cs = merge_csplit(rows, D);
   const dim3 g(rows, cs), blk((D / 4 / cs) * kMergeGroups);
-  if (many_slots)
-    hipLaunchKernelGGL((merge_v4_kernel<OUT, DECODE, 32>), g, blk, 0, s, o_part, m_part, l_part, rss, dp, D, cs, out,
-                       lse);
-  else
-    hipLaunchKernelGGL((merge_v4_kernel<OUT, DECODE, 8>), g, blk, 0, s, o_part, m_part, l_part, rss, dp, D, cs, out,
-                       lse);
+  // Up to 512 rows the merge is a latency chain (a few hundred workgroups):
+  // the speculative first pass and the butterfly shorten it.  With more rows
+  // it is bound by the work of its many workgroups, where the lean serial
+  // combine is faster and wasted speculative loads on short rows add up
+  // (128K rows: 9.8 vs 11.2 us; ragged 2048 rows: 15.6 vs 20.5 us).
+  const bool few = rows <= 512;
+#define LCDG_MERGE_V4(U_, FEW_)                                                                                  \
+  hipLaunchKernelGGL((merge_v4_kernel<OUT, DECODE, U_, FEW_>), g, blk, 0, s, o_part, m_part, l_part, rss, dp, D, cs, \
+                     out, lse)
+  if (many_slots) {
+    if (few) LCDG_MERGE_V4(32, true);
+    else LCDG_MERGE_V4(32, false);
+  } else {
+    if (few) LCDG_MERGE_V4(8, true);
+    else LCDG_MERGE_V4(8, false);
+  }
+#undef LCDG_MERGE_V4
 }
 
 hipError_t launch_merge(const float *o_part, const float *m_part, const float *l_part, const int32_t *rss,

@@ -155,15 +155,16 @@ def test_token_index_subset():
     check(out, lse, ref, ref_lse)
 
 
-@pytest.mark.parametrize("D,maxc,misaligned", [(128, 9, False), (128, 300, False), (64, 300, False),
-                                               (4, 70, False), (37, 40, False), (128, 50, True)])
-def test_merge_lse_of_oracle_partials(D, maxc, misaligned):
+@pytest.mark.parametrize("D,maxc,misaligned,rows", [(128, 9, False, 37), (128, 300, False, 37), (64, 300, False, 37),
+                                                    (4, 70, False, 37), (37, 40, False, 37), (128, 50, True, 37),
+                                                    (128, 12, False, 700), (64, 200, False, 600)])
+def test_merge_lse_of_oracle_partials(D, maxc, misaligned, rows):
     """attn_merge_lse on random partials: empty rows, empty partials holding
     NaN outputs (they must be ignored), rows longer than one pass of the
-    single-pass kernel, odd head sizes and an output not 16-byte aligned
-    (the general kernel)."""
+    single-pass kernel, odd head sizes, an output not 16-byte aligned (the
+    general kernel), and more than 512 rows (the single-pass kernel's
+    serial combine instead of its butterfly)."""
     rng = np.random.default_rng(3 + D + maxc)
-    rows = 37
     counts = rng.integers(0, maxc, size=rows)
     counts[0] = 0
     rss = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
@@ -173,7 +174,7 @@ def test_merge_lse_of_oracle_partials(D, maxc, misaligned):
     l[rng.random(n) < 0.1] = 0.0          # empty chunks
     o = rng.normal(0, 1, (n, D))
     o[l == 0.0] = np.nan
-    log_case(f"merge of oracle partials D={D} max count={maxc} misaligned={misaligned}")
+    log_case(f"merge of oracle partials D={D} max count={maxc} misaligned={misaligned} rows={rows}")
     out_buf = torch.empty(rows * D + 1, dtype=torch.float32, device=DEV)
     out_t = out_buf[1:].view(rows, D) if misaligned else out_buf[:rows * D].view(rows, D)
     out, lse = pkg.attn_merge_lse(to_dev(o.astype(np.float32)), to_dev(m.astype(np.float32)),
