@@ -234,8 +234,10 @@ def bench_int8(pkg, torch, synth, steps, warmup, dev):
 
     tokens = w.kv_tokens()
     p = prep(64, pkg.QUANT_EXACT)
-    # the quantisation passes just wrote 1.5 GiB: a longer untimed warm-up lets the step settle
-    ms, dk, mg = time_decode(torch, p, steps, max(2 * warmup, 10))
+    # the quantisation passes just wrote 1.5 GiB and the host then idled on the scale read: the
+    # first few dozen steps after that run 4-6 us slow (the same configuration timed again later,
+    # as the scheme "bf16_query_k64", does not), so the untimed warm-up is 50 steps (about 10 ms)
+    ms, dk, mg = time_decode(torch, p, steps, max(2 * warmup, 50))
     kvb = kv_bytes(tokens, w.KH, w.D, 1) + k_codes[64][1].numel() * 4 + 4
     schemes = {}
     for name, part, qq in (("A_k64", 64, pkg.QUANT_ROW), ("A_k128", 128, pkg.QUANT_ROW),
