@@ -33,8 +33,9 @@ __device__ __forceinline__ float half_sum(float v) {
 }
 
 // DC: the head-size class (64, 128 or 256) that sizes the per-thread load
-// registers; two tiles' loads are in flight while one is computed.
-template <int DC>
+// registers; two tiles' loads are in flight while one is computed.  IDX:
+// positions go through the kept-token list.
+template <int DC, bool IDX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_valu_kernel(DecodeParams p) {
   constexpr int kVChunks = kVTile * DC / 4 / 256;  // 16-byte loads per thread for K (and V) of a tile
   __shared__ float s_q[16][kVMaxD];                  // q * softmax_scale
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int L = min(max(p.seq_lens[b], 0), p.max_seq_len);
     int npos = L;
     const int *idxp = nullptr;
-    if (p.token_idx) {
+    if constexpr (IDX) {
       npos = L > 0 ? min(max(p.n_idx[pair], 0), p.idx_stride) : 0;
       idxp = p.token_idx + (int64_t)pair * p.idx_stride;
     }
@@ -85,8 +86,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 
     // The K and V rows of the tile starting at position pos: chunk
-    // c = tid + 256 j is row c / cpr, channels 4 (c % cpr) ..; rows at or past
-    // the segment's end load nothing (zeros).
+    // c = tid + 256 j is row c / cpr, channels 4 (c % cpr) ...  The loads are
+    // unconditional, so the compiler can wait for one tile's loads while the
+    // next tile's stay in flight: a row at or past the segment's end (or past
+    // the tile) reads the segment's last row instead, which is harmless, as
+    // positions past the end get probability 0 and rows past the tile are
+    // never staged.  pos_end > 0 whenever this is called.
     struct TileRegs {
       f32x4_t k[kVChunks], v[kVChunks];
     };
@@ -96,14 +101,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int j = 0; j < kVChunks; ++j) {
         const int c = tid + 256 * j, r = c / cpr;
-        rk[j] = rv[j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-        if (r < kVTile && pos + r < pos_end) {
-          int tok = pos + r;
-          if (idxp) tok = min(max(idxp[tok], 0), L - 1);
-          const int64_t off = (int64_t)tok * p.stride_t + 4 * (c - r * cpr);
-          rk[j] = *(const f32x4_t *)(kb + off);
-          rv[j] = *(const f32x4_t *)(vb + off);
-        }
+        int tok = min(pos + min(r, kVTile - 1), pos_end - 1);
+        if constexpr (IDX) tok = min(max(idxp[tok], 0), L - 1);
+        const int64_t off = (int64_t)tok * p.stride_t + 4 * (c - r * cpr);
+        rk[j] = *(const f32x4_t *)(kb + off);
+        rv[j] = *(const f32x4_t *)(vb + off);
       }
     };
     auto store_tile = [&](const TileRegs &R) {
@@ -226,9 +228,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 hipError_t launch_decode_valu(const DecodeParams &p, int q_dtype, int kv_dtype, hipStream_t s) {
   if (q_dtype != ATTN_F32 || kv_dtype != ATTN_F32 || p.D > kVMaxD || p.D % 4) return hipErrorInvalidValue;
-  if (p.D <= 64) hipLaunchKernelGGL(decode_valu_kernel<64>, dim3(p.grid), dim3(256), 0, s, p);
-  else if (p.D <= 128) hipLaunchKernelGGL(decode_valu_kernel<128>, dim3(p.grid), dim3(256), 0, s, p);
-  else hipLaunchKernelGGL(decode_valu_kernel<256>, dim3(p.grid), dim3(256), 0, s, p);
+  const bool idx = p.token_idx != nullptr;
+  if (p.D <= 64) {
+    if (idx) hipLaunchKernelGGL((decode_valu_kernel<64, true>), dim3(p.grid), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((decode_valu_kernel<64, false>), dim3(p.grid), dim3(256), 0, s, p);
+  } else if (p.D <= 128) {
+    if (idx) hipLaunchKernelGGL((decode_valu_kernel<128, true>), dim3(p.grid), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((decode_valu_kernel<128, false>), dim3(p.grid), dim3(256), 0, s, p);
+  } else {
+    if (idx) hipLaunchKernelGGL((decode_valu_kernel<256, true>), dim3(p.grid), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((decode_valu_kernel<256, false>), dim3(p.grid), dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 
