@@ -240,3 +240,37 @@ def test_one_kv_head_share_full_size_sampled_rows(name):
     """One GPU's share of a split over 8 GPUs by KV heads (KH = 1, the rest of the shape as named),
     in the library's default launch: 512 workers of 32 tiles instead of 2048."""
     _full_size_sampled_rows(name, 12, 5, KH=1, split_tokens=0)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_reused_workspace_after_longer_rows(out_dtype):
+    """The merge's first slot loads run ahead of a row's own chunk count, so
+    slots past that count may still hold live partials of an earlier call on
+    the same workspace: a call over full-length rows followed by one over
+    shorter rows (prefixes of the same K/V, the same workspace and chunk
+    layout) must give exactly the shorter rows' result."""
+    import dataclasses
+    full = 4096
+    w = synth.workload("gqa32k", B=4, KH=2, lens=np.full(4, full, np.int32), split_tokens=256, seed=141)
+    q, k, v, g = synth.generate(w)
+    qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
+    kd, vd = to_dev(k), to_dev(v)
+    geom = dev_geom(g)
+    lse = torch.empty((w.B, w.QH), dtype=torch.float32, device=DEV)
+    p = pkg.prepare_decode(qd, kd, vd, geom, w.G, lse=lse, out_dtype=out_dtype, split_tokens=w.split_tokens)
+    log_case(f"reused workspace: full-length call ({out_dtype})")
+    p()
+    torch.cuda.synchronize()
+    ref_full, _ = oracle.attention_rows(problem(w, q, k, v, g), [(0, 0), (3, w.QH - 1)])
+    got_full = p.out.float().cpu().numpy().reshape(w.B * w.QH, w.D)[[0, 4 * w.QH - 1]]
+    assert np.abs(got_full - ref_full).max() <= TOL + (np.abs(ref_full).max() * 2.0 ** -9)
+    short = np.array([100, 0, full, 1500], np.int32)
+    geom.seq_lens.copy_(torch.from_numpy(short))
+    log_case(f"reused workspace: shorter rows {short.tolist()} ({out_dtype})")
+    p()
+    torch.cuda.synchronize()
+    g2 = dataclasses.replace(g, lens=short)
+    pr = problem(w, q, k, v, g2)
+    ref, ref_lse = oracle.attention_rows(pr, oracle.all_rows(pr), nthreads=8)
+    check(p.out.float().cpu().numpy().reshape(w.B * w.QH, w.D), lse.cpu().numpy().reshape(-1), ref, ref_lse,
+          bf16_out=out_dtype == torch.bfloat16)
