@@ -2,46 +2,56 @@
 // size 4..256 (a multiple of 4) and any group size.  Same work split and
 // partial format as the matrix-core kernel; used for fp32 inputs.
 //
-// One 256-thread workgroup per worker.  Each 32-token tile of a segment is
-// staged in LDS with coalesced 16-byte loads (K transposed, so the score
+// One 256-thread workgroup per worker.  Each tile of a segment (64
+// positions, 32 for head sizes above 128) is staged in LDS with coalesced 16-byte loads (K transposed, so the score
 // loop reads consecutive tokens across lanes), and the next two tiles' loads
 // are in flight in registers while the current one is computed.  The tile then
 // follows the online softmax of the Flash Attention block pseudo-code
 // ("注意力优化（Attention Optimization）"): scores -> new running max ->
 // rescale (alpha) -> probabilities -> O = alpha*O + P V, in natural-log
 // units; the chunk's (m, l, O/l) is the partial triple of
-// "优化稀疏注意力中的令牌丢弃机制" §5.  Thread (head g, token i) of a half
-// wave computes that score and takes the head's running max and sum with
-// half-wave shuffles, so the softmax needs no serial loop.
+// "优化稀疏注意力中的令牌丢弃机制" §5.  Thread (head g, position i) of a
+// lane group (a wave, or half of one for 32-position tiles) computes that
+// score and takes the head's running max and sum with shuffles inside the
+// group, so the softmax needs no serial loop.
 #include "common.hpp"
 
 namespace lcdg {
 namespace {
 
-constexpr int kVTile = 32;   // tokens per tile = lanes per head in the score phase
+constexpr int kWT = 32;      // tokens per tile of the work split (the lane walk's unit)
 constexpr int kVMaxD = 256;  // largest head size
 
-__device__ __forceinline__ float half_max(float v) {
+// max / sum over the W lanes of a lane group (W = 32 or 64)
+template <int W>
+__device__ __forceinline__ float group_max(float v) {
 #pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 32));
+  for (int o = W / 2; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, W));
   return v;
 }
-__device__ __forceinline__ float half_sum(float v) {
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
 #pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, 32);
+  for (int o = W / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, W);
   return v;
 }
 
 // DC: the head-size class (64, 128 or 256) that sizes the per-thread load
-// registers; two tiles' loads are in flight while one is computed.  IDX:
-// positions go through the kept-token list.
+// registers; two tiles' loads are in flight while one is computed.  A
+// compute tile holds TT = 64 positions (32 for head sizes above 128, which
+// would not fit two tiles' loads in registers): the steps of a segment are a
+// chain of dependent LDS phases and barriers, so fewer, larger steps finish
+// it sooner.  IDX: positions go through the kept-token list.
 template <int DC, bool IDX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_valu_kernel(DecodeParams p) {
-  constexpr int kVChunks = kVTile * DC / 4 / 256;  // 16-byte loads per thread for K (and V) of a tile
-  __shared__ float s_q[16][kVMaxD];                  // q * softmax_scale
-  __shared__ float s_kt[kVMaxD][kVTile + 1];         // K^T of the tile
-  __shared__ __attribute__((aligned(16))) float s_v[kVTile][kVMaxD];
-  __shared__ float s_p[16][kVTile];                  // probabilities (0 past the segment)
+  constexpr int TT = DC > 128 ? 32 : 64;         // positions per compute tile = lanes per head (scores)
+  constexpr int NP = 16 * TT / 256;                // score passes over the 16 heads of a block
+  constexpr int KO = 16 * DC / 256;                // (head, channel) outputs per thread
+  constexpr int kVChunks = TT * DC / 4 / 256;      // 16-byte loads per thread for K (and V) of a tile
+  __shared__ float s_q[16][DC];                    // q * softmax_scale
+  __shared__ float s_kt[DC][TT + 1];               // K^T of the tile
+  __shared__ __attribute__((aligned(16))) float s_v[TT][DC];
+  __shared__ float s_p[16][TT];                    // probabilities (0 past the segment)
   __shared__ float s_alpha[16], s_m[16], s_l[16];
 
   const int tid = threadIdx.x;
@@ -54,9 +64,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   if ((int)blockIdx.x >= nwg) return;
   const int t_begin = (int)((int64_t)blockIdx.x * T / nwg);
   const int t_end = (int)((int64_t)(blockIdx.x + 1) * T / nwg);
-  const int ct = p.split / kVTile;
-  // score-phase roles: head tid / 32 (+ 8 for the second pass), token tid % 32
-  const int sg = tid / kVTile, si = tid % kVTile;
+  const int ct = p.split / kWT;
+  // score-phase roles: head tid / TT (+ 256 / TT per further pass), position tid % TT
+  const int sg = tid / TT, si = tid % TT;
 
   // every wave of the workgroup walks the lanes alike
   LaneHit hit = wave_find_lane(p, t_begin);
@@ -101,7 +111,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int j = 0; j < kVChunks; ++j) {
         const int c = tid + 256 * j, r = c / cpr;
-        int tok = min(pos + min(r, kVTile - 1), pos_end - 1);
+        int tok = min(pos + min(r, TT - 1), pos_end - 1);
         if constexpr (IDX) tok = min(max(idxp[tok], 0), L - 1);
         const int64_t off = (int64_t)tok * p.stride_t + 4 * (c - r * cpr);
         rk[j] = *(const f32x4_t *)(kb + off);
@@ -114,7 +124,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int j = 0; j < kVChunks; ++j) {
         const int c = tid + 256 * j, r = c / cpr;
-        if (r < kVTile) {
+        if (r < TT) {
           const int d = 4 * (c - r * cpr);
 #pragma unroll
           for (int i = 0; i < 4; ++i) s_kt[d + i][r] = rk[j][i];
@@ -128,13 +138,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const int chunk = (seg_t0 - lane_t0) / ct;
       const int chunk_t1 = min(lane_t1, lane_t0 + (chunk + 1) * ct);
       const int seg_t1 = min(run_end, chunk_t1);
-      const int pos0 = (seg_t0 - lane_t0) * kVTile;
-      const int pos1 = min(npos, (seg_t1 - lane_t0) * kVTile);
-      // running max and sum of heads sg and sg + 8 (every lane of a half wave holds its head's)
-      float m_run[2] = {NEG_INF, NEG_INF}, l_run[2] = {0.f, 0.f};
-      float o[16];
+      const int pos0 = (seg_t0 - lane_t0) * kWT;
+      const int pos1 = min(npos, (seg_t1 - lane_t0) * kWT);
+      // running max and sum of heads sg + (256 / TT) h (every lane of a head's
+      // lane group holds that head's)
+      float m_run[NP], l_run[NP];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) o[k] = 0.f;
+      for (int h = 0; h < NP; ++h) {
+        m_run[h] = NEG_INF;
+        l_run[h] = 0.f;
+      }
+      float o[KO];
+#pragma unroll
+      for (int k = 0; k < KO; ++k) o[k] = 0.f;
 
       // tile tp: stage it (its loads were issued two tiles ago), issue the
       // loads of tile tp + 2 tiles into the same registers, compute
@@ -142,13 +158,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         if (tp >= pos1) return;
         __syncthreads();  // the previous tile's readers are done
         store_tile(R);
-        load_tile(R, tp + 2 * kVTile, pos1);
+        load_tile(R, tp + 2 * TT, pos1);
         __syncthreads();
-        const int n = min(kVTile, pos1 - tp);
+        const int n = min(TT, pos1 - tp);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int g = sg + 8 * h;
-          if (g < gcount) {  // uniform over the half wave
+        for (int h = 0; h < NP; ++h) {
+          const int g = sg + (256 / TT) * h;
+          if (g < gcount) {  // uniform over the lane group
             float acc = 0.f;
             int d = 0;
             for (; d + 8 <= D; d += 8) {
@@ -157,10 +173,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
             for (; d < D; ++d) acc += s_q[g][d] * s_kt[d][si];
             const float s = si < n ? acc : NEG_INF;
-            const float m_new = fmaxf(m_run[h], half_max(s));  // finite: the tile has a token
+            const float m_new = fmaxf(m_run[h], group_max<TT>(s));  // finite: the tile has a token
             const float e = si < n ? expf(s - m_new) : 0.f;
             const float alpha = m_run[h] == NEG_INF ? 0.f : expf(m_run[h] - m_new);
-            l_run[h] = alpha * l_run[h] + half_sum(e);
+            l_run[h] = alpha * l_run[h] + group_sum<TT>(e);
             m_run[h] = m_new;
             s_p[g][si] = e;
             if (si == 0) s_alpha[g] = alpha;
@@ -169,27 +185,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         __syncthreads();
         // O = alpha O + P V for the (g, d) outputs this thread owns
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
+        for (int k = 0; k < KO; ++k) {
           const int e = tid + 256 * k;
           if (e < gcount * D) {
             const int g = e / D, d = e - g * D;
             float acc = o[k] * s_alpha[g];
 #pragma unroll
-            for (int i = 0; i < kVTile; ++i) acc += s_p[g][i] * s_v[i][d];
+            for (int i = 0; i < TT; ++i) acc += s_p[g][i] * s_v[i][d];
             o[k] = acc;
           }
         }
       };
       TileRegs ra, rb;
       load_tile(ra, pos0, pos1);
-      load_tile(rb, pos0 + kVTile, pos1);
-      for (int tp = pos0; tp < pos1; tp += 2 * kVTile) {
+      load_tile(rb, pos0 + TT, pos1);
+      for (int tp = pos0; tp < pos1; tp += 2 * TT) {
         step(ra, tp);
-        step(rb, tp + kVTile);
+        step(rb, tp + TT);
       }
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int g = sg + 8 * h;
+      for (int h = 0; h < NP; ++h) {
+        const int g = sg + (256 / TT) * h;
         if (g < gcount && si == 0) {
           s_m[g] = m_run[h];
           s_l[g] = l_run[h];
@@ -200,7 +216,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const int half = (seg_t0 == lane_t0 + chunk * ct) ? 0 : 1;
       const bool fill_second = half == 0 && seg_t1 == chunk_t1;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
+      for (int k = 0; k < KO; ++k) {
         const int e = tid + 256 * k;
         if (e < gcount * D) {
           const int g = e / D, d = e - g * D;
