@@ -607,14 +607,32 @@ __global__ __launch_bounds__(256) void oam_select_kernel(OamDev o) {
   } else {
     select_threshold<false>(o, pair, L, b0, need, nullptr, nullptr, s_hist, s_tmp, s_res, &T, &I_T);
   }
-  for (int j = tid; j < nblk; j += 256) s_kept[j] = 0;
-  __syncthreads();
-  const float *sc = o.scores + (int64_t)pair * o.L_max;
-  auto count_kept = [&](uint32_t key, int idx) {
-    if ((int)(key >> 21) == b0 && (key > T || (key == T && idx <= I_T))) atomicAdd(&s_kept[idx / kBlockTok], 1);
-  };
-  if (in_lds) for_items<true>(s_ck, s_ci, sc, C, count_kept);
-  else for_items<false>(s_ck, s_ci, sc, L, count_kept);
+  if (in_lds) {
+    // the gathered list is in block order (block j's candidates are items
+    // s_pre[j] .. s_pre[j+1]-1), so wave w counts blocks w, w+4, ... with
+    // ballots: per-item atomics on one block's counter would serialise
+    const int wave = tid >> 6, lane = tid & 63;
+    for (int j = wave; j < nblk; j += 4) {
+      int cnt = 0;
+      for (int i0 = s_pre[j]; i0 < s_pre[j + 1]; i0 += 64) {
+        const int i = i0 + lane;
+        bool kept = false;
+        if (i < s_pre[j + 1]) {
+          const uint32_t key = s_ck[i];
+          kept = key > T || (key == T && s_ci[i] <= I_T);
+        }
+        cnt += __popcll(__ballot(kept));
+      }
+      if (lane == 0) s_kept[j] = cnt;
+    }
+  } else {
+    for (int j = tid; j < nblk; j += 256) s_kept[j] = 0;
+    __syncthreads();
+    const float *sc = o.scores + (int64_t)pair * o.L_max;
+    for_items<false>(s_ck, s_ci, sc, L, [&](uint32_t key, int idx) {
+      if ((int)(key >> 21) == b0 && (key > T || (key == T && idx <= I_T))) atomicAdd(&s_kept[idx / kBlockTok], 1);
+    });
+  }
   __syncthreads();
   int run = 0;
   for (int j0 = 0; j0 < nblk; j0 += 256) {
