@@ -355,7 +355,8 @@ static void launch_merge_v4(const float *o_part, const float *m_part, const floa
   // the speculative first pass and the butterfly shorten it.  With more rows
   // it is bound by the work of its many workgroups, where the lean serial
   // combine is faster and wasted speculative loads on short rows add up
-  // (128K rows: 9.8 vs 11.2 us; ragged 2048 rows: 15.6 vs 20.5 us).
+  // (the 128K step's 256 rows: 9.8 vs 11.2 us; the ragged batch's 2048
+  // rows: 15.6 vs 20.5 us).
   const bool few = rows <= 512;
 #define LCDG_MERGE_V4(U_, FEW_)                                                                                  \
   hipLaunchKernelGGL((merge_v4_kernel<OUT, DECODE, U_, FEW_>), g, blk, 0, s, o_part, m_part, l_part, rss, dp, D, cs, \
