@@ -143,22 +143,26 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *o_par
 }
 
 // Single-pass merge for D % 4 == 0.  Workgroup (row, c) of csplit takes
-// the row's channel slices [c*nq, (c+1)*nq), nq = D/4/csplit, with nq * 16
-// threads, so rows with many partials get more, smaller workgroups.
-// Thread (grp, q) owns the 16-byte column slice q and the slots grp,
-// grp + 16, ... of the row (consecutive threads read consecutive slices of
-// one slot), and folds them in order with a running maximum (online
-// log-sum-exp: on a larger m the sums so far are rescaled), issuing U slots'
-// loads before folding them, so a pass covers 16 U slots in one round trip
-// to memory.  A decode call's first pass is addressed from the workspace
-// layout alone and goes out together with the read of the sequence length
-// that says how many of its slots count.  The 16 groups' states of a slice
-// then meet in 16 consecutive lanes (one transpose through LDS) and combine
-// by a fixed butterfly (xor 8, 4, 2, 1); lane 0 of the 16 writes the slice.
+// the row's channel slices [c*nq, (c+1)*nq), nq = D/4/csplit, with nq * ng
+// threads, ng slot groups per slice (16, or 4 beyond 512 rows), so rows
+// with many partials get more, smaller workgroups.  Thread (grp, q) owns
+// the 16-byte column slice q and the slots grp, grp + ng, ... of the row
+// (consecutive threads read consecutive slices of one slot), and folds them
+// in order with a running maximum (online log-sum-exp: on a larger m the
+// sums so far are rescaled), issuing U slots' loads before folding them, so
+// a pass covers ng U slots in one round trip to memory.  Up to 512 rows, a
+// decode call's first pass is addressed from the workspace layout alone and
+// goes out together with the read of the sequence length that says how many
+// of its slots count, and the 16 groups' states of a slice then meet in 16
+// consecutive lanes (one transpose through LDS) and combine by a fixed
+// butterfly (xor 8, 4, 2, 1); lane 0 of the 16 writes the slice.  Beyond
+// 512 rows, thread q of the first nq combines its slice's groups in order.
 // Neither csplit nor U changes which slots a thread folds, in what order, or
-// how the groups combine, so the result depends only on the partials.
+// how the groups combine, so the result depends only on the partials and on
+// which side of 512 rows the call falls.
 constexpr int kMergeV4Threads = 512;  // at most: D = 128 in one workgroup
-constexpr int kMergeGroups = 16;      // slot groups per column slice
+constexpr int kMergeGroups = 16;      // slot groups per column slice (up to 512 rows)
+constexpr int kMergeGroupsMany = 4;   // slot groups per column slice beyond 512 rows
 
 // (m, l, acc) of a fold, rescaled to the larger maximum and added; an empty
 // state has l = 0 and is the identity
@@ -193,7 +197,7 @@ __global__ __launch_bounds__(kMergeV4Threads) void merge_v4_kernel(const float *
   }
   const int tid = threadIdx.x;
   const float NEG_INF = -__builtin_huge_valf();
-  constexpr int ng = kMergeGroups;
+  constexpr int ng = FEW ? kMergeGroups : kMergeGroupsMany;
   const int nq = D / 4 / csplit;  // column slices of this workgroup
   const int grp = tid / nq, ql = tid - grp * nq;
   const int q = blockIdx.y * nq + ql;  // the row's slice
@@ -350,14 +354,15 @@ static void launch_merge_v4(const float *o_part, const float *m_part, const floa
                             const DecodeParams &dp, int rows, int D, bool many_slots, void *out, float *lse,
                             hipStream_t s) {
   const int cs = merge_csplit(rows, D);
-  const dim3 g(rows, cs), blk((D / 4 / cs) * kMergeGroups);
+  const bool few = rows <= 512;
+  const dim3 g(rows, cs), blk((D / 4 / cs) * (few ? kMergeGroups : kMergeGroupsMany));
   // Up to 512 rows the merge is a latency chain (a few hundred workgroups):
   // the speculative first pass and the butterfly shorten it.  With more rows
   // it is bound by the work of its many workgroups, where the lean serial
   // combine is faster and wasted speculative loads on short rows add up
   // (the 128K step's 256 rows: 9.8 vs 11.2 us; the ragged batch's 2048
-  // rows: 15.6 vs 20.5 us).
-  const bool few = rows <= 512;
+  // rows: 15.6 vs 20.5 us); there each slice also has 4 slot groups
+  // instead of 16, so short rows do not occupy 16 mostly idle groups.
 #define LCDG_MERGE_V4(U_, FEW_)                                                                                  \
   hipLaunchKernelGGL((merge_v4_kernel<OUT, DECODE, U_, FEW_>), g, blk, 0, s, o_part, m_part, l_part, rss, dp, D, cs, \
                      out, lse)
