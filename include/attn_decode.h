@@ -156,15 +156,22 @@ typedef struct {
  *               (each < L_b; any order; n_idx <= idx_stride), e.g. the kept
  *               set written by oam_score_topk
  *   softmax_scale  multiplies q.k; 0 selects 1/sqrt(D)
- *   split_tokens   tokens per split-KV chunk (multiple of 32); 0 = library
- *               default: for bf16/int8 about one chunk per decode worker
- *               (up to 2048 bf16 workers, 1024 int8 or 32-column ones),
- *               from B, KH, G, q_rows and max_seq_len (or idx_stride),
- *               between 32 and 4096 tokens (at most 64 pages of a paged
- *               cache; 128 to 1024 kept tokens with token_idx); 256 for
- *               fp32.  attn_decode_split_tokens reports the choice
+ *   split_tokens   the split-KV granularity, a multiple of 32; 0 = library
+ *               default.  bf16/int8 KV: the positions of all (b, kh) are laid
+ *               end to end and cut into one equal contiguous range per
+ *               decode worker, each range at least split_tokens positions
+ *               long (fewer workers when there is less work); a (b, kh)
+ *               then spans at most ceil(L_b / split_tokens) + 1 ranges, each
+ *               giving one partial.  Default 4096 (128 kept tokens for int8
+ *               or 256 for bf16 with token_idx, up to 1024 for long lists).
+ *               fp32 KV: chunks of split_tokens positions, default 256.
+ *               attn_decode_split_tokens reports the choice
  *   workspace   caller-owned scratch of at least attn_decode_workspace_size()
- *               bytes, 256-byte aligned; holds the work-list and partials
+ *               bytes, 256-byte aligned; holds the partials and, for
+ *               bf16/int8 KV, one arrival counter per (b, kh).  It needs no
+ *               initialisation: every call leaves its counters at zero
+ *               arrivals and takes over a counter word that holds anything
+ *               else (a fixed 40-bit tag marks the library's words)
  *   out         [B][KH*G][D] in out_dtype (ATTN_F32 or ATTN_BF16)
  *   lse         optional fp32 [B][KH*G]: natural-log log-sum-exp of the
  *               scaled scores (-inf for a sequence with no tokens)
@@ -195,37 +202,44 @@ typedef struct {
 } attn_decode_args;
 
 /* Host-only: bytes of workspace attn_decode_splitkv needs for these args
- * (depends on B, KH, G, D, max_seq_len or idx_stride, split_tokens, dtypes).
+ * (depends on B, KH, G, D, max_seq_len or idx_stride, split_tokens, dtypes
+ * and the current device's compute-unit count).
  * Writes *bytes; returns ATTN_ERR_INVALID_ARG / ATTN_ERR_UNSUPPORTED for
  * arguments attn_decode_splitkv would reject. */
 attn_status attn_decode_workspace_size(const attn_decode_args *args, size_t *bytes);
 
-/* Host-only: the chunk length in tokens (split_tokens) attn_decode_splitkv
+/* Host-only: the split granularity in tokens (split_tokens) attn_decode_splitkv
  * uses for these args: the given one, or for split_tokens = 0 the library's
- * default, chosen from the lengths' upper bound, dtypes and query rows.
+ * default, chosen from the dtypes and, with token_idx, the list length.
  * Writes *split_tokens; same argument errors as attn_decode_workspace_size. */
 attn_status attn_decode_split_tokens(const attn_decode_args *args, int32_t *split_tokens);
 
 /*
  * Split-KV decode attention ("优化稀疏注意力中的令牌丢弃机制" §5 Split-KV;
- * "注意力优化" Flash Attention online softmax).  One call enqueues:
- *  (1) a persistent decode kernel.  Every (b, kh) token range is cut into
- *      tiles of 32 positions and all ranges are laid end to end; each worker
- *      streams an equal contiguous share of that tile stream once, and for
- *      each chunk of split_tokens positions it touches writes the partial
- *      (m, l, o) of each of the G query heads;
- *  (2) the log-sum-exp merge of those partials into out (and lse), the
- *      operation attn_merge_lse exposes on its own.
- * Results are deterministic: no floating-point atomics are used, and the
- * work split depends only on the lengths and the device's compute-unit count.
+ * "注意力优化" Flash Attention online softmax).  Every (b, kh) position range
+ * is cut into tiles of 32 positions and all ranges are laid end to end; each
+ * worker of a persistent grid streams an equal contiguous share of that tile
+ * stream once.
+ *  bf16/int8 KV: one launch.  A worker's part of a (b, kh) is one partial
+ *      (m, l, o) per query head, written to the workspace; a worker holding
+ *      a whole (b, kh) writes out and lse directly.  The last worker to finish
+ *      a shared (b, kh) (an integer arrival counter) merges its partials by
+ *      the log-sum-exp rule into out and lse inside the same launch.
+ *  fp32 KV: a decode launch writes partials per chunk of split_tokens
+ *      positions, and a second launch merges them (the operation
+ *      attn_merge_lse exposes on its own).
+ * Results are deterministic: no floating-point atomics are used, partials
+ * are merged in a fixed order, and the work split depends only on the
+ * lengths and the device's compute-unit count.
  */
 attn_status attn_decode_splitkv(const attn_decode_args *args, attn_stream_t stream);
 
 /*
  * attn_decode_splitkv plus timing marks: events[0..2] (hipEvent_t created by
  * the caller, any may be NULL) are recorded on `stream` before the decode
- * kernel, before the merge and after the merge, so the caller can read each
- * phase's duration.  Same arguments and errors.
+ * kernel, after it, and after the merge launch (for bf16/int8 KV the merge
+ * runs inside the decode kernel, so the last two marks follow each other).
+ * Same arguments and errors.
  */
 attn_status attn_decode_splitkv_profiled(const attn_decode_args *args, attn_stream_t stream, void *const events[3]);
 

@@ -71,11 +71,12 @@ attn_status check_geom(const attn_kv_geom &g, int es, bool need_ptrs) {
 }
 
 struct DecodeLayout {
-  size_t m, l, o, total;
-  int64_t max_partials, max_chunks;
-  int32_t split, ngb, max_tokens;
-  int32_t cols;  // matrix-core columns per decode worker (16, or 32 for more than 16 rows per KV head)
-  bool mfma;
+  size_t m, l, o, ctr, total;
+  int64_t max_partials, max_chunks, max_slots, lanes;
+  int32_t split, ngb, max_tokens, grid;
+  int32_t cols;  // matrix-core columns per decode wave (16, or 32 for more than 16 rows per KV head)
+  int32_t wpg;   // waves per decode worker (workgroup)
+  bool mfma;     // matrix-core decode (bf16/int8 KV), whose launch also merges
 };
 
 attn_status plan_decode(const attn_decode_args *a, DecodeLayout *L) {
@@ -135,62 +136,72 @@ attn_status plan_decode(const attn_decode_args *a, DecodeLayout *L) {
       return fail(ATTN_ERR_INVALID_ARG, "q, k and v must be 16-byte aligned");
   }
   L->mfma = mfma;
-  // More than 16 query rows per KV head: each worker computes 32 columns
+  // More than 16 query rows per KV head: each wave computes 32 columns
   // (two blocks sharing every K/V load) instead of streaming the cache once
   // per 16-column block.
   L->cols = (mfma && R * a->G > 16) ? 32 : 16;
   L->ngb = (R * a->G + L->cols - 1) / L->cols;
   L->max_tokens = a->token_idx ? a->idx_stride : g.max_seq_len;
+  L->lanes = (int64_t)g.B * g.KH * (mfma ? 1 : L->ngb);
+  const int64_t lane_tiles_max = ((int64_t)L->max_tokens + 31) / 32;
+  const int64_t max_tiles = L->lanes * lane_tiles_max;
+  if (max_tiles >= (int64_t(1) << 31)) return fail(ATTN_ERR_UNSUPPORTED, "too many positions in one call");
+  // Workers: matrix-core waves run eight per compute unit (two per SIMD, the
+  // register budget) for bf16 and four (one per SIMD) for int8 or 32-column
+  // waves, in workers of four waves.  The vector-ALU kernel runs four
+  // 256-thread workgroups per unit.
+  L->wpg = mfma ? 4 : 1;
+  const int cus = device_cu_count();
+  const int waves_per_cu = (L->cols == 32 || a->kv_dtype == ATTN_I8) ? 4 : 8;
+  const int64_t grid_cap = mfma ? (int64_t)cus * waves_per_cu / L->wpg : (int64_t)cus * 4;
   if (a->split_tokens) {
     L->split = a->split_tokens;
   } else if (!mfma) {
     L->split = 256;
   } else if (a->token_idx) {
-    // Gathered runs are short and a worker's fixed costs weigh more: chunks
-    // of at least 256 (bf16) or 128 (int8) and at most 1024 kept tokens
-    // (4096 kept tokens per pair, bf16: 2048 two-tile workers took 26.6 us,
-    // 512 eight-tile workers 23.3 us, 256 sixteen-tile workers 26.7 us;
-    // int8: 27.6, 24.8 with four-tile workers, 26.1 us).
-    const int64_t tiles = (int64_t)g.B * g.KH * L->ngb * (((int64_t)L->max_tokens + 31) / 32);
-    const int64_t ct = std::min<int64_t>(std::max<int64_t>(tiles / 2048, a->kv_dtype == ATTN_I8 ? 4 : 8), 32);
+    // Gathered runs are short and a worker's fixed costs weigh more: at
+    // least 256 (bf16) or 128 (int8) and at most 1024 kept tokens per
+    // worker (4096 kept tokens per pair, bf16: 2048 two-tile workers took
+    // 26.6 us, 512 eight-tile workers 23.3 us, 256 sixteen-tile workers
+    // 26.7 us; int8: 27.6, 24.8 with four-tile workers, 26.1 us).
+    const int64_t ct = std::min<int64_t>(std::max<int64_t>(max_tiles / 2048, a->kv_dtype == ATTN_I8 ? 4 : 8), 32);
     L->split = (int32_t)(32 * ct);
   } else {
-    // About one chunk per worker, each worker streaming at least 32 tiles
-    // when there are enough: every partial costs a write in the stream and
-    // a read in the merge, and two one-wave workers per compute unit with
-    // their register rings already keep HBM busy.  At most 2048 bf16
-    // workers (two per SIMD) and 1024 int8 or 32-column workers (one per
-    // SIMD); chunks of at most 4096 tokens.  The tile count is the bound
-    // from max_seq_len (the lengths are on the device).  Measured on a
-    // 256 MiB bf16 step (16384 tiles): 2048 workers 61 us, 512 workers
-    // 52 us; on the 1 GiB int8 128K step: 2048 workers 205 us, 1024 with
-    // 4096-token chunks 193 us; on the ragged bf16 batch: 2048-token chunks
-    // 648 us, 4096-token 640 us.
-    const int64_t tiles = (int64_t)g.B * g.KH * L->ngb * (((int64_t)L->max_tokens + 31) / 32);
-    const bool one_per_simd = L->cols == 32 || a->kv_dtype == ATTN_I8;
-    const int64_t wmax = one_per_simd ? 1024 : 2048;
-    const int64_t workers = std::min<int64_t>(std::max<int64_t>(tiles / 32, 256), wmax);
-    int64_t ct = std::min<int64_t>(std::max<int64_t>(tiles / workers, 1), 128);
-    if (g.block_table) ct = std::min<int64_t>(ct, 2 * (int64_t)g.page_tokens);  // a chunk spans <= 64 pages
-    L->split = (int32_t)(32 * ct);
+    // Every wave streams at least 32 tiles when there are enough: each
+    // worker's result costs a partial write and a read in the merge, and
+    // the grid's waves with their register rings already keep HBM busy.
+    L->split = 32 * 32 * L->wpg;
   }
-  if (mfma && ((int64_t)g.max_seq_len + 64) * g.stride_t * elem_size(a->kv_dtype) >= (int64_t(1) << 31))
-    return fail(ATTN_ERR_UNSUPPORTED, "one (sequence, KV head) may span at most 2 GiB of rows");
-  if (mfma && a->token_idx && L->split > 1024)
-    return fail(ATTN_ERR_UNSUPPORTED, "with token_idx, split_tokens must be <= 1024");
-  if (g.block_table && (int64_t)L->split > 64 * (int64_t)g.page_tokens)
-    return fail(ATTN_ERR_UNSUPPORTED, "with a paged cache, split_tokens must be <= 64 * page_tokens");
-  L->max_chunks = ((int64_t)L->max_tokens + L->split - 1) / L->split;
+  // Buffer resources use 32-bit offsets: over one (sequence, KV head), or
+  // over one page of a paged cache.
+  const int64_t span_rows = (g.block_table ? (int64_t)g.page_tokens : (int64_t)g.max_seq_len) + 64;
+  if (mfma && span_rows * g.stride_t * elem_size(a->kv_dtype) >= (int64_t(1) << 31))
+    return fail(ATTN_ERR_UNSUPPORTED, "one (sequence, KV head) or page may span at most 2 GiB of rows");
+  // The grid: at most grid_cap workers, and no more than ranges of at least
+  // split_tokens positions (the kernel's own rule), so the workers in use
+  // are the first ones dispatched.
+  const int64_t ct = L->split / 32;
+  L->grid = (int32_t)std::max<int64_t>(1, std::min<int64_t>(grid_cap, (max_tiles + ct - 1) / ct));
   const int64_t QH = (int64_t)g.KH * a->G * R;
-  L->max_partials = 2 * (int64_t)g.B * QH * L->max_chunks;
-  const int64_t nlanes = (int64_t)g.B * g.KH * L->ngb;
-  const int64_t max_tiles = nlanes * (((int64_t)L->max_tokens + 31) / 32);
-  if (L->max_partials >= (int64_t(1) << 31) || max_tiles >= (int64_t(1) << 31))
+  if (mfma) {
+    // A lane's workers: its tiles over ranges of at least ct tiles touch at
+    // most ceil(tiles / ct) + 1 ranges, and there are at most grid workers.
+    L->max_chunks = 0;
+    L->max_slots = std::min<int64_t>(L->grid, (lane_tiles_max + ct - 1) / ct + 1);
+    L->max_partials = (int64_t)g.B * QH * L->max_slots;
+  } else {
+    L->max_chunks = ((int64_t)L->max_tokens + L->split - 1) / L->split;
+    L->max_slots = 0;
+    L->max_partials = 2 * (int64_t)g.B * QH * L->max_chunks;
+  }
+  if (L->max_partials >= (int64_t(1) << 31))
     return fail(ATTN_ERR_UNSUPPORTED, "too many split-KV partials (reduce max_seq_len or raise split_tokens)");
   size_t off = 0;
   L->m = off; off = align256(off + L->max_partials * sizeof(float));
   L->l = off; off = align256(off + L->max_partials * sizeof(float));
   L->o = off; off = align256(off + (size_t)L->max_partials * g.D * sizeof(float));
+  L->ctr = off;
+  if (mfma) off = align256(off + (size_t)L->lanes * sizeof(uint64_t));
   L->total = off;
   return ATTN_OK;
 }
@@ -257,6 +268,7 @@ static attn_status decode_impl(const attn_decode_args *a, attn_stream_t stream, 
   p.D = a->kv.D;
   p.QH = a->kv.KH * p.G;
   p.ngb = L.ngb;
+  p.lpp = L.mfma ? 1 : L.ngb;
   p.cols_per_wave = L.cols;
   p.seq_lens = a->kv.seq_lens;
   p.seq_offset = a->kv.seq_offset;
@@ -283,24 +295,16 @@ static attn_status decode_impl(const attn_decode_args *a, attn_stream_t stream, 
   p.split = L.split;
   p.max_seq_len = a->kv.max_seq_len;
   p.max_chunks = (int32_t)L.max_chunks;
-  {
-    // persistent grid: the MFMA kernel runs one-wave workers, eight per compute
-    // unit (two per SIMD, its register budget; four, one per SIMD, for
-    // 32-column workers); the vector-ALU kernel four 256-thread workgroups
-    // per unit; capped by the largest possible tile count
-    const int cus = device_cu_count();
-    const int64_t max_tiles = (int64_t)p.B * p.KH * L.ngb * (((int64_t)L.max_tokens + 31) / 32);
-    int64_t grid = (int64_t)cus * (L.mfma ? (L.cols == 32 ? 4 : 8) : 4);
-    if (grid > max_tiles) grid = max_tiles;
-    // no more workers than ranges of at least one chunk (the kernel's own
-    // rule), so the workers in use are the first ones dispatched
-    const int64_t ct = L.split / 32;
-    if (grid > (max_tiles + ct - 1) / ct) grid = (max_tiles + ct - 1) / ct;
-    p.grid = (int)(grid < 1 ? 1 : grid);
-  }
+  p.max_slots = (int32_t)L.max_slots;
+  p.wpg = L.wpg;
+  p.grid = L.grid;
   p.wl.m_part = reinterpret_cast<float *>(ws + L.m);
   p.wl.l_part = reinterpret_cast<float *>(ws + L.l);
   p.wl.o_part = reinterpret_cast<float *>(ws + L.o);
+  p.wl.ctr = L.mfma ? reinterpret_cast<uint64_t *>(ws + L.ctr) : nullptr;
+  p.out_dtype = a->out_dtype;
+  p.out = a->out;
+  p.lse = a->lse;
 
   auto mark = [&](int i) -> hipError_t {
     if (events && events[i]) return hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s);
@@ -312,8 +316,10 @@ static attn_status decode_impl(const attn_decode_args *a, attn_stream_t stream, 
   else e = launch_decode_valu(p, a->q_dtype, a->kv_dtype, s);
   if (e != hipSuccess) return fail_hip(e, "decode launch");
   if ((e = mark(1)) != hipSuccess) return fail_hip(e, "event record");
-  e = launch_merge_decode(p, a->out_dtype, a->out, a->lse, s);
-  if (e != hipSuccess) return fail_hip(e, "merge launch");
+  if (!L.mfma) {
+    e = launch_merge_decode(p, a->out_dtype, a->out, a->lse, s);
+    if (e != hipSuccess) return fail_hip(e, "merge launch");
+  }
   if ((e = mark(2)) != hipSuccess) return fail_hip(e, "event record");
   return ATTN_OK;
 }

@@ -78,22 +78,33 @@ __device__ __forceinline__ int64_t uniform_i64(int64_t v) {
 
 // ---------------------------------------------------------------- work split
 
-// Split-KV partial buffers.  Pair (b, kh) = b*KH + kh owns 2*max_chunks slots,
-// two per chunk of split_tokens positions: at most one worker-range boundary
-// can fall inside a chunk, so slot 2j holds the part of chunk j before that
-// boundary (or all of it) and slot 2j+1 the part after it (or an empty
-// partial: m = -inf, l = 0).  The partial of head g in slot j is entry
-// (pair*2*max_chunks + j)*G + g, so one worker's partials of a head group are
-// contiguous.  Slots of chunks past the pair's own chunk count are never read.
+// Split-KV partial buffers.  The matrix-core decode gives each pair (b, kh) =
+// b*KH + kh max_slots slots: a lane's partial from its k-th worker goes to
+// slot k, the entry of column g being (pair*max_slots + k)*G + g.  The
+// vector-ALU decode gives each pair 2*max_chunks slots, two per chunk of
+// split_tokens positions: at most one worker-range boundary can fall inside
+// a chunk, so slot 2j holds the part of chunk j before that boundary (or all
+// of it) and slot 2j+1 the part after it (or an empty partial: m = -inf,
+// l = 0), at entry (pair*2*max_chunks + j)*G + g; its merge is a separate
+// launch.
 struct WorkList {
   float *m_part;             // [max partials] natural-log max
   float *l_part;             // [max partials]
   float *o_part;             // [max partials][D]
+  // Merge inside the matrix-core decode launch: one arrival counter per lane.  A counter
+  // word holds (kCtrTag << 24) | arrivals.  Every call leaves its counters at
+  // zero arrivals, and a word without the tag (a workspace that has held
+  // something else) is taken over by the first arrival, so the workspace
+  // needs no clearing.
+  uint64_t *ctr;             // [lanes] (matrix-core decode)
 };
 
 struct DecodeParams {
   // G: query rows per KV head (the matrix-core columns), R * Gq; QH = KH * G
-  int32_t B, KH, G, D, QH, ngb;
+  // ngb: column blocks per KV head (16-row blocks for the vector-ALU decode,
+  // 32-column groups of one worker for the matrix-core decode); lpp: lanes
+  // per pair (ngb for the vector-ALU decode, 1 for the matrix-core decode)
+  int32_t B, KH, G, D, QH, ngb, lpp;
   int32_t Gq, R;  // query heads per KV head, query rows per sequence
   int32_t cols_per_wave;  // matrix-core columns a decode worker computes: 16, or 32 when G > 16
   const int32_t *seq_lens;
@@ -113,9 +124,15 @@ struct DecodeParams {
   float softmax_scale;
   int32_t split;        // tokens per chunk (multiple of 32)
   int32_t max_seq_len;  // lengths are clamped to this bound
-  int32_t max_chunks;   // chunks of the longest possible row
+  int32_t max_chunks;   // chunks of the longest possible row (vector-ALU decode)
+  int32_t max_slots;    // partial slots per pair (matrix-core decode)
   int32_t grid;         // workgroups launched for the decode kernel
+  int32_t wpg;          // waves per decode workgroup (the MFMA kernel's workers)
   WorkList wl;
+  // outputs, written by the matrix-core decode launch
+  int32_t out_dtype;
+  void *out;
+  float *lse;
 };
 
 // Row of q/out/lse ([B][R][KH*Gq]) of column gc (= r*Gq + g) of KV head kh.
@@ -124,8 +141,9 @@ __device__ __forceinline__ int64_t q_row_index(const DecodeParams &p, int b, int
   return ((int64_t)(b * p.R + r) * p.KH + kh) * p.Gq + g;
 }
 
-// A "lane" is (b, kh, query-head block of up to 16 heads): lane q belongs to
-// pair q / ngb = b*KH + kh and covers ceil(n / 32) tiles of 32 positions,
+// A "lane" is (b, kh, query-head block) (the matrix-core decode: (b, kh)):
+// lane q belongs to pair q / lpp = b*KH + kh and covers ceil(n / 32) tiles of
+// 32 positions,
 // n = the sequence length (or kept-index count in indexed mode), clamped to
 // the declared bounds.  All lanes' tiles are laid end to end in lane order;
 // decode workers split that stream into equal contiguous ranges, so every
@@ -140,7 +158,7 @@ __device__ __forceinline__ int pair_chunks(const DecodeParams &p, int pair) {
   return (pair_positions(p, pair) + p.split - 1) / p.split;
 }
 __device__ __forceinline__ int lane_tiles(const DecodeParams &p, int q) {
-  return q < p.B * p.KH * p.ngb ? (pair_positions(p, q / p.ngb) + 31) / 32 : 0;
+  return q < p.B * p.KH * p.lpp ? (pair_positions(p, q / p.lpp) + 31) / 32 : 0;
 }
 
 __device__ __forceinline__ int wave_incl_scan(int v) {
@@ -155,7 +173,7 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 
 // Tiles of all lanes (wave-wide; every thread of the wave gets the total).
 __device__ __forceinline__ int wave_total_tiles(const DecodeParams &p) {
-  const int nl = p.B * p.KH * p.ngb;
+  const int nl = p.B * p.KH * p.lpp;
   int acc = 0;
   for (int q = threadIdx.x & 63; q < nl; q += 64) acc += lane_tiles(p, q);
   return __builtin_amdgcn_readfirstlane(wave_sum_int(acc));
@@ -168,7 +186,7 @@ struct LaneHit {
 };
 __device__ __forceinline__ LaneHit wave_find_lane(const DecodeParams &p, int t) {
   const int lane = threadIdx.x & 63;
-  const int nl = p.B * p.KH * p.ngb;
+  const int nl = p.B * p.KH * p.lpp;
   LaneHit h = {0, 0, 0};
   int run = 0;
   for (int base = 0; base < nl; base += 64) {
@@ -190,7 +208,7 @@ __device__ __forceinline__ LaneHit wave_find_lane(const DecodeParams &p, int t) 
 
 // The lane after h that has tiles (its first tile follows h's last).
 __device__ __forceinline__ LaneHit next_lane(const DecodeParams &p, LaneHit h) {
-  const int nl = p.B * p.KH * p.ngb;
+  const int nl = p.B * p.KH * p.lpp;
   LaneHit n = {h.q, h.t0 + h.nt, 0};
   while (n.nt == 0 && n.q + 1 < nl) {
     ++n.q;
@@ -204,6 +222,57 @@ __device__ __forceinline__ LaneHit next_lane(const DecodeParams &p, LaneHit h) {
 __device__ __forceinline__ int workers_for(const DecodeParams &p, int total_tiles) {
   return total_tiles == 0 ? 0 : min(p.grid, max(1, total_tiles / (p.split / 32)));
 }
+
+// The worker whose range [w*T/W, (w+1)*T/W) holds tile t (0 <= t < T): the
+// largest w with floor(w*T/W) <= t.
+__device__ __forceinline__ int worker_of(int t, int T, int W) {
+  return (int)(((int64_t)(t + 1) * W - 1) / T);
+}
+
+// One arrival on a lane counter (see WorkList::ctr); returns the arrivals of
+// this call so far, this one included.  The usual case is one atomic add.  An
+// arrival that finds a word without the tag sets it to the tagged count 1 by
+// compare-and-swap, or, when another arrival did that first, adds itself
+// again (its first add went into the old word); this loop ends because every
+// failed exchange means another arrival changed the word.  Relaxed at agent
+// scope: the caller orders its own partial stores before this call (they are
+// device-scope stores, complete once vmcnt drains) and issues the merge's
+// loads only after the result returns.
+constexpr uint64_t kCtrTag = 0x5A17C0DE42ull;  // 40 bits
+__device__ __forceinline__ int lane_arrive(uint64_t *c) {
+  const uint64_t clean = kCtrTag << 24;
+  const uint64_t old = __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((old >> 24) == kCtrTag) return (int)(old & 0xFFFFFFu) + 1;
+  uint64_t cur = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (;;) {
+    if ((cur >> 24) == kCtrTag) {
+      const uint64_t again = __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return (int)(again & 0xFFFFFFu) + 1;
+    }
+    uint64_t expect = cur;
+    if (__hip_atomic_compare_exchange_strong(c, &expect, clean | 1u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return 1;
+    cur = expect;
+  }
+}
+
+// The last arrival of a call leaves the counter at zero arrivals.
+__device__ __forceinline__ void lane_reset(uint64_t *c) {
+  __hip_atomic_store(c, kCtrTag << 24, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until every vector-memory access this wave issued has completed; for
+// device-scope (sc1) stores that means they are visible to every compute unit.
+__device__ __forceinline__ void wait_vmem() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt left free
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Cache policy of the merge's buffer accesses: device scope (sc1), so stores
+// write through to memory every XCD reads and loads fetch from there.
+constexpr int kDeviceScope = 16;
 
 // Host-side launchers (each returns hipSuccess or the launch error).
 hipError_t launch_merge_decode(const DecodeParams &p, int32_t out_dtype, void *out, float *lse, hipStream_t s);

@@ -1,10 +1,10 @@
 // Split-KV GQA decode attention on gfx950 matrix cores (bf16 or int8 KV).
 //
-// One wave is one worker of a persistent grid.  The 32-token tiles of every
-// (sequence b, KV head kh, column block) are laid end to end and each wave
-// streams one balanced contiguous range of them, cut into chunks of
-// split_tokens positions, with its next tiles in flight in a register ring
-// while it computes the current one:
+// A workgroup of one or four waves is one worker of a persistent grid.  The
+// 32-token tiles of every (sequence b, KV head kh, column block) are laid end
+// to end and each worker streams one balanced contiguous range of them, with
+// its next tiles in flight in a register ring while it computes the current
+// one:
 //
 //   S^T[t][g]  = K[t][:] . Q[g][:]            v_mfma_f32_16x16x32_{bf16,f16}
 //   online softmax per query head g (running max m, sum l; exp2 domain)
@@ -14,8 +14,9 @@
 // ("注意力优化（Attention Optimization）", Flash Attention pseudo-code; NVIDIA
 // blog "共同设计 AI 模型注意力…", BMM1 -> online softmax -> BMM2), and the
 // G query heads of a KV head share every K/V byte that is loaded (GQA head
-// sharing on the same pages).  The chunk's partial (m, l, o) is written for
-// the log-sum-exp merge ("优化稀疏注意力中的令牌丢弃机制" §5).
+// sharing on the same pages).  A worker's result over its part of a lane is
+// a partial (m, l, o), merged with the lane's other partials by the
+// log-sum-exp rule inside the same launch ("优化稀疏注意力中的令牌丢弃机制" §5).
 //
 // Operand layouts (16x16x32 MFMA, lane = 16*c + r, c = lane/16, r = lane%16):
 //  * A operand row r, k-slots 8c..8c+7 (8 consecutive elements of one lane).
@@ -106,24 +107,39 @@ struct Step {
   TileT t[TPS];
 };
 
-// Tokens per chunk of the indexed variant (its index list is staged in LDS).
+// Positions of an indexed segment (its index list is staged in LDS).
 constexpr int kMaxIdxChunk = 1024;
-// Page ids a segment of the paged variant stages in LDS (a chunk may span at
-// most 64 pages, so at most 65 are touched).
-constexpr int kMaxSegPages = 72;
+// Page ids a segment of the paged variant stages in LDS (a segment spans at
+// most 512 pages of tokens, so at most 513 are touched).
+constexpr int kMaxSegPages = 520;
 
-// One wave = one worker.  The work-list lays every (b, kh, head block) lane's
-// tiles end to end; worker w streams the contiguous tile range
-// [w*T/W, (w+1)*T/W), so all workers move the same number of K/V bytes
+// A workgroup of WPG waves is one worker.  The work-list lays every (b, kh,
+// column block) lane's tiles end to end; worker w streams the contiguous tile
+// range [w*T/W, (w+1)*T/W), so all workers move the same number of K/V bytes
 // whatever the mix of sequence lengths, with no atomics and no barriers in
-// the loop.  A range is cut into runs (one lane each) and runs into segments
-// (one chunk piece each); a segment's partial (m, l, o) goes straight from
-// registers to its slot.
+// the loop.  A range is cut into runs, one per lane it touches.  The waves of
+// a worker take a run's steps in turn (wave i: steps i, i + WPG, ...), so
+// together they read one contiguous stream; at the run's end they combine
+// their (m, l, O) through LDS (one wave keeps its own in registers).
+//
+// A run that covers its whole lane is the lane's result: it goes straight to
+// out and lse.  Otherwise it is one partial of the lane, in the slot given by
+// the worker's position among the lane's workers, and the merge runs inside
+// the launch: each worker arrives on the counters of its shared lanes (at
+// most its first and last) when its partial stores are complete, and the
+// arrival that completes a lane's count folds the lane's partials into out
+// and lse by the log-sum-exp rule ("优化稀疏注意力中的令牌丢弃机制" §5,
+// cross-shard online softmax).  Partials are stored and loaded at device
+// scope (they write through to memory every XCD reads), and the merge reads
+// only after its arrival returned the lane's full count.
+constexpr int kWPG = 4;  // waves per worker
+
 template <int D, int KVT, bool IDX, bool QI8, bool PAGED, int CB>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(CB == 2 ? 1 : 2, CB == 2 ? 1 : 2))) void
+__global__ __launch_bounds__(64 * kWPG) __attribute__((amdgpu_waves_per_eu(CB == 2 ? 1 : 2, CB == 2 ? 1 : 2))) void
 decode_mfma_kernel(DecodeParams p) {
   static_assert(!(IDX && PAGED), "a paged cache is read by position");
   static_assert(CB == 1 || CB == 2, "one or two 16-column blocks per wave");
+  constexpr int WPG = kWPG;
   typedef Tile<D, KVT, IDX> TileT;
   typedef Step<D, KVT, IDX, CB> StepT;
   constexpr int TPS = StepT::TPS;
@@ -132,6 +148,9 @@ decode_mfma_kernel(DecodeParams p) {
   constexpr int KL = TileT::KL;
   constexpr int KB = D / 32;
   constexpr int VW = TileT::VW;
+  constexpr int NT = 64 * WPG;     // threads of a worker
+  constexpr int kCols = 16 * CB;   // matrix-core columns of a wave
+  constexpr int NQ = D / 4;        // 16-byte slices of a row
   typedef typename std::conditional<KVT == ATTN_BF16, bf16x8_t, f16x8_t>::type OpT;
 
   __shared__ int s_idx[IDX ? kMaxIdxChunk : 1];
@@ -141,36 +160,111 @@ decode_mfma_kernel(DecodeParams p) {
   // int8 digit planes of each row's 22-bit fixed-point query (see below).
   constexpr int kQRow = D * 2 + 16;
   constexpr int kQDRow = D + 16;
-  constexpr int kQBytes = CB * (KVT == ATTN_I8 ? 3 * 16 * kQDRow : 16 * kQRow);
-  __shared__ __attribute__((aligned(16))) unsigned char s_q[kQBytes];
+  constexpr int kQBytes = CB * (KVT == ATTN_I8 ? 3 * 16 * kQDRow : 16 * kQRow);  // one column group
+  constexpr int kGroups = CB == 2 ? 2 : 1;  // column groups a worker can hold
+  __shared__ __attribute__((aligned(16))) unsigned char s_q[kGroups * kQBytes];
+  __shared__ float s_qs[KVT == ATTN_I8 ? kGroups * kCols : 1];  // int8: each column's query scale
+  // combination of the waves' states at a segment's end (WPG > 1)
+  __shared__ float s_cm[WPG * kCols], s_cl[WPG * kCols];
+  __shared__ f32x4_t s_co[WPG * kCols * NQ];
+  __shared__ int s_last;
 
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, cg = lane >> 4;
+  // More than 32 query rows per KV head: the waves form p.ngb = 2 column
+  // groups of 32 columns, and wave wi of each group takes the same steps, so
+  // both groups use every K/V tile while it is fresh in this compute unit's
+  // caches and the cache streams from HBM once.
+  const int S = WPG / p.ngb;                 // waves per column group
+  const int gi = wv / S, wi = wv - gi * S;   // this wave's group and its turn in the group
+  const int g0 = gi * kCols;                 // the group's first column
   const float c1 = p.softmax_scale * kLog2e;
   const float NEG_INF = -__builtin_huge_valf();
 
+  // out row orow, channels 4*sl .. 4*sl+3 (fp32 or bf16, rounded to nearest
+  // even); element stores where out is not aligned for the vector store
+  const uintptr_t out_addr = reinterpret_cast<uintptr_t>(p.out);
+  const bool out_vec = out_addr % (p.out_dtype == ATTN_F32 ? 16 : 4) == 0;
+  auto store_out4 = [&](int64_t orow, int sl, f32x4_t v) {
+    if (p.out_dtype == ATTN_F32) {
+      float *po = (float *)p.out + orow * D + 4 * sl;
+      if (out_vec) {
+        *(f32x4_t *)po = v;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) po[i] = v[i];
+      }
+    } else {
+      uint16_t *po = (uint16_t *)p.out + orow * D + 4 * sl;
+      if (out_vec) {
+        ((uint32_t *)po)[0] = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+        ((uint32_t *)po)[1] = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) po[i] = (uint16_t)f32_to_bf16_bits(v[i]);
+      }
+    }
+  };
+  // a pair's partials: entries pe0 .. pe0 + ne - 1 (max_slots * G of them)
+  auto o_rsrc = [&](int64_t pe0, int ne) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(p.wl.o_part + pe0 * D), (short)0, ne * D * 4, 0x00020000);
+  };
+  auto m_rsrc = [&](int64_t pe0, int ne) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(p.wl.m_part + pe0), (short)0, ne * 4, 0x00020000);
+  };
+  auto l_rsrc = [&](int64_t pe0, int ne) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(p.wl.l_part + pe0), (short)0, ne * 4, 0x00020000);
+  };
+
   const int T = wave_total_tiles(p);
   const int nworkers = workers_for(p, T);
+  if (wv == 0) {
+    // No worker visits a lane without positions, so its rows get out = 0 and
+    // lse = -inf here; lane qq belongs to
+    // workgroup qq % gridDim.x.
+    const int nl = p.B * p.KH;
+    for (int base = 0; base < nl; base += 64) {
+      const int qq = base + lane;
+      unsigned long long m = __ballot(qq < nl && qq % (int)gridDim.x == (int)blockIdx.x && lane_tiles(p, qq) == 0);
+      while (m) {
+        const int pz = base + __builtin_ctzll(m);
+        m &= m - 1;
+        const int bz = pz / p.KH, khz = pz - bz * p.KH;
+        for (int u = lane; u < p.G * NQ; u += 64) {
+          const int c = u / NQ, sl = u - c * NQ;
+          const int64_t orow = q_row_index(p, bz, khz, c);
+          store_out4(orow, sl, (f32x4_t){0.f, 0.f, 0.f, 0.f});
+          if (sl == 0 && p.lse) p.lse[orow] = NEG_INF;
+        }
+      }
+    }
+  }
   if ((int)blockIdx.x >= nworkers) return;
   const int t_begin = (int)((int64_t)blockIdx.x * T / nworkers);
   const int t_end = (int)((int64_t)(blockIdx.x + 1) * T / nworkers);
-  const int ct = p.split / kTile;  // tiles per chunk
 
   // the lane (b, kh, query-head block) holding the first tile of the range;
   // each later run takes the next lane that has tiles
   LaneHit hit = wave_find_lane(p, t_begin);
+  // lanes this worker shares with others, whose arrivals wait for its end
+  int npend = 0, pend_q0 = 0, pend_need0 = 0, pend_q1 = 0, pend_need1 = 0;
   for (int t = t_begin; t < t_end;) {
     if (hit.nt == 0) break;  // lane walk exhausted (cannot happen for t < total)
     const int q = hit.q;
     const int lane_t0 = hit.t0, lane_t1 = hit.t0 + hit.nt;
     const int run_end = min(t_end, lane_t1);
-    const int pair = q / p.ngb, gb = q - pair * p.ngb;
+    // workers holding part of this lane, and this worker's slot among them
+    const int w_first = worker_of(lane_t0, T, nworkers);
+    const int need = worker_of(lane_t1 - 1, T, nworkers) - w_first + 1;
+    const int slot = (int)blockIdx.x - w_first;
+    const int pair = q;
     const int b = pair / p.KH, kh = pair - b * p.KH;
     const int L = uniform_i32(min(max(p.seq_lens[b], 0), p.max_seq_len));
     int npos = L;
     if constexpr (IDX) npos = uniform_i32(L > 0 ? min(max(p.n_idx[pair], 0), p.idx_stride) : 0);
     // this lane's column of block cb is query row g0 + 16*cb + col of the KV head
-    const int g0 = gb * 16 * CB;
     bool qvalid[CB];
     int col_end[CB];
 #pragma unroll
@@ -199,11 +293,9 @@ decode_mfma_kernel(DecodeParams p) {
     const __amdgpu_buffer_rsrc_t ksrs = __builtin_amdgcn_make_buffer_rsrc(
         i8 ? (void *)(p.k_scale + (int64_t)pair * p.k_scale_stride) : nullptr, (short)0,
         i8 ? max(p.k_scale_stride, 1) * 4 : 0, 0x00020000);
-
     // Stage Q (the 16 heads of this block, zero past G) in LDS in MFMA
-    // operand form; tiles read their B operand from there.  The partial
-    // slots of this lane's rows are loaded now as well: a global load inside
-    // the segment loop would make the compiler wait for every load in
+    // operand form; tiles read their B operand from there.  A global load
+    // inside the segment loop would make the compiler wait for every load in
     // flight, the tile prefetch included.
     //
     // int8 KV: the scores run on the int8 matrix cores straight from the K
@@ -213,101 +305,105 @@ decode_mfma_kernel(DecodeParams p) {
     // int8 MFMA, and the three integer sums recombine exactly in fp32.  An
     // int8 query (QI8: per-row or static scale) is plane 0 alone.
     float qs[CB];  // int8: this lane's column scale s_col in each block
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) qs[cb] = 0.f;
     __syncthreads();
     if constexpr (KVT == ATTN_I8) {
-      constexpr int CPL = D / 4;  // lane (col, cg) takes column col, channels [cg*CPL, cg*CPL + CPL)
-      unsigned char *sq_blk = s_q;
+      if (wi == 0) {  // the first wave of each column group stages the group's query
+        constexpr int CPL = D / 4;  // lane (col, cg) takes column col, channels [cg*CPL, cg*CPL + CPL)
+        unsigned char *sq_blk = s_q + gi * kQBytes;
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb, sq_blk += 3 * 16 * kQDRow) {
-        float qv[CPL];
-        const uint16_t *qrow = (const uint16_t *)p.q + q_row_index(p, b, kh, g0 + 16 * cb + col) * D + cg * CPL;
+        for (int cb = 0; cb < CB; ++cb, sq_blk += 3 * 16 * kQDRow) {
+          float qv[CPL];
+          const uint16_t *qrow = (const uint16_t *)p.q + q_row_index(p, b, kh, g0 + 16 * cb + col) * D + cg * CPL;
 #pragma unroll
-        for (int x = 0; x < CPL / 8; ++x) {
-          u32x4_t w = (u32x4_t){0u, 0u, 0u, 0u};
-          if (qvalid[cb]) w = *(const u32x4_t *)(qrow + 8 * x);
-#pragma unroll
-          for (int y = 0; y < 4; ++y) {
-            qv[8 * x + 2 * y] = bf16_lo(w[y]);
-            qv[8 * x + 2 * y + 1] = bf16_hi(w[y]);
-          }
-        }
-        float mx = 0.f;
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) mx = fmaxf(mx, fabsf(qv[j]));
-        mx = rows_max(mx);  // the four lanes of column col hold all D channels
-        if constexpr (QI8) {
-          // int8 query (one digit plane): s = max|q_row| / 127, or the static
-          // scale, and code = clamp(rint(q / s), -127, 127), in IEEE fp32
-          // (correctly rounded divides, round half to even).
-          const float sq = p.q_quant == ATTN_QUANT_ROW ? mx / 127.0f : p.q_scale;
-          qs[cb] = sq;
-#pragma unroll
-          for (int x = 0; x < CPL / 16; ++x) {
-            uint32_t w[4];
-#pragma unroll
-            for (int j4 = 0; j4 < 4; ++j4) {
-              uint32_t acc = 0u;
-#pragma unroll
-              for (int y = 0; y < 4; ++y) {
-                float c = 0.f;
-                if (sq > 0.f) c = fminf(127.f, fmaxf(-127.f, __builtin_rintf(qv[16 * x + 4 * j4 + y] / sq)));
-                acc |= ((uint32_t)(int)c & 0xFFu) << (8 * y);
-              }
-              w[j4] = acc;
-            }
-            *(u32x4_t *)(sq_blk + col * kQDRow + cg * CPL + 16 * x) = (u32x4_t){w[0], w[1], w[2], w[3]};
-          }
-        } else {
-          const float inv = mx > 0.f ? 4194304.0f / mx : 0.f;
-          qs[cb] = mx * (1.0f / 4194304.0f);
-          uint32_t dw[3][CPL / 4];
-#pragma unroll
-          for (int j4 = 0; j4 < CPL / 4; ++j4) {
-            uint32_t w0 = 0u, w1 = 0u, w2 = 0u;
+          for (int x = 0; x < CPL / 8; ++x) {
+            u32x4_t w = (u32x4_t){0u, 0u, 0u, 0u};
+            if (qvalid[cb]) w = *(const u32x4_t *)(qrow + 8 * x);
 #pragma unroll
             for (int y = 0; y < 4; ++y) {
-              const int n = (int)__builtin_rintf(qv[4 * j4 + y] * inv);
-              const int d0 = (int)(int8_t)(n & 0xFF);
-              const int r1 = (n - d0) >> 8;
-              const int d1 = (int)(int8_t)(r1 & 0xFF);
-              const int d2 = (r1 - d1) >> 8;
-              w0 |= (uint32_t)(d0 & 0xFF) << (8 * y);
-              w1 |= (uint32_t)(d1 & 0xFF) << (8 * y);
-              w2 |= (uint32_t)(d2 & 0xFF) << (8 * y);
+              qv[8 * x + 2 * y] = bf16_lo(w[y]);
+              qv[8 * x + 2 * y + 1] = bf16_hi(w[y]);
             }
-            dw[0][j4] = w0;
-            dw[1][j4] = w1;
-            dw[2][j4] = w2;
           }
+          float mx = 0.f;
 #pragma unroll
-          for (int dg = 0; dg < 3; ++dg)
+          for (int j = 0; j < CPL; ++j) mx = fmaxf(mx, fabsf(qv[j]));
+          mx = rows_max(mx);  // the four lanes of column col hold all D channels
+          float sc;
+          if constexpr (QI8) {
+            // int8 query (one digit plane): s = max|q_row| / 127, or the static
+            // scale, and code = clamp(rint(q / s), -127, 127), in IEEE fp32
+            // (correctly rounded divides, round half to even).
+            const float sq = p.q_quant == ATTN_QUANT_ROW ? mx / 127.0f : p.q_scale;
+            sc = sq;
 #pragma unroll
-            for (int x = 0; x < CPL / 16; ++x)
-              *(u32x4_t *)(sq_blk + (dg * 16 + col) * kQDRow + cg * CPL + 16 * x) =
-                  (u32x4_t){dw[dg][4 * x], dw[dg][4 * x + 1], dw[dg][4 * x + 2], dw[dg][4 * x + 3]};
+            for (int x = 0; x < CPL / 16; ++x) {
+              uint32_t w[4];
+#pragma unroll
+              for (int j4 = 0; j4 < 4; ++j4) {
+                uint32_t acc = 0u;
+#pragma unroll
+                for (int y = 0; y < 4; ++y) {
+                  float c = 0.f;
+                  if (sq > 0.f) c = fminf(127.f, fmaxf(-127.f, __builtin_rintf(qv[16 * x + 4 * j4 + y] / sq)));
+                  acc |= ((uint32_t)(int)c & 0xFFu) << (8 * y);
+                }
+                w[j4] = acc;
+              }
+              *(u32x4_t *)(sq_blk + col * kQDRow + cg * CPL + 16 * x) = (u32x4_t){w[0], w[1], w[2], w[3]};
+            }
+          } else {
+            const float inv = mx > 0.f ? 4194304.0f / mx : 0.f;
+            sc = mx * (1.0f / 4194304.0f);
+            uint32_t dw[3][CPL / 4];
+#pragma unroll
+            for (int j4 = 0; j4 < CPL / 4; ++j4) {
+              uint32_t w0 = 0u, w1 = 0u, w2 = 0u;
+#pragma unroll
+              for (int y = 0; y < 4; ++y) {
+                const int n = (int)__builtin_rintf(qv[4 * j4 + y] * inv);
+                const int d0 = (int)(int8_t)(n & 0xFF);
+                const int r1 = (n - d0) >> 8;
+                const int d1 = (int)(int8_t)(r1 & 0xFF);
+                const int d2 = (r1 - d1) >> 8;
+                w0 |= (uint32_t)(d0 & 0xFF) << (8 * y);
+                w1 |= (uint32_t)(d1 & 0xFF) << (8 * y);
+                w2 |= (uint32_t)(d2 & 0xFF) << (8 * y);
+              }
+              dw[0][j4] = w0;
+              dw[1][j4] = w1;
+              dw[2][j4] = w2;
+            }
+#pragma unroll
+            for (int dg = 0; dg < 3; ++dg)
+#pragma unroll
+              for (int x = 0; x < CPL / 16; ++x)
+                *(u32x4_t *)(sq_blk + (dg * 16 + col) * kQDRow + cg * CPL + 16 * x) =
+                    (u32x4_t){dw[dg][4 * x], dw[dg][4 * x + 1], dw[dg][4 * x + 2], dw[dg][4 * x + 3]};
+          }
+          if (cg == 0) s_qs[g0 + 16 * cb + col] = sc;
         }
       }
     } else {
-      for (int e = lane; e < 16 * CB * (D / 8); e += 64) {
-        const int g = e / (D / 8), c8 = e - g * (D / 8);
+      // every column group's rows: column gc of the pair at row gc (a group
+      // is kCols rows, kQBytes bytes)
+      for (int e = tid; e < p.ngb * kCols * (D / 8); e += NT) {
+        const int gc = e / (D / 8), c8 = e - gc * (D / 8);
         u32x4_t w = (u32x4_t){0u, 0u, 0u, 0u};
-        if (g0 + g < p.G)
-          w = *(const u32x4_t *)((const uint16_t *)p.q + q_row_index(p, b, kh, g0 + g) * D + 8 * c8);
-        *(u32x4_t *)(s_q + g * kQRow + 16 * c8) = w;
+        if (gc < p.G) w = *(const u32x4_t *)((const uint16_t *)p.q + q_row_index(p, b, kh, gc) * D + 8 * c8);
+        *(u32x4_t *)(s_q + gc * kQRow + 16 * c8) = w;
       }
     }
-    // partial (pair, slot j, column g) lives at (pair*2*max_chunks + j)*G + g
-    const int slot_base = pair * 2 * p.max_chunks * p.G + g0 + col;
     __syncthreads();
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) qs[cb] = KVT == ATTN_I8 ? s_qs[g0 + 16 * cb + col] : 0.f;
+    const unsigned char *sq = s_q + gi * kQBytes;  // this wave's column group
     auto q_operand = [&](int cb, int kb) -> bf16x8_t {
-      return __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(s_q + (16 * cb + col) * kQRow + 16 * (4 * kb + cg)));
+      return __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(sq + (16 * cb + col) * kQRow + 16 * (4 * kb + cg)));
     };
     // int8: digit plane dg of channels 64kb + 16cg .. + 15 of column col of block cb
     auto q_digits = [&](int cb, int dg, int kb) -> i32x4_t {
       return __builtin_bit_cast(i32x4_t,
-                                *(const u32x4_t *)(s_q + ((3 * cb + dg) * 16 + col) * kQDRow + 64 * kb + 16 * cg));
+                                *(const u32x4_t *)(sq + ((3 * cb + dg) * 16 + col) * kQDRow + 64 * kb + 16 * cg));
     };
 
     // Positions of the current segment (IDX: its staged index list starts at
@@ -458,7 +554,9 @@ decode_mfma_kernel(DecodeParams p) {
         mt = rows_max(mt);
         const float m_new = fmaxf(m_run[cb], mt);
         if (__any(m_new > m_run[cb])) {
-          const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - m_new);
+          // a column with no position seen yet (m_run = -inf) holds zeros;
+          // the rescale must not form exp2(-inf - -inf)
+          const float alpha = m_run[cb] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(m_run[cb] - m_new);
           l_run[cb] *= alpha;
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) O[cb][nb] *= alpha;
@@ -535,34 +633,31 @@ decode_mfma_kernel(DecodeParams p) {
       for (int j = 0; j < TPS; ++j) finish_tile(S.t[j], tile0 + j, r.t[j]);
     };
 
-    // Segments: the run cut at chunk boundaries.  The NBUF register buffers
-    // rotate statically: a segment takes a multiple of NBUF steps (the last
-    // ones may be empty), and step s is loaded NBUF-1 steps before it is
-    // consumed.  Loads issued past the segment's last step already fetch the
-    // first steps of the next segment of the run (positions, not index
-    // lists, so not in indexed mode), through one load site so that both
-    // cases share the same registers.
+    // Segments of the run: the loads of a segment's positions go through
+    // LDS-staged index lists (IDX, at most kMaxIdxChunk positions) or page
+    // ids (PAGED, at most 512 pages), so those runs are cut into segments at
+    // lane-relative multiples of cs tiles; a plain run is one segment.  The
+    // running state carries across segments.  Local step s of this wave in
+    // a segment starting at tile s0 is the segment's step s*S + wi; the
+    // NBUF register buffers rotate statically, a segment takes a multiple of
+    // NBUF local steps (the last ones may be empty), and local step s is
+    // loaded NBUF-1 steps before it is consumed.
     constexpr int NBUF = StepT::NBUF;
     StepT buf[NBUF];
-    auto seg_end_of = [&](int s0) { return min(run_end, lane_t0 + ((s0 - lane_t0) / ct + 1) * ct); };
-    if constexpr (!IDX && !PAGED) {
-      const int t1 = seg_end_of(t);
-#pragma unroll
-      for (int j = 0; j + 1 < NBUF; ++j) load_step(buf[j], t + j * TPS, t1);
-    }
+    const int cs = IDX ? kMaxIdxChunk / kTile : PAGED ? 16 * p.page_tokens : 0x40000000;
+    auto seg_end_of = [&](int s0) {
+      return (int)min((int64_t)run_end, (int64_t)lane_t0 + ((int64_t)(s0 - lane_t0) / cs + 1) * cs);
+    };
+    auto tile_of = [&](int s0, int s) { return s0 + (s * S + wi) * TPS; };
     for (int seg_t0 = t; seg_t0 < run_end;) {
       const int seg_t1 = seg_end_of(seg_t0);
-      const int chunk = (seg_t0 - lane_t0) / ct;
-      const int chunk_t1 = min(lane_t1, lane_t0 + (chunk + 1) * ct);
       seg_pos0 = (seg_t0 - lane_t0) * kTile;
       seg_pos1 = min(npos, (seg_t1 - lane_t0) * kTile);
       if constexpr (IDX) {
         const int *src = p.token_idx + (int64_t)pair * p.idx_stride;
         __syncthreads();
-        for (int i = lane; i < seg_pos1 - seg_pos0; i += 64) s_idx[i] = min(max(src[seg_pos0 + i], 0), L - 1);
+        for (int i = tid; i < seg_pos1 - seg_pos0; i += NT) s_idx[i] = min(max(src[seg_pos0 + i], 0), L - 1);
         __syncthreads();
-#pragma unroll
-        for (int j = 0; j + 1 < NBUF; ++j) load_step(buf[j], seg_t0 + j * TPS, seg_t1);
       }
       if constexpr (PAGED) {
         // the page ids of this segment's positions (at most kMaxSegPages)
@@ -570,19 +665,17 @@ decode_mfma_kernel(DecodeParams p) {
         const int npg = (seg_pos1 - 1) / p.page_tokens - seg_page0 + 1;
         const int *tbl = p.block_table + (int64_t)b * p.table_stride + seg_page0;
         __syncthreads();
-        for (int i = lane; i < min(npg, kMaxSegPages); i += 64) s_pages[i] = max(tbl[i], 0);
+        for (int i = tid; i < min(npg, kMaxSegPages); i += NT) s_pages[i] = max(tbl[i], 0);
         __syncthreads();
-#pragma unroll
-        for (int j = 0; j + 1 < NBUF; ++j) load_step(buf[j], seg_t0 + j * TPS, seg_t1);
       }
+#pragma unroll
+      for (int j = 0; j + 1 < NBUF; ++j) load_step(buf[j], tile_of(seg_t0, j), seg_t1);
       const int nsteps = (seg_t1 - seg_t0 + TPS - 1) / TPS;
-      const int steps = (nsteps + NBUF - 1) / NBUF * NBUF;
-      const int next_t1 = seg_end_of(seg_t1);
+      const int wsteps = (nsteps + S - 1) / S;  // local steps of the busiest wave
+      const int steps = (wsteps + NBUF - 1) / NBUF * NBUF;
       auto issue = [&](StepT &S, int s) {
-        const bool in_seg = s < steps;
-        const int tn = in_seg ? seg_t0 + s * TPS : seg_t1 + (s - steps) * TPS;
-        const int lim = in_seg ? seg_t1 : (IDX || PAGED ? 0 : next_t1);
-        load_step(S, tn < lim ? tn : seg_t0, tn < lim ? lim : 0);
+        const int tn = tile_of(seg_t0, s);
+        load_step(S, tn < seg_t1 ? tn : seg_t0, tn < seg_t1 ? seg_t1 : 0);
       };
       if constexpr (StepT::PIPE) {
         // the raw scores of step s + 1 are started before step s's softmax
@@ -593,7 +686,7 @@ decode_mfma_kernel(DecodeParams p) {
           for (int j = 0; j < NBUF; ++j) {
             issue(buf[(j + NBUF - 1) % NBUF], i + j + NBUF - 1);
             const RawStep nxt = qk_step(buf[(j + 1) % NBUF]);
-            finish_step(buf[j], seg_t0 + (i + j) * TPS, pend);
+            finish_step(buf[j], tile_of(seg_t0, i + j), pend);
             pend = nxt;
           }
         }
@@ -602,49 +695,172 @@ decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
           for (int j = 0; j < NBUF; ++j) {
             issue(buf[(j + NBUF - 1) % NBUF], i + j + NBUF - 1);
-            finish_step(buf[j], seg_t0 + (i + j) * TPS, qk_step(buf[j]));
+            finish_step(buf[j], tile_of(seg_t0, i + j), qk_step(buf[j]));
           }
         }
-      }
-
-      // Partial of this segment, straight from registers, for each column
-      // block.  Lane (col, cg) holds channels NB*(4*cg + i) + nb =
-      // 4*NB*cg + NB*i + nb of its column.
-      const int half = (seg_t0 == lane_t0 + chunk * ct) ? 0 : 1;
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const float lsum = rows_sum(l_run[cb]);
-        if (qvalid[cb]) {
-          const int slot = slot_base + 16 * cb + (2 * chunk + half) * p.G;
-          const float out_scale = (KVT == ATTN_I8) ? p.v_scale : 1.0f;
-          const float inv = lsum > 0.f ? out_scale / lsum : 0.f;
-          float *op = p.wl.o_part + (int64_t)slot * D + 4 * NB * cg;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int n4 = 0; n4 < NB / 4; ++n4) {
-              const f32x4_t v = {O[cb][4 * n4][i] * inv, O[cb][4 * n4 + 1][i] * inv, O[cb][4 * n4 + 2][i] * inv,
-                                 O[cb][4 * n4 + 3][i] * inv};
-              *(f32x4_t *)(op + NB * i + 4 * n4) = v;
-            }
-          if (cg == 0) {
-            p.wl.m_part[slot] = lsum > 0.f ? m_run[cb] * kLn2 : NEG_INF;
-            p.wl.l_part[slot] = lsum;
-            if (half == 0 && seg_t1 == chunk_t1) {
-              p.wl.m_part[slot + p.G] = NEG_INF;
-              p.wl.l_part[slot + p.G] = 0.f;
-            }
-          }
-        }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) O[cb][nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-        m_run[cb] = NEG_INF;
-        l_run[cb] = 0.f;
       }
       seg_t0 = seg_t1;
     }
+
+    // The run's result for each column.  Lane (col, cg) holds channels
+    // NB*(4*cg + i) + nb = 4*NB*cg + NB*i + nb of its column, i.e. the 16-byte
+    // slices NB*(4*cg + i)/4 + n4.  The waves of a column group combine
+    // through LDS: M = max of their maxima, each wave's sum and output
+    // rescaled by exp2(m_w - M) and added in wave order.  A worker that holds
+    // the whole lane writes out and lse; otherwise the run's partial
+    // (m, l, o) goes to slot `slot` of the lane: entry slot*G + gc of the pair
+    // for column gc.
+    const float out_scale = (KVT == ATTN_I8) ? p.v_scale : 1.0f;
+    const bool direct = need == 1;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const float lsum = rows_sum(l_run[cb]);
+      if (cg == 0) {
+        s_cm[wv * kCols + 16 * cb + col] = m_run[cb];
+        s_cl[wv * kCols + 16 * cb + col] = lsum;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      float M = NEG_INF;
+#pragma unroll
+      for (int j = 0; j < WPG; ++j)
+        if (j < S) M = fmaxf(M, s_cm[(gi * S + j) * kCols + 16 * cb + col]);
+      const float alpha = m_run[cb] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(m_run[cb] - M);
+      f32x4_t *dst = s_co + (wv * kCols + 16 * cb + col) * NQ;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int n4 = 0; n4 < NB / 4; ++n4)
+          dst[(NB * (4 * cg + i)) / 4 + n4] =
+              (f32x4_t){O[cb][4 * n4][i], O[cb][4 * n4 + 1][i], O[cb][4 * n4 + 2][i], O[cb][4 * n4 + 3][i]} * alpha;
+    }
+    __syncthreads();
+    {
+      const int64_t pe0 = (int64_t)pair * p.max_slots * p.G;
+      const int pne = p.max_slots * p.G;
+      for (int u = tid; u < p.G * NQ; u += NT) {
+        const int gc = u / NQ, sl = u - gc * NQ;
+        const int gu = gc / kCols, c = gc - gu * kCols;  // column group and column within it
+        float M = NEG_INF;
+#pragma unroll
+        for (int j = 0; j < WPG; ++j)
+          if (j < S) M = fmaxf(M, s_cm[(gu * S + j) * kCols + c]);
+        float lt = 0.f;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < WPG; ++j) {
+          if (j < S) {
+            const int w = gu * S + j;
+            const float mw = s_cm[w * kCols + c];
+            lt += mw == NEG_INF ? 0.f : s_cl[w * kCols + c] * __builtin_amdgcn_exp2f(mw - M);
+            acc += s_co[(w * kCols + c) * NQ + sl];
+          }
+        }
+        const float inv = lt > 0.f ? out_scale / lt : 0.f;
+        const f32x4_t o = acc * inv;
+        if (direct) {
+          const int64_t orow = q_row_index(p, b, kh, gc);
+          store_out4(orow, sl, o);
+          if (sl == 0 && p.lse) p.lse[orow] = lt > 0.f ? M * kLn2 + logf(lt) : NEG_INF;
+        } else {
+          const uint32_t e = (uint32_t)(slot * p.G + gc);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), o_rsrc(pe0, pne),
+                                                 (e * D + 4 * sl) * 4, 0, kDeviceScope);
+          if (sl == 0) {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lt > 0.f ? M * kLn2 : NEG_INF), m_rsrc(pe0, pne),
+                                                  e * 4, 0, kDeviceScope);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lt), l_rsrc(pe0, pne), e * 4, 0, kDeviceScope);
+          }
+        }
+      }
+    }
+    __syncthreads();  // the combine buffers are free again
+    if (!direct) {
+      if (npend == 0) {
+        pend_q0 = q;
+        pend_need0 = need;
+      } else {
+        pend_q1 = q;
+        pend_need1 = need;
+      }
+      ++npend;
+    }
     t = run_end;
     if (t < t_end) hit = next_lane(p, hit);
+  }
+
+  // Merge inside the launch.  Only a worker's first and last runs can share
+  // their lane with other workers (every run between covers a whole lane).
+  // Once this worker's partial stores are complete it arrives on those
+  // lanes' counters; the arrival that completes a lane's count folds the
+  // lane's slots 0 .. need-1 in slot order (online log-sum-exp) into out
+  // and lse.
+  if (npend > 0) {
+    wait_vmem();
+    __syncthreads();
+    if (tid == 0) {
+      int last = 0;
+      const int a0 = lane_arrive(p.wl.ctr + pend_q0);
+      const int a1 = npend > 1 ? lane_arrive(p.wl.ctr + pend_q1) : 0;
+      if (a0 == pend_need0) {
+        lane_reset(p.wl.ctr + pend_q0);
+        last |= 1;
+      }
+      if (npend > 1 && a1 == pend_need1) {
+        lane_reset(p.wl.ctr + pend_q1);
+        last |= 2;
+      }
+      s_last = last;
+    }
+    __syncthreads();
+    const int last = s_last;
+    for (int i = 0; i < npend; ++i) {
+      if (!((last >> i) & 1)) continue;
+      const int pm = i == 0 ? pend_q0 : pend_q1, nm = i == 0 ? pend_need0 : pend_need1;
+      const int bm = pm / p.KH, khm = pm - bm * p.KH;
+      const int64_t pe0 = (int64_t)pm * p.max_slots * p.G;
+      const int pne = p.max_slots * p.G;
+      const __amdgpu_buffer_rsrc_t ors = o_rsrc(pe0, pne), mrs = m_rsrc(pe0, pne), lrs = l_rsrc(pe0, pne);
+      constexpr int U = 8;
+      for (int u = tid; u < p.G * NQ; u += NT) {
+        const int c = u / NQ, sl = u - c * NQ;
+        float mt = NEG_INF, lt = 0.f;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < nm; k0 += U) {
+          float mv[U], lv[U];
+          f32x4_t ov[U];
+#pragma unroll
+          for (int k = 0; k < U; ++k) {
+            const uint32_t e = (uint32_t)(min(k0 + k, nm - 1) * p.G + c);
+            const float l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lrs, e * 4, 0, kDeviceScope));
+            lv[k] = k0 + k < nm ? l : 0.f;
+            mv[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mrs, e * 4, 0, kDeviceScope));
+            ov[k] = __builtin_bit_cast(
+                f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ors, (e * D + 4 * sl) * 4, 0, kDeviceScope));
+          }
+#pragma unroll
+          for (int k = 0; k < U; ++k) {
+            if (lv[k] > 0.f) {  // an empty partial (l = 0) may hold any o
+              if (mv[k] > mt) {
+                const float sc = expf(mt - mv[k]);
+                acc *= sc;
+                lt *= sc;
+                mt = mv[k];
+              }
+              const float w = expf(mv[k] - mt) * lv[k];
+              acc += w * ov[k];
+              lt += w;
+            }
+          }
+        }
+        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+        const int64_t orow = q_row_index(p, bm, khm, c);
+        store_out4(orow, sl, acc * inv);
+        if (sl == 0 && p.lse) p.lse[orow] = lt > 0.f ? mt + logf(lt) : NEG_INF;
+      }
+    }
   }
 }
 
@@ -652,7 +868,7 @@ decode_mfma_kernel(DecodeParams p) {
 
 template <bool IDX, bool PAGED, int CB>
 static void launch_variant(const DecodeParams &p, int kv_dtype, dim3 g, hipStream_t s) {
-  dim3 blk(64);
+  dim3 blk(64 * kWPG);
   if (kv_dtype == ATTN_BF16) {
     if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_BF16, IDX, false, PAGED, CB>), g, blk, 0, s, p);
     else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_BF16, IDX, false, PAGED, CB>), g, blk, 0, s, p);
@@ -672,11 +888,13 @@ static void launch_cb(const DecodeParams &p, int kv_dtype, dim3 g, hipStream_t s
 }
 
 hipError_t launch_decode_mfma(const DecodeParams &p, int kv_dtype, hipStream_t s) {
+  if (p.wpg != kWPG) return hipErrorInvalidValue;
+  if (p.ngb < 1 || p.ngb > (p.cols_per_wave == 32 ? 2 : 1)) return hipErrorInvalidValue;
+  if (!p.wl.ctr || p.max_slots < 1) return hipErrorInvalidValue;
   if (p.token_idx) {
-    if (p.split > kMaxIdxChunk || p.block_table) return hipErrorInvalidValue;
+    if (p.block_table) return hipErrorInvalidValue;
     launch_cb<true, false>(p, kv_dtype, dim3(p.grid), s);
   } else if (p.block_table) {
-    if (p.split > 64 * p.page_tokens) return hipErrorInvalidValue;
     launch_cb<false, true>(p, kv_dtype, dim3(p.grid), s);
   } else {
     launch_cb<false, false>(p, kv_dtype, dim3(p.grid), s);

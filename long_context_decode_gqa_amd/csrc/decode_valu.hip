@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int q = hit.q;
     const int lane_t0 = hit.t0, lane_t1 = hit.t0 + hit.nt;
     const int run_end = min(t_end, lane_t1);
-    const int pair = q / p.ngb, gb = q - pair * p.ngb;
+    const int pair = q / p.lpp, gb = q - pair * p.lpp;
     const int b = pair / p.KH, kh = pair - b * p.KH;
     const int L = min(max(p.seq_lens[b], 0), p.max_seq_len);
     int npos = L;

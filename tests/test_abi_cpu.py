@@ -84,28 +84,26 @@ I8 = dict(kv_dtype=_lib.ATTN_I8, k_scale=FAKE, k_part_tokens=64, k_scale_stride=
 
 
 @pytest.mark.parametrize("over,split", [
-    # 128K tokens x 4 sequences x 8 KV heads = 131072 tiles of 32: 2048 bf16 workers of 64 tiles
-    (dict(g_B=4, g_max_seq_len=131072), 2048),
-    # int8: 1024 workers (one per SIMD) of 128 tiles
+    # bf16 and int8 KV: workers of four waves, each wave streaming at least 32 tiles of 32
+    # positions, so a worker's range is at least 4096 positions (the grid's size decides the rest)
+    (dict(g_B=4, g_max_seq_len=131072), 4096),
     (dict(g_B=4, g_max_seq_len=131072, **I8), 4096),
-    # 4 query rows per sequence (32 columns): 1024 workers
     (dict(g_B=4, g_max_seq_len=131072, q_rows=4), 4096),
-    # one KV head (a tensor-parallel share): 16384 tiles, 512 workers of at least 32 tiles
-    (dict(g_B=4, g_KH=1, g_max_seq_len=131072), 1024),
-    # small problems: at least 256 workers
-    (dict(g_B=1, g_KH=1, g_max_seq_len=4096), 32),
-    # paged int8 with 32-token pages: a chunk spans at most 64 pages
+    (dict(g_B=4, g_KH=1, g_max_seq_len=131072), 4096),
+    (dict(g_B=1, g_KH=1, g_max_seq_len=4096), 4096),
     (dict(g_B=4, g_max_seq_len=131072, g_seq_offset=None, g_block_table=FAKE, g_page_tokens=32,
-          g_table_stride=4096, g_page_stride=32 * 8 * 128, **I8), 2048),
-    # kept-token lists of 4096: chunks of 256 (bf16) or 128 (int8) kept tokens
+          g_table_stride=4096, g_page_stride=32 * 8 * 128, **I8), 4096),
+    # kept-token lists of 4096: at least 256 (bf16) or 128 (int8) kept tokens per worker
     (dict(g_B=4, g_max_seq_len=131072, token_idx=FAKE, n_idx=FAKE, idx_stride=4096), 256),
     (dict(g_B=4, g_max_seq_len=131072, token_idx=FAKE, n_idx=FAKE, idx_stride=4096, **I8), 128),
+    # fp32 KV (vector-ALU decode): chunks of 256
+    (dict(q_dtype=_lib.ATTN_F32, kv_dtype=_lib.ATTN_F32), 256),
     # a given split is kept
     (dict(split_tokens=96), 96),
 ])
 def test_default_split_tokens(over, split):
-    """The library's default chunk length, as attn_decode_split_tokens reports it (the device-size
-    independent part of the work split; workers = tiles / chunk tiles)."""
+    """The library's default split_tokens, as attn_decode_split_tokens reports it: the smallest
+    range of positions a decode worker takes (workers = min(grid, positions / split_tokens))."""
     st, n = _split(_args(**over))
     assert st == 0 and n == split, (over, n)
     assert _split(_args(G=0))[0] == _lib.ATTN_ERR_UNSUPPORTED
@@ -218,12 +216,12 @@ def test_paged_geometry_is_validated():
     for over, status in ((dict(g_page_tokens=48), _lib.ATTN_ERR_INVALID_ARG),
                          (dict(g_table_stride=63), _lib.ATTN_ERR_INVALID_ARG),
                          (dict(g_page_stride=0), _lib.ATTN_ERR_INVALID_ARG),
-                         (dict(g_page_tokens=32, split_tokens=4096), _lib.ATTN_ERR_UNSUPPORTED),
+                         (dict(g_page_tokens=32, split_tokens=1 << 20), _lib.ATTN_OK),
                          (dict(token_idx=FAKE, n_idx=FAKE, idx_stride=10), _lib.ATTN_ERR_UNSUPPORTED),
                          (dict(q_dtype=_lib.ATTN_F32, kv_dtype=_lib.ATTN_F32), _lib.ATTN_ERR_UNSUPPORTED)):
         a = _args(**{**paged, **over})
         if "g_page_tokens" in over and over["g_page_tokens"] == 32:
-            a.kv.table_stride = 128
+            a.kv.table_stride = 128  # 4096 tokens in 32-token pages
         assert _ws(a)[0] == status, over
     # the quantiser, the value norms and OAM selection read a paged cache too; their geometry
     # checks still run before any launch (a page stride of 4 bf16 elements is not 16-byte aligned)
@@ -243,3 +241,24 @@ def test_paged_geometry_is_validated():
     assert L.oam_score_topk_workspace_size(ctypes.byref(o), ctypes.byref(n)) == 0 and n.value > 0
     o.kv.page_stride = 64 * 1024 + 4
     assert L.oam_score_topk_workspace_size(ctypes.byref(o), ctypes.byref(n)) == _lib.ATTN_ERR_INVALID_ARG
+
+
+def test_long_paged_token_major_cache_is_accepted():
+    """A paged cache's buffer offsets span one page, not one sequence: a token-major pool
+    (KH=8, D=128 bf16, 2 KiB per token row) of 1.5M-token sequences is accepted by the decode and
+    OAM workspace queries, while the same length in one contiguous (sequence, head) is not."""
+    L = _lib.load()
+    n_tok = 3 << 19
+    pages = n_tok // 64
+    paged = dict(g_B=2, g_max_seq_len=n_tok, g_block_table=FAKE, g_page_tokens=64, g_table_stride=pages,
+                 g_page_stride=64 * 8 * 128, g_seq_offset=None, g_stride_h=128, g_stride_t=8 * 128)
+    assert _ws(_args(**paged))[0] == _lib.ATTN_OK
+    contiguous = dict(g_B=2, g_max_seq_len=n_tok, g_stride_h=128, g_stride_t=8 * 128)
+    assert _ws(_args(**contiguous))[0] == _lib.ATTN_ERR_UNSUPPORTED
+    g = _lib.AttnKvGeom(2, 8, 128, n_tok, FAKE, None, 128, 8 * 128)
+    g.block_table, g.page_tokens, g.table_stride, g.page_stride = FAKE, 64, pages, 64 * 8 * 128
+    o = _lib.OamTopkArgs()
+    o.kv, o.G, o.q, o.k, o.kv_dtype, o.vlog, o.vlog_stride = g, 8, FAKE, FAKE, _lib.ATTN_BF16, FAKE, n_tok
+    o.top_k, o.idx_out, o.n_kept, o.beta, o.eps = 4096, FAKE, FAKE, 1.0, 1e-6
+    n = ctypes.c_size_t(0)
+    assert L.oam_score_topk_workspace_size(ctypes.byref(o), ctypes.byref(n)) == _lib.ATTN_OK
