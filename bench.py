@@ -2,14 +2,17 @@
 """Decode-attention benchmark on one MI355X.
 
 Headline: bf16 GQA decode at 128K KV (B=4 sequences, 8 KV heads, G=8 query
-heads per KV head, head dim 128, 131072 tokens each, split-KV chunks of the
-library's default size merged by log-sum-exp).  One step = one
-attn_decode_splitkv call (decode kernel + merge) over inputs already resident
-in HBM.  Prints one JSON line: KV GB/s (value), us/step, fraction of HBM peak,
-the roofline of the decode kernel, the CPU oracle baseline and, unless
---headline-only, the other workloads (32K GQA, ragged batch, INT8 KV and its
-scheme table, a paged cache, multi-row speculative steps, OAM token dropping
-on bf16 and INT8 caches, and block-granular selection).
+heads per KV head, head dim 128, 131072 tokens each, split-KV over the
+library's default work split, partials merged by log-sum-exp inside the same
+launch).  One step = one attn_decode_splitkv call over inputs already resident
+in HBM.  Prints one JSON line: KV GB/s (value), us/step (mean of back-to-back
+steps, and the median and minimum of single steps timed one by one), fraction
+of HBM peak and of a measured read-only HBM probe, the roofline of the decode
+kernel, the CPU oracle baseline and, unless --headline-only, the other
+workloads (32K GQA, ragged batch with the balanced and the unbalanced
+schedules, INT8 KV and its scheme table, a paged cache, multi-row speculative
+steps, OAM token dropping on bf16 and INT8 caches, and block-granular
+selection).
 """
 from __future__ import annotations
 
@@ -62,11 +65,16 @@ def partial_bytes(n_partials: int, D: int) -> int:
 # ------------------------------------------------------------------ helpers
 
 def host_threads() -> int:
+    """Host cores this job may use: the cores it may run on, capped by the CPU share the machine
+    grants it (OMP_NUM_THREADS where set); the CPU baseline uses every one of them."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
         n = os.cpu_count() or 1
-    return max(1, min(16, n))
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    if share.isdigit() and int(share) > 0:
+        n = min(n, int(share))
+    return max(1, n)
 
 
 def sources_sha256(paths) -> str:
@@ -136,12 +144,11 @@ def dev_geom(pkg, torch, g, dev):
 
 
 def time_decode(torch, prepared, steps, warmup):
-    """Returns (ms per step, mean decode-kernel ms, mean merge ms).
-
-    The step time comes from `steps` plain calls between two events; the
-    per-kernel times from a second run of `steps` calls through the profiled
-    entry point, whose events sit between the kernels (and add their own small
-    cost, so they are kept out of the step time)."""
+    """Returns a dict of ms: `step` = mean of `steps` plain calls back to back between two events;
+    `decode` / `merge` = mean duration of the decode and merge launches, from a second run of
+    `steps` calls through the profiled entry point, whose events sit on the calls' stream around
+    each launch (bf16/int8 KV: the merge runs inside the decode launch, so `merge` is ~0 and
+    `decode` is the whole step); `median` / `min` = of those per-call decode+merge durations."""
     for _ in range(warmup):
         prepared()
     t = Timer(torch, steps)
@@ -155,14 +162,24 @@ def time_decode(torch, prepared, steps, warmup):
     for i in range(steps):
         prepared.profiled(t.phase[i])
     torch.cuda.synchronize()
-    dk = sum(e[0].elapsed_time(e[1]) for e in t.phase) / steps
-    mg = sum(e[1].elapsed_time(e[2]) for e in t.phase) / steps
-    return total / steps, dk, mg
+    dk = [e[0].elapsed_time(e[1]) for e in t.phase]
+    mg = [e[1].elapsed_time(e[2]) for e in t.phase]
+    per = sorted(a + b for a, b in zip(dk, mg))
+    return {"step": total / steps, "decode": sum(dk) / steps, "merge": sum(mg) / steps,
+            "median": per[len(per) // 2], "min": per[0]}
 
 
 # ------------------------------------------------------------------ workloads
 
-def bench_dense(pkg, torch, synth, name, steps, warmup, dev, **over):
+def grid_slots(pkg, w) -> int:
+    """Decode workers the balanced split runs for a bf16 workload of this shape on this GPU (four-wave
+    workers, eight waves per compute unit)."""
+    import torch
+    n = torch.cuda.get_device_properties(0).multi_processor_count
+    return n * 8 // 4
+
+
+def bench_dense(pkg, torch, synth, name, steps, warmup, dev, unbalanced=False, **over):
     w = synth.workload(name, **over)
     q, k, v, g = synth.generate(w, nthreads=host_threads())
     qd = to_dev(torch, q.reshape(-1), dev).view(w.B, w.QH, w.D)
@@ -170,22 +187,41 @@ def bench_dense(pkg, torch, synth, name, steps, warmup, dev, **over):
     del k, v
     geom = dev_geom(pkg, torch, g, dev)
     p = pkg.prepare_decode(qd, kd, vd, geom, w.G, split_tokens=w.split_tokens)
-    ms, dk, mg = time_decode(torch, p, steps, warmup)
+    t = time_decode(torch, p, steps, warmup)
     tokens = w.kv_tokens()
     kvb = kv_bytes(tokens, w.KH, w.D, 2)
-    split = p.split_tokens
-    nparts = w.QH * sum(-(-int(L) // split) for L in w.lens)
-    algo = kvb + w.B * w.QH * w.D * 2 + partial_bytes(nparts, w.D)
-    return dict(w=w, q=q, g=g, ms=ms, decode_ms=dk, merge_ms=mg, kv_bytes=kvb,
-                decode_algo_bytes=algo, tokens=tokens, split=split)
+    # the bytes the step must move: K/V once, Q in and out (bf16 Q, fp32 out)
+    algo = kvb + w.B * w.QH * w.D * (2 + 4)
+    res = dict(w=w, q=q, g=g, t=t, ms=t["step"], decode_ms=t["decode"], merge_ms=t["merge"], kv_bytes=kvb,
+               decode_algo_bytes=algo, tokens=tokens, split=p.split_tokens)
+    if unbalanced:
+        # The unbalanced schedules on the same inputs, every (b, kh) in the same number of equal
+        # splits whatever its length: one worker per (b, kh); as many splits as fill the grid once;
+        # and as many as cut the longest sequence into pieces of the balanced range (flash-decoding
+        # style, the split count chosen for the longest sequence).
+        lanes = w.B * w.KH
+        W = grid_slots(pkg, w)
+        tiles = [-(-int(L) // 32) for L in w.lens]
+        T = w.KH * sum(tiles)
+        fill = max(1, -(-W // lanes))
+        longest = max(1, -(-max(tiles) * W // T))
+        for tag, S in (("per_sequence", 1), (f"fixed_{fill}_splits", fill), (f"fixed_{longest}_splits", longest)):
+            pu = pkg.prepare_decode(qd, kd, vd, geom, w.G, fixed_splits=S)
+            res.setdefault("unbalanced", {})[tag] = time_decode(torch, pu, max(3, steps // 2), 2)
+            res["unbalanced"][tag]["splits_per_sequence"] = S
+            del pu
+    return res
 
 
-def summary(r, extra=None):
+def summary(r, extra=None, probe_gbs=None):
     d = {"us_per_step": round(r["ms"] * 1e3, 2), "kv_gbs": round(r["kv_bytes"] / r["ms"] / 1e6, 1),
          "frac_of_peak": round(r["kv_bytes"] / r["ms"] / 1e6 / HBM_PEAK_GBS, 4),
+         "us_per_step_median": round(r["t"]["median"] * 1e3, 2), "us_per_step_min": round(r["t"]["min"] * 1e3, 2),
          "decode_kernel_us": round(r["decode_ms"] * 1e3, 2), "merge_us": round(r["merge_ms"] * 1e3, 2),
          "kernel_kv_gbs": round(r["kv_bytes"] / r["decode_ms"] / 1e6, 1),
          "kernel_frac_of_peak": round(r["kv_bytes"] / r["decode_ms"] / 1e6 / HBM_PEAK_GBS, 4)}
+    if probe_gbs:
+        d["frac_of_probe"] = round(r["kv_bytes"] / r["ms"] / 1e6 / probe_gbs, 4)
     if "split" in r:
         d["split_tokens"] = r["split"]
     if extra:
@@ -237,20 +273,22 @@ def bench_int8(pkg, torch, synth, steps, warmup, dev):
     # the quantisation passes just wrote 1.5 GiB and the host then idled on the scale read: the
     # first few dozen steps after that run 4-6 us slow (the same configuration timed again later,
     # as the scheme "bf16_query_k64", does not), so the untimed warm-up is 50 steps (about 10 ms)
-    ms, dk, mg = time_decode(torch, p, steps, max(2 * warmup, 50))
+    t = time_decode(torch, p, steps, max(2 * warmup, 50))
     kvb = kv_bytes(tokens, w.KH, w.D, 1) + k_codes[64][1].numel() * 4 + 4
     schemes = {}
     for name, part, qq in (("A_k64", 64, pkg.QUANT_ROW), ("A_k128", 128, pkg.QUANT_ROW),
                            ("B", 0, pkg.QUANT_ROW), ("baseline", 0, pkg.QUANT_STATIC),
                            ("bf16_query_k64", 64, pkg.QUANT_EXACT)):
         ps = prep(part, qq)
-        ms_s, dk_s, mg_s = time_decode(torch, ps, steps, warmup)
+        ts = time_decode(torch, ps, steps, warmup)
+        ms_s, dk_s = ts["step"], ts["decode"]
         err = float(torch.linalg.norm(ps.out - ref_out) / torch.linalg.norm(ref_out))
         b = kv_bytes(tokens, w.KH, w.D, 1) + k_codes[part][1].numel() * 4 + 4
         schemes[name] = {"us_per_step": round(ms_s * 1e3, 2), "decode_kernel_us": round(dk_s * 1e3, 2),
                          "kv_gbs": round(b / ms_s / 1e6, 1), "rel_err_vs_bf16": round(err, 5)}
         del ps
-    return dict(ms=ms, decode_ms=dk, merge_ms=mg, kv_bytes=kvb, split=p.split_tokens, schemes=schemes,
+    return dict(t=t, ms=t["step"], decode_ms=t["decode"], merge_ms=t["merge"], kv_bytes=kvb, split=p.split_tokens,
+                schemes=schemes,
                 quant=quant)
 
 
@@ -284,8 +322,8 @@ def bench_paged(pkg, torch, synth, steps, warmup, dev, page_tokens=64, layout="h
                           block_table=table, page_tokens=P, page_stride=P * KH * D)
     qd = to_dev(torch, q.reshape(-1), dev).view(w.B, w.QH, w.D)
     p = pkg.prepare_decode(qd, kp, vp, geom, w.G, split_tokens=w.split_tokens)
-    ms, dk, mg = time_decode(torch, p, steps, warmup)
-    res = dict(ms=ms, decode_ms=dk, merge_ms=mg, kv_bytes=kv_bytes(w.kv_tokens(), KH, D, 2),
+    t = time_decode(torch, p, steps, warmup)
+    res = dict(t=t, ms=t["step"], decode_ms=t["decode"], merge_ms=t["merge"], kv_bytes=kv_bytes(w.kv_tokens(), KH, D, 2),
                split=p.split_tokens)
     if layout == "head_major":
         # OAM selection (top 4096 of the 128K tokens) over the same pool, value term cached
@@ -335,8 +373,8 @@ def bench_multirow(pkg, torch, synth, steps, warmup, dev, R):
     q = synth.fill_q(151, w.B, R * w.QH, w.D, synth.BF16)
     qd = to_dev(torch, q.reshape(-1), dev).view(w.B, R, w.QH, w.D)
     p = pkg.prepare_decode(qd, kd, vd, geom, w.G, split_tokens=w.split_tokens, q_rows=R)
-    ms, dk, mg = time_decode(torch, p, steps, warmup)
-    return dict(ms=ms, decode_ms=dk, merge_ms=mg, kv_bytes=kv_bytes(w.kv_tokens(), w.KH, w.D, 2),
+    t = time_decode(torch, p, steps, warmup)
+    return dict(t=t, ms=t["step"], decode_ms=t["decode"], merge_ms=t["merge"], kv_bytes=kv_bytes(w.kv_tokens(), w.KH, w.D, 2),
                 split=p.split_tokens)
 
 
@@ -442,6 +480,30 @@ def bench_oam(pkg, torch, synth, steps, warmup, dev):
     return res
 
 
+def hbm_read_probe(pkg, torch, dev, nbytes=4 << 30, reps=20):
+    """The library's read-only sweep (attn_util_read: 16-byte loads, one checksum word per
+    workgroup) over nbytes of HBM, timed with events around each launch on the current stream: the
+    achievable read bandwidth next to the 8 TB/s vendor figure."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+    src.fill_(1.0)
+    sink = torch.empty(4096, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        pkg.util_read(src, sink)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        pkg.util_read(src, sink)
+        b.record()
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    del src, sink
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "launches": reps, "us_median": round(per[len(per) // 2] * 1e3, 2),
+            "gbs_median": round(nbytes / per[len(per) // 2] / 1e6, 1), "gbs_max": round(nbytes / per[0] / 1e6, 1),
+            "kernel": "read_kernel (attn_util_read)"}
+
+
 def cpu_baseline(r, budget_s=10.0):
     """The fp64 oracle on host threads over whole (b, kh) pairs of the headline workload."""
     import numpy as np
@@ -455,6 +517,11 @@ def cpu_baseline(r, budget_s=10.0):
                        k, v, 1.0 / math.sqrt(w.D))
     n = host_threads()
     pairs = [(b, kh) for b in range(w.B) for kh in range(w.KH)]
+    cpu_count = os.cpu_count()
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = cpu_count
     per_batch = max(1, n // w.G)
     done = 0
     t0 = time.perf_counter()
@@ -467,7 +534,9 @@ def cpu_baseline(r, budget_s=10.0):
         done += len(batch)
     dt = time.perf_counter() - t0
     bytes_done = kv_bytes(int(w.lens[0]) * done, 1, w.D, 2)
-    return {"value": round(bytes_done / dt / 1e9, 3), "unit": "GB/s", "cores": n, "kind": "oracle",
+    return {"value": round(bytes_done / dt / 1e9, 3), "unit": "GB/s", "cores": n, "os_cpu_count": cpu_count,
+            "affinity_cores": affinity, "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "kind": "oracle",
             "seconds": round(dt, 2), "us_per_step_equiv": round(dt / done * len(pairs) * 1e6, 1),
             "sample": f"{done} (sequence, KV head) pair passes ({done / len(pairs):.1f} sweeps of the "
                       f"{len(pairs)} pairs) of the 128K bf16 workload, all {w.G} query heads each, fp64 oracle "
@@ -513,22 +582,29 @@ def main():
         print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": W + K}), flush=True)
         return
 
+    probe = hbm_read_probe(pkg, torch, dev)
+    pg = probe["gbs_median"]
     head = bench_dense(pkg, torch, synth, "dense128k", K, W, dev)
     w = head["w"]
     ms = head["ms"]
     value = head["kv_bytes"] / ms / 1e6          # GB/s (1e9 bytes per second)
+    # the decode kernel is the whole step (the merge runs inside it): its launch duration from the
+    # events around each launch on the calls' stream
     dk_s = head["decode_ms"] / 1e3
     achieved = head["decode_algo_bytes"] / dk_s / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_pmc_traffic(),
-                "kernel": "decode_mfma_kernel<128, bf16>",
+                "kernel": "decode_mfma_kernel<128, bf16> (decode and merge, one launch)",
                 "algorithmic_bytes_per_launch": head["decode_algo_bytes"],
-                "avg_launch_us": round(head["decode_ms"] * 1e3, 2)}
+                "avg_launch_us": round(head["decode_ms"] * 1e3, 2),
+                "frac_of_probe": round(achieved / pg, 4)}
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms, 4), "us_per_step": round(ms * 1e3, 2), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "us_per_step_median": round(head["t"]["median"] * 1e3, 2), "us_per_step_min": round(head["t"]["min"] * 1e3, 2),
+        "frac_of_probe": round(value / pg, 4), "hbm_read_probe": probe,
         "config": {"workload": "gqa_decode_bf16_128k", "batch": w.B, "kv_heads": w.KH, "group_size": w.G,
                    "head_dim": w.D, "kv_len": int(w.lens[0]), "split_tokens": head["split"],
                    "split_chosen_by": "library" if w.split_tokens == 0 else "caller",
@@ -536,7 +612,7 @@ def main():
                    "eq6_bytes_per_step": decode_eq_elements(w.B, w.KH, w.G, w.D, int(w.lens[0])) * 2,
                    "flops_per_step": decode_eq_flops(w.B, w.QH, int(w.lens[0]), w.D)},
         "phases_us": {"decode": round(head["decode_ms"] * 1e3, 2),
-                      "merge": round(head["merge_ms"] * 1e3, 2)},
+                      "merge": round(head["merge_ms"] * 1e3, 2), "launches_per_step": 1},
         "roofline": roofline,
     }
     if not args.headline_only:
@@ -544,7 +620,7 @@ def main():
         todo = set(x.strip() for x in args.others.split(",") if x.strip())
         if "gqa32k" in todo:
             r = bench_dense(pkg, torch, synth, "gqa32k", max(5, K // 2), W, dev)
-            others["gqa32k_bf16"] = summary(r)
+            others["gqa32k_bf16"] = summary(r, probe_gbs=pg)
             del r
         if "tiny" in todo:
             others["tiny_fp32"] = bench_tiny(pkg, torch, synth, K, W, dev)
@@ -553,18 +629,23 @@ def main():
             # the same per-head work at 1/8 of the bytes, where fixed costs weigh more
             for name in ("gqa32k", "dense128k"):
                 r = bench_dense(pkg, torch, synth, name, max(5, K // 2), W, dev, KH=1, split_tokens=0)
-                others[f"{name}_tp8_share_kh1"] = summary(r, {"kv_heads": 1, "batch": int(r["w"].B)})
+                others[f"{name}_tp8_share_kh1"] = summary(r, {"kv_heads": 1, "batch": int(r["w"].B)}, probe_gbs=pg)
                 del r
         if "ragged" in todo:
-            r = bench_dense(pkg, torch, synth, "ragged", max(5, K // 2), W, dev)
+            r = bench_dense(pkg, torch, synth, "ragged", max(5, K // 2), W, dev, unbalanced=True)
+            unb = {tag: {"us_per_step": round(t["step"] * 1e3, 2), "us_per_step_median": round(t["median"] * 1e3, 2),
+                         "splits_per_sequence": t["splits_per_sequence"],
+                         "balanced_speedup": round(t["step"] / r["ms"], 3)}
+                   for tag, t in r["unbalanced"].items()}
             others["ragged_bf16"] = summary(r, {"total_kv_tokens_per_head": r["tokens"],
                                                  "lens_min": int(r["w"].lens.min()),
-                                                 "lens_max": int(r["w"].lens.max())})
+                                                 "lens_max": int(r["w"].lens.max()),
+                                                 "unbalanced_schedules": unb}, probe_gbs=pg)
             del r
         if "int8" in todo:
             try:
                 r = bench_int8(pkg, torch, synth, K, W, dev)
-                others["int8_128k"] = summary(r)
+                others["int8_128k"] = summary(r, probe_gbs=pg)
                 others["int8_128k_schemes"] = r["schemes"]
                 others["int8_128k_quantisation"] = r["quant"]
             except pkg.AttnError as e:

@@ -171,10 +171,23 @@ typedef struct {
  *               bf16/int8 KV, one arrival counter per (b, kh).  It needs no
  *               initialisation: every call leaves its counters at zero
  *               arrivals and takes over a counter word that holds anything
- *               else (a fixed 40-bit tag marks the library's words)
+ *               else.  A fixed 40-bit tag marks the library's counter words,
+ *               so the one content it cannot tell from a live counter is its
+ *               own tag with a nonzero count, left by a call on the same
+ *               workspace that was cut off mid-launch or overlapped by
+ *               another call (other data matches the tag with probability
+ *               2^-40 per word); filling the workspace with zeros restores it
  *   out         [B][KH*G][D] in out_dtype (ATTN_F32 or ATTN_BF16)
  *   lse         optional fp32 [B][KH*G]: natural-log log-sum-exp of the
  *               scaled scores (-inf for a sequence with no tokens)
+ *   fixed_splits  0: the balanced split above (the default).  S >= 1 (bf16
+ *               or int8 KV): the unbalanced schedule it replaces, kept for
+ *               comparison: every (b, kh) is cut into S equal splits, one
+ *               worker each, whatever its length, so with mixed lengths
+ *               most workers idle while the longest sequence's finish
+ *               ("优化稀疏注意力中的令牌丢弃机制" §5: 128K next to 512 tokens is
+ *               250x the work).  S = 1 is one worker per (b, kh); split_tokens
+ *               is then ignored
  * A sequence (or kept set) with no tokens gives out = 0.
  */
 typedef struct {
@@ -199,6 +212,7 @@ typedef struct {
   size_t workspace_bytes;
   void *out;
   float *lse;
+  int32_t fixed_splits;
 } attn_decode_args;
 
 /* Host-only: bytes of workspace attn_decode_splitkv needs for these args
@@ -291,7 +305,8 @@ attn_status kv_quant_int8(const attn_kv_geom *geom, const void *x_bf16, int32_t 
 
 /*
  * ln(||v_t||_2 + eps) of every V row, the value term of the OAM score
- * ("优化稀疏注意力中的令牌丢弃机制" §3: torch.log(v_i.norm() + eps)).  A row never
+ * ("优化稀疏注意力中的令牌丢弃机制" §3: the natural log of the value's L2 norm
+ * plus eps).  A row never
  * changes once appended, so this can be computed at append time and passed
  * to oam_score_topk.  vlog[(b*KH + kh)*vlog_stride + t] for t < L_b
  * (vlog_stride >= max_seq_len).  v_dtype is ATTN_BF16, or ATTN_I8 for an

@@ -9,7 +9,6 @@ import of the binding's entry points raises (there is no CPU fallback).
 from __future__ import annotations
 
 import ctypes
-import math
 from dataclasses import dataclass
 from typing import Optional
 
@@ -91,7 +90,7 @@ class KVGeometry:
 
 def _decode_args(q, k, v, geom: KVGeometry, G, out, lse, k_scale, k_part_tokens, k_scale_stride, v_scale,
                  token_idx, n_idx, idx_stride, softmax_scale, split_tokens, workspace, q_quant=0, q_scale=0.0,
-                 q_rows=1):
+                 q_rows=1, fixed_splits=0):
     a = _lib.AttnDecodeArgs()
     a.kv = geom.c()
     a.G = G
@@ -109,6 +108,7 @@ def _decode_args(q, k, v, geom: KVGeometry, G, out, lse, k_scale, k_part_tokens,
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     a.out, a.lse = _ptr(out), _ptr(lse)
+    a.fixed_splits = fixed_splits
     return a
 
 
@@ -154,14 +154,15 @@ def prepare_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, geom: KVGe
                    k_part_tokens: int = 64, k_scale_stride: Optional[int] = None, v_scale: float = 1.0,
                    token_idx: Optional[torch.Tensor] = None, n_idx: Optional[torch.Tensor] = None,
                    idx_stride: Optional[int] = None, softmax_scale: float = 0.0, split_tokens: int = 0,
-                   q_quant: int = 0, q_scale: float = 0.0, q_rows: int = 1,
+                   q_quant: int = 0, q_scale: float = 0.0, q_rows: int = 1, fixed_splits: int = 0,
                    workspace: Optional[torch.Tensor] = None) -> PreparedDecode:
     """Build (and allocate outputs/workspace for) one ``attn_decode_splitkv`` call.
 
     With int8 KV, ``k_part_tokens=0`` selects one per-tensor K scale (``k_scale[0]``) and
     ``q_quant`` (QUANT_EXACT / QUANT_ROW / QUANT_STATIC, with ``q_scale``) how the query is
     quantised.  ``q_rows`` > 1 is a multi-row (speculative) step: q, out and lse are
-    [B, q_rows, KH*G, ...] and row r attends to the first L - (q_rows - 1) + r tokens."""
+    [B, q_rows, KH*G, ...] and row r attends to the first L - (q_rows - 1) + r tokens.
+    ``fixed_splits`` > 0 selects the unbalanced schedule (every (b, kh) in that many splits)."""
     dev = q.device
     QH = geom.KH * G
     if out is None:
@@ -173,7 +174,7 @@ def prepare_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, geom: KVGe
     if token_idx is not None and idx_stride is None:
         idx_stride = token_idx.shape[-1]
     a = _decode_args(q, k, v, geom, G, out, lse, k_scale, k_part_tokens, k_scale_stride, v_scale, token_idx, n_idx,
-                     idx_stride or 0, softmax_scale, split_tokens, None, q_quant, q_scale, q_rows)
+                     idx_stride or 0, softmax_scale, split_tokens, None, q_quant, q_scale, q_rows, fixed_splits)
     need = decode_workspace_size(a)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
@@ -326,7 +327,3 @@ def util_copy(dst: torch.Tensor, src: torch.Tensor, nbytes: Optional[int] = None
 def util_read(src: torch.Tensor, sink: torch.Tensor, nbytes: Optional[int] = None, stream=None):
     n = src.numel() * src.element_size() if nbytes is None else nbytes
     _lib.check(_lib.load().attn_util_read(_ptr(src), n, _ptr(sink), _stream(stream)), "attn_util_read")
-
-
-def default_softmax_scale(D: int) -> float:
-    return 1.0 / math.sqrt(D)

@@ -24,7 +24,8 @@ class AttnDecodeArgs(ctypes.Structure):
     _fields_ = [("kv", AttnKvGeom), ("G", i32), ("q_rows", i32), ("q_dtype", i32), ("kv_dtype", i32), ("out_dtype", i32),
                 ("q", vp), ("k", vp), ("v", vp), ("k_scale", vp), ("k_part_tokens", i32), ("k_scale_stride", i32),
                 ("v_scale", f32), ("q_quant", i32), ("q_scale", f32), ("token_idx", vp), ("n_idx", vp), ("idx_stride", i32), ("softmax_scale", f32),
-                ("split_tokens", i32), ("workspace", vp), ("workspace_bytes", sz), ("out", vp), ("lse", vp)]
+                ("split_tokens", i32), ("workspace", vp), ("workspace_bytes", sz), ("out", vp), ("lse", vp),
+                ("fixed_splits", i32)]
 
 
 class OamTopkArgs(ctypes.Structure):

@@ -111,6 +111,10 @@ attn_status plan_decode(const attn_decode_args *a, DecodeLayout *L) {
   if (!(fabsf(a->softmax_scale) < INFINITY)) return fail(ATTN_ERR_INVALID_ARG, "softmax_scale must be finite");
   if (a->split_tokens < 0 || (a->split_tokens && (a->split_tokens % 32 || a->split_tokens > (1 << 20))))
     return fail(ATTN_ERR_INVALID_ARG, "split_tokens must be 0 or a positive multiple of 32 (<= 2^20)");
+  if (a->fixed_splits < 0 || a->fixed_splits > 65536)
+    return fail(ATTN_ERR_INVALID_ARG, "fixed_splits must be in [0, 65536]");
+  if (a->fixed_splits > 0 && a->kv_dtype == ATTN_F32)
+    return fail(ATTN_ERR_UNSUPPORTED, "fixed_splits needs bf16 or int8 KV");
   if (a->token_idx && (!a->n_idx || a->idx_stride < 0))
     return fail(ATTN_ERR_INVALID_ARG, "token_idx needs n_idx and idx_stride >= 0");
   if (a->q_quant != ATTN_QUANT_EXACT && a->q_quant != ATTN_QUANT_ROW && a->q_quant != ATTN_QUANT_STATIC)
@@ -182,12 +186,20 @@ attn_status plan_decode(const attn_decode_args *a, DecodeLayout *L) {
   // are the first ones dispatched.
   const int64_t ct = L->split / 32;
   L->grid = (int32_t)std::max<int64_t>(1, std::min<int64_t>(grid_cap, (max_tiles + ct - 1) / ct));
+  if (a->fixed_splits > 0) {
+    // the unbalanced schedule: one worker per split of every lane
+    if (L->lanes * a->fixed_splits >= (int64_t(1) << 31))
+      return fail(ATTN_ERR_UNSUPPORTED, "fixed_splits: too many workers");
+    L->grid = (int32_t)(L->lanes * a->fixed_splits);
+  }
   const int64_t QH = (int64_t)g.KH * a->G * R;
   if (mfma) {
-    // A lane's workers: its tiles over ranges of at least ct tiles touch at
-    // most ceil(tiles / ct) + 1 ranges, and there are at most grid workers.
+    // A lane's workers: every worker's range is at least ct tiles (the
+    // kernel's worker count ensures it), so a lane touches at most
+    // ceil(tiles / ct) + 1 ranges, and there are at most grid workers.
     L->max_chunks = 0;
-    L->max_slots = std::min<int64_t>(L->grid, (lane_tiles_max + ct - 1) / ct + 1);
+    L->max_slots = a->fixed_splits > 0 ? a->fixed_splits
+                                       : std::min<int64_t>(L->grid, (lane_tiles_max + ct - 1) / ct + 1);
     L->max_partials = (int64_t)g.B * QH * L->max_slots;
   } else {
     L->max_chunks = ((int64_t)L->max_tokens + L->split - 1) / L->split;
@@ -297,6 +309,7 @@ static attn_status decode_impl(const attn_decode_args *a, attn_stream_t stream, 
   p.max_chunks = (int32_t)L.max_chunks;
   p.max_slots = (int32_t)L.max_slots;
   p.wpg = L.wpg;
+  p.fixed_splits = a->fixed_splits;
   p.grid = L.grid;
   p.wl.m_part = reinterpret_cast<float *>(ws + L.m);
   p.wl.l_part = reinterpret_cast<float *>(ws + L.l);

@@ -91,11 +91,11 @@ struct WorkList {
   float *m_part;             // [max partials] natural-log max
   float *l_part;             // [max partials]
   float *o_part;             // [max partials][D]
-  // Merge inside the matrix-core decode launch: one arrival counter per lane.  A counter
-  // word holds (kCtrTag << 24) | arrivals.  Every call leaves its counters at
-  // zero arrivals, and a word without the tag (a workspace that has held
-  // something else) is taken over by the first arrival, so the workspace
-  // needs no clearing.
+  // Merge inside the matrix-core decode launch: one arrival counter per lane.
+  // A counter word holds (kCtrTag << 24) | arrivals.  Every call leaves its counters at zero
+  // arrivals, and a word without the tag (a workspace that has held something
+  // else) is taken over by the first arrival, so the workspace needs no
+  // clearing.
   uint64_t *ctr;             // [lanes] (matrix-core decode)
 };
 
@@ -128,6 +128,7 @@ struct DecodeParams {
   int32_t max_slots;    // partial slots per pair (matrix-core decode)
   int32_t grid;         // workgroups launched for the decode kernel
   int32_t wpg;          // waves per decode workgroup (the MFMA kernel's workers)
+  int32_t fixed_splits; // matrix-core decode: 0 = balanced split; S > 0 = each lane in S splits, one worker each
   WorkList wl;
   // outputs, written by the matrix-core decode launch
   int32_t out_dtype;
@@ -223,25 +224,76 @@ __device__ __forceinline__ int workers_for(const DecodeParams &p, int total_tile
   return total_tiles == 0 ? 0 : min(p.grid, max(1, total_tiles / (p.split / 32)));
 }
 
-// The worker whose range [w*T/W, (w+1)*T/W) holds tile t (0 <= t < T): the
-// largest w with floor(w*T/W) <= t.
-__device__ __forceinline__ int worker_of(int t, int T, int W) {
-  return (int)(((int64_t)(t + 1) * W - 1) / T);
+// Static split of the matrix-core decode's tile stream into one contiguous
+// range per worker.  When the work fills the whole grid (every compute unit
+// runs its full complement of workers) the split is XCD-aware: workgroup w
+// runs on XCD w % 8 (workgroups are dealt to the eight XCDs in turn), and
+// under that full load the odd-numbered XCDs stream about 6% slower than
+// the even ones (measured per worker on several MI355X boxes, with the
+// ranges rotated by one worker to show it follows the XCD, not the memory
+// range), so a worker on an odd XCD gets weight 15 and one on an even XCD
+// 16: worker w's range is [start(w), start(w+1)), start(w) = floor(T * S(w)
+// / S(W)), S(w) = the sum of the weights of workers 0 .. w-1.  With fewer
+// workers the XCDs do not contend and the split is equal, start(w) =
+// floor(w * T / W).  Every range is at least ct = split / 32 tiles: the
+// weighted split runs W = grid <= 15 T / (16 ct) workers, and start(w+1) -
+// start(w) >= floor(15 T / (16 W)) >= ct; the equal one at most T / ct.  So
+// no range is empty, and a lane of n tiles touches at most ceil(n / ct) + 1.
+struct StreamSplit {
+  int W;          // workers
+  bool weighted;  // XCD-weighted (else equal)
+};
+__device__ __forceinline__ int64_t xcd_weight_sum(int w) {
+  const int r = w & 7;
+  return (int64_t)(w >> 3) * (4 * 16 + 4 * 15) + (int64_t)((r + 1) / 2) * 16 + (int64_t)(r / 2) * 15;
+}
+__device__ __forceinline__ StreamSplit stream_split(const DecodeParams &p, int T) {
+  StreamSplit r = {0, false};
+  if (T == 0) return r;
+  const int64_t ct = p.split / 32;
+  if ((int64_t)T * 15 / (16 * ct) >= p.grid) {
+    r.W = p.grid;
+    r.weighted = true;
+  } else {
+    r.W = (int)min((int64_t)p.grid, max((int64_t)1, (int64_t)T / ct));
+  }
+  return r;
+}
+__device__ __forceinline__ int range_start(int w, int T, StreamSplit sp) {
+  if (sp.weighted) return (int)((int64_t)T * xcd_weight_sum(w) / xcd_weight_sum(sp.W));
+  return (int)((int64_t)w * T / sp.W);
+}
+// The worker whose range holds tile t (0 <= t < T): the largest w with
+// start(w) <= t.  Equal split: w = floor(((t+1)*W - 1) / T).  Weighted: the
+// largest w with T*S(w) < (t+1)*S(W), i.e. S(w) <= X = floor(((t+1)*S(W) - 1)
+// / T); S(8k + r) = 124k + P(r) (124 = four weights of 16 and four of 15;
+// P(r) = 0, 16, 31, 47, 62, 78, 93, 109), so w = 8k + r with k = X / 124 and r
+// the largest with P(r) <= X - 124k.  One 64-bit division either way.
+__device__ __forceinline__ int worker_of(int t, int T, StreamSplit sp) {
+  if (!sp.weighted) return (int)(((int64_t)(t + 1) * sp.W - 1) / T);
+  const int64_t X = ((int64_t)(t + 1) * xcd_weight_sum(sp.W) - 1) / T;
+  const int k = (int)(X / 124), rem = (int)(X - (int64_t)k * 124);
+  const int r = (rem >= 16) + (rem >= 31) + (rem >= 47) + (rem >= 62) + (rem >= 78) + (rem >= 93) + (rem >= 109);
+  return min(8 * k + r, sp.W - 1);
 }
 
-// One arrival on a lane counter (see WorkList::ctr); returns the arrivals of
-// this call so far, this one included.  The usual case is one atomic add.  An
-// arrival that finds a word without the tag sets it to the tagged count 1 by
-// compare-and-swap, or, when another arrival did that first, adds itself
-// again (its first add went into the old word); this loop ends because every
-// failed exchange means another arrival changed the word.  Relaxed at agent
-// scope: the caller orders its own partial stores before this call (they are
-// device-scope stores, complete once vmcnt drains) and issues the merge's
-// loads only after the result returns.
+// One arrival on a counter word (see WorkList::ctr), in two halves so that
+// several arrivals can be in flight together: counter_add issues the atomic
+// add and returns the old word; counter_resolve turns that into the
+// arrivals of this call so far, this one included.  The usual case is the
+// one atomic add.  An arrival that finds a word without the tag sets it to
+// the tagged count 1 by compare-and-swap, or, when another arrival did that
+// first, adds itself again (its first add went into the old word); this
+// loop ends because every failed exchange means another arrival changed the
+// word.  Relaxed at agent scope: the caller orders its own partial stores
+// before the add (they are device-scope stores, complete once vmcnt drains)
+// and issues the merge's loads only after the result returns.
 constexpr uint64_t kCtrTag = 0x5A17C0DE42ull;  // 40 bits
-__device__ __forceinline__ int lane_arrive(uint64_t *c) {
+__device__ __forceinline__ uint64_t counter_add(uint64_t *c) {
+  return __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int counter_resolve(uint64_t *c, uint64_t old) {
   const uint64_t clean = kCtrTag << 24;
-  const uint64_t old = __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if ((old >> 24) == kCtrTag) return (int)(old & 0xFFFFFFu) + 1;
   uint64_t cur = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (;;) {
@@ -258,7 +310,7 @@ __device__ __forceinline__ int lane_arrive(uint64_t *c) {
 }
 
 // The last arrival of a call leaves the counter at zero arrivals.
-__device__ __forceinline__ void lane_reset(uint64_t *c) {
+__device__ __forceinline__ void counter_reset(uint64_t *c) {
   __hip_atomic_store(c, kCtrTag << 24, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

@@ -113,11 +113,11 @@ constexpr int kMaxIdxChunk = 1024;
 // most 512 pages of tokens, so at most 513 are touched).
 constexpr int kMaxSegPages = 520;
 
-// A workgroup of WPG waves is one worker.  The work-list lays every (b, kh,
-// column block) lane's tiles end to end; worker w streams the contiguous tile
-// range [w*T/W, (w+1)*T/W), so all workers move the same number of K/V bytes
-// whatever the mix of sequence lengths, with no atomics and no barriers in
-// the loop.  A range is cut into runs, one per lane it touches.  The waves of
+// A workgroup of WPG waves is one worker.  The work-list lays every (b, kh)
+// lane's tiles end to end; worker w streams one contiguous tile range of a
+// static split (XCD-weighted when the work fills the grid, see
+// stream_split), so the workers' shares do not depend on the mix of sequence
+// lengths, with no atomics and no barriers in the loop.  A range is cut into runs, one per lane it touches.  The waves of
 // a worker take a run's steps in turn (wave i: steps i, i + WPG, ...), so
 // together they read one contiguous stream; at the run's end they combine
 // their (m, l, O) through LDS (one wave keeps its own in registers).
@@ -219,7 +219,11 @@ decode_mfma_kernel(DecodeParams p) {
   };
 
   const int T = wave_total_tiles(p);
-  const int nworkers = workers_for(p, T);
+  // fixed_splits = S > 0: the unbalanced schedule, worker w = q*S + s takes
+  // split s of lane q; otherwise the balanced split of the whole stream
+  const int FS = p.fixed_splits;
+  const StreamSplit split = stream_split(p, T);
+  const int nworkers = FS > 0 ? p.B * p.KH * FS : split.W;
   if (wv == 0) {
     // No worker visits a lane without positions, so its rows get out = 0 and
     // lse = -inf here; lane qq belongs to
@@ -242,23 +246,118 @@ decode_mfma_kernel(DecodeParams p) {
     }
   }
   if ((int)blockIdx.x >= nworkers) return;
-  const int t_begin = (int)((int64_t)blockIdx.x * T / nworkers);
-  const int t_end = (int)((int64_t)(blockIdx.x + 1) * T / nworkers);
 
-  // the lane (b, kh, query-head block) holding the first tile of the range;
-  // each later run takes the next lane that has tiles
-  LaneHit hit = wave_find_lane(p, t_begin);
   // lanes this worker shares with others, whose arrivals wait for its end
   int npend = 0, pend_q0 = 0, pend_need0 = 0, pend_q1 = 0, pend_need1 = 0;
+
+  // Merge inside the launch.  Only a worker's first and last runs can share
+  // their lane with other workers (every run between covers a whole lane).
+  // Once this worker's partial stores are complete it arrives on those
+  // lanes' counters; the arrival that completes a lane's count folds the
+  // lane's slots 0 .. need-1 in slot order (online log-sum-exp) into out
+  // and lse.
+  auto arrive_and_merge = [&]() {
+  if (npend > 0) {
+    wait_vmem();
+    __syncthreads();
+    if (tid == 0) {
+      int last = 0;
+      // both adds in flight together, then resolved
+      const uint64_t o0 = counter_add(p.wl.ctr + pend_q0);
+      const uint64_t o1 = npend > 1 ? counter_add(p.wl.ctr + pend_q1) : 0;
+      if (counter_resolve(p.wl.ctr + pend_q0, o0) == pend_need0) {
+        counter_reset(p.wl.ctr + pend_q0);
+        last |= 1;
+      }
+      if (npend > 1 && counter_resolve(p.wl.ctr + pend_q1, o1) == pend_need1) {
+        counter_reset(p.wl.ctr + pend_q1);
+        last |= 2;
+      }
+      s_last = last;
+    }
+    __syncthreads();
+    const int last = s_last;
+    for (int i = 0; i < npend; ++i) {
+      if (!((last >> i) & 1)) continue;
+      const int pm = i == 0 ? pend_q0 : pend_q1, nm = i == 0 ? pend_need0 : pend_need1;
+      const int bm = pm / p.KH, khm = pm - bm * p.KH;
+      const int64_t pe0 = (int64_t)pm * p.max_slots * p.G;
+      const int pne = p.max_slots * p.G;
+      const __amdgpu_buffer_rsrc_t ors = o_rsrc(pe0, pne), mrs = m_rsrc(pe0, pne), lrs = l_rsrc(pe0, pne);
+      constexpr int U = 8;
+      for (int u = tid; u < p.G * NQ; u += NT) {
+        const int c = u / NQ, sl = u - c * NQ;
+        float mt = NEG_INF, lt = 0.f;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < nm; k0 += U) {
+          float mv[U], lv[U];
+          f32x4_t ov[U];
+#pragma unroll
+          for (int k = 0; k < U; ++k) {
+            const uint32_t e = (uint32_t)(min(k0 + k, nm - 1) * p.G + c);
+            const float l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lrs, e * 4, 0, kDeviceScope));
+            lv[k] = k0 + k < nm ? l : 0.f;
+            mv[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mrs, e * 4, 0, kDeviceScope));
+            ov[k] = __builtin_bit_cast(
+                f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ors, (e * D + 4 * sl) * 4, 0, kDeviceScope));
+          }
+#pragma unroll
+          for (int k = 0; k < U; ++k) {
+            if (lv[k] > 0.f) {  // an empty partial (l = 0) may hold any o
+              if (mv[k] > mt) {
+                const float sc = expf(mt - mv[k]);
+                acc *= sc;
+                lt *= sc;
+                mt = mv[k];
+              }
+              const float w = expf(mv[k] - mt) * lv[k];
+              acc += w * ov[k];
+              lt += w;
+            }
+          }
+        }
+        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+        const int64_t orow = q_row_index(p, bm, khm, c);
+        store_out4(orow, sl, acc * inv);
+        if (sl == 0 && p.lse) p.lse[orow] = lt > 0.f ? mt + logf(lt) : NEG_INF;
+      }
+    }
+  }
+  };
+
+  // The worker's range; each lane it touches is one run.
+  int t_begin, t_end, fs_need = 0, fs_slot = 0;
+  if (FS > 0) {
+    // split s of lane q: [t0 + s*n/S, t0 + (s+1)*n/S) of the lane's n tiles,
+    // t0 = the tiles of the lanes before q; the lane's non-empty splits are
+    // its partials, in split order
+    const int q = (int)blockIdx.x / FS, sp = (int)blockIdx.x - q * FS;
+    int acc = 0;
+    for (int qq = lane; qq < q; qq += 64) acc += lane_tiles(p, qq);
+    const int t0 = uniform_i32(wave_sum_int(acc)), n = uniform_i32(lane_tiles(p, q));
+    t_begin = t0 + (int)((int64_t)sp * n / FS);
+    t_end = t0 + (int)((int64_t)(sp + 1) * n / FS);
+    fs_need = min(FS, n);
+    fs_slot = n < FS ? t_begin - t0 : sp;
+  } else {
+    t_begin = range_start(blockIdx.x, T, split);
+    t_end = range_start(blockIdx.x + 1, T, split);
+  }
+  // the lane (b, kh) holding the first tile of the range; each later run
+  // takes the next lane that has tiles
+  LaneHit hit = wave_find_lane(p, t_begin);
   for (int t = t_begin; t < t_end;) {
     if (hit.nt == 0) break;  // lane walk exhausted (cannot happen for t < total)
     const int q = hit.q;
     const int lane_t0 = hit.t0, lane_t1 = hit.t0 + hit.nt;
     const int run_end = min(t_end, lane_t1);
     // workers holding part of this lane, and this worker's slot among them
-    const int w_first = worker_of(lane_t0, T, nworkers);
-    const int need = worker_of(lane_t1 - 1, T, nworkers) - w_first + 1;
-    const int slot = (int)blockIdx.x - w_first;
+    int need = fs_need, slot = fs_slot;
+    if (FS == 0) {
+      const int w_first = worker_of(lane_t0, T, split);
+      need = worker_of(lane_t1 - 1, T, split) - w_first + 1;
+      slot = (int)blockIdx.x - w_first;
+    }
     const int pair = q;
     const int b = pair / p.KH, kh = pair - b * p.KH;
     const int L = uniform_i32(min(max(p.seq_lens[b], 0), p.max_seq_len));
@@ -790,78 +889,7 @@ decode_mfma_kernel(DecodeParams p) {
     t = run_end;
     if (t < t_end) hit = next_lane(p, hit);
   }
-
-  // Merge inside the launch.  Only a worker's first and last runs can share
-  // their lane with other workers (every run between covers a whole lane).
-  // Once this worker's partial stores are complete it arrives on those
-  // lanes' counters; the arrival that completes a lane's count folds the
-  // lane's slots 0 .. need-1 in slot order (online log-sum-exp) into out
-  // and lse.
-  if (npend > 0) {
-    wait_vmem();
-    __syncthreads();
-    if (tid == 0) {
-      int last = 0;
-      const int a0 = lane_arrive(p.wl.ctr + pend_q0);
-      const int a1 = npend > 1 ? lane_arrive(p.wl.ctr + pend_q1) : 0;
-      if (a0 == pend_need0) {
-        lane_reset(p.wl.ctr + pend_q0);
-        last |= 1;
-      }
-      if (npend > 1 && a1 == pend_need1) {
-        lane_reset(p.wl.ctr + pend_q1);
-        last |= 2;
-      }
-      s_last = last;
-    }
-    __syncthreads();
-    const int last = s_last;
-    for (int i = 0; i < npend; ++i) {
-      if (!((last >> i) & 1)) continue;
-      const int pm = i == 0 ? pend_q0 : pend_q1, nm = i == 0 ? pend_need0 : pend_need1;
-      const int bm = pm / p.KH, khm = pm - bm * p.KH;
-      const int64_t pe0 = (int64_t)pm * p.max_slots * p.G;
-      const int pne = p.max_slots * p.G;
-      const __amdgpu_buffer_rsrc_t ors = o_rsrc(pe0, pne), mrs = m_rsrc(pe0, pne), lrs = l_rsrc(pe0, pne);
-      constexpr int U = 8;
-      for (int u = tid; u < p.G * NQ; u += NT) {
-        const int c = u / NQ, sl = u - c * NQ;
-        float mt = NEG_INF, lt = 0.f;
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < nm; k0 += U) {
-          float mv[U], lv[U];
-          f32x4_t ov[U];
-#pragma unroll
-          for (int k = 0; k < U; ++k) {
-            const uint32_t e = (uint32_t)(min(k0 + k, nm - 1) * p.G + c);
-            const float l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lrs, e * 4, 0, kDeviceScope));
-            lv[k] = k0 + k < nm ? l : 0.f;
-            mv[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mrs, e * 4, 0, kDeviceScope));
-            ov[k] = __builtin_bit_cast(
-                f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ors, (e * D + 4 * sl) * 4, 0, kDeviceScope));
-          }
-#pragma unroll
-          for (int k = 0; k < U; ++k) {
-            if (lv[k] > 0.f) {  // an empty partial (l = 0) may hold any o
-              if (mv[k] > mt) {
-                const float sc = expf(mt - mv[k]);
-                acc *= sc;
-                lt *= sc;
-                mt = mv[k];
-              }
-              const float w = expf(mv[k] - mt) * lv[k];
-              acc += w * ov[k];
-              lt += w;
-            }
-          }
-        }
-        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-        const int64_t orow = q_row_index(p, bm, khm, c);
-        store_out4(orow, sl, acc * inv);
-        if (sl == 0 && p.lse) p.lse[orow] = lt > 0.f ? mt + logf(lt) : NEG_INF;
-      }
-    }
-  }
+  arrive_and_merge();
 }
 
 }  // namespace

@@ -128,6 +128,9 @@ def test_default_split_tokens(over, split):
     (dict(kv_dtype=_lib.ATTN_I8, k_scale=FAKE, k_part_tokens=64, k_scale_stride=3), _lib.ATTN_ERR_INVALID_ARG),
     (dict(kv_dtype=_lib.ATTN_I8, k_scale=FAKE, k_part_tokens=40, k_scale_stride=64), _lib.ATTN_ERR_INVALID_ARG),
     (dict(token_idx=FAKE), _lib.ATTN_ERR_INVALID_ARG),                 # no n_idx
+    (dict(fixed_splits=-1), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(fixed_splits=70000), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(fixed_splits=2, q_dtype=_lib.ATTN_F32, kv_dtype=_lib.ATTN_F32), _lib.ATTN_ERR_UNSUPPORTED),
     (dict(softmax_scale=float("inf")), _lib.ATTN_ERR_INVALID_ARG),
     (dict(q_quant=3), _lib.ATTN_ERR_INVALID_ARG),
     (dict(q_quant=_lib.ATTN_QUANT_ROW), _lib.ATTN_ERR_UNSUPPORTED),   # int8 query needs int8 KV

@@ -274,3 +274,98 @@ def test_reused_workspace_after_longer_rows(out_dtype):
     ref, ref_lse = oracle.attention_rows(pr, oracle.all_rows(pr), nthreads=8)
     check(p.out.float().cpu().numpy().reshape(w.B * w.QH, w.D), lse.cpu().numpy().reshape(-1), ref, ref_lse,
           bf16_out=out_dtype == torch.bfloat16)
+
+
+@pytest.mark.parametrize("fill", ["random", "ones", "zeros"])
+def test_workspace_needs_no_clearing(fill):
+    """The merge inside the decode launch counts arrivals per (b, kh) in the workspace.  Whatever
+    the workspace holds before a call (random bytes, all ones, zeros), the result equals the
+    oracle's and a second call on the same workspace reproduces it bit for bit."""
+    lens = np.array([3000, 65, 0, 4097], np.int32)
+    w = synth.workload("gqa32k", B=4, KH=4, G=8, lens=lens, layout="token_major", seed=171)
+    q, k, v, g = synth.generate(w)
+    qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
+    kd, vd = to_dev(k), to_dev(v)
+    lse = torch.empty((w.B, w.QH), dtype=torch.float32, device=DEV)
+    p = pkg.prepare_decode(qd, kd, vd, dev_geom(g), w.G, lse=lse, split_tokens=128)
+    ws = p.workspace
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    if fill == "random":
+        ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, generator=gen))
+    elif fill == "ones":
+        ws.fill_(255)
+    else:
+        ws.zero_()
+    log_case(f"workspace filled with {fill}")
+    p()
+    torch.cuda.synchronize()
+    a_out, a_lse = p.out.cpu().numpy().copy(), lse.cpu().numpy().copy()
+    pr = problem(w, q, k, v, g)
+    ref, ref_lse = oracle.attention_rows(pr, oracle.all_rows(pr), nthreads=8)
+    check(a_out.reshape(w.B * w.QH, w.D), a_lse.reshape(-1), ref, ref_lse)
+    p()
+    torch.cuda.synchronize()
+    check(p.out.cpu().numpy().reshape(w.B * w.QH, w.D), lse.cpu().numpy().reshape(-1), ref, ref_lse)
+    assert np.array_equal(a_out, p.out.cpu().numpy()) and np.array_equal(a_lse, lse.cpu().numpy())
+
+
+def test_many_workers_per_sequence_and_whole_sequences_per_worker():
+    """split_tokens = 32 cuts one long sequence over hundreds of workers (hundreds of partials
+    folded by the last arrival), while a batch of short sequences puts several whole sequences in
+    one worker's range (their outputs written directly, no partial)."""
+    lens = np.array([60000, 40, 33, 1, 200, 96], np.int32)
+    w = synth.workload("gqa32k", B=len(lens), KH=1, G=8, lens=lens, layout="head_major", seed=172)
+    q, k, v, g = synth.generate(w)
+    pr = problem(w, q, k, v, g)
+    ref, ref_lse = oracle.attention_rows(pr, oracle.all_rows(pr), nthreads=8)
+    for split in (32, 0, 1 << 20):
+        log_case(f"split {split}")
+        out, lse = run_decode(w, q, k, v, g, split_tokens=split)
+        check(out, lse, ref, ref_lse)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_unaligned_output(out_dtype):
+    """out may start at any element: the merge's stores fall back to element stores when out is
+    not aligned for vector stores; the values equal the aligned call's bit for bit."""
+    w = synth.workload("gqa32k", B=2, KH=2, L=3000, seed=173)
+    q, k, v, g = synth.generate(w)
+    qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
+    kd, vd, geom = to_dev(k), to_dev(v), dev_geom(g)
+    n = w.B * w.QH * w.D
+    big = torch.zeros(n + 1, dtype=out_dtype, device=DEV)
+    odd = big[1:].view(w.B, w.QH, w.D)
+    log_case(f"unaligned out {out_dtype}")
+    a, _ = pkg.attn_decode_splitkv(qd, kd, vd, geom, w.G, out_dtype=out_dtype)
+    b, _ = pkg.attn_decode_splitkv(qd, kd, vd, geom, w.G, out=odd)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("splits", [1, 3, 40])
+def test_fixed_splits_schedule_matches_oracle(splits):
+    """The unbalanced schedule kept for comparison (every (b, kh) cut into the same number of
+    splits, one worker each): sequences shorter than the split count, an empty one and a long
+    one, bf16 and int8."""
+    lens = np.array([5000, 17, 0, 900, 1], np.int32)
+    w = synth.workload("gqa32k", B=len(lens), KH=2, G=8, lens=lens, layout="token_major", seed=174)
+    q, k, v, g = synth.generate(w)
+    pr = problem(w, q, k, v, g)
+    ref, ref_lse = oracle.attention_rows(pr, oracle.all_rows(pr), nthreads=8)
+    log_case(f"fixed splits {splits} bf16")
+    out, lse = run_decode(w, q, k, v, g, fixed_splits=splits)
+    check(out, lse, ref, ref_lse)
+    geom = dev_geom(g)
+    kc, ks = pkg.kv_quant_int8(to_dev(k), geom, 64)
+    vc, vs = pkg.kv_quant_int8(to_dev(v), geom, 0)
+    torch.cuda.synchronize()
+    p8 = problem(w, q, kc.cpu().numpy(), vc.cpu().numpy(), g, k_scale=ks.cpu().numpy(), k_part=64,
+                 k_scale_stride=-(-int(g.max_len) // 64), v_scale=float(vs.item()))
+    ref8, ref8_lse = oracle.attention_rows(p8, oracle.all_rows(p8), nthreads=8)
+    log_case(f"fixed splits {splits} int8")
+    qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
+    lse8 = torch.empty((w.B, w.QH), dtype=torch.float32, device=DEV)
+    o8, _ = pkg.attn_decode_splitkv(qd, kc, vc, geom, w.G, lse=lse8, k_scale=ks, k_part_tokens=64,
+                                    v_scale=float(vs.item()), fixed_splits=splits)
+    torch.cuda.synchronize()
+    check(o8.cpu().numpy().reshape(w.B * w.QH, w.D), lse8.cpu().numpy().reshape(-1), ref8, ref8_lse)
