@@ -18,7 +18,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.cpp")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB points the loader at another build of oracle.cpp (the sanitizer test builds one with
+# AddressSanitizer and UndefinedBehaviorSanitizer and runs the pins against it)
+_LIB = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 F32, BF16, I8 = 0, 1, 2
 
