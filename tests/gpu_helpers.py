@@ -34,3 +34,27 @@ def bf16_to_f32(t: torch.Tensor) -> np.ndarray:
 
 def log_case(msg: str):
     print(f"[case] {msg}", flush=True)
+
+
+def host_threads() -> int:
+    """Host threads for the oracle: the cores this process may use, capped by the CPU share the
+    machine grants it (OMP_NUM_THREADS where set)."""
+    import os
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    if share.isdigit() and int(share) > 0:
+        n = min(n, int(share))
+    return max(1, n)
+
+
+def oracle_all_rows(p):
+    """The oracle over every output row of a problem, on all host threads; logs the host time."""
+    import time
+    t0 = time.perf_counter()
+    ref, ref_lse = oracle.attention_rows(p, oracle.all_rows(p), nthreads=host_threads())
+    print(f"[info] oracle over {ref.shape[0]} rows: {time.perf_counter() - t0:.1f} s on {host_threads()} threads",
+          flush=True)
+    return ref, ref_lse

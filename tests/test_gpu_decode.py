@@ -13,7 +13,7 @@ import torch
 import long_context_decode_gqa_amd as pkg
 import oracle
 import synth
-from gpu_helpers import DEV, bf16_to_f32, dev_geom, log_case, problem, to_dev
+from gpu_helpers import DEV, bf16_to_f32, dev_geom, log_case, oracle_all_rows, problem, to_dev
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
@@ -196,22 +196,17 @@ def test_merge_lse_of_oracle_partials(D, maxc, misaligned, rows):
             assert abs(lse[r] - rl) <= 1e-5
 
 
-def _full_size_sampled_rows(name, nrows, seed, **over):
-    """A full-size workload in the benchmark's launch configuration (its own
-    split-KV chunk size), compared with the oracle on sampled output rows;
-    then, for every row, the property that the softmax weights sum to one: a
-    constant V comes back unchanged, and lse does not depend on V."""
+def _full_size_all_rows(name, **over):
+    """A full-size workload in the benchmark's launch configuration, every output row compared
+    with the oracle; then the property that the softmax weights sum to one: a constant V comes
+    back unchanged, and lse does not depend on V."""
     w = synth.workload(name, **over)
     q, k, v, g = synth.generate(w)
     log_case(f"{name} full size, split {w.split_tokens}")
     out, lse = run_decode(w, q, k, v, g, split_tokens=w.split_tokens)
     p = problem(w, q, k, v, g)
-    rng = np.random.default_rng(seed)
-    rows = [(int(b), int(h)) for b, h in zip(rng.integers(0, w.B, nrows), rng.integers(0, w.QH, nrows))]
-    rows += [(0, 0), (w.B - 1, w.QH - 1)]
-    ref, ref_lse = oracle.attention_rows(p, rows, nthreads=16)
-    idx = [b * w.QH + h for b, h in rows]
-    check(out[idx], lse[idx], ref, ref_lse)
+    ref, ref_lse = oracle_all_rows(p)
+    check(out, lse, ref, ref_lse)
     del p, v
     vc = np.full(k.shape, 0x3FC0, dtype=np.uint16)  # bf16 1.5 everywhere
     out_c, lse_c = run_decode(w, q, k, vc, g, split_tokens=w.split_tokens)
@@ -220,26 +215,26 @@ def _full_size_sampled_rows(name, nrows, seed, **over):
     assert np.array_equal(lse_c, lse)
 
 
-def test_gqa32k_full_size_sampled_rows():
+def test_gqa32k_full_size_all_rows():
     """The 16 x 8 x 8 x 128 x 32768 bf16 workload."""
-    _full_size_sampled_rows("gqa32k", 24, 1)
+    _full_size_all_rows("gqa32k")
 
 
-def test_dense128k_full_size_sampled_rows():
+def test_dense128k_full_size_all_rows():
     """The 4 x 8 x 8 x 128 x 131072 bf16 workload the benchmark's headline line times."""
-    _full_size_sampled_rows("dense128k", 16, 3)
+    _full_size_all_rows("dense128k")
 
 
-def test_ragged_full_size_sampled_rows():
+def test_ragged_full_size_all_rows():
     """The 32-sequence ragged batch (512..131072 tokens, head-major packed cache)."""
-    _full_size_sampled_rows("ragged", 16, 4)
+    _full_size_all_rows("ragged")
 
 
 @pytest.mark.parametrize("name", ["gqa32k", "dense128k"])
-def test_one_kv_head_share_full_size_sampled_rows(name):
+def test_one_kv_head_share_full_size_all_rows(name):
     """One GPU's share of a split over 8 GPUs by KV heads (KH = 1, the rest of the shape as named),
-    in the library's default launch: 512 workers of 32 tiles instead of 2048."""
-    _full_size_sampled_rows(name, 12, 5, KH=1, split_tokens=0)
+    in the library's default launch."""
+    _full_size_all_rows(name, KH=1, split_tokens=0)
 
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])

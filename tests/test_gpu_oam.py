@@ -15,7 +15,7 @@ import torch
 import long_context_decode_gqa_amd as pkg
 import oracle
 import synth
-from gpu_helpers import DEV, dev_geom, log_case, problem, to_dev
+from gpu_helpers import DEV, dev_geom, log_case, oracle_all_rows, problem, to_dev
 
 pytestmark = pytest.mark.gpu
 BAND = 1e-4
@@ -121,27 +121,26 @@ def test_oam_feeds_exact_attention_over_kept_tokens():
 
 
 def test_oam_128k_full_size():
-    """4 x 8 KV heads x 131072 tokens, keep 4096 per (b, kh), then exact attention."""
+    """4 x 8 KV heads x 131072 tokens, keep 4096 per (b, kh): scores and kept sets of all 32 pairs,
+    then exact attention over the kept tokens on every output row."""
     w = synth.workload("oam_128k")
     q, k, v, g = synth.generate(w)
     log_case("oam 128k full size")
     idx, nk, sc = run_oam(w, q, k, v, g, w.top_k)
     p = problem(w, q, k, v, g)
-    for pr in (0, 13, 31):
+    # every (b, kh) pair: scores and kept set against the oracle (check_pair also checks the set
+    # against the top-K of the GPU's own fp32 scores)
+    for pr in range(w.B * w.KH):
         b, kh = divmod(pr, w.KH)
         check_pair(oracle.oam_scores(p, b, kh, 1.0, 1e-6), sc[pr], idx[pr], nk[pr], w.top_k)
-    # every pair: exactness against its own fp32 scores
-    for pr in range(w.B * w.KH):
-        np.testing.assert_array_equal(idx[pr], exact_topk(sc[pr], w.top_k))
     qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
-    out, _ = pkg.attn_decode_splitkv(qd, to_dev(k), to_dev(v), dev_geom(g), w.G, token_idx=to_dev(idx),
-                                     n_idx=to_dev(nk), split_tokens=w.split_tokens)
+    out, lse = pkg.attn_decode_splitkv(qd, to_dev(k), to_dev(v), dev_geom(g), w.G, token_idx=to_dev(idx),
+                                       n_idx=to_dev(nk), split_tokens=w.split_tokens)
     torch.cuda.synchronize()
     pk = problem(w, q, k, v, g, tok_idx=idx.reshape(-1), n_idx=nk, idx_stride=w.top_k)
-    rows = [(0, 0), (1, 17), (2, 40), (3, 63)]
-    ref, _ = oracle.attention_rows(pk, rows, nthreads=4)
-    o = out.cpu().numpy().reshape(-1, w.D)[[b * w.QH + h for b, h in rows]]
-    assert np.abs(o - ref).max() <= 2e-3
+    ref, ref_lse = oracle_all_rows(pk)
+    assert np.abs(out.cpu().numpy().reshape(-1, w.D) - ref).max() <= 2e-3
+    assert np.abs(lse.cpu().numpy().reshape(-1) - ref_lse).max() <= 1e-3
 
 
 def _topk_from_vlog(vlog_row, top_k, D=128, G=8):
@@ -265,10 +264,10 @@ def test_oam_int8_stack_feeds_int8_attention(q_quant):
     assert np.abs(out.cpu().numpy().reshape(-1, w.D) - ref).max() <= 2e-3
 
 
-def test_oam_int8_128k_full_size_sampled_pairs():
+def test_oam_int8_128k_full_size():
     """The 128K OAM workload (4 x 8 KV heads x 131072 tokens, top 4096) on an INT8 cache (64-token K
-    partitions, per-tensor V), in the benchmark's configuration: scores and kept sets of sampled
-    (b, kh) pairs against the oracle, then INT8 attention over the kept tokens on sampled rows."""
+    partitions, per-tensor V), in the benchmark's configuration: scores and kept sets of all 32
+    (b, kh) pairs against the oracle, then INT8 attention over the kept tokens on every output row."""
     w = synth.workload("oam_128k")
     q, k, v, g = synth.generate(w)
     log_case("oam int8 128k full size")
@@ -276,20 +275,19 @@ def test_oam_int8_128k_full_size_sampled_pairs():
     del k, v
     idx, nk, sc = run_oam_int8(w, q, g, kc, ks, vc, vs, 64, w.top_k, True)
     qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
-    out, _ = pkg.attn_decode_splitkv(qd, kc, vc, dev_geom(g), w.G, token_idx=idx, n_idx=nk, k_scale=ks,
-                                     k_part_tokens=64, v_scale=vs, split_tokens=w.split_tokens)
+    out, lse = pkg.attn_decode_splitkv(qd, kc, vc, dev_geom(g), w.G, token_idx=idx, n_idx=nk, k_scale=ks,
+                                       k_part_tokens=64, v_scale=vs, split_tokens=w.split_tokens)
     torch.cuda.synchronize()
     idx_h, nk_h = idx.cpu().numpy(), nk.cpu().numpy()
     p = problem(w, q, kc.cpu().numpy(), vc.cpu().numpy(), g, v_scale=vs, **kk)
-    for b, kh in ((0, 0), (3, 7), (2, 5)):
-        pr = b * w.KH + kh
+    for pr in range(w.B * w.KH):
+        b, kh = divmod(pr, w.KH)
         check_pair(oracle.oam_scores(p, b, kh, w.beta, w.eps), sc[pr], idx_h[pr], nk_h[pr], w.top_k)
     pk = problem(w, q, kc.cpu().numpy(), vc.cpu().numpy(), g, v_scale=vs, tok_idx=idx_h.reshape(-1), n_idx=nk_h,
                  idx_stride=w.top_k, **kk)
-    rows = [(0, 0), (3, 63), (2, 41), (1, 17)]
-    ref, _ = oracle.attention_rows(pk, rows, nthreads=16)
-    got = out.cpu().numpy().reshape(w.B * w.QH, w.D)[[b * w.QH + h for b, h in rows]]
-    assert np.abs(got - ref).max() <= 2e-3
+    ref, ref_lse = oracle_all_rows(pk)
+    assert np.abs(out.cpu().numpy().reshape(-1, w.D) - ref).max() <= 2e-3
+    assert np.abs(lse.cpu().numpy().reshape(-1) - ref_lse).max() <= 1e-3
 
 
 # --- block-granular selection (NSA page §2.1, selected attention; block score = mean of its tokens' scores) ---
@@ -365,9 +363,9 @@ def test_block_select_on_int8_cache_feeds_attention():
     assert np.abs(out.cpu().numpy().reshape(-1, w.D) - ref).max() <= 2e-3
 
 
-def test_block_select_128k_full_size_sampled_pairs():
-    """128K tokens, 64-token blocks, the best 64 blocks (4096 tokens, as many as the token top-K keeps),
-    on sampled (b, kh) pairs, then attention over them on sampled rows."""
+def test_block_select_128k_full_size():
+    """128K tokens, 64-token blocks, the best 64 blocks (4096 tokens, as many as the token top-K keeps):
+    kept blocks of all 32 (b, kh) pairs against the oracle, then attention over them on every row."""
     w = synth.workload("oam_128k")
     q, k, v, g = synth.generate(w)
     bt, n = 64, 64
@@ -376,15 +374,16 @@ def test_block_select_128k_full_size_sampled_pairs():
     kd, vd = to_dev(k), to_dev(v)
     geom = dev_geom(g)
     idx, nk = pkg.oam_score_topk(qd, kd, geom, w.G, n, v=vd, beta=0.0, block_tokens=bt)
-    out, _ = pkg.attn_decode_splitkv(qd, kd, vd, geom, w.G, token_idx=idx, n_idx=nk, split_tokens=w.split_tokens)
+    out, lse = pkg.attn_decode_splitkv(qd, kd, vd, geom, w.G, token_idx=idx, n_idx=nk,
+                                       split_tokens=w.split_tokens)
     torch.cuda.synchronize()
     idx_h, nk_h = idx.cpu().numpy(), nk.cpu().numpy()
     p = problem(w, q, k, v, g)
-    for b, kh in ((0, 0), (3, 7), (1, 4)):
+    for pr in range(w.B * w.KH):
+        b, kh = divmod(pr, w.KH)
         ref_idx, ref_bs = oracle.block_select(p, b, kh, bt, n, beta=0.0)
-        check_blocks(ref_idx, ref_bs, idx_h[b * w.KH + kh], nk_h[b * w.KH + kh], n, bt, int(w.lens[b]))
+        check_blocks(ref_idx, ref_bs, idx_h[pr], nk_h[pr], n, bt, int(w.lens[b]))
     pk = problem(w, q, k, v, g, tok_idx=idx_h.reshape(-1), n_idx=nk_h, idx_stride=n * bt)
-    rows = [(0, 0), (3, 63), (2, 9)]
-    ref, _ = oracle.attention_rows(pk, rows, nthreads=16)
-    got = out.cpu().numpy().reshape(w.B * w.QH, w.D)[[b * w.QH + h for b, h in rows]]
-    assert np.abs(got - ref).max() <= 2e-3
+    ref, ref_lse = oracle_all_rows(pk)
+    assert np.abs(out.cpu().numpy().reshape(-1, w.D) - ref).max() <= 2e-3
+    assert np.abs(lse.cpu().numpy().reshape(-1) - ref_lse).max() <= 1e-3
