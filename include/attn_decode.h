@@ -169,14 +169,13 @@ typedef struct {
  *   workspace   caller-owned scratch of at least attn_decode_workspace_size()
  *               bytes, 256-byte aligned; holds the partials and, for
  *               bf16/int8 KV, one arrival counter per (b, kh).  It needs no
- *               initialisation: every call leaves its counters at zero
- *               arrivals and takes over a counter word that holds anything
- *               else.  A fixed 40-bit tag marks the library's counter words,
- *               so the one content it cannot tell from a live counter is its
- *               own tag with a nonzero count, left by a call on the same
- *               workspace that was cut off mid-launch or overlapped by
- *               another call (other data matches the tag with probability
- *               2^-40 per word); filling the workspace with zeros restores it
+ *               initialisation: a counter word carries a 40-bit tag that
+ *               changes with every call in the process, every call leaves
+ *               its counters at zero arrivals, and a call's first arrival
+ *               takes over a word without its tag (whatever an earlier call
+ *               left, finished or cut off, or other data, which matches a
+ *               tag with probability 2^-40 per word).  Calls that run at the
+ *               same time on one workspace race
  *   out         [B][KH*G][D] in out_dtype (ATTN_F32 or ATTN_BF16)
  *   lse         optional fp32 [B][KH*G]: natural-log log-sum-exp of the
  *               scaled scores (-inf for a sequence with no tokens)

@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <mutex>
 #include <string>
 
@@ -261,16 +262,32 @@ attn_status attn_decode_split_tokens(const attn_decode_args *args, int32_t *spli
   return ATTN_OK;
 }
 
-static attn_status decode_impl(const attn_decode_args *a, attn_stream_t stream, void *const *events) {
+}  // extern "C"
+
+namespace lcdg {
+
+// The tag of one call's arrival counters: a 40-bit value that changes with
+// every call in the process (2^40 calls before one repeats), offset so that
+// small integers and zeroed memory do not carry it.
+static uint64_t next_counter_tag() {
+  static std::atomic<uint64_t> seq{0};
+  return (0x5A17C0DE42ull + seq.fetch_add(1, std::memory_order_relaxed)) & ((uint64_t(1) << 40) - 1);
+}
+
+// One decode call on a validated workspace: `workspace` / `workspace_bytes`
+// take the place of the arguments' own (the no-allocation entry point passes
+// its static scratch here).
+attn_status decode_run(const attn_decode_args *a, void *workspace, size_t workspace_bytes, attn_stream_t stream,
+                       void *const *events) {
   DecodeLayout L;
   attn_status st = plan_decode(a, &L);
   if (st != ATTN_OK) return st;
   if (a->kv.B == 0) return ATTN_OK;
-  if (!a->workspace || (reinterpret_cast<uintptr_t>(a->workspace) & 255))
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255))
     return fail(ATTN_ERR_INVALID_ARG, "workspace must be a 256-byte aligned device pointer");
-  if (a->workspace_bytes < L.total) return fail(ATTN_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than required");
+  if (workspace_bytes < L.total) return fail(ATTN_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than required");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  char *ws = static_cast<char *>(a->workspace);
+  char *ws = static_cast<char *>(workspace);
   DecodeParams p;
   p.B = a->kv.B;
   p.KH = a->kv.KH;
@@ -315,6 +332,7 @@ static attn_status decode_impl(const attn_decode_args *a, attn_stream_t stream, 
   p.wl.l_part = reinterpret_cast<float *>(ws + L.l);
   p.wl.o_part = reinterpret_cast<float *>(ws + L.o);
   p.wl.ctr = L.mfma ? reinterpret_cast<uint64_t *>(ws + L.ctr) : nullptr;
+  p.wl.ctr_tag = next_counter_tag();
   p.out_dtype = a->out_dtype;
   p.out = a->out;
   p.lse = a->lse;
@@ -337,12 +355,18 @@ static attn_status decode_impl(const attn_decode_args *a, attn_stream_t stream, 
   return ATTN_OK;
 }
 
+}  // namespace lcdg
+
+extern "C" {
+
 attn_status attn_decode_splitkv(const attn_decode_args *a, attn_stream_t stream) {
-  return decode_impl(a, stream, nullptr);
+  if (!a) return fail(ATTN_ERR_INVALID_ARG, "args is NULL");
+  return decode_run(a, a->workspace, a->workspace_bytes, stream, nullptr);
 }
 
 attn_status attn_decode_splitkv_profiled(const attn_decode_args *a, attn_stream_t stream, void *const events[3]) {
-  return decode_impl(a, stream, events);
+  if (!a) return fail(ATTN_ERR_INVALID_ARG, "args is NULL");
+  return decode_run(a, a->workspace, a->workspace_bytes, stream, events);
 }
 
 attn_status attn_merge_lse(const float *o_part, const float *m_part, const float *l_part,

@@ -92,11 +92,13 @@ struct WorkList {
   float *l_part;             // [max partials]
   float *o_part;             // [max partials][D]
   // Merge inside the matrix-core decode launch: one arrival counter per lane.
-  // A counter word holds (kCtrTag << 24) | arrivals.  Every call leaves its counters at zero
-  // arrivals, and a word without the tag (a workspace that has held something
-  // else) is taken over by the first arrival, so the workspace needs no
-  // clearing.
+  // A counter word holds (ctr_tag << 24) | arrivals, ctr_tag being a 40-bit
+  // tag the host draws anew for every call.  Every call leaves its counters
+  // at zero arrivals, and a word without this call's tag (left by an earlier
+  // call, finished or cut off, or other data) is taken over by the call's
+  // first arrival, so the workspace needs no clearing.
   uint64_t *ctr;             // [lanes] (matrix-core decode)
+  uint64_t ctr_tag;          // < 2^40
 };
 
 struct DecodeParams {
@@ -234,8 +236,10 @@ __device__ __forceinline__ int workers_for(const DecodeParams &p, int total_tile
 // range), so a worker on an odd XCD gets weight 15 and one on an even XCD
 // 16: worker w's range is [start(w), start(w+1)), start(w) = floor(T * S(w)
 // / S(W)), S(w) = the sum of the weights of workers 0 .. w-1.  With fewer
-// workers the XCDs do not contend and the split is equal, start(w) =
-// floor(w * T / W).  Every range is at least ct = split / 32 tiles: the
+// workers the XCDs do not contend, and with two column groups per worker
+// (more than 32 query rows per KV head) each byte carries twice the matrix
+// work and the weighted split measured 2% slower than the equal one; in
+// both cases the split is equal, start(w) = floor(w * T / W).  Every range is at least ct = split / 32 tiles: the
 // weighted split runs W = grid <= 15 T / (16 ct) workers, and start(w+1) -
 // start(w) >= floor(15 T / (16 W)) >= ct; the equal one at most T / ct.  So
 // no range is empty, and a lane of n tiles touches at most ceil(n / ct) + 1.
@@ -251,7 +255,7 @@ __device__ __forceinline__ StreamSplit stream_split(const DecodeParams &p, int T
   StreamSplit r = {0, false};
   if (T == 0) return r;
   const int64_t ct = p.split / 32;
-  if ((int64_t)T * 15 / (16 * ct) >= p.grid) {
+  if (p.ngb == 1 && (int64_t)T * 15 / (16 * ct) >= p.grid) {
     r.W = p.grid;
     r.weighted = true;
   } else {
@@ -280,24 +284,24 @@ __device__ __forceinline__ int worker_of(int t, int T, StreamSplit sp) {
 // One arrival on a counter word (see WorkList::ctr), in two halves so that
 // several arrivals can be in flight together: counter_add issues the atomic
 // add and returns the old word; counter_resolve turns that into the
-// arrivals of this call so far, this one included.  The usual case is the
-// one atomic add.  An arrival that finds a word without the tag sets it to
-// the tagged count 1 by compare-and-swap, or, when another arrival did that
-// first, adds itself again (its first add went into the old word); this
-// loop ends because every failed exchange means another arrival changed the
-// word.  Relaxed at agent scope: the caller orders its own partial stores
-// before the add (they are device-scope stores, complete once vmcnt drains)
-// and issues the merge's loads only after the result returns.
-constexpr uint64_t kCtrTag = 0x5A17C0DE42ull;  // 40 bits
+// arrivals of this call so far, this one included.  With the call's tag in
+// the old word that is the one atomic add.  An arrival that finds another
+// tag (the first of each shared lane in a call) sets the word to the tagged
+// count 1 by compare-and-swap, or, when another arrival did that first, adds
+// itself again (its first add went into the old word); this loop ends
+// because every failed exchange means another arrival changed the word.
+// Relaxed at agent scope: the caller orders its own partial stores before
+// the add (they are device-scope stores, complete once vmcnt drains) and
+// issues the merge's loads only after the result returns.
 __device__ __forceinline__ uint64_t counter_add(uint64_t *c) {
   return __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ int counter_resolve(uint64_t *c, uint64_t old) {
-  const uint64_t clean = kCtrTag << 24;
-  if ((old >> 24) == kCtrTag) return (int)(old & 0xFFFFFFu) + 1;
+__device__ __forceinline__ int counter_resolve(uint64_t *c, uint64_t old, uint64_t tag) {
+  const uint64_t clean = tag << 24;
+  if ((old >> 24) == tag) return (int)(old & 0xFFFFFFu) + 1;
   uint64_t cur = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (;;) {
-    if ((cur >> 24) == kCtrTag) {
+    if ((cur >> 24) == tag) {
       const uint64_t again = __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return (int)(again & 0xFFFFFFu) + 1;
     }
@@ -310,8 +314,8 @@ __device__ __forceinline__ int counter_resolve(uint64_t *c, uint64_t old) {
 }
 
 // The last arrival of a call leaves the counter at zero arrivals.
-__device__ __forceinline__ void counter_reset(uint64_t *c) {
-  __hip_atomic_store(c, kCtrTag << 24, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void counter_reset(uint64_t *c, uint64_t tag) {
+  __hip_atomic_store(c, tag << 24, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Wait until every vector-memory access this wave issued has completed; for

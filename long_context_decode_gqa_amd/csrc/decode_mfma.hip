@@ -265,12 +265,12 @@ decode_mfma_kernel(DecodeParams p) {
       // both adds in flight together, then resolved
       const uint64_t o0 = counter_add(p.wl.ctr + pend_q0);
       const uint64_t o1 = npend > 1 ? counter_add(p.wl.ctr + pend_q1) : 0;
-      if (counter_resolve(p.wl.ctr + pend_q0, o0) == pend_need0) {
-        counter_reset(p.wl.ctr + pend_q0);
+      if (counter_resolve(p.wl.ctr + pend_q0, o0, p.wl.ctr_tag) == pend_need0) {
+        counter_reset(p.wl.ctr + pend_q0, p.wl.ctr_tag);
         last |= 1;
       }
-      if (npend > 1 && counter_resolve(p.wl.ctr + pend_q1, o1) == pend_need1) {
-        counter_reset(p.wl.ctr + pend_q1);
+      if (npend > 1 && counter_resolve(p.wl.ctr + pend_q1, o1, p.wl.ctr_tag) == pend_need1) {
+        counter_reset(p.wl.ctr + pend_q1, p.wl.ctr_tag);
         last |= 2;
       }
       s_last = last;

@@ -134,8 +134,9 @@ def test_oam_128k_full_size():
         b, kh = divmod(pr, w.KH)
         check_pair(oracle.oam_scores(p, b, kh, 1.0, 1e-6), sc[pr], idx[pr], nk[pr], w.top_k)
     qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
-    out, lse = pkg.attn_decode_splitkv(qd, to_dev(k), to_dev(v), dev_geom(g), w.G, token_idx=to_dev(idx),
-                                       n_idx=to_dev(nk), split_tokens=w.split_tokens)
+    lse = torch.empty((w.B, w.QH), dtype=torch.float32, device=DEV)
+    out, _ = pkg.attn_decode_splitkv(qd, to_dev(k), to_dev(v), dev_geom(g), w.G, token_idx=to_dev(idx),
+                                     n_idx=to_dev(nk), lse=lse, split_tokens=w.split_tokens)
     torch.cuda.synchronize()
     pk = problem(w, q, k, v, g, tok_idx=idx.reshape(-1), n_idx=nk, idx_stride=w.top_k)
     ref, ref_lse = oracle_all_rows(pk)
@@ -275,8 +276,9 @@ def test_oam_int8_128k_full_size():
     del k, v
     idx, nk, sc = run_oam_int8(w, q, g, kc, ks, vc, vs, 64, w.top_k, True)
     qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
-    out, lse = pkg.attn_decode_splitkv(qd, kc, vc, dev_geom(g), w.G, token_idx=idx, n_idx=nk, k_scale=ks,
-                                       k_part_tokens=64, v_scale=vs, split_tokens=w.split_tokens)
+    lse = torch.empty((w.B, w.QH), dtype=torch.float32, device=DEV)
+    out, _ = pkg.attn_decode_splitkv(qd, kc, vc, dev_geom(g), w.G, token_idx=idx, n_idx=nk, k_scale=ks,
+                                     k_part_tokens=64, v_scale=vs, lse=lse, split_tokens=w.split_tokens)
     torch.cuda.synchronize()
     idx_h, nk_h = idx.cpu().numpy(), nk.cpu().numpy()
     p = problem(w, q, kc.cpu().numpy(), vc.cpu().numpy(), g, v_scale=vs, **kk)
@@ -374,8 +376,9 @@ def test_block_select_128k_full_size():
     kd, vd = to_dev(k), to_dev(v)
     geom = dev_geom(g)
     idx, nk = pkg.oam_score_topk(qd, kd, geom, w.G, n, v=vd, beta=0.0, block_tokens=bt)
-    out, lse = pkg.attn_decode_splitkv(qd, kd, vd, geom, w.G, token_idx=idx, n_idx=nk,
-                                       split_tokens=w.split_tokens)
+    lse = torch.empty((w.B, w.QH), dtype=torch.float32, device=DEV)
+    out, _ = pkg.attn_decode_splitkv(qd, kd, vd, geom, w.G, token_idx=idx, n_idx=nk, lse=lse,
+                                     split_tokens=w.split_tokens)
     torch.cuda.synchronize()
     idx_h, nk_h = idx.cpu().numpy(), nk.cpu().numpy()
     p = problem(w, q, k, v, g)
