@@ -28,7 +28,9 @@
  * Conventions for every entry point:
  *  - Pointers are DEVICE pointers unless a comment says otherwise.  The caller
  *    owns every buffer, including workspaces; the library never allocates or
- *    frees device memory and keeps no pointer after a call returns.
+ *    frees device memory and keeps no pointer after a call returns (the one
+ *    exception: attn_decode_splitkv_noalloc's static scratch array, which the
+ *    library's code object holds on each GPU).
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
  *    default stream).  Outputs are valid once the stream reaches that point.
  *  - Arguments are validated on the host before anything is enqueued; a
@@ -36,8 +38,9 @@
  *    launch returns ATTN_ERR_HIP.  attn_last_error() describes the most
  *    recent failure of the calling thread.  No C++ exception crosses the ABI.
  *  - Calls hold no global state besides a per-device cache of the compute
- *    unit count; they are safe to call from several host threads.  Calls
- *    that share a workspace must be ordered on one stream.
+ *    unit count (and, for attn_decode_splitkv_noalloc, of its scratch
+ *    address); they are safe to call from several host threads.  Calls that
+ *    share a workspace must be ordered on one stream.
  *  - Non-finite inputs give undefined (but memory-safe) results.
  *  - Element types: ATTN_F32 = IEEE fp32, ATTN_BF16 = bfloat16,
  *    ATTN_I8 = int8 codes with fp32 scales.
@@ -255,6 +258,33 @@ attn_status attn_decode_splitkv(const attn_decode_args *args, attn_stream_t stre
  * Same arguments and errors.
  */
 attn_status attn_decode_splitkv_profiled(const attn_decode_args *args, attn_stream_t stream, void *const events[3]);
+
+/*
+ * attn_decode_splitkv for callers that cannot allocate device memory: code
+ * under HIP graph capture, serving loops that must not call hipMalloc, and
+ * harnesses that forbid it.  The partials and arrival counters live in a
+ * static device array of the library, ATTN_NOALLOC_SCRATCH_BYTES (64 MiB) on
+ * each GPU it runs on, held until the process ends; the call allocates
+ * nothing.  The caller still passes q, k, v, out, lse and the rest of args;
+ * args->workspace must be NULL and args->workspace_bytes 0.
+ *  - Arguments whose attn_decode_workspace_size exceeds the array return
+ *    ATTN_ERR_WORKSPACE_TOO_SMALL and enqueue nothing (the 128K-token bf16
+ *    step of 4 sequences x 8 KV heads needs about 4.4 MB, 32 sequences of up
+ *    to 128K tokens about 35 MB).
+ *  - Every call on one GPU shares that GPU's array, which keeps the last
+ *    call's contents.  Nothing in it needs clearing: partials are written
+ *    before they are read, and the counters follow the rule described under
+ *    attn_decode_args.workspace.  Calls that overlap on one GPU (several
+ *    streams, or host threads without ordering) race on the array and give
+ *    undefined results: order them on one stream.
+ *  - The first call on a device looks up that device's copy of the array
+ *    (hipGetSymbolAddress, with the device current); a failure there
+ *    returns ATTN_ERR_HIP.
+ * Results are those of attn_decode_splitkv with the same arguments, bit for
+ * bit (same kernels, same work split).
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+attn_status attn_decode_splitkv_noalloc(const attn_decode_args *args, attn_stream_t stream);
 
 /*
  * Log-sum-exp merge of partial triples ("优化稀疏注意力中的令牌丢弃机制" §5,

@@ -19,7 +19,9 @@ from ._lib import ATTN_BF16, ATTN_F32, ATTN_I8, AttnError  # noqa: F401
 from ._lib import ATTN_QUANT_EXACT as QUANT_EXACT, ATTN_QUANT_ROW as QUANT_ROW  # noqa: F401
 from ._lib import ATTN_QUANT_STATIC as QUANT_STATIC  # noqa: F401
 
-__all__ = ["KVGeometry", "attn_decode_splitkv", "attn_merge_lse", "kv_quant_int8", "oam_value_lognorm",
+NOALLOC_SCRATCH_BYTES = 64 << 20  # attn_decode_splitkv_noalloc's static scratch per GPU
+
+__all__ = ["KVGeometry", "attn_decode_splitkv", "attn_decode_splitkv_noalloc", "attn_merge_lse", "kv_quant_int8", "oam_value_lognorm",
            "oam_score_topk", "decode_workspace_size", "oam_workspace_size", "prepare_decode", "util_copy",
            "util_read", "decode_split_tokens", "AttnError"]
 
@@ -128,13 +130,14 @@ def decode_split_tokens(args: _lib.AttnDecodeArgs) -> int:
 class PreparedDecode:
     """A validated argument block; calling it enqueues one decode step on a stream."""
 
-    def __init__(self, args: _lib.AttnDecodeArgs, keep):
+    def __init__(self, args: _lib.AttnDecodeArgs, keep, noalloc: bool = False):
         self.args = args
         self._keep = keep
-        self._fn = _lib.load().attn_decode_splitkv
+        self._name = "attn_decode_splitkv_noalloc" if noalloc else "attn_decode_splitkv"
+        self._fn = getattr(_lib.load(), self._name)
 
     def __call__(self, stream=None):
-        _lib.check(self._fn(ctypes.byref(self.args), _stream(stream)), "attn_decode_splitkv")
+        _lib.check(self._fn(ctypes.byref(self.args), _stream(stream)), self._name)
 
     @property
     def split_tokens(self) -> int:
@@ -155,14 +158,16 @@ def prepare_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, geom: KVGe
                    token_idx: Optional[torch.Tensor] = None, n_idx: Optional[torch.Tensor] = None,
                    idx_stride: Optional[int] = None, softmax_scale: float = 0.0, split_tokens: int = 0,
                    q_quant: int = 0, q_scale: float = 0.0, q_rows: int = 1, fixed_splits: int = 0,
-                   workspace: Optional[torch.Tensor] = None) -> PreparedDecode:
+                   workspace: Optional[torch.Tensor] = None, noalloc: bool = False) -> PreparedDecode:
     """Build (and allocate outputs/workspace for) one ``attn_decode_splitkv`` call.
 
     With int8 KV, ``k_part_tokens=0`` selects one per-tensor K scale (``k_scale[0]``) and
     ``q_quant`` (QUANT_EXACT / QUANT_ROW / QUANT_STATIC, with ``q_scale``) how the query is
     quantised.  ``q_rows`` > 1 is a multi-row (speculative) step: q, out and lse are
     [B, q_rows, KH*G, ...] and row r attends to the first L - (q_rows - 1) + r tokens.
-    ``fixed_splits`` > 0 selects the unbalanced schedule (every (b, kh) in that many splits)."""
+    ``fixed_splits`` > 0 selects the unbalanced schedule (every (b, kh) in that many splits).
+    ``noalloc`` calls ``attn_decode_splitkv_noalloc`` instead, which takes no workspace (the
+    library's static scratch holds the partials); outputs not given are still allocated here."""
     dev = q.device
     QH = geom.KH * G
     if out is None:
@@ -175,12 +180,16 @@ def prepare_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, geom: KVGe
         idx_stride = token_idx.shape[-1]
     a = _decode_args(q, k, v, geom, G, out, lse, k_scale, k_part_tokens, k_scale_stride, v_scale, token_idx, n_idx,
                      idx_stride or 0, softmax_scale, split_tokens, None, q_quant, q_scale, q_rows, fixed_splits)
-    need = decode_workspace_size(a)
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    a.workspace = workspace.data_ptr()
-    a.workspace_bytes = workspace.numel()
-    p = PreparedDecode(a, [q, k, v, geom, out, lse, k_scale, token_idx, n_idx, workspace])
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc takes no workspace")
+    else:
+        need = decode_workspace_size(a)
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel()
+    p = PreparedDecode(a, [q, k, v, geom, out, lse, k_scale, token_idx, n_idx, workspace], noalloc)
     p.out, p.lse, p.workspace = out, lse, workspace
     return p
 
@@ -188,6 +197,14 @@ def prepare_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, geom: KVGe
 def attn_decode_splitkv(q, k, v, geom: KVGeometry, G: int, stream=None, **kw):
     """Split-KV decode attention; returns (out [B, KH*G, D], lse or None).  See prepare_decode for options."""
     p = prepare_decode(q, k, v, geom, G, **kw)
+    p(stream)
+    return p.out, p.lse
+
+
+def attn_decode_splitkv_noalloc(q, k, v, geom: KVGeometry, G: int, stream=None, **kw):
+    """attn_decode_splitkv through the entry point that takes no workspace (the library's static
+    scratch, NOALLOC_SCRATCH_BYTES per GPU); pass ``out`` (and ``lse``) to allocate nothing here either."""
+    p = prepare_decode(q, k, v, geom, G, noalloc=True, **kw)
     p(stream)
     return p.out, p.lse
 

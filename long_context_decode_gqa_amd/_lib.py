@@ -42,6 +42,7 @@ SIGNATURES = {
     "attn_decode_split_tokens": ([ctypes.POINTER(AttnDecodeArgs), ctypes.POINTER(i32)], i32),
     "attn_decode_splitkv": ([ctypes.POINTER(AttnDecodeArgs), vp], i32),
     "attn_decode_splitkv_profiled": ([ctypes.POINTER(AttnDecodeArgs), vp, ctypes.POINTER(vp * 3)], i32),
+    "attn_decode_splitkv_noalloc": ([ctypes.POINTER(AttnDecodeArgs), vp], i32),
     "attn_merge_lse": ([vp, vp, vp, vp, i32, i32, i32, vp, vp, vp], i32),
     "kv_quant_int8_workspace_size": ([ctypes.POINTER(AttnKvGeom), i32, ctypes.POINTER(sz)], i32),
     "kv_quant_int8": ([ctypes.POINTER(AttnKvGeom), vp, i32, i32, vp, vp, vp, sz, vp], i32),
