@@ -173,12 +173,14 @@ typedef struct {
  *               bytes, 256-byte aligned; holds the partials and, for
  *               bf16/int8 KV, one arrival counter per (b, kh).  It needs no
  *               initialisation: a counter word carries a 40-bit tag that
- *               changes with every call in the process, every call leaves
- *               its counters at zero arrivals, and a call's first arrival
- *               takes over a word without its tag (whatever an earlier call
+ *               changes with every call on the same counter array, a call
+ *               leaves its counters at zero arrivals under the tag of the
+ *               next call on that array, and a call's first arrival takes
+ *               over a word without its own tag (whatever an earlier call
  *               left, finished or cut off, or other data, which matches a
- *               tag with probability 2^-40 per word).  Calls that run at the
- *               same time on one workspace race
+ *               tag with probability 2^-40 per word).  The library keeps the
+ *               tags of the last 64 counter arrays on the host.  Calls that
+ *               run at the same time on one workspace race
  *   out         [B][KH*G][D] in out_dtype (ATTN_F32 or ATTN_BF16)
  *   lse         optional fp32 [B][KH*G]: natural-log log-sum-exp of the
  *               scaled scores (-inf for a sequence with no tokens)

@@ -266,12 +266,28 @@ attn_status attn_decode_split_tokens(const attn_decode_args *args, int32_t *spli
 
 namespace lcdg {
 
-// The tag of one call's arrival counters: a 40-bit value that changes with
-// every call in the process (2^40 calls before one repeats), offset so that
-// small integers and zeroed memory do not carry it.
-static uint64_t next_counter_tag() {
-  static std::atomic<uint64_t> seq{0};
-  return (0x5A17C0DE42ull + seq.fetch_add(1, std::memory_order_relaxed)) & ((uint64_t(1) << 40) - 1);
+// The 40-bit tag of one call's arrival counters.  Each counter array (a
+// workspace address and layout) gets the tag after the one its previous call
+// used, which is the tag that call's last arrivals left in the words, so the
+// common case costs one atomic add per arrival; an array not seen recently
+// (64 remembered, replaced in turn) gets a fresh tag from a scrambled
+// sequence, and its first arrivals take the words over.  Tags change with
+// every call, so words left by any earlier call are never mistaken for live
+// counts of this one.
+static uint64_t counter_tag_for(const void *ctr) {
+  constexpr uint64_t kMask = (uint64_t(1) << 40) - 1;
+  static std::mutex mu;
+  static const void *addr[64] = {nullptr};
+  static uint64_t tag[64];
+  static unsigned victim = 0;
+  static uint64_t fresh = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < 64; ++i)
+    if (addr[i] == ctr) return tag[i] = (tag[i] + 1) & kMask;
+  const unsigned i = victim++ % 64;
+  addr[i] = ctr;
+  tag[i] = ((++fresh) * 0x9E3779B97F4A7C15ull >> 24) & kMask;
+  return tag[i];
 }
 
 // One decode call on a validated workspace: `workspace` / `workspace_bytes`
@@ -332,7 +348,7 @@ attn_status decode_run(const attn_decode_args *a, void *workspace, size_t worksp
   p.wl.l_part = reinterpret_cast<float *>(ws + L.l);
   p.wl.o_part = reinterpret_cast<float *>(ws + L.o);
   p.wl.ctr = L.mfma ? reinterpret_cast<uint64_t *>(ws + L.ctr) : nullptr;
-  p.wl.ctr_tag = next_counter_tag();
+  p.wl.ctr_tag = L.mfma ? counter_tag_for(p.wl.ctr) : 0;
   p.out_dtype = a->out_dtype;
   p.out = a->out;
   p.lse = a->lse;

@@ -93,10 +93,11 @@ struct WorkList {
   float *o_part;             // [max partials][D]
   // Merge inside the matrix-core decode launch: one arrival counter per lane.
   // A counter word holds (ctr_tag << 24) | arrivals, ctr_tag being a 40-bit
-  // tag the host draws anew for every call.  Every call leaves its counters
-  // at zero arrivals, and a word without this call's tag (left by an earlier
-  // call, finished or cut off, or other data) is taken over by the call's
-  // first arrival, so the workspace needs no clearing.
+  // tag that changes with every call on the same counter array.  A call's
+  // last arrivals leave their words at zero arrivals under the next call's
+  // tag, and a word without this call's tag (left by an earlier call,
+  // finished or cut off, or other data) is taken over by the call's first
+  // arrival, so the workspace needs no clearing.
   uint64_t *ctr;             // [lanes] (matrix-core decode)
   uint64_t ctr_tag;          // < 2^40
 };
@@ -313,9 +314,10 @@ __device__ __forceinline__ int counter_resolve(uint64_t *c, uint64_t old, uint64
   }
 }
 
-// The last arrival of a call leaves the counter at zero arrivals.
+// The last arrival of a call leaves the counter at zero arrivals under the
+// next tag, the one the next call on the same counter array uses.
 __device__ __forceinline__ void counter_reset(uint64_t *c, uint64_t tag) {
-  __hip_atomic_store(c, tag << 24, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(c, ((tag + 1) & ((1ull << 40) - 1)) << 24, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Wait until every vector-memory access this wave issued has completed; for
