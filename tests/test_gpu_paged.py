@@ -14,7 +14,7 @@ import torch
 import long_context_decode_gqa_amd as pkg
 import oracle
 import synth
-from gpu_helpers import DEV, dev_geom, log_case, problem, to_dev
+from gpu_helpers import DEV, dev_geom, log_case, oracle_all_rows, problem, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -79,7 +79,8 @@ def run(qd, k, v, geom, G, B, QH, **kw):
 @pytest.mark.parametrize("D", [128, 64])
 def test_paged_equals_contiguous_bit_exact(P, layout, kv, D):
     lens = np.array([1, 700, 4096, 2049, 0, 33], np.int32)
-    w = synth.workload("gqa32k", B=len(lens), KH=2, G=8, D=D, lens=lens, layout="token_major", seed=130 + P)
+    # the contiguous cache in the pool's row order (any order gives the same bits)
+    w = synth.workload("gqa32k", B=len(lens), KH=2, G=8, D=D, lens=lens, layout=layout, seed=130 + P)
     q, k, v, g = synth.generate(w)
     log_case(f"paged P={P} {layout} {kv} D={D}")
     qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
@@ -111,22 +112,42 @@ def test_paged_equals_contiguous_bit_exact(P, layout, kv, D):
 
 
 def test_paged_128k_full_size_equals_contiguous():
-    """The 128K bf16 workload (4 x 8 KV heads x 131072 tokens) in a scrambled pool of 64-token
-    token-major pages, in the benchmark's launch configuration: bit-identical to the contiguous cache."""
+    """The 128K bf16 workload (4 x 8 KV heads x 131072 tokens) in scrambled pools of 64-token
+    pages, in the benchmark's launch configuration: head-major pages, token-major pages and the
+    same data packed token-major all bit-identical to the dense cache, and every row of the
+    token-major result against the oracle."""
     w = synth.workload("dense128k")
     q, k, v, g = synth.generate(w)
     log_case("paged 128k full size")
     qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
-    out_c, lse_c = run(qd, to_dev(k), to_dev(v), dev_geom(g), w.G, w.B, w.QH, split_tokens=w.split_tokens)
     P = 64
-    kp, table, st, sh, ps = make_pool(k, g, P, "token_major", 11, np.uint16(0x7FC0))
-    del k
-    vp, _, _, _, _ = make_pool(v, g, P, "token_major", 11, np.uint16(0x7FC0))
-    del v
+    out_c, lse_c = run(qd, to_dev(k), to_dev(v), dev_geom(g), w.G, w.B, w.QH, split_tokens=w.split_tokens)
+    kp, table, st, sh, ps = make_pool(k, g, P, "head_major", 11, np.uint16(0x7FC0))
+    vp, _, _, _, _ = make_pool(v, g, P, "head_major", 11, np.uint16(0x7FC0))
     out_p, lse_p = run(qd, to_dev(kp), to_dev(vp), paged_geom(g, table, P, st, sh, ps), w.G, w.B, w.QH,
                        split_tokens=w.split_tokens)
+    del kp, vp
     np.testing.assert_array_equal(out_p, out_c)
     np.testing.assert_array_equal(lse_p, lse_c)
+    # token-major: the same cache packed [B*L][KH][D], and in token-major pages
+    L = int(w.lens[0])
+    wt = synth.workload("dense128k", layout="token_major")
+    gt = wt.geometry()
+    kt = np.ascontiguousarray(k.reshape(w.B, w.KH, L, w.D).transpose(0, 2, 1, 3)).reshape(-1)
+    vt = np.ascontiguousarray(v.reshape(w.B, w.KH, L, w.D).transpose(0, 2, 1, 3)).reshape(-1)
+    out_t, lse_t = run(qd, to_dev(kt), to_dev(vt), dev_geom(gt), w.G, w.B, w.QH, split_tokens=w.split_tokens)
+    kp, table, st, sh, ps = make_pool(k, g, P, "token_major", 11, np.uint16(0x7FC0))
+    vp, _, _, _, _ = make_pool(v, g, P, "token_major", 11, np.uint16(0x7FC0))
+    out_p, lse_p = run(qd, to_dev(kp), to_dev(vp), paged_geom(g, table, P, st, sh, ps), w.G, w.B, w.QH,
+                       split_tokens=w.split_tokens)
+    del kp, vp, kt, vt
+    np.testing.assert_array_equal(out_t, out_c)
+    np.testing.assert_array_equal(lse_t, lse_c)
+    np.testing.assert_array_equal(out_p, out_c)
+    np.testing.assert_array_equal(lse_p, lse_c)
+    ref, ref_lse = oracle_all_rows(problem(w, q, k, v, g))
+    assert np.abs(out_p.reshape(-1, w.D) - ref).max() <= 2e-3
+    assert np.abs(lse_p.reshape(-1) - ref_lse).max() <= 1e-3
 
 
 # --- the rest of the path over a paged cache: quantisation when rows are written, the cached
