@@ -304,6 +304,51 @@ def test_workspace_needs_no_clearing(fill):
     assert np.array_equal(a_out, p.out.cpu().numpy()) and np.array_equal(a_lse, lse.cpu().numpy())
 
 
+def test_interleaved_calls_sharing_one_workspace():
+    """Two decode problems of different shapes take turns on one workspace tensor (their counter
+    arrays sit at different offsets of it and the partials of one overwrite the other's), each
+    several times, with the profiled entry point in between: every call reproduces its first
+    result bit for bit, and the first results match the oracle."""
+    probs = []
+    for lens, KH, split, seed in ((np.array([5000, 70, 2049], np.int32), 2, 256, 181),
+                                  (np.array([900, 40000], np.int32), 4, 512, 182)):
+        w = synth.workload("gqa32k", B=len(lens), KH=KH, G=8, lens=lens, layout="token_major", seed=seed)
+        q, k, v, g = synth.generate(w)
+        probs.append((w, q, k, v, g, split))
+    need = 0
+    preps = []
+    for w, q, k, v, g, split in probs:
+        qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
+        lse = torch.empty((w.B, w.QH), dtype=torch.float32, device=DEV)
+        preps.append((qd, to_dev(k), to_dev(v), dev_geom(g), lse))
+    for (w, *_rest, split), (qd, kd, vd, geom, lse) in zip(probs, preps):
+        a = pkg.prepare_decode(qd, kd, vd, geom, w.G, lse=lse, split_tokens=split)
+        need = max(need, a.workspace.numel())
+    ws = torch.full((need,), 0x5A, dtype=torch.uint8, device=DEV)
+    calls = [pkg.prepare_decode(qd, kd, vd, geom, w.G, lse=lse, split_tokens=split, workspace=ws)
+             for (w, *_rest, split), (qd, kd, vd, geom, lse) in zip(probs, preps)]
+    first = []
+    for i, c in enumerate(calls):
+        log_case(f"shared workspace, problem {i}")
+        c()
+        torch.cuda.synchronize()
+        first.append((c.out.cpu().numpy().copy(), preps[i][4].cpu().numpy().copy()))
+    for (w, q, k, v, g, _), (o, l) in zip(probs, first):
+        pr = problem(w, q, k, v, g)
+        ref, ref_lse = oracle.attention_rows(pr, oracle.all_rows(pr), nthreads=8)
+        check(o.reshape(w.B * w.QH, w.D), l.reshape(-1), ref, ref_lse)
+    events = [None, None, None]
+    for r in range(6):
+        i = r % 2
+        if r == 3:
+            calls[i].profiled(events)
+        else:
+            calls[i]()
+        torch.cuda.synchronize()
+        assert np.array_equal(calls[i].out.cpu().numpy(), first[i][0]), f"call {r} (problem {i})"
+        assert np.array_equal(preps[i][4].cpu().numpy(), first[i][1]), f"call {r} (problem {i})"
+
+
 def test_many_workers_per_sequence_and_whole_sequences_per_worker():
     """split_tokens = 32 cuts one long sequence over hundreds of workers (hundreds of partials
     folded by the last arrival), while a batch of short sequences puts several whole sequences in
