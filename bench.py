@@ -556,8 +556,8 @@ def main():
                     help="only run the library's plain copy kernel over this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU sharding of this path is not built", file=sys.stderr)
+        print(f"bench.py: the decode path runs on one GPU only (asked for --gpus {args.gpus}); "
+              "its sharding over several GPUs is not implemented", file=sys.stderr)
         sys.exit(2)
 
     import torch

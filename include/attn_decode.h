@@ -165,8 +165,8 @@ typedef struct {
  *               decode worker, each range at least split_tokens positions
  *               long (fewer workers when there is less work); a (b, kh)
  *               then spans at most ceil(L_b / split_tokens) + 1 ranges, each
- *               giving one partial.  Default 4096 (128 kept tokens for int8
- *               or 256 for bf16 with token_idx, up to 1024 for long lists).
+ *               giving one partial.  Default 4096 (with token_idx 512 kept
+ *               tokens, up to 1024 for long lists).
  *               fp32 KV: chunks of split_tokens positions, default 256.
  *               attn_decode_split_tokens reports the choice
  *   workspace   caller-owned scratch of at least attn_decode_workspace_size()

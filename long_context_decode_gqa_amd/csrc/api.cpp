@@ -164,12 +164,13 @@ attn_status plan_decode(const attn_decode_args *a, DecodeLayout *L) {
   } else if (!mfma) {
     L->split = 256;
   } else if (a->token_idx) {
-    // Gathered runs are short and a worker's fixed costs weigh more: at
-    // least 256 (bf16) or 128 (int8) and at most 1024 kept tokens per
-    // worker (4096 kept tokens per pair, bf16: 2048 two-tile workers took
-    // 26.6 us, 512 eight-tile workers 23.3 us, 256 sixteen-tile workers
-    // 26.7 us; int8: 27.6, 24.8 with four-tile workers, 26.1 us).
-    const int64_t ct = std::min<int64_t>(std::max<int64_t>(max_tiles / 2048, a->kv_dtype == ATTN_I8 ? 4 : 8), 32);
+    // Gathered runs are short and a worker's fixed costs (staging its index
+    // list and query, the combine, a partial) weigh more: at least 512 and
+    // at most 1024 kept tokens per four-wave worker (32 pairs x 4096 kept
+    // tokens of 128K, bf16: 256 per worker 26.3 us, 512 24.5 us, 1024
+    // 26.2 us, 2048 37.9 us; int8: 128 26.4 us, 256 26.3, 512 25.7, 1024
+    // 28.7 us).
+    const int64_t ct = std::min<int64_t>(std::max<int64_t>(max_tiles / 256, 16), 32);
     L->split = (int32_t)(32 * ct);
   } else {
     // Every wave streams at least 32 tiles when there are enough: each

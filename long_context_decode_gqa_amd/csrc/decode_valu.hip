@@ -3,9 +3,10 @@
 // partial format as the matrix-core kernel; used for fp32 inputs.
 //
 // One 256-thread workgroup per worker.  Each tile of a segment (64
-// positions, 32 for head sizes above 128) is staged in LDS with coalesced 16-byte loads (K transposed, so the score
-// loop reads consecutive tokens across lanes), and the next two tiles' loads
-// are in flight in registers while the current one is computed.  The tile then
+// positions, 32 for head sizes above 128) is staged in LDS with coalesced
+// 16-byte loads (K rows padded by 16 bytes, so lanes reading 16-byte pieces
+// of different rows hit different banks), and the next two tiles' loads are
+// in flight in registers while the current one is computed.  The tile then
 // follows the online softmax of the Flash Attention block pseudo-code
 // ("注意力优化（Attention Optimization）"): scores -> new running max ->
 // rescale (alpha) -> probabilities -> O = alpha*O + P V, in natural-log
@@ -48,10 +49,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int NP = 16 * TT / 256;                // score passes over the 16 heads of a block
   constexpr int KO = 16 * DC / 256;                // (head, channel) outputs per thread
   constexpr int kVChunks = TT * DC / 4 / 256;      // 16-byte loads per thread for K (and V) of a tile
-  __shared__ float s_q[16][DC];                    // q * softmax_scale
-  __shared__ float s_kt[DC][TT + 1];               // K^T of the tile
+  constexpr int KR = DC + 4;                       // padded K row (floats)
+  __shared__ __attribute__((aligned(16))) float s_q[16][DC];  // q * softmax_scale
+  __shared__ __attribute__((aligned(16))) float s_k[TT][KR];  // K rows of the tile
   __shared__ __attribute__((aligned(16))) float s_v[TT][DC];
-  __shared__ float s_p[16][TT];                    // probabilities (0 past the segment)
+  __shared__ __attribute__((aligned(16))) float s_p[16][TT];  // probabilities (0 past the segment)
   __shared__ float s_alpha[16], s_m[16], s_l[16];
 
   const int tid = threadIdx.x;
@@ -126,8 +128,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int c = tid + 256 * j, r = c / cpr;
         if (r < TT) {
           const int d = 4 * (c - r * cpr);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s_kt[d + i][r] = rk[j][i];
+          *(f32x4_t *)&s_k[r][d] = rk[j];
           *(f32x4_t *)&s_v[r][d] = rv[j];
         }
       }
@@ -165,13 +166,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int h = 0; h < NP; ++h) {
           const int g = sg + (256 / TT) * h;
           if (g < gcount) {  // uniform over the lane group
-            float acc = 0.f;
-            int d = 0;
-            for (; d + 8 <= D; d += 8) {
+            // 16-byte LDS reads: the head's query (one address for the
+            // group) and this lane's K row
+            const f32x4_t *qr = (const f32x4_t *)&s_q[g][0];
+            const f32x4_t *kr = (const f32x4_t *)&s_k[si][0];
+            f32x4_t a4 = {0.f, 0.f, 0.f, 0.f};
+            int d4 = 0;
+            for (; d4 + 4 <= cpr; d4 += 4) {
 #pragma unroll
-              for (int u = 0; u < 8; ++u) acc += s_q[g][d + u] * s_kt[d + u][si];
+              for (int u = 0; u < 4; ++u) a4 += qr[d4 + u] * kr[d4 + u];
             }
-            for (; d < D; ++d) acc += s_q[g][d] * s_kt[d][si];
+            for (; d4 < cpr; ++d4) a4 += qr[d4] * kr[d4];
+            const float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
             const float s = si < n ? acc : NEG_INF;
             const float m_new = fmaxf(m_run[h], group_max<TT>(s));  // finite: the tile has a token
             const float e = si < n ? expf(s - m_new) : 0.f;
@@ -191,7 +197,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const int g = e / D, d = e - g * D;
             float acc = o[k] * s_alpha[g];
 #pragma unroll
-            for (int i = 0; i < TT; ++i) acc += s_p[g][i] * s_v[i][d];
+            for (int i = 0; i < TT; i += 4) {
+              const f32x4_t pp = *(const f32x4_t *)&s_p[g][i];
+#pragma unroll
+              for (int u = 0; u < 4; ++u) acc += pp[u] * s_v[i + u][d];
+            }
             o[k] = acc;
           }
         }

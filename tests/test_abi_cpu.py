@@ -93,9 +93,10 @@ I8 = dict(kv_dtype=_lib.ATTN_I8, k_scale=FAKE, k_part_tokens=64, k_scale_stride=
     (dict(g_B=1, g_KH=1, g_max_seq_len=4096), 4096),
     (dict(g_B=4, g_max_seq_len=131072, g_seq_offset=None, g_block_table=FAKE, g_page_tokens=32,
           g_table_stride=4096, g_page_stride=32 * 8 * 128, **I8), 4096),
-    # kept-token lists of 4096: at least 256 (bf16) or 128 (int8) kept tokens per worker
-    (dict(g_B=4, g_max_seq_len=131072, token_idx=FAKE, n_idx=FAKE, idx_stride=4096), 256),
-    (dict(g_B=4, g_max_seq_len=131072, token_idx=FAKE, n_idx=FAKE, idx_stride=4096, **I8), 128),
+    # kept-token lists: at least 512 and at most 1024 kept tokens per worker
+    (dict(g_B=4, g_max_seq_len=131072, token_idx=FAKE, n_idx=FAKE, idx_stride=4096), 512),
+    (dict(g_B=4, g_max_seq_len=131072, token_idx=FAKE, n_idx=FAKE, idx_stride=4096, **I8), 512),
+    (dict(g_B=4, g_max_seq_len=131072, token_idx=FAKE, n_idx=FAKE, idx_stride=16384), 1024),
     # fp32 KV (vector-ALU decode): chunks of 256
     (dict(q_dtype=_lib.ATTN_F32, kv_dtype=_lib.ATTN_F32), 256),
     # a given split is kept
