@@ -175,12 +175,16 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// Tiles of all lanes (wave-wide; every thread of the wave gets the total).
-__device__ __forceinline__ int wave_total_tiles(const DecodeParams &p) {
-  const int nl = p.B * p.KH * p.lpp;
+// Tiles of all nl lanes (wave-wide; every thread of the wave gets the total),
+// tiles(q) giving lane q's tile count.
+template <class F>
+__device__ __forceinline__ int wave_total_tiles_of(int nl, F tiles) {
   int acc = 0;
-  for (int q = threadIdx.x & 63; q < nl; q += 64) acc += lane_tiles(p, q);
+  for (int q = threadIdx.x & 63; q < nl; q += 64) acc += tiles(q);
   return __builtin_amdgcn_readfirstlane(wave_sum_int(acc));
+}
+__device__ __forceinline__ int wave_total_tiles(const DecodeParams &p) {
+  return wave_total_tiles_of(p.B * p.KH * p.lpp, [&](int q) { return lane_tiles(p, q); });
 }
 
 // The lane holding tile t (0 <= t < total) and that lane's first tile and tile
@@ -188,13 +192,13 @@ __device__ __forceinline__ int wave_total_tiles(const DecodeParams &p) {
 struct LaneHit {
   int q, t0, nt;
 };
-__device__ __forceinline__ LaneHit wave_find_lane(const DecodeParams &p, int t) {
+template <class F>
+__device__ __forceinline__ LaneHit wave_find_lane_of(int nl, int t, F tiles) {
   const int lane = threadIdx.x & 63;
-  const int nl = p.B * p.KH * p.lpp;
   LaneHit h = {0, 0, 0};
   int run = 0;
   for (int base = 0; base < nl; base += 64) {
-    const int nt = lane_tiles(p, base + lane);
+    const int nt = base + lane < nl ? tiles(base + lane) : 0;
     const int incl = wave_incl_scan(nt);
     const int excl = run + incl - nt;
     const unsigned long long own = __ballot(nt > 0 && excl <= t && t < excl + nt);
@@ -209,16 +213,22 @@ __device__ __forceinline__ LaneHit wave_find_lane(const DecodeParams &p, int t) 
   }
   return h;
 }
+__device__ __forceinline__ LaneHit wave_find_lane(const DecodeParams &p, int t) {
+  return wave_find_lane_of(p.B * p.KH * p.lpp, t, [&](int q) { return lane_tiles(p, q); });
+}
 
 // The lane after h that has tiles (its first tile follows h's last).
-__device__ __forceinline__ LaneHit next_lane(const DecodeParams &p, LaneHit h) {
-  const int nl = p.B * p.KH * p.lpp;
+template <class F>
+__device__ __forceinline__ LaneHit next_lane_of(int nl, LaneHit h, F tiles) {
   LaneHit n = {h.q, h.t0 + h.nt, 0};
   while (n.nt == 0 && n.q + 1 < nl) {
     ++n.q;
-    n.nt = __builtin_amdgcn_readfirstlane(lane_tiles(p, n.q));
+    n.nt = __builtin_amdgcn_readfirstlane(tiles(n.q));
   }
   return n;
+}
+__device__ __forceinline__ LaneHit next_lane(const DecodeParams &p, LaneHit h) {
+  return next_lane_of(p.B * p.KH * p.lpp, h, [&](int q) { return lane_tiles(p, q); });
 }
 
 // Workers that get a range: at most one per chunk's worth of tiles, so every

@@ -168,6 +168,15 @@ decode_mfma_kernel(DecodeParams p) {
   __shared__ float s_cm[WPG * kCols], s_cl[WPG * kCols];
   __shared__ f32x4_t s_co[WPG * kCols * NQ];
   __shared__ int s_last;
+  // The lane table: each lane's positions and each sequence's clamped length
+  // and offset, staged once at the start with one round of loads, so the
+  // work split, the lane walk and every run's set-up read LDS instead of a
+  // chain of dependent global loads (worth several microseconds before the
+  // first tile's loads could issue).  Batches with more than NT lanes read
+  // them from global memory instead.
+  __shared__ int s_np[NT];
+  __shared__ int s_len[NT];
+  __shared__ int64_t s_off[NT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -218,7 +227,31 @@ decode_mfma_kernel(DecodeParams p) {
     return __builtin_amdgcn_make_buffer_rsrc((void *)(p.wl.l_part + pe0), (short)0, ne * 4, 0x00020000);
   };
 
-  const int T = wave_total_tiles(p);
+  const int nl = p.B * p.KH;
+  const bool cached = nl <= NT;  // then B <= NT as well
+  if (cached) {
+    // thread i: lane i's positions, and sequence i's length and offset; all
+    // loads of the worker in flight together
+    int np = 0, len = 0;
+    int64_t off = 0;
+    if (tid < nl) {
+      const int L = min(max(p.seq_lens[tid / p.KH], 0), p.max_seq_len);
+      np = L;
+      if constexpr (IDX) np = L > 0 ? min(max(p.n_idx[tid], 0), p.idx_stride) : 0;
+    }
+    if (tid < p.B) {
+      len = min(max(p.seq_lens[tid], 0), p.max_seq_len);
+      if constexpr (!PAGED) off = p.seq_offset[tid];
+    }
+    s_np[tid] = np;
+    s_len[tid] = len;
+    s_off[tid] = off;
+  }
+  __syncthreads();
+  // positions and tiles of lane (pair) q < nl
+  auto lane_pos = [&](int q) -> int { return cached ? s_np[q] : pair_positions(p, q); };
+  auto tiles_of = [&](int q) -> int { return (lane_pos(q) + 31) / 32; };
+  const int T = wave_total_tiles_of(nl, tiles_of);
   // fixed_splits = S > 0: the unbalanced schedule, worker w = q*S + s takes
   // split s of lane q; otherwise the balanced split of the whole stream
   const int FS = p.fixed_splits;
@@ -228,10 +261,9 @@ decode_mfma_kernel(DecodeParams p) {
     // No worker visits a lane without positions, so its rows get out = 0 and
     // lse = -inf here; lane qq belongs to
     // workgroup qq % gridDim.x.
-    const int nl = p.B * p.KH;
     for (int base = 0; base < nl; base += 64) {
       const int qq = base + lane;
-      unsigned long long m = __ballot(qq < nl && qq % (int)gridDim.x == (int)blockIdx.x && lane_tiles(p, qq) == 0);
+      unsigned long long m = __ballot(qq < nl && qq % (int)gridDim.x == (int)blockIdx.x && tiles_of(qq) == 0);
       while (m) {
         const int pz = base + __builtin_ctzll(m);
         m &= m - 1;
@@ -333,8 +365,8 @@ decode_mfma_kernel(DecodeParams p) {
     // its partials, in split order
     const int q = (int)blockIdx.x / FS, sp = (int)blockIdx.x - q * FS;
     int acc = 0;
-    for (int qq = lane; qq < q; qq += 64) acc += lane_tiles(p, qq);
-    const int t0 = uniform_i32(wave_sum_int(acc)), n = uniform_i32(lane_tiles(p, q));
+    for (int qq = lane; qq < q; qq += 64) acc += tiles_of(qq);
+    const int t0 = uniform_i32(wave_sum_int(acc)), n = uniform_i32(q < nl ? tiles_of(q) : 0);
     t_begin = t0 + (int)((int64_t)sp * n / FS);
     t_end = t0 + (int)((int64_t)(sp + 1) * n / FS);
     fs_need = min(FS, n);
@@ -345,7 +377,7 @@ decode_mfma_kernel(DecodeParams p) {
   }
   // the lane (b, kh) holding the first tile of the range; each later run
   // takes the next lane that has tiles
-  LaneHit hit = wave_find_lane(p, t_begin);
+  LaneHit hit = wave_find_lane_of(nl, t_begin, tiles_of);
   for (int t = t_begin; t < t_end;) {
     if (hit.nt == 0) break;  // lane walk exhausted (cannot happen for t < total)
     const int q = hit.q;
@@ -360,9 +392,9 @@ decode_mfma_kernel(DecodeParams p) {
     }
     const int pair = q;
     const int b = pair / p.KH, kh = pair - b * p.KH;
-    const int L = uniform_i32(min(max(p.seq_lens[b], 0), p.max_seq_len));
+    const int L = uniform_i32(cached ? s_len[b] : min(max(p.seq_lens[b], 0), p.max_seq_len));
     int npos = L;
-    if constexpr (IDX) npos = uniform_i32(L > 0 ? min(max(p.n_idx[pair], 0), p.idx_stride) : 0);
+    if constexpr (IDX) npos = uniform_i32(lane_pos(pair));
     // this lane's column of block cb is query row g0 + 16*cb + col of the KV head
     bool qvalid[CB];
     int col_end[CB];
@@ -377,7 +409,7 @@ decode_mfma_kernel(DecodeParams p) {
     // Buffer resources over this (b, kh)'s rows: 32-bit offsets, and rows at
     // or past L read as zero (their scores are masked), so no clamping.  A
     // paged cache gets one resource per tile instead (see load_tile).
-    const int64_t head_off = PAGED ? 0 : uniform_i64(p.seq_offset[b]) + (int64_t)kh * p.stride_h;
+    const int64_t head_off = PAGED ? 0 : uniform_i64(cached ? s_off[b] : p.seq_offset[b]) + (int64_t)kh * p.stride_h;
     const char *kbase = (const char *)p.k + head_off * ES;
     const char *vbase = (const char *)p.v + head_off * ES;
     const uint32_t rs = (uint32_t)(p.stride_t * ES);
@@ -392,10 +424,12 @@ decode_mfma_kernel(DecodeParams p) {
     const __amdgpu_buffer_rsrc_t ksrs = __builtin_amdgcn_make_buffer_rsrc(
         i8 ? (void *)(p.k_scale + (int64_t)pair * p.k_scale_stride) : nullptr, (short)0,
         i8 ? max(p.k_scale_stride, 1) * 4 : 0, 0x00020000);
-    // Stage Q (the 16 heads of this block, zero past G) in LDS in MFMA
+    // Q (the 16 heads of this block, zero past G) is staged in LDS in MFMA
     // operand form; tiles read their B operand from there.  A global load
     // inside the segment loop would make the compiler wait for every load in
-    // flight, the tile prefetch included.
+    // flight, the tile prefetch included.  The query's loads are issued here,
+    // and stage_q turns them into the LDS operand once the first segment's
+    // tile loads are in flight, so their latencies overlap.
     //
     // int8 KV: the scores run on the int8 matrix cores straight from the K
     // codes.  Head g's query becomes q = s_g * n with s_g = max|q_g| / 2^22
@@ -403,29 +437,51 @@ decode_mfma_kernel(DecodeParams p) {
     // and |d2| <= 64 (|error| <= max|q_g| * 2^-23); each digit plane is one
     // int8 MFMA, and the three integer sums recombine exactly in fp32.  An
     // int8 query (QI8: per-row or static scale) is plane 0 alone.
+    constexpr int CPL = D / 4;  // int8: lane (col, cg) takes column col, channels [cg*CPL, cg*CPL + CPL)
+    constexpr int kQL = KVT == ATTN_I8 ? CB * (CPL / 8) : (kGroups * kCols * (D / 8) + NT - 1) / NT;
+    const int nqe = p.ngb * kCols * (D / 8);  // bf16: 16-byte pieces of the worker's query rows
+    u32x4_t qraw[kQL];
+    if constexpr (KVT == ATTN_I8) {
+      // the first wave of each column group loads the group's query
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const uint16_t *qrow = (const uint16_t *)p.q + q_row_index(p, b, kh, g0 + 16 * cb + col) * D + cg * CPL;
+#pragma unroll
+        for (int x = 0; x < CPL / 8; ++x) {
+          u32x4_t w = (u32x4_t){0u, 0u, 0u, 0u};
+          if (wi == 0 && qvalid[cb]) w = *(const u32x4_t *)(qrow + 8 * x);
+          qraw[cb * (CPL / 8) + x] = w;
+        }
+      }
+    } else {
+      // every column group's rows: column gc of the pair at row gc (a group
+      // is kCols rows, kQBytes bytes)
+#pragma unroll
+      for (int j = 0; j < kQL; ++j) {
+        const int e = tid + j * NT, gc = e / (D / 8), c8 = e - gc * (D / 8);
+        u32x4_t w = (u32x4_t){0u, 0u, 0u, 0u};
+        if (e < nqe && gc < p.G) w = *(const u32x4_t *)((const uint16_t *)p.q + q_row_index(p, b, kh, gc) * D + 8 * c8);
+        qraw[j] = w;
+      }
+    }
     float qs[CB];  // int8: this lane's column scale s_col in each block
-    __syncthreads();
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) qs[cb] = 0.f;
+    auto stage_q = [&]() {
     if constexpr (KVT == ATTN_I8) {
       if (wi == 0) {  // the first wave of each column group stages the group's query
-        constexpr int CPL = D / 4;  // lane (col, cg) takes column col, channels [cg*CPL, cg*CPL + CPL)
         unsigned char *sq_blk = s_q + gi * kQBytes;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb, sq_blk += 3 * 16 * kQDRow) {
-          float qv[CPL];
-          const uint16_t *qrow = (const uint16_t *)p.q + q_row_index(p, b, kh, g0 + 16 * cb + col) * D + cg * CPL;
-#pragma unroll
-          for (int x = 0; x < CPL / 8; ++x) {
-            u32x4_t w = (u32x4_t){0u, 0u, 0u, 0u};
-            if (qvalid[cb]) w = *(const u32x4_t *)(qrow + 8 * x);
-#pragma unroll
-            for (int y = 0; y < 4; ++y) {
-              qv[8 * x + 2 * y] = bf16_lo(w[y]);
-              qv[8 * x + 2 * y + 1] = bf16_hi(w[y]);
-            }
-          }
+          // channel j of this lane's CPL, decoded where it is used (few
+          // registers: the first segment's tile loads are in flight)
+          auto qval = [&](int j) -> float {
+            const uint32_t w = qraw[cb * (CPL / 8) + (j >> 3)][(j >> 1) & 3];
+            return (j & 1) ? bf16_hi(w) : bf16_lo(w);
+          };
           float mx = 0.f;
 #pragma unroll
-          for (int j = 0; j < CPL; ++j) mx = fmaxf(mx, fabsf(qv[j]));
+          for (int j = 0; j < CPL; ++j) mx = fmaxf(mx, fabsf(qval(j)));
           mx = rows_max(mx);  // the four lanes of column col hold all D channels
           float sc;
           if constexpr (QI8) {
@@ -443,7 +499,7 @@ decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
                 for (int y = 0; y < 4; ++y) {
                   float c = 0.f;
-                  if (sq > 0.f) c = fminf(127.f, fmaxf(-127.f, __builtin_rintf(qv[16 * x + 4 * j4 + y] / sq)));
+                  if (sq > 0.f) c = fminf(127.f, fmaxf(-127.f, __builtin_rintf(qval(16 * x + 4 * j4 + y) / sq)));
                   acc |= ((uint32_t)(int)c & 0xFFu) << (8 * y);
                 }
                 w[j4] = acc;
@@ -453,48 +509,48 @@ decode_mfma_kernel(DecodeParams p) {
           } else {
             const float inv = mx > 0.f ? 4194304.0f / mx : 0.f;
             sc = mx * (1.0f / 4194304.0f);
-            uint32_t dw[3][CPL / 4];
 #pragma unroll
-            for (int j4 = 0; j4 < CPL / 4; ++j4) {
-              uint32_t w0 = 0u, w1 = 0u, w2 = 0u;
+            for (int x = 0; x < CPL / 16; ++x) {
+              // channels 16x .. 16x+15: one 16-byte piece of each digit plane
+              uint32_t dw[3][4];
 #pragma unroll
-              for (int y = 0; y < 4; ++y) {
-                const int n = (int)__builtin_rintf(qv[4 * j4 + y] * inv);
-                const int d0 = (int)(int8_t)(n & 0xFF);
-                const int r1 = (n - d0) >> 8;
-                const int d1 = (int)(int8_t)(r1 & 0xFF);
-                const int d2 = (r1 - d1) >> 8;
-                w0 |= (uint32_t)(d0 & 0xFF) << (8 * y);
-                w1 |= (uint32_t)(d1 & 0xFF) << (8 * y);
-                w2 |= (uint32_t)(d2 & 0xFF) << (8 * y);
+              for (int j4 = 0; j4 < 4; ++j4) {
+                uint32_t w0 = 0u, w1 = 0u, w2 = 0u;
+#pragma unroll
+                for (int y = 0; y < 4; ++y) {
+                  const int n = (int)__builtin_rintf(qval(16 * x + 4 * j4 + y) * inv);
+                  const int d0 = (int)(int8_t)(n & 0xFF);
+                  const int r1 = (n - d0) >> 8;
+                  const int d1 = (int)(int8_t)(r1 & 0xFF);
+                  const int d2 = (r1 - d1) >> 8;
+                  w0 |= (uint32_t)(d0 & 0xFF) << (8 * y);
+                  w1 |= (uint32_t)(d1 & 0xFF) << (8 * y);
+                  w2 |= (uint32_t)(d2 & 0xFF) << (8 * y);
+                }
+                dw[0][j4] = w0;
+                dw[1][j4] = w1;
+                dw[2][j4] = w2;
               }
-              dw[0][j4] = w0;
-              dw[1][j4] = w1;
-              dw[2][j4] = w2;
-            }
 #pragma unroll
-            for (int dg = 0; dg < 3; ++dg)
-#pragma unroll
-              for (int x = 0; x < CPL / 16; ++x)
+              for (int dg = 0; dg < 3; ++dg)
                 *(u32x4_t *)(sq_blk + (dg * 16 + col) * kQDRow + cg * CPL + 16 * x) =
-                    (u32x4_t){dw[dg][4 * x], dw[dg][4 * x + 1], dw[dg][4 * x + 2], dw[dg][4 * x + 3]};
+                    (u32x4_t){dw[dg][0], dw[dg][1], dw[dg][2], dw[dg][3]};
+            }
           }
           if (cg == 0) s_qs[g0 + 16 * cb + col] = sc;
         }
       }
     } else {
-      // every column group's rows: column gc of the pair at row gc (a group
-      // is kCols rows, kQBytes bytes)
-      for (int e = tid; e < p.ngb * kCols * (D / 8); e += NT) {
-        const int gc = e / (D / 8), c8 = e - gc * (D / 8);
-        u32x4_t w = (u32x4_t){0u, 0u, 0u, 0u};
-        if (gc < p.G) w = *(const u32x4_t *)((const uint16_t *)p.q + q_row_index(p, b, kh, gc) * D + 8 * c8);
-        *(u32x4_t *)(s_q + gc * kQRow + 16 * c8) = w;
+#pragma unroll
+      for (int j = 0; j < kQL; ++j) {
+        const int e = tid + j * NT, gc = e / (D / 8), c8 = e - gc * (D / 8);
+        if (e < nqe) *(u32x4_t *)(s_q + gc * kQRow + 16 * c8) = qraw[j];
       }
     }
     __syncthreads();
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) qs[cb] = KVT == ATTN_I8 ? s_qs[g0 + 16 * cb + col] : 0.f;
+    };
     const unsigned char *sq = s_q + gi * kQBytes;  // this wave's column group
     auto q_operand = [&](int cb, int kb) -> bf16x8_t {
       return __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(sq + (16 * cb + col) * kQRow + 16 * (4 * kb + cg)));
@@ -748,7 +804,12 @@ decode_mfma_kernel(DecodeParams p) {
       return (int)min((int64_t)run_end, (int64_t)lane_t0 + ((int64_t)(s0 - lane_t0) / cs + 1) * cs);
     };
     auto tile_of = [&](int s0, int s) { return s0 + (s * S + wi) * TPS; };
-    for (int seg_t0 = t; seg_t0 < run_end;) {
+    // Opens the segment starting at tile s0 (its index list or page ids
+    // staged, the loads of its first NBUF-1 local steps issued) and returns
+    // its end.  The run's first segment is opened before the query is staged
+    // (whose loads are then in flight with the tiles'), so the query's
+    // registers are free before the steps begin.
+    auto open_segment = [&](int seg_t0) -> int {
       const int seg_t1 = seg_end_of(seg_t0);
       seg_pos0 = (seg_t0 - lane_t0) * kTile;
       seg_pos1 = min(npos, (seg_t1 - lane_t0) * kTile);
@@ -769,6 +830,12 @@ decode_mfma_kernel(DecodeParams p) {
       }
 #pragma unroll
       for (int j = 0; j + 1 < NBUF; ++j) load_step(buf[j], tile_of(seg_t0, j), seg_t1);
+      return seg_t1;
+    };
+    int seg_t0 = t;  // t < run_end
+    int seg_t1 = open_segment(seg_t0);
+    stage_q();
+    for (;;) {
       const int nsteps = (seg_t1 - seg_t0 + TPS - 1) / TPS;
       const int wsteps = (nsteps + S - 1) / S;  // local steps of the busiest wave
       const int steps = (wsteps + NBUF - 1) / NBUF * NBUF;
@@ -799,6 +866,8 @@ decode_mfma_kernel(DecodeParams p) {
         }
       }
       seg_t0 = seg_t1;
+      if (seg_t0 >= run_end) break;
+      seg_t1 = open_segment(seg_t0);
     }
 
     // The run's result for each column.  Lane (col, cg) holds channels
@@ -887,7 +956,7 @@ decode_mfma_kernel(DecodeParams p) {
       ++npend;
     }
     t = run_end;
-    if (t < t_end) hit = next_lane(p, hit);
+    if (t < t_end) hit = next_lane_of(nl, hit, tiles_of);
   }
   arrive_and_merge();
 }

@@ -88,6 +88,56 @@ def test_many_one_token_sequences_return_their_value():
             assert np.abs(out[b, kh * w.G:(kh + 1) * w.G] - row[None, :]).max() <= 1e-6
 
 
+@pytest.mark.parametrize("kind", ["bf16", "int8", "indexed"])
+def test_more_lanes_than_a_worker_stages(kind):
+    """70 sequences x 4 KV heads = 280 (b, kh) lanes, more than the 256 whose lengths a decode
+    worker stages in LDS at its start: the work split and the lane walk then read the lengths and
+    offsets from global memory.  Ragged lengths with empty sequences; every output row and lse
+    against the oracle, on a bf16 cache, an INT8 cache, and a kept-token list per lane."""
+    rng = np.random.default_rng(175)
+    lens = rng.integers(1, 700, 70).astype(np.int32)
+    lens[::9] = 0
+    lens[5] = 4000
+    w = synth.workload("gqa32k", B=70, KH=4, G=8, lens=lens, layout="token_major", seed=175)
+    q, k, v, g = synth.generate(w)
+    log_case(f"280 lanes, {kind}")
+    qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
+    geom = dev_geom(g)
+    lse = torch.empty((w.B, w.QH), dtype=torch.float32, device=DEV)
+    pk, kh_, vh_ = {}, k, v
+    kw = dict(lse=lse, split_tokens=256)
+    if kind == "int8":
+        kc, ks = pkg.kv_quant_int8(to_dev(k), geom, 64)
+        vc, vs = pkg.kv_quant_int8(to_dev(v), geom, 0)
+        torch.cuda.synchronize()
+        out, _ = pkg.attn_decode_splitkv(qd, kc, vc, geom, w.G, k_scale=ks, k_part_tokens=64,
+                                         v_scale=float(vs.item()), **kw)
+        kh_, vh_ = kc.cpu().numpy(), vc.cpu().numpy()
+        pk = dict(k_scale=ks.cpu().numpy(), k_part=64, k_scale_stride=-(-int(g.max_len) // 64),
+                  v_scale=float(vs.item()))
+    else:
+        if kind == "indexed":
+            stride = 300
+            idx = np.full((w.B * w.KH, stride), -1, np.int32)
+            nk = np.zeros(w.B * w.KH, np.int32)
+            for pr in range(w.B * w.KH):
+                L = int(lens[pr // w.KH])
+                n = min(L, int(rng.integers(0, stride + 1)))
+                idx[pr, :n] = np.sort(rng.choice(L, n, replace=False)) if n else idx[pr, :0]
+                nk[pr] = n
+            kw.update(token_idx=to_dev(idx), n_idx=to_dev(nk))
+            pk = dict(tok_idx=idx.reshape(-1), n_idx=nk, idx_stride=stride)
+        out, _ = pkg.attn_decode_splitkv(qd, to_dev(k), to_dev(v), geom, w.G, **kw)
+    torch.cuda.synchronize()
+    p = problem(w, q, kh_, vh_, g, **pk)
+    ref, ref_lse = oracle.attention_rows(p, oracle.all_rows(p), nthreads=8)
+    assert np.abs(out.cpu().numpy().reshape(-1, w.D) - ref).max() <= 2e-3
+    got_lse = lse.cpu().numpy().reshape(-1)
+    empty = np.isneginf(ref_lse)
+    assert np.array_equal(np.isneginf(got_lse), empty)
+    assert np.abs(got_lse[~empty] - ref_lse[~empty]).max() <= 1e-3
+
+
 @pytest.mark.parametrize("split", [0, 64, 2048])
 def test_lengths_at_tile_and_chunk_boundaries(split):
     lens = np.array([31, 32, 33, 63, 64, 65, 2047, 2048, 2049, 4096], np.int32)
