@@ -42,11 +42,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
-__device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
 
 // Reductions across the four 16-lane rows of a wave (lanes l, l^16, l^32,
 // l^48 end with the same result).  gfx950's row-swap permutes exchange whole
@@ -165,15 +160,22 @@ __device__ __forceinline__ int lane_tiles(const DecodeParams &p, int q) {
   return q < p.B * p.KH * p.lpp ? (pair_positions(p, q / p.lpp) + 31) / 32 : 0;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave, in six DPP moves (no
+// trip through the LDS crossbar): shifts by 1, 2, 4 and 8 lanes inside each
+// row of 16 lanes (a lane whose source lies before its row's start adds 0),
+// then lane 15's sum into the next row for rows 1 and 3 (row_bcast:15), and
+// lane 31's (rows 0-1) into rows 2 and 3 (row_bcast:31).
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int x = __shfl_up(v, o);
-    if (lane >= o) v += x;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return v;
 }
+// The sum over the wave (uniform).
+__device__ __forceinline__ int wave_sum_int(int v) { return __builtin_amdgcn_readlane(wave_incl_scan(v), 63); }
 
 // Tiles of all nl lanes (wave-wide; every thread of the wave gets the total),
 // tiles(q) giving lane q's tile count.
@@ -258,6 +260,15 @@ struct StreamSplit {
   int W;          // workers
   bool weighted;  // XCD-weighted (else equal)
 };
+// floor(n / d) for 0 <= n < 2^53 and d > 0, exactly, in fp64: an integer
+// quotient is exact, and otherwise the correctly rounded quotient r of q =
+// n / d stays in [floor(q), floor(q) + 1), because q lies at least 1/d below
+// the next integer while |r - q| <= q * 2^-53 < 1/d.  About twenty fp64
+// instructions, where a 64-bit integer division is a chain of more than a
+// hundred (several per worker at every launch's start).
+__device__ __forceinline__ int64_t floor_div53(int64_t n, int64_t d) {
+  return (int64_t)((double)n / (double)d);
+}
 __device__ __forceinline__ int64_t xcd_weight_sum(int w) {
   const int r = w & 7;
   return (int64_t)(w >> 3) * (4 * 16 + 4 * 15) + (int64_t)((r + 1) / 2) * 16 + (int64_t)(r / 2) * 15;
@@ -265,29 +276,31 @@ __device__ __forceinline__ int64_t xcd_weight_sum(int w) {
 __device__ __forceinline__ StreamSplit stream_split(const DecodeParams &p, int T) {
   StreamSplit r = {0, false};
   if (T == 0) return r;
-  const int64_t ct = p.split / 32;
-  if (p.ngb == 1 && (int64_t)T * 15 / (16 * ct) >= p.grid) {
+  const int ct = p.split / 32;
+  // floor(15 T / (16 ct)) >= grid, without the division
+  if (p.ngb == 1 && (int64_t)T * 15 >= (int64_t)p.grid * 16 * ct) {
     r.W = p.grid;
     r.weighted = true;
   } else {
-    r.W = (int)min((int64_t)p.grid, max((int64_t)1, (int64_t)T / ct));
+    r.W = min(p.grid, max(1, T / ct));
   }
   return r;
 }
+// The products below stay far under 2^53: T < 2^31 tiles and S(W) < 2^18.
 __device__ __forceinline__ int range_start(int w, int T, StreamSplit sp) {
-  if (sp.weighted) return (int)((int64_t)T * xcd_weight_sum(w) / xcd_weight_sum(sp.W));
-  return (int)((int64_t)w * T / sp.W);
+  if (sp.weighted) return (int)floor_div53((int64_t)T * xcd_weight_sum(w), xcd_weight_sum(sp.W));
+  return (int)floor_div53((int64_t)w * T, sp.W);
 }
 // The worker whose range holds tile t (0 <= t < T): the largest w with
 // start(w) <= t.  Equal split: w = floor(((t+1)*W - 1) / T).  Weighted: the
 // largest w with T*S(w) < (t+1)*S(W), i.e. S(w) <= X = floor(((t+1)*S(W) - 1)
 // / T); S(8k + r) = 124k + P(r) (124 = four weights of 16 and four of 15;
 // P(r) = 0, 16, 31, 47, 62, 78, 93, 109), so w = 8k + r with k = X / 124 and r
-// the largest with P(r) <= X - 124k.  One 64-bit division either way.
+// the largest with P(r) <= X - 124k.
 __device__ __forceinline__ int worker_of(int t, int T, StreamSplit sp) {
-  if (!sp.weighted) return (int)(((int64_t)(t + 1) * sp.W - 1) / T);
-  const int64_t X = ((int64_t)(t + 1) * xcd_weight_sum(sp.W) - 1) / T;
-  const int k = (int)(X / 124), rem = (int)(X - (int64_t)k * 124);
+  if (!sp.weighted) return (int)floor_div53((int64_t)(t + 1) * sp.W - 1, T);
+  const int X = (int)floor_div53((int64_t)(t + 1) * xcd_weight_sum(sp.W) - 1, T);
+  const int k = X / 124, rem = X - k * 124;
   const int r = (rem >= 16) + (rem >= 31) + (rem >= 47) + (rem >= 62) + (rem >= 78) + (rem >= 93) + (rem >= 109);
   return min(8 * k + r, sp.W - 1);
 }

@@ -230,22 +230,18 @@ decode_mfma_kernel(DecodeParams p) {
   const int nl = p.B * p.KH;
   const bool cached = nl <= NT;  // then B <= NT as well
   if (cached) {
-    // thread i: lane i's positions, and sequence i's length and offset; all
-    // loads of the worker in flight together
-    int np = 0, len = 0;
-    int64_t off = 0;
-    if (tid < nl) {
-      const int L = min(max(p.seq_lens[tid / p.KH], 0), p.max_seq_len);
-      np = L;
-      if constexpr (IDX) np = L > 0 ? min(max(p.n_idx[tid], 0), p.idx_stride) : 0;
-    }
-    if (tid < p.B) {
-      len = min(max(p.seq_lens[tid], 0), p.max_seq_len);
-      if constexpr (!PAGED) off = p.seq_offset[tid];
-    }
-    s_np[tid] = np;
-    s_len[tid] = len;
-    s_off[tid] = off;
+    // thread i: lane i's positions, and sequence i's length and offset.  The
+    // loads go to clamped indices without a branch, so all of them are in
+    // flight together (one memory latency, not one per array).
+    const int qi = min(tid, nl - 1), bi = min(tid, p.B - 1);
+    const int lq = p.seq_lens[qi / p.KH], lb = p.seq_lens[bi];
+    const int nq = IDX ? p.n_idx[qi] : 0;
+    const int64_t off = PAGED ? 0 : p.seq_offset[bi];
+    const int Lq = min(max(lq, 0), p.max_seq_len);
+    const int np = IDX ? (Lq > 0 ? min(max(nq, 0), p.idx_stride) : 0) : Lq;
+    s_np[tid] = tid < nl ? np : 0;
+    s_len[tid] = tid < p.B ? min(max(lb, 0), p.max_seq_len) : 0;
+    s_off[tid] = tid < p.B ? off : 0;
   }
   __syncthreads();
   // positions and tiles of lane (pair) q < nl

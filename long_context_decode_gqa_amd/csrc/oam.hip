@@ -162,6 +162,7 @@ __device__ __forceinline__ float quad_sum3(float v) {
 template <int D, int KVT, bool PAGED>
 __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
   constexpr bool I8 = KVT == ATTN_I8;
+  static_assert(D <= 256, "one thread per channel for the mean query");
   constexpr int KB = I8 ? D / 64 : D / 32;  // MFMAs per 16 tokens (16x16x64 int8 or 16x16x32 bf16)
   constexpr int ES = I8 ? 1 : 2;            // bytes per K element
   // an int8 tile carries half the bytes of a bf16 one: more tiles in flight
@@ -174,77 +175,32 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
   // 32 + 1 pages, as a page holds a positive multiple of 32 tokens)
   __shared__ int s_pages[PAGED ? 4 : 1][PAGED ? kScoreTok / 4 / 32 + 1 : 1];
   const int pair = blockIdx.y;
-  const int L = pair_len(o, pair);
+  const int b = pair / o.KH, kh = pair - b * o.KH;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // The set-up's loads (the length, the offset and the group's G <= 16
+  // queries of channel tid) go out together, before the length is checked:
+  // one memory latency instead of three in a row.
+  const int len_raw = o.seq_lens[b];
+  const int64_t seq_off = PAGED ? 0 : o.seq_offset[b];
+  float qv[16];
+  {
+    const uint16_t *q0 = o.q + ((int64_t)b * o.QH + (int64_t)kh * o.G) * D + min(tid, D - 1);
+#pragma unroll
+    for (int g = 0; g < 16; ++g) qv[g] = bf16_bits_to_f32(q0[(int64_t)min(g, o.G - 1) * D]);
+  }
+  const int L = min(max(len_raw, 0), o.L_cap);
   const int blk0 = blockIdx.x * kScoreTok;
   if (blk0 >= L) return;
-  const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the tile loop is a scalar loop
   const int col = lane & 15, cg = lane >> 4;
   for (int i = tid; i < kBins; i += 256) s_hist[i] = 0u;
-  const int b = pair / o.KH, kh = pair - b * o.KH;
-  // mean query of the group, in fp32, summed in head order; the G (<= 16)
-  // loads of a channel are all issued before the first is used
-  for (int d = tid; d < D; d += 256) {
-    const uint16_t *q0 = o.q + ((int64_t)b * o.QH + (int64_t)kh * o.G) * D + d;
-    float qv[16];
-#pragma unroll
-    for (int g = 0; g < 16; ++g) qv[g] = bf16_bits_to_f32(q0[(int64_t)min(g, o.G - 1) * D]);
-#pragma unroll
-    for (int g = 0; g < 16; ++g) qv[g] = g < o.G ? qv[g] : 0.f;
-    float acc = 0.f;
-#pragma unroll
-    for (int g = 0; g < 16; ++g) acc += qv[g];  // adding the zeros past G changes nothing
-    s_qbar[d] = acc / (float)o.G;
-  }
-  __syncthreads();
   typedef typename std::conditional<I8, i32x4_t, bf16x8_t>::type QOp;
   QOp qop[KB];
   const int part = col & 3;  // bf16: 0 hi, 1 mid, 2 lo; int8: digit plane 0, 1, 2; 3: zero
   float qscale = 1.f;        // int8: q_bar = qscale * (fixed-point integer)
-  if constexpr (I8) {
-    // q_bar as a 22-bit fixed-point integer n = rint(q_bar / s), s = max|q_bar| / 2^22,
-    // in three balanced int8 digits n = 65536 d2 + 256 d1 + d0 (column part p holds digit p)
-    float mx = 0.f;
-    for (int d = 0; d < D; ++d) mx = fmaxf(mx, fabsf(s_qbar[d]));
-    const float inv = mx > 0.f ? 4194304.0f / mx : 0.f;
-    qscale = mx * (1.0f / 4194304.0f);
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        uint32_t w = 0u;
-#pragma unroll
-        for (int y = 0; y < 4; ++y) {
-          const int n = (int)__builtin_rintf(s_qbar[64 * kb + 16 * cg + 4 * j4 + y] * inv);
-          const int d0 = (int)(int8_t)(n & 0xFF);
-          const int r1 = (n - d0) >> 8;
-          const int d1 = (int)(int8_t)(r1 & 0xFF);
-          const int d2 = (r1 - d1) >> 8;
-          const int dg = part == 0 ? d0 : part == 1 ? d1 : part == 2 ? d2 : 0;
-          w |= (uint32_t)(dg & 0xFF) << (8 * y);
-        }
-        qop[kb][j4] = (int)w;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float x = s_qbar[8 * (4 * kb + cg) + j];
-        const uint32_t hb = f32_to_bf16_bits(x);
-        const float r1 = x - __uint_as_float(hb << 16);
-        const uint32_t mb = f32_to_bf16_bits(r1);
-        const float r2 = r1 - __uint_as_float(mb << 16);
-        const uint32_t lb = f32_to_bf16_bits(r2);
-        const uint32_t sel = part == 0 ? hb : part == 1 ? mb : part == 2 ? lb : 0u;
-        qop[kb][j] = __builtin_bit_cast(__bf16, (uint16_t)sel);
-      }
-    }
-  }
   // int8: the integer digit sums recombine with weights 1, 256, 65536 in the quad add
   const float dweight = part == 0 ? 1.f : part == 1 ? 256.f : part == 2 ? 65536.f : 0.f;
-  const int64_t head_off = (PAGED ? 0 : o.seq_offset[b]) + (int64_t)kh * o.stride_h;
+  const int64_t head_off = seq_off + (int64_t)kh * o.stride_h;
   const uint32_t rs = (uint32_t)(o.stride_t * ES);
   const int nrec = (int)((uint32_t)(L - 1) * rs + D * ES);
   const __amdgpu_buffer_rsrc_t krs =
@@ -352,6 +308,59 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
   KTile buf[NBUF];
 #pragma unroll
   for (int j = 0; j + 1 < NBUF; ++j) load(buf[j], tw0 + j, j < ntw);
+  // The query operand is built while the first tiles are in flight (the
+  // queries' loads went out first, so waiting for them leaves the tiles').
+  // mean query of the group, in fp32, summed in head order
+  if (tid < D) {
+#pragma unroll
+    for (int g = 0; g < 16; ++g) qv[g] = g < o.G ? qv[g] : 0.f;
+    float acc = 0.f;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) acc += qv[g];  // adding the zeros past G changes nothing
+    s_qbar[tid] = acc / (float)o.G;
+  }
+  __syncthreads();
+  if constexpr (I8) {
+    // q_bar as a 22-bit fixed-point integer n = rint(q_bar / s), s = max|q_bar| / 2^22,
+    // in three balanced int8 digits n = 65536 d2 + 256 d1 + d0 (column part p holds digit p)
+    float mx = 0.f;
+    for (int d = 0; d < D; ++d) mx = fmaxf(mx, fabsf(s_qbar[d]));
+    const float inv = mx > 0.f ? 4194304.0f / mx : 0.f;
+    qscale = mx * (1.0f / 4194304.0f);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        uint32_t w = 0u;
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          const int n = (int)__builtin_rintf(s_qbar[64 * kb + 16 * cg + 4 * j4 + y] * inv);
+          const int d0 = (int)(int8_t)(n & 0xFF);
+          const int r1 = (n - d0) >> 8;
+          const int d1 = (int)(int8_t)(r1 & 0xFF);
+          const int d2 = (r1 - d1) >> 8;
+          const int dg = part == 0 ? d0 : part == 1 ? d1 : part == 2 ? d2 : 0;
+          w |= (uint32_t)(dg & 0xFF) << (8 * y);
+        }
+        qop[kb][j4] = (int)w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = s_qbar[8 * (4 * kb + cg) + j];
+        const uint32_t hb = f32_to_bf16_bits(x);
+        const float r1 = x - __uint_as_float(hb << 16);
+        const uint32_t mb = f32_to_bf16_bits(r1);
+        const float r2 = r1 - __uint_as_float(mb << 16);
+        const uint32_t lb = f32_to_bf16_bits(r2);
+        const uint32_t sel = part == 0 ? hb : part == 1 ? mb : part == 2 ? lb : 0u;
+        qop[kb][j] = __builtin_bit_cast(__bf16, (uint16_t)sel);
+      }
+    }
+  }
   for (int i = 0; i < nst; i += NBUF) {
 #pragma unroll
     for (int j = 0; j < NBUF; ++j) {
