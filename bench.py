@@ -481,9 +481,10 @@ def bench_oam(pkg, torch, synth, steps, warmup, dev):
 
 
 def hbm_read_probe(pkg, torch, dev, nbytes=4 << 30, reps=20):
-    """The library's read-only sweep (attn_util_read: 16-byte loads, one checksum word per
-    workgroup) over nbytes of HBM, timed with events around each launch on the current stream: the
-    achievable read bandwidth next to the 8 TB/s vendor figure."""
+    """The library's read-only sweep (attn_util_read: one contiguous chunk per workgroup, sixteen
+    non-temporal 16-byte buffer loads per thread in flight, one checksum word per workgroup) over
+    nbytes of HBM, timed with events around each launch on the current stream: the achievable read
+    bandwidth next to the 8 TB/s vendor figure."""
     src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
     src.fill_(1.0)
     sink = torch.empty(4096, dtype=torch.float32, device=dev)
@@ -594,7 +595,7 @@ def main():
     achieved = head["decode_algo_bytes"] / dk_s / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_pmc_traffic(),
-                "kernel": "decode_mfma_kernel<128, bf16> (decode and merge, one launch)",
+                "kernel": "decode_mfma_kernel<128, bf16, non-temporal K/V> (decode and merge, one launch)",
                 "algorithmic_bytes_per_launch": head["decode_algo_bytes"],
                 "avg_launch_us": round(head["decode_ms"] * 1e3, 2),
                 "frac_of_probe": round(achieved / pg, 4)}

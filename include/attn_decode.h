@@ -426,8 +426,11 @@ const char *attn_last_error(void);
 /*
  * Measurement helpers (not part of the method): a plain device copy of
  * `bytes` (multiple of 16, 16-byte aligned pointers) and a read-only sweep
- * that writes one checksum word per workgroup into sink (>= 4096 floats).
- * They calibrate hardware byte counters and the achievable HBM bandwidth.
+ * (non-temporal 16-byte loads, one contiguous chunk per workgroup) that
+ * writes one checksum word per workgroup into sink (>= 4096 floats).  They
+ * calibrate hardware byte counters and the achievable HBM bandwidth.
+ * attn_util_read returns ATTN_ERR_UNSUPPORTED for 2^43 bytes or more (a
+ * workgroup's chunk must stay under 2 GiB).
  */
 attn_status attn_util_copy(void *dst, const void *src, size_t bytes, attn_stream_t stream);
 attn_status attn_util_read(const void *src, size_t bytes, float *sink, attn_stream_t stream);

@@ -78,6 +78,7 @@ struct DecodeLayout {
   int32_t cols;  // matrix-core columns per decode wave (16, or 32 for more than 16 rows per KV head)
   int32_t wpg;   // waves per decode worker (workgroup)
   bool mfma;     // matrix-core decode (bf16/int8 KV), whose launch also merges
+  bool stream_nt;  // matrix-core decode: non-temporal K/V loads
 };
 
 attn_status plan_decode(const attn_decode_args *a, DecodeLayout *L) {
@@ -194,6 +195,17 @@ attn_status plan_decode(const attn_decode_args *a, DecodeLayout *L) {
       return fail(ATTN_ERR_UNSUPPORTED, "fixed_splits: too many workers");
     L->grid = (int32_t)(L->lanes * a->fixed_splits);
   }
+  // Non-temporal K/V loads: a plain 4 GiB read through buffer loads with
+  // the nt bit moved 7.0-7.1 TB/s against 6.1-6.3 TB/s without, and the
+  // 128K decode steps went from 361 to 329 us (bf16) and 188 to 168 us
+  // (int8).  Each such load takes longer, though: with few workers in flight
+  // they lose (a 4-lane share of the 128K step: 54 -> 75 us), and so do two
+  // column groups of one worker, which meet each tile in the caches (8
+  // query rows per sequence: 448 -> 601 us).  So they are used where the
+  // kernel's XCD-weighted split applies at the longest lengths the call
+  // allows: one column group, and work for every worker.
+  L->stream_nt = mfma && !a->token_idx && a->fixed_splits == 0 && L->ngb == 1 &&
+                 max_tiles * 15 >= (int64_t)L->grid * 16 * ct;
   const int64_t QH = (int64_t)g.KH * a->G * R;
   if (mfma) {
     // A lane's workers: every worker's range is at least ct tiles (the
@@ -344,6 +356,7 @@ attn_status decode_run(const attn_decode_args *a, void *workspace, size_t worksp
   p.max_slots = (int32_t)L.max_slots;
   p.wpg = L.wpg;
   p.fixed_splits = a->fixed_splits;
+  p.stream_nt = L.stream_nt ? 1 : 0;
   p.grid = L.grid;
   p.wl.m_part = reinterpret_cast<float *>(ws + L.m);
   p.wl.l_part = reinterpret_cast<float *>(ws + L.l);
@@ -412,6 +425,7 @@ attn_status attn_util_copy(void *dst, const void *src, size_t bytes, attn_stream
 attn_status attn_util_read(const void *src, size_t bytes, float *sink, attn_stream_t stream) {
   if (bytes % 16 || (bytes && (!src || !sink || !aligned16(src))))
     return fail(ATTN_ERR_INVALID_ARG, "read: bytes % 16 == 0, aligned src and a sink are required");
+  if (bytes >= ((size_t)1 << 43)) return fail(ATTN_ERR_UNSUPPORTED, "read: at most 2^43 - 16 bytes");
   hipError_t e = launch_read(src, bytes, sink, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : fail_hip(e, "read launch");
 }

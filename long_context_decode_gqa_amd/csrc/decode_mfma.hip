@@ -134,11 +134,15 @@ constexpr int kMaxSegPages = 520;
 // only after its arrival returned the lane's full count.
 constexpr int kWPG = 4;  // waves per worker
 
-template <int D, int KVT, bool IDX, bool QI8, bool PAGED, int CB>
+template <int D, int KVT, bool IDX, bool QI8, bool PAGED, int CB, bool STREAM>
 __global__ __launch_bounds__(64 * kWPG) __attribute__((amdgpu_waves_per_eu(CB == 2 ? 1 : 2, CB == 2 ? 1 : 2))) void
 decode_mfma_kernel(DecodeParams p) {
   static_assert(!(IDX && PAGED), "a paged cache is read by position");
   static_assert(CB == 1 || CB == 2, "one or two 16-column blocks per wave");
+  static_assert(!(STREAM && IDX), "gathered kept rows use the default cache policy");
+  // K/V cache policy: non-temporal where the launch streams the whole cache
+  // over a full grid (STREAM, chosen by the host), the default otherwise
+  constexpr int kKVPol = STREAM ? kStream : 0;
   constexpr int WPG = kWPG;
   typedef Tile<D, KVT, IDX> TileT;
   typedef Step<D, KVT, IDX, CB> StepT;
@@ -590,15 +594,15 @@ decode_mfma_kernel(DecodeParams p) {
       for (int tb = 0; tb < 2; ++tb) {
         const uint32_t off = ((uint32_t)(row_of(tpos + 16 * tb + col) + rshift) * rs + 16 * cg) | oob;
 #pragma unroll
-        for (int kl = 0; kl < KL; ++kl) R.k[tb][kl] = __builtin_amdgcn_raw_buffer_load_b128(tk, off + 64 * kl, 0, 0);
+        for (int kl = 0; kl < KL; ++kl) R.k[tb][kl] = __builtin_amdgcn_raw_buffer_load_b128(tk, off + 64 * kl, 0, kKVPol);
       }
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const int slot = (jj < 4) ? (4 * cg + jj) : (16 + 4 * cg + jj - 4);
         const uint32_t off = ((uint32_t)(row_of(tpos + slot) + rshift) * rs + col * VW * 4) | oob;
-        if constexpr (VW == 4) R.v[jj] = __builtin_amdgcn_raw_buffer_load_b128(tv, off, 0, 0);
-        else if constexpr (VW == 2) R.v[jj] = __builtin_amdgcn_raw_buffer_load_b64(tv, off, 0, 0);
-        else R.v[jj] = __builtin_amdgcn_raw_buffer_load_b32(tv, off, 0, 0);
+        if constexpr (VW == 4) R.v[jj] = __builtin_amdgcn_raw_buffer_load_b128(tv, off, 0, kKVPol);
+        else if constexpr (VW == 2) R.v[jj] = __builtin_amdgcn_raw_buffer_load_b64(tv, off, 0, kKVPol);
+        else R.v[jj] = __builtin_amdgcn_raw_buffer_load_b32(tv, off, 0, kKVPol);
       }
       if constexpr (KVT == ATTN_I8) {
         const int last = max(npos - 1, 0);
@@ -959,25 +963,32 @@ decode_mfma_kernel(DecodeParams p) {
 
 }  // namespace
 
-template <bool IDX, bool PAGED, int CB>
+template <bool IDX, bool PAGED, int CB, bool STREAM>
 static void launch_variant(const DecodeParams &p, int kv_dtype, dim3 g, hipStream_t s) {
   dim3 blk(64 * kWPG);
   if (kv_dtype == ATTN_BF16) {
-    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_BF16, IDX, false, PAGED, CB>), g, blk, 0, s, p);
-    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_BF16, IDX, false, PAGED, CB>), g, blk, 0, s, p);
+    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_BF16, IDX, false, PAGED, CB, STREAM>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_BF16, IDX, false, PAGED, CB, STREAM>), g, blk, 0, s, p);
   } else if (p.q_quant == ATTN_QUANT_EXACT) {
-    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_I8, IDX, false, PAGED, CB>), g, blk, 0, s, p);
-    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_I8, IDX, false, PAGED, CB>), g, blk, 0, s, p);
+    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_I8, IDX, false, PAGED, CB, STREAM>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_I8, IDX, false, PAGED, CB, STREAM>), g, blk, 0, s, p);
   } else {
-    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_I8, IDX, true, PAGED, CB>), g, blk, 0, s, p);
-    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_I8, IDX, true, PAGED, CB>), g, blk, 0, s, p);
+    if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_I8, IDX, true, PAGED, CB, STREAM>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_I8, IDX, true, PAGED, CB, STREAM>), g, blk, 0, s, p);
   }
 }
 
 template <bool IDX, bool PAGED>
 static void launch_cb(const DecodeParams &p, int kv_dtype, dim3 g, hipStream_t s) {
-  if (p.cols_per_wave == 32) launch_variant<IDX, PAGED, 2>(p, kv_dtype, g, s);
-  else launch_variant<IDX, PAGED, 1>(p, kv_dtype, g, s);
+  if constexpr (!IDX) {
+    if (p.stream_nt) {
+      if (p.cols_per_wave == 32) launch_variant<IDX, PAGED, 2, true>(p, kv_dtype, g, s);
+      else launch_variant<IDX, PAGED, 1, true>(p, kv_dtype, g, s);
+      return;
+    }
+  }
+  if (p.cols_per_wave == 32) launch_variant<IDX, PAGED, 2, false>(p, kv_dtype, g, s);
+  else launch_variant<IDX, PAGED, 1, false>(p, kv_dtype, g, s);
 }
 
 hipError_t launch_decode_mfma(const DecodeParams &p, int kv_dtype, hipStream_t s) {

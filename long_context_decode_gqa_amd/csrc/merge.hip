@@ -314,11 +314,26 @@ __global__ __launch_bounds__(256) void copy_kernel(u32x4_t *dst, const u32x4_t *
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) dst[i] = src[i];
 }
 
+// One contiguous chunk per workgroup, read through a buffer resource with
+// non-temporal loads, sixteen 16-byte loads per thread in flight: the fastest
+// plain read measured on MI355X (7.0-7.1 TB/s over 4 GiB; the same sweep
+// with the default cache policy 6.1-6.3 TB/s, and one grid-stride load per
+// thread 5.2-6.4 TB/s depending on the grid).
 __global__ __launch_bounds__(256) void read_kernel(const u32x4_t *src, size_t n, float *sink) {
+  constexpr int U = 16;
+  const size_t per = (n + gridDim.x - 1) / gridDim.x;
+  const size_t b0 = min(n, (size_t)blockIdx.x * per);
+  const size_t b1 = min(n, b0 + per);
+  const uint32_t cnt = (uint32_t)(b1 - b0);  // < 2^27 pieces: the launcher bounds the chunk
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(src + b0), (short)0, (int)(cnt * 16u), 0x00020000);
   uint32_t acc = 0;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
-    const u32x4_t v = src[i];
-    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  for (uint32_t i = threadIdx.x; i < cnt; i += 256 * U) {
+    u32x4_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (i + 256u * u) * 16u, 0, kStream);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
   __shared__ uint32_t s[256];
   s[threadIdx.x] = acc;
@@ -435,8 +450,11 @@ hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s) 
 hipError_t launch_read(const void *src, size_t bytes, float *sink, hipStream_t s) {
   const size_t n = bytes / 16;
   if (!n) return hipSuccess;
-  const size_t want = (n + 255) / 256;
+  // up to 4096 workgroups (the sink's length) of at least 4096 pieces each;
+  // a chunk's byte count must fit the buffer resource's 31 bits
+  const size_t want = (n + 4095) / 4096;
   const int grid = (int)(want < 4096 ? want : 4096);
+  if ((n + grid - 1) / grid >= ((size_t)1 << 27)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(read_kernel, dim3(grid), dim3(256), 0, s, (const u32x4_t *)src, n, sink);
   return hipGetLastError();
 }
