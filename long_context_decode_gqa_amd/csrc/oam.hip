@@ -167,13 +167,12 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
   constexpr int ES = I8 ? 1 : 2;            // bytes per K element
   // an int8 tile carries half the bytes of a bf16 one: more tiles in flight
   constexpr int NBUF = I8 ? 5 : kScoreBufs;
-  constexpr int kTilesPerWave = kScoreTok / 32 / 4;
   __shared__ uint32_t s_hist[kBins];
   __shared__ float s_qbar[D];
   __shared__ float s_sc[kScoreTok];
-  // paged: the page ids under each wave's tokens (at most kTilesPerWave * 32 /
-  // 32 + 1 pages, as a page holds a positive multiple of 32 tokens)
-  __shared__ int s_pages[PAGED ? 4 : 1][PAGED ? kScoreTok / 4 / 32 + 1 : 1];
+  // paged: the page ids under the workgroup's tokens (at most kScoreTok / 32
+  // + 1 pages, as a page holds a positive multiple of 32 tokens)
+  __shared__ int s_pages[PAGED ? kScoreTok / 32 + 1 : 1];
   const int pair = blockIdx.y;
   const int b = pair / o.KH, kh = pair - b * o.KH;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -205,13 +204,13 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
   const int nrec = (int)((uint32_t)(L - 1) * rs + D * ES);
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)o.k + head_off * ES), (short)0, nrec, 0x00020000);
-  // paged: this wave's page ids, staged once (a wave reads only its own)
-  const int wtok0 = blk0 + 32 * kTilesPerWave * wave;  // the wave's first token
-  const int wpage0 = PAGED ? wtok0 / o.page_tokens : 0;
+  // paged: the workgroup's page ids, staged once
+  const int bpage0 = PAGED ? blk0 / o.page_tokens : 0;
   if constexpr (PAGED) {
-    const int npg = min(kScoreTok / 4 / 32 + 1, (min(L, wtok0 + 32 * kTilesPerWave) - 1) / o.page_tokens - wpage0 + 1);
-    const int *tbl = o.block_table + (int64_t)b * o.table_stride + wpage0;
-    for (int i = lane; i < npg; i += 64) s_pages[wave][i] = max(tbl[i], 0);
+    const int npg = min(kScoreTok / 32 + 1, (min(L, blk0 + kScoreTok) - 1) / o.page_tokens - bpage0 + 1);
+    const int *tbl = o.block_table + (int64_t)b * o.table_stride + bpage0;
+    for (int i = tid; i < npg; i += 256) s_pages[i] = max(tbl[i], 0);
+    __syncthreads();
   }
   const __amdgpu_buffer_rsrc_t ksrs = __builtin_amdgcn_make_buffer_rsrc(
       I8 ? (void *)(o.k_scale + (int64_t)pair * o.k_scale_stride) : nullptr, (short)0,
@@ -239,8 +238,7 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
     int rbase = t0;
     if constexpr (PAGED) {
       const int pidx = t0 / o.page_tokens;
-      const int pg = __builtin_amdgcn_readfirstlane(
-          s_pages[wave][min(max(pidx - wpage0, 0), kScoreTok / 4 / 32)]);
+      const int pg = __builtin_amdgcn_readfirstlane(s_pages[min(max(pidx - bpage0, 0), kScoreTok / 32)]);
       const int prows = min(o.page_tokens, L - pidx * o.page_tokens);
       const int nrec_p = prows > 0 ? (int)((uint32_t)(prows - 1) * rs + D * ES) : 0;
       tk = __builtin_amdgcn_make_buffer_rsrc(
@@ -299,15 +297,20 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
       }
     }
   };
-  // This wave's tiles through a ring of NBUF register buffers: tile i is
-  // loaded NBUF-1 tiles before it is scored.  The step count is rounded up
-  // to a multiple of the ring; the extra steps load and publish nothing.
-  const int tw0 = kTilesPerWave * wave;
-  const int ntw = max(0, min(kTilesPerWave, (L - blk0 - 32 * tw0 + 31) / 32));
+  // The workgroup's tiles are dealt to its four waves in turn (wave w:
+  // tiles w, w + 4, ...), so together they read one contiguous stream (one
+  // stream per wave, 64 tiles each, measured 8 us slower on the 128K step).
+  // Each wave's tiles pass through a ring of NBUF register buffers: its
+  // j-th tile is loaded NBUF-1 tiles before it is scored.  The step count is
+  // rounded up to a multiple of the ring; the extra steps load and publish
+  // nothing.
+  const int ntile = min(kScoreTok / 32, (L - blk0 + 31) / 32);
+  const int ntw = max(0, (ntile - wave + 3) / 4);
   const int nst = (ntw + NBUF - 1) / NBUF * NBUF;
+  auto tile_at = [&](int j) { return wave + 4 * j; };
   KTile buf[NBUF];
 #pragma unroll
-  for (int j = 0; j + 1 < NBUF; ++j) load(buf[j], tw0 + j, j < ntw);
+  for (int j = 0; j + 1 < NBUF; ++j) load(buf[j], tile_at(j), j < ntw);
   // The query operand is built while the first tiles are in flight (the
   // queries' loads went out first, so waiting for them leaves the tiles').
   // mean query of the group, in fp32, summed in head order
@@ -365,19 +368,15 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
 #pragma unroll
     for (int j = 0; j < NBUF; ++j) {
       const int ahead = i + j + NBUF - 1;
-      load(buf[(j + NBUF - 1) % NBUF], tw0 + ahead, ahead < ntw);
-      compute(buf[j], tw0 + i + j, i + j < ntw);
+      load(buf[(j + NBUF - 1) % NBUF], tile_at(ahead), ahead < ntw);
+      compute(buf[j], tile_at(i + j), i + j < ntw);
     }
   }
-  // each wave writes its own tokens' scores as soon as its tiles are done
-  // (its LDS writes are its own), so early waves' writes overlap the others'
-  // loads instead of all landing after the workgroup's last tile
+  // the block's scores go out once, in full coalesced lines
   const int nblk_tok = min(kScoreTok, L - blk0);
-  if (o.write_scores) {
-    const int w0 = 32 * tw0, w1 = min(nblk_tok, w0 + 32 * kTilesPerWave);
-    for (int i = w0 + lane; i < w1; i += 64) sc[blk0 + i] = s_sc[i];
-  }
   __syncthreads();
+  if (o.write_scores)
+    for (int i = tid; i < nblk_tok; i += 256) sc[blk0 + i] = s_sc[i];
   if (token_mode) {
     uint32_t *gh = o.hist + (size_t)pair * kBins;
     for (int i = tid; i < kBins; i += 256)
