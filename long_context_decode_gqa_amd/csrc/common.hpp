@@ -274,14 +274,14 @@ __device__ __forceinline__ int64_t xcd_weight_sum(int w) {
   const int r = w & 7;
   return (int64_t)(w >> 3) * (4 * 16 + 4 * 15) + (int64_t)((r + 1) / 2) * 16 + (int64_t)(r / 2) * 15;
 }
-__device__ __forceinline__ StreamSplit stream_split(const DecodeParams &p, int T) {
+__device__ __forceinline__ StreamSplit stream_split(const DecodeParams &p, int T, bool xcd_weights) {
   StreamSplit r = {0, false};
   if (T == 0) return r;
   const int ct = p.split / 32;
   // floor(15 T / (16 ct)) >= grid, without the division
   if (p.ngb == 1 && (int64_t)T * 15 >= (int64_t)p.grid * 16 * ct) {
     r.W = p.grid;
-    r.weighted = true;
+    r.weighted = xcd_weights;
   } else {
     r.W = min(p.grid, max(1, T / ct));
   }

@@ -255,7 +255,11 @@ decode_mfma_kernel(DecodeParams p) {
   // fixed_splits = S > 0: the unbalanced schedule, worker w = q*S + s takes
   // split s of lane q; otherwise the balanced split of the whole stream
   const int FS = p.fixed_splits;
-  const StreamSplit split = stream_split(p, T);
+  // The XCD weights offset a slowness of the odd XCDs that the default
+  // cache policy shows; with non-temporal loads the XCDs stream alike (per
+  // worker clocks: with the weights, the even XCDs ended 6% later, the
+  // weights' own ratio), so a streaming launch splits equally.
+  const StreamSplit split = stream_split(p, T, !STREAM);
   const int nworkers = FS > 0 ? p.B * p.KH * FS : split.W;
   if (wv == 0) {
     // No worker visits a lane without positions, so its rows get out = 0 and
