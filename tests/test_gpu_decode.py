@@ -409,3 +409,19 @@ def test_fixed_splits_schedule_matches_oracle(splits):
                                     v_scale=float(vs.item()), fixed_splits=splits)
     torch.cuda.synchronize()
     check(o8.cpu().numpy().reshape(w.B * w.QH, w.D), lse8.cpu().numpy().reshape(-1), ref8, ref8_lse)
+
+
+def test_indexed_full_grid_uses_the_xcd_weighted_split():
+    """Kept-token attention whose lists hold every position of 4 x 8 lanes of 32768 tokens: enough
+    tiles for the whole grid under the default cache policy, so the XCD-weighted work split runs
+    (streaming launches split equally, and gathered rows keep the default policy).  Listing every
+    position makes it dense attention: every output row and lse against the oracle's."""
+    L = 32768
+    w = synth.workload("gqa32k", B=4, KH=8, G=8, lens=np.full(4, L, np.int32), layout="head_major", seed=176)
+    q, k, v, g = synth.generate(w)
+    idx = np.tile(np.arange(L, dtype=np.int32), (w.B * w.KH, 1))
+    nk = np.full(w.B * w.KH, L, np.int32)
+    log_case("indexed, every position listed, full grid")
+    out, lse = run_decode(w, q, k, v, g, token_idx=to_dev(idx), n_idx=to_dev(nk))
+    ref, ref_lse = oracle_all_rows(problem(w, q, k, v, g))
+    check(out, lse, ref, ref_lse)
