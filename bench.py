@@ -145,10 +145,11 @@ def dev_geom(pkg, torch, g, dev):
 
 def time_decode(torch, prepared, steps, warmup):
     """Returns a dict of ms: `step` = mean of `steps` plain calls back to back between two events;
-    `decode` / `merge` = mean duration of the decode and merge launches, from a second run of
-    `steps` calls through the profiled entry point, whose events sit on the calls' stream around
-    each launch (bf16/int8 KV: the merge runs inside the decode launch, so `merge` is ~0 and
-    `decode` is the whole step); `median` / `min` = of those per-call decode+merge durations."""
+    `decode` = mean duration of the decode launch, from a second run of `steps` calls through the
+    profiled entry point, whose events sit on the calls' stream around each launch (bf16/int8 KV:
+    the merge runs inside the decode launch, so that launch is the whole step, and the profiled
+    entry point's merge phase is empty: its two events only measure their own gap, about 4.5 us,
+    which is left out); `median` / `min` = of those per-call decode launch durations."""
     for _ in range(warmup):
         prepared()
     t = Timer(torch, steps)
@@ -163,10 +164,8 @@ def time_decode(torch, prepared, steps, warmup):
         prepared.profiled(t.phase[i])
     torch.cuda.synchronize()
     dk = [e[0].elapsed_time(e[1]) for e in t.phase]
-    mg = [e[1].elapsed_time(e[2]) for e in t.phase]
-    per = sorted(a + b for a, b in zip(dk, mg))
-    return {"step": total / steps, "decode": sum(dk) / steps, "merge": sum(mg) / steps,
-            "median": per[len(per) // 2], "min": per[0]}
+    per = sorted(dk)
+    return {"step": total / steps, "decode": sum(dk) / steps, "median": per[len(per) // 2], "min": per[0]}
 
 
 # ------------------------------------------------------------------ workloads
@@ -192,7 +191,7 @@ def bench_dense(pkg, torch, synth, name, steps, warmup, dev, unbalanced=False, *
     kvb = kv_bytes(tokens, w.KH, w.D, 2)
     # the bytes the step must move: K/V once, Q in and out (bf16 Q, fp32 out)
     algo = kvb + w.B * w.QH * w.D * (2 + 4)
-    res = dict(w=w, q=q, g=g, t=t, ms=t["step"], decode_ms=t["decode"], merge_ms=t["merge"], kv_bytes=kvb,
+    res = dict(w=w, q=q, g=g, t=t, ms=t["step"], decode_ms=t["decode"], kv_bytes=kvb,
                decode_algo_bytes=algo, tokens=tokens, split=p.split_tokens)
     if unbalanced:
         # The unbalanced schedules on the same inputs, every (b, kh) in the same number of equal
@@ -217,7 +216,7 @@ def summary(r, extra=None, probe_gbs=None):
     d = {"us_per_step": round(r["ms"] * 1e3, 2), "kv_gbs": round(r["kv_bytes"] / r["ms"] / 1e6, 1),
          "frac_of_peak": round(r["kv_bytes"] / r["ms"] / 1e6 / HBM_PEAK_GBS, 4),
          "us_per_step_median": round(r["t"]["median"] * 1e3, 2), "us_per_step_min": round(r["t"]["min"] * 1e3, 2),
-         "decode_kernel_us": round(r["decode_ms"] * 1e3, 2), "merge_us": round(r["merge_ms"] * 1e3, 2),
+         "decode_kernel_us": round(r["decode_ms"] * 1e3, 2),
          "kernel_kv_gbs": round(r["kv_bytes"] / r["decode_ms"] / 1e6, 1),
          "kernel_frac_of_peak": round(r["kv_bytes"] / r["decode_ms"] / 1e6 / HBM_PEAK_GBS, 4)}
     if probe_gbs:
@@ -288,7 +287,7 @@ def bench_int8(pkg, torch, synth, steps, warmup, dev):
         schemes[name] = {"us_per_step": round(ms_s * 1e3, 2), "decode_kernel_us": round(dk_s * 1e3, 2),
                          "kv_gbs": round(b / ms_s / 1e6, 1), "rel_err_vs_bf16": round(err, 5)}
         del ps
-    return dict(t=t, ms=t["step"], decode_ms=t["decode"], merge_ms=t["merge"], kv_bytes=kvb, split=p.split_tokens,
+    return dict(t=t, ms=t["step"], decode_ms=t["decode"], kv_bytes=kvb, split=p.split_tokens,
                 schemes=schemes,
                 quant=quant)
 
@@ -324,7 +323,7 @@ def bench_paged(pkg, torch, synth, steps, warmup, dev, page_tokens=64, layout="h
     qd = to_dev(torch, q.reshape(-1), dev).view(w.B, w.QH, w.D)
     p = pkg.prepare_decode(qd, kp, vp, geom, w.G, split_tokens=w.split_tokens)
     t = time_decode(torch, p, steps, warmup)
-    res = dict(t=t, ms=t["step"], decode_ms=t["decode"], merge_ms=t["merge"], kv_bytes=kv_bytes(w.kv_tokens(), KH, D, 2),
+    res = dict(t=t, ms=t["step"], decode_ms=t["decode"], kv_bytes=kv_bytes(w.kv_tokens(), KH, D, 2),
                split=p.split_tokens)
     if layout == "head_major":
         # OAM selection (top 4096 of the 128K tokens) over the same pool, value term cached
@@ -375,7 +374,7 @@ def bench_multirow(pkg, torch, synth, steps, warmup, dev, R):
     qd = to_dev(torch, q.reshape(-1), dev).view(w.B, R, w.QH, w.D)
     p = pkg.prepare_decode(qd, kd, vd, geom, w.G, split_tokens=w.split_tokens, q_rows=R)
     t = time_decode(torch, p, steps, warmup)
-    return dict(t=t, ms=t["step"], decode_ms=t["decode"], merge_ms=t["merge"], kv_bytes=kv_bytes(w.kv_tokens(), w.KH, w.D, 2),
+    return dict(t=t, ms=t["step"], decode_ms=t["decode"], kv_bytes=kv_bytes(w.kv_tokens(), w.KH, w.D, 2),
                 split=p.split_tokens)
 
 
@@ -614,7 +613,7 @@ def main():
                    "eq6_bytes_per_step": decode_eq_elements(w.B, w.KH, w.G, w.D, int(w.lens[0])) * 2,
                    "flops_per_step": decode_eq_flops(w.B, w.QH, int(w.lens[0]), w.D)},
         "phases_us": {"decode": round(head["decode_ms"] * 1e3, 2),
-                      "merge": round(head["merge_ms"] * 1e3, 2), "launches_per_step": 1},
+                      "launches_per_step": 1},
         "roofline": roofline,
     }
     if not args.headline_only:
