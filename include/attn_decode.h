@@ -166,7 +166,11 @@ typedef struct {
  *               long (fewer workers when there is less work); a (b, kh)
  *               then spans at most ceil(L_b / split_tokens) + 1 ranges, each
  *               giving one partial.  Default 4096 (with token_idx 512 kept
- *               tokens, up to 1024 for long lists).
+ *               tokens, up to 1024 for long lists; over token-major pages
+ *               of a paged cache 2048, with twice the workers that fit at
+ *               once).  With a given split_tokens the split depends only on
+ *               the lengths, so equal split_tokens give bit-identical
+ *               results over every cache layout.
  *               fp32 KV: chunks of split_tokens positions, default 256.
  *               attn_decode_split_tokens reports the choice
  *   workspace   caller-owned scratch of at least attn_decode_workspace_size()

@@ -93,6 +93,11 @@ I8 = dict(kv_dtype=_lib.ATTN_I8, k_scale=FAKE, k_part_tokens=64, k_scale_stride=
     (dict(g_B=1, g_KH=1, g_max_seq_len=4096), 4096),
     (dict(g_B=4, g_max_seq_len=131072, g_seq_offset=None, g_block_table=FAKE, g_page_tokens=32,
           g_table_stride=4096, g_page_stride=32 * 8 * 128, **I8), 4096),
+    # token-major pages (a KV head's rows KH * D apart): twice the workers over half the range
+    (dict(g_B=4, g_max_seq_len=131072, g_seq_offset=None, g_block_table=FAKE, g_page_tokens=64,
+          g_table_stride=2048, g_page_stride=64 * 8 * 128, g_stride_h=128, g_stride_t=8 * 128), 2048),
+    # a contiguous token-major cache keeps the one-round split
+    (dict(g_B=4, g_max_seq_len=131072, g_stride_h=128, g_stride_t=8 * 128), 4096),
     # kept-token lists: at least 512 and at most 1024 kept tokens per worker
     (dict(g_B=4, g_max_seq_len=131072, token_idx=FAKE, n_idx=FAKE, idx_stride=4096), 512),
     (dict(g_B=4, g_max_seq_len=131072, token_idx=FAKE, n_idx=FAKE, idx_stride=4096, **I8), 512),
