@@ -23,17 +23,41 @@ namespace {
 constexpr int kWT = 32;      // tokens per tile of the work split (the lane walk's unit)
 constexpr int kVMaxD = 256;  // largest head size
 
-// max / sum over the W lanes of a lane group (W = 32 or 64)
+// max / sum over the W lanes of a lane group (W = 32 or 64), every lane of the
+// group getting the result: DPP moves inside each row of 16 lanes (swap
+// neighbours, swap pairs, mirror each half-row, mirror the row), then the row
+// swaps of gfx950 (rows 0<->1, 2<->3, and for W = 64 the two halves), with no
+// trip through the LDS crossbar.
+template <int C>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), C, 0xF, 0xF, false));
+}
 template <int W>
 __device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int o = W / 2; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, W));
+  v = fmaxf(v, dpp_move<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_move<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_move<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_move<0x140>(v));  // row_mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  if constexpr (W == 64) {
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  }
   return v;
 }
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = W / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, W);
+  v += dpp_move<0xB1>(v);
+  v += dpp_move<0x4E>(v);
+  v += dpp_move<0x141>(v);
+  v += dpp_move<0x140>(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  if constexpr (W == 64) {
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  }
   return v;
 }
 
