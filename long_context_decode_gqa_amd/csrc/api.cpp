@@ -292,7 +292,8 @@ attn_status attn_decode_split_tokens(const attn_decode_args *args, int32_t *spli
 
 namespace lcdg {
 
-// The 40-bit tag of one call's arrival counters.  Each counter array (a
+// The 40-bit tag of one call's arrival counters (or of the OAM selection's
+// histogram words, which follow the same rule).  Each counter array (a
 // workspace address and layout) gets the tag after the one its previous call
 // used, which is the tag that call's last arrivals left in the words, so the
 // common case costs one atomic add per arrival; an array not seen recently
@@ -300,7 +301,7 @@ namespace lcdg {
 // sequence, and its first arrivals take the words over.  Tags change with
 // every call, so words left by any earlier call are never mistaken for live
 // counts of this one.
-static uint64_t counter_tag_for(const void *ctr) {
+uint64_t counter_tag_for(const void *ctr) {
   constexpr uint64_t kMask = (uint64_t(1) << 40) - 1;
   static std::mutex mu;
   static const void *addr[64] = {nullptr};

@@ -86,7 +86,7 @@ attn_status oam_value_lognorm(const attn_kv_geom *geom, const void *v, int32_t v
 namespace {
 
 struct OamLayout {
-  size_t scores, vlog, hist, state, blk_gt, blk_off, blk_nc, cand_key, cand_idx, bscores, total;
+  size_t scores, vlog, hist, state, blk_gt, blk_nc, cand_key, cand_idx, bscores, total;
   int32_t bs_stride;
 };
 
@@ -148,10 +148,9 @@ attn_status plan_oam(const oam_topk_args *a, OamLayout *L) {
   L->scores = off; off = al(off + (a->scores_out ? 0 : npairs * stride * sizeof(float)));
   L->vlog = off; off = al(off + (a->vlog ? 0 : npairs * stride * sizeof(float)));
   const size_t nblk_max = (size_t)oam_max_tokens() / 2048;
-  L->hist = off; off = al(off + (size_t)npairs * 2048 * sizeof(uint32_t));
+  L->hist = off; off = al(off + (size_t)npairs * 2048 * sizeof(uint64_t));
   L->state = off; off = al(off + (size_t)npairs * 8 * sizeof(int32_t));
   L->blk_gt = off; off = al(off + (size_t)npairs * nblk_max * sizeof(int32_t));
-  L->blk_off = off; off = al(off + (size_t)npairs * nblk_max * sizeof(int32_t));
   L->blk_nc = off; off = al(off + (size_t)npairs * nblk_max * sizeof(int32_t));
   L->cand_key = off; off = al(off + (size_t)npairs * stride * sizeof(uint32_t));
   L->cand_idx = off; off = al(off + (size_t)npairs * stride * sizeof(int32_t));
@@ -188,13 +187,12 @@ attn_status oam_score_topk(const oam_topk_args *a, attn_stream_t stream) {
   plan.score_stride = a->kv.max_seq_len;
   plan.vlog = a->vlog ? const_cast<float *>(a->vlog) : reinterpret_cast<float *>(ws + L.vlog);
   plan.vlog_stride = a->vlog ? a->vlog_stride : a->kv.max_seq_len;
-  plan.hist = reinterpret_cast<uint32_t *>(ws + L.hist);
+  plan.hist = reinterpret_cast<uint64_t *>(ws + L.hist);
   plan.blk_nc = reinterpret_cast<int32_t *>(ws + L.blk_nc);
   plan.bscores = reinterpret_cast<float *>(ws + L.bscores);
   plan.bs_stride = L.bs_stride;
   plan.state = reinterpret_cast<int32_t *>(ws + L.state);
   plan.blk_gt = reinterpret_cast<int32_t *>(ws + L.blk_gt);
-  plan.blk_off = reinterpret_cast<int32_t *>(ws + L.blk_off);
   plan.cand_key = reinterpret_cast<uint32_t *>(ws + L.cand_key);
   plan.cand_idx = reinterpret_cast<int32_t *>(ws + L.cand_idx);
   hipError_t e = launch_oam(*a, plan, reinterpret_cast<hipStream_t>(stream));

@@ -381,10 +381,9 @@ struct OamPlan {
   int32_t score_stride;
   float *vlog;           // value log-norms: the caller's or computed into the workspace
   int32_t vlog_stride;
-  uint32_t *hist;        // [npairs][2048] level-0 key histogram, followed by
+  uint64_t *hist;        // [npairs][2048] level-0 key histogram, tagged words (tag << 24) | count
   int32_t *state;        // [npairs][8] selection state
   int32_t *blk_gt;       // [npairs][oam_max_tokens() / 2048]
-  int32_t *blk_off;      // [npairs][oam_max_tokens() / 2048]
   int32_t *blk_nc;       // [npairs][1024] candidates per block
   float *bscores;        // [npairs][bs_stride] block scores (block-granular selection)
   int32_t bs_stride;
@@ -396,5 +395,7 @@ int oam_max_tokens();  // longest sequence oam_score_topk selects over
 int oam_max_select_blocks();  // most token blocks per pair in block-granular selection
 
 int device_cu_count();
+// The tag of the next call on a tagged counter array (arrival counters, OAM histogram words).
+uint64_t counter_tag_for(const void *ctr);
 
 }  // namespace lcdg

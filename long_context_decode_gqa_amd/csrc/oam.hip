@@ -11,19 +11,21 @@
 //   score      (token blocks x pairs) S = K Q^T on the matrix cores, mean over
 //              the G heads, scale, + beta * vlog; write the fp32 score and
 //              count the top 11 key bits into the pair's level-0 histogram.
+//              The histogram's words carry a per-call tag (the rule of the
+//              decode's arrival counters), so no pass has to clear them.
 //   candidates (2048-token blocks x pairs) every block reads the pair's
 //              histogram and finds the threshold's top digit b0 (all blocks
 //              find the same); it counts its keys above bin b0 and writes its
 //              keys of bin b0, with their indices, to its own region of the
 //              pair's candidate array, and their count.
-//   select     (one workgroup per pair) gathers the candidates into LDS, then
-//              finds the exact threshold key T and the last kept index I_T
-//              among keys equal to T; then the output offset of every block.
-//              (If there are more candidates than LDS holds - many equal
-//              scores - it selects over the pair's scores directly.)
-//   write      (2048-token blocks x pairs) ordered compaction of the kept
-//              tokens, key > T or (key == T and index <= I_T), at the block's
-//              offset, so idx_out is ascending.
+//   select and write (8192-token blocks x pairs) every block gathers the
+//              pair's candidates (into LDS when they fit) and finds the exact
+//              threshold key T and the last kept index I_T among keys equal to
+//              T (all blocks of a pair find the same), then its output offset
+//              (keys above bin b0 and kept candidates of the blocks before it)
+//              and writes its kept tokens, key > T or (key == T and index <=
+//              I_T), in index order, so idx_out is ascending.  Repeating the
+//              selection in every block costs less than one more launch.
 // Only integer atomics (histogram counts) cross workgroups within a pass.
 #include "common.hpp"
 
@@ -32,7 +34,8 @@ namespace {
 
 constexpr int kBins = 2048;       // 11-bit digits (the 10-bit ones use 1024)
 constexpr int kBlockTok = 2048;   // tokens per workgroup of the candidate and write passes
-constexpr int kCandCap = 12288;   // candidates the select pass holds in LDS (10 bytes each)
+constexpr int kSWTok = 8192;      // tokens per workgroup of the select-and-write pass
+constexpr int kSWCap = 6144;      // candidates a select-and-write workgroup holds in LDS (10 bytes each)
 constexpr int kMaxBlocks = 1024;  // blocks of kBlockTok per pair (sequences up to 2M tokens)
 constexpr int kMaxSelBlocks = 8192;  // token blocks per pair the block-granular select holds
 
@@ -41,13 +44,11 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Per-pair selection state, passed from one pass to the next.
+// Per-pair selection state, passed from the candidate pass to the next.
 struct OamState {
   int32_t b0;        // top 11 bits of the threshold key
   int32_t need;      // keys of bin b0 to keep
-  uint32_t T;        // threshold key
-  int32_t I_T;       // last kept index among keys equal to T
-  int32_t pad[4];
+  int32_t pad[6];
 };
 
 struct OamDev {
@@ -66,10 +67,10 @@ struct OamDev {
   int32_t vlog_stride;
   float score_scale, beta;
   float *scores;       // [npairs][L_max]
-  uint32_t *hist;      // [npairs][kBins]  level-0 histogram
+  uint64_t *hist;      // [npairs][kBins]  level-0 histogram, words (hist_tag << 24) | count
+  uint64_t hist_tag;   // this call's 40-bit tag; words with another tag count zero
   OamState *state;     // [npairs]
   int32_t *blk_gt;     // [npairs][kMaxBlocks]  keys above bin b0 per block
-  int32_t *blk_off;    // [npairs][kMaxBlocks]  first output slot per block
   int32_t *blk_nc;     // [npairs][kMaxBlocks]  candidates (keys in bin b0) per block
   uint32_t *cand_key;  // [npairs][L_max]  block j's candidates at [j*kBlockTok, + blk_nc)
   int32_t *cand_idx;   // [npairs][L_max]
@@ -135,8 +136,27 @@ __device__ int select_bin(const uint32_t *hist, int nb, int need, int *above, in
   return bin;
 }
 
-__global__ __launch_bounds__(256) void zero_kernel(uint32_t *p, size_t n) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
+// Adds cnt to a histogram word of this call (tag): the arrival-counter rule
+// with a count.  A word with another tag (left by an earlier call on the
+// workspace, or other data) is taken over by compare-and-swap with the tagged
+// count cnt; when another workgroup took it over first, cnt is added again
+// (the first add went into the old word).  Every failed exchange means that
+// another workgroup changed the word, so the loop ends.
+__device__ __forceinline__ void tagged_add(uint64_t *w, uint32_t cnt, uint64_t tag) {
+  const uint64_t old = __hip_atomic_fetch_add(w, (uint64_t)cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((old >> 24) == tag) return;
+  uint64_t cur = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (;;) {
+    if ((cur >> 24) == tag) {
+      __hip_atomic_fetch_add(w, (uint64_t)cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    uint64_t expect = cur;
+    if (__hip_atomic_compare_exchange_strong(w, &expect, (tag << 24) | cnt, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return;
+    cur = expect;
+  }
 }
 
 // Score pass.  The mean query of the KV head's G heads, q_bar (fp32), is
@@ -378,9 +398,9 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
   if (o.write_scores)
     for (int i = tid; i < nblk_tok; i += 256) sc[blk0 + i] = s_sc[i];
   if (token_mode) {
-    uint32_t *gh = o.hist + (size_t)pair * kBins;
+    uint64_t *gh = o.hist + (size_t)pair * kBins;
     for (int i = tid; i < kBins; i += 256)
-      if (s_hist[i]) atomicAdd(gh + i, s_hist[i]);
+      if (s_hist[i]) tagged_add(gh + i, s_hist[i], o.hist_tag);
   } else {
     // block scores: the mean of each block's token scores (block_tokens is a
     // power of two dividing kScoreTok, so blocks never straddle workgroups)
@@ -397,53 +417,75 @@ __global__ __launch_bounds__(256) void oam_score_kernel(OamDev o) {
   }
 }
 
-// Exact selection inside bin b0 by the select pass: the
-// need-th largest key T among the items of bin b0, and, among the items equal
-// to T, the need'-th smallest index I_T (need' = how many of them are kept).
-// Items come from the candidate list or, if it overflowed, from all scores.
-// Calls f(key, idx) for the items 0..n-1, thread tid taking i = tid + 256 r:
-// the candidate list in LDS, or the pair's whole score row, whose loads are
-// issued 16 per thread before any is used.
-template <bool FROM_LIST, typename F>
-__device__ __forceinline__ void for_items(const uint32_t *ck, const int32_t *ci, const float *sc, int n, F &&f) {
+// The candidate block holding item i of a pair's gathered candidate list:
+// the last block j with s_pre[j] <= i (s_pre: the blocks' first items,
+// s_pre[nblk] the total; blocks without candidates start where the next one
+// does, so the last such j is the one whose items include i).
+__device__ __forceinline__ int block_of(const int *s_pre, int nblk, int i) {
+  int lo = 0, hi = nblk - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_pre[mid] <= i) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Where the exact selection reads the candidates (keys of bin b0 and their
+// indices): a copy gathered in LDS, or the pair's candidate regions in
+// global memory (block j's items at j * kBlockTok, located through s_pre).
+enum { kFromLds = 0, kFromGlobal = 1 };
+
+// Calls f(key, idx) for the items 0..n-1, thread tid taking i = tid + 256 r;
+// from global memory 16 items' loads per thread are issued before any is used.
+template <int SRC, typename F>
+__device__ __forceinline__ void for_items(const uint32_t *ck, const int32_t *ci, const int *s_pre, int nblk, int n,
+                                          F &&f) {
   const int tid = threadIdx.x;
-  if constexpr (FROM_LIST) {
+  if constexpr (SRC == kFromLds) {
     for (int i = tid; i < n; i += 256) f(ck[i], ci[i]);
   } else {
     constexpr int U = 16;
     for (int i0 = 0; i0 < n; i0 += 256 * U) {
-      float v[U];
+      uint32_t kr[U];
+      int32_t ir[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = sc[min(i0 + tid + 256 * u, n - 1)];
+      for (int u = 0; u < U; ++u) {
+        const int i = min(i0 + tid + 256 * u, n - 1);
+        const int j = block_of(s_pre, nblk, i);
+        const int64_t src = (int64_t)j * kBlockTok + (i - s_pre[j]);
+        kr[u] = ck[src];
+        ir[u] = ci[src];
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int i = i0 + tid + 256 * u;
-        if (i < n) f(order_key(v[u]), i);
+        if (i < n) f(kr[u], ir[u]);
       }
     }
   }
 }
 
-template <bool FROM_LIST>
-__device__ void select_threshold(const OamDev &o, int pair, int n, int b0, int need, const uint32_t *ck,
-                                 const int32_t *ci, uint32_t *s_hist, int *s_tmp, int *s_res, uint32_t *T_out,
-                                 int *I_out) {
+// Exact selection inside bin b0 over the pair's n >= need candidates: the
+// need-th largest key T, and, among the candidates equal to T, the need'-th
+// smallest index I_T (need' = how many of them are kept; I_T = INT_MAX when
+// all of them are).  All 256 threads call it and get the result.
+template <int SRC>
+__device__ void select_threshold(int n, int b0, int need, const uint32_t *ck, const int32_t *ci, const int *s_pre,
+                                 int nblk, uint32_t *s_hist, int *s_tmp, int *s_res, uint32_t *T_out, int *I_out) {
   const int tid = threadIdx.x;
-  const float *sc = o.scores + (int64_t)pair * o.L_max;
   int above;
-  // digit 2: key bits 20..10 of the items with top digit b0
+  // digit 2: key bits 20..10 (every candidate has top digit b0)
   for (int i = tid; i < kBins; i += 256) s_hist[i] = 0u;
   __syncthreads();
-  for_items<FROM_LIST>(ck, ci, sc, n, [&](uint32_t key, int idx) {
-    if ((int)(key >> 21) == b0) atomicAdd(&s_hist[(key >> 10) & 0x7FFu], 1u);
-  });
+  for_items<SRC>(ck, ci, s_pre, nblk, n, [&](uint32_t key, int idx) { atomicAdd(&s_hist[(key >> 10) & 0x7FFu], 1u); });
   __syncthreads();
   uint32_t prefix = ((uint32_t)b0 << 11) | (uint32_t)select_bin(s_hist, kBins, need, &above, s_tmp, s_res);
   need -= above;
   // digit 3: key bits 9..0
   for (int i = tid; i < kBins; i += 256) s_hist[i] = 0u;
   __syncthreads();
-  for_items<FROM_LIST>(ck, ci, sc, n, [&](uint32_t key, int idx) {
+  for_items<SRC>(ck, ci, s_pre, nblk, n, [&](uint32_t key, int idx) {
     if ((key >> 10) == prefix) atomicAdd(&s_hist[key & 0x3FFu], 1u);
   });
   __syncthreads();
@@ -462,7 +504,7 @@ __device__ void select_threshold(const OamDev &o, int pair, int n, int b0, int n
   // bits of the index, bins reversed so "largest bin" means smallest index
   for (int i = tid; i < kBins; i += 256) s_hist[i] = 0u;
   __syncthreads();
-  for_items<FROM_LIST>(ck, ci, sc, n, [&](uint32_t key, int idx) {
+  for_items<SRC>(ck, ci, s_pre, nblk, n, [&](uint32_t key, int idx) {
     if (key == T) atomicAdd(&s_hist[2047 - (idx >> 10)], 1u);
   });
   __syncthreads();
@@ -470,7 +512,7 @@ __device__ void select_threshold(const OamDev &o, int pair, int n, int b0, int n
   need -= above;
   for (int i = tid; i < kBins; i += 256) s_hist[i] = 0u;
   __syncthreads();
-  for_items<FROM_LIST>(ck, ci, sc, n, [&](uint32_t key, int idx) {
+  for_items<SRC>(ck, ci, s_pre, nblk, n, [&](uint32_t key, int idx) {
     if (key == T && (idx >> 10) == ihi) atomicAdd(&s_hist[1023 - (idx & 0x3FF)], 1u);
   });
   __syncthreads();
@@ -495,7 +537,7 @@ __global__ __launch_bounds__(256) void oam_candidate_kernel(OamDev o) {
   // histogram only and the score loads' latency overlaps it.
   const float *sc = o.scores + (int64_t)pair * o.L_max;
   const int n = min(kBlockTok, L - blk0);
-  uint32_t hv[kBins / 256];
+  uint64_t hv[kBins / 256];
 #pragma unroll
   for (int j = 0; j < kBins / 256; ++j) hv[j] = o.hist[(size_t)pair * kBins + tid + 256 * j];
   // unconditional buffer loads (past n they read zero), so the wait for the
@@ -506,8 +548,10 @@ __global__ __launch_bounds__(256) void oam_candidate_kernel(OamDev o) {
 #pragma unroll
   for (int j = 0; j < 8; ++j)
     sv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(srs, (uint32_t)(tid + 256 * j) * 4u, 0, 0));
+  // words without this call's tag count zero
 #pragma unroll
-  for (int j = 0; j < kBins / 256; ++j) s_hist[tid + 256 * j] = hv[j];
+  for (int j = 0; j < kBins / 256; ++j)
+    s_hist[tid + 256 * j] = (hv[j] >> 24) == o.hist_tag ? (uint32_t)(hv[j] & 0xFFFFFFu) : 0u;
   __syncthreads();
   int above;
   const int b0 = select_bin(s_hist, kBins, o.top_k, &above, s_tmp, s_res);
@@ -546,46 +590,78 @@ __global__ __launch_bounds__(256) void oam_candidate_kernel(OamDev o) {
   }
 }
 
-// Select pass, one workgroup per pair: T and I_T, then the output offset of
-// every block (keys above bin b0 plus kept keys of bin b0 before it).
-__global__ __launch_bounds__(256) void oam_select_kernel(OamDev o) {
+// Select-and-write pass, (kSWTok-token blocks) x pairs.  Block 0 of a pair
+// sets n_kept and fills idx_out past it with -1, and leaves the pair's
+// histogram words at zero counts under the next call's tag (the candidate
+// pass, their last reader, is complete).  Each block then selects T and I_T
+// from the pair's candidates, counts what the blocks before it keep, and
+// writes its own kept tokens in order: thread t holds tokens 32t..32t+31 of
+// the block.
+__global__ __launch_bounds__(256) void oam_select_write_kernel(OamDev o) {
   __shared__ uint32_t s_hist[kBins];
-  __shared__ int s_kept[kMaxBlocks];
   __shared__ int s_pre[kMaxBlocks + 1];
-  __shared__ uint32_t s_ck[kCandCap];
-  __shared__ int32_t s_ci[kCandCap];
-  __shared__ uint16_t s_own[kCandCap];  // block of each gathered candidate
+  __shared__ uint32_t s_ck[kSWCap];
+  __shared__ int32_t s_ci[kSWCap];
+  __shared__ uint16_t s_own[kSWCap];  // candidate block of each gathered item
   __shared__ int s_tmp[4], s_res[2];
-  const int pair = blockIdx.x;
+  const int pair = blockIdx.y;
   const int L = pair_len(o, pair);
-  if (L == 0 || o.top_k >= L) return;
   const int tid = threadIdx.x;
+  int32_t *out = o.idx_out + (int64_t)pair * o.top_k;
+  if (blockIdx.x == 0) {
+    const int nk = min(o.top_k, L);
+    if (tid == 0) o.n_kept[pair] = nk;
+    for (int i = nk + tid; i < o.top_k; i += 256) out[i] = -1;
+    uint64_t *gh = o.hist + (size_t)pair * kBins;
+    const uint64_t next = ((o.hist_tag + 1) & ((1ull << 40) - 1)) << 24;
+    for (int i = tid; i < kBins; i += 256) gh[i] = next;
+  }
+  const int blk0 = blockIdx.x * kSWTok;
+  if (blk0 >= L) return;
+  const int n = min(kSWTok, L - blk0);
+  if (o.top_k >= L) {  // every token is kept
+    for (int i = tid; i < n; i += 256) out[blk0 + i] = blk0 + i;
+    return;
+  }
+  // this block's scores first (buffer loads past n read zero), so their
+  // latency overlaps the selection
+  const float *sc = o.scores + (int64_t)pair * o.L_max;
+  const __amdgpu_buffer_rsrc_t srs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(sc + blk0), (short)0, n * 4, 0x00020000);
+  u32x4_t sv[kSWTok / 1024];
+#pragma unroll
+  for (int j = 0; j < kSWTok / 1024; ++j)
+    sv[j] = __builtin_amdgcn_raw_buffer_load_b128(srs, (uint32_t)(kSWTok / 256 * tid + 4 * j) * 4u, 0, 0);
   const int b0 = o.state[pair].b0, need = o.state[pair].need;
   const int nblk = (L + kBlockTok - 1) / kBlockTok;
-  // where each block's candidates start in the gathered list
-  int C = 0;
+  const int jf = blk0 / kBlockTok;  // this block's first candidate block
+  // where each candidate block's items start in the gathered list, and the
+  // keys above bin b0 in the candidate blocks before jf
+  int C = 0, gt_before = 0;
   for (int j0 = 0; j0 < nblk; j0 += 256) {
     const int j = j0 + tid;
     const int v = j < nblk ? o.blk_nc[(size_t)pair * kMaxBlocks + j] : 0;
-    int tot;
+    const int g = j < jf ? o.blk_gt[(size_t)pair * kMaxBlocks + j] : 0;
+    int tot, gtot;
     const int ex = block_exclusive_scan(v, s_tmp, &tot);
+    block_exclusive_scan(g, s_tmp, &gtot);
     if (j < nblk) s_pre[j] = C + ex;
     C += tot;
+    gt_before += gtot;
   }
   if (tid == 0) s_pre[nblk] = C;
   __syncthreads();
+  const uint32_t *gk = o.cand_key + (int64_t)pair * o.L_max;
+  const int32_t *gi = o.cand_idx + (int64_t)pair * o.L_max;
+  const int nbefore = s_pre[jf];  // candidates of the blocks before jf
   uint32_t T;
-  int I_T;
-  const bool in_lds = C > 0 && C <= kCandCap;
-  if (in_lds) {
-    // Gather into LDS: item i lies in the block j with s_pre[j] <= i < s_pre[j+1].
-    constexpr int kPer = 16;  // loads of one gather round per thread
-    const uint32_t *gk = o.cand_key + (int64_t)pair * o.L_max;
-    const int32_t *gi = o.cand_idx + (int64_t)pair * o.L_max;
-    // Owner map first (LDS only): wave w writes block j's number over its
-    // items, for blocks j = w, w+4, ...  Then each item costs two LDS reads
-    // before its loads, and all of a thread's loads are in flight together
-    // (clamped to the last item, so they are unconditional).
+  int I_T, kc_before = 0;
+  if (C <= kSWCap) {
+    // Gather into LDS.  Owner map first (LDS only): wave w writes block j's
+    // number over its items, for blocks j = w, w+4, ...; then each item costs
+    // two LDS reads before its loads, and all of a thread's loads are in
+    // flight together (clamped to the last item, so they are unconditional).
+    constexpr int kPer = 16;
     const int wave = tid >> 6, lane = tid & 63;
     for (int j = wave; j < nblk; j += 4)
       for (int l = s_pre[j] + lane; l < s_pre[j + 1]; l += 64) s_own[l] = (uint16_t)j;
@@ -611,107 +687,38 @@ __global__ __launch_bounds__(256) void oam_select_kernel(OamDev o) {
       }
     }
     __syncthreads();
-    select_threshold<true>(o, pair, C, b0, need, s_ck, s_ci, s_hist, s_tmp, s_res, &T, &I_T);
+    select_threshold<kFromLds>(C, b0, need, s_ck, s_ci, s_pre, nblk, s_hist, s_tmp, s_res, &T, &I_T);
+    for_items<kFromLds>(s_ck, s_ci, s_pre, nblk, nbefore,
+                        [&](uint32_t key, int idx) { kc_before += key > T || (key == T && idx <= I_T); });
   } else {
-    select_threshold<false>(o, pair, L, b0, need, nullptr, nullptr, s_hist, s_tmp, s_res, &T, &I_T);
+    select_threshold<kFromGlobal>(C, b0, need, gk, gi, s_pre, nblk, s_hist, s_tmp, s_res, &T, &I_T);
+    for_items<kFromGlobal>(gk, gi, s_pre, nblk, nbefore,
+                           [&](uint32_t key, int idx) { kc_before += key > T || (key == T && idx <= I_T); });
   }
-  if (in_lds) {
-    // the gathered list is in block order (block j's candidates are items
-    // s_pre[j] .. s_pre[j+1]-1), so wave w counts blocks w, w+4, ... with
-    // ballots: per-item atomics on one block's counter would serialise
-    const int wave = tid >> 6, lane = tid & 63;
-    for (int j = wave; j < nblk; j += 4) {
-      int cnt = 0;
-      for (int i0 = s_pre[j]; i0 < s_pre[j + 1]; i0 += 64) {
-        const int i = i0 + lane;
-        bool kept = false;
-        if (i < s_pre[j + 1]) {
-          const uint32_t key = s_ck[i];
-          kept = key > T || (key == T && s_ci[i] <= I_T);
-        }
-        cnt += __popcll(__ballot(kept));
-      }
-      if (lane == 0) s_kept[j] = cnt;
+  int kept_before;
+  block_exclusive_scan(kc_before, s_tmp, &kept_before);
+  // ordered compaction of this block's kept tokens; a key above bin b0 is
+  // above T
+  uint32_t km = 0u;
+#pragma unroll
+  for (int j = 0; j < kSWTok / 1024; ++j)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      const int r = kSWTok / 256 * tid + 4 * j + y;
+      const uint32_t key = order_key(__uint_as_float(sv[j][y]));
+      const bool keep = r < n && (key > T || (key == T && blk0 + r <= I_T));
+      km |= (uint32_t)keep << (4 * j + y);
     }
-  } else {
-    for (int j = tid; j < nblk; j += 256) s_kept[j] = 0;
-    __syncthreads();
-    const float *sc = o.scores + (int64_t)pair * o.L_max;
-    for_items<false>(s_ck, s_ci, sc, L, [&](uint32_t key, int idx) {
-      if ((int)(key >> 21) == b0 && (key > T || (key == T && idx <= I_T))) atomicAdd(&s_kept[idx / kBlockTok], 1);
-    });
-  }
-  __syncthreads();
-  int run = 0;
-  for (int j0 = 0; j0 < nblk; j0 += 256) {
-    const int j = j0 + tid;
-    const int v = j < nblk ? o.blk_gt[(size_t)pair * kMaxBlocks + j] + s_kept[j] : 0;
-    int tot;
-    const int ex = block_exclusive_scan(v, s_tmp, &tot);
-    if (j < nblk) o.blk_off[(size_t)pair * kMaxBlocks + j] = run + ex;
-    run += tot;
-  }
-  if (tid == 0) {
-    o.state[pair].T = T;
-    o.state[pair].I_T = I_T;
-  }
-}
-
-// Ordered compaction: the block's keys are staged in LDS with coalesced
-// loads, then thread t takes tokens 8t..8t+7 of the block in order.
-__global__ __launch_bounds__(256) void oam_write_kernel(OamDev o) {
-  __shared__ uint32_t s_key[kBlockTok + kBlockTok / 8];  // one pad word per 8 keys
-  __shared__ int s_tmp[4];
-  const int pair = blockIdx.y;
-  const int L = pair_len(o, pair);
-  const int tid = threadIdx.x;
-  int32_t *out = o.idx_out + (int64_t)pair * o.top_k;
-  const int nk = min(o.top_k, L);
-  if (blockIdx.x == 0) {
-    if (tid == 0) o.n_kept[pair] = nk;
-    for (int i = nk + tid; i < o.top_k; i += 256) out[i] = -1;
-  }
-  const int blk0 = blockIdx.x * kBlockTok;
-  if (blk0 >= L) return;
-  const bool keep_all = o.top_k >= L;
-  const float *sc = o.scores + (int64_t)pair * o.L_max;
-  const int n = min(kBlockTok, L - blk0);
-  if (keep_all) {
-    for (int i = tid; i < n; i += 256) out[blk0 + i] = blk0 + i;
-    return;
-  }
-  // the threshold and this block's offset are read first, then the scores
-  // with unconditional buffer loads (past n they read zero), all in flight
-  // together
-  const uint32_t T = o.state[pair].T;
-  const int I_T = o.state[pair].I_T;
-  const int off0 = o.blk_off[(size_t)pair * kMaxBlocks + blockIdx.x];
-  const __amdgpu_buffer_rsrc_t srs =
-      __builtin_amdgcn_make_buffer_rsrc((void *)(sc + blk0), (short)0, n * 4, 0x00020000);
-  float sv[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    sv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(srs, (uint32_t)(tid + 256 * j) * 4u, 0, 0));
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = tid + 256 * j;
-    s_key[r + (r >> 3)] = order_key(sv[j]);
-  }
-  __syncthreads();
-  bool keep[8];
-  int kc = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 8 * tid + j;
-    const uint32_t key = s_key[r + (r >> 3)];
-    keep[j] = r < n && (key > T || (key == T && blk0 + r <= I_T));
-    kc += keep[j];
-  }
   int tot;
-  int pos = off0 + block_exclusive_scan(kc, s_tmp, &tot);
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (keep[j]) out[pos++] = blk0 + 8 * tid + j;
+  int pos = gt_before + kept_before + block_exclusive_scan(__popc(km), s_tmp, &tot);
+  const int t0 = blk0 + kSWTok / 256 * tid;
+  // (the slots past top_k are never reached when the candidate lists agree
+  // with the histogram; the bound keeps every store inside the pair's row)
+  while (km) {
+    if (pos < o.top_k) out[pos] = t0 + __ffs(km) - 1;
+    ++pos;
+    km &= km - 1u;
+  }
 }
 
 // Block-granular select, one workgroup per pair: the top_k blocks by
@@ -848,7 +855,6 @@ hipError_t launch_oam(const oam_topk_args &a, const OamPlan &plan, hipStream_t s
   o.blk_nc = plan.blk_nc;
   o.state = reinterpret_cast<OamState *>(plan.state);
   o.blk_gt = plan.blk_gt;
-  o.blk_off = plan.blk_off;
   o.cand_key = plan.cand_key;
   o.cand_idx = plan.cand_idx;
   o.idx_out = a.idx_out;
@@ -860,15 +866,9 @@ hipError_t launch_oam(const oam_topk_args &a, const OamPlan &plan, hipStream_t s
 
   hipError_t e;
   const bool block_mode = a.block_tokens > 1;
+  o.hist_tag = block_mode ? 0 : counter_tag_for(plan.hist);
   const int nblk = (g.max_seq_len + kBlockTok - 1) / kBlockTok;
   if (nblk > 0) {
-    if (!block_mode) {
-      // the histogram starts at zero (a fill kernel, not a memset)
-      const size_t nz = (size_t)npairs * kBins;
-      hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((nz + 255) / 256 < 128 ? (nz + 255) / 256 : 128)), dim3(256),
-                         0, s, plan.hist, nz);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
     if (!a.vlog) {
       e = launch_value_lognorm(g, a.v, a.kv_dtype, a.v_scale, a.eps, plan.vlog, plan.vlog_stride, s);
       if (e != hipSuccess) return e;
@@ -880,13 +880,15 @@ hipError_t launch_oam(const oam_topk_args &a, const OamPlan &plan, hipStream_t s
     if (!block_mode) {
       hipLaunchKernelGGL(oam_candidate_kernel, dim3(nblk, npairs), blk, 0, s, o);
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      hipLaunchKernelGGL(oam_select_kernel, dim3(npairs), blk, 0, s, o);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
   // the last pass also runs for empty caches: it sets n_kept and the -1 fill
-  if (block_mode) hipLaunchKernelGGL(oam_block_select_kernel, dim3(npairs), dim3(256), 0, s, o);
-  else hipLaunchKernelGGL(oam_write_kernel, dim3(nblk > 0 ? nblk : 1, npairs), dim3(256), 0, s, o);
+  if (block_mode) {
+    hipLaunchKernelGGL(oam_block_select_kernel, dim3(npairs), dim3(256), 0, s, o);
+  } else {
+    const int nsw = (g.max_seq_len + kSWTok - 1) / kSWTok;
+    hipLaunchKernelGGL(oam_select_write_kernel, dim3(nsw > 0 ? nsw : 1, npairs), dim3(256), 0, s, o);
+  }
   return hipGetLastError();
 }
 

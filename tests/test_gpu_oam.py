@@ -390,3 +390,55 @@ def test_block_select_128k_full_size():
     ref, ref_lse = oracle_all_rows(pk)
     assert np.abs(out.cpu().numpy().reshape(-1, w.D) - ref).max() <= 2e-3
     assert np.abs(lse.cpu().numpy().reshape(-1) - ref_lse).max() <= 1e-3
+
+
+def test_oam_workspace_needs_no_clearing():
+    # The selection's histogram words carry a per-call tag: a workspace holding
+    # garbage, or the words an earlier call on other inputs left, must give the
+    # same kept sets as a fresh workspace, call after call.
+    cases = []
+    for i, (lens, top_k) in enumerate(((np.array([9000, 4097, 0], np.int32), 300),
+                                      (np.array([20000, 17], np.int32), 1000),
+                                      (np.array([3000, 12000, 8193], np.int32), 77))):
+        w = synth.workload("oam_128k", B=len(lens), KH=2, lens=lens, layout="token_major", seed=80 + i)
+        q, k, v, g = synth.generate(w)
+        cases.append((w, q, k, v, g, top_k))
+
+    def call(c, ws):
+        w, q, k, v, g, top_k = c
+        qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
+        prep = pkg.prepare_oam(qd, to_dev(k), dev_geom(g), w.G, top_k, v=to_dev(v), workspace=ws)
+        assert prep.workspace.data_ptr() == ws.data_ptr()  # the given workspace, not a fresh one
+        prep()
+        torch.cuda.synchronize()
+        return prep.idx_out.cpu().numpy(), prep.n_kept.cpu().numpy()
+
+    fresh = []
+    for c in cases:
+        zero_ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
+        fresh.append(call(c, zero_ws))
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    for fill in ("random", "ones"):
+        log_case(f"oam reused workspace ({fill})")
+        if fill == "random":
+            ws = torch.randint(0, 256, (64 << 20,), dtype=torch.uint8, generator=gen).to(DEV)
+        else:
+            ws = torch.full((64 << 20,), 255, dtype=torch.uint8, device=DEV)
+        for rnd in range(2):
+            for c, (ref_idx, ref_nk) in zip(cases, fresh):
+                idx, nk = call(c, ws)
+                np.testing.assert_array_equal(nk, ref_nk)
+                np.testing.assert_array_equal(idx, ref_idx)
+    # and the fresh results are the right ones
+    w, q, k, v, g, top_k = cases[0]
+    p = problem(w, q, k, v, g)
+    qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
+    scores = torch.full((w.B * w.KH, int(g.max_len)), float("nan"), dtype=torch.float32, device=DEV)
+    idx, nk = pkg.oam_score_topk(qd, to_dev(k), dev_geom(g), w.G, top_k, v=to_dev(v), scores_out=scores)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), fresh[0][0])
+    sc = scores.cpu().numpy()
+    for b in range(w.B):
+        for kh in range(w.KH):
+            pr = b * w.KH + kh
+            check_pair(oracle.oam_scores(p, b, kh, 1.0, 1e-6), sc[pr], fresh[0][0][pr], fresh[0][1][pr], top_k)
