@@ -728,11 +728,11 @@ decode_mfma_kernel(DecodeParams p) {
           pv = qvalid[cb] ? pv : 0.f;
           l_run[cb] += pv;
           if constexpr (KVT == ATTN_BF16) {
-            const uint32_t hb = f32_to_bf16_bits(pv);
-            const float hf = __uint_as_float(hb << 16);
-            const uint32_t lb = f32_to_bf16_bits(pv - hf);
-            phi[cb][i] = __builtin_bit_cast(__bf16, (uint16_t)hb);
-            plo[cb][i] = __builtin_bit_cast(__bf16, (uint16_t)lb);
+            // round to nearest even; pairs of these conversions become one
+            // v_cvt_pk_bf16_f32
+            const __bf16 h = (__bf16)pv;
+            phi[cb][i] = h;
+            plo[cb][i] = (__bf16)(pv - (float)h);
           } else {
             const _Float16 h = (_Float16)pv;
             phi[cb][i] = h;
