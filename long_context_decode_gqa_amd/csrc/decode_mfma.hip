@@ -45,6 +45,11 @@ namespace lcdg {
 namespace {
 
 constexpr int kTile = 32;
+// Online softmax: a column's reference maximum is raised only when a tile's
+// scores exceed it by more than this (log2 units), so most tiles skip the
+// rescale of the accumulators (every tile of a 32-column wave would
+// otherwise pay it, as some column's maximum rises in nearly every tile).
+constexpr float kLazyRescale = 8.0f;
 
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
@@ -693,26 +698,42 @@ decode_mfma_kernel(DecodeParams p) {
     // operands are assembled once and serve every column block.
     auto finish_tile = [&](const TileT &R, int tile, const Raw &raw) {
       const int tpos = (tile - lane_t0) * kTile;
+      // a tile below every column's end needs no position mask (the first
+      // query row, r = 0, ends first)
+      const bool full = tpos + kTile <= min(seg_pos1, p.R > 1 ? L - (p.R - 1) : seg_pos1);
       OpT phi[CB], plo[CB];
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        const int lim = min(seg_pos1, col_end[cb]);
         float s[8];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int pos = tpos + 16 * tb + 4 * cg + i;
             float sc = c1;
             if constexpr (KVT == ATTN_I8) sc *= qs[cb] * (IDX ? R.ks[4 * tb + i] : R.ks[tb]);
-            s[4 * tb + i] = (pos < lim) ? raw.v[cb][4 * tb + i] * sc : NEG_INF;
+            s[4 * tb + i] = raw.v[cb][4 * tb + i] * sc;
           }
+        if (!full) {
+          const int lim = min(seg_pos1, col_end[cb]);
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (tpos + 16 * tb + 4 * cg + i >= lim) s[4 * tb + i] = NEG_INF;
+        }
         float mt = s[0];
 #pragma unroll
         for (int i = 1; i < 8; ++i) mt = fmaxf(mt, s[i]);
         mt = rows_max(mt);
-        const float m_new = fmaxf(m_run[cb], mt);
-        if (__any(m_new > m_run[cb])) {
+        // The reference m_run moves only when the tile's maximum exceeds it
+        // by more than kLazyRescale (log2 units): the weights exp2(s - m_run)
+        // then stay at most 2^kLazyRescale, and the final (m, l, O) are the
+        // same quantities for any reference.  A column whose reference does
+        // not move keeps alpha = 1 exactly, so each column's arithmetic is
+        // independent of the other columns of the wave.
+        const bool up = mt > m_run[cb] + kLazyRescale;
+        if (__any(up)) {
+          const float m_new = up ? mt : m_run[cb];
           // a column with no position seen yet (m_run = -inf) holds zeros;
           // the rescale must not form exp2(-inf - -inf)
           const float alpha = m_run[cb] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(m_run[cb] - m_new);
@@ -724,8 +745,9 @@ decode_mfma_kernel(DecodeParams p) {
         const float mref = (m_run[cb] == NEG_INF) ? 0.f : m_run[cb];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          float pv = __builtin_amdgcn_exp2f(s[i] - mref);
-          pv = qvalid[cb] ? pv : 0.f;
+          // (a column past the group's rows has a zero query: its weights
+          // are finite and its sums are never read)
+          const float pv = __builtin_amdgcn_exp2f(s[i] - mref);
           l_run[cb] += pv;
           if constexpr (KVT == ATTN_BF16) {
             // round to nearest even; pairs of these conversions become one
