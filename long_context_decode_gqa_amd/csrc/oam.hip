@@ -35,7 +35,8 @@ namespace {
 constexpr int kBins = 2048;       // 11-bit digits (the 10-bit ones use 1024)
 constexpr int kBlockTok = 2048;   // tokens per workgroup of the candidate and write passes
 constexpr int kSWTok = 8192;      // tokens per workgroup of the select-and-write pass
-constexpr int kSWCap = 6144;      // candidates a select-and-write workgroup holds in LDS (10 bytes each)
+constexpr int kSWCap = 12288;     // candidate keys a select-and-write workgroup holds in LDS
+constexpr int kSWOwn = 8192;      // up to this many, an owner map (2 bytes per key) fits beside them
 constexpr int kMaxBlocks = 1024;  // blocks of kBlockTok per pair (sequences up to 2M tokens)
 constexpr int kMaxSelBlocks = 8192;  // token blocks per pair the block-granular select holds
 
@@ -450,18 +451,21 @@ __device__ __forceinline__ int block_of(const int *s_pre, int nblk, int i) {
 }
 
 // Where the exact selection reads the candidates (keys of bin b0 and their
-// indices): a copy gathered in LDS, or the pair's candidate regions in
-// global memory (block j's items at j * kBlockTok, located through s_pre).
+// indices): the keys gathered in LDS (no indices: the index passes, needed
+// only when a group of equal keys is cut at the threshold, read global
+// memory), or the pair's candidate regions in global memory (block j's
+// items at j * kBlockTok, located through s_pre).
 enum { kFromLds = 0, kFromGlobal = 1 };
 
-// Calls f(key, idx) for the items 0..n-1, thread tid taking i = tid + 256 r;
-// from global memory 16 items' loads per thread are issued before any is used.
+// Calls f(key, idx) for the items 0..n-1 (idx is -1 from LDS), thread tid
+// taking i = tid + 256 r; from global memory 16 items' loads per thread are
+// issued before any is used.
 template <int SRC, typename F>
 __device__ __forceinline__ void for_items(const uint32_t *ck, const int32_t *ci, const int *s_pre, int nblk, int n,
                                           F &&f) {
   const int tid = threadIdx.x;
   if constexpr (SRC == kFromLds) {
-    for (int i = tid; i < n; i += 256) f(ck[i], ci[i]);
+    for (int i = tid; i < n; i += 256) f(ck[i], -1);
   } else {
     constexpr int U = 16;
     for (int i0 = 0; i0 < n; i0 += 256 * U) {
@@ -488,22 +492,25 @@ __device__ __forceinline__ void for_items(const uint32_t *ck, const int32_t *ci,
 // need-th largest key T, and, among the candidates equal to T, the need'-th
 // smallest index I_T (need' = how many of them are kept; I_T = INT_MAX when
 // all of them are).  All 256 threads call it and get the result.
+// The digit passes read the keys from SRC (ck: LDS keys, or the global
+// list); the index passes read the global list (gk, gi).
 template <int SRC>
-__device__ void select_threshold(int n, int b0, int need, const uint32_t *ck, const int32_t *ci, const int *s_pre,
-                                 int nblk, uint32_t *s_hist, int *s_tmp, int *s_res, uint32_t *T_out, int *I_out) {
+__device__ void select_threshold(int n, int b0, int need, const uint32_t *ck, const uint32_t *gk, const int32_t *gi,
+                                 const int *s_pre, int nblk, uint32_t *s_hist, int *s_tmp, int *s_res, uint32_t *T_out,
+                                 int *I_out) {
   const int tid = threadIdx.x;
   int above;
   // digit 2: key bits 20..10 (every candidate has top digit b0)
   for (int i = tid; i < kBins; i += 256) s_hist[i] = 0u;
   __syncthreads();
-  for_items<SRC>(ck, ci, s_pre, nblk, n, [&](uint32_t key, int idx) { atomicAdd(&s_hist[(key >> 10) & 0x7FFu], 1u); });
+  for_items<SRC>(ck, gi, s_pre, nblk, n, [&](uint32_t key, int idx) { atomicAdd(&s_hist[(key >> 10) & 0x7FFu], 1u); });
   __syncthreads();
   uint32_t prefix = ((uint32_t)b0 << 11) | (uint32_t)select_bin(s_hist, kBins, need, &above, s_tmp, s_res);
   need -= above;
   // digit 3: key bits 9..0
   for (int i = tid; i < kBins; i += 256) s_hist[i] = 0u;
   __syncthreads();
-  for_items<SRC>(ck, ci, s_pre, nblk, n, [&](uint32_t key, int idx) {
+  for_items<SRC>(ck, gi, s_pre, nblk, n, [&](uint32_t key, int idx) {
     if ((key >> 10) == prefix) atomicAdd(&s_hist[key & 0x3FFu], 1u);
   });
   __syncthreads();
@@ -522,7 +529,7 @@ __device__ void select_threshold(int n, int b0, int need, const uint32_t *ck, co
   // bits of the index, bins reversed so "largest bin" means smallest index
   for (int i = tid; i < kBins; i += 256) s_hist[i] = 0u;
   __syncthreads();
-  for_items<SRC>(ck, ci, s_pre, nblk, n, [&](uint32_t key, int idx) {
+  for_items<kFromGlobal>(gk, gi, s_pre, nblk, n, [&](uint32_t key, int idx) {
     if (key == T) atomicAdd(&s_hist[2047 - (idx >> 10)], 1u);
   });
   __syncthreads();
@@ -530,7 +537,7 @@ __device__ void select_threshold(int n, int b0, int need, const uint32_t *ck, co
   need -= above;
   for (int i = tid; i < kBins; i += 256) s_hist[i] = 0u;
   __syncthreads();
-  for_items<SRC>(ck, ci, s_pre, nblk, n, [&](uint32_t key, int idx) {
+  for_items<kFromGlobal>(gk, gi, s_pre, nblk, n, [&](uint32_t key, int idx) {
     if (key == T && (idx >> 10) == ihi) atomicAdd(&s_hist[1023 - (idx & 0x3FF)], 1u);
   });
   __syncthreads();
@@ -618,9 +625,11 @@ __global__ __launch_bounds__(256) void oam_candidate_kernel(OamDev o) {
 __global__ __launch_bounds__(256) void oam_select_write_kernel(OamDev o) {
   __shared__ uint32_t s_hist[kBins];
   __shared__ int s_pre[kMaxBlocks + 1];
+  // the gathered keys; with at most kSWOwn of them, the candidate block of
+  // each (the owner map) is kept in the words past kSWOwn
   __shared__ uint32_t s_ck[kSWCap];
-  __shared__ int32_t s_ci[kSWCap];
-  __shared__ uint16_t s_own[kSWCap];  // candidate block of each gathered item
+  uint16_t *s_own = reinterpret_cast<uint16_t *>(s_ck + kSWOwn);
+  static_assert(2 * kSWOwn <= 4 * (kSWCap - kSWOwn), "owner map beside kSWOwn keys");
   __shared__ int s_tmp[4], s_res[2];
   const int pair = blockIdx.y;
   const int L = pair_len(o, pair);
@@ -675,41 +684,43 @@ __global__ __launch_bounds__(256) void oam_select_write_kernel(OamDev o) {
   uint32_t T;
   int I_T, kc_before = 0;
   if (C <= kSWCap) {
-    // Gather into LDS.  Owner map first (LDS only): wave w writes block j's
-    // number over its items, for blocks j = w, w+4, ...; then each item costs
-    // two LDS reads before its loads, and all of a thread's loads are in
-    // flight together (clamped to the last item, so they are unconditional).
+    // Gather the keys into LDS.  With an owner map (built first, LDS only:
+    // wave w writes block j's number over its items, for blocks j = w, w+4,
+    // ...) each item costs two LDS reads before its load, else a binary
+    // search over the block starts; all of a thread's loads are in flight
+    // together (clamped to the last item, so they are unconditional).
     constexpr int kPer = 16;
-    const int wave = tid >> 6, lane = tid & 63;
-    for (int j = wave; j < nblk; j += 4)
-      for (int l = s_pre[j] + lane; l < s_pre[j + 1]; l += 64) s_own[l] = (uint16_t)j;
-    __syncthreads();
+    const bool own_map = C <= kSWOwn;
+    if (own_map) {
+      const int wave = tid >> 6, lane = tid & 63;
+      for (int j = wave; j < nblk; j += 4)
+        for (int l = s_pre[j] + lane; l < s_pre[j + 1]; l += 64) s_own[l] = (uint16_t)j;
+      __syncthreads();
+    }
     for (int i0 = 0; i0 < C; i0 += 256 * kPer) {
       uint32_t kr[kPer];
-      int32_t ir[kPer];
 #pragma unroll
       for (int r = 0; r < kPer; ++r) {
         const int i = min(i0 + tid + 256 * r, C - 1);
-        const int j = s_own[i];
-        const int64_t src = (int64_t)j * kBlockTok + (i - s_pre[j]);
-        kr[r] = gk[src];
-        ir[r] = gi[src];
+        const int j = own_map ? (int)s_own[i] : block_of(s_pre, nblk, i);
+        kr[r] = gk[(int64_t)j * kBlockTok + (i - s_pre[j])];
       }
 #pragma unroll
       for (int r = 0; r < kPer; ++r) {
         const int i = i0 + tid + 256 * r;
-        if (i < C) {
-          s_ck[i] = kr[r];
-          s_ci[i] = ir[r];
-        }
+        if (i < C) s_ck[i] = kr[r];
       }
     }
     __syncthreads();
-    select_threshold<kFromLds>(C, b0, need, s_ck, s_ci, s_pre, nblk, s_hist, s_tmp, s_res, &T, &I_T);
-    for_items<kFromLds>(s_ck, s_ci, s_pre, nblk, nbefore,
-                        [&](uint32_t key, int idx) { kc_before += key > T || (key == T && idx <= I_T); });
+    select_threshold<kFromLds>(C, b0, need, s_ck, gk, gi, s_pre, nblk, s_hist, s_tmp, s_res, &T, &I_T);
   } else {
-    select_threshold<kFromGlobal>(C, b0, need, gk, gi, s_pre, nblk, s_hist, s_tmp, s_res, &T, &I_T);
+    select_threshold<kFromGlobal>(C, b0, need, gk, gk, gi, s_pre, nblk, s_hist, s_tmp, s_res, &T, &I_T);
+  }
+  // kept candidates of the blocks before this one: keys >= T when every key
+  // equal to T is kept, else the indices of the keys equal to T decide
+  if (C <= kSWCap && I_T == 0x7FFFFFFF) {
+    for_items<kFromLds>(s_ck, gi, s_pre, nblk, nbefore, [&](uint32_t key, int idx) { kc_before += key >= T; });
+  } else {
     for_items<kFromGlobal>(gk, gi, s_pre, nblk, nbefore,
                            [&](uint32_t key, int idx) { kc_before += key > T || (key == T && idx <= I_T); });
   }

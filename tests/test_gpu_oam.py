@@ -164,11 +164,12 @@ def _topk_from_vlog(vlog_row, top_k, D=128, G=8):
     return idx.cpu().numpy()[0], int(nk.cpu().numpy()[0])
 
 
-@pytest.mark.parametrize("n", [10000, 20000])
+@pytest.mark.parametrize("n", [6000, 10000, 20000])
 def test_oam_many_candidates_in_threshold_bin(n):
-    # n distinct scores inside one top-digit bin ([1.0, 1.25)): 10000 candidates
-    # are gathered into LDS in several rounds; 20000 are more than the list
-    # holds, so the selection reads the pair's scores
+    # n distinct scores inside one top-digit bin ([1.0, 1.25)): 6000 candidate
+    # keys are gathered into LDS in two rounds through the owner map, 10000 in
+    # three rounds through a search of the block starts; 20000 are more than
+    # LDS holds, so the selection reads the candidate lists in memory
     rng = np.random.default_rng(70)
     vl = (1.0 + 0.2 * rng.permutation(n) / n).astype(np.float32)
     log_case(f"oam candidates in one bin n={n}")
