@@ -31,8 +31,10 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, vendor figure
 METRIC = "decode-attention KV GB/s (% of MI355X HBM peak) + µs/step at 128K KV"
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_mfma_dense128k_pmc.txt")
-# the decode kernel and the header it inlines; counters taken on other sources are stale
-DECODE_SOURCES = [os.path.join(ROOT, "long_context_decode_gqa_amd", "csrc", f) for f in ("decode_mfma.hip", "common.hpp")]
+# the decode kernel, the header it inlines and the build script (its compiler flags); counters
+# taken on other sources are stale
+DECODE_SOURCES = [os.path.join(ROOT, "long_context_decode_gqa_amd", f)
+                  for f in ("csrc/decode_mfma.hip", "csrc/common.hpp", "build.py")]
 
 
 # ------------------------------------------------------------------ byte/flop accounting

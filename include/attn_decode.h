@@ -379,7 +379,11 @@ attn_status oam_value_lognorm(const attn_kv_geom *geom, const void *v, int32_t v
  *               indices in ascending order; entries past n_kept are -1
  *   n_kept      int32 [B][KH]: kept tokens, min(top_k, L_b) for tokens
  *   scores_out  optional fp32 [B][KH][max_seq_len]: the scores
- *   workspace   >= oam_score_topk_workspace_size() bytes, 256-byte aligned
+ *   workspace   >= oam_score_topk_workspace_size() bytes, 256-byte aligned;
+ *               needs no initialisation: the selection's histogram words
+ *               carry a tag that changes with every call, so words left by
+ *               an earlier call (or other data) count as zero.  Calls that
+ *               share a workspace must be ordered on one stream
  */
 typedef struct {
   attn_kv_geom kv;
