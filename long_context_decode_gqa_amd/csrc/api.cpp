@@ -75,7 +75,7 @@ struct DecodeLayout {
   size_t m, l, o, ctr, total;
   int64_t max_partials, max_chunks, max_slots, lanes;
   int32_t split, ngb, max_tokens, grid;
-  int32_t cols;  // matrix-core columns per decode wave (16, or 32 for more than 16 rows per KV head)
+  int32_t cols;  // matrix-core columns per decode wave: 16, 32 (more than 16 rows per KV head) or 64
   int32_t wpg;   // waves per decode worker (workgroup)
   bool mfma;     // matrix-core decode (bf16/int8 KV), whose launch also merges
   bool stream_nt;  // matrix-core decode: non-temporal K/V loads
@@ -144,8 +144,12 @@ attn_status plan_decode(const attn_decode_args *a, DecodeLayout *L) {
   L->mfma = mfma;
   // More than 16 query rows per KV head: each wave computes 32 columns
   // (two blocks sharing every K/V load) instead of streaming the cache once
-  // per 16-column block.
-  L->cols = (mfma && R * a->G > 16) ? 32 : 16;
+  // per 16-column block.  More than 32 over a bf16 cache read by position:
+  // 64 columns (four blocks) in one wave, so every wave of a worker streams
+  // tiles of its own; two 32-column groups in one worker (int8, kept
+  // tokens) load each tile once per group.
+  const bool cols64 = mfma && R * a->G > 32 && a->kv_dtype == ATTN_BF16 && !a->token_idx;
+  L->cols = cols64 ? 64 : (mfma && R * a->G > 16) ? 32 : 16;
   L->ngb = (R * a->G + L->cols - 1) / L->cols;
   L->max_tokens = a->token_idx ? a->idx_stride : g.max_seq_len;
   L->lanes = (int64_t)g.B * g.KH * (mfma ? 1 : L->ngb);
@@ -158,7 +162,7 @@ attn_status plan_decode(const attn_decode_args *a, DecodeLayout *L) {
   // 256-thread workgroups per unit.
   L->wpg = mfma ? 4 : 1;
   const int cus = device_cu_count();
-  const int waves_per_cu = (L->cols == 32 || a->kv_dtype == ATTN_I8) ? 4 : 8;
+  const int waves_per_cu = (L->cols >= 32 || a->kv_dtype == ATTN_I8) ? 4 : 8;
   // A paged cache whose pages hold each token's heads together (token-major
   // pages: a KV head's rows stride_t > D apart): twice as many workers as fit
   // at once, over half-length ranges, so the workers active together cover

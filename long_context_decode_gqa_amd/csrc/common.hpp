@@ -104,7 +104,7 @@ struct DecodeParams {
   // per pair (ngb for the vector-ALU decode, 1 for the matrix-core decode)
   int32_t B, KH, G, D, QH, ngb, lpp;
   int32_t Gq, R;  // query heads per KV head, query rows per sequence
-  int32_t cols_per_wave;  // matrix-core columns a decode worker computes: 16, or 32 when G > 16
+  int32_t cols_per_wave;  // matrix-core columns of a decode wave: 16, 32 when G > 16, 64 (bf16 by position) when G > 32
   const int32_t *seq_lens;
   const int64_t *seq_offset;
   int64_t stride_h, stride_t;

@@ -106,7 +106,7 @@ struct Step {
   // step holds two tiles or token indices take registers.
   // Two column blocks per wave (CB = 2) run one wave per SIMD with twice the
   // registers, so the ring is deeper to keep as many bytes in flight per SIMD.
-  static constexpr int NBUF = CB == 2 ? (KVT == ATTN_BF16 ? 4 : (TPS == 1 && !IDX ? 6 : 4))
+  static constexpr int NBUF = CB == 4 ? 3 : CB == 2 ? (KVT == ATTN_BF16 ? 4 : (TPS == 1 && !IDX ? 6 : 4))
                                       : (KVT == ATTN_BF16 ? 2 : (TPS == 1 && !IDX ? 4 : 3));
   static constexpr bool PIPE = KVT == ATTN_I8;
   TileT t[TPS];
@@ -140,10 +140,10 @@ constexpr int kMaxSegPages = 520;
 constexpr int kWPG = 4;  // waves per worker
 
 template <int D, int KVT, bool IDX, bool QI8, bool PAGED, int CB, bool STREAM>
-__global__ __launch_bounds__(64 * kWPG) __attribute__((amdgpu_waves_per_eu(CB == 2 ? 1 : 2, CB == 2 ? 1 : 2))) void
+__global__ __launch_bounds__(64 * kWPG) __attribute__((amdgpu_waves_per_eu(CB >= 2 ? 1 : 2, CB >= 2 ? 1 : 2))) void
 decode_mfma_kernel(DecodeParams p) {
   static_assert(!(IDX && PAGED), "a paged cache is read by position");
-  static_assert(CB == 1 || CB == 2, "one or two 16-column blocks per wave");
+  static_assert(CB == 1 || CB == 2 || (CB == 4 && KVT == ATTN_BF16), "one, two or (bf16) four 16-column blocks per wave");
   static_assert(!(STREAM && IDX), "gathered kept rows use the default cache policy");
   // K/V cache policy: non-temporal where the launch streams the whole cache
   // over a full grid (STREAM, chosen by the host), the default otherwise
@@ -1017,10 +1017,30 @@ static void launch_cb(const DecodeParams &p, int kv_dtype, dim3 g, hipStream_t s
   else launch_variant<IDX, PAGED, 1, false>(p, kv_dtype, g, s);
 }
 
+// 64 columns per wave: bf16 caches read by position only (the host routes
+// nothing else here)
+template <bool PAGED, bool STREAM>
+static void launch_cb4(const DecodeParams &p, dim3 g, hipStream_t s) {
+  dim3 blk(64 * kWPG);
+  if (p.D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, ATTN_BF16, false, false, PAGED, 4, STREAM>), g, blk, 0, s, p);
+  else hipLaunchKernelGGL((decode_mfma_kernel<64, ATTN_BF16, false, false, PAGED, 4, STREAM>), g, blk, 0, s, p);
+}
+
 hipError_t launch_decode_mfma(const DecodeParams &p, int kv_dtype, hipStream_t s) {
   if (p.wpg != kWPG) return hipErrorInvalidValue;
   if (p.ngb < 1 || p.ngb > (p.cols_per_wave == 32 ? 2 : 1)) return hipErrorInvalidValue;
   if (!p.wl.ctr || p.max_slots < 1) return hipErrorInvalidValue;
+  if (p.cols_per_wave == 64) {
+    if (kv_dtype != ATTN_BF16 || p.token_idx) return hipErrorInvalidValue;
+    if (p.block_table) {
+      if (p.stream_nt) launch_cb4<true, true>(p, dim3(p.grid), s);
+      else launch_cb4<true, false>(p, dim3(p.grid), s);
+    } else {
+      if (p.stream_nt) launch_cb4<false, true>(p, dim3(p.grid), s);
+      else launch_cb4<false, false>(p, dim3(p.grid), s);
+    }
+    return hipGetLastError();
+  }
   if (p.token_idx) {
     if (p.block_table) return hipErrorInvalidValue;
     launch_cb<true, false>(p, kv_dtype, dim3(p.grid), s);

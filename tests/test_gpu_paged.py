@@ -113,6 +113,33 @@ def test_paged_equals_contiguous_bit_exact(P, layout, kv, D):
         assert np.abs(out_p.reshape(-1, w.D) - ref).max() <= 2e-3
 
 
+@pytest.mark.parametrize("P,layout", [(64, "head_major"), (32, "token_major")])
+@pytest.mark.parametrize("D", [128, 64])
+def test_paged_64_column_waves_equal_contiguous(P, layout, D):
+    # 48 query heads per KV head over a bf16 cache: 64-column waves (four
+    # 16-column blocks per wave), contiguous and paged, bit for bit, and
+    # against the oracle
+    lens = np.array([3000, 1, 4097, 0, 640], np.int32)
+    w = synth.workload("gqa32k", B=len(lens), KH=2, G=48, D=D, lens=lens, layout=layout, seed=150 + P + D)
+    q, k, v, g = synth.generate(w)
+    log_case(f"64-column waves P={P} {layout} D={D}")
+    qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
+    kw = dict(split_tokens=1024)
+    out_c, lse_c = run(qd, to_dev(k), to_dev(v), dev_geom(g), w.G, w.B, w.QH, **kw)
+    junk = np.uint16(0x7FC0)  # NaN: rows past L must never be read
+    kp, table, st, sh, ps = make_pool(k, g, P, layout, 9 + P, junk)
+    vp, _, _, _, _ = make_pool(v, g, P, layout, 9 + P, junk)
+    out_p, lse_p = run(qd, to_dev(kp), to_dev(vp), paged_geom(g, table, P, st, sh, ps), w.G, w.B, w.QH, **kw)
+    assert np.isfinite(out_p).all()
+    np.testing.assert_array_equal(out_p, out_c)
+    np.testing.assert_array_equal(lse_p, lse_c)
+    p = problem(w, q, k, v, g)
+    ref, ref_lse = oracle.attention_rows(p, oracle.all_rows(p), nthreads=8)
+    assert np.abs(out_c.reshape(-1, w.D) - ref).max() <= 2e-3
+    live = np.isfinite(ref_lse)
+    assert np.abs(lse_c.reshape(-1)[live] - ref_lse[live]).max() <= 1e-3
+
+
 def test_paged_128k_full_size_equals_contiguous():
     """The 128K bf16 workload (4 x 8 KV heads x 131072 tokens) in scrambled pools of 64-token
     pages.  In the benchmark's launch configuration (the library's default split) head-major
