@@ -32,7 +32,10 @@ def run(w, q, k, v, g, R, **kw):
     return out.float().cpu().numpy(), lse.cpu().numpy()
 
 
-@pytest.mark.parametrize("R,G,D", [(2, 8, 128), (4, 4, 128), (2, 16, 64), (3, 8, 64), (8, 8, 128)])
+# R * G columns per KV head: 16 or fewer (one 16-column block per wave), 17-32 (32-column waves),
+# 33-64 (64-column waves over bf16, two 32-column groups over int8)
+@pytest.mark.parametrize("R,G,D", [(2, 8, 128), (4, 4, 128), (2, 16, 64), (3, 8, 64), (8, 8, 128), (5, 8, 64),
+                                   (8, 6, 128)])
 @pytest.mark.parametrize("kv", ["bf16", "int8", "int8_qrow"])
 def test_multirow_against_oracle(R, G, D, kv):
     lens = np.array([1, 2, 700, 4096, 0, 2049, 5], np.int32)
