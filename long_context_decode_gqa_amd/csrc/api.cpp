@@ -375,6 +375,10 @@ attn_status decode_run(const attn_decode_args *a, void *workspace, size_t worksp
   p.wpg = L.wpg;
   p.fixed_splits = a->fixed_splits;
   p.stream_nt = L.stream_nt ? 1 : 0;
+  // the vector-ALU decode with one worker and one chunk per lane: every
+  // lane's partial is its result, so the kernel writes out and lse and the
+  // merge launch is skipped
+  p.direct_out = (!L.mfma && L.grid == 1 && L.max_chunks == 1 && a->fixed_splits == 0) ? 1 : 0;
   p.grid = L.grid;
   p.wl.m_part = reinterpret_cast<float *>(ws + L.m);
   p.wl.l_part = reinterpret_cast<float *>(ws + L.l);
@@ -395,7 +399,7 @@ attn_status decode_run(const attn_decode_args *a, void *workspace, size_t worksp
   else e = launch_decode_valu(p, a->q_dtype, a->kv_dtype, s);
   if (e != hipSuccess) return fail_hip(e, "decode launch");
   if ((e = mark(1)) != hipSuccess) return fail_hip(e, "event record");
-  if (!L.mfma) {
+  if (!L.mfma && !p.direct_out) {
     e = launch_merge_decode(p, a->out_dtype, a->out, a->lse, s);
     if (e != hipSuccess) return fail_hip(e, "merge launch");
   }

@@ -128,6 +128,7 @@ struct DecodeParams {
   int32_t wpg;          // waves per decode workgroup (the MFMA kernel's workers)
   int32_t fixed_splits; // matrix-core decode: 0 = balanced split; S > 0 = each lane in S splits, one worker each
   int32_t stream_nt;    // matrix-core decode: non-temporal K/V loads (the launch streams over a full grid)
+  int32_t direct_out;   // vector-ALU decode: one worker and one chunk per lane, so it writes out and lse itself
   WorkList wl;
   // outputs, written by the matrix-core decode launch
   int32_t out_dtype;

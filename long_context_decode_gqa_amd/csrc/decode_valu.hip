@@ -85,6 +85,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int cpr = D / 4;  // 16-byte chunks per row
   const float NEG_INF = -__builtin_huge_valf();
 
+  if (p.direct_out && blockIdx.x == 0) {
+    // no merge follows: the lanes without positions get out = 0 and
+    // lse = -inf here (every other lane is one segment of this worker)
+    const int nlanes = p.B * p.KH * p.lpp;
+    for (int q = 0; q < nlanes; ++q) {
+      const int pair = q / p.lpp, gb = q - pair * p.lpp;
+      const int b = pair / p.KH, kh = pair - b * p.KH;
+      const int L = min(max(p.seq_lens[b], 0), p.max_seq_len);
+      const int npos = IDX ? (L > 0 ? min(max(p.n_idx[pair], 0), p.idx_stride) : 0) : L;
+      if (npos > 0) continue;
+      const int g0 = gb * 16, gcount = min(16, p.G - g0);
+      for (int e = tid; e < gcount * D; e += 256) {
+        const int g = e / D, d = e - g * D;
+        const int64_t orow = q_row_index(p, b, kh, g0 + g);
+        if (p.out_dtype == ATTN_F32) ((float *)p.out)[orow * D + d] = 0.f;
+        else ((uint16_t *)p.out)[orow * D + d] = 0u;
+        if (d == 0 && p.lse) p.lse[orow] = NEG_INF;
+      }
+    }
+  }
+
   const int T = wave_total_tiles(p);
   const int nwg = workers_for(p, T);
   if ((int)blockIdx.x >= nwg) return;
@@ -247,6 +268,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
       __syncthreads();
 
+      if (p.direct_out) {
+        // the segment is the whole lane: out = O / l and lse = m + ln l
+#pragma unroll
+        for (int k = 0; k < KO; ++k) {
+          const int e = tid + 256 * k;
+          if (e < gcount * D) {
+            const int g = e / D, d = e - g * D;
+            const float l = s_l[g];
+            const float ov = (l > 0.f) ? o[k] / l : 0.f;
+            const int64_t orow = q_row_index(p, b, kh, g0 + g);
+            if (p.out_dtype == ATTN_F32) ((float *)p.out)[orow * D + d] = ov;
+            else ((uint16_t *)p.out)[orow * D + d] = (uint16_t)f32_to_bf16_bits(ov);
+            if (d == 0 && p.lse) p.lse[orow] = (l > 0.f) ? s_m[g] + logf(l) : NEG_INF;
+          }
+        }
+        seg_t0 = seg_t1;
+        continue;
+      }
       const int half = (seg_t0 == lane_t0 + chunk * ct) ? 0 : 1;
       const bool fill_second = half == 0 && seg_t1 == chunk_t1;
 #pragma unroll

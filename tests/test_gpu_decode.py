@@ -48,7 +48,10 @@ def test_tiny_fp32_unsplit_and_split(split):
     check(out, lse, ref, ref_lse, tol=1e-5)
 
 
-@pytest.mark.parametrize("D,G,split", [(4, 3, 0), (36, 20, 64), (100, 7, 96), (256, 16, 0), (64, 33, 256)])
+# split 4096 / 16384: one worker and one chunk per lane, so the decode writes the rows itself
+# (empty lanes included) and no merge runs
+@pytest.mark.parametrize("D,G,split", [(4, 3, 0), (36, 20, 64), (100, 7, 96), (256, 16, 0), (64, 33, 256),
+                                       (100, 7, 4096), (64, 33, 16384)])
 def test_fp32_ragged_head_sizes_and_groups(D, G, split):
     """The fp32 path over ragged lengths (empty, shorter than a tile, tile and chunk boundaries)
     for head sizes 4..256 and group sizes beyond one 16-head block."""
@@ -62,8 +65,10 @@ def test_fp32_ragged_head_sizes_and_groups(D, G, split):
     check(out, lse, ref, ref_lse, tol=1e-5)
 
 
-def test_fp32_kept_token_subset():
-    """The fp32 path with a per-(sequence, KV head) list of kept positions."""
+@pytest.mark.parametrize("split", [64, 4096])
+def test_fp32_kept_token_subset(split):
+    """The fp32 path with a per-(sequence, KV head) list of kept positions (split 4096: one worker,
+    no merge)."""
     lens = np.array([500, 77, 0, 1200], np.int32)
     w = synth.workload("tiny", B=len(lens), KH=2, G=4, D=64, lens=lens, layout="head_major", seed=131)
     q, k, v, g = synth.generate(w)
@@ -76,8 +81,8 @@ def test_fp32_kept_token_subset():
             n = min(int(lens[b]), int(rng.integers(1, stride + 1)))
             idx[b, kh, :n] = np.sort(rng.choice(int(lens[b]), n, replace=False)) if n else []
             nidx[b, kh] = n
-    log_case("fp32 kept tokens")
-    out, lse = run_decode(w, q, k, v, g, split_tokens=64, token_idx=to_dev(idx), n_idx=to_dev(nidx))
+    log_case(f"fp32 kept tokens split={split}")
+    out, lse = run_decode(w, q, k, v, g, split_tokens=split, token_idx=to_dev(idx), n_idx=to_dev(nidx))
     p = problem(w, q, k, v, g, tok_idx=idx.reshape(-1), n_idx=nidx.reshape(-1), idx_stride=stride)
     ref, ref_lse = oracle.attention_rows(p, oracle.all_rows(p))
     check(out, lse, ref, ref_lse, tol=1e-5)
