@@ -443,3 +443,18 @@ def test_oam_workspace_needs_no_clearing():
         for kh in range(w.KH):
             pr = b * w.KH + kh
             check_pair(oracle.oam_scores(p, b, kh, 1.0, 1e-6), sc[pr], fresh[0][0][pr], fresh[0][1][pr], top_k)
+
+
+def test_oam_sequence_past_256_candidate_blocks():
+    # 600 000 tokens: 293 candidate blocks of 2048 tokens, so the select-and-write
+    # pass scans the block counts in several rounds; a second, short sequence
+    # shares the launch
+    lens = np.array([600000, 3000], np.int32)
+    w = synth.workload("oam_128k", B=2, KH=1, lens=lens, layout="head_major", seed=90)
+    q, k, v, g = synth.generate(w, nthreads=8)
+    log_case("oam 600000-token sequence")
+    top_k = 5000
+    idx, nk, sc = run_oam(w, q, k, v, g, top_k)
+    p = problem(w, q, k, v, g)
+    for b in range(w.B):
+        check_pair(oracle.oam_scores(p, b, 0, 1.0, 1e-6), sc[b], idx[b], nk[b], top_k)
