@@ -101,3 +101,54 @@ def test_multirow_128k_full_size():
     print(f"[info] oracle over {len(rows)} rows: {time.perf_counter() - t0:.1f} s", flush=True)
     assert np.abs(out.reshape(-1, w.D) - ref).max() <= 2e-3
     assert np.abs(lse.reshape(-1) - ref_lse).max() <= 1e-3
+
+
+def test_multirow_128k_eight_rows():
+    """R = 8 at the 128K bf16 shape (64 columns per KV head: 64-column waves over a full grid with
+    non-temporal loads, the benchmark's launch): every row against the oracle."""
+    w = synth.workload("dense128k")
+    _, k, v, g = synth.generate(w)
+    R = 8
+    q = multirow_q(w, R, 152)
+    log_case("multirow 128k eight rows")
+    out, lse = run(w, q, to_dev(k), to_dev(v), g, R, split_tokens=w.split_tokens)
+    p = problem(w, np.ascontiguousarray(q[:, 0]), k, v, g)
+    p.q = q
+    rows = [(b, r, qh) for b in range(w.B) for r in range(R) for qh in range(w.QH)]
+    t0 = time.perf_counter()
+    ref, ref_lse = oracle.attention_multirow(p, R, rows, nthreads=host_threads())
+    print(f"[info] oracle over {len(rows)} rows: {time.perf_counter() - t0:.1f} s", flush=True)
+    assert np.abs(out.reshape(-1, w.D) - ref).max() <= 2e-3
+    assert np.abs(lse.reshape(-1) - ref_lse).max() <= 1e-3
+
+
+def test_multirow_paged_full_grid():
+    """R = 8 over a head-major paged pool with enough tiles for the full-grid launch (64-column
+    waves, page table, non-temporal loads): bit for bit the contiguous decode, and against the
+    oracle."""
+    from test_gpu_paged import make_pool, paged_geom
+    L, P = 40960, 64
+    w = synth.workload("dense128k", L=L)
+    _, k, v, g = synth.generate(w)
+    R = 8
+    q = multirow_q(w, R, 153)
+    log_case("multirow paged full grid")
+    kw = dict(split_tokens=w.split_tokens)
+    out_c, lse_c = run(w, q, to_dev(k), to_dev(v), g, R, **kw)
+    kp, table, st, sh, ps = make_pool(k, g, P, "head_major", 17, np.uint16(0x7FC0))
+    vp, _, _, _, _ = make_pool(v, g, P, "head_major", 17, np.uint16(0x7FC0))
+    qd = to_dev(q.reshape(-1)).view(w.B, R, w.QH, w.D)
+    lse_p = torch.empty((w.B, R, w.QH), dtype=torch.float32, device=DEV)
+    out_p, _ = pkg.attn_decode_splitkv(qd, to_dev(kp), to_dev(vp), paged_geom(g, table, P, st, sh, ps), w.G,
+                                       lse=lse_p, q_rows=R, **kw)
+    torch.cuda.synchronize()
+    out_p, lse_p = out_p.float().cpu().numpy(), lse_p.cpu().numpy()
+    assert np.isfinite(out_p).all()
+    np.testing.assert_array_equal(out_p, out_c)
+    np.testing.assert_array_equal(lse_p, lse_c)
+    p = problem(w, np.ascontiguousarray(q[:, 0]), k, v, g)
+    p.q = q
+    rows = [(b, r, qh) for b in range(w.B) for r in range(R) for qh in range(w.QH)]
+    ref, ref_lse = oracle.attention_multirow(p, R, rows, nthreads=host_threads())
+    assert np.abs(out_c.reshape(-1, w.D) - ref).max() <= 2e-3
+    assert np.abs(lse_c.reshape(-1) - ref_lse).max() <= 1e-3
