@@ -152,3 +152,33 @@ def test_multirow_paged_full_grid():
     ref, ref_lse = oracle.attention_multirow(p, R, rows, nthreads=host_threads())
     assert np.abs(out_c.reshape(-1, w.D) - ref).max() <= 2e-3
     assert np.abs(lse_c.reshape(-1) - ref_lse).max() <= 1e-3
+
+
+def test_multirow_four_rows_full_grid():
+    """R = 4 (32-column waves, one column group) with enough tiles for the full-grid launch
+    (non-temporal loads), contiguous and over a head-major paged pool: bit for bit the same, and
+    against the oracle."""
+    from test_gpu_paged import make_pool, paged_geom
+    L, P = 40960, 64
+    w = synth.workload("dense128k", L=L)
+    _, k, v, g = synth.generate(w)
+    R = 4
+    q = multirow_q(w, R, 154)
+    log_case("multirow four rows full grid")
+    kw = dict(split_tokens=w.split_tokens)
+    out_c, lse_c = run(w, q, to_dev(k), to_dev(v), g, R, **kw)
+    kp, table, st, sh, ps = make_pool(k, g, P, "head_major", 19, np.uint16(0x7FC0))
+    vp, _, _, _, _ = make_pool(v, g, P, "head_major", 19, np.uint16(0x7FC0))
+    qd = to_dev(q.reshape(-1)).view(w.B, R, w.QH, w.D)
+    lse_p = torch.empty((w.B, R, w.QH), dtype=torch.float32, device=DEV)
+    out_p, _ = pkg.attn_decode_splitkv(qd, to_dev(kp), to_dev(vp), paged_geom(g, table, P, st, sh, ps), w.G,
+                                       lse=lse_p, q_rows=R, **kw)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out_p.float().cpu().numpy(), out_c)
+    np.testing.assert_array_equal(lse_p.cpu().numpy(), lse_c)
+    p = problem(w, np.ascontiguousarray(q[:, 0]), k, v, g)
+    p.q = q
+    rows = [(b, r, qh) for b in range(w.B) for r in range(R) for qh in range(w.QH)]
+    ref, ref_lse = oracle.attention_multirow(p, R, rows, nthreads=host_threads())
+    assert np.abs(out_c.reshape(-1, w.D) - ref).max() <= 2e-3
+    assert np.abs(lse_c.reshape(-1) - ref_lse).max() <= 1e-3
