@@ -291,31 +291,35 @@ def test_paged_value_norms_and_oam_equal_contiguous(P, layout, kv):
                 np.testing.assert_array_equal(sp_h[b * g.KH + kh, :L], s_h[b * g.KH + kh, :L])
 
 
-@pytest.mark.parametrize("kv", ["int8", "int8_qrow"])
-def test_paged_int8_full_grid_equals_contiguous(kv):
-    """An INT8 cache with enough tiles for the full-grid launch (non-temporal loads) in head-major
-    pages: bit for bit the contiguous INT8 decode, and against the oracle on the cached values."""
-    L, P = 40960, 64
-    w = synth.workload("dense128k", L=L)
+@pytest.mark.parametrize("kv", ["bf16", "int8", "int8_qrow"])
+@pytest.mark.parametrize("D", [128, 64])
+def test_paged_full_grid_equals_contiguous(kv, D):
+    """Caches with enough tiles for the full-grid launch (non-temporal loads), contiguous and in
+    head-major pages: bit for bit the same, and against the oracle on the cached values."""
+    L, P = 40960 * 128 // D, 64
+    w = synth.workload("dense128k", L=L, D=D)
     q, k, v, g = synth.generate(w)
-    log_case(f"paged int8 full grid {kv}")
+    log_case(f"paged full grid {kv} D={D}")
     qd = to_dev(q.reshape(-1)).view(w.B, w.QH, w.D)
     geom_c = dev_geom(g)
-    kc, ks = pkg.kv_quant_int8(to_dev(k), geom_c, 64)
-    vc, vs = pkg.kv_quant_int8(to_dev(v), geom_c, 0)
-    torch.cuda.synchronize()
-    kx, vx = kc.cpu().numpy(), vc.cpu().numpy()
-    del kc, vc
-    kw = dict(split_tokens=w.split_tokens, k_scale=ks, k_part_tokens=64, v_scale=float(vs.item()))
-    pk = dict(k_scale=ks.cpu().numpy(), k_part=64, k_scale_stride=-(-L // 64), v_scale=float(vs.item()))
-    qo = q
-    if kv == "int8_qrow":
-        kw["q_quant"] = pkg.QUANT_ROW
-        qc, qs = oracle.quant_rows(q.reshape(-1, w.D))
-        qo, pk["q_scale"] = qc.reshape(q.shape), qs
+    kw, pk, qo = dict(split_tokens=w.split_tokens), {}, q
+    if kv == "bf16":
+        kx, vx, junk = k, v, np.uint16(0x7FC0)
+    else:
+        kc, ks = pkg.kv_quant_int8(to_dev(k), geom_c, 64)
+        vc, vs = pkg.kv_quant_int8(to_dev(v), geom_c, 0)
+        torch.cuda.synchronize()
+        kx, vx, junk = kc.cpu().numpy(), vc.cpu().numpy(), np.int8(0)
+        del kc, vc
+        kw.update(k_scale=ks, k_part_tokens=64, v_scale=float(vs.item()))
+        pk = dict(k_scale=ks.cpu().numpy(), k_part=64, k_scale_stride=-(-L // 64), v_scale=float(vs.item()))
+        if kv == "int8_qrow":
+            kw["q_quant"] = pkg.QUANT_ROW
+            qc, qs = oracle.quant_rows(q.reshape(-1, w.D))
+            qo, pk["q_scale"] = qc.reshape(q.shape), qs
     out_c, lse_c = run(qd, to_dev(kx), to_dev(vx), geom_c, w.G, w.B, w.QH, **kw)
-    kp, table, st, sh, ps = make_pool(kx, g, P, "head_major", 23, np.int8(0))
-    vp, _, _, _, _ = make_pool(vx, g, P, "head_major", 23, np.int8(0))
+    kp, table, st, sh, ps = make_pool(kx, g, P, "head_major", 23, junk)
+    vp, _, _, _, _ = make_pool(vx, g, P, "head_major", 23, junk)
     out_p, lse_p = run(qd, to_dev(kp), to_dev(vp), paged_geom(g, table, P, st, sh, ps), w.G, w.B, w.QH, **kw)
     np.testing.assert_array_equal(out_p, out_c)
     np.testing.assert_array_equal(lse_p, lse_c)
