@@ -122,13 +122,14 @@ def test_multirow_128k_eight_rows():
     assert np.abs(lse.reshape(-1) - ref_lse).max() <= 1e-3
 
 
-def test_multirow_paged_full_grid():
+@pytest.mark.parametrize("D", [128, 64])
+def test_multirow_paged_full_grid(D):
     """R = 8 over a head-major paged pool with enough tiles for the full-grid launch (64-column
     waves, page table, non-temporal loads): bit for bit the contiguous decode, and against the
     oracle."""
     from test_gpu_paged import make_pool, paged_geom
-    L, P = 40960, 64
-    w = synth.workload("dense128k", L=L)
+    L, P = 40960 * 128 // D, 64
+    w = synth.workload("dense128k", L=L, D=D)
     _, k, v, g = synth.generate(w)
     R = 8
     q = multirow_q(w, R, 153)
@@ -154,13 +155,14 @@ def test_multirow_paged_full_grid():
     assert np.abs(lse_c.reshape(-1) - ref_lse).max() <= 1e-3
 
 
-def test_multirow_four_rows_full_grid():
+@pytest.mark.parametrize("D", [128, 64])
+def test_multirow_four_rows_full_grid(D):
     """R = 4 (32-column waves, one column group) with enough tiles for the full-grid launch
     (non-temporal loads), contiguous and over a head-major paged pool: bit for bit the same, and
     against the oracle."""
     from test_gpu_paged import make_pool, paged_geom
-    L, P = 40960, 64
-    w = synth.workload("dense128k", L=L)
+    L, P = 40960 * 128 // D, 64
+    w = synth.workload("dense128k", L=L, D=D)
     _, k, v, g = synth.generate(w)
     R = 4
     q = multirow_q(w, R, 154)
