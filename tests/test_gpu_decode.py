@@ -138,9 +138,10 @@ def test_large_scores_and_peaked_softmax():
     check(out, lse, ref, ref_lse)
 
 
-def test_token_index_subset():
+@pytest.mark.parametrize("G", [8, 24, 48])  # one 16-column block, one 32-column group, two groups
+def test_token_index_subset(G):
     lens = np.array([3000, 1500], np.int32)
-    w = synth.workload("gqa32k", B=2, KH=2, G=8, lens=lens, layout="token_major", seed=11)
+    w = synth.workload("gqa32k", B=2, KH=2, G=G, lens=lens, layout="token_major", seed=11)
     q, k, v, g = synth.generate(w)
     rng = np.random.default_rng(0)
     stride = 700
@@ -153,7 +154,7 @@ def test_token_index_subset():
     nidx = np.array([len(x) for x in lists], np.int32)
     for i, x in enumerate(lists):
         idx[i, :len(x)] = x
-    log_case("token index subset")
+    log_case(f"token index subset G={G}")
     p = problem(w, q, k, v, g, tok_idx=idx.reshape(-1), n_idx=nidx, idx_stride=stride)
     ref, ref_lse = oracle.attention_rows(p, oracle.all_rows(p), nthreads=8)
     out, lse = run_decode(w, q, k, v, g, split_tokens=256, token_idx=to_dev(idx), n_idx=to_dev(nidx))

@@ -175,9 +175,10 @@ def test_int8_decode_matches_oracle_on_dequantised_values(G, D):
         assert np.abs(lse - ref_lse).max() <= 1e-3
 
 
-def test_int8_decode_with_kept_token_subset():
+@pytest.mark.parametrize("G", [8, 24, 40])  # one 16-column block, one 32-column group, two groups
+def test_int8_decode_with_kept_token_subset(G):
     lens = np.array([2000, 900], np.int32)
-    w = synth.workload("int8_128k", B=2, KH=2, G=8, lens=lens, layout="token_major", seed=58)
+    w = synth.workload("int8_128k", B=2, KH=2, G=G, lens=lens, layout="token_major", seed=58)
     q, k, v, g = gen_kv(w)
     kc, ks = gpu_quant(k, g, 64)
     vc, vsa = gpu_quant(v, g, 0)
@@ -187,7 +188,7 @@ def test_int8_decode_with_kept_token_subset():
     nidx = np.array([600, 17, 300, 1], np.int32)
     for i in range(4):
         idx[i, :nidx[i]] = np.sort(rng.choice(lens[i // 2], size=nidx[i], replace=False))
-    log_case("int8 decode kept subset")
+    log_case(f"int8 decode kept subset G={G}")
     p = problem(w, q, kc, vc, g, k_scale=ks, k_part=64, k_scale_stride=-(-2000 // 64), v_scale=float(vsa[0]),
                 tok_idx=idx.reshape(-1), n_idx=nidx, idx_stride=stride)
     ref, ref_lse = oracle.attention_rows(p, oracle.all_rows(p), nthreads=8)
